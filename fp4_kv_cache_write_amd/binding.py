@@ -1,0 +1,258 @@
+"""ctypes binding of libcsa2.so — argument marshalling only.
+
+torch supplies device memory and the current HIP stream; every step of the path
+runs in the library's HIP kernels.  There is no fallback: a missing library or a
+failed call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libcsa2.so")
+
+D_LATENT, D_INDEX, H_INDEX, PAGE = 512, 64, 4, 64
+FN_INDEX_FULL, FN_REINDEX, FN_SPARSE_DECODE, FN_PREFILL_CHUNK = 1, 2, 3, 4
+
+EXPORTS = ("csa2_bytes_per_entry", "csa2_strerror", "csa2_workspace_size", "csa2_write_kv",
+           "csa2_index_full", "csa2_reindex", "csa2_sparse_decode", "csa2_prefill_chunk",
+           "csa2_debug_gather")
+
+
+class Csa2Error(RuntimeError):
+    pass
+
+
+class CacheT(ctypes.Structure):
+    _fields_ = [("lat_codes", ctypes.c_void_p), ("lat_scales", ctypes.c_void_p),
+                ("idx_codes", ctypes.c_void_p), ("idx_scales", ctypes.c_void_p),
+                ("n_pages", ctypes.c_int32), ("block_table", ctypes.c_void_p),
+                ("max_pages", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise Csa2Error(f"{_LIB_PATH} is missing: run __graft_entry__.build() first")
+        L = ctypes.CDLL(_LIB_PATH)
+        P, I, I64, SZ, F = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
+        C = ctypes.POINTER(CacheT)
+        L.csa2_bytes_per_entry.restype = I
+        L.csa2_bytes_per_entry.argtypes = []
+        L.csa2_strerror.restype = ctypes.c_char_p
+        L.csa2_strerror.argtypes = [I]
+        L.csa2_workspace_size.restype = SZ
+        L.csa2_workspace_size.argtypes = [I, I, I, I64, I, I, I]
+        L.csa2_write_kv.restype = I
+        L.csa2_write_kv.argtypes = [C, I, P, I, P, P, P, I, P]
+        L.csa2_index_full.restype = I
+        L.csa2_index_full.argtypes = [C, I, P, I64, P, P, I, I, I, P, P, P, SZ, P]
+        L.csa2_reindex.restype = I
+        L.csa2_reindex.argtypes = [C, I, P, P, P, P, I, I, I, P, P, SZ, P]
+        L.csa2_sparse_decode.restype = I
+        L.csa2_sparse_decode.argtypes = [C, I, I, P, P, P, I, P, I, F, P, P, P, SZ, P]
+        L.csa2_prefill_chunk.restype = I
+        L.csa2_prefill_chunk.argtypes = [C, I, I, P, I64, I, P, P, P, P, I, I, F, P, P, P, SZ, P]
+        L.csa2_debug_gather.restype = I
+        L.csa2_debug_gather.argtypes = [C, I, P, I, P, P, P]
+        _lib = L
+    return _lib
+
+
+def _check(rc: int, what: str) -> None:
+    if rc != 0:
+        raise Csa2Error(f"{what}: {lib().csa2_strerror(rc).decode()} ({rc})")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _need(t: torch.Tensor, dtype, name: str, shape=None) -> None:
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _bf16(t: torch.Tensor, name: str, shape=None) -> None:
+    _need(t, torch.bfloat16, name, shape)
+
+
+class PagedCache:
+    """Device byte arrays of the paged FP4 cache plus its block table (see csa2.h)."""
+
+    def __init__(self, lat_codes, lat_scales, idx_codes, idx_scales, block_table):
+        self.lat_codes, self.lat_scales = lat_codes, lat_scales
+        self.idx_codes, self.idx_scales = idx_codes, idx_scales
+        self.block_table = block_table
+        for name in ("lat_codes", "lat_scales", "idx_codes", "idx_scales"):
+            _need(getattr(self, name), torch.uint8, name)
+        _need(block_table, torch.int32, "block_table")
+        self.n_pages = lat_codes.shape[0]
+        self.max_pages = block_table.shape[1]
+        self._struct = CacheT(lat_codes.data_ptr(), lat_scales.data_ptr(), idx_codes.data_ptr(),
+                              idx_scales.data_ptr(), self.n_pages, block_table.data_ptr(),
+                              self.max_pages)
+
+    @classmethod
+    def allocate(cls, n_pages: int, block_table: torch.Tensor, device="cuda", fill: int = 0):
+        mk = lambda *s: torch.full(s, fill, dtype=torch.uint8, device=device)
+        return cls(mk(n_pages, PAGE, D_LATENT // 2), mk(n_pages, PAGE, D_LATENT // 32),
+                   mk(n_pages, PAGE, D_INDEX // 2), mk(n_pages, PAGE, D_INDEX // 32),
+                   block_table.to(device=device, dtype=torch.int32).contiguous())
+
+    def clone(self) -> "PagedCache":
+        return PagedCache(self.lat_codes.clone(), self.lat_scales.clone(), self.idx_codes.clone(),
+                          self.idx_scales.clone(), self.block_table.clone())
+
+    @property
+    def ref(self):
+        return ctypes.byref(self._struct)
+
+    @property
+    def B(self) -> int:
+        return self.block_table.shape[0]
+
+
+def bytes_per_entry() -> int:
+    return lib().csa2_bytes_per_entry()
+
+
+def workspace_size(fn: int, B: int, H: int = 0, max_ctx: int = 0, topk: int = 512,
+                   pool_blocks: int = 0, C: int = 0) -> int:
+    return lib().csa2_workspace_size(fn, B, H, max_ctx, topk, pool_blocks, C)
+
+
+def workspace(fn: int, device="cuda", **kw) -> Optional[torch.Tensor]:
+    n = workspace_size(fn, **kw)
+    return torch.zeros(max(n, 1), dtype=torch.uint8, device=device) if n > 0 else None
+
+
+def write_kv(cache: PagedCache, start_tok: torch.Tensor, x: torch.Tensor, w: torch.Tensor,
+             k_idx: torch.Tensor, ratio: int = 2, stream=None) -> None:
+    B, T = x.shape[0], x.shape[1]
+    _bf16(x, "x", (B, T, D_LATENT))
+    _bf16(w, "w", (B, T, D_LATENT))
+    _bf16(k_idx, "k_idx", (B, T // 2, D_INDEX))
+    _need(start_tok, torch.int32, "start_tok", (B,))
+    _check(lib().csa2_write_kv(cache.ref, B, _ptr(start_tok), T, _ptr(x), _ptr(w), _ptr(k_idx), ratio,
+                               _stream(stream)), "csa2_write_kv")
+
+
+def index_full(cache: PagedCache, ctx_len: torch.Tensor, max_ctx: int, q_idx: torch.Tensor,
+               w_idx: torch.Tensor, topk: int = 512, pool_blocks: int = 0, cand_block: int = 8,
+               ws: Optional[torch.Tensor] = None, topk_idx: Optional[torch.Tensor] = None,
+               pool: Optional[torch.Tensor] = None, stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    B = ctx_len.shape[0]
+    _need(ctx_len, torch.int32, "ctx_len", (B,))
+    _bf16(q_idx, "q_idx", (B, H_INDEX, D_INDEX))
+    _bf16(w_idx, "w_idx", (B, H_INDEX))
+    dev = q_idx.device
+    if topk_idx is None:
+        topk_idx = torch.empty((B, topk), dtype=torch.int32, device=dev)
+    if pool_blocks > 0 and pool is None:
+        pool = torch.empty((B, pool_blocks), dtype=torch.int32, device=dev)
+    if ws is None:
+        ws = workspace(FN_INDEX_FULL, device=dev, B=B, max_ctx=max_ctx, topk=topk, pool_blocks=pool_blocks)
+    wsb = ws.numel() if ws is not None else 0
+    _check(lib().csa2_index_full(cache.ref, B, _ptr(ctx_len), max_ctx, _ptr(q_idx), _ptr(w_idx), topk,
+                                 pool_blocks, cand_block, _ptr(topk_idx), _ptr(pool), _ptr(ws), wsb,
+                                 _stream(stream)), "csa2_index_full")
+    return topk_idx, pool
+
+
+def reindex(cache: PagedCache, ctx_len: torch.Tensor, q_idx: torch.Tensor, w_idx: torch.Tensor,
+            pool: torch.Tensor, topk: int = 512, cand_block: int = 8,
+            topk_idx: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    B = ctx_len.shape[0]
+    _need(ctx_len, torch.int32, "ctx_len", (B,))
+    _bf16(q_idx, "q_idx", (B, H_INDEX, D_INDEX))
+    _bf16(w_idx, "w_idx", (B, H_INDEX))
+    _need(pool, torch.int32, "pool")
+    if topk_idx is None:
+        topk_idx = torch.empty((B, topk), dtype=torch.int32, device=q_idx.device)
+    _check(lib().csa2_reindex(cache.ref, B, _ptr(ctx_len), _ptr(q_idx), _ptr(w_idx), _ptr(pool),
+                              pool.shape[1], cand_block, topk, _ptr(topk_idx), None, 0, _stream(stream)),
+           "csa2_reindex")
+    return topk_idx
+
+
+def sparse_decode(cache: PagedCache, ctx_len: torch.Tensor, q: torch.Tensor, topk_idx: torch.Tensor,
+                  swa: torch.Tensor, sm_scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+                  lse: Optional[torch.Tensor] = None, want_lse: bool = True,
+                  ws: Optional[torch.Tensor] = None, stream=None):
+    B, H = q.shape[0], q.shape[1]
+    W = swa.shape[1]
+    _need(ctx_len, torch.int32, "ctx_len", (B,))
+    _bf16(q, "q", (B, H, D_LATENT))
+    _bf16(swa, "swa", (B, W, D_LATENT))
+    _need(topk_idx, torch.int32, "topk_idx")
+    topk = topk_idx.shape[1]
+    if sm_scale is None:
+        sm_scale = D_LATENT ** -0.5
+    if out is None:
+        out = torch.empty((B, H, D_LATENT), dtype=torch.bfloat16, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
+    if ws is None:
+        ws = workspace(FN_SPARSE_DECODE, device=q.device, B=B, H=H, topk=topk)
+    wsb = ws.numel() if ws is not None else 0
+    _check(lib().csa2_sparse_decode(cache.ref, B, H, _ptr(ctx_len), _ptr(q), _ptr(topk_idx), topk,
+                                    _ptr(swa), W, sm_scale, _ptr(out), _ptr(lse), _ptr(ws), wsb,
+                                    _stream(stream)), "csa2_sparse_decode")
+    return out, lse
+
+
+def prefill_chunk(cache: PagedCache, prior_len: torch.Tensor, max_ctx: int, q: torch.Tensor,
+                  q_idx: torch.Tensor, w_idx: torch.Tensor, local: torch.Tensor, topk: int = 512,
+                  sm_scale: Optional[float] = None, want_topk: bool = True,
+                  out: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None, stream=None):
+    B, C, H = q.shape[0], q.shape[1], q.shape[2]
+    W = local.shape[1] - C + 1
+    _need(prior_len, torch.int32, "prior_len", (B,))
+    _bf16(q, "q", (B, C, H, D_LATENT))
+    _bf16(q_idx, "q_idx", (B, C, H_INDEX, D_INDEX))
+    _bf16(w_idx, "w_idx", (B, C, H_INDEX))
+    _bf16(local, "local", (B, W - 1 + C, D_LATENT))
+    if sm_scale is None:
+        sm_scale = D_LATENT ** -0.5
+    if out is None:
+        out = torch.empty((B, C, H, D_LATENT), dtype=torch.bfloat16, device=q.device)
+    tk = torch.empty((B, C, topk), dtype=torch.int32, device=q.device) if want_topk else None
+    if ws is None:
+        ws = workspace(FN_PREFILL_CHUNK, device=q.device, B=B, H=H, max_ctx=max_ctx, topk=topk, C=C)
+    wsb = ws.numel() if ws is not None else 0
+    _check(lib().csa2_prefill_chunk(cache.ref, B, H, _ptr(prior_len), max_ctx, C, _ptr(q), _ptr(q_idx),
+                                    _ptr(w_idx), _ptr(local), W, topk, sm_scale, _ptr(out), _ptr(tk),
+                                    _ptr(ws), wsb, _stream(stream)), "csa2_prefill_chunk")
+    return out, tk
+
+
+def debug_gather(cache: PagedCache, idx: torch.Tensor, stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    B, n = idx.shape
+    _need(idx, torch.int32, "idx")
+    lat = torch.empty((B, n, D_LATENT), dtype=torch.float32, device=idx.device)
+    key = torch.empty((B, n, D_INDEX), dtype=torch.float32, device=idx.device)
+    _check(lib().csa2_debug_gather(cache.ref, B, _ptr(idx), n, _ptr(lat), _ptr(key), _stream(stream)),
+           "csa2_debug_gather")
+    return lat, key

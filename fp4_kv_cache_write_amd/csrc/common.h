@@ -1,0 +1,108 @@
+// Device helpers shared by the CSA2 kernels (gfx950 only).
+//
+// FP4 format (see csa2.h): e2m1 codes, two per byte with the even channel in the
+// low nibble, one e8m0 scale byte u per 32 channels standing for 2^(u-127).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "csa2.h"
+
+namespace csa2 {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+// Round fp32 to bf16, nearest with ties to even; NaN -> canonical quiet NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  uint32_t b = __float_as_uint(f);
+  if ((b & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
+  b += 0x7fffu + ((b >> 16) & 1u);
+  return b >> 16;
+}
+
+// Scale 2^(u-127) of an e8m0 byte as an fp32 multiplier (u = 0 is the subnormal 2^-127).
+__device__ __forceinline__ float e8m0_scale(uint32_t u) {
+  return __uint_as_float(u ? (u << 23) : 0x00400000u);
+}
+
+// Two e2m1 codes (byte SEL of `codes`: low nibble -> element 0) times `scale`, as bf16.
+// e2m1 * 2^k is exact in bf16 over the whole range the quantiser produces.
+template <int SEL>
+__device__ __forceinline__ uint32_t fp4x2_to_bf16x2(uint32_t codes, float scale) {
+  bf16x2 v = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, SEL);
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// Eight e2m1 codes (one dword, channels 8 apart in order) -> 8 bf16 packed as 4 dwords.
+__device__ __forceinline__ u32x4 fp4x8_to_bf16x8(uint32_t codes, float scale) {
+  u32x4 r;
+  r.x = fp4x2_to_bf16x2<0>(codes, scale);
+  r.y = fp4x2_to_bf16x2<1>(codes, scale);
+  r.z = fp4x2_to_bf16x2<2>(codes, scale);
+  r.w = fp4x2_to_bf16x2<3>(codes, scale);
+  return r;
+}
+
+// Order-preserving map of an fp32 score onto uint32 (larger score -> larger key).
+// -0 is folded onto +0 so that equal scores give equal keys.  Key 0 is reserved for
+// "no entry" (it would be a NaN pattern).
+__device__ __forceinline__ uint32_t score_key(float s) {
+  if (s == 0.0f) s = 0.0f;
+  uint32_t b = __float_as_uint(s);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+__device__ __forceinline__ float key_score(uint32_t k) {
+  uint32_t b = (k & 0x80000000u) ? (k & 0x7fffffffu) : ~k;
+  return __uint_as_float(b);
+}
+
+// Wave-wide reductions over 64 lanes.
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    uint32_t t = __shfl_up(v, o, kWave);
+    if (lane >= o) v += t;
+  }
+  return v;
+}
+
+// Page lookup with bounds checks: returns -1 for an absent or out-of-range page.
+__device__ __forceinline__ int page_of(const int32_t* __restrict__ block_table, int max_pages,
+                                       int n_pages, int b, int entry) {
+  int pi = entry >> 6;
+  if (entry < 0 || pi >= max_pages) return -1;
+  int p = block_table[(int64_t)b * max_pages + pi];
+  return (p >= 0 && p < n_pages) ? p : -1;
+}
+
+}  // namespace csa2

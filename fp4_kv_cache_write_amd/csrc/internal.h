@@ -1,0 +1,45 @@
+// Host-side launchers behind the C ABI (csa2.h).  Each returns a CSA2_* code.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "csa2.h"
+
+namespace csa2 {
+
+// Workspace layout of csa2_index_full, shared by the size query and the launcher.
+struct IndexFullPlan {
+  int chunk;          // entries scored by one workgroup (power of two, >= topk)
+  int n_chunks;       // chunks covering max_ctx/2 entries
+  int max_blocks;     // candidate blocks covering max_ctx/2 entries
+  size_t off_cand_key, off_cand_idx, off_cand_cnt, off_blockmax, total;
+};
+IndexFullPlan plan_index_full(int B, int64_t max_ctx, int topk, int pool_blocks, int cand_block);
+
+int launch_write_kv(const csa2_cache_t& c, int B, const int32_t* start_tok, int T_new,
+                    const uint16_t* x, const uint16_t* w, const uint16_t* k_idx, hipStream_t s);
+int launch_debug_gather(const csa2_cache_t& c, int B, const int32_t* idx, int n, float* out_lat,
+                        float* out_idx, hipStream_t s);
+int launch_index_full(const csa2_cache_t& c, int B, const int32_t* ctx_len, int64_t max_ctx,
+                      const uint16_t* q_idx, const uint16_t* w_idx, int topk, int pool_blocks,
+                      int cand_block, int32_t* topk_idx, int32_t* pool, void* ws, hipStream_t s);
+int launch_reindex(const csa2_cache_t& c, int B, const int32_t* ctx_len, const uint16_t* q_idx,
+                   const uint16_t* w_idx, const int32_t* pool, int pool_blocks, int cand_block,
+                   int topk, int32_t* topk_idx, hipStream_t s);
+size_t sparse_decode_ws(int B, int H, int topk);
+int launch_sparse_decode(const csa2_cache_t& c, int B, int H, const int32_t* ctx_len,
+                         const uint16_t* q, const int32_t* topk_idx, int topk, const uint16_t* swa,
+                         int W, float sm_scale, uint16_t* out, float* lse, void* ws, hipStream_t s);
+size_t prefill_ws(int B, int H, int64_t max_ctx, int topk, int C);
+int launch_prefill_chunk(const csa2_cache_t& c, int B, int H, const int32_t* prior_len,
+                         int64_t max_ctx, int C, const uint16_t* q, const uint16_t* q_idx,
+                         const uint16_t* w_idx, const uint16_t* local, int W, int topk,
+                         float sm_scale, uint16_t* out, int32_t* topk_idx, void* ws, hipStream_t s);
+
+inline int hip_status() {
+  return hipGetLastError() == hipSuccess ? CSA2_OK : CSA2_EHIP;
+}
+
+}  // namespace csa2

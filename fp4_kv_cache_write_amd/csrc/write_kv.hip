@@ -1,0 +1,183 @@
+// Write path: pairwise merge of two tokens into one entry, MXFP4 quantisation of the
+// 512-d latent and the 64-d indexer key, scatter into the paged cache.
+//
+// [P1] "DeepSeek-v4.1 Flash: KVキャッシュ圧縮の限界を押し広げる" §1.1 (the encoder
+// merges two adjacent positions with learned per-channel weights) and §2.3.1 (no
+// window overlap, no absolute position embedding; the indexer key is derived from
+// the entry).  FP4 block format and rounding: see csa2.h.
+//
+// One wavefront per entry.  Lane l owns channels 8l..8l+7: four 16-byte loads
+// (x and w of both tokens), one fused multiply-add per channel, an MX block of 32
+// channels spans 4 adjacent lanes (max via two lane swaps), and the lane stores one
+// dword of codes, so a wave writes the entry's 256 code bytes in one coalesced
+// store.  The kernel is HBM-bound: 4 KB read and 306 B written per entry.
+#include "common.h"
+#include "internal.h"
+
+namespace csa2 {
+namespace {
+
+// Quantise the lane's 8 values; the 32-value block is lanes 4q..4q+3.
+__device__ __forceinline__ void mx_quant8(const float (&y)[8], uint32_t& codes, uint32_t& u) {
+  float a = 0.0f;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) a = fmaxf(a, fabsf(y[k]));
+  a = fmaxf(a, __shfl_xor(a, 1, kWave));
+  a = fmaxf(a, __shfl_xor(a, 2, kWave));
+  // scale exponent e = floor(log2 a) - 2 clamped at -127  ->  byte u = e + 127
+  const uint32_t bexp = (__float_as_uint(a) >> 23) & 0xffu;
+  u = bexp > 2u ? bexp - 2u : 0u;
+  const float inv = __uint_as_float((254u - u) << 23);   // 2^-e, exact
+  const bool zero = (a == 0.0f);
+  codes = 0u;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const float v = fabsf(y[k]) * inv;                   // in [0, 8), exact
+    // nearest e2m1 magnitude, ties to the even code: 0.25->0 0.75->2 1.25->2
+    // 1.75->4 2.5->4 3.5->6 5->6, saturating at 6 (code 7)
+    uint32_t m = (uint32_t)(v > 0.25f) + (uint32_t)(v >= 0.75f) + (uint32_t)(v > 1.25f) +
+                 (uint32_t)(v >= 1.75f) + (uint32_t)(v > 2.5f) + (uint32_t)(v >= 3.5f) +
+                 (uint32_t)(v > 5.0f);
+    const uint32_t s = __float_as_uint(y[k]) >> 31;
+    const uint32_t c = zero ? 0u : (m | (s << 3));
+    codes |= c << (4 * k);
+  }
+}
+
+__device__ __forceinline__ float lo_bf16(uint32_t d) { return __uint_as_float(d << 16); }
+__device__ __forceinline__ float hi_bf16(uint32_t d) { return __uint_as_float(d & 0xffff0000u); }
+
+__global__ __launch_bounds__(256) void write_kv_kernel(
+    uint8_t* __restrict__ lat_codes, uint8_t* __restrict__ lat_scales,
+    uint8_t* __restrict__ idx_codes, uint8_t* __restrict__ idx_scales, int n_pages,
+    const int32_t* __restrict__ block_table, int max_pages, const int32_t* __restrict__ start_tok,
+    int half, int64_t total, const uint16_t* __restrict__ x, const uint16_t* __restrict__ w,
+    const uint16_t* __restrict__ k_idx) {
+  const int64_t e = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (e >= total) return;
+  const int lane = threadIdx.x & 63;
+  const int b = (int)(e / half);
+  const int i = (int)(e - (int64_t)b * half);
+  const int st = start_tok[b];
+  if (st < 0 || (st & 1)) return;                        // caller contract: even start
+  const int j = (st >> 1) + i;
+  const int page = page_of(block_table, max_pages, n_pages, b, j);
+  if (page < 0) return;
+  const int64_t row = (int64_t)page * CSA2_PAGE + (j & (CSA2_PAGE - 1));
+
+  // ---- latent: y = w0*x0 + w1*x1 with one rounding (w1*x1 is exact in fp32) ----
+  const int64_t tok0 = ((int64_t)b * 2 * half + 2 * i) * CSA2_D_LATENT + lane * 8;
+  const u32x4 xa = *reinterpret_cast<const u32x4*>(x + tok0);
+  const u32x4 xb = *reinterpret_cast<const u32x4*>(x + tok0 + CSA2_D_LATENT);
+  const u32x4 wa = *reinterpret_cast<const u32x4*>(w + tok0);
+  const u32x4 wb = *reinterpret_cast<const u32x4*>(w + tok0 + CSA2_D_LATENT);
+  float y[8];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    y[2 * q] = fmaf(lo_bf16(wa[q]), lo_bf16(xa[q]), lo_bf16(wb[q]) * lo_bf16(xb[q]));
+    y[2 * q + 1] = fmaf(hi_bf16(wa[q]), hi_bf16(xa[q]), hi_bf16(wb[q]) * hi_bf16(xb[q]));
+  }
+  uint32_t codes, u;
+  mx_quant8(y, codes, u);
+  *reinterpret_cast<uint32_t*>(lat_codes + row * CSA2_LAT_CODE_BYTES + lane * 4) = codes;
+  if ((lane & 3) == 0) lat_scales[row * CSA2_LAT_SCALE_BYTES + (lane >> 2)] = (uint8_t)u;
+
+  // ---- indexer key: lanes 0..7 own 8 channels each (two MX blocks) ----
+  float kv[8];
+  if (lane < 8) {
+    const u32x4 ka = *reinterpret_cast<const u32x4*>(
+        k_idx + ((int64_t)b * half + i) * CSA2_D_INDEX + lane * 8);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      kv[2 * q] = lo_bf16(ka[q]);
+      kv[2 * q + 1] = hi_bf16(ka[q]);
+    }
+  } else {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) kv[q] = 0.0f;
+  }
+  mx_quant8(kv, codes, u);
+  if (lane < 8) {
+    *reinterpret_cast<uint32_t*>(idx_codes + row * CSA2_IDX_CODE_BYTES + lane * 4) = codes;
+    if ((lane & 3) == 0) idx_scales[row * CSA2_IDX_SCALE_BYTES + (lane >> 2)] = (uint8_t)u;
+  }
+}
+
+// Dequantise entries through the page table with the kernels' own FP4 decode.
+__global__ __launch_bounds__(256) void debug_gather_kernel(
+    const uint8_t* __restrict__ lat_codes, const uint8_t* __restrict__ lat_scales,
+    const uint8_t* __restrict__ idx_codes, const uint8_t* __restrict__ idx_scales, int n_pages,
+    const int32_t* __restrict__ block_table, int max_pages, const int32_t* __restrict__ idx, int n,
+    int64_t total, float* __restrict__ out_lat, float* __restrict__ out_idx) {
+  const int64_t e = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (e >= total) return;
+  const int lane = threadIdx.x & 63;
+  const int b = (int)(e / n);
+  const int j = idx[e];
+  const int page = page_of(block_table, max_pages, n_pages, b, j);
+  const float nan = __uint_as_float(0x7fc00000u);
+  const int64_t row = (int64_t)page * CSA2_PAGE + (j & (CSA2_PAGE - 1));
+  if (out_lat) {
+    float* o = out_lat + e * CSA2_D_LATENT + lane * 8;
+    if (page < 0) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) o[k] = nan;
+    } else {
+      const uint32_t codes =
+          *reinterpret_cast<const uint32_t*>(lat_codes + row * CSA2_LAT_CODE_BYTES + lane * 4);
+      const float sc = e8m0_scale(lat_scales[row * CSA2_LAT_SCALE_BYTES + (lane >> 2)]);
+      const u32x4 v = fp4x8_to_bf16x8(codes, sc);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        o[2 * q] = lo_bf16(v[q]);
+        o[2 * q + 1] = hi_bf16(v[q]);
+      }
+    }
+  }
+  if (out_idx && lane < 8) {
+    float* o = out_idx + e * CSA2_D_INDEX + lane * 8;
+    if (page < 0) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) o[k] = nan;
+    } else {
+      const uint32_t codes =
+          *reinterpret_cast<const uint32_t*>(idx_codes + row * CSA2_IDX_CODE_BYTES + lane * 4);
+      const float sc = e8m0_scale(idx_scales[row * CSA2_IDX_SCALE_BYTES + (lane >> 2)]);
+      const u32x4 v = fp4x8_to_bf16x8(codes, sc);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        o[2 * q] = lo_bf16(v[q]);
+        o[2 * q + 1] = hi_bf16(v[q]);
+      }
+    }
+  }
+}
+
+}  // namespace
+
+int launch_write_kv(const csa2_cache_t& c, int B, const int32_t* start_tok, int T_new,
+                    const uint16_t* x, const uint16_t* w, const uint16_t* k_idx, hipStream_t s) {
+  const int half = T_new / 2;
+  const int64_t total = (int64_t)B * half;
+  if (total == 0) return CSA2_OK;
+  const int64_t grid = (total + 3) / 4;
+  if (grid > 0x7fffffff) return CSA2_EUNSUPPORTED;
+  hipLaunchKernelGGL(write_kv_kernel, dim3((unsigned)grid), dim3(256), 0, s, c.lat_codes,
+                     c.lat_scales, c.idx_codes, c.idx_scales, c.n_pages, c.block_table,
+                     c.max_pages, start_tok, half, total, x, w, k_idx);
+  return hip_status();
+}
+
+int launch_debug_gather(const csa2_cache_t& c, int B, const int32_t* idx, int n, float* out_lat,
+                        float* out_idx, hipStream_t s) {
+  const int64_t total = (int64_t)B * n;
+  if (total == 0) return CSA2_OK;
+  const int64_t grid = (total + 3) / 4;
+  if (grid > 0x7fffffff) return CSA2_EUNSUPPORTED;
+  hipLaunchKernelGGL(debug_gather_kernel, dim3((unsigned)grid), dim3(256), 0, s, c.lat_codes,
+                     c.lat_scales, c.idx_codes, c.idx_scales, c.n_pages, c.block_table,
+                     c.max_pages, idx, n, total, out_lat, out_idx);
+  return hip_status();
+}
+
+}  // namespace csa2

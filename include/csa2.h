@@ -1,0 +1,191 @@
+/*
+ * csa2.h — C ABI of libcsa2.so: CSA2 compressed-KV sparse decode on MI355X (gfx950).
+ *
+ * Sources (web pages on DeepSeek-V4.1 Flash and its CSA2 attention):
+ *   [P1] "DeepSeek-v4.1 Flash: KVキャッシュ圧縮の限界を押し広げる" (hackernews.jp
+ *        translation of zartbot's walk-through of the tech report)
+ *   [P2] ai.freelance-job.com news summary of that walk-through
+ *   [P3] "DeepSeek V4.1 Flash architecture: making a giant AI faster through reuse"
+ *        (yasmorita.com)
+ *
+ * Conventions for every entry point
+ *   - Pointers marked (device) point to GPU memory; everything else is host memory.
+ *     The caller allocates and frees all memory: cache pages, tables, inputs, outputs
+ *     and workspace.  The library allocates nothing and keeps no mutable global state.
+ *   - bf16 values travel as uint16_t bit patterns.
+ *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL = default
+ *     stream).  A return of CSA2_OK means the launch was accepted; results are ready
+ *     once the stream is synchronised.
+ *   - Return codes: CSA2_OK (0) or a negative CSA2_E* code.  Only host-visible
+ *     arguments are validated, and nothing is enqueued when validation fails.  Device
+ *     arrays are read defensively: an entry index outside [0, visible entries), a page
+ *     id outside [0, n_pages) or a context beyond the cache table is treated as an
+ *     absent row, never dereferenced.
+ *   - Token positions: a decode query for a context of L tokens sits at position
+ *     t = L - 1; entry j merges tokens 2j and 2j+1 and is visible to t iff 2j+1 <= t
+ *     ([P3], causal-mask section), so floor(L/2) entries are visible.
+ */
+#ifndef CSA2_H
+#define CSA2_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Fixed shapes.  512-d shared latent ([P1] §1.1, [P2] spec table); 64-d indexer
+ * key and 4 indexer heads (the pages leave them blank); e2m1 codes with one e8m0
+ * scale byte per 32 channels (the pages only say FP4 plus magnitude data, [P3]);
+ * 64 entries per page ([P3], memory is taken in fixed blocks). */
+#define CSA2_D_LATENT 512
+#define CSA2_D_INDEX 64
+#define CSA2_H_INDEX 4
+#define CSA2_MX_BLOCK 32
+#define CSA2_PAGE 64
+#define CSA2_LAT_CODE_BYTES 256   /* per entry */
+#define CSA2_LAT_SCALE_BYTES 16
+#define CSA2_IDX_CODE_BYTES 32
+#define CSA2_IDX_SCALE_BYTES 2
+#define CSA2_MAX_TOPK 2048
+#define CSA2_MAX_WINDOW 1024
+
+enum {
+  CSA2_OK = 0,
+  CSA2_EINVAL = -1,       /* null pointer, bad size, odd token count, ... */
+  CSA2_EWORKSPACE = -2,   /* workspace missing or smaller than csa2_workspace_size() */
+  CSA2_EUNSUPPORTED = -3, /* a valid request this build does not implement */
+  CSA2_EHIP = -4          /* the HIP runtime refused a launch */
+};
+
+/* Workspace-sized functions (argument `fn` of csa2_workspace_size). */
+enum {
+  CSA2_FN_INDEX_FULL = 1,
+  CSA2_FN_REINDEX = 2,
+  CSA2_FN_SPARSE_DECODE = 3,
+  CSA2_FN_PREFILL_CHUNK = 4
+};
+
+/* Paged cache of merged entries.  Entry j of sequence b lives in slot j % 64 of
+ * page block_table[b * max_pages + j / 64].  Per entry:
+ *   lat_codes  [n_pages][64][256]  512 e2m1 codes, channel 2i in the low nibble
+ *   lat_scales [n_pages][64][16]   e8m0 scale byte of channels 32k..32k+31
+ *   idx_codes  [n_pages][64][32]   64 e2m1 indexer-key codes
+ *   idx_scales [n_pages][64][2]
+ * A code c stands for (-1)^(c>>3) * {0, .5, 1, 1.5, 2, 3, 4, 6}[c & 7] and a scale
+ * byte u for 2^(u-127).  All pointers (device); the struct itself is host memory. */
+typedef struct csa2_cache_t {
+  uint8_t *lat_codes;
+  uint8_t *lat_scales;
+  uint8_t *idx_codes;
+  uint8_t *idx_scales;
+  int32_t n_pages;
+  const int32_t *block_table; /* [B][max_pages] int32 (device) */
+  int32_t max_pages;
+} csa2_cache_t;
+
+/* Bytes one merged entry occupies: 272 latent + 34 indexer = 306. */
+int csa2_bytes_per_entry(void);
+
+/* Static description of a return code. */
+const char *csa2_strerror(int code);
+
+/* Workspace bytes `fn` needs for these sizes (0 if none).  max_ctx bounds every
+ * ctx_len / prior_len + C (tokens); pool_blocks is the Full layer's pool quota. */
+size_t csa2_workspace_size(int fn, int B, int H, int64_t max_ctx, int topk, int pool_blocks, int C);
+
+/* csa2_write_kv — encoder write path ([P1] §1.1 sequence dimension, §2.3.1
+ * compressor): merge token pairs with per-channel weights, quantise to FP4, store.
+ *   For each sequence b and i < T_new/2, entry j = start_tok[b]/2 + i is
+ *     y_c = fp32_rne(w[b][2i][c] * x[b][2i][c] + w[b][2i+1][c] * x[b][2i+1][c])
+ *   (exact products and sum, one rounding; no normalisation), then every block of
+ *   32 channels is quantised: scale exponent e = clamp(floor(log2 max|y|) - 2,
+ *   -127, 127), code = nearest e2m1 value of |y|/2^e with ties to the even code,
+ *   saturating at 6, sign bit = sign of y; an all-zero block stores scale 0 and +0
+ *   codes.  The indexer key k_idx[b][i] (64 bf16; its projection from the entry is a
+ *   trained weight the caller applies, [P1] §2.3.1) is quantised the same way.
+ *   x, w: [B][T_new][512] bf16 (device); k_idx: [B][T_new/2][64] bf16 (device);
+ *   start_tok: [B] int32 (device), even.  T_new must be even (> 0); an unpaired last
+ *   token is the caller's to resubmit with the next one.  ratio must be 2 (the
+ *   decoder's ratio 1 is not built: CSA2_EUNSUPPORTED).  The table must already hold
+ *   pages for every written entry. */
+int csa2_write_kv(const csa2_cache_t *cache, int B, const int32_t *start_tok, int T_new,
+                  const uint16_t *x, const uint16_t *w, const uint16_t *k_idx, int ratio,
+                  void *stream);
+
+/* csa2_index_full — Full-mode indexer ([P1] §2.3.2 Full mode, §2.3.4 HSI).
+ *   For every sequence b with n = floor(ctx_len[b]/2) visible entries:
+ *     s_j = sum_{h<4} w_idx[b][h] * max(0, q_idx[b][h] . k_j)   (k_j dequantised)
+ *   topk_idx[b] = the min(topk, n) entries with the largest s (ties: lower j), in
+ *   ascending j order, padded with -1.  If pool_blocks > 0: block maxima over blocks
+ *   of cand_block entries (last block padded with -inf), the block holding entry n-1
+ *   forced to +inf, the best min(pool_blocks, #blocks) blocks (ties: lower block id)
+ *   written to pool[b] in ascending order, padded with -1.
+ *   ctx_len: [B] int32 tokens (device), each <= max_ctx; q_idx: [B][4][64] bf16;
+ *   w_idx: [B][4] bf16; topk_idx: [B][topk] int32; pool: [B][pool_blocks] int32 or
+ *   NULL when pool_blocks == 0 (all device).  1 <= topk <= 2048; cand_block in
+ *   {1,2,4,8,16,32}; max_ctx/2 <= 64 * max_pages.  ws: csa2_workspace_size(
+ *   CSA2_FN_INDEX_FULL, B, 0, max_ctx, topk, pool_blocks, 0) bytes (device). */
+int csa2_index_full(const csa2_cache_t *cache, int B, const int32_t *ctx_len, int64_t max_ctx,
+                    const uint16_t *q_idx, const uint16_t *w_idx, int topk, int pool_blocks,
+                    int cand_block, int32_t *topk_idx, int32_t *pool, void *ws, size_t ws_bytes,
+                    void *stream);
+
+/* csa2_reindex — Reindex mode ([P1] §2.3.2 Reindex mode, §2.3.4: later indexers
+ *   score only the candidate pool).  Scores, with this layer's q_idx / w_idx, the
+ *   visible entries j < floor(ctx_len[b]/2) of the blocks listed in pool[b] (block
+ *   ids, -1 entries ignored, each block covering cand_block entries), and writes the
+ *   min(topk, pool size) best (ties: lower j) to topk_idx[b] in ascending order,
+ *   padded with -1.  Shapes as in csa2_index_full; pool_blocks * cand_block <= 16384.
+ *   ws: csa2_workspace_size(CSA2_FN_REINDEX, ...) bytes (0 in this build; ws may be
+ *   NULL). */
+int csa2_reindex(const csa2_cache_t *cache, int B, const int32_t *ctx_len, const uint16_t *q_idx,
+                 const uint16_t *w_idx, const int32_t *pool, int pool_blocks, int cand_block,
+                 int topk, int32_t *topk_idx, void *ws, size_t ws_bytes, void *stream);
+
+/* csa2_sparse_decode — one CSA2 attention for one decode query per sequence
+ *   ([P1] §2.3.1: each query attends to the selected entries and the layer's window
+ *   KV together; [P3]: scores -> weights summing to 1 -> weighted sum of values).
+ *   Rows R = dequantised latent of every valid topk_idx[b][i] (valid: 0 <= j <
+ *   floor(ctx_len[b]/2)) followed by the window rows of positions max(0, t-W+1)..t,
+ *   t = ctx_len[b]-1, taken from swa[b][pos % W].  For every head h:
+ *     z_r = sm_scale * q[b][h] . R_r,  p = softmax(z),  out[b][h] = sum_r p_r R_r
+ *   (K = V = the 512-d latent), rounded to bf16; lse[b][h] = log sum_r exp(z_r).
+ *   Reuse mode ([P1] §2.3.2) is this call with an earlier layer's topk_idx.
+ *   q: [B][H][512] bf16; topk_idx: [B][topk] int32; swa: [B][W][512] bf16;
+ *   out: [B][H][512] bf16; lse: [B][H] float or NULL (all device).  H a multiple of
+ *   16; 1 <= W <= 1024; 0 <= topk <= 2048.  ws: csa2_workspace_size(
+ *   CSA2_FN_SPARSE_DECODE, B, H, 0, topk, 0, 0) bytes. */
+int csa2_sparse_decode(const csa2_cache_t *cache, int B, int H, const int32_t *ctx_len,
+                       const uint16_t *q, const int32_t *topk_idx, int topk, const uint16_t *swa,
+                       int W, float sm_scale, uint16_t *out, float *lse, void *ws, size_t ws_bytes,
+                       void *stream);
+
+/* csa2_prefill_chunk — chunked prefill after csa2_write_kv stored the chunk.
+ *   For sequence b and chunk query i (position t = prior_len[b] + i): Full-mode
+ *   indexer over the floor((t+1)/2) entries visible to t, top-K as in
+ *   csa2_index_full, then the attention of csa2_sparse_decode with window rows for
+ *   positions max(0, t-W+1)..t taken from local[b][pos - prior_len[b] + W - 1].
+ *   q: [B][C][H][512]; q_idx: [B][C][4][64]; w_idx: [B][C][4]; local: [B][W-1+C][512]
+ *   (bf16, device); out: [B][C][H][512] bf16; topk_idx: [B][C][topk] int32 or NULL.
+ *   prior_len: [B] int32 (device), prior_len[b] + C <= max_ctx.
+ *   ws: csa2_workspace_size(CSA2_FN_PREFILL_CHUNK, B, H, max_ctx, topk, 0, C). */
+int csa2_prefill_chunk(const csa2_cache_t *cache, int B, int H, const int32_t *prior_len,
+                       int64_t max_ctx, int C, const uint16_t *q, const uint16_t *q_idx,
+                       const uint16_t *w_idx, const uint16_t *local, int W, int topk,
+                       float sm_scale, uint16_t *out, int32_t *topk_idx, void *ws,
+                       size_t ws_bytes, void *stream);
+
+/* csa2_debug_gather — test hook: dequantise entries through the page table with the
+ *   same FP4 decode the kernels use.  idx: [B][n] int32 entry ids (device);
+ *   out_lat: [B][n][512] float, out_idx: [B][n][64] float (device; either may be
+ *   NULL).  An id < 0 or a page id outside [0, n_pages) yields NaN rows. */
+int csa2_debug_gather(const csa2_cache_t *cache, int B, const int32_t *idx, int n, float *out_lat,
+                      float *out_idx, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CSA2_H */

@@ -1,0 +1,57 @@
+"""Test-side glue between synth inputs, the oracle and the HIP binding."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from oracle import OracleCache
+
+
+def bits(t: torch.Tensor) -> np.ndarray:
+    """bf16 tensor -> numpy uint16 bit patterns (on the host)."""
+    assert t.dtype == torch.bfloat16
+    return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def gpu_available() -> bool:
+    return torch.cuda.is_available()
+
+
+def oracle_cache_for(case, recipe: str = "l2", seqs=None) -> OracleCache:
+    """Oracle cache holding the pre-built part of every sequence of a DecodeCase."""
+    oc = OracleCache(case.n_pages, case.block_table.numpy())
+    for b in (range(case.B) if seqs is None else seqs):
+        if case.prebuilt[b] == 0:
+            continue
+        x, w, k = case.seq_tokens(b, recipe)
+        oc.write(b, 0, bits(x), bits(w), bits(k))
+    return oc
+
+
+def gpu_cache_for(case, recipe: str = "l2", device="cuda"):
+    """PagedCache filled by csa2_write_kv with the same pre-built tokens, one sequence at a time."""
+    import fp4_kv_cache_write_amd as fk
+    cache = fk.PagedCache.allocate(case.n_pages, case.block_table, device=device)
+    full = torch.from_numpy(np.ascontiguousarray(case.block_table.numpy()))
+    for b in range(case.B):
+        T = case.prebuilt[b]
+        if T == 0:
+            continue
+        x, w, k = case.seq_tokens(b, recipe)
+        sub = fk.PagedCache(cache.lat_codes, cache.lat_scales, cache.idx_codes, cache.idx_scales,
+                            full[b:b + 1].to(device))
+        start = torch.zeros(1, dtype=torch.int32, device=device)
+        fk.write_kv(sub, start, x.to(device)[None].contiguous(), w.to(device)[None].contiguous(),
+                    k.to(device)[None].contiguous())
+    torch.cuda.synchronize()
+    return cache
+
+
+def cache_bytes_equal(gc, oc) -> dict:
+    """Per-field equality of the GPU cache bytes and the oracle's."""
+    res = {}
+    for name in ("lat_codes", "lat_scales", "idx_codes", "idx_scales"):
+        g = getattr(gc, name).cpu().numpy()
+        o = getattr(oc, name)
+        res[name] = int((g != o).sum())
+    return res

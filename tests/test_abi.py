@@ -1,0 +1,84 @@
+"""The C-ABI library loads, exports what include/csa2.h declares, and rejects bad
+host arguments before any launch (CPU only: no compute call reaches the GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import fp4_kv_cache_write_amd as fk
+from fp4_kv_cache_write_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    src = open(os.path.join(ROOT, "include", "csa2.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(csa2_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_function():
+    L = fk.lib()
+    names = _declared_functions()
+    assert len(names) >= 9
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(binding.EXPORTS) == set(names)
+
+
+def test_constants_and_strerror():
+    assert fk.bytes_per_entry() == 306
+    L = fk.lib()
+    for code in (0, -1, -2, -3, -4):
+        assert L.csa2_strerror(code)
+    assert L.csa2_strerror(-99) == b"unknown error"
+
+
+def test_workspace_sizes_are_consistent():
+    a = fk.workspace_size(fk.FN_INDEX_FULL, B=32, max_ctx=65536, topk=512, pool_blocks=512)
+    b = fk.workspace_size(fk.FN_INDEX_FULL, B=32, max_ctx=65536, topk=512, pool_blocks=0)
+    assert a > 0 and b > 0 and a >= b
+    assert fk.workspace_size(fk.FN_INDEX_FULL, B=0, max_ctx=100) == 0
+    assert fk.workspace_size(99, B=1) == 0
+
+
+def _fake_cache(max_pages=4):
+    # Non-null host addresses: validation must reject the call before anything
+    # dereferences them or launches a kernel.
+    buf = (ctypes.c_uint8 * 64)()
+    addr = ctypes.addressof(buf)
+    return binding.CacheT(addr, addr, addr, addr, 4, addr, max_pages), buf
+
+
+def test_host_argument_errors_return_before_launch():
+    L = fk.lib()
+    c, keep = _fake_cache()
+    p = ctypes.c_void_p(ctypes.addressof(keep))
+    ref = ctypes.byref(c)
+    EINVAL, EWS, EUNS = -1, -2, -3
+    assert L.csa2_write_kv(None, 1, p, 2, p, p, p, 2, None) == EINVAL
+    assert L.csa2_write_kv(ref, 1, p, 3, p, p, p, 2, None) == EINVAL        # odd token count
+    assert L.csa2_write_kv(ref, 1, p, 0, p, p, p, 2, None) == EINVAL
+    assert L.csa2_write_kv(ref, 1, p, 2, p, p, p, 1, None) == EUNS         # ratio 1 not built
+    assert L.csa2_write_kv(ref, 1, None, 2, p, p, p, 2, None) == EINVAL
+    assert L.csa2_index_full(ref, 1, p, 128, p, p, 0, 0, 8, p, None, None, 0, None) == EINVAL  # topk 0
+    assert L.csa2_index_full(ref, 1, p, 128, p, p, 4096, 0, 8, p, None, None, 0, None) == EINVAL
+    assert L.csa2_index_full(ref, 1, p, 128, p, p, 16, 4, 8, p, None, None, 0, None) == EINVAL  # pool NULL
+    assert L.csa2_index_full(ref, 1, p, 128, p, p, 16, 0, 3, p, None, None, 0, None) == EINVAL  # block 3
+    assert L.csa2_index_full(ref, 1, p, 10 ** 6, p, p, 16, 0, 8, p, None, None, 0, None) == EINVAL  # table too short
+    assert L.csa2_index_full(ref, 1, p, 128, p, p, 16, 0, 8, p, None, None, 0, None) == EWS
+    assert L.csa2_reindex(ref, 1, p, p, p, p, 0, 8, 16, p, None, 0, None) == EINVAL
+    assert L.csa2_reindex(ref, 1, p, p, p, p, 4096, 8, 16, p, None, 0, None) == EUNS
+    assert L.csa2_sparse_decode(ref, 1, 12, p, p, p, 16, p, 128, 0.1, p, None, None, 0, None) == EINVAL
+    assert L.csa2_sparse_decode(ref, 1, 16, p, p, p, 16, p, 0, 0.1, p, None, None, 0, None) == EINVAL
+    assert L.csa2_sparse_decode(ref, 1, 16, p, p, None, 16, p, 128, 0.1, p, None, None, 0, None) == EINVAL
+    assert L.csa2_prefill_chunk(ref, 1, 16, p, 128, 0, p, p, p, p, 128, 16, 0.1, p, None, None, 0, None) == EINVAL
+    assert L.csa2_debug_gather(ref, 1, p, 4, None, None, None) == EINVAL
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(binding, "_lib", None)
+    monkeypatch.setattr(binding, "_LIB_PATH", str(tmp_path / "nope.so"))
+    with pytest.raises(binding.Csa2Error):
+        binding.lib()
