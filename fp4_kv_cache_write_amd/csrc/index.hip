@@ -309,6 +309,21 @@ __global__ __launch_bounds__(kReindexThreads) void reindex_kernel(ReindexArgs a)
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// Kernels here take up to ~150 KB of dynamic LDS (gfx950 has 160 KB per CU); raise
+// each kernel's limit once per process.
+bool lds_limits_set() {
+  static const bool ok = [] {
+    bool r = hipFuncSetAttribute(reinterpret_cast<const void*>(index_scan_kernel),
+                                 hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) == hipSuccess;
+    r = r && hipFuncSetAttribute(reinterpret_cast<const void*>(index_merge_kernel),
+                                 hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) == hipSuccess;
+    r = r && hipFuncSetAttribute(reinterpret_cast<const void*>(reindex_kernel),
+                                 hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) == hipSuccess;
+    return r;
+  }();
+  return ok;
+}
+
 }  // namespace
 
 IndexFullPlan plan_index_full(int B, int64_t max_ctx, int topk, int pool_blocks, int cand_block) {
@@ -349,6 +364,7 @@ int launch_index_full(const csa2_cache_t& c, int B, const int32_t* ctx_len, int6
   const IndexFullPlan p = plan_index_full(B, max_ctx, topk, pool_blocks, cand_block);
   if (p.chunk == 0) return CSA2_EUNSUPPORTED;
   if (pool_blocks > 0 && (max_ctx / 2 + cand_block - 1) / cand_block > kMergeCap) return CSA2_EUNSUPPORTED;
+  if (!lds_limits_set()) return CSA2_EHIP;
   uint8_t* w = static_cast<uint8_t*>(ws);
   ScanArgs sa;
   sa.idx_codes = c.idx_codes;
@@ -401,6 +417,7 @@ int launch_reindex(const csa2_cache_t& c, int B, const int32_t* ctx_len, const u
                    const uint16_t* w_idx, const int32_t* pool, int pool_blocks, int cand_block,
                    int topk, int32_t* topk_idx, hipStream_t s) {
   if ((int64_t)pool_blocks * cand_block > kReindexCap) return CSA2_EUNSUPPORTED;
+  if (!lds_limits_set()) return CSA2_EHIP;
   ReindexArgs ra;
   ra.idx_codes = c.idx_codes;
   ra.idx_scales = c.idx_scales;

@@ -55,3 +55,31 @@ def cache_bytes_equal(gc, oc) -> dict:
         o = getattr(oc, name)
         res[name] = int((g != o).sum())
     return res
+
+
+def check_topk_set(gpu_ids, domain, scores, k: int, tol: float = 1e-3) -> dict:
+    """Compare a GPU top-K against the oracle's scores over `domain` (entry ids).
+
+    The sets must agree except for entries whose oracle score is within `tol` of
+    the K-th largest score; sizes must agree; GPU ids must be distinct members of
+    the domain, ascending, and padded with -1.
+    """
+    g = np.asarray(gpu_ids)
+    valid = g[g >= 0]
+    assert np.all(g[len(valid):] == -1), "padding must follow the ids"
+    assert np.all(np.diff(valid) > 0), "ids must be ascending and distinct"
+    domain = np.asarray(domain)
+    s = dict(zip(domain.tolist(), np.asarray(scores).tolist()))
+    assert set(valid.tolist()) <= set(s), "id outside the visible domain"
+    n_sel = min(k, len(domain))
+    assert len(valid) == n_sel, (len(valid), n_sel)
+    order = np.lexsort((domain, -np.asarray(scores)))
+    want = set(domain[order[:n_sel]].tolist())
+    diff = want.symmetric_difference(set(valid.tolist()))
+    if n_sel == len(domain):
+        assert not diff
+        return {"diff": 0}
+    s_k = float(np.asarray(scores)[order[n_sel - 1]])
+    far = [j for j in diff if abs(s[j] - s_k) > tol]
+    assert not far, f"{len(far)} entries differ beyond {tol} of the K-th score {s_k}: {far[:5]}"
+    return {"diff": len(diff)}

@@ -1,0 +1,113 @@
+"""GPU parity of the Full indexer (top-K + HSI pool) and Reindex against the oracle."""
+import numpy as np
+import pytest
+import torch
+
+from oracle.indexer import full_layer, hsi_pool, index_scores, pool_positions, reindex_layer
+from synth import make_decode_case, small_decode
+from tests.helpers import bits, check_topk_set, gpu_cache_for, oracle_cache_for
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def fk():
+    import fp4_kv_cache_write_amd as m
+    m.lib()
+    return m
+
+
+def _check_pool(gpu_pool, s, n_vis, cb, nb, tol=1e-3):
+    g = np.asarray(gpu_pool)
+    valid = g[g >= 0]
+    assert np.all(g[len(valid):] == -1) and np.all(np.diff(valid) > 0)
+    want, _ = hsi_pool(s, n_vis, cb, nb)
+    assert len(valid) == len(want)
+    if n_vis == 0:
+        return
+    latest = (n_vis - 1) // cb
+    assert latest in valid.tolist()
+    pad = (-n_vis) % cb
+    bmax = np.concatenate([s, np.full(pad, -np.inf)]).reshape(-1, cb).max(axis=1)
+    bmax[latest] = np.inf
+    diff = set(want.tolist()).symmetric_difference(valid.tolist())
+    if diff:
+        order = np.lexsort((np.arange(len(bmax)), -bmax))
+        edge = bmax[order[len(want) - 1]]
+        far = [k for k in diff if abs(bmax[k] - edge) > tol]
+        assert not far, far
+
+
+CASES = [
+    # (ctx per sequence, topk, pool_blocks, cand_block, pages)
+    ((2048,), 512, 256, 8, "identity"),                                   # config-0 shape
+    ((0, 2, 14, 1022, 1024, 1026, 8192, 8194, 20000), 512, 40, 8, "random"),  # ragged tails
+    ((9000, 30000), 64, 100, 4, "fragmented"),
+    ((65536, 3000), 512, 512, 8, "random"),                               # config-1 length
+    ((5000,), 2048, 300, 16, "identity"),
+    ((16390,), 100, 5, 1, "random"),
+]
+
+
+@pytest.mark.parametrize("ctx,topk,pool_blocks,cb,pages", CASES)
+def test_index_full_matches_oracle(fk, ctx, topk, pool_blocks, cb, pages):
+    cfg = small_decode(1, B=len(ctx), ctx=ctx, pages=pages, heavy_frac=0.05, append=0,
+                       layers=small_decode(1, B=1, ctx=(2,)).layers)
+    case = make_decode_case(cfg, "cpu")
+    oc = oracle_cache_for(case)
+    gc = gpu_cache_for(case)
+    L = case.layer(0)
+    ctx_len = torch.tensor(case.ctx_len, dtype=torch.int32, device="cuda")
+    max_ctx = max(case.ctx_len)
+    tk, pool = fk.index_full(gc, ctx_len, max_ctx, L["q_idx"].cuda(), L["w_idx"].cuda(), topk=topk,
+                             pool_blocks=pool_blocks, cand_block=cb)
+    torch.cuda.synchronize()
+    tk, pool = tk.cpu().numpy(), pool.cpu().numpy()
+    stats = []
+    for b in range(case.B):
+        n_vis = case.n_vis[b]
+        keys = oc.index_keys(b, np.arange(n_vis))
+        s = index_scores(bits(L["q_idx"][b]), bits(L["w_idx"][b]), keys)
+        stats.append(check_topk_set(tk[b], np.arange(n_vis), s, topk)["diff"])
+        _check_pool(pool[b], s, n_vis, cb, pool_blocks)
+    print("near-tie differences per sequence:", stats)
+
+
+def test_index_full_without_pool_and_repeatable(fk):
+    cfg = small_decode(2, B=3, ctx=(40000, 1000, 77778), pages="random", append=0)
+    case = make_decode_case(cfg, "cpu")
+    oc = oracle_cache_for(case)
+    gc = gpu_cache_for(case)
+    L = case.layer(0)
+    ctx_len = torch.tensor(case.ctx_len, dtype=torch.int32, device="cuda")
+    outs = [fk.index_full(gc, ctx_len, max(case.ctx_len), L["q_idx"].cuda(), L["w_idx"].cuda(),
+                          topk=512)[0].cpu() for _ in range(3)]
+    assert all(torch.equal(outs[0], o) for o in outs[1:])
+    for b in range(case.B):
+        n_vis = case.n_vis[b]
+        s = index_scores(bits(L["q_idx"][b]), bits(L["w_idx"][b]), oc.index_keys(b, np.arange(n_vis)))
+        check_topk_set(outs[0][b].numpy(), np.arange(n_vis), s, 512)
+
+
+@pytest.mark.parametrize("ctx,pool_blocks,cb,topk", [((65536, 9000, 300), 512, 8, 512),
+                                                     ((20000,), 100, 4, 64), ((778,), 200, 8, 512)])
+def test_reindex_matches_oracle_on_oracle_pool(fk, ctx, pool_blocks, cb, topk):
+    cfg = small_decode(1, B=len(ctx), ctx=ctx, pages="random", heavy_frac=0.05, append=0)
+    case = make_decode_case(cfg, "cpu")
+    oc = oracle_cache_for(case)
+    gc = gpu_cache_for(case)
+    L0, L1 = case.layer(0), case.layer(1)
+    pools = np.full((case.B, pool_blocks), -1, np.int32)
+    for b in range(case.B):
+        _, blocks, _ = full_layer(oc, b, case.n_vis[b], bits(L0["q_idx"][b]), bits(L0["w_idx"][b]), topk,
+                                  pool_blocks, cb)
+        pools[b, :len(blocks)] = blocks
+    ctx_len = torch.tensor(case.ctx_len, dtype=torch.int32, device="cuda")
+    tk = fk.reindex(gc, ctx_len, L1["q_idx"].cuda(), L1["w_idx"].cuda(), torch.from_numpy(pools).cuda(),
+                    topk=topk, cand_block=cb)
+    torch.cuda.synchronize()
+    tk = tk.cpu().numpy()
+    for b in range(case.B):
+        pos = pool_positions(pools[b][pools[b] >= 0], case.n_vis[b], cb)
+        s = index_scores(bits(L1["q_idx"][b]), bits(L1["w_idx"][b]), oc.index_keys(b, pos))
+        check_topk_set(tk[b], pos, s, topk)
