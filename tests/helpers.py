@@ -83,3 +83,20 @@ def check_topk_set(gpu_ids, domain, scores, k: int, tol: float = 1e-3) -> dict:
     far = [j for j in diff if abs(s[j] - s_k) > tol]
     assert not far, f"{len(far)} entries differ beyond {tol} of the K-th score {s_k}: {far[:5]}"
     return {"diff": len(diff)}
+
+
+def check_attention_rows(o_gpu_bits, o_ref, tol: float = 2e-3) -> float:
+    """Per output row (one head): max_d (|o_gpu - o_ref| - 2^-8 |o_gpu|)_+ <= tol * max_d |o_ref|.
+
+    o_gpu_bits: bf16 bit patterns [..., 512]; o_ref: float64 [..., 512].  The
+    2^-8 |o_gpu| term is the bf16 rounding of the output; what remains is the
+    fp32-accumulation error the bar limits.  Returns the worst ratio seen.
+    """
+    from oracle import bf16_bits_to_f64
+    og = bf16_bits_to_f64(o_gpu_bits)
+    err = np.maximum(np.abs(og - o_ref) - 2.0 ** -8 * np.abs(og), 0.0).max(axis=-1)
+    ref = np.abs(o_ref).max(axis=-1)
+    ratio = err / np.maximum(ref, 1e-300)
+    worst = float(ratio.max())
+    assert np.all(err <= tol * ref), f"worst ratio {worst:.3e} > {tol}"
+    return worst

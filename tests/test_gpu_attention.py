@@ -1,0 +1,112 @@
+"""GPU parity of csa2_sparse_decode against the oracle, with the oracle's own index
+sets as the shared input (the index sets themselves are checked in test_gpu_index)."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import bf16_bits_to_f64, sparse_attention
+from oracle.attention import gather_rows
+from oracle.indexer import full_layer
+from synth import make_decode_case, small_decode
+from tests.helpers import bits, check_attention_rows, gpu_cache_for, oracle_cache_for
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def fk():
+    import fp4_kv_cache_write_amd as m
+    m.lib()
+    return m
+
+
+def _oracle_topk(case, oc, layer, topk):
+    out = np.full((case.B, topk), -1, np.int32)
+    for b in range(case.B):
+        t, _, _ = full_layer(oc, b, case.n_vis[b], bits(layer["q_idx"][b]), bits(layer["w_idx"][b]), topk)
+        out[b, :len(t)] = t
+    return out
+
+
+@pytest.mark.parametrize("ctx,H,topk,W", [
+    ((2048,), 16, 512, 128),                    # config-0 shape
+    ((65536, 300, 4000, 100), 64, 512, 128),    # config-1 length, short contexts, ragged tiles
+    ((9000, 18), 32, 100, 37),                  # ragged top-K and window
+    ((5000,), 16, 2048, 128),
+])
+def test_sparse_decode_matches_oracle(fk, ctx, H, topk, W):
+    cfg = small_decode(1, B=len(ctx), ctx=ctx, H=H, pages="random", heavy_frac=0.05, append=0,
+                       topk=topk, window=W)
+    case = make_decode_case(cfg, "cpu")
+    oc = oracle_cache_for(case)
+    gc = gpu_cache_for(case)
+    L = case.layer(0)
+    tk = _oracle_topk(case, oc, L, topk)
+    ctx_len = torch.tensor(case.ctx_len, dtype=torch.int32, device="cuda")
+    out, lse = fk.sparse_decode(gc, ctx_len, L["q"].cuda(), torch.from_numpy(tk).cuda(), L["swa"].cuda())
+    torch.cuda.synchronize()
+    out_b, lse = bits(out.cpu()), lse.cpu().numpy()
+    worst = 0.0
+    for b in range(case.B):
+        t = case.ctx_len[b] - 1
+        rows = gather_rows(oc, b, tk[b], bits(L["swa"][b]), t, W)
+        o_ref, lse_ref = sparse_attention(bits(L["q"][b]), rows, 1 / math.sqrt(512))
+        worst = max(worst, check_attention_rows(out_b[b], o_ref))
+        assert np.allclose(lse[b], lse_ref, rtol=0, atol=1e-4), np.abs(lse[b] - lse_ref).max()
+    print(f"worst error / (2e-3 bar): {worst / 2e-3:.3f}")
+
+
+def test_reuse_reads_only_selected_and_ignores_bad_ids(fk):
+    cfg = small_decode(1, B=2, ctx=(12000, 3000), H=16, pages="random", append=0)
+    case = make_decode_case(cfg, "cpu")
+    oc = oracle_cache_for(case)
+    gc = gpu_cache_for(case)
+    L = case.layer(2)
+    tk = _oracle_topk(case, oc, case.layer(0), 512)
+    ctx_len = torch.tensor(case.ctx_len, dtype=torch.int32, device="cuda")
+    q, swa = L["q"].cuda(), L["swa"].cuda()
+    out1, lse1 = fk.sparse_decode(gc, ctx_len, q, torch.from_numpy(tk).cuda(), swa)
+    # poison every non-selected entry (scale byte 254) and add ids that must be ignored
+    poisoned = gc.clone()
+    bt = case.block_table.numpy()
+    for b in range(case.B):
+        keep = np.zeros(case.n_vis[b], bool)
+        keep[tk[b][tk[b] >= 0]] = True
+        js = np.nonzero(~keep)[0]
+        pages = torch.from_numpy(bt[b, js // 64].astype(np.int64)).cuda()
+        slots = torch.from_numpy((js % 64).astype(np.int64)).cuda()
+        poisoned.lat_scales[pages, slots] = 254
+    tk_bad = tk.copy()
+    tk_bad[0, -3:] = [-1, 10 ** 8, case.n_vis[0]]          # absent, beyond the table, not visible
+    out2, lse2 = fk.sparse_decode(poisoned, ctx_len, q, torch.from_numpy(tk).cuda(), swa)
+    torch.cuda.synchronize()
+    assert torch.equal(out1, out2) and torch.equal(lse1, lse2)
+    # the bad ids behave exactly like dropping those three rows
+    tk_drop = tk.copy()
+    tk_drop[0, -3:] = -1
+    o3, _ = fk.sparse_decode(gc, ctx_len, q, torch.from_numpy(tk_bad).cuda(), swa)
+    o4, _ = fk.sparse_decode(gc, ctx_len, q, torch.from_numpy(tk_drop).cuda(), swa)
+    torch.cuda.synchronize()
+    assert torch.equal(o3, o4)
+
+
+def test_window_only_and_single_row(fk):
+    cfg = small_decode(1, B=3, ctx=(2, 4, 600), H=16, pages="identity", append=0, window=128)
+    case = make_decode_case(cfg, "cpu")
+    oc = oracle_cache_for(case)
+    gc = gpu_cache_for(case)
+    L = case.layer(0)
+    ctx_len = torch.tensor(case.ctx_len, dtype=torch.int32, device="cuda")
+    tk = torch.full((case.B, 0), -1, dtype=torch.int32, device="cuda")
+    out, lse = fk.sparse_decode(gc, ctx_len, L["q"].cuda(), tk, L["swa"].cuda())
+    torch.cuda.synchronize()
+    out_b = bits(out.cpu())
+    for b in range(case.B):
+        t = case.ctx_len[b] - 1
+        rows = gather_rows(oc, b, np.zeros(0, np.int64), bits(L["swa"][b]), t, 128)
+        o_ref, lse_ref = sparse_attention(bits(L["q"][b]), rows, 1 / math.sqrt(512))
+        check_attention_rows(out_b[b], o_ref)
+    # ctx 2 -> t = 1: two window rows; ctx 1 impossible (even), so check the row count
+    assert gather_rows(oc, 0, np.zeros(0, np.int64), bits(L["swa"][0]), 1, 128).shape[0] == 2
