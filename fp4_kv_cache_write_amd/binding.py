@@ -12,7 +12,8 @@ from typing import Optional, Tuple
 
 import torch
 
-_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libcsa2.so")
+# CSA2_LIB may name another build of the same library (same ABI).
+_LIB_PATH = os.environ.get("CSA2_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libcsa2.so")
 
 D_LATENT, D_INDEX, H_INDEX, PAGE = 512, 64, 4, 64
 FN_INDEX_FULL, FN_REINDEX, FN_SPARSE_DECODE, FN_PREFILL_CHUNK = 1, 2, 3, 4

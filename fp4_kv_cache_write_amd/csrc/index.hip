@@ -25,14 +25,14 @@
 namespace csa2 {
 namespace {
 
-constexpr int kScanThreads = 256;
-constexpr int kScanR = 8;            // histogram replicas in the scan kernel
+constexpr int kScanThreads = 512;
+constexpr int kScanRound = 16;       // groups of 16 entries a wave loads before scoring them (4 pages)
 constexpr int kMergeThreads = 1024;
-constexpr int kMergeR = 16;
-constexpr int kMergeCap = 32768;     // keys the merge / pool workgroup holds in LDS
+constexpr int kMergeCap = 32768;     // keys the merge / pool workgroup selects from
+constexpr int kMergeKpt = kMergeCap / kMergeThreads;
 constexpr int kReindexThreads = 512;
-constexpr int kReindexR = 16;
 constexpr int kReindexCap = 16384;
+constexpr int kReindexKpt = kReindexCap / kReindexThreads;
 
 __device__ __forceinline__ int n_visible_entries(const int32_t* ctx_len, int b, int64_t max_ctx) {
   int64_t L = ctx_len[b];
@@ -88,30 +88,34 @@ struct ScanArgs {
   int64_t max_ctx;
   const uint16_t* q_idx;
   const uint16_t* w_idx;
-  int topk, chunk, n_chunks, cand_block, want_blocks, max_blocks;
+  int topk, n_chunks, cand_block, want_blocks, max_blocks;
   uint32_t* cand_key;
   int32_t* cand_idx;
   int32_t* cand_cnt;
   uint32_t* block_max;
 };
 
+template <int CHUNK>
 __global__ __launch_bounds__(kScanThreads) void index_scan_kernel(ScanArgs a) {
+  constexpr int KPT = CHUNK / kScanThreads;
+  constexpr int GPW = CHUNK / 16 / (kScanThreads / 64);   // groups per wave
   extern __shared__ uint32_t smem[];
-  uint32_t* keys = smem;                          // [chunk]
-  uint32_t* hist = smem + a.chunk;                // [256 * R]
-  uint32_t* misc = hist + 256 * kScanR;           // [512]
+  uint32_t* keys = smem;                          // [CHUNK]
+  uint32_t* hist = smem + CHUNK;                  // [kSelectHist]
+  uint32_t* scratch = hist + kSelectHist;         // [kSelectScratch]
   const int b = blockIdx.x / a.n_chunks;
   const int c = blockIdx.x - b * a.n_chunks;
   const int n_vis = n_visible_entries(a.ctx_len, b, a.max_ctx);
-  const int e0 = c * a.chunk;
+  const int e0 = c * CHUNK;
   const int64_t slot = (int64_t)b * a.n_chunks + c;
   if (e0 >= n_vis) {
     if (threadIdx.x == 0) a.cand_cnt[slot] = 0;
     return;
   }
-  const int n_in = min(a.chunk, n_vis - e0);
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  const int n_grp = (n_in + 15) >> 4;
+  const int n_in = min(CHUNK, n_vis - e0);
+  const int lane = threadIdx.x & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
+  const int n = lane & 15, g = lane >> 4;
 
   bf16x8 a0, a1;
   load_q_frags(a.q_idx, b, a0, a1);
@@ -119,36 +123,43 @@ __global__ __launch_bounds__(kScanThreads) void index_scan_kernel(ScanArgs a) {
 #pragma unroll
   for (int h = 0; h < 4; ++h) wh[h] = bf16_to_f32(a.w_idx[b * CSA2_H_INDEX + h]);
 
-  const int n = lane & 15, g = lane >> 4;
-  // Each wave scores groups wid, wid+4, ...; four groups per step keep 4 loads in flight.
-  constexpr int U = 4;
-  for (int gb = wid * U; gb < n_grp; gb += 4 * U) {
-    u32x2 cd[U];
-    uint32_t sb[U];
+  // Wave w streams groups [w*GPW, (w+1)*GPW) of 16 entries.  A round covers 4
+  // pages: their ids are fetched first with scalar loads, then all code and scale
+  // loads of the round are issued before the first one is consumed.
+  const int32_t* bt = a.block_table + (int64_t)b * a.max_pages;
+  for (int r0 = 0; r0 < GPW; r0 += kScanRound) {
+    const int eb0 = e0 + (wid * GPW + r0) * 16;               // wave-uniform round start
+    int pg[kScanRound / 4];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int grp = gb + u;
-      const int e = e0 + grp * 16 + n;           // this lane's entry
+    for (int q = 0; q < kScanRound / 4; ++q) {
+      const int pi = (eb0 >> 6) + q;
+      int p = (eb0 + 64 * q < n_vis && pi < a.max_pages) ? bt[pi] : -1;
+      pg[q] = (p >= 0 && p < a.n_pages) ? p : -1;
+    }
+    u32x2 cd[kScanRound];
+    uint32_t sb[kScanRound];
+#pragma unroll
+    for (int u = 0; u < kScanRound; ++u) {
+      const int e = eb0 + u * 16 + n;
+      const int page = pg[u >> 2];
       cd[u] = u32x2{0u, 0u};
       sb[u] = 0u;
-      if (grp < n_grp && e < n_vis) {
-        const int page = page_of(a.block_table, a.max_pages, a.n_pages, b, e);
-        if (page >= 0) {
-          const int64_t row = (int64_t)page * CSA2_PAGE + (e & (CSA2_PAGE - 1));
-          cd[u] = *reinterpret_cast<const u32x2*>(a.idx_codes + row * CSA2_IDX_CODE_BYTES + 8 * g);
-          sb[u] = a.idx_scales[row * CSA2_IDX_SCALE_BYTES + (g >> 1)];
-        }
+      if (page >= 0 && e < n_vis) {
+        const int64_t row = (int64_t)page * CSA2_PAGE + (e & (CSA2_PAGE - 1));
+        cd[u] = *reinterpret_cast<const u32x2*>(a.idx_codes + row * CSA2_IDX_CODE_BYTES + 8 * g);
+        sb[u] = a.idx_scales[row * CSA2_IDX_SCALE_BYTES + (g >> 1)];
       }
     }
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int grp = gb + u;
-      if (grp >= n_grp) break;                    // wave-uniform
+    for (int u = 0; u < kScanRound; ++u) {
+      const int le = (wid * GPW + r0 + u) * 16;
+      if (e0 + le >= n_vis) break;                        // wave-uniform
       const float s = score16(cd[u], sb[u], a0, a1, wh);
-      const int le = grp * 16 + n;
-      if (lane < 16) keys[le] = (le < n_in) ? score_key(s) : 0u;
+      if (lane < 16) keys[le + n] = (le + n < n_in) ? score_key(s) : 0u;
     }
   }
+  // tail of a partial chunk: keys of absent entries are 0
+  for (int i = ((n_in + 15) & ~15) + threadIdx.x; i < CHUNK; i += kScanThreads) keys[i] = 0u;
   __syncthreads();
 
   // HSI block maxima of this chunk (as keys): block k covers entries k*cb .. +cb-1.
@@ -164,12 +175,22 @@ __global__ __launch_bounds__(kScanThreads) void index_scan_kernel(ScanArgs a) {
     }
   }
 
-  const SelectResult sr = block_select<kScanThreads, kScanR>(keys, n_in, a.topk, SelectSmem{hist, misc});
+  uint32_t kr[KPT];
+#pragma unroll
+  for (int i = 0; i < KPT; i += 4) {
+    const u32x4 v = *reinterpret_cast<const u32x4*>(keys + threadIdx.x * KPT + i);
+    kr[i] = v.x;
+    kr[i + 1] = v.y;
+    kr[i + 2] = v.z;
+    kr[i + 3] = v.w;
+  }
+  const SelectResult sr = block_select<kScanThreads, KPT>(kr, a.topk, hist, scratch);
   uint32_t* ck = a.cand_key + slot * a.topk;
   int32_t* ci = a.cand_idx + slot * a.topk;
-  block_emit_ordered<kScanThreads>(keys, n_in, sr, misc + 256 + 8, [&](int v, uint32_t pos) {
-    ck[pos] = keys[v];
-    ci[pos] = e0 + v;
+  const int p0 = threadIdx.x * KPT;
+  block_emit<kScanThreads, KPT>(kr, sr, scratch, [&](int i, uint32_t pos) {
+    ck[pos] = kr[i];
+    ci[pos] = e0 + p0 + i;
   });
   if (threadIdx.x == 0) a.cand_cnt[slot] = (int32_t)sr.count;
 }
@@ -188,41 +209,50 @@ struct MergeArgs {
 
 // blockIdx.y == 0: top-K over the chunk candidates; == 1: HSI pool over block maxima.
 __global__ __launch_bounds__(kMergeThreads) void index_merge_kernel(MergeArgs a) {
-  extern __shared__ uint32_t smem[];
-  uint32_t* keys = smem;                          // [kMergeCap]
-  uint32_t* hist = smem + kMergeCap;              // [256 * R]
-  uint32_t* misc = hist + 256 * kMergeR;          // [512]
+  __shared__ uint32_t hist[kSelectHist];
+  __shared__ uint32_t scratch[kSelectScratch];
   const int b = blockIdx.x;
   const int n_vis = n_visible_entries(a.ctx_len, b, a.max_ctx);
   const int tid = threadIdx.x;
+  const int p0 = tid * kMergeKpt;
+  uint32_t kr[kMergeKpt];
   if (blockIdx.y == 0) {
+    // virtual position v = chunk * topk + i, in entry order
     const int nc = (n_vis + a.chunk - 1) / a.chunk;
-    const int N = nc * a.topk;                    // virtual slot v = chunk * topk + i
-    for (int v = tid; v < N; v += kMergeThreads) {
-      const int cch = v / a.topk, i = v - cch * a.topk;
-      const int64_t slot = (int64_t)b * a.n_chunks + cch;
-      keys[v] = (i < a.cand_cnt[slot]) ? a.cand_key[slot * a.topk + i] : 0u;
+    const int N = nc * a.topk;
+    // slot v = chunk * topk + j, walked incrementally from this thread's first slot
+    const int c0 = p0 / a.topk, j0 = p0 - c0 * a.topk;
+    const uint32_t* ckey = a.cand_key + (int64_t)b * a.n_chunks * a.topk;
+    {
+      int cch = c0, j = j0;
+      int cnt = (p0 < N) ? a.cand_cnt[(int64_t)b * a.n_chunks + cch] : 0;
+#pragma unroll
+      for (int i = 0; i < kMergeKpt; ++i) {
+        kr[i] = (p0 + i < N && j < cnt) ? ckey[p0 + i] : 0u;
+        if (++j == a.topk) {
+          j = 0;
+          ++cch;
+          cnt = (p0 + i + 1 < N) ? a.cand_cnt[(int64_t)b * a.n_chunks + cch] : 0;
+        }
+      }
     }
-    __syncthreads();
-    const SelectResult sr = block_select<kMergeThreads, kMergeR>(keys, N, a.topk, SelectSmem{hist, misc});
+    const SelectResult sr = block_select<kMergeThreads, kMergeKpt>(kr, a.topk, hist, scratch);
     int32_t* out = a.topk_idx + (int64_t)b * a.topk;
-    block_emit_ordered<kMergeThreads>(keys, N, sr, misc + 256 + 8, [&](int v, uint32_t pos) {
-      const int cch = v / a.topk, i = v - cch * a.topk;
-      out[pos] = a.cand_idx[((int64_t)b * a.n_chunks + cch) * a.topk + i];
-    });
+    const int32_t* cidx = a.cand_idx + (int64_t)b * a.n_chunks * a.topk;
+    block_emit<kMergeThreads, kMergeKpt>(kr, sr, scratch, [&](int i, uint32_t pos) { out[pos] = cidx[p0 + i]; });
     for (int p = (int)sr.count + tid; p < a.topk; p += kMergeThreads) out[p] = -1;
   } else {
     const int cb = a.cand_block;
     const int nb = (n_vis + cb - 1) / cb;
     const uint32_t* bm = a.block_max + (int64_t)b * a.max_blocks;
-    for (int v = tid; v < nb; v += kMergeThreads) keys[v] = bm[v];
-    __syncthreads();
-    if (tid == 0 && nb > 0) keys[nb - 1] = 0xffffffffu;   // newest visible block: +inf
-    __syncthreads();
-    const SelectResult sr = block_select<kMergeThreads, kMergeR>(keys, nb, a.pool_blocks, SelectSmem{hist, misc});
+#pragma unroll
+    for (int i = 0; i < kMergeKpt; ++i) {
+      const int v = p0 + i;
+      kr[i] = v < nb ? (v == nb - 1 ? 0xffffffffu : bm[v]) : 0u;   // newest visible block: +inf
+    }
+    const SelectResult sr = block_select<kMergeThreads, kMergeKpt>(kr, a.pool_blocks, hist, scratch);
     int32_t* out = a.pool + (int64_t)b * a.pool_blocks;
-    block_emit_ordered<kMergeThreads>(keys, nb, sr, misc + 256 + 8,
-                                      [&](int v, uint32_t pos) { out[pos] = v; });
+    block_emit<kMergeThreads, kMergeKpt>(kr, sr, scratch, [&](int i, uint32_t pos) { out[pos] = p0 + i; });
     for (int p = (int)sr.count + tid; p < a.pool_blocks; p += kMergeThreads) out[p] = -1;
   }
 }
@@ -244,9 +274,9 @@ struct ReindexArgs {
 // pool[p]*cb + i), keep the top-K.  The pool is ascending, so slot order is entry order.
 __global__ __launch_bounds__(kReindexThreads) void reindex_kernel(ReindexArgs a) {
   extern __shared__ uint32_t smem[];
-  uint32_t* keys = smem;                          // [pool_blocks * cb]
+  uint32_t* keys = smem;                          // [kReindexCap]
   uint32_t* hist = smem + kReindexCap;
-  uint32_t* misc = hist + 256 * kReindexR;
+  uint32_t* scratch = hist + kSelectHist;
   const int b = blockIdx.x;
   int64_t L = a.ctx_len[b];
   if (L < 0) L = 0;
@@ -262,46 +292,69 @@ __global__ __launch_bounds__(kReindexThreads) void reindex_kernel(ReindexArgs a)
 #pragma unroll
   for (int h = 0; h < 4; ++h) wh[h] = bf16_to_f32(a.w_idx[b * CSA2_H_INDEX + h]);
   const int32_t* pool = a.pool + (int64_t)b * a.pool_blocks;
+  // Resolve every pool slot to its cache row (or -1) first, into the key array.
+  int32_t* rowid = reinterpret_cast<int32_t*>(keys);
+  for (int v = threadIdx.x; v < N; v += kReindexThreads) {
+    const int blk = pool[v / cb];
+    const int64_t e = (int64_t)blk * cb + (v % cb);
+    int32_t rid = -1;
+    if (blk >= 0 && e < n_vis) {
+      const int page = page_of(a.block_table, a.max_pages, a.n_pages, b, (int)e);
+      if (page >= 0) rid = page * CSA2_PAGE + (int)(e & (CSA2_PAGE - 1));
+    }
+    rowid[v] = rid;
+  }
+  __syncthreads();
   const int n_grp = (N + 15) >> 4;
-  constexpr int U = 4;
-  for (int gb = wid * U; gb < n_grp; gb += NW * U) {
-    u32x2 cd[U];
-    uint32_t sb[U];
-    bool ok[U];
+  const int wv = __builtin_amdgcn_readfirstlane(wid);
+  const int gpw = (n_grp + NW - 1) / NW;
+  const int g0 = wv * gpw, g1 = min(n_grp, g0 + gpw);
+  for (int r0 = g0; r0 < g1; r0 += kScanRound) {
+    u32x2 cd[kScanRound];
+    uint32_t sb[kScanRound];
+    int32_t rid[kScanRound];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int v = (gb + u) * 16 + n;
-      cd[u] = u32x2{0u, 0u};
-      sb[u] = 0u;
-      ok[u] = false;
-      if (v < N) {
-        const int blk = pool[v / cb];
-        const int64_t e = (int64_t)blk * cb + (v % cb);
-        if (blk >= 0 && e < n_vis) {
-          const int page = page_of(a.block_table, a.max_pages, a.n_pages, b, (int)e);
-          if (page >= 0) {
-            const int64_t row = (int64_t)page * CSA2_PAGE + (e & (CSA2_PAGE - 1));
-            cd[u] = *reinterpret_cast<const u32x2*>(a.idx_codes + row * CSA2_IDX_CODE_BYTES + 8 * g);
-            sb[u] = a.idx_scales[row * CSA2_IDX_SCALE_BYTES + (g >> 1)];
-            ok[u] = true;
-          }
-        }
-      }
+    for (int u = 0; u < kScanRound; ++u) {
+      const int v = (r0 + u) * 16 + n;
+      rid[u] = (r0 + u < g1 && v < N) ? rowid[v] : -1;
     }
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int grp = gb + u;
-      if (grp >= n_grp) break;
+    for (int u = 0; u < kScanRound; ++u) {
+      cd[u] = u32x2{0u, 0u};
+      sb[u] = 0u;
+      if (rid[u] >= 0) {
+        cd[u] = *reinterpret_cast<const u32x2*>(a.idx_codes + (int64_t)rid[u] * CSA2_IDX_CODE_BYTES + 8 * g);
+        sb[u] = a.idx_scales[(int64_t)rid[u] * CSA2_IDX_SCALE_BYTES + (g >> 1)];
+      }
+    }
+    // slot v's row id and key share a word; both are touched only by this wave,
+    // in program order, so the read above precedes the write below
+#pragma unroll
+    for (int u = 0; u < kScanRound; ++u) {
+      if (r0 + u >= g1) break;                    // wave-uniform
       const float s = score16(cd[u], sb[u], a0, a1, wh);
-      // entry validity lives in the lane that loaded it (lane n + 16*g); lanes 0..15 hold g = 0
-      const int v = grp * 16 + n;
-      if (lane < 16 && v < N) keys[v] = ok[u] ? score_key(s) : 0u;
+      const int v = (r0 + u) * 16 + n;
+      // validity lives in the lane that loaded the entry; lanes 0..15 hold g = 0
+      if (lane < 16 && v < N) keys[v] = rid[u] >= 0 ? score_key(s) : 0u;
     }
   }
   __syncthreads();
-  const SelectResult sr = block_select<kReindexThreads, kReindexR>(keys, N, a.topk, SelectSmem{hist, misc});
+  for (int i = N + threadIdx.x; i < kReindexCap; i += kReindexThreads) keys[i] = 0u;
+  __syncthreads();
+  uint32_t kr[kReindexKpt];
+  const int p0 = threadIdx.x * kReindexKpt;
+#pragma unroll
+  for (int i = 0; i < kReindexKpt; i += 4) {
+    const u32x4 v = *reinterpret_cast<const u32x4*>(keys + p0 + i);
+    kr[i] = v.x;
+    kr[i + 1] = v.y;
+    kr[i + 2] = v.z;
+    kr[i + 3] = v.w;
+  }
+  const SelectResult sr = block_select<kReindexThreads, kReindexKpt>(kr, a.topk, hist, scratch);
   int32_t* out = a.topk_idx + (int64_t)b * a.topk;
-  block_emit_ordered<kReindexThreads>(keys, N, sr, misc + 256 + 8, [&](int v, uint32_t pos) {
+  block_emit<kReindexThreads, kReindexKpt>(kr, sr, scratch, [&](int i, uint32_t pos) {
+    const int v = p0 + i;
     out[pos] = pool[v / cb] * cb + (v % cb);
   });
   for (int p = (int)sr.count + threadIdx.x; p < a.topk; p += kReindexThreads) out[p] = -1;
@@ -309,16 +362,17 @@ __global__ __launch_bounds__(kReindexThreads) void reindex_kernel(ReindexArgs a)
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// Kernels here take up to ~150 KB of dynamic LDS (gfx950 has 160 KB per CU); raise
+// Kernels here take up to ~80 KB of dynamic LDS (gfx950 has 160 KB per CU); raise
 // each kernel's limit once per process.
 bool lds_limits_set() {
   static const bool ok = [] {
-    bool r = hipFuncSetAttribute(reinterpret_cast<const void*>(index_scan_kernel),
-                                 hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) == hipSuccess;
-    r = r && hipFuncSetAttribute(reinterpret_cast<const void*>(index_merge_kernel),
-                                 hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) == hipSuccess;
-    r = r && hipFuncSetAttribute(reinterpret_cast<const void*>(reindex_kernel),
-                                 hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) == hipSuccess;
+    const void* ks[] = {reinterpret_cast<const void*>(index_scan_kernel<4096>),
+                        reinterpret_cast<const void*>(index_scan_kernel<8192>),
+                        reinterpret_cast<const void*>(index_scan_kernel<16384>),
+                        reinterpret_cast<const void*>(reindex_kernel)};
+    bool r = true;
+    for (const void* k : ks)
+      r = r && hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) == hipSuccess;
     return r;
   }();
   return ok;
@@ -377,7 +431,6 @@ int launch_index_full(const csa2_cache_t& c, int B, const int32_t* ctx_len, int6
   sa.q_idx = q_idx;
   sa.w_idx = w_idx;
   sa.topk = topk;
-  sa.chunk = p.chunk;
   sa.n_chunks = p.n_chunks;
   sa.cand_block = cand_block;
   sa.want_blocks = pool_blocks > 0;
@@ -386,10 +439,15 @@ int launch_index_full(const csa2_cache_t& c, int B, const int32_t* ctx_len, int6
   sa.cand_idx = reinterpret_cast<int32_t*>(w + p.off_cand_idx);
   sa.cand_cnt = reinterpret_cast<int32_t*>(w + p.off_cand_cnt);
   sa.block_max = reinterpret_cast<uint32_t*>(w + p.off_blockmax);
-  const size_t scan_lds = (size_t)(p.chunk + 256 * kScanR + 512) * 4;
+  const size_t scan_lds = (size_t)(p.chunk + kSelectHist + kSelectScratch) * 4;
   const int64_t grid = (int64_t)B * p.n_chunks;
   if (grid > 0x7fffffff) return CSA2_EUNSUPPORTED;
-  hipLaunchKernelGGL(index_scan_kernel, dim3((unsigned)grid), dim3(kScanThreads), scan_lds, s, sa);
+  if (p.chunk == 4096)
+    hipLaunchKernelGGL(index_scan_kernel<4096>, dim3((unsigned)grid), dim3(kScanThreads), scan_lds, s, sa);
+  else if (p.chunk == 8192)
+    hipLaunchKernelGGL(index_scan_kernel<8192>, dim3((unsigned)grid), dim3(kScanThreads), scan_lds, s, sa);
+  else
+    hipLaunchKernelGGL(index_scan_kernel<16384>, dim3((unsigned)grid), dim3(kScanThreads), scan_lds, s, sa);
   if (hip_status() != CSA2_OK) return CSA2_EHIP;
 
   MergeArgs ma;
@@ -407,9 +465,7 @@ int launch_index_full(const csa2_cache_t& c, int B, const int32_t* ctx_len, int6
   ma.block_max = sa.block_max;
   ma.topk_idx = topk_idx;
   ma.pool = pool;
-  const size_t merge_lds = (size_t)(kMergeCap + 256 * kMergeR + 512) * 4;
-  hipLaunchKernelGGL(index_merge_kernel, dim3(B, pool_blocks > 0 ? 2 : 1), dim3(kMergeThreads),
-                     merge_lds, s, ma);
+  hipLaunchKernelGGL(index_merge_kernel, dim3(B, pool_blocks > 0 ? 2 : 1), dim3(kMergeThreads), 0, s, ma);
   return hip_status();
 }
 
@@ -432,7 +488,7 @@ int launch_reindex(const csa2_cache_t& c, int B, const int32_t* ctx_len, const u
   ra.cand_block = cand_block;
   ra.topk = topk;
   ra.topk_idx = topk_idx;
-  const size_t lds = (size_t)(kReindexCap + 256 * kReindexR + 512) * 4;
+  const size_t lds = (size_t)(kReindexCap + kSelectHist + kSelectScratch) * 4;
   hipLaunchKernelGGL(reindex_kernel, dim3(B), dim3(kReindexThreads), lds, s, ra);
   return hip_status();
 }

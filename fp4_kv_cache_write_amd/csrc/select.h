@@ -1,167 +1,152 @@
-// Exact workgroup-level top-K over uint32 keys held in LDS.
+// Exact workgroup-level top-K over uint32 keys held in registers.
 //
 // Keys are order-preserving images of fp32 scores (score_key); key 0 marks "no
-// entry".  The K largest keys are found by an MSB-first radix select (8-bit
-// digits, histogram in LDS replicated R ways to spread atomics), which yields a
-// threshold key T and the number k_eq of keys equal to T that still belong to the
-// top K.  Selected items are then emitted in ascending position order: every key
-// above T, and among keys equal to T the k_eq with the lowest positions -- the
-// "larger score first, lower index on ties" order of the indexer top-K and the HSI
-// block ranking ([P1] §2.3.4, ties unspecified there; lower index is this
-// library's rule).
+// entry".  Thread t holds the keys of positions t*KPT .. t*KPT+KPT-1 (blocked
+// layout).  The K largest keys are found by an MSB-first radix select with
+// 11/11/10-bit digits; the first digit covers the sign, the exponent and two
+// mantissa bits, so even a narrow score range spreads over dozens of histogram
+// bins.  The select yields a threshold key T and the number k_eq of keys equal to
+// T that still belong to the top K.  Selected positions are then emitted in
+// ascending order: every key above T, and among keys equal to T the k_eq lowest
+// positions -- the "larger score first, lower index on ties" order of the
+// indexer top-K and the HSI block ranking ([P1] §2.3.4; the pages leave ties open,
+// lower index is this library's rule).
 #pragma once
 
 #include "common.h"
 
 namespace csa2 {
 
-struct SelectSmem {
-  uint32_t* hist;   // [256 * R]
-  uint32_t* misc;   // [512]: bin totals, results, per-wave round counts
-};
+// LDS the select needs: two histogram buffers + scratch [64 + 8].  A buffer holds
+// 2048 bins with one pad word after every 32 (bin d lives at d + d/32), so the
+// search wave -- lane l reading bins 32l..32l+31 -- touches 64 distinct banks.
+constexpr int kHistStride = 2048 + 64;
+constexpr int kSelectHist = 2 * kHistStride;
+constexpr int kSelectScratch = 72;
 
-// Result: selected entries satisfy key > thr, or key == thr and rank among equal
-// keys (in position order) < krem.  `count` is the number selected (min(K, #valid)).
+// Selected: key > thr, or key == thr among the first krem equal keys (position
+// order).  count = min(K, #valid).
 struct SelectResult {
   uint32_t thr;
   uint32_t krem;
   uint32_t count;
 };
 
+// Exclusive scan over the block in thread order; *total gets the block sum.
 template <int NT>
-__device__ __forceinline__ uint32_t block_sum_u32(uint32_t v, uint32_t* scratch) {
+__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* scratch, uint32_t* total) {
   constexpr int NW = NT / 64;
-  v = wave_sum_u32(v);
-  const int wid = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const uint32_t inc = wave_incl_scan(v);
+  if (lane == 63) scratch[wid] = inc;
   __syncthreads();
-  if ((threadIdx.x & 63) == 0) scratch[wid] = v;
-  __syncthreads();
-  uint32_t t = 0;
+  uint32_t before = 0, tot = 0;
 #pragma unroll
-  for (int i = 0; i < NW; ++i) t += scratch[i];
+  for (int w = 0; w < NW; ++w) {
+    const uint32_t s = scratch[w];
+    before += (w < wid) ? s : 0u;
+    tot += s;
+  }
   __syncthreads();
-  return t;
+  *total = tot;
+  return before + inc - v;
 }
 
-template <int NT, int R>
-__device__ SelectResult block_select(const uint32_t* __restrict__ keys, int N, int K, SelectSmem sm) {
-  static_assert((R & (R - 1)) == 0 && R <= 64, "replicas");
-  const int tid = threadIdx.x;
-  uint32_t prefix = 0, mask = 0;
-  uint32_t k = (uint32_t)K;
-  uint32_t* tot = sm.misc;           // [256]
-  uint32_t* res = sm.misc + 256;     // [4]
-  uint32_t valid = 0;
-  SelectResult out{0u, 0u, 0u};
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    for (int i = tid; i < 256 * R; i += NT) sm.hist[i] = 0u;
-    __syncthreads();
-    const uint32_t rep = (uint32_t)(tid & (R - 1));
-    for (int v = tid; v < N; v += NT) {
-      const uint32_t key = keys[v];
-      if (key != 0u && (key & mask) == prefix)
-        atomicAdd(&sm.hist[((key >> shift) & 255u) * R + rep], 1u);
-    }
-    __syncthreads();
-    for (int bin = tid; bin < 256; bin += NT) {
-      uint32_t s = 0;
+// Radix select with two histogram buffers: every pass is "all threads add their
+// keys, barrier, wave 0 finds the bin holding the K-th key while the other waves
+// clear the next pass's buffer, barrier".
+template <int NT, int KPT>
+__device__ SelectResult block_select(const uint32_t (&key)[KPT], int K, uint32_t* hist, uint32_t* scratch) {
+  static_assert(NT >= 128, "needs a second wave to clear buffers");
+  const int tid = threadIdx.x, lane = tid & 63;
+  uint32_t* res = scratch + 64;
+  for (int i = tid; i < kSelectHist; i += NT) hist[i] = 0u;
+  __syncthreads();
+  uint32_t prefix = 0u, mask = 0u, k = (uint32_t)K;
+#pragma unroll 1
+  for (int pass = 0; pass < 3; ++pass) {
+    const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
+    const int nb = pass == 2 ? 1024 : 2048;
+    uint32_t* H = hist + (pass & 1) * kHistStride;
 #pragma unroll
-      for (int r = 0; r < R; ++r) s += sm.hist[bin * R + r];
-      tot[bin] = s;
+    for (int i = 0; i < KPT; ++i) {
+      const uint32_t x = key[i];
+      if (x != 0u && (x & mask) == prefix) {
+        const uint32_t d = (x >> shift) & (uint32_t)(nb - 1);
+        atomicAdd(&H[d + (d >> 5)], 1u);
+      }
     }
     __syncthreads();
     if (tid < 64) {
-      // lane l owns bins 4l..4l+3; "above" = keys in higher bins of this prefix
-      const int l = tid;
-      const uint32_t c0 = tot[4 * l], c1 = tot[4 * l + 1], c2 = tot[4 * l + 2], c3 = tot[4 * l + 3];
-      const uint32_t sl = c0 + c1 + c2 + c3;
-      uint32_t suf = sl;
+      // Two-level search.  Lane l owns bins [l*bpl, (l+1)*bpl): one prefix scan over
+      // the lane sums finds the lane holding the K-th key, a second one over that
+      // lane's bins (one bin per lane) finds the bin.  "above" = keys in higher bins.
+      const int bpl = nb / 64;
+      const uint32_t* hl = H + lane * bpl + ((lane * bpl) >> 5);
+      uint32_t ls = 0;
 #pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const uint32_t t = __shfl_down(suf, o, kWave);
-        if (l + o < 64) suf += t;
+      for (int j = 0; j < 32; ++j) ls += (j < bpl) ? hl[j] : 0u;
+      const uint32_t pre = wave_incl_scan(ls);
+      const uint32_t tot = __builtin_amdgcn_readlane(pre, 63);
+      const uint32_t above_l = tot - pre;                       // keys in lanes above l
+      const uint64_t hit = __ballot(above_l < k && k <= above_l + ls);
+      const int ls_lane = __builtin_ctzll(hit);                 // exactly one lane
+      const uint32_t above0 = __builtin_amdgcn_readlane(above_l, ls_lane);
+      const int bin = ls_lane * bpl + lane;
+      const uint32_t cb = lane < bpl ? H[bin + (bin >> 5)] : 0u;
+      const uint32_t pre2 = wave_incl_scan(cb);
+      const uint32_t tot2 = __builtin_amdgcn_readlane(pre2, 63);
+      const uint32_t above_b = above0 + tot2 - pre2;            // keys in higher bins
+      const uint64_t hit2 = __ballot(lane < bpl && above_b < k && k <= above_b + cb);
+      const int jb = __builtin_ctzll(hit2);
+      if (lane == jb) {
+        res[0] = (uint32_t)bin;
+        res[1] = k - above_b;
+        res[2] = cb;
       }
-      const uint32_t excl = suf - sl;
-      if (shift == 24 && l == 0) res[2] = suf;   // all valid keys
-      const uint32_t above[4] = {excl + c3 + c2 + c1, excl + c3 + c2, excl + c3, excl};
-      const uint32_t cnt[4] = {c0, c1, c2, c3};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if (above[i] < k && k <= above[i] + cnt[i]) {
-          res[0] = (uint32_t)(4 * l + i);
-          res[1] = k - above[i];
-          res[3] = cnt[i];
-        }
-      }
+      if (lane == 0) res[3] = tot;                              // all keys of this pass
+    } else {
+      uint32_t* other = hist + ((pass + 1) & 1) * kHistStride;
+      for (int i = tid - 64; i < kHistStride; i += NT - 64) other[i] = 0u;
     }
     __syncthreads();
-    if (shift == 24) {
-      valid = res[2];
-      if (valid <= (uint32_t)K) {            // fewer valid keys than K: take them all
-        out = SelectResult{0u, 0u, valid};
-        __syncthreads();
-        return out;
-      }
-    }
-    const uint32_t d = res[0];
-    const uint32_t knew = res[1];
-    const uint32_t in_bin = res[3];
-    __syncthreads();
+    if (pass == 0 && res[3] <= (uint32_t)K) return SelectResult{0u, 0u, res[3]};   // take every valid key
+    const uint32_t d = res[0], knew = res[1], in_bin = res[2];
     const uint32_t lo = prefix | (d << shift);
-    if (knew == in_bin) {                    // the whole bin is taken: threshold below it
-      out = SelectResult{lo == 0u ? 0u : lo - 1u, 0u, (uint32_t)K};
-      return out;
-    }
+    if (knew == in_bin) return SelectResult{lo == 0u ? 0u : lo - 1u, 0u, (uint32_t)K};
     prefix = lo;
-    mask |= 255u << shift;
+    mask |= (uint32_t)(nb - 1) << shift;
     k = knew;
   }
-  out = SelectResult{prefix, k, (uint32_t)K};
-  return out;
+  return SelectResult{prefix, k, (uint32_t)K};
 }
 
-// Emit selected positions in ascending order: emit(v, pos) for the pos-th selected v.
-template <int NT, class Emit>
-__device__ void block_emit_ordered(const uint32_t* __restrict__ keys, int N, SelectResult sr,
-                                   uint32_t* wave_counts /*[2][2][NT/64]*/, Emit emit) {
-  constexpr int NW = NT / 64;
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  uint32_t out_run = 0, eq_run = 0;
-  int parity = 0;
-  for (int base = 0; base < N; base += NT, parity ^= 1) {
-    const int v = base + tid;
-    const uint32_t key = v < N ? keys[v] : 0u;
-    const bool gt = key != 0u && key > sr.thr;
-    const bool eq = key != 0u && key == sr.thr && sr.krem > 0u;
-    const uint64_t mg = __ballot(gt);
-    const uint64_t me = __ballot(eq);
-    uint32_t* wc = wave_counts + parity * 2 * NW;
-    if (lane == 0) {
-      wc[wid] = (uint32_t)__popcll(mg);
-      wc[NW + wid] = (uint32_t)__popcll(me);
-    }
-    __syncthreads();
-    uint32_t gt_before = (uint32_t)__popcll(mg & lt_mask);
-    uint32_t eq_before = (uint32_t)__popcll(me & lt_mask);
-    uint32_t gt_tot = 0, eq_tot = 0;
+// Emit selected positions in ascending order: emit(i, pos) for the key in slot i of
+// this thread (position t*KPT+i) when it is the pos-th selected entry.
+template <int NT, int KPT, class Emit>
+__device__ __forceinline__ void block_emit(const uint32_t (&key)[KPT], SelectResult sr, uint32_t* scratch, Emit emit) {
+  uint32_t gt_c = 0, eq_c = 0;
 #pragma unroll
-    for (int i = 0; i < NW; ++i) {
-      const uint32_t g = wc[i], e = wc[NW + i];
-      if (i < wid) {
-        gt_before += g;
-        eq_before += e;
-      }
-      gt_tot += g;
-      eq_tot += e;
-    }
-    const uint32_t eq_left = sr.krem > eq_run ? sr.krem - eq_run : 0u;
-    const bool sel = gt || (eq && eq_before < eq_left);
-    if (sel) emit(v, out_run + gt_before + min(eq_before, eq_left));
-    out_run += gt_tot + min(eq_tot, eq_left);
-    eq_run += eq_tot;
+  for (int i = 0; i < KPT; ++i) {
+    const uint32_t x = key[i];
+    gt_c += (x != 0u && x > sr.thr) ? 1u : 0u;
+    eq_c += (x != 0u && x == sr.thr) ? 1u : 0u;
   }
-  __syncthreads();
+  uint32_t tot;
+  const uint32_t ex = block_excl_scan<NT>((gt_c << 16) | eq_c, scratch, &tot);
+  uint32_t eq_before = ex & 0xffffu;
+  uint32_t out = (ex >> 16) + min(eq_before, sr.krem);
+#pragma unroll
+  for (int i = 0; i < KPT; ++i) {
+    const uint32_t x = key[i];
+    if (x == 0u) continue;
+    if (x > sr.thr) {
+      emit(i, out++);
+    } else if (x == sr.thr) {
+      if (eq_before < sr.krem) emit(i, out++);
+      ++eq_before;
+    }
+  }
 }
 
 }  // namespace csa2
