@@ -1,14 +1,16 @@
-// Sparse gather-attention for one decode query per sequence: the top-K FP4 latent
-// rows plus the bf16 sliding window, one softmax, K = V = the 512-d latent.
+// Sparse gather-attention: the top-K FP4 latent rows plus the bf16 sliding window,
+// one softmax, K = V = the 512-d latent.  Serves one decode query per sequence and,
+// in prefill mode, C chunk queries per sequence whose window rows come from the
+// caller's array of the chunk's own tokens.
 //
 // [P1] "DeepSeek-v4.1 Flash: KVキャッシュ圧縮の限界を押し広げる" §1.2 (window 128,
 // every head shares one 512-d latent) and §2.3.1 (each query attends to the selected
 // entries and the layer's window KV together); [P3] "DeepSeek V4.1 Flash
 // architecture..." (scores -> weights summing to 1 -> weighted sum of values).
 //
-// Decomposition: one workgroup per (sequence, group of 16 heads); blockIdx is mapped
-// so that the head groups of one sequence run on the same XCD and share its L2 for
-// the gathered rows.  Four waves, one per SIMD, 512 registers each.  All row data
+// Decomposition: one workgroup per (query, group of 16 heads); blockIdx is mapped
+// so that the head groups of one query, and neighbouring queries of one sequence,
+// run on the same XCD and share its L2 for the gathered rows.  Four waves, one per SIMD, 512 registers each.  All row data
 // reaches LDS through global_load_lds_dwordx4 (no registers, everything in flight at
 // once), in two phases that reuse one 136 KB staging area:
 //   A. the window rows (bf16, 1 KB each, pitch 1040 B) -- they need no index
@@ -68,16 +70,16 @@ struct DecArgs {
   const uint8_t* lat_scales;
   const int32_t* block_table;
   int n_pages, max_pages;
-  const int32_t* ctx_len;
+  const int32_t* len;      // decode: context length; prefill: tokens before the chunk
   const uint16_t* q;
   const int32_t* topk_idx;
   int topk;
-  const uint16_t* swa;
+  const uint16_t* win;     // decode: ring [B][W][512]; prefill: [B][W-1+C][512]
   int W;
-  float scale_log2;   // sm_scale * log2(e)
+  float scale_log2;        // sm_scale * log2(e)
   uint16_t* out;
   float* lse;
-  int B, H, HG;
+  int B, C, H, HG, prefill, q_per_xcd;
 };
 
 // low halves of a and b -> (a.lo, b.lo); high halves -> (a.hi, b.hi)
@@ -293,23 +295,27 @@ __global__ __launch_bounds__(kThreads) void sparse_decode_kernel(DecArgs a) {
   float* m_g = l_w + kWaves * 16;
   float* l_g = m_g + 16;
 
-  // XCD-aware mapping: consecutive workgroup ids go to different XCDs, so all head
-  // groups of a sequence get the same id modulo 8.
+  // XCD-aware mapping: consecutive workgroup ids go to different XCDs; XCD x takes
+  // the contiguous query range [x * q_per_xcd, (x+1) * q_per_xcd), all head groups.
   const int xcd = blockIdx.x & 7;
   const int li = blockIdx.x >> 3;
-  const int b = xcd + 8 * (li / a.HG);
-  const int hg = li % a.HG;
-  if (b >= a.B) return;
+  const int ql = li / a.HG;
+  const int hg = li - ql * a.HG;
+  const int64_t qi = (int64_t)xcd * a.q_per_xcd + ql;
+  if (ql >= a.q_per_xcd || qi >= (int64_t)a.B * a.C) return;
+  const int b = (int)(qi / a.C);
+  const int ci = (int)(qi - (int64_t)b * a.C);
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15, g = lane >> 4;
 
-  int64_t L = a.ctx_len[b];
+  int64_t L = a.len[b];
   if (L < 0) L = 0;
+  if (a.prefill) L += ci + 1;   // chunk query ci sits at position prior + ci
   const int n_vis = (int)(L >> 1);
   const int t = (int)L - 1;
-  const uint16_t* swa_b = a.swa + (int64_t)b * a.W * CSA2_D_LATENT;
+  const uint16_t* win_b = a.win + (int64_t)b * (a.prefill ? a.W - 1 + a.C : a.W) * CSA2_D_LATENT;
 
   // window batch: LDS chunk c (16 bytes) = piece c%65 of row c/65 (piece 64 = pad)
   auto stage_window = [&](int w0, int nw) {
@@ -319,7 +325,8 @@ __global__ __launch_bounds__(kThreads) void sparse_decode_kernel(DecArgs a) {
       const int r = c / 65, piece = c - r * 65;
       if (c < chunks && piece < 64 && win_valid(a.W, t, w0 + r)) {
         const int pos = t - (a.W - 1) + w0 + r;
-        const uint16_t* src = swa_b + (int64_t)(pos % a.W) * CSA2_D_LATENT + 8 * piece;
+        const int row = a.prefill ? ci + w0 + r : pos % a.W;
+        const uint16_t* src = win_b + (int64_t)row * CSA2_D_LATENT + 8 * piece;
         __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src), stage + ins * 1024, 16, 0, 0);
       }
     }
@@ -357,7 +364,7 @@ __global__ __launch_bounds__(kThreads) void sparse_decode_kernel(DecArgs a) {
   // q operand of head hg*16+n: dims 128g + 8s .. +7 for k-step s
   u32x4 qf[16];
   {
-    const uint16_t* qp = a.q + ((int64_t)b * a.H + hg * 16 + n) * CSA2_D_LATENT + 128 * g;
+    const uint16_t* qp = a.q + (qi * a.H + hg * 16 + n) * CSA2_D_LATENT + 128 * g;
 #pragma unroll
     for (int s = 0; s < 16; ++s) qf[s] = *reinterpret_cast<const u32x4*>(qp + 8 * s);
   }
@@ -369,7 +376,7 @@ __global__ __launch_bounds__(kThreads) void sparse_decode_kernel(DecArgs a) {
 #pragma unroll
     for (int u = 0; u < RPT; ++u) {
       const int i = tid + u * kThreads;
-      e[u] = i < nrows ? a.topk_idx[(int64_t)b * a.topk + r0 + i] : -1;
+      e[u] = i < nrows ? a.topk_idx[qi * a.topk + r0 + i] : -1;
     }
     int pg[RPT];
 #pragma unroll
@@ -521,12 +528,12 @@ __global__ __launch_bounds__(kThreads) void sparse_decode_kernel(DecArgs a) {
     const float inv = l > 0.f ? 1.f / l : 0.f;
     const uint32_t v0 = f32_to_bf16_rne(s4[0] * inv), v1 = f32_to_bf16_rne(s4[1] * inv);
     const uint32_t v2 = f32_to_bf16_rne(s4[2] * inv), v3 = f32_to_bf16_rne(s4[3] * inv);
-    *reinterpret_cast<u32x2*>(a.out + ((int64_t)b * a.H + hg * 16 + h) * CSA2_D_LATENT + d) =
+    *reinterpret_cast<u32x2*>(a.out + (qi * a.H + hg * 16 + h) * CSA2_D_LATENT + d) =
         u32x2{v0 | (v1 << 16), v2 | (v3 << 16)};
   }
   if (a.lse && tid < 16) {
     const float l = l_g[tid];
-    a.lse[(int64_t)b * a.H + hg * 16 + tid] = l > 0.f ? (m_g[tid] + log2f(l)) * kLn2 : -INFINITY;
+    a.lse[qi * a.H + hg * 16 + tid] = l > 0.f ? (m_g[tid] + log2f(l)) * kLn2 : -INFINITY;
   }
 }
 
@@ -545,10 +552,9 @@ size_t sparse_decode_ws(int B, int H, int topk) {
   return 0;
 }
 
-int launch_sparse_decode(const csa2_cache_t& c, int B, int H, const int32_t* ctx_len,
-                         const uint16_t* q, const int32_t* topk_idx, int topk, const uint16_t* swa,
-                         int W, float sm_scale, uint16_t* out, float* lse, void* ws, hipStream_t s) {
-  (void)ws;
+int launch_gather_attention(const csa2_cache_t& c, int B, int C, int H, const int32_t* len, bool prefill,
+                            const uint16_t* q, const int32_t* topk_idx, int topk, const uint16_t* win,
+                            int W, float sm_scale, uint16_t* out, float* lse, hipStream_t s) {
   if (!lds_limit_set()) return CSA2_EHIP;
   DecArgs a;
   a.lat_codes = c.lat_codes;
@@ -556,22 +562,33 @@ int launch_sparse_decode(const csa2_cache_t& c, int B, int H, const int32_t* ctx
   a.block_table = c.block_table;
   a.n_pages = c.n_pages;
   a.max_pages = c.max_pages;
-  a.ctx_len = ctx_len;
+  a.len = len;
   a.q = q;
   a.topk_idx = topk_idx;
   a.topk = topk;
-  a.swa = swa;
+  a.win = win;
   a.W = W;
   a.scale_log2 = sm_scale * kLog2e;
   a.out = out;
   a.lse = lse;
   a.B = B;
+  a.C = C;
   a.H = H;
   a.HG = H / 16;
-  const int64_t grid = 8 * ((int64_t)(B + 7) / 8) * a.HG;
+  a.prefill = prefill ? 1 : 0;
+  const int64_t per = ((int64_t)B * C + 7) / 8;
+  const int64_t grid = 8 * per * a.HG;
   if (grid > 0x7fffffff) return CSA2_EUNSUPPORTED;
+  a.q_per_xcd = (int)per;
   hipLaunchKernelGGL(sparse_decode_kernel, dim3((unsigned)grid), dim3(kThreads), kLdsBytes, s, a);
   return hip_status();
+}
+
+int launch_sparse_decode(const csa2_cache_t& c, int B, int H, const int32_t* ctx_len,
+                         const uint16_t* q, const int32_t* topk_idx, int topk, const uint16_t* swa,
+                         int W, float sm_scale, uint16_t* out, float* lse, void* ws, hipStream_t s) {
+  (void)ws;
+  return launch_gather_attention(c, B, 1, H, ctx_len, false, q, topk_idx, topk, swa, W, sm_scale, out, lse, s);
 }
 
 }  // namespace csa2

@@ -155,7 +155,7 @@ __global__ __launch_bounds__(kScanThreads) void index_scan_kernel(ScanArgs a) {
       const int le = (wid * GPW + r0 + u) * 16;
       if (e0 + le >= n_vis) break;                        // wave-uniform
       const float s = score16(cd[u], sb[u], a0, a1, wh);
-      if (lane < 16) keys[le + n] = (le + n < n_in) ? score_key(s) : 0u;
+      if (lane < 16) keys[le + n] = (le + n < n_in && pg[u >> 2] >= 0) ? score_key(s) : 0u;   // absent page: no entry
     }
   }
   // tail of a partial chunk: keys of absent entries are 0

@@ -32,6 +32,12 @@ size_t sparse_decode_ws(int B, int H, int topk);
 int launch_sparse_decode(const csa2_cache_t& c, int B, int H, const int32_t* ctx_len,
                          const uint16_t* q, const int32_t* topk_idx, int topk, const uint16_t* swa,
                          int W, float sm_scale, uint16_t* out, float* lse, void* ws, hipStream_t s);
+// The attention kernel for B*C queries: C = 1 and prefill = false is the decode
+// call; prefill = true reads query positions as len[b] + chunk index and window
+// rows from a [B][W-1+C][512] array.
+int launch_gather_attention(const csa2_cache_t& c, int B, int C, int H, const int32_t* len, bool prefill,
+                            const uint16_t* q, const int32_t* topk_idx, int topk, const uint16_t* win,
+                            int W, float sm_scale, uint16_t* out, float* lse, hipStream_t s);
 size_t prefill_ws(int B, int H, int64_t max_ctx, int topk, int C);
 int launch_prefill_chunk(const csa2_cache_t& c, int B, int H, const int32_t* prior_len,
                          int64_t max_ctx, int C, const uint16_t* q, const uint16_t* q_idx,

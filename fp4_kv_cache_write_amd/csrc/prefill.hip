@@ -1,15 +1,353 @@
-// Chunked prefill (placeholder until the kernel lands).
+// Chunked prefill: the causal Full indexer of every chunk query, then the sparse
+// gather-attention of every chunk query (the decode attention kernel, run with C
+// queries per sequence and window rows read from the caller's `local` array).
+//
+// [P1] "DeepSeek-v4.1 Flash: KVキャッシュ圧縮の限界を押し広げる" §2.3.1 (each query
+// scores every entry its causal mask lets it see and keeps the top K), §2.2 (the
+// prefill cost is what the compression targets); [P3] "DeepSeek V4.1 Flash
+// architecture..." (causal mask: a query sees only entries whose tokens precede it).
+//
+// Indexer (prefill_index_kernel): one wave per (sequence, 4 consecutive queries).
+// The 4 queries x 4 indexer heads fill the 16 rows of a 16x16x32 bf16 MFMA, so a
+// 16-entry key group costs two MFMAs and every lane ends with one finished score:
+// lane l holds query l/16 against entry l%16 (rows 4q..4q+3 of the accumulator are
+// query q's heads).  Keys stream page by page straight from the paged cache, two
+// pages ahead of the MFMAs; page ids come 64 at a time in one vector load and are
+// read out with v_readlane.
+//
+// Top-K per query is streamed: every query keeps a buffer of (key, entry) pairs in
+// LDS, in entry order, and a threshold tau.  A score enters the buffer only when its
+// key beats tau.  When a buffer nears capacity the wave selects its K best pairs
+// exactly (MSB-first radix select over 8-bit digits, ties to the lower entry) and
+// compacts the buffer in place, keeping entry order; tau becomes the smallest kept
+// key.  This is exact: every dropped pair, and every later pair that does not beat
+// tau, has K pairs ranked above it (equal keys rank by entry, and later pairs have
+// higher entries).  At the end the same select writes the K entries in ascending
+// order.
 #include "common.h"
 #include "internal.h"
 
 namespace csa2 {
+namespace {
 
-size_t prefill_ws(int, int, int64_t, int, int) { return 0; }
+constexpr int kPfQ = 4;        // queries per wave
+constexpr int kPfHist = 256;   // radix-select histogram bins (8-bit digits)
 
-int launch_prefill_chunk(const csa2_cache_t&, int, int, const int32_t*, int64_t, int,
-                         const uint16_t*, const uint16_t*, const uint16_t*, const uint16_t*, int, int,
-                         float, uint16_t*, int32_t*, void*, hipStream_t) {
-  return CSA2_EUNSUPPORTED;
+struct PfIndexArgs {
+  const uint8_t* idx_codes;
+  const uint8_t* idx_scales;
+  const int32_t* block_table;
+  int n_pages, max_pages;
+  const int32_t* prior_len;
+  int64_t max_ctx;
+  const uint16_t* q_idx;
+  const uint16_t* w_idx;
+  int C, topk, cap;
+  int32_t* topk_idx;
+  int n_units, per_xcd;
+};
+
+// Number of set bits of m at lanes below this one.
+__device__ __forceinline__ uint32_t lanes_below(uint64_t m) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+// Selected: key > thr, or key == thr among the first krem such keys in buffer order.
+struct WaveSel {
+  uint32_t thr, krem;
+};
+
+// Exact selection of the k largest of the cnt (> k) nonzero keys buf[0..cnt), by
+// one wave.  Lane l owns histogram bins 4l..4l+3, so a scan over the lane sums
+// finds the lane holding the k-th key and four compares find the bin.
+__device__ WaveSel wave_select(const uint32_t* buf, int cnt, uint32_t k, uint32_t* hist) {
+  const int lane = threadIdx.x & 63;
+  uint32_t prefix = 0u, mask = 0u;
+#pragma unroll 1
+  for (int pass = 0; pass < 4; ++pass) {
+    const int shift = 24 - 8 * pass;
+    *reinterpret_cast<u32x4*>(hist + 4 * lane) = u32x4{0u, 0u, 0u, 0u};
+    __syncthreads();
+    for (int p = lane; p < cnt; p += 64) {
+      const uint32_t x = buf[p];
+      if ((x & mask) == prefix) atomicAdd(&hist[(x >> shift) & 255u], 1u);
+    }
+    __syncthreads();
+    const u32x4 c = *reinterpret_cast<const u32x4*>(hist + 4 * lane);
+    const uint32_t ls = c.x + c.y + c.z + c.w;
+    const uint32_t incl = wave_incl_scan(ls);
+    const uint32_t above_l = __builtin_amdgcn_readlane(incl, 63) - incl;   // keys in higher lanes
+    const uint64_t hit = __ballot(above_l < k && k <= above_l + ls);
+    const int hl = (int)(__builtin_ctzll(hit | (1ull << 63)));
+    const uint32_t cs[4] = {c.x, c.y, c.z, c.w};
+    uint32_t above = above_l, bin = 0u, knew = 0u, inb = 0u;
+    bool found = false;
+#pragma unroll
+    for (int j = 3; j >= 0; --j) {
+      if (!found && above < k && k <= above + cs[j]) {
+        found = true;
+        bin = 4u * lane + j;
+        knew = k - above;
+        inb = cs[j];
+      }
+      above += cs[j];
+    }
+    bin = __builtin_amdgcn_readlane(bin, hl);
+    knew = __builtin_amdgcn_readlane(knew, hl);
+    inb = __builtin_amdgcn_readlane(inb, hl);
+    const uint32_t lo = prefix | (bin << shift);
+    __syncthreads();
+    if (knew == inb) return WaveSel{lo ? lo - 1u : 0u, 0u};   // the whole bin is in
+    prefix = lo;
+    mask |= 255u << shift;
+    k = knew;
+  }
+  return WaveSel{prefix, k};
+}
+
+// Keep the selected pairs of buf[0..cnt) in order: in place (out == nullptr) or as
+// entry ids into out.  Returns the number kept; *kmin gets the smallest kept key.
+__device__ int wave_keep(uint32_t* keys, int32_t* ids, int cnt, WaveSel s, int32_t* out, uint32_t* kmin) {
+  const int lane = threadIdx.x & 63;
+  uint32_t kept = 0u, eq_before = 0u, mn = 0xffffffffu;
+#pragma unroll 1
+  for (int p0 = 0; p0 < cnt; p0 += 64) {
+    const int p = p0 + lane;
+    const uint32_t x = p < cnt ? keys[p] : 0u;
+    const int32_t id = p < cnt ? ids[p] : -1;
+    const bool eq = x != 0u && x == s.thr;
+    const uint64_t meq = __ballot(eq);
+    const bool sel = x != 0u && (x > s.thr || (eq && eq_before + lanes_below(meq) < s.krem));
+    const uint64_t ms = __ballot(sel);
+    const uint32_t dst = kept + lanes_below(ms);
+    if (sel) {
+      if (out) {
+        out[dst] = id;
+      } else {
+        keys[dst] = x;
+        ids[dst] = id;
+      }
+      mn = min(mn, x);
+    }
+    kept += (uint32_t)__builtin_popcountll(ms);
+    eq_before += (uint32_t)__builtin_popcountll(meq);
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) mn = min(mn, (uint32_t)__shfl_xor((int)mn, o, kWave));
+  *kmin = mn;
+  return (int)kept;
+}
+
+__global__ __launch_bounds__(64) void prefill_index_kernel(PfIndexArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint32_t pf_lds[];
+  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  const int unit = xcd * a.per_xcd + slot;   // contiguous query groups per XCD
+  if (slot >= a.per_xcd || unit >= a.n_units) return;
+  const int qpb = (a.C + kPfQ - 1) / kPfQ;
+  const int b = unit / qpb;
+  const int i0 = (unit - b * qpb) * kPfQ;
+  const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
+  uint32_t* hist = pf_lds;
+  uint32_t* kbuf = pf_lds + kPfHist;                                  // [4][cap]
+  int32_t* ibuf = reinterpret_cast<int32_t*>(kbuf + kPfQ * a.cap);    // [4][cap]
+
+  int64_t prior = a.prior_len[b];
+  if (prior < 0) prior = 0;
+  auto n_vis = [&](int i) -> int {   // entries visible to chunk query i
+    if (i >= a.C) return 0;
+    int64_t L = prior + i + 1;
+    if (L > a.max_ctx) L = a.max_ctx;
+    return (int)(L >> 1);
+  };
+  const int nv = n_vis(i0 + g);                       // this lane's query
+  const int nv_max = n_vis(min(i0 + kPfQ - 1, a.C - 1));
+
+  // A operand: row m = l%16 is head m%4 of query i0 + m/4, dims 16g .. 16g+15.
+  u32x4 qa0 = {0u, 0u, 0u, 0u}, qa1 = {0u, 0u, 0u, 0u};
+  {
+    const int qr = i0 + (n >> 2);
+    if (qr < a.C) {
+      const uint16_t* qp = a.q_idx + (((int64_t)b * a.C + qr) * CSA2_H_INDEX + (n & 3)) * CSA2_D_INDEX + 16 * g;
+      qa0 = *reinterpret_cast<const u32x4*>(qp);
+      qa1 = *reinterpret_cast<const u32x4*>(qp + 8);
+    }
+  }
+  const bf16x8 a0 = __builtin_bit_cast(bf16x8, qa0), a1 = __builtin_bit_cast(bf16x8, qa1);
+  float wh[4] = {0.f, 0.f, 0.f, 0.f};
+  if (i0 + g < a.C) {
+#pragma unroll
+    for (int h = 0; h < 4; ++h) wh[h] = bf16_to_f32(a.w_idx[((int64_t)b * a.C + i0 + g) * CSA2_H_INDEX + h]);
+  }
+
+  uint32_t* kq = kbuf + g * a.cap;
+  int32_t* iq = ibuf + g * a.cap;
+  uint32_t tau = 0u;   // key 0 = no entry, so every real key beats the initial tau
+  int cnt = 0;
+
+  const int32_t* bt = a.block_table + (int64_t)b * a.max_pages;
+  const int np = (nv_max + CSA2_PAGE - 1) / CSA2_PAGE;
+  auto bt_batch = [&](int k) -> int {   // page ids 64k .. 64k+63, one per lane
+    const int pi = 64 * k + lane;
+    return (pi < np && pi < a.max_pages) ? bt[pi] : -1;
+  };
+  int bt_cur = bt_batch(0), bt_nxt = bt_batch(1);
+
+  struct Page {
+    u32x2 cd[4];
+    uint32_t sb[4];
+    int ok;
+  };
+  auto load_page = [&](int p, int phys, Page& pg) {
+    pg.ok = (p < np && phys >= 0 && phys < a.n_pages) ? 1 : 0;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      pg.cd[t] = u32x2{0u, 0u};
+      pg.sb[t] = 0u;
+    }
+    if (pg.ok) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int64_t row = (int64_t)phys * CSA2_PAGE + 16 * t + n;
+        pg.cd[t] = *reinterpret_cast<const u32x2*>(a.idx_codes + row * CSA2_IDX_CODE_BYTES + 8 * g);
+        pg.sb[t] = a.idx_scales[row * CSA2_IDX_SCALE_BYTES + (g >> 1)];
+      }
+    }
+  };
+  Page p0, p1;
+  load_page(0, __builtin_amdgcn_readlane(bt_cur, 0), p0);
+  load_page(1, __builtin_amdgcn_readlane(bt_cur, 1), p1);
+
+#pragma unroll 1
+  for (int p = 0; p < np; ++p) {
+    // issue the loads of page p + 2 before scoring page p
+    const int lp = p + 2;
+    if ((lp & 63) == 0) {
+      bt_cur = bt_nxt;
+      bt_nxt = bt_batch((lp >> 6) + 1);
+    }
+    Page p2;
+    load_page(lp, __builtin_amdgcn_readlane(bt_cur, lp & 63), p2);
+
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const float sc = e8m0_scale(p0.sb[t]);
+      u32x4 lo, hi;
+      lo.x = fp4x2_to_bf16x2<0>(p0.cd[t].x, sc);
+      lo.y = fp4x2_to_bf16x2<1>(p0.cd[t].x, sc);
+      lo.z = fp4x2_to_bf16x2<2>(p0.cd[t].x, sc);
+      lo.w = fp4x2_to_bf16x2<3>(p0.cd[t].x, sc);
+      hi.x = fp4x2_to_bf16x2<0>(p0.cd[t].y, sc);
+      hi.y = fp4x2_to_bf16x2<1>(p0.cd[t].y, sc);
+      hi.z = fp4x2_to_bf16x2<2>(p0.cd[t].y, sc);
+      hi.w = fp4x2_to_bf16x2<3>(p0.cd[t].y, sc);
+      f32x4 d = {0.f, 0.f, 0.f, 0.f};
+      d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, __builtin_bit_cast(bf16x8, lo), d, 0, 0, 0);
+      d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, __builtin_bit_cast(bf16x8, hi), d, 0, 0, 0);
+      // lane l: d[i] = head i of query l/16 against entry l%16 of the group
+      const float s = wh[0] * fmaxf(d[0], 0.f) + wh[1] * fmaxf(d[1], 0.f) + wh[2] * fmaxf(d[2], 0.f) +
+                      wh[3] * fmaxf(d[3], 0.f);
+      const int e = p * CSA2_PAGE + 16 * t + n;
+      const uint32_t key = (p0.ok && e < nv) ? score_key(s) : 0u;
+      const bool app = key > tau;
+      const uint64_t m = __ballot(app);
+      if (m) {
+        const uint32_t mg = (uint32_t)(m >> (16 * g)) & 0xffffu;
+        if (app) {
+          const int dst = cnt + __builtin_popcount(mg & ((1u << n) - 1u));
+          kq[dst] = key;
+          iq[dst] = e;
+        }
+        cnt += __builtin_popcount(mg);
+      }
+    }
+    p0 = p1;
+    p1 = p2;
+
+    // a page adds at most 64 pairs per query: compact before a buffer could overflow
+    if (__ballot(cnt > a.cap - CSA2_PAGE)) {
+#pragma unroll 1
+      for (int qq = 0; qq < kPfQ; ++qq) {
+        const int c = __builtin_amdgcn_readlane(cnt, 16 * qq);
+        if (c <= a.cap - CSA2_PAGE) continue;
+        uint32_t* kb = kbuf + qq * a.cap;
+        int32_t* ib = ibuf + qq * a.cap;
+        const WaveSel s = wave_select(kb, c, (uint32_t)a.topk, hist);
+        uint32_t mn;
+        const int kept = wave_keep(kb, ib, c, s, nullptr, &mn);
+        __syncthreads();
+        if (g == qq) {
+          cnt = kept;
+          tau = mn;
+        }
+      }
+    }
+  }
+
+  // final exact top-K of each query, entries ascending, padded with -1
+#pragma unroll 1
+  for (int qq = 0; qq < kPfQ; ++qq) {
+    if (i0 + qq >= a.C) break;
+    const int c = __builtin_amdgcn_readlane(cnt, 16 * qq);
+    uint32_t* kb = kbuf + qq * a.cap;
+    int32_t* ib = ibuf + qq * a.cap;
+    const WaveSel s = c > a.topk ? wave_select(kb, c, (uint32_t)a.topk, hist) : WaveSel{0u, 0u};
+    int32_t* out = a.topk_idx + ((int64_t)b * a.C + i0 + qq) * a.topk;
+    uint32_t mn;
+    const int kept = wave_keep(kb, ib, c, s, out, &mn);
+    for (int r = kept + lane; r < a.topk; r += 64) out[r] = -1;
+  }
+}
+
+int pf_cap(int topk) {
+  const int c = max(1024, topk + 512);
+  return (c + 63) & ~63;
+}
+
+size_t pf_lds_bytes(int topk) { return (size_t)(kPfHist + 2 * kPfQ * pf_cap(topk)) * 4; }
+
+}  // namespace
+
+size_t prefill_ws(int B, int H, int64_t max_ctx, int topk, int C) {
+  (void)H;
+  (void)max_ctx;
+  // top-K lists of all chunk queries, used when the caller passes no topk_idx
+  return (((size_t)B * C * topk * 4) + 255) & ~(size_t)255;
+}
+
+int launch_prefill_chunk(const csa2_cache_t& c, int B, int H, const int32_t* prior_len,
+                         int64_t max_ctx, int C, const uint16_t* q, const uint16_t* q_idx,
+                         const uint16_t* w_idx, const uint16_t* local, int W, int topk,
+                         float sm_scale, uint16_t* out, int32_t* topk_idx, void* ws, hipStream_t s) {
+  int32_t* tk = topk_idx ? topk_idx : reinterpret_cast<int32_t*>(ws);
+  const size_t lds = pf_lds_bytes(topk);
+  if (lds > 160 * 1024) return CSA2_EUNSUPPORTED;
+  static const bool attr_ok = hipFuncSetAttribute(reinterpret_cast<const void*>(prefill_index_kernel),
+                                                  hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                  160 * 1024) == hipSuccess;
+  if (!attr_ok) return CSA2_EHIP;
+  PfIndexArgs a;
+  a.idx_codes = c.idx_codes;
+  a.idx_scales = c.idx_scales;
+  a.block_table = c.block_table;
+  a.n_pages = c.n_pages;
+  a.max_pages = c.max_pages;
+  a.prior_len = prior_len;
+  a.max_ctx = max_ctx;
+  a.q_idx = q_idx;
+  a.w_idx = w_idx;
+  a.C = C;
+  a.topk = topk;
+  a.cap = pf_cap(topk);
+  a.topk_idx = tk;
+  const int64_t units = (int64_t)B * ((C + kPfQ - 1) / kPfQ);
+  if (units > 0x0fffffff) return CSA2_EUNSUPPORTED;
+  a.n_units = (int)units;
+  a.per_xcd = (int)((units + 7) / 8);
+  hipLaunchKernelGGL(prefill_index_kernel, dim3(8u * (unsigned)a.per_xcd), dim3(64), lds, s, a);
+  const int rc = hip_status();
+  if (rc != CSA2_OK) return rc;
+  return launch_gather_attention(c, B, C, H, prior_len, true, q, tk, topk, local, W, sm_scale, out,
+                                 nullptr, s);
 }
 
 }  // namespace csa2

@@ -162,15 +162,19 @@ int csa2_sparse_decode(const csa2_cache_t *cache, int B, int H, const int32_t *c
                        int W, float sm_scale, uint16_t *out, float *lse, void *ws, size_t ws_bytes,
                        void *stream);
 
-/* csa2_prefill_chunk — chunked prefill after csa2_write_kv stored the chunk.
- *   For sequence b and chunk query i (position t = prior_len[b] + i): Full-mode
- *   indexer over the floor((t+1)/2) entries visible to t, top-K as in
- *   csa2_index_full, then the attention of csa2_sparse_decode with window rows for
- *   positions max(0, t-W+1)..t taken from local[b][pos - prior_len[b] + W - 1].
+/* csa2_prefill_chunk — chunked prefill after csa2_write_kv stored the chunk
+ *   ([P1] §2.3.1: every query runs the indexer over the entries its causal mask
+ *   lets it see, keeps the top K and attends to them plus its window; [P3] causal
+ *   mask).  For sequence b and chunk query i (position t = prior_len[b] + i):
+ *   Full-mode indexer over the floor((t+1)/2) entries visible to t, top-K as in
+ *   csa2_index_full (no pool), then the attention of csa2_sparse_decode with window
+ *   rows for positions max(0, t-W+1)..t taken from local[b][pos - prior_len[b] + W - 1].
  *   q: [B][C][H][512]; q_idx: [B][C][4][64]; w_idx: [B][C][4]; local: [B][W-1+C][512]
- *   (bf16, device); out: [B][C][H][512] bf16; topk_idx: [B][C][topk] int32 or NULL.
- *   prior_len: [B] int32 (device), prior_len[b] + C <= max_ctx.
- *   ws: csa2_workspace_size(CSA2_FN_PREFILL_CHUNK, B, H, max_ctx, topk, 0, C). */
+ *   (bf16, device); out: [B][C][H][512] bf16; topk_idx: [B][C][topk] int32 or NULL
+ *   (then the lists live in the workspace).  prior_len: [B] int32 (device),
+ *   prior_len[b] + C <= max_ctx.  H a multiple of 16; 1 <= W <= 1024; 1 <= topk <= 2048.
+ *   ws: csa2_workspace_size(CSA2_FN_PREFILL_CHUNK, B, H, max_ctx, topk, 0, C) bytes,
+ *   needed only when topk_idx is NULL (ws may be NULL otherwise). */
 int csa2_prefill_chunk(const csa2_cache_t *cache, int B, int H, const int32_t *prior_len,
                        int64_t max_ctx, int C, const uint16_t *q, const uint16_t *q_idx,
                        const uint16_t *w_idx, const uint16_t *local, int W, int topk,

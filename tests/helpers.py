@@ -100,3 +100,35 @@ def check_attention_rows(o_gpu_bits, o_ref, tol: float = 2e-3) -> float:
     worst = float(ratio.max())
     assert np.all(err <= tol * ref), f"worst ratio {worst:.3e} > {tol}"
     return worst
+
+
+def prefill_caches(case, device="cuda", oracle_seqs=(), k_override=None):
+    """GPU cache and oracle cache of a PrefillCase: prior tokens, then the chunk.
+
+    The GPU cache receives every sequence; the oracle writes only `oracle_seqs`.
+    k_override(b, kidx) may replace the indexer keys (both sides get the same).
+    Returns (gpu_cache, oracle_cache, chunk dict of CPU tensors).
+    """
+    import fp4_kv_cache_write_amd as fk
+    cfg = case.cfg
+    gc = fk.PagedCache.allocate(case.n_pages, case.block_table, device=device)
+    oc = OracleCache(case.n_pages, case.block_table.numpy())
+    bt = case.block_table.to(device)
+    ch = case.chunk()
+    if k_override is not None:
+        ch["k_idx"] = torch.stack([k_override(b, ch["k_idx"][b]) for b in range(case.B)])
+    for b in range(case.B):
+        if cfg.prior > 0:
+            x, w, k = case.prior_tokens(b)
+            if k_override is not None:
+                k = k_override(b, k)
+            sub = fk.PagedCache(gc.lat_codes, gc.lat_scales, gc.idx_codes, gc.idx_scales, bt[b:b + 1].contiguous())
+            fk.write_kv(sub, torch.zeros(1, dtype=torch.int32, device=device), x.to(device)[None].contiguous(),
+                        w.to(device)[None].contiguous(), k.to(device)[None].contiguous())
+            if b in oracle_seqs:
+                oc.write(b, 0, bits(x), bits(w), bits(k))
+    fk.write_kv(gc, ch["start_tok"].to(device), ch["x"].to(device), ch["w"].to(device), ch["k_idx"].to(device))
+    for b in oracle_seqs:
+        oc.write(b, cfg.prior, bits(ch["x"][b]), bits(ch["w"][b]), bits(ch["k_idx"][b]))
+    torch.cuda.synchronize()
+    return gc, oc, ch
