@@ -39,27 +39,30 @@ class OracleCache:
         js = np.asarray(js, dtype=np.int64)
         return self.block_table[b, js // PAGE], js % PAGE
 
-    def write(self, b: int, start_tok: int, x_bits, w_bits, kidx_bits, chunk: int = 2048) -> None:
+    def write(self, b: int, start_tok: int, x_bits, w_bits, kidx_bits, chunk: int = 2048,
+              latent: bool = True) -> None:
         """Merge token pairs (start_tok, start_tok+1), ... and store entries start_tok/2 onward.
 
         x_bits, w_bits: bf16 bit patterns [T, 512]; kidx_bits: [T/2, 64].  T and
-        start_tok even.
+        start_tok even.  latent=False stores only the indexer keys (x and w unused),
+        for checks that read the latent of a few entries written separately.
         """
         x = np.asarray(x_bits)
         w = np.asarray(w_bits)
         k = np.asarray(kidx_bits)
-        T = x.shape[0]
-        assert T % 2 == 0 and start_tok % 2 == 0 and k.shape[0] == T // 2
+        T = 2 * k.shape[0]
+        assert start_tok % 2 == 0 and (not latent or x.shape[0] == T)
         for i0 in range(0, T // 2, chunk):
             i1 = min(T // 2, i0 + chunk)
-            xs = bf16_bits_to_f64(x[2 * i0: 2 * i1])
-            ws = bf16_bits_to_f64(w[2 * i0: 2 * i1])
-            y = merge_pair_f32(xs[0::2], xs[1::2], ws[0::2], ws[1::2])
-            lc, lu = quantise_blocks(y.astype(np.float64))
-            ic, iu = quantise_blocks(bf16_bits_to_f64(k[i0:i1]))
             pg, sl = self.slots(b, np.arange(start_tok // 2 + i0, start_tok // 2 + i1))
-            self.lat_codes[pg, sl] = pack_nibbles(lc)
-            self.lat_scales[pg, sl] = lu
+            if latent:
+                xs = bf16_bits_to_f64(x[2 * i0: 2 * i1])
+                ws = bf16_bits_to_f64(w[2 * i0: 2 * i1])
+                y = merge_pair_f32(xs[0::2], xs[1::2], ws[0::2], ws[1::2])
+                lc, lu = quantise_blocks(y.astype(np.float64))
+                self.lat_codes[pg, sl] = pack_nibbles(lc)
+                self.lat_scales[pg, sl] = lu
+            ic, iu = quantise_blocks(bf16_bits_to_f64(k[i0:i1]))
             self.idx_codes[pg, sl] = pack_nibbles(ic)
             self.idx_scales[pg, sl] = iu
 
