@@ -240,7 +240,7 @@ def prefill_chunk(cache: PagedCache, prior_len: torch.Tensor, max_ctx: int, q: t
     if out is None:
         out = torch.empty((B, C, H, D_LATENT), dtype=torch.bfloat16, device=q.device)
     tk = torch.empty((B, C, topk), dtype=torch.int32, device=q.device) if want_topk else None
-    if ws is None and tk is None:
+    if ws is None:
         ws = workspace(FN_PREFILL_CHUNK, device=q.device, B=B, H=H, max_ctx=max_ctx, topk=topk, C=C)
     wsb = ws.numel() if ws is not None else 0
     _check(lib().csa2_prefill_chunk(cache.ref, B, H, _ptr(prior_len), max_ctx, C, _ptr(q), _ptr(q_idx),

@@ -116,7 +116,7 @@ int csa2_prefill_chunk(const csa2_cache_t* cache, int B, int H, const int32_t* p
   if (H <= 0 || (H % 16) != 0 || C <= 0 || W < 1 || W > CSA2_MAX_WINDOW) return CSA2_EINVAL;
   if (topk < 1 || topk > CSA2_MAX_TOPK || max_ctx < C) return CSA2_EINVAL;
   if (max_ctx / 2 > (int64_t)cache->max_pages * CSA2_PAGE) return CSA2_EINVAL;
-  const size_t need = topk_idx ? 0 : prefill_ws(B, H, max_ctx, topk, C);
+  const size_t need = prefill_ws(B, H, max_ctx, topk, C);
   if (need > 0 && (!ws || ws_bytes < need)) return CSA2_EWORKSPACE;
   return launch_prefill_chunk(*cache, B, H, prior_len, max_ctx, C, q, q_idx, w_idx, local, W, topk,
                               sm_scale, out, topk_idx, ws, (hipStream_t)stream);

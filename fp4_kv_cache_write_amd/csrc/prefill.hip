@@ -15,15 +15,17 @@
 // pages ahead of the MFMAs; page ids come 64 at a time in one vector load and are
 // read out with v_readlane.
 //
-// Top-K per query is streamed: every query keeps a buffer of (key, entry) pairs in
-// LDS, in entry order, and a threshold tau.  A score enters the buffer only when its
-// key beats tau.  When a buffer nears capacity the wave selects its K best pairs
-// exactly (MSB-first radix select over 8-bit digits, ties to the lower entry) and
-// compacts the buffer in place, keeping entry order; tau becomes the smallest kept
-// key.  This is exact: every dropped pair, and every later pair that does not beat
-// tau, has K pairs ranked above it (equal keys rank by entry, and later pairs have
-// higher entries).  At the end the same select writes the K entries in ascending
-// order.
+// Top-K per query is streamed: every query keeps a list of (key, entry) pairs in
+// the workspace, in entry order, and a threshold tau.  A score joins the list only
+// when it beats tau.  When a list nears capacity the wave loads it into registers,
+// selects its K best pairs exactly (MSB-first radix select over 8-bit digits in an
+// LDS histogram, ties to the lower entry) and writes them back in entry order; tau
+// becomes the smallest kept key.  This is exact: every dropped pair, and every later
+// pair that does not beat tau, has K pairs ranked above it (equal keys rank by
+// entry, and later pairs have higher entries).  At the end the same select writes
+// the K entries in ascending order.  Keeping the lists out of LDS leaves the
+// occupancy to the register budget, so enough waves are resident to cover the
+// latency of the key stream.
 #include "common.h"
 #include "internal.h"
 
@@ -43,6 +45,7 @@ struct PfIndexArgs {
   const uint16_t* q_idx;
   const uint16_t* w_idx;
   int C, topk, cap;
+  u32x2* lists;          // [B*C][cap] (key, entry) pairs
   int32_t* topk_idx;
   int n_units, per_xcd;
 };
@@ -52,15 +55,15 @@ __device__ __forceinline__ uint32_t lanes_below(uint64_t m) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 
-// Selected: key > thr, or key == thr among the first krem such keys in buffer order.
+// Selected: key > thr, or key == thr among the first krem such keys in list order.
 struct WaveSel {
   uint32_t thr, krem;
 };
 
-// Exact selection of the k largest of the cnt (> k) nonzero keys buf[0..cnt), by
-// one wave.  Lane l owns histogram bins 4l..4l+3, so a scan over the lane sums
-// finds the lane holding the k-th key and four compares find the bin.
-__device__ WaveSel wave_select(const uint32_t* buf, int cnt, uint32_t k, uint32_t* hist) {
+// Exact selection of the k largest nonzero keys of kst[0..cnt) (at least k + 1 of
+// them) by one wave.  Lane l owns histogram bins 4l..4l+3, so a scan over the lane
+// sums finds the lane holding the k-th key and four compares find the bin.
+__device__ WaveSel wave_select(const uint32_t* kst, int cnt, uint32_t k, uint32_t* hist) {
   const int lane = threadIdx.x & 63;
   uint32_t prefix = 0u, mask = 0u;
 #pragma unroll 1
@@ -69,8 +72,8 @@ __device__ WaveSel wave_select(const uint32_t* buf, int cnt, uint32_t k, uint32_
     *reinterpret_cast<u32x4*>(hist + 4 * lane) = u32x4{0u, 0u, 0u, 0u};
     __syncthreads();
     for (int p = lane; p < cnt; p += 64) {
-      const uint32_t x = buf[p];
-      if ((x & mask) == prefix) atomicAdd(&hist[(x >> shift) & 255u], 1u);
+      const uint32_t x = kst[p];
+      if (x != 0u && (x & mask) == prefix) atomicAdd(&hist[(x >> shift) & 255u], 1u);
     }
     __syncthreads();
     const u32x4 c = *reinterpret_cast<const u32x4*>(hist + 4 * lane);
@@ -105,27 +108,41 @@ __device__ WaveSel wave_select(const uint32_t* buf, int cnt, uint32_t k, uint32_
   return WaveSel{prefix, k};
 }
 
-// Keep the selected pairs of buf[0..cnt) in order: in place (out == nullptr) or as
-// entry ids into out.  Returns the number kept; *kmin gets the smallest kept key.
-__device__ int wave_keep(uint32_t* keys, int32_t* ids, int cnt, WaveSel s, int32_t* out, uint32_t* kmin) {
+// Keep the selected pairs of list[0..cnt) in order -- back into the list (out ==
+// nullptr) or as entry ids into out -- and return how many were kept; *kmin gets
+// the smallest kept key.  sel_all keeps every pair.  The keys are copied into the
+// wave's LDS area kst with direct global->LDS loads (no registers held across the
+// scan); entry ids are read from the list only for the pairs kept.
+__device__ int list_keep(u32x2* list, int cnt, int topk, bool sel_all, uint32_t* kst, uint32_t* hist,
+                         int32_t* out, uint32_t* kmin) {
   const int lane = threadIdx.x & 63;
+  const uint32_t* words = reinterpret_cast<const uint32_t*>(list);
+  const int nr = (cnt + 63) >> 6;
+  for (int r = 0; r < nr; ++r) {
+    const int p = 64 * r + lane;
+    if (p < cnt) __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(words + 2 * p), kst + 64 * r, 4, 0, 0);
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  const WaveSel s = sel_all ? WaveSel{0u, 0u} : wave_select(kst, cnt, (uint32_t)topk, hist);
   uint32_t kept = 0u, eq_before = 0u, mn = 0xffffffffu;
 #pragma unroll 1
-  for (int p0 = 0; p0 < cnt; p0 += 64) {
-    const int p = p0 + lane;
-    const uint32_t x = p < cnt ? keys[p] : 0u;
-    const int32_t id = p < cnt ? ids[p] : -1;
+  for (int r = 0; r < nr; ++r) {
+    const int p = 64 * r + lane;
+    const uint32_t x = p < cnt ? kst[p] : 0u;
     const bool eq = x != 0u && x == s.thr;
     const uint64_t meq = __ballot(eq);
     const bool sel = x != 0u && (x > s.thr || (eq && eq_before + lanes_below(meq) < s.krem));
     const uint64_t ms = __ballot(sel);
     const uint32_t dst = kept + lanes_below(ms);
+    // the row's ids are read before any of its kept pairs is written back (dst <= p,
+    // and earlier rows were written before this row was read)
+    const int32_t id = sel ? (int32_t)words[2 * p + 1] : -1;
     if (sel) {
       if (out) {
         out[dst] = id;
       } else {
-        keys[dst] = x;
-        ids[dst] = id;
+        list[dst] = u32x2{x, (uint32_t)id};
       }
       mn = min(mn, x);
     }
@@ -134,12 +151,15 @@ __device__ int wave_keep(uint32_t* keys, int32_t* ids, int cnt, WaveSel s, int32
   }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) mn = min(mn, (uint32_t)__shfl_xor((int)mn, o, kWave));
+  __syncthreads();   // kst is reused by the next call
   *kmin = mn;
   return (int)kept;
 }
 
 __global__ __launch_bounds__(64) void prefill_index_kernel(PfIndexArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint32_t pf_lds[];
+  uint32_t* hist = pf_lds;             // [256]
+  uint32_t* kst = pf_lds + kPfHist;    // [cap] keys of the list being compacted
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
   const int unit = xcd * a.per_xcd + slot;   // contiguous query groups per XCD
   if (slot >= a.per_xcd || unit >= a.n_units) return;
@@ -147,9 +167,6 @@ __global__ __launch_bounds__(64) void prefill_index_kernel(PfIndexArgs a) {
   const int b = unit / qpb;
   const int i0 = (unit - b * qpb) * kPfQ;
   const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
-  uint32_t* hist = pf_lds;
-  uint32_t* kbuf = pf_lds + kPfHist;                                  // [4][cap]
-  int32_t* ibuf = reinterpret_cast<int32_t*>(kbuf + kPfQ * a.cap);    // [4][cap]
 
   int64_t prior = a.prior_len[b];
   if (prior < 0) prior = 0;
@@ -179,9 +196,11 @@ __global__ __launch_bounds__(64) void prefill_index_kernel(PfIndexArgs a) {
     for (int h = 0; h < 4; ++h) wh[h] = bf16_to_f32(a.w_idx[((int64_t)b * a.C + i0 + g) * CSA2_H_INDEX + h]);
   }
 
-  uint32_t* kq = kbuf + g * a.cap;
-  int32_t* iq = ibuf + g * a.cap;
-  uint32_t tau = 0u;   // key 0 = no entry, so every real key beats the initial tau
+  // this lane's query list, threshold (as a key and as a score) and fill
+  u32x2* const list0 = a.lists + ((int64_t)b * a.C + i0) * a.cap;
+  u32x2* const lq = list0 + (int64_t)g * a.cap;
+  uint32_t tau = 0u;          // key 0 = no entry, so every real key beats the initial tau
+  float tau_s = -INFINITY;    // a score beats tau iff it exceeds tau_s
   int cnt = 0;
 
   const int32_t* bt = a.block_table + (int64_t)b * a.max_pages;
@@ -247,84 +266,74 @@ __global__ __launch_bounds__(64) void prefill_index_kernel(PfIndexArgs a) {
       const float s = wh[0] * fmaxf(d[0], 0.f) + wh[1] * fmaxf(d[1], 0.f) + wh[2] * fmaxf(d[2], 0.f) +
                       wh[3] * fmaxf(d[3], 0.f);
       const int e = p * CSA2_PAGE + 16 * t + n;
-      const uint32_t key = (p0.ok && e < nv) ? score_key(s) : 0u;
-      const bool app = key > tau;
+      const bool app = p0.ok && e < nv && s > tau_s;
       const uint64_t m = __ballot(app);
       if (m) {
         const uint32_t mg = (uint32_t)(m >> (16 * g)) & 0xffffu;
-        if (app) {
-          const int dst = cnt + __builtin_popcount(mg & ((1u << n) - 1u));
-          kq[dst] = key;
-          iq[dst] = e;
-        }
+        if (app) lq[cnt + __builtin_popcount(mg & ((1u << n) - 1u))] = u32x2{score_key(s), (uint32_t)e};
         cnt += __builtin_popcount(mg);
       }
     }
     p0 = p1;
     p1 = p2;
 
-    // a page adds at most 64 pairs per query: compact before a buffer could overflow
+    // a page adds at most 64 pairs per query: compact before a list could overflow
     if (__ballot(cnt > a.cap - CSA2_PAGE)) {
+      __threadfence_block();   // the wave's list stores are visible to all its lanes
 #pragma unroll 1
       for (int qq = 0; qq < kPfQ; ++qq) {
         const int c = __builtin_amdgcn_readlane(cnt, 16 * qq);
         if (c <= a.cap - CSA2_PAGE) continue;
-        uint32_t* kb = kbuf + qq * a.cap;
-        int32_t* ib = ibuf + qq * a.cap;
-        const WaveSel s = wave_select(kb, c, (uint32_t)a.topk, hist);
         uint32_t mn;
-        const int kept = wave_keep(kb, ib, c, s, nullptr, &mn);
-        __syncthreads();
+        const int kept = list_keep(list0 + (int64_t)qq * a.cap, c, a.topk, false, kst, hist, nullptr, &mn);
         if (g == qq) {
           cnt = kept;
           tau = mn;
+          tau_s = key_score(mn);
         }
       }
+      __threadfence_block();
     }
   }
+  (void)tau;
 
   // final exact top-K of each query, entries ascending, padded with -1
+  __threadfence_block();
 #pragma unroll 1
   for (int qq = 0; qq < kPfQ; ++qq) {
     if (i0 + qq >= a.C) break;
     const int c = __builtin_amdgcn_readlane(cnt, 16 * qq);
-    uint32_t* kb = kbuf + qq * a.cap;
-    int32_t* ib = ibuf + qq * a.cap;
-    const WaveSel s = c > a.topk ? wave_select(kb, c, (uint32_t)a.topk, hist) : WaveSel{0u, 0u};
     int32_t* out = a.topk_idx + ((int64_t)b * a.C + i0 + qq) * a.topk;
     uint32_t mn;
-    const int kept = wave_keep(kb, ib, c, s, out, &mn);
+    const int kept = list_keep(list0 + (int64_t)qq * a.cap, c, a.topk, c <= a.topk, kst, hist, out, &mn);
     for (int r = kept + lane; r < a.topk; r += 64) out[r] = -1;
   }
 }
 
-int pf_cap(int topk) {
-  const int c = max(1024, topk + 512);
-  return (c + 63) & ~63;
-}
-
-size_t pf_lds_bytes(int topk) { return (size_t)(kPfHist + 2 * kPfQ * pf_cap(topk)) * 4; }
+// List capacity: K kept pairs plus at least 512 slots of slack.
+int pf_cap(int topk) { return (max(topk + 512, 1024) + 63) & ~63; }
 
 }  // namespace
+
+// Workspace: the candidate lists of all chunk queries, then their top-K lists
+// (used when the caller passes no topk_idx).
+static size_t pf_lists_bytes(int B, int C, int topk) {
+  return (((size_t)B * C * pf_cap(topk) * 8) + 255) & ~(size_t)255;
+}
 
 size_t prefill_ws(int B, int H, int64_t max_ctx, int topk, int C) {
   (void)H;
   (void)max_ctx;
-  // top-K lists of all chunk queries, used when the caller passes no topk_idx
-  return (((size_t)B * C * topk * 4) + 255) & ~(size_t)255;
+  return pf_lists_bytes(B, C, topk) + ((((size_t)B * C * topk * 4) + 255) & ~(size_t)255);
 }
 
 int launch_prefill_chunk(const csa2_cache_t& c, int B, int H, const int32_t* prior_len,
                          int64_t max_ctx, int C, const uint16_t* q, const uint16_t* q_idx,
                          const uint16_t* w_idx, const uint16_t* local, int W, int topk,
                          float sm_scale, uint16_t* out, int32_t* topk_idx, void* ws, hipStream_t s) {
-  int32_t* tk = topk_idx ? topk_idx : reinterpret_cast<int32_t*>(ws);
-  const size_t lds = pf_lds_bytes(topk);
-  if (lds > 160 * 1024) return CSA2_EUNSUPPORTED;
-  static const bool attr_ok = hipFuncSetAttribute(reinterpret_cast<const void*>(prefill_index_kernel),
-                                                  hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                  160 * 1024) == hipSuccess;
-  if (!attr_ok) return CSA2_EHIP;
+  u32x2* lists = reinterpret_cast<u32x2*>(ws);
+  int32_t* tk = topk_idx ? topk_idx : reinterpret_cast<int32_t*>(reinterpret_cast<uint8_t*>(ws) +
+                                                                  pf_lists_bytes(B, C, topk));
   PfIndexArgs a;
   a.idx_codes = c.idx_codes;
   a.idx_scales = c.idx_scales;
@@ -338,11 +347,13 @@ int launch_prefill_chunk(const csa2_cache_t& c, int B, int H, const int32_t* pri
   a.C = C;
   a.topk = topk;
   a.cap = pf_cap(topk);
+  a.lists = lists;
   a.topk_idx = tk;
   const int64_t units = (int64_t)B * ((C + kPfQ - 1) / kPfQ);
   if (units > 0x0fffffff) return CSA2_EUNSUPPORTED;
   a.n_units = (int)units;
   a.per_xcd = (int)((units + 7) / 8);
+  const size_t lds = (size_t)(kPfHist + a.cap) * 4;
   hipLaunchKernelGGL(prefill_index_kernel, dim3(8u * (unsigned)a.per_xcd), dim3(64), lds, s, a);
   const int rc = hip_status();
   if (rc != CSA2_OK) return rc;

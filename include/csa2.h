@@ -173,8 +173,8 @@ int csa2_sparse_decode(const csa2_cache_t *cache, int B, int H, const int32_t *c
  *   (bf16, device); out: [B][C][H][512] bf16; topk_idx: [B][C][topk] int32 or NULL
  *   (then the lists live in the workspace).  prior_len: [B] int32 (device),
  *   prior_len[b] + C <= max_ctx.  H a multiple of 16; 1 <= W <= 1024; 1 <= topk <= 2048.
- *   ws: csa2_workspace_size(CSA2_FN_PREFILL_CHUNK, B, H, max_ctx, topk, 0, C) bytes,
- *   needed only when topk_idx is NULL (ws may be NULL otherwise). */
+ *   ws: csa2_workspace_size(CSA2_FN_PREFILL_CHUNK, B, H, max_ctx, topk, 0, C) bytes
+ *   (device): per-query candidate lists, and the top-K lists when topk_idx is NULL. */
 int csa2_prefill_chunk(const csa2_cache_t *cache, int B, int H, const int32_t *prior_len,
                        int64_t max_ctx, int C, const uint16_t *q, const uint16_t *q_idx,
                        const uint16_t *w_idx, const uint16_t *local, int W, int topk,
