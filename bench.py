@@ -1,24 +1,26 @@
 #!/usr/bin/env python3
 """CSA2 sparse-decode benchmark on one MI355X.
 
-Workload (default): decode batch of 32 sequences at 65,536 tokens (32,768 merged
-entries each), 64 query heads, three layers on one cache -- Full (indexer over all
-entries, HSI pool of 512 blocks x 8, top-512), Reindex (re-score within the pool),
-Reuse (same entries, new query) -- each followed by sparse attention over the 512
-selected FP4 entries plus the 128-token bf16 window.  One step also completes the
-newest token pair: it merges and writes that pair's entry (the write path) before
-the Full layer reads it.  Inputs are seeded synthetic data already resident in HBM;
-timed steps rotate over cache replicas so the 256 MB Infinity Cache cannot serve a
-step from the previous one.
+Headline workload (`value`): decode batch of 32 sequences at 65,536 tokens (32,768
+merged entries each), 64 query heads, three layers on one cache -- Full (indexer
+over all entries, HSI pool of 512 blocks x 8, top-512), Reindex (re-score within
+the pool), Reuse (same entries, new query) -- each followed by sparse attention over
+the 512 selected FP4 entries plus the 128-token bf16 window.  One step also
+completes the newest token pair: it merges and writes that pair's entry (the write
+path) before the Full layer reads it.  Inputs are seeded synthetic data already
+resident in HBM; timed steps rotate over cache replicas so the 256 MB Infinity
+Cache cannot serve a step from the previous one.  Steps are replayed as HIP graphs.
 
-Prints one JSON line.  `value` = decode queries/s (sequences finishing the
-three-layer step per second) with each step replayed as a HIP graph.
+The same JSON line carries, under "secondary", the 1M-token decode (8 sequences,
+Full scan + attention) and the chunked prefill (4 x 4,096 queries against 131,072
+prior tokens) measured the same way.  `--workload` runs one of them alone instead.
+
+Prints one JSON line.
 """
 from __future__ import annotations
 
 import argparse
 import json
-import math
 import os
 import sys
 import time
@@ -32,6 +34,7 @@ if ROOT not in sys.path:
 
 METRIC = "sparse-decode queries/s and achieved HBM GB/s (% of peak) at 64K/1M ctx"
 HBM_PEAK_GBS = 8000.0           # MI355X published HBM3E bandwidth
+MFMA_BF16_PEAK_TFS = 2500.0     # MI355X dense bf16 MFMA
 BYTES_LAT, BYTES_IDX = 272, 34  # per merged entry (FP4 codes + e8m0 scales)
 
 
@@ -45,129 +48,150 @@ def parse():
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--replicas", type=int, default=8)
+    p.add_argument("--workload", choices=("c1", "c2", "c3", "c4"), default="c1",
+                   help="c1 = headline decode line (+ secondary c2, c3); others alone")
+    p.add_argument("--no-secondary", action="store_true")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seqs", type=int, default=2, help="sequences in the oracle's timed sample")
     p.add_argument("--no-graph", action="store_true", help="time eager launches instead of graph replay")
     return p.parse_args()
 
 
-class Replica:
-    """One independent copy of the step's inputs (cache + per-layer tensors)."""
+# ----------------------------------------------------------------------------------
+# decode workloads
+# ----------------------------------------------------------------------------------
 
-    def __init__(self, cache, layers, pair):
+class Replica:
+    """One independent copy of the step's inputs (cache + per-layer tensors + write)."""
+
+    def __init__(self, cache, layers, write):
         self.cache = cache
         self.layers = layers
-        self.pair = pair
+        self.write = write
 
 
-def build(case, fk, n_rep: int):
-    B = case.B
+def build_decode(case, fk, n_rep: int):
+    """Cache with every sequence's pre-built tokens; the step's write re-submits the
+    newest pair (no append) or submits the appended tokens."""
     dev = "cuda"
+    cfg = case.cfg
     cache = fk.PagedCache.allocate(case.n_pages, case.block_table, device=dev)
     bt_rows = case.block_table.to(dev)
     pair_x, pair_w, pair_k = [], [], []
-    for b in range(B):
+    for b in range(case.B):
         x, w, k = case.seq_tokens(b)
         T = x.shape[0]
         sub = fk.PagedCache(cache.lat_codes, cache.lat_scales, cache.idx_codes, cache.idx_scales,
                             bt_rows[b:b + 1].contiguous())
         fk.write_kv(sub, torch.zeros(1, dtype=torch.int32, device=dev), x[None].contiguous(),
                     w[None].contiguous(), k[None].contiguous())
-        pair_x.append(x[T - 2:].clone())
-        pair_w.append(w[T - 2:].clone())
-        pair_k.append(k[T // 2 - 1:].clone())
+        if cfg.append == 0:
+            pair_x.append(x[T - 2:].clone())
+            pair_w.append(w[T - 2:].clone())
+            pair_k.append(k[T // 2 - 1:].clone())
         del x, w, k
     torch.cuda.synchronize()
-    pair = dict(x=torch.stack(pair_x).contiguous(), w=torch.stack(pair_w).contiguous(),
-                k=torch.stack(pair_k).contiguous(),
-                start=torch.tensor([L - 2 for L in case.ctx_len], dtype=torch.int32, device=dev))
-    layers = [case.layer(l) for l in range(case.cfg.n_layers)]
+    if cfg.append == 0:
+        write = dict(x=torch.stack(pair_x).contiguous(), w=torch.stack(pair_w).contiguous(),
+                     k=torch.stack(pair_k).contiguous(),
+                     start=torch.tensor([L - 2 for L in case.ctx_len], dtype=torch.int32, device=dev))
+    else:
+        xa, wa, ka, start = case.append_tokens()
+        write = dict(x=xa.contiguous(), w=wa.contiguous(), k=ka.contiguous(), start=start.to(dev))
+    layers = [case.layer(l) for l in range(cfg.n_layers)]
     reps = []
     for r in range(n_rep):
         c = cache if r == 0 else cache.clone()
         ls = [{k: (v if r == 0 else v.clone()) for k, v in L.items()} for L in layers]
-        pr = {k: (v if r == 0 else v.clone()) for k, v in pair.items()}
-        reps.append(Replica(c, ls, pr))
+        wr = {k: (v if r == 0 else v.clone()) for k, v in write.items()}
+        reps.append(Replica(c, ls, wr))
     torch.cuda.synchronize()
     return reps
 
 
-def main() -> int:
-    args = parse()
-    world = int(os.environ.get("WORLD_SIZE", "1"))
-    if args.gpus != 1 or world != 1:
-        print("bench.py: this build runs on one GPU only (the path has no multi-GPU sharding); "
-              f"got --gpus {args.gpus}, WORLD_SIZE={world}", file=sys.stderr)
-        return 2
-    import fp4_kv_cache_write_amd as fk
-    from synth import CONFIGS, make_decode_case
+def decode_bytes(case):
+    """Algorithmic HBM bytes of every call type for one step (formulas in the design doc)."""
+    cfg = case.cfg
+    B, H, topk, W = case.B, cfg.H, cfg.topk, cfg.window
+    n_vis = case.n_vis
+    pool_blocks = max([sp.pool_blocks for sp in cfg.layers] + [0])
+    n_t = [min(topk, v) for v in n_vis]
+    n_pool = [min(pool_blocks * cfg.cand_block, v) for v in n_vis]
+    n_win = [min(W, L) for L in case.ctx_len]
+    T_w = 2 if cfg.append == 0 else cfg.append
+    per = {
+        "write_kv": B * (T_w * 2 * 1024 + (T_w // 2) * 128 + 4 + (T_w // 2) * 306),
+        "index_full": sum(v * BYTES_IDX + 520 + 4 * topk + 4 * pool_blocks for v in n_vis),
+        "reindex": sum(p * BYTES_IDX + 520 + 4 * pool_blocks + 4 * topk for p in n_pool),
+        "sparse_decode": sum(t * BYTES_LAT + w * 1024 + 2 * H * 1024 + 4 * t + 4 * H for t, w in zip(n_t, n_win)),
+    }
+    count = {"write_kv": 1, "index_full": 0, "reindex": 0, "sparse_decode": 0}
+    for sp in cfg.layers:
+        count["sparse_decode"] += 1
+        if sp.mode == "full":
+            count["index_full"] += 1
+        elif sp.mode == "reindex":
+            count["reindex"] += 1
+    step = sum(per[n] * count[n] for n in per)
+    return per, count, step
 
-    fk.lib()
-    assert torch.cuda.is_available(), "no GPU visible"
-    cfg = CONFIGS[1]
-    topk, W = cfg.topk, cfg.window
-    pool_blocks = cfg.layers[0].pool_blocks
-    log(f"building workload {cfg.name} ({args.replicas} replicas)")
+
+def bench_decode(fk, cfg_id: int, steps: int, warmup: int, n_rep: int, use_graph: bool, per_call_timing: bool):
+    from synth import CONFIGS, make_decode_case
+    cfg = CONFIGS[cfg_id]
+    log(f"building {cfg.name} ({n_rep} replicas)")
     t0 = time.time()
     case = make_decode_case(cfg, device="cuda")
-    reps = build(case, fk, args.replicas)
-    B, H = case.B, cfg.H
+    reps = build_decode(case, fk, n_rep)
     log(f"built in {time.time() - t0:.1f}s")
-
     dev = "cuda"
+    B, H, topk = case.B, cfg.H, cfg.topk
     ctx = torch.tensor(case.ctx_len, dtype=torch.int32, device=dev)
     max_ctx = max(case.ctx_len)
-    ws_full = fk.workspace(fk.FN_INDEX_FULL, device=dev, B=B, max_ctx=max_ctx, topk=topk,
-                           pool_blocks=pool_blocks)
-    tk_full = torch.empty((B, topk), dtype=torch.int32, device=dev)
-    tk_re = torch.empty((B, topk), dtype=torch.int32, device=dev)
-    pool = torch.empty((B, pool_blocks), dtype=torch.int32, device=dev)
-    outs = [torch.empty((B, H, 512), dtype=torch.bfloat16, device=dev) for _ in range(3)]
-    lses = [torch.empty((B, H), dtype=torch.float32, device=dev) for _ in range(3)]
+    pool_blocks = max([sp.pool_blocks for sp in cfg.layers] + [0])
+    ws_full = fk.workspace(fk.FN_INDEX_FULL, device=dev, B=B, max_ctx=max_ctx, topk=topk, pool_blocks=pool_blocks)
+    tk_buf = [torch.empty((B, topk), dtype=torch.int32, device=dev) for _ in range(2)]
+    pool = torch.empty((B, max(pool_blocks, 1)), dtype=torch.int32, device=dev)
+    outs = [torch.empty((B, H, 512), dtype=torch.bfloat16, device=dev) for _ in cfg.layers]
+    lses = [torch.empty((B, H), dtype=torch.float32, device=dev) for _ in cfg.layers]
 
     def calls(r):
         R = reps[r]
-        L = R.layers
-        P = R.pair
-        return [
-            ("write_kv", lambda: fk.write_kv(R.cache, P["start"], P["x"], P["w"], P["k"])),
-            ("index_full", lambda: fk.index_full(R.cache, ctx, max_ctx, L[0]["q_idx"], L[0]["w_idx"], topk=topk,
-                                                 pool_blocks=pool_blocks, ws=ws_full, topk_idx=tk_full,
-                                                 pool=pool)),
-            ("sparse_decode", lambda: fk.sparse_decode(R.cache, ctx, L[0]["q"], tk_full, L[0]["swa"],
-                                                       out=outs[0], lse=lses[0])),
-            ("reindex", lambda: fk.reindex(R.cache, ctx, L[1]["q_idx"], L[1]["w_idx"], pool, topk=topk,
-                                           topk_idx=tk_re)),
-            ("sparse_decode", lambda: fk.sparse_decode(R.cache, ctx, L[1]["q"], tk_re, L[1]["swa"],
-                                                       out=outs[1], lse=lses[1])),
-            ("sparse_decode", lambda: fk.sparse_decode(R.cache, ctx, L[2]["q"], tk_re, L[2]["swa"],
-                                                       out=outs[2], lse=lses[2])),
-        ]
+        Wr = R.write
+        out = [("write_kv", lambda: fk.write_kv(R.cache, Wr["start"], Wr["x"], Wr["w"], Wr["k"]))]
+        cur = None
+        nxt = 0
+        for l, sp in enumerate(cfg.layers):
+            L = R.layers[l]
+            if sp.mode == "full":
+                tk = tk_buf[nxt]
+                nxt ^= 1
+                pb = sp.pool_blocks
+                out.append(("index_full", lambda L=L, tk=tk, pb=pb: fk.index_full(
+                    R.cache, ctx, max_ctx, L["q_idx"], L["w_idx"], topk=topk, pool_blocks=pb,
+                    cand_block=cfg.cand_block, ws=ws_full, topk_idx=tk, pool=pool if pb > 0 else None)))
+                cur = tk
+            elif sp.mode == "reindex":
+                tk = tk_buf[nxt]
+                nxt ^= 1
+                out.append(("reindex", lambda L=L, tk=tk: fk.reindex(R.cache, ctx, L["q_idx"], L["w_idx"], pool,
+                                                                     topk=topk, cand_block=cfg.cand_block,
+                                                                     topk_idx=tk)))
+                cur = tk
+            out.append(("sparse_decode", lambda L=L, tk=cur, l=l: fk.sparse_decode(
+                R.cache, ctx, L["q"], tk, L["swa"], out=outs[l], lse=lses[l])))
+        return out
 
     def run_step(r):
         for _, f in calls(r):
             f()
 
-    # eager warm-up (also sets kernel attributes outside any capture)
-    for r in range(len(reps)):
+    for r in range(len(reps)):          # eager warm-up (sets kernel attributes outside capture)
         run_step(r)
     torch.cuda.synchronize()
 
-    # ---- algorithmic bytes per step (formulas in DESIGN.md) ----
-    n_vis = case.n_vis
-    n_t = [min(topk, v) for v in n_vis]
-    n_pool = [min(pool_blocks * cfg.cand_block, v) for v in n_vis]
-    n_win = [min(W, L) for L in case.ctx_len]
-    by_write = sum(2 * 2 * 1024 + 128 + 4 + 306 for _ in range(B))
-    by_full = sum(v * BYTES_IDX + 520 + 4 * topk + 4 * pool_blocks for v in n_vis)
-    by_re = sum(p * BYTES_IDX + 520 + 4 * topk + 4 * pool_blocks for p in n_pool)
-    by_att = sum(t * BYTES_LAT + w * 1024 + 2 * H * 1024 + 4 * t + 4 * H for t, w in zip(n_t, n_win))
-    step_bytes = by_write + by_full + by_re + 3 * by_att
-    per_call_bytes = {"write_kv": by_write, "index_full": by_full, "reindex": by_re, "sparse_decode": by_att}
-
-    # ---- graphs: one per replica, each holding one whole step ----
+    per_bytes, count, step_bytes = decode_bytes(case)
     graphs = []
-    use_graph = not args.no_graph
     if use_graph:
         try:
             s = torch.cuda.Stream()
@@ -181,10 +205,9 @@ def main() -> int:
             for g in graphs:
                 g.replay()
             torch.cuda.synchronize()
-        except Exception as e:  # graph capture unavailable: time eager launches
+        except Exception as e:
             log(f"graph capture failed ({e!r}); timing eager launches")
-            use_graph = False
-            graphs = []
+            use_graph, graphs = False, []
 
     def step(i):
         if use_graph:
@@ -192,75 +215,28 @@ def main() -> int:
         else:
             run_step(i % len(reps))
 
-    for i in range(args.warmup):
+    for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
-    log(f"timing {args.steps} steps ({'graph' if use_graph else 'eager'})")
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     t_start = time.perf_counter()
     ev0.record()
-    for i in range(args.steps):
+    for i in range(steps):
         step(i)
     ev1.record()
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_start
-    ms_step = ev0.elapsed_time(ev1) / args.steps
-    ms_step_wall = t_wall * 1e3 / args.steps
-    ms = max(ms_step, ms_step_wall)
+    ms = max(ev0.elapsed_time(ev1) / steps, t_wall * 1e3 / steps)
     qps = B / (ms / 1e3)
     gbs = step_bytes / (ms / 1e3) / 1e9
-    log(f"{ms * 1e3:.1f} us/step, {qps:.0f} queries/s, {gbs:.0f} GB/s algorithmic")
+    log(f"{cfg.name}: {ms * 1e3:.1f} us/step, {qps:.0f} queries/s, {gbs:.0f} GB/s algorithmic")
 
-    # eager timing for reference
-    for i in range(4):
-        run_step(i % len(reps))
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    n_eager = max(10, args.steps // 4)
-    for i in range(n_eager):
-        run_step(i % len(reps))
-    e1.record()
-    torch.cuda.synchronize()
-    ms_eager = e0.elapsed_time(e1) / n_eager
-
-    # ---- per-call durations: timing events captured between the calls of a step ----
     per_call = {}
-    timing_mode = None
-    try:
-        names = [n for n, _ in calls(0)]
-        tg = []
-        evs_all = []
-        s = torch.cuda.Stream()
-        s.wait_stream(torch.cuda.current_stream())
-        for r in range(len(reps)):
-            evs = [torch.cuda.Event(enable_timing=True, external=True) for _ in range(len(names) + 1)]
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g, stream=s):
-                for k, (_, f) in enumerate(calls(r)):
-                    evs[k].record()
-                    f()
-                evs[-1].record()
-            tg.append(g)
-            evs_all.append(evs)
-        torch.cuda.current_stream().wait_stream(s)
-        acc = {n: [] for n in set(names)}
-        n_rounds = max(4, args.steps // (4 * len(reps)))
-        for rnd in range(n_rounds):
-            for r, g in enumerate(tg):
-                g.replay()
-                torch.cuda.synchronize()
-                evs = evs_all[r]
-                for k, n in enumerate(names):
-                    acc[n].append(evs[k].elapsed_time(evs[k + 1]))
-        per_call = {n: float(np.mean(v)) for n, v in acc.items()}
-        timing_mode = "graph-events"
-    except Exception as e:
-        log(f"in-graph timing events unavailable ({e!r}); averaging graph replays per call")
-        per_call = {}
-        try:
-            for name in ("write_kv", "index_full", "reindex", "sparse_decode"):
+    if per_call_timing:
+        # each call type alone: a graph holding that call once per replica, replayed 8 times
+        # (launched and timed on the current stream)
+        for name in [n for n in ("write_kv", "index_full", "reindex", "sparse_decode") if count[n] > 0]:
+            try:
                 s = torch.cuda.Stream()
                 s.wait_stream(torch.cuda.current_stream())
                 g = torch.cuda.CUDAGraph()
@@ -280,56 +256,159 @@ def main() -> int:
                 a1.record()
                 torch.cuda.synchronize()
                 per_call[name] = a0.elapsed_time(a1) / (8 * len(reps))
-            timing_mode = "graph-replay-average"
-        except Exception as e2:
-            log(f"per-call timing failed ({e2!r})")
-    calls_per_step = {"write_kv": 1, "index_full": 1, "reindex": 1, "sparse_decode": 3}
+            except Exception as e:
+                log(f"per-call timing of {name} failed ({e!r})")
+        log("per call (us): " + ", ".join(f"{n}={v * 1e3:.1f}" for n, v in per_call.items()))
     roofline = None
     if per_call:
-        totals = {n: per_call[n] * calls_per_step[n] for n in per_call}
+        totals = {n: per_call[n] * count[n] for n in per_call}
         dom = max(totals, key=totals.get)
-        achieved = per_call_bytes[dom] / (per_call[dom] / 1e3) / 1e9
+        achieved = per_bytes[dom] / (per_call[dom] / 1e3) / 1e9
         roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                    "avg_launch_us": round(per_call[dom] * 1e3, 2), "timing": timing_mode}
-        log("per call (us): " + ", ".join(f"{n}={v * 1e3:.1f}" for n, v in per_call.items()))
+                    "bytes_per_launch": per_bytes[dom], "avg_launch_us": round(per_call[dom] * 1e3, 2),
+                    "timing": "graph replay of that call, averaged per launch"}
+    return dict(case=case, reps=reps, ms=ms, qps=qps, gbs=gbs, step_bytes=step_bytes, per_call=per_call,
+                roofline=roofline, use_graph=use_graph, count=count, per_bytes=per_bytes)
 
-    # ---- CPU oracle on a bounded sample of the same workload ----
+
+# ----------------------------------------------------------------------------------
+# chunked prefill
+# ----------------------------------------------------------------------------------
+
+def bench_prefill(fk, steps: int, warmup: int):
+    from synth import CONFIGS, make_prefill_case
+    cfg = CONFIGS[3]
+    dev = "cuda"
+    log(f"building {cfg.name}")
+    case = make_prefill_case(cfg, dev)
+    gc = fk.PagedCache.allocate(case.n_pages, case.block_table, device=dev)
+    bt = case.block_table.to(dev)
+    for b in range(case.B):
+        x, w, k = case.prior_tokens(b)
+        sub = fk.PagedCache(gc.lat_codes, gc.lat_scales, gc.idx_codes, gc.idx_scales, bt[b:b + 1].contiguous())
+        fk.write_kv(sub, torch.zeros(1, dtype=torch.int32, device=dev), x[None].contiguous(), w[None].contiguous(),
+                    k[None].contiguous())
+        del x, w, k
+    ch = case.chunk()
+    prior = torch.full((case.B,), cfg.prior, dtype=torch.int32, device=dev)
+    start = ch["start_tok"].to(dev)
+    max_ctx = cfg.prior + cfg.C
+    out = torch.empty((case.B, cfg.C, cfg.H, 512), dtype=torch.bfloat16, device=dev)
+    tk = torch.empty((case.B, cfg.C, cfg.topk), dtype=torch.int32, device=dev)
+    ws = fk.workspace(fk.FN_PREFILL_CHUNK, device=dev, B=case.B, H=cfg.H, max_ctx=max_ctx, topk=cfg.topk, C=cfg.C)
+
+    def write():
+        fk.write_kv(gc, start, ch["x"], ch["w"], ch["k_idx"])
+
+    def attend():
+        fk.prefill_chunk(gc, prior, max_ctx, ch["q"], ch["q_idx"], ch["w_idx"], ch["local"], topk=cfg.topk,
+                         out=out, topk_idx=tk, ws=ws)
+
+    for _ in range(warmup):
+        write()
+        attend()
+    torch.cuda.synchronize()
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    t_w = t_a = 0.0
+    for _ in range(steps):
+        e[0].record()
+        write()
+        e[1].record()
+        attend()
+        e[2].record()
+        torch.cuda.synchronize()
+        t_w += e[0].elapsed_time(e[1])
+        t_a += e[1].elapsed_time(e[2])
+    ms_w, ms_a = t_w / steps, t_a / steps
+    ms = ms_w + ms_a
+    nv = (cfg.prior + np.arange(cfg.C) + 1) // 2
+    n_win = np.minimum(cfg.window, cfg.prior + np.arange(cfg.C) + 1)
+    fl_idx = case.B * float(np.sum(nv)) * 4 * 64 * 2
+    fl_att = case.B * float(np.sum(cfg.H * (np.minimum(nv, cfg.topk) + n_win) * 512 * 2 * 2))
+    tfs = (fl_idx + fl_att) / (ms_a / 1e3) / 1e12
+    toks = case.B * cfg.C / (ms / 1e3)
+    log(f"{cfg.name}: write {ms_w * 1e3:.0f} us + prefill {ms_a * 1e3:.0f} us; {toks:.0f} tokens/s, "
+        f"{tfs:.1f} TFLOP/s")
+    return {"workload": cfg.name, "metric": "prefill query tokens/s", "value": round(toks, 1),
+            "unit": "tokens/s", "ms_per_step": round(ms, 4), "ms_write": round(ms_w, 4),
+            "ms_index_attention": round(ms_a, 4), "flop_indexer": fl_idx, "flop_attention": fl_att,
+            "roofline": {"bound": "mfma", "achieved": round(tfs, 2), "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
+                         "frac": round(tfs / MFMA_BF16_PEAK_TFS, 4), "traffic": None},
+            "dtype": "bf16", "steps": steps, "warmup": warmup}
+
+
+# ----------------------------------------------------------------------------------
+
+def main() -> int:
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this build runs on one GPU only (the path has no multi-GPU sharding); "
+              f"got --gpus {args.gpus}, WORLD_SIZE={world}", file=sys.stderr)
+        return 2
+    import fp4_kv_cache_write_amd as fk
+    fk.lib()
+    assert torch.cuda.is_available(), "no GPU visible"
+
+    if args.workload == "c3":
+        r = bench_prefill(fk, max(2, args.steps // 40), max(1, args.warmup // 10))
+        print(json.dumps(dict(r, n_gpus=1, higher_is_better=True, data="synthetic", vs_baseline=None,
+                              config={"workload": r["workload"]})), flush=True)
+        return 0
+
+    cfg_id = {"c1": 1, "c2": 2, "c4": 4}[args.workload]
+    d = bench_decode(fk, cfg_id, args.steps, args.warmup, args.replicas, not args.no_graph, True)
+    case = d["case"]
+    cfg = case.cfg
+    secondary = {}
+    if args.workload == "c1" and not args.no_secondary:
+        c2 = bench_decode(fk, 2, max(20, args.steps // 4), max(5, args.warmup // 4), 4, not args.no_graph, True)
+        secondary["c2_b8_ctx1m"] = {
+            "workload": c2["case"].cfg.name, "value": round(c2["qps"], 1), "unit": "queries/s",
+            "ms_per_step": round(c2["ms"], 5), "achieved_gbs": round(c2["gbs"], 1),
+            "frac_hbm_peak": round(c2["gbs"] / HBM_PEAK_GBS, 4), "algorithmic_bytes_per_step": c2["step_bytes"],
+            "per_call_us": {n: round(v * 1e3, 2) for n, v in c2["per_call"].items()}, "roofline": c2["roofline"]}
+        del c2
+        torch.cuda.empty_cache()
+        secondary["c3_prefill"] = bench_prefill(fk, 5, 2)
+        torch.cuda.empty_cache()
+
     cpu = None
-    if not args.no_cpu_baseline:
-        cpu = cpu_baseline(case, reps[0], topk, W, pool_blocks, args.cpu_seqs)
+    if args.workload == "c1" and not args.no_cpu_baseline:
+        cpu = cpu_baseline(case, d["reps"][0], cfg.topk, cfg.window, args.cpu_seqs)
 
     line = {
         "metric": METRIC,
-        "value": round(qps, 1),
+        "value": round(d["qps"], 1),
         "unit": "queries/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms, 5),
+        "ms_per_step": round(d["ms"], 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": cfg.name, "B": B, "ctx_tokens": max_ctx, "entries_per_seq": max(n_vis),
-                   "H": H, "topk": topk, "window": W, "pool_blocks": pool_blocks,
-                   "cand_block": cfg.cand_block, "layers": "full,reindex,reuse",
-                   "pair_write_per_step": True, "replicas": len(reps),
-                   "launch": "hip-graph" if use_graph else "eager"},
-        "algorithmic_bytes_per_step": step_bytes,
-        "achieved_gbs": round(gbs, 1),
-        "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
-        "ms_per_step_eager": round(ms_eager, 5),
-        "per_call_us": {n: round(v * 1e3, 2) for n, v in per_call.items()},
-        "roofline": roofline,
+        "config": {"workload": cfg.name, "B": case.B, "ctx_tokens": max(case.ctx_len),
+                   "entries_per_seq": max(case.n_vis), "H": cfg.H, "topk": cfg.topk, "window": cfg.window,
+                   "pool_blocks": max([sp.pool_blocks for sp in cfg.layers] + [0]), "cand_block": cfg.cand_block,
+                   "layers": ",".join(sp.mode for sp in cfg.layers), "write_per_step": True,
+                   "replicas": len(d["reps"]), "launch": "hip-graph" if d["use_graph"] else "eager"},
+        "algorithmic_bytes_per_step": d["step_bytes"],
+        "achieved_gbs": round(d["gbs"], 1),
+        "frac_hbm_peak": round(d["gbs"] / HBM_PEAK_GBS, 4),
+        "per_call_us": {n: round(v * 1e3, 2) for n, v in d["per_call"].items()},
+        "roofline": d["roofline"],
         "cpu_baseline": cpu,
+        "secondary": secondary or None,
     }
     print(json.dumps(line), flush=True)
     return 0
 
 
-def cpu_baseline(case, rep, topk, W, pool_blocks, n_seqs, min_seconds=10.0):
+def cpu_baseline(case, rep, topk, W, n_seqs, min_seconds=10.0):
     """Time the NumPy oracle on `n_seqs` sequences of the same inputs (host cores)."""
     from oracle import OracleCache
     from oracle.schedule import run_decode

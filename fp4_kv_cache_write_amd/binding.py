@@ -227,7 +227,8 @@ def sparse_decode(cache: PagedCache, ctx_len: torch.Tensor, q: torch.Tensor, top
 def prefill_chunk(cache: PagedCache, prior_len: torch.Tensor, max_ctx: int, q: torch.Tensor,
                   q_idx: torch.Tensor, w_idx: torch.Tensor, local: torch.Tensor, topk: int = 512,
                   sm_scale: Optional[float] = None, want_topk: bool = True,
-                  out: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None, stream=None):
+                  out: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None,
+                  topk_idx: Optional[torch.Tensor] = None, stream=None):
     B, C, H = q.shape[0], q.shape[1], q.shape[2]
     W = local.shape[1] - C + 1
     _need(prior_len, torch.int32, "prior_len", (B,))
@@ -239,7 +240,11 @@ def prefill_chunk(cache: PagedCache, prior_len: torch.Tensor, max_ctx: int, q: t
         sm_scale = D_LATENT ** -0.5
     if out is None:
         out = torch.empty((B, C, H, D_LATENT), dtype=torch.bfloat16, device=q.device)
-    tk = torch.empty((B, C, topk), dtype=torch.int32, device=q.device) if want_topk else None
+    if topk_idx is not None:
+        _need(topk_idx, torch.int32, "topk_idx", (B, C, topk))
+        tk = topk_idx
+    else:
+        tk = torch.empty((B, C, topk), dtype=torch.int32, device=q.device) if want_topk else None
     if ws is None:
         ws = workspace(FN_PREFILL_CHUNK, device=q.device, B=B, H=H, max_ctx=max_ctx, topk=topk, C=C)
     wsb = ws.numel() if ws is not None else 0
