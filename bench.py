@@ -54,6 +54,7 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seqs", type=int, default=2, help="sequences in the oracle's timed sample")
     p.add_argument("--no-graph", action="store_true", help="time eager launches instead of graph replay")
+    p.add_argument("--serial", action="store_true", help="issue every call of a step on one stream")
     return p.parse_args()
 
 
@@ -136,7 +137,8 @@ def decode_bytes(case):
     return per, count, step
 
 
-def bench_decode(fk, cfg_id: int, steps: int, warmup: int, n_rep: int, use_graph: bool, per_call_timing: bool):
+def bench_decode(fk, cfg_id: int, steps: int, warmup: int, n_rep: int, use_graph: bool, per_call_timing: bool,
+                 concurrent: bool = True):
     from synth import CONFIGS, make_decode_case
     cfg = CONFIGS[cfg_id]
     log(f"building {cfg.name} ({n_rep} replicas)")
@@ -182,9 +184,30 @@ def bench_decode(fk, cfg_id: int, steps: int, warmup: int, n_rep: int, use_graph
                 R.cache, ctx, L["q"], tk, L["swa"], out=outs[l], lse=lses[l])))
         return out
 
+    # The selector calls (write, Full, Reindex) form one chain on the launching stream;
+    # each layer's attention needs only its selector's output, so it is forked onto a
+    # stream of its own and joined back at the end of the step.  Attention of layer l
+    # then runs beside the next layer's Reindex and beside the other layers' attention.
+    side = [torch.cuda.Stream() for _ in cfg.layers] if concurrent else []
+
     def run_step(r):
-        for _, f in calls(r):
-            f()
+        if not concurrent:
+            for _, f in calls(r):
+                f()
+            return
+        main = torch.cuda.current_stream()
+        layer = 0
+        for name, f in calls(r):
+            if name == "sparse_decode":
+                s = side[layer]
+                s.wait_stream(main)
+                with torch.cuda.stream(s):
+                    f()
+                layer += 1
+            else:
+                f()
+        for s in side:
+            main.wait_stream(s)
 
     for r in range(len(reps)):          # eager warm-up (sets kernel attributes outside capture)
         run_step(r)
@@ -358,12 +381,13 @@ def main() -> int:
         return 0
 
     cfg_id = {"c1": 1, "c2": 2, "c4": 4}[args.workload]
-    d = bench_decode(fk, cfg_id, args.steps, args.warmup, args.replicas, not args.no_graph, True)
+    d = bench_decode(fk, cfg_id, args.steps, args.warmup, args.replicas, not args.no_graph, True, not args.serial)
     case = d["case"]
     cfg = case.cfg
     secondary = {}
     if args.workload == "c1" and not args.no_secondary:
-        c2 = bench_decode(fk, 2, max(20, args.steps // 4), max(5, args.warmup // 4), 4, not args.no_graph, True)
+        c2 = bench_decode(fk, 2, max(20, args.steps // 4), max(5, args.warmup // 4), 4, not args.no_graph, True,
+                          not args.serial)
         secondary["c2_b8_ctx1m"] = {
             "workload": c2["case"].cfg.name, "value": round(c2["qps"], 1), "unit": "queries/s",
             "ms_per_step": round(c2["ms"], 5), "achieved_gbs": round(c2["gbs"], 1),
@@ -395,7 +419,8 @@ def main() -> int:
                    "entries_per_seq": max(case.n_vis), "H": cfg.H, "topk": cfg.topk, "window": cfg.window,
                    "pool_blocks": max([sp.pool_blocks for sp in cfg.layers] + [0]), "cand_block": cfg.cand_block,
                    "layers": ",".join(sp.mode for sp in cfg.layers), "write_per_step": True,
-                   "replicas": len(d["reps"]), "launch": "hip-graph" if d["use_graph"] else "eager"},
+                   "replicas": len(d["reps"]), "launch": ("hip-graph" if d["use_graph"] else "eager") +
+                   ("; each layer's attention on its own forked stream" if not args.serial else "; one stream")},
         "algorithmic_bytes_per_step": d["step_bytes"],
         "achieved_gbs": round(d["gbs"], 1),
         "frac_hbm_peak": round(d["gbs"] / HBM_PEAK_GBS, 4),

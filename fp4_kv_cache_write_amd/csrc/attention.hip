@@ -8,58 +8,53 @@
 // entries and the layer's window KV together); [P3] "DeepSeek V4.1 Flash
 // architecture..." (scores -> weights summing to 1 -> weighted sum of values).
 //
-// Decomposition: one workgroup per (query, group of 16 heads); blockIdx is mapped
-// so that the head groups of one query, and neighbouring queries of one sequence,
-// run on the same XCD and share its L2 for the gathered rows.  Four waves, one per SIMD, 512 registers each.  All row data
-// reaches LDS through global_load_lds_dwordx4 (no registers, everything in flight at
-// once), in two phases that reuse one 136 KB staging area:
-//   A. the window rows (bf16, 1 KB each, pitch 1040 B) -- they need no index
-//      lookups, so their copies start at once while the selected entries' row ids
-//      are resolved through the page table;
-//   B. the selected FP4 rows (256 code bytes + 16 scale bytes, pitch 272 B), up to
-//      512 per pass.
-// Within a phase each wave first computes the scores of all its 32-row tiles, takes
-// one maximum, then accumulates P.V -- the accumulators are rescaled at most once
-// per phase, so they never leave the MFMA accumulator registers inside the loops.
-// The waves' softmax states and accumulators are merged through LDS at the end.
+// Decomposition: one workgroup per (query, group of 16 heads), 8 waves (two per
+// SIMD).  blockIdx is mapped so that the head groups of a query, and neighbouring
+// queries of a sequence, run on one XCD and share its L2 for the gathered rows.
 //
-// Per 32-row tile:
-//   QK  D[row][head] via 16x16x32 bf16 MFMA; A = rows (lane: row l%16, dims
-//       128g+8s..+7 at k-step s, g = l/16), B = q (lane: head l%16, same dims).
-//       FP4 rows become bf16 operands through the hardware convert with the e8m0
-//       scale folded in (exact).
-//   P   the lane then holds rows {4g..4g+3, 16+4g..16+4g+3} of head l%16 --
-//       exactly the K-slots of the P operand of the PV MFMA, so P needs no
-//       cross-lane movement.  P enters as a bf16 head plus a bf16 residual (two
-//       MFMAs): plain bf16 weights (8 bits) would use most of the 2e-3 error budget
-//       on flat softmaxes.
-//   PV  O[head][dim] += P . R via 16x16x32 bf16 MFMA, n-tile t holding dims 32n+t
-//       for lane column n, so each lane reads one 16-byte run per row and
-//       transposes register pairs (v_perm) into the B operand.
+// Rows are processed in batches that live in one of two 68 KB LDS buffers: window
+// batches of 64 bf16 rows (pitch 1040 B), then FP4 batches of 256 rows (256 code
+// bytes + 16 scale bytes, pitch 272 B).  All row data reaches LDS through
+// global_load_lds_dwordx4 (no registers); the copy of batch k+1 is issued as soon as
+// batch k's data has arrived, so it overlaps batch k's arithmetic.  Per batch:
+//   QK  wave w scores 32-row tile w: D[row][head] via 16x16x32 bf16 MFMAs, A = rows
+//       (lane: row l%16, dims 128g+8s..+7 at k-step s, g = l/16; FP4 rows become
+//       bf16 through the hardware convert with the e8m0 scale folded in, exact),
+//       B = q (lane: head l%16, same dims; q stays in registers).
+//   max the batch maximum of every head goes through LDS, so all waves hold the
+//       same running maximum; accumulators are rescaled once per batch.
+//   P   the scoring wave turns its 32 scores per head into the P operand of the PV
+//       MFMA -- a bf16 head plus a bf16 residual, since plain bf16 weights would use
+//       most of the 2e-3 error budget on flat softmaxes -- and parks it in LDS.  The
+//       lane's scores are already the K-slots of that operand (rows 4g..4g+3 and
+//       16+4g..16+4g+3 of head l%16), so no lane exchange is needed.
+//   PV  every wave accumulates O[16 heads][its 64 dims] over all tiles of the batch:
+//       n-tile t of lane column n is dim 64w + 4n + t, so a lane reads 4 adjacent
+//       dims (2 FP4 bytes or 8 bf16 bytes) of each of its 8 rows and v_perm pairs
+//       rows into the B operand.  Dims are split across waves, so no wave merges
+//       accumulators with another and each wave writes its own slice of the output.
 #include "common.h"
 #include "internal.h"
 
 namespace csa2 {
 namespace {
 
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
-constexpr int kRowB = 272;          // FP4 row in LDS: 256 code bytes then 16 scale bytes
-constexpr int kWinB = 1040;         // window row in LDS: 1024 bytes + 16 pad
-constexpr int kBatchRows = 512;     // FP4 rows staged per pass
-constexpr int kWinBatch = 128;      // window rows staged per pass
-constexpr int kMaxT = 4;            // 32-row tiles per wave per pass
-constexpr int kQStride = 520;       // bf16 per head row of q in LDS (512 + pad)
-constexpr int kOStride = 576;       // floats per head row of a wave's merge slot (36 per 32 dims)
-constexpr int kOffRows = 0;
-constexpr int kStageBytes = kBatchRows * kRowB;           // 139264 >= kWinBatch * kWinB
-constexpr int kOffQ = kStageBytes;                        // spare: part of the merge slots
-constexpr int kOffRowId = kOffQ + 16 * kQStride * 2;      // 155904
-constexpr int kOffSm = kOffRowId + kBatchRows * 4;        // 157952
-constexpr int kLdsBytes = kOffSm + (2 * kWaves * 16 + 32) * 4;
-static_assert(kWinBatch * kWinB <= kStageBytes, "window batch fits the staging area");
-static_assert(kBatchRows / 32 <= kWaves * kMaxT && kWinBatch / 32 <= kWaves * kMaxT, "tiles per wave");
-static_assert(kWaves * 16 * kOStride * 4 <= kOffRowId, "merge slots alias the staging and q areas");
+constexpr int kRowB = 272;           // FP4 row in LDS: 256 code bytes then 16 scale bytes
+constexpr int kWinB = 1040;          // window row in LDS: 1024 bytes + 16 pad
+constexpr int kFp4Batch = 256;       // FP4 rows per batch (8 tiles)
+constexpr int kWinBatch = 64;        // window rows per batch (2 tiles)
+constexpr int kBufBytes = kFp4Batch * kRowB;              // 69632 >= kWinBatch * kWinB
+constexpr int kPBytes = 32;                               // per lane and tile: P head + residual
+constexpr int kOffBuf = 0;
+constexpr int kOffP = 2 * kBufBytes;                      // [8 tiles][64 lanes][32 B]
+constexpr int kOffRowId = kOffP + 8 * 64 * kPBytes;       // [2][256] int32
+constexpr int kOffMax = kOffRowId + 2 * kFp4Batch * 4;    // [8 waves][16] float
+constexpr int kOffL = kOffMax + kWaves * 16 * 4;          // [8 waves][16] float
+constexpr int kLdsBytes = kOffL + kWaves * 16 * 4;
+static_assert(kWinBatch * kWinB <= kBufBytes, "window batch fits a buffer");
+static_assert(kFp4Batch / 32 == kWaves, "one FP4 tile per wave");
 static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
 
 constexpr float kLog2e = 1.4426950408889634f;
@@ -89,11 +84,17 @@ __device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) { return __b
 template <class T>
 __device__ __forceinline__ T lds_ld(const uint8_t* p) { return *reinterpret_cast<const T*>(p); }
 
+// Row of K-slot j for lane group g: rows 4g..4g+3, then 16+4g..16+4g+3.
+__device__ __forceinline__ int slot_row(int g, int j) { return j < 4 ? 4 * g + j : 16 + 4 * g + (j - 4); }
+
+// Window slot w (position t-W+1+w) holds a row, i.e. w < W and the position is >= 0.
+__device__ __forceinline__ bool win_valid(int W, int t, int w) { return w < W && t - (W - 1) + w >= 0; }
+
 // P operand (bf16 head + bf16 residual) of this lane's 8 scores (log2 units, -inf =
 // absent) against the running max m; adds the weights to l_part.
-__device__ __forceinline__ void make_p(const float (&z)[8], float m, float& l_part, bf16x8& pa_hi, bf16x8& pa_lo) {
+__device__ __forceinline__ void make_p(const float (&z)[8], float m, float& l_part, u32x4& phi, u32x4& plo) {
   const float mb = (m == -INFINITY) ? 0.f : m;
-  uint32_t phi[4], plo[4];
+  uint32_t h[4], r[4];
 #pragma unroll
   for (int j = 0; j < 8; j += 2) {
     const float p0 = exp2f(z[j] - mb), p1 = exp2f(z[j + 1] - mb);
@@ -101,36 +102,14 @@ __device__ __forceinline__ void make_p(const float (&z)[8], float m, float& l_pa
     const uint32_t h0 = f32_to_bf16_rne(p0), h1 = f32_to_bf16_rne(p1);
     const uint32_t r0 = f32_to_bf16_rne(p0 - bf16_to_f32(h0));
     const uint32_t r1 = f32_to_bf16_rne(p1 - bf16_to_f32(h1));
-    phi[j >> 1] = h0 | (h1 << 16);
-    plo[j >> 1] = r0 | (r1 << 16);
+    h[j >> 1] = h0 | (h1 << 16);
+    r[j >> 1] = r0 | (r1 << 16);
   }
-  pa_hi = __builtin_bit_cast(bf16x8, u32x4{phi[0], phi[1], phi[2], phi[3]});
-  pa_lo = __builtin_bit_cast(bf16x8, u32x4{plo[0], plo[1], plo[2], plo[3]});
+  phi = u32x4{h[0], h[1], h[2], h[3]};
+  plo = u32x4{r[0], r[1], r[2], r[3]};
 }
 
-// B operands of 8 n-tiles t0..t0+7 from 8 rows' bf16 pairs: d[k][j] holds dims
-// (t0+2k, t0+2k+1) of row-slot j.  Eight independent accumulator chains, P head
-// first, then P residual.
-__device__ __forceinline__ void pv_quad(f32x4 (&acc)[32], int t0, bf16x8 pa_hi, bf16x8 pa_lo,
-                                        const uint32_t (&d)[4][8]) {
-  bf16x8 bf[8];
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    bf[2 * k] = __builtin_bit_cast(bf16x8, u32x4{pack_lo(d[k][0], d[k][1]), pack_lo(d[k][2], d[k][3]),
-                                                 pack_lo(d[k][4], d[k][5]), pack_lo(d[k][6], d[k][7])});
-    bf[2 * k + 1] = __builtin_bit_cast(bf16x8, u32x4{pack_hi(d[k][0], d[k][1]), pack_hi(d[k][2], d[k][3]),
-                                                     pack_hi(d[k][4], d[k][5]), pack_hi(d[k][6], d[k][7])});
-  }
-#pragma unroll
-  for (int k = 0; k < 8; ++k) acc[t0 + k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa_hi, bf[k], acc[t0 + k], 0, 0, 0);
-#pragma unroll
-  for (int k = 0; k < 8; ++k) acc[t0 + k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa_lo, bf[k], acc[t0 + k], 0, 0, 0);
-}
-
-// Row slot of K-slot j for lane group g: rows 4g..4g+3, then 16+4g..16+4g+3.
-__device__ __forceinline__ int slot_row(int g, int j) { return j < 4 ? 4 * g + j : 16 + 4 * g + (j - 4); }
-
-// Scores of an FP4 tile staged in LDS (rows base..base+31 of the batch).
+// Scores of the FP4 tile at row `base` of the batch in LDS.
 __device__ __forceinline__ void fp4_qk(const uint8_t* rows, const int32_t* rowid, int nrows, int base,
                                        const u32x4 (&qf)[16], float scale_log2, float (&z)[8]) {
   const int lane = threadIdx.x & 63;
@@ -153,7 +132,7 @@ __device__ __forceinline__ void fp4_qk(const uint8_t* rows, const int32_t* rowid
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const bf16x8 qv = __builtin_bit_cast(bf16x8, qf[4 * c + k]);
-      const int e = k & 1;   // two partial sums per row-tile keep four MFMA chains in flight
+      const int e = k & 1;   // two partial sums per row half keep four MFMA chains in flight
       sa[e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, fp4x8_to_bf16x8(cd0[c][k], sc0)),
                                                       qv, sa[e], 0, 0, 0);
       sa[2 + e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
@@ -169,36 +148,7 @@ __device__ __forceinline__ void fp4_qk(const uint8_t* rows, const int32_t* rowid
   }
 }
 
-// P.V of an FP4 tile staged in LDS: lane (n, g) reads the 16-byte MX block n of its 8 rows.
-__device__ __forceinline__ void fp4_pv(const uint8_t* rows, int base, bf16x8 pa_hi, bf16x8 pa_lo, f32x4 (&acc)[32]) {
-  const int lane = threadIdx.x & 63;
-  const int n = lane & 15, g = lane >> 4;
-  u32x4 cd[8];
-  float sc[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const uint8_t* rp = rows + (base + slot_row(g, j)) * kRowB;
-    cd[j] = lds_ld<u32x4>(rp + 16 * n);
-    sc[j] = e8m0_scale(rp[256 + n]);
-  }
-#pragma unroll
-  for (int qd = 0; qd < 4; ++qd) {
-    uint32_t d[4][8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      d[0][j] = fp4x2_to_bf16x2<0>(cd[j][qd], sc[j]);
-      d[1][j] = fp4x2_to_bf16x2<1>(cd[j][qd], sc[j]);
-      d[2][j] = fp4x2_to_bf16x2<2>(cd[j][qd], sc[j]);
-      d[3][j] = fp4x2_to_bf16x2<3>(cd[j][qd], sc[j]);
-    }
-    pv_quad(acc, 8 * qd, pa_hi, pa_lo, d);
-  }
-}
-
-// Window slot w (position t-W+1+w) holds a row, i.e. w < W and the position is >= 0.
-__device__ __forceinline__ bool win_valid(int W, int t, int w) { return w < W && t - (W - 1) + w >= 0; }
-
-// Scores of a window tile staged in LDS (rows base..base+31 of the window batch w0..).
+// Scores of the window tile at row `base` of the batch in LDS (window slots w0 + row).
 __device__ __forceinline__ void win_qk(const uint8_t* wrows, int W, int t, int w0, int base, const u32x4 (&qf)[16],
                                        float scale_log2, float (&z)[8]) {
   const int lane = threadIdx.x & 63;
@@ -210,7 +160,7 @@ __device__ __forceinline__ void win_qk(const uint8_t* wrows, int W, int t, int w
   for (int half = 0; half < 2; ++half) {
     u32x4 r0[8], r1[8];
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {          // all LDS reads of the half first
+    for (int s = 0; s < 8; ++s) {
       r0[s] = lds_ld<u32x4>(r0p + 16 * (8 * half + s));
       r1[s] = lds_ld<u32x4>(r1p + 16 * (8 * half + s));
     }
@@ -230,70 +180,31 @@ __device__ __forceinline__ void win_qk(const uint8_t* wrows, int W, int t, int w
   }
 }
 
-// P.V of a window tile staged in LDS: lane (n, g) reads dims 32n..32n+31 of its 8 rows.
-__device__ __forceinline__ void win_pv(const uint8_t* wrows, int base, bf16x8 pa_hi, bf16x8 pa_lo, f32x4 (&acc)[32]) {
-  const int lane = threadIdx.x & 63;
-  const int n = lane & 15, g = lane >> 4;
+// PV for this wave's 64 dims from 8 rows given as pairs d01[j] = dims (4n, 4n+1),
+// d23[j] = dims (4n+2, 4n+3) of row slot j: n-tile t holds dim 4n + t.
+__device__ __forceinline__ void pv4(f32x4 (&acc)[4], const uint32_t (&d01)[8], const uint32_t (&d23)[8], bf16x8 ph,
+                                    bf16x8 pl) {
+  bf16x8 bf[4];
+  bf[0] = __builtin_bit_cast(bf16x8, u32x4{pack_lo(d01[0], d01[1]), pack_lo(d01[2], d01[3]),
+                                           pack_lo(d01[4], d01[5]), pack_lo(d01[6], d01[7])});
+  bf[1] = __builtin_bit_cast(bf16x8, u32x4{pack_hi(d01[0], d01[1]), pack_hi(d01[2], d01[3]),
+                                           pack_hi(d01[4], d01[5]), pack_hi(d01[6], d01[7])});
+  bf[2] = __builtin_bit_cast(bf16x8, u32x4{pack_lo(d23[0], d23[1]), pack_lo(d23[2], d23[3]),
+                                           pack_lo(d23[4], d23[5]), pack_lo(d23[6], d23[7])});
+  bf[3] = __builtin_bit_cast(bf16x8, u32x4{pack_hi(d23[0], d23[1]), pack_hi(d23[2], d23[3]),
+                                           pack_hi(d23[4], d23[5]), pack_hi(d23[6], d23[7])});
 #pragma unroll
-  for (int ch = 0; ch < 4; ++ch) {   // dims 32n + 8ch .. +7
-    uint32_t d[4][8];
+  for (int t = 0; t < 4; ++t) acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph, bf[t], acc[t], 0, 0, 0);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const u32x4 v = lds_ld<u32x4>(wrows + (base + slot_row(g, j)) * kWinB + 64 * n + 16 * ch);
-      d[0][j] = v.x;
-      d[1][j] = v.y;
-      d[2][j] = v.z;
-      d[3][j] = v.w;
-    }
-    pv_quad(acc, 8 * ch, pa_hi, pa_lo, d);
-  }
-}
-
-// Raise the running max of head l%16 to cover this phase's scores; rescales the
-// accumulators (output head 4g+i's factor comes from lane 4g+i) only when needed.
-__device__ __forceinline__ void phase_max(const float (&z)[kMaxT][8], float& m_run, float& l_part,
-                                          f32x4 (&acc)[32]) {
-  const int lane = threadIdx.x & 63, g = lane >> 4;
-  float tmax = -INFINITY;
-#pragma unroll
-  for (int i = 0; i < kMaxT; ++i) {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) tmax = fmaxf(tmax, z[i][j]);
-  }
-  tmax = fmaxf(tmax, __shfl_xor(tmax, 16, kWave));
-  tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
-  const bool had = m_run > -INFINITY;   // accumulators hold weights only after a finite max
-  float fac = 1.f;
-  if (tmax > m_run) {
-    fac = had ? exp2f(m_run - tmax) : 0.f;
-    l_part *= fac;
-    m_run = tmax;
-  }
-  float fo[4];
-  bool any = false;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    fo[i] = __shfl(fac, 4 * g + i, kWave);
-    const float mh = __shfl(had ? 1.f : 0.f, 4 * g + i, kWave);
-    any = any || (fo[i] != 1.f && mh != 0.f);
-  }
-  if (__builtin_amdgcn_read_exec() && __any(any)) {
-#pragma unroll
-    for (int tt = 0; tt < 32; ++tt) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) acc[tt][i] *= fo[i];
-    }
-  }
+  for (int t = 0; t < 4; ++t) acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, bf[t], acc[t], 0, 0, 0);
 }
 
 __global__ __launch_bounds__(kThreads) void sparse_decode_kernel(DecArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-  uint8_t* stage = lds + kOffRows;
-  int32_t* rowid = reinterpret_cast<int32_t*>(lds + kOffRowId);
-  float* m_w = reinterpret_cast<float*>(lds + kOffSm);
-  float* l_w = m_w + kWaves * 16;
-  float* m_g = l_w + kWaves * 16;
-  float* l_g = m_g + 16;
+  uint8_t* plds = lds + kOffP;
+  int32_t* rowid_all = reinterpret_cast<int32_t*>(lds + kOffRowId);
+  float* m_part = reinterpret_cast<float*>(lds + kOffMax);
+  float* l_w = reinterpret_cast<float*>(lds + kOffL);
 
   // XCD-aware mapping: consecutive workgroup ids go to different XCDs; XCD x takes
   // the contiguous query range [x * q_per_xcd, (x+1) * q_per_xcd), all head groups.
@@ -316,224 +227,236 @@ __global__ __launch_bounds__(kThreads) void sparse_decode_kernel(DecArgs a) {
   const int n_vis = (int)(L >> 1);
   const int t = (int)L - 1;
   const uint16_t* win_b = a.win + (int64_t)b * (a.prefill ? a.W - 1 + a.C : a.W) * CSA2_D_LATENT;
+  const int32_t* tk = a.topk_idx + qi * a.topk;
+  const int32_t* bt = a.block_table + (int64_t)b * a.max_pages;
 
-  // window batch: LDS chunk c (16 bytes) = piece c%65 of row c/65 (piece 64 = pad)
-  auto stage_window = [&](int w0, int nw) {
-    const int chunks = nw * 65;
-    for (int ins = wid; ins * 64 < chunks; ins += kWaves) {
-      const int c = ins * 64 + lane;
-      const int r = c / 65, piece = c - r * 65;
-      if (c < chunks && piece < 64 && win_valid(a.W, t, w0 + r)) {
-        const int pos = t - (a.W - 1) + w0 + r;
-        const int row = a.prefill ? ci + w0 + r : pos % a.W;
-        const uint16_t* src = win_b + (int64_t)row * CSA2_D_LATENT + 8 * piece;
-        __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src), stage + ins * 1024, 16, 0, 0);
+  const int n_wb = (a.W + kWinBatch - 1) / kWinBatch;
+  const int n_fb = a.topk > 0 ? (a.topk + kFp4Batch - 1) / kFp4Batch : 0;
+  const int nb = n_wb + n_fb;
+
+  // row ids of FP4 batch f into slot f % 2 (entry ids first, then their pages)
+  auto resolve_rows = [&](int f) {
+    const int r0 = f * kFp4Batch;
+    const int nrows = min(a.topk - r0, kFp4Batch);
+    int32_t* rowid = rowid_all + (f & 1) * kFp4Batch;
+    for (int i = tid; i < kFp4Batch; i += kThreads) {
+      int r = -1;
+      if (i < nrows) {
+        const int e = tk[r0 + i];
+        if (e >= 0 && e < n_vis && (e >> 6) < a.max_pages) {
+          const int p = bt[e >> 6];
+          if (p >= 0 && p < a.n_pages) r = p * CSA2_PAGE + (e & (CSA2_PAGE - 1));
+        }
       }
+      rowid[i] = r;
     }
   };
-  // FP4 batch: LDS chunk c = piece c%17 of row c/17 (16 code pieces, then the scales).
-  // Row ids of 8 copy instructions are read from LDS before any copy is issued.
-  auto stage_fp4 = [&](int nrows) {
-    const int chunks = nrows * 17;
-    const int n_ins = (chunks + 63) >> 6;
-    for (int i0 = wid; i0 < n_ins; i0 += 8 * kWaves) {
-      int rid[8], piece[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int c = (i0 + u * kWaves) * 64 + lane;
-        const int r = c / 17;
-        piece[u] = c - r * 17;
-        rid[u] = c < chunks ? rowid[r] : -1;
+  // copies of batch k into buffer k % 2
+  auto issue = [&](int k) {
+    uint8_t* buf = lds + kOffBuf + (k & 1) * kBufBytes;
+    if (k < n_wb) {
+      // window: LDS chunk c (16 bytes) = piece c%65 of row c/65 (piece 64 = pad)
+      const int w0 = k * kWinBatch;
+      const int nw = min(a.W - w0, kWinBatch);
+      const int chunks = nw * 65;
+      for (int ins = wid; ins * 64 < chunks; ins += kWaves) {
+        const int c = ins * 64 + lane;
+        const int r = c / 65, piece = c - r * 65;
+        if (c < chunks && piece < 64 && win_valid(a.W, t, w0 + r)) {
+          const int pos = t - (a.W - 1) + w0 + r;
+          const int row = a.prefill ? ci + w0 + r : pos % a.W;
+          const uint16_t* src = win_b + (int64_t)row * CSA2_D_LATENT + 8 * piece;
+          __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src), buf + ins * 1024, 16, 0, 0);
+        }
       }
+    } else {
+      // FP4: LDS chunk c = piece c%17 of row c/17 (16 code pieces, then the scales)
+      const int f = k - n_wb;
+      const int nrows = min(a.topk - f * kFp4Batch, kFp4Batch);
+      const int32_t* rowid = rowid_all + (f & 1) * kFp4Batch;
+      const int chunks = nrows * 17;
+      const int n_ins = (chunks + 63) >> 6;
+      for (int i0 = wid; i0 < n_ins; i0 += 4 * kWaves) {
+        int rid[4], piece[4];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int ins = i0 + u * kWaves;
-        if (ins < n_ins && rid[u] >= 0) {
-          const uint8_t* src = piece[u] < 16
-                                   ? a.lat_codes + (int64_t)rid[u] * CSA2_LAT_CODE_BYTES + 16 * piece[u]
-                                   : a.lat_scales + (int64_t)rid[u] * CSA2_LAT_SCALE_BYTES;
-          __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src), stage + ins * 1024, 16, 0, 0);
+        for (int u = 0; u < 4; ++u) {
+          const int c = (i0 + u * kWaves) * 64 + lane;
+          const int r = c / 17;
+          piece[u] = c - r * 17;
+          rid[u] = c < chunks ? rowid[r] : -1;
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int ins = i0 + u * kWaves;
+          if (ins < n_ins && rid[u] >= 0) {
+            const uint8_t* src = piece[u] < 16
+                                     ? a.lat_codes + (int64_t)rid[u] * CSA2_LAT_CODE_BYTES + 16 * piece[u]
+                                     : a.lat_scales + (int64_t)rid[u] * CSA2_LAT_SCALE_BYTES;
+            __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src), buf + ins * 1024, 16, 0, 0);
+          }
         }
       }
     }
   };
 
-  // ---- start: window batch 0 copies, q fragments, FP4 row ids of batch 0 ----
-  const int n_wb = (a.W + kWinBatch - 1) / kWinBatch;
-  stage_window(0, min(a.W, kWinBatch));
-  // q operand of head hg*16+n: dims 128g + 8s .. +7 for k-step s
-  u32x4 qf[16];
+  // ---- start: window copies first (no lookups), then q, then the first row ids ----
+  if (n_wb > 0) issue(0);
+  u32x4 qf[16];   // q operand of head hg*16+n: dims 128g + 8s .. +7 for k-step s
   {
     const uint16_t* qp = a.q + (qi * a.H + hg * 16 + n) * CSA2_D_LATENT + 128 * g;
 #pragma unroll
     for (int s = 0; s < 16; ++s) qf[s] = *reinterpret_cast<const u32x4*>(qp + 8 * s);
   }
-  const int n_batches = a.topk > 0 ? (a.topk + kBatchRows - 1) / kBatchRows : 0;
-  // row ids of batch r0: entry ids first (independent loads), then their pages
-  auto resolve_rows = [&](int r0, int nrows) {
-    constexpr int RPT = kBatchRows / kThreads;
-    int e[RPT];
-#pragma unroll
-    for (int u = 0; u < RPT; ++u) {
-      const int i = tid + u * kThreads;
-      e[u] = i < nrows ? a.topk_idx[qi * a.topk + r0 + i] : -1;
-    }
-    int pg[RPT];
-#pragma unroll
-    for (int u = 0; u < RPT; ++u) {
-      const bool ok = e[u] >= 0 && e[u] < n_vis && (e[u] >> 6) < a.max_pages;
-      pg[u] = ok ? a.block_table[(int64_t)b * a.max_pages + (e[u] >> 6)] : -1;
-    }
-#pragma unroll
-    for (int u = 0; u < RPT; ++u) {
-      const int i = tid + u * kThreads;
-      if (i < nrows)
-        rowid[i] = (pg[u] >= 0 && pg[u] < a.n_pages) ? pg[u] * CSA2_PAGE + (e[u] & (CSA2_PAGE - 1)) : -1;
-    }
-  };
-  resolve_rows(0, min(a.topk, kBatchRows));
+  if (n_fb > 0) resolve_rows(0);
+  if (n_fb > 1) resolve_rows(1);
+  if (n_wb == 0) {
+    __syncthreads();   // row ids of the first batch
+    issue(0);
+  }
 
-  f32x4 acc[32];
+  f32x4 acc[4];
 #pragma unroll
-  for (int i = 0; i < 32; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < 4; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_part = 0.f;
-  float z[kMaxT][8];
 
-  // ---- phase A: window rows ----
-  for (int wb = 0; wb < n_wb; ++wb) {
-    const int w0 = wb * kWinBatch;
-    const int nw = min(a.W - w0, kWinBatch);
-    if (wb > 0) {
-      __syncthreads();
-      stage_window(w0, nw);
+#pragma unroll 1
+  for (int k = 0; k < nb; ++k) {
+    const bool is_win = k < n_wb;
+    uint8_t* buf = lds + kOffBuf + (k & 1) * kBufBytes;
+    const int f = k - n_wb;
+    const int w0 = k * kWinBatch;
+    const int nrows = is_win ? min(a.W - w0, kWinBatch) : min(a.topk - f * kFp4Batch, kFp4Batch);
+    const int32_t* rowid = rowid_all + (f & 1) * kFp4Batch;
+    const int ntl = (nrows + 31) >> 5;
+
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's copies of batch k
+    __syncthreads();                                    // everyone's; batch k-1 fully consumed
+    if (k + 1 < nb) {
+      if (k + 1 >= n_wb && k + 1 - n_wb >= 2) {         // FP4 batches past the first two
+        resolve_rows(k + 1 - n_wb);
+        __syncthreads();
+      }
+      issue(k + 1);
     }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    const int padded = ((nw + 31) >> 5) << 5;
-    for (int c = tid; c < padded * 65; c += kThreads) {
-      const int r = c / 65;
-      if (!win_valid(a.W, t, w0 + r) || r >= nw) *reinterpret_cast<u32x4*>(stage + c * 16) = u32x4{0u, 0u, 0u, 0u};
+    // rows that were not copied hold stale bytes: zero them (P is 0 there, but 0 * NaN is not)
+    {
+      const int pitch16 = is_win ? 65 : 17;
+      for (int c = tid; c < ntl * 32 * pitch16; c += kThreads) {
+        const int r = c / pitch16;
+        const bool ok = is_win ? (r < nrows && win_valid(a.W, t, w0 + r)) : (r < nrows && rowid[r] >= 0);
+        if (!ok) *reinterpret_cast<u32x4*>(buf + c * 16) = u32x4{0u, 0u, 0u, 0u};
+      }
     }
     __syncthreads();
-    const int ntl = padded >> 5;
+
+    // ---- QK: wave w scores tile w ----
+    float z[8];
+    if (wid < ntl) {
+      if (is_win)
+        win_qk(buf, a.W, t, w0, wid * 32, qf, a.scale_log2, z);
+      else
+        fp4_qk(buf, rowid, nrows, wid * 32, qf, a.scale_log2, z);
+    } else {
 #pragma unroll
-    for (int i = 0; i < kMaxT; ++i) {
-      const int tile = wid + kWaves * i;
-      if (tile < ntl) {
-        win_qk(stage, a.W, t, w0, tile * 32, qf, a.scale_log2, z[i]);
+      for (int j = 0; j < 8; ++j) z[j] = -INFINITY;
+    }
+    float tmax = z[0];
+#pragma unroll
+    for (int j = 1; j < 8; ++j) tmax = fmaxf(tmax, z[j]);
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, kWave));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
+    if (g == 0) m_part[wid * 16 + n] = tmax;
+    __syncthreads();
+
+    // ---- batch max of head n (identical in every wave), P for the scored tile ----
+    float mb = m_part[n];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) mb = fmaxf(mb, m_part[w * 16 + n]);
+    const float m_new = fmaxf(m_run, mb);
+    const float fac = (m_run == -INFINITY || m_new == m_run) ? 1.f : exp2f(m_run - m_new);
+    l_part *= fac;
+    if (wid < ntl) {
+      u32x4 ph, pl;
+      make_p(z, m_new, l_part, ph, pl);
+      uint8_t* pp = plds + (wid * 64 + lane) * kPBytes;
+      *reinterpret_cast<u32x4*>(pp) = ph;
+      *reinterpret_cast<u32x4*>(pp + 16) = pl;
+    }
+    // rescale: acc[t][i] belongs to head 4g+i, whose factor lives in lane 4g+i
+    {
+      float fo[4];
+      bool any = false;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        fo[i] = __shfl(fac, 4 * g + i, kWave);
+        any = any || fo[i] != 1.f;
+      }
+      if (__any(any)) {
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[tt][i] *= fo[i];
+        }
+      }
+    }
+    m_run = m_new;
+    __syncthreads();
+
+    // ---- PV over every tile of the batch, this wave's 64 dims ----
+#pragma unroll 1
+    for (int tile = 0; tile < ntl; ++tile) {
+      const uint8_t* pp = plds + (tile * 64 + lane) * kPBytes;
+      const bf16x8 ph = __builtin_bit_cast(bf16x8, lds_ld<u32x4>(pp));
+      const bf16x8 pl = __builtin_bit_cast(bf16x8, lds_ld<u32x4>(pp + 16));
+      uint32_t d01[8], d23[8];
+      if (is_win) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const u32x2 v = lds_ld<u32x2>(buf + (tile * 32 + slot_row(g, j)) * kWinB + 128 * wid + 8 * n);
+          d01[j] = v.x;
+          d23[j] = v.y;
+        }
       } else {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) z[i][j] = -INFINITY;
+        for (int j = 0; j < 8; ++j) {
+          const uint8_t* rp = buf + (tile * 32 + slot_row(g, j)) * kRowB;
+          const uint32_t c2 = lds_ld<uint16_t>(rp + 32 * wid + 2 * n);
+          const float sc = e8m0_scale(rp[256 + 2 * wid + (n >> 3)]);
+          d01[j] = fp4x2_to_bf16x2<0>(c2, sc);
+          d23[j] = fp4x2_to_bf16x2<1>(c2, sc);
+        }
       }
-    }
-    phase_max(z, m_run, l_part, acc);
-#pragma unroll
-    for (int i = 0; i < kMaxT; ++i) {
-      const int tile = wid + kWaves * i;
-      if (tile < ntl) {
-        bf16x8 ph, pl;
-        make_p(z[i], m_run, l_part, ph, pl);
-        win_pv(stage, tile * 32, ph, pl, acc);
-      }
+      pv4(acc, d01, d23, ph, pl);
     }
   }
 
-  // ---- phase B: selected FP4 rows ----
-  for (int bt = 0; bt < n_batches; ++bt) {
-    const int r0 = bt * kBatchRows;
-    const int nrows = min(a.topk - r0, kBatchRows);
-    __syncthreads();                               // staging area and row ids free
-    if (bt > 0) {
-      resolve_rows(r0, nrows);
-      __syncthreads();
-    }
-    stage_fp4(nrows);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    const int padded = ((nrows + 31) >> 5) << 5;
-    for (int c = tid; c < padded * 17; c += kThreads) {
-      const int r = c / 17;
-      if (r >= nrows || rowid[r] < 0) *reinterpret_cast<u32x4*>(stage + c * 16) = u32x4{0u, 0u, 0u, 0u};
-    }
-    __syncthreads();
-    const int ntl = padded >> 5;
-#pragma unroll
-    for (int i = 0; i < kMaxT; ++i) {
-      const int tile = wid + kWaves * i;
-      if (tile < ntl) {
-        fp4_qk(stage, rowid, nrows, tile * 32, qf, a.scale_log2, z[i]);
-      } else {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) z[i][j] = -INFINITY;
-      }
-    }
-    phase_max(z, m_run, l_part, acc);
-#pragma unroll
-    for (int i = 0; i < kMaxT; ++i) {
-      const int tile = wid + kWaves * i;
-      if (tile < ntl) {
-        bf16x8 ph, pl;
-        make_p(z[i], m_run, l_part, ph, pl);
-        fp4_pv(stage, tile * 32, ph, pl, acc);
-      }
-    }
-  }
-  __syncthreads();
-
-  // ---------------- merge the waves ----------------
+  // ---- softmax denominators, output ----
   float l_head = l_part;
   l_head += __shfl_xor(l_head, 16, kWave);
   l_head += __shfl_xor(l_head, 32, kWave);
-  if (g == 0) {
-    m_w[wid * 16 + n] = m_run;
-    l_w[wid * 16 + n] = l_head;
-  }
+  if (g == 0) l_w[wid * 16 + n] = l_head;
   __syncthreads();
-  if (tid < 16) {
-    float m = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) m = fmaxf(m, m_w[w * 16 + tid]);
-    float l = 0.f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w)
-      if (m_w[w * 16 + tid] > -INFINITY) l += l_w[w * 16 + tid] * exp2f(m_w[w * 16 + tid] - m);
-    m_g[tid] = m;
-    l_g[tid] = l;
-  }
-  __syncthreads();
-  // Each wave writes its rescaled accumulators to a slot of its own (plain stores;
-  // LDS float atomics serialise badly here).  Lane (n, g) holds O[head 4g+i][dim
-  // 32n+t] in acc[t][i]; head 4g+i's running max lives in lane 4g+i.  A slot row
-  // keeps 36 floats per 32 dims so the 16 lanes of a store hit distinct banks.
-  float* slot = reinterpret_cast<float*>(lds) + wid * 16 * kOStride;
+  float lh[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const float mh = __shfl(m_run, 4 * g + i, kWave);
-    const float f = (mh == -INFINITY) ? 0.f : exp2f(mh - m_g[4 * g + i]);
-    float* dst = slot + (4 * g + i) * kOStride + 36 * n;
+    float s = 0.f;
 #pragma unroll
-    for (int t4 = 0; t4 < 8; ++t4)
-      *reinterpret_cast<f32x4*>(dst + 4 * t4) = f32x4{acc[4 * t4][i] * f, acc[4 * t4 + 1][i] * f,
-                                                      acc[4 * t4 + 2][i] * f, acc[4 * t4 + 3][i] * f};
+    for (int w = 0; w < kWaves; ++w) s += l_w[w * 16 + 4 * g + i];
+    lh[i] = s;
   }
-  __syncthreads();
-  const float* base = reinterpret_cast<const float*>(lds);
-  for (int i = tid; i < 16 * CSA2_D_LATENT / 4; i += kThreads) {
-    const int h = (4 * i) / CSA2_D_LATENT, d = (4 * i) % CSA2_D_LATENT;
-    const int off = h * kOStride + 36 * (d >> 5) + (d & 31);
-    f32x4 s4 = *reinterpret_cast<const f32x4*>(base + off);
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w) s4 += *reinterpret_cast<const f32x4*>(base + w * 16 * kOStride + off);
-    const float l = l_g[h];
-    const float inv = l > 0.f ? 1.f / l : 0.f;
-    const uint32_t v0 = f32_to_bf16_rne(s4[0] * inv), v1 = f32_to_bf16_rne(s4[1] * inv);
-    const uint32_t v2 = f32_to_bf16_rne(s4[2] * inv), v3 = f32_to_bf16_rne(s4[3] * inv);
-    *reinterpret_cast<u32x2*>(a.out + (qi * a.H + hg * 16 + h) * CSA2_D_LATENT + d) =
+  for (int i = 0; i < 4; ++i) {
+    const float inv = lh[i] > 0.f ? 1.f / lh[i] : 0.f;
+    const uint32_t v0 = f32_to_bf16_rne(acc[0][i] * inv), v1 = f32_to_bf16_rne(acc[1][i] * inv);
+    const uint32_t v2 = f32_to_bf16_rne(acc[2][i] * inv), v3 = f32_to_bf16_rne(acc[3][i] * inv);
+    *reinterpret_cast<u32x2*>(a.out + (qi * a.H + hg * 16 + 4 * g + i) * CSA2_D_LATENT + 64 * wid + 4 * n) =
         u32x2{v0 | (v1 << 16), v2 | (v3 << 16)};
   }
-  if (a.lse && tid < 16) {
-    const float l = l_g[tid];
-    a.lse[qi * a.H + hg * 16 + tid] = l > 0.f ? (m_g[tid] + log2f(l)) * kLn2 : -INFINITY;
+  if (a.lse && wid == 0 && g == 0) {
+    float s = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) s += l_w[w * 16 + n];
+    a.lse[qi * a.H + hg * 16 + n] = s > 0.f ? (m_run + log2f(s)) * kLn2 : -INFINITY;
   }
 }
 
