@@ -16,7 +16,10 @@
 // batches of 64 bf16 rows (pitch 1040 B), then FP4 batches of 256 rows (256 code
 // bytes + 16 scale bytes, pitch 272 B).  All row data reaches LDS through
 // global_load_lds_dwordx4 (no registers); the copy of batch k+1 is issued as soon as
-// batch k's data has arrived, so it overlaps batch k's arithmetic.  Per batch:
+// batch k's data has arrived, so it overlaps batch k's arithmetic.  The selected
+// entries' page lookups are loads into registers issued at the start and consumed
+// only when the first FP4 batch is copied, so they hide behind the window batches.
+// Per batch:
 //   QK  wave w scores 32-row tile w: D[row][head] via 16x16x32 bf16 MFMAs, A = rows
 //       (lane: row l%16, dims 128g+8s..+7 at k-step s, g = l/16; FP4 rows become
 //       bf16 through the hardware convert with the e8m0 scale folded in, exact),
@@ -45,16 +48,18 @@ constexpr int kRowB = 272;           // FP4 row in LDS: 256 code bytes then 16 s
 constexpr int kWinB = 1040;          // window row in LDS: 1024 bytes + 16 pad
 constexpr int kFp4Batch = 256;       // FP4 rows per batch (8 tiles)
 constexpr int kWinBatch = 64;        // window rows per batch (2 tiles)
+constexpr int kMaxTiles = kFp4Batch / 32;
 constexpr int kBufBytes = kFp4Batch * kRowB;              // 69632 >= kWinBatch * kWinB
 constexpr int kPBytes = 32;                               // per lane and tile: P head + residual
 constexpr int kOffBuf = 0;
 constexpr int kOffP = 2 * kBufBytes;                      // [8 tiles][64 lanes][32 B]
-constexpr int kOffRowId = kOffP + 8 * 64 * kPBytes;       // [2][256] int32
+constexpr int kOffRowId = kOffP + kMaxTiles * 64 * kPBytes;   // [2][256] int32
 constexpr int kOffMax = kOffRowId + 2 * kFp4Batch * 4;    // [8 waves][16] float
 constexpr int kOffL = kOffMax + kWaves * 16 * 4;          // [8 waves][16] float
 constexpr int kLdsBytes = kOffL + kWaves * 16 * 4;
 static_assert(kWinBatch * kWinB <= kBufBytes, "window batch fits a buffer");
-static_assert(kFp4Batch / 32 == kWaves, "one FP4 tile per wave");
+static_assert(kMaxTiles == kWaves, "one FP4 tile per wave");
+static_assert(2 * kFp4Batch == kThreads, "one prefetched row id per thread (two FP4 batches)");
 static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
 
 constexpr float kLog2e = 1.4426950408889634f;
@@ -221,11 +226,11 @@ __global__ __launch_bounds__(kThreads) void sparse_decode_kernel(DecArgs a) {
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15, g = lane >> 4;
 
-  int64_t L = a.len[b];
-  if (L < 0) L = 0;
-  if (a.prefill) L += ci + 1;   // chunk query ci sits at position prior + ci
-  const int n_vis = (int)(L >> 1);
-  const int t = (int)L - 1;
+  int64_t Lq = a.len[b];
+  if (Lq < 0) Lq = 0;
+  if (a.prefill) Lq += ci + 1;   // chunk query ci sits at position prior + ci
+  const int n_vis = (int)(Lq >> 1);
+  const int t = (int)Lq - 1;
   const uint16_t* win_b = a.win + (int64_t)b * (a.prefill ? a.W - 1 + a.C : a.W) * CSA2_D_LATENT;
   const int32_t* tk = a.topk_idx + qi * a.topk;
   const int32_t* bt = a.block_table + (int64_t)b * a.max_pages;
@@ -234,37 +239,43 @@ __global__ __launch_bounds__(kThreads) void sparse_decode_kernel(DecArgs a) {
   const int n_fb = a.topk > 0 ? (a.topk + kFp4Batch - 1) / kFp4Batch : 0;
   const int nb = n_wb + n_fb;
 
-  // row ids of FP4 batch f into slot f % 2 (entry ids first, then their pages)
+  // row id of entry e (-1: invalid id, absent page)
+  auto row_of = [&](int e, int page) -> int {
+    return (e >= 0 && e < n_vis && page >= 0 && page < a.n_pages) ? page * CSA2_PAGE + (e & (CSA2_PAGE - 1)) : -1;
+  };
+  auto page_ok = [&](int e) { return e >= 0 && e < n_vis && (e >> 6) < a.max_pages; };
+  // FP4 batch f >= 2: ids resolved when the batch is issued
   auto resolve_rows = [&](int f) {
     const int r0 = f * kFp4Batch;
     const int nrows = min(a.topk - r0, kFp4Batch);
     int32_t* rowid = rowid_all + (f & 1) * kFp4Batch;
     for (int i = tid; i < kFp4Batch; i += kThreads) {
-      int r = -1;
-      if (i < nrows) {
-        const int e = tk[r0 + i];
-        if (e >= 0 && e < n_vis && (e >> 6) < a.max_pages) {
-          const int p = bt[e >> 6];
-          if (p >= 0 && p < a.n_pages) r = p * CSA2_PAGE + (e & (CSA2_PAGE - 1));
-        }
-      }
-      rowid[i] = r;
+      const int e = i < nrows ? tk[r0 + i] : -1;
+      rowid[i] = page_ok(e) ? row_of(e, bt[e >> 6]) : -1;
     }
   };
   // copies of batch k into buffer k % 2
   auto issue = [&](int k) {
     uint8_t* buf = lds + kOffBuf + (k & 1) * kBufBytes;
     if (k < n_wb) {
-      // window: LDS chunk c (16 bytes) = piece c%65 of row c/65 (piece 64 = pad)
+      // window: LDS chunk c (16 bytes) = piece c%65 of row c/65 (piece 64 = pad).
+      // Ring slot of row r: (slot0 + r) mod W, slot0 = first position of the batch mod W.
       const int w0 = k * kWinBatch;
       const int nw = min(a.W - w0, kWinBatch);
       const int chunks = nw * 65;
+      int slot0 = (t - (a.W - 1) + w0) % a.W;
+      if (slot0 < 0) slot0 += a.W;
       for (int ins = wid; ins * 64 < chunks; ins += kWaves) {
         const int c = ins * 64 + lane;
         const int r = c / 65, piece = c - r * 65;
         if (c < chunks && piece < 64 && win_valid(a.W, t, w0 + r)) {
-          const int pos = t - (a.W - 1) + w0 + r;
-          const int row = a.prefill ? ci + w0 + r : pos % a.W;
+          int row;
+          if (a.prefill) {
+            row = ci + w0 + r;
+          } else {
+            row = slot0 + r;
+            if (row >= a.W) row -= a.W;
+          }
           const uint16_t* src = win_b + (int64_t)row * CSA2_D_LATENT + 8 * piece;
           __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src), buf + ins * 1024, 16, 0, 0);
         }
@@ -299,20 +310,19 @@ __global__ __launch_bounds__(kThreads) void sparse_decode_kernel(DecArgs a) {
     }
   };
 
-  // ---- start: window copies first (no lookups), then q, then the first row ids ----
-  if (n_wb > 0) issue(0);
+  // ---- start: window copies first (no lookups); entry ids of the first two FP4
+  // batches (thread tid: batch tid/256, row tid%256) and q, all in flight at once ----
+  issue(0);
+  const int pf_i = tid & (kFp4Batch - 1), pf_f = tid >> 8;
+  const int pf_r = pf_f * kFp4Batch + pf_i;
+  const int pf_e = (pf_f < n_fb && pf_r < a.topk) ? tk[pf_r] : -1;
   u32x4 qf[16];   // q operand of head hg*16+n: dims 128g + 8s .. +7 for k-step s
   {
     const uint16_t* qp = a.q + (qi * a.H + hg * 16 + n) * CSA2_D_LATENT + 128 * g;
 #pragma unroll
     for (int s = 0; s < 16; ++s) qf[s] = *reinterpret_cast<const u32x4*>(qp + 8 * s);
   }
-  if (n_fb > 0) resolve_rows(0);
-  if (n_fb > 1) resolve_rows(1);
-  if (n_wb == 0) {
-    __syncthreads();   // row ids of the first batch
-    issue(0);
-  }
+  int pf_page = -1;
 
   f32x4 acc[4];
 #pragma unroll
@@ -331,23 +341,30 @@ __global__ __launch_bounds__(kThreads) void sparse_decode_kernel(DecArgs a) {
 
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's copies of batch k
     __syncthreads();                                    // everyone's; batch k-1 fully consumed
+    if (k == 0 && page_ok(pf_e)) pf_page = bt[pf_e >> 6];   // page lookups, consumed later
     if (k + 1 < nb) {
-      if (k + 1 >= n_wb && k + 1 - n_wb >= 2) {         // FP4 batches past the first two
-        resolve_rows(k + 1 - n_wb);
+      const int f1 = k + 1 - n_wb;
+      if (f1 == 0) {              // first FP4 batch: row ids of the two prefetched batches
+        rowid_all[tid] = row_of(pf_e, pf_page);
+        __syncthreads();
+      } else if (f1 >= 2) {
+        resolve_rows(f1);
         __syncthreads();
       }
       issue(k + 1);
     }
-    // rows that were not copied hold stale bytes: zero them (P is 0 there, but 0 * NaN is not)
-    {
-      const int pitch16 = is_win ? 65 : 17;
-      for (int c = tid; c < ntl * 32 * pitch16; c += kThreads) {
-        const int r = c / pitch16;
-        const bool ok = is_win ? (r < nrows && win_valid(a.W, t, w0 + r)) : (r < nrows && rowid[r] >= 0);
-        if (!ok) *reinterpret_cast<u32x4*>(buf + c * 16) = u32x4{0u, 0u, 0u, 0u};
+
+    // Rows that were not copied (absent ids, positions before 0, the padded tail of
+    // the last tile) hold stale bytes: their P is 0, but 0 * NaN is not, so they are
+    // zeroed before the PV pass (two barriers later).  Usually no row is.
+    if (tid < ntl * 32) {
+      const bool ok = is_win ? (tid < nrows && win_valid(a.W, t, w0 + tid)) : (tid < nrows && rowid[tid] >= 0);
+      if (!ok) {
+        const int pitch16 = is_win ? kWinB / 16 : kRowB / 16;
+        u32x4* rp = reinterpret_cast<u32x4*>(buf + tid * pitch16 * 16);
+        for (int c = 0; c < pitch16; ++c) rp[c] = u32x4{0u, 0u, 0u, 0u};
       }
     }
-    __syncthreads();
 
     // ---- QK: wave w scores tile w ----
     float z[8];
@@ -387,15 +404,15 @@ __global__ __launch_bounds__(kThreads) void sparse_decode_kernel(DecArgs a) {
       float fo[4];
       bool any = false;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        fo[i] = __shfl(fac, 4 * g + i, kWave);
-        any = any || fo[i] != 1.f;
+      for (int ii = 0; ii < 4; ++ii) {
+        fo[ii] = __shfl(fac, 4 * g + ii, kWave);
+        any = any || fo[ii] != 1.f;
       }
       if (__any(any)) {
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) acc[tt][i] *= fo[i];
+          for (int ii = 0; ii < 4; ++ii) acc[tt][ii] *= fo[ii];
         }
       }
     }
@@ -438,18 +455,18 @@ __global__ __launch_bounds__(kThreads) void sparse_decode_kernel(DecArgs a) {
   __syncthreads();
   float lh[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int ii = 0; ii < 4; ++ii) {
     float s = 0.f;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) s += l_w[w * 16 + 4 * g + i];
-    lh[i] = s;
+    for (int w = 0; w < kWaves; ++w) s += l_w[w * 16 + 4 * g + ii];
+    lh[ii] = s;
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float inv = lh[i] > 0.f ? 1.f / lh[i] : 0.f;
-    const uint32_t v0 = f32_to_bf16_rne(acc[0][i] * inv), v1 = f32_to_bf16_rne(acc[1][i] * inv);
-    const uint32_t v2 = f32_to_bf16_rne(acc[2][i] * inv), v3 = f32_to_bf16_rne(acc[3][i] * inv);
-    *reinterpret_cast<u32x2*>(a.out + (qi * a.H + hg * 16 + 4 * g + i) * CSA2_D_LATENT + 64 * wid + 4 * n) =
+  for (int ii = 0; ii < 4; ++ii) {
+    const float inv = lh[ii] > 0.f ? 1.f / lh[ii] : 0.f;
+    const uint32_t v0 = f32_to_bf16_rne(acc[0][ii] * inv), v1 = f32_to_bf16_rne(acc[1][ii] * inv);
+    const uint32_t v2 = f32_to_bf16_rne(acc[2][ii] * inv), v3 = f32_to_bf16_rne(acc[3][ii] * inv);
+    *reinterpret_cast<u32x2*>(a.out + (qi * a.H + hg * 16 + 4 * g + ii) * CSA2_D_LATENT + 64 * wid + 4 * n) =
         u32x2{v0 | (v1 << 16), v2 | (v3 << 16)};
   }
   if (a.lse && wid == 0 && g == 0) {

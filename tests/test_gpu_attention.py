@@ -34,7 +34,8 @@ def _oracle_topk(case, oc, layer, topk):
     ((2048,), 16, 512, 128),                    # config-0 shape
     ((65536, 300, 4000, 100), 64, 512, 128),    # config-1 length, short contexts, ragged tiles
     ((9000, 18), 32, 100, 37),                  # ragged top-K and window
-    ((5000,), 16, 2048, 128),
+    ((5000,), 16, 2048, 128),                   # eight FP4 batches
+    ((700, 3000), 16, 512, 1024),               # long window: 16 window batches
 ])
 def test_sparse_decode_matches_oracle(fk, ctx, H, topk, W):
     cfg = small_decode(1, B=len(ctx), ctx=ctx, H=H, pages="random", heavy_frac=0.05, append=0,
