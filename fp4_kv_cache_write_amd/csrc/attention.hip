@@ -14,11 +14,14 @@
 //
 // Rows are processed in batches that live in one of two 68 KB LDS buffers: window
 // batches of 64 bf16 rows (pitch 1040 B), then FP4 batches of 256 rows (256 code
-// bytes + 16 scale bytes, pitch 272 B).  All row data reaches LDS through
-// global_load_lds_dwordx4 (no registers); the copy of batch k+1 is issued as soon as
-// batch k's data has arrived, so it overlaps batch k's arithmetic.  The selected
-// entries' page lookups are loads into registers issued at the start and consumed
-// only when the first FP4 batch is copied, so they hide behind the window batches.
+// bytes + 16 scale bytes, pitch 272 B).  Batch k+1 is loaded into registers (9 x 16 B
+// per thread) when batch k starts and written to the free buffer after batch k's PV,
+// so the loads overlap batch k's arithmetic.  (Direct global->LDS loads would not:
+// the compiler cannot tell their destination from the buffer being read and waits
+// for them before every LDS read.)  Chunks of rows that are absent are written as
+// zeros, so stale bytes never meet a zero weight (0 * NaN is not 0).  The selected
+// entries' page lookups are loads issued at the start and consumed only when the
+// first FP4 batch is loaded, so they hide behind the window batches.
 // Per batch:
 //   QK  wave w scores 32-row tile w: D[row][head] via 16x16x32 bf16 MFMAs, A = rows
 //       (lane: row l%16, dims 128g+8s..+7 at k-step s, g = l/16; FP4 rows become
@@ -51,6 +54,7 @@ constexpr int kWinBatch = 64;        // window rows per batch (2 tiles)
 constexpr int kMaxTiles = kFp4Batch / 32;
 constexpr int kBufBytes = kFp4Batch * kRowB;              // 69632 >= kWinBatch * kWinB
 constexpr int kPBytes = 32;                               // per lane and tile: P head + residual
+constexpr int kStage = (kFp4Batch * 17 + kThreads - 1) / kThreads;   // 16-byte chunks per thread
 constexpr int kOffBuf = 0;
 constexpr int kOffP = 2 * kBufBytes;                      // [8 tiles][64 lanes][32 B]
 constexpr int kOffRowId = kOffP + kMaxTiles * 64 * kPBytes;   // [2][256] int32
@@ -254,21 +258,21 @@ __global__ __launch_bounds__(kThreads) void sparse_decode_kernel(DecArgs a) {
       rowid[i] = page_ok(e) ? row_of(e, bt[e >> 6]) : -1;
     }
   };
-  // copies of batch k into buffer k % 2
-  auto issue = [&](int k) {
-    uint8_t* buf = lds + kOffBuf + (k & 1) * kBufBytes;
+  // Batch k in registers: thread tid holds chunks c = tid + 512u (16 bytes each) of
+  // the batch image -- FP4: piece c%17 of row c/17 (16 code pieces, then the scales);
+  // window: piece c%64 of row c/64 -- zeros where no row is.
+  auto load_batch = [&](int k, u32x4 (&st)[kStage]) {
+#pragma unroll
+    for (int u = 0; u < kStage; ++u) st[u] = u32x4{0u, 0u, 0u, 0u};
     if (k < n_wb) {
-      // window: LDS chunk c (16 bytes) = piece c%65 of row c/65 (piece 64 = pad).
-      // Ring slot of row r: (slot0 + r) mod W, slot0 = first position of the batch mod W.
       const int w0 = k * kWinBatch;
-      const int nw = min(a.W - w0, kWinBatch);
-      const int chunks = nw * 65;
-      int slot0 = (t - (a.W - 1) + w0) % a.W;
+      int slot0 = (t - (a.W - 1) + w0) % a.W;   // ring slot of the batch's first position
       if (slot0 < 0) slot0 += a.W;
-      for (int ins = wid; ins * 64 < chunks; ins += kWaves) {
-        const int c = ins * 64 + lane;
-        const int r = c / 65, piece = c - r * 65;
-        if (c < chunks && piece < 64 && win_valid(a.W, t, w0 + r)) {
+#pragma unroll
+      for (int u = 0; u < kWinBatch * 64 / kThreads; ++u) {
+        const int c = tid + kThreads * u;
+        const int r = c >> 6, piece = c & 63;
+        if (win_valid(a.W, t, w0 + r)) {
           int row;
           if (a.prefill) {
             row = ci + w0 + r;
@@ -276,43 +280,45 @@ __global__ __launch_bounds__(kThreads) void sparse_decode_kernel(DecArgs a) {
             row = slot0 + r;
             if (row >= a.W) row -= a.W;
           }
-          const uint16_t* src = win_b + (int64_t)row * CSA2_D_LATENT + 8 * piece;
-          __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src), buf + ins * 1024, 16, 0, 0);
+          st[u] = *reinterpret_cast<const u32x4*>(win_b + (int64_t)row * CSA2_D_LATENT + 8 * piece);
         }
       }
     } else {
-      // FP4: LDS chunk c = piece c%17 of row c/17 (16 code pieces, then the scales)
       const int f = k - n_wb;
       const int nrows = min(a.topk - f * kFp4Batch, kFp4Batch);
       const int32_t* rowid = rowid_all + (f & 1) * kFp4Batch;
-      const int chunks = nrows * 17;
-      const int n_ins = (chunks + 63) >> 6;
-      for (int i0 = wid; i0 < n_ins; i0 += 4 * kWaves) {
-        int rid[4], piece[4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int c = (i0 + u * kWaves) * 64 + lane;
-          const int r = c / 17;
-          piece[u] = c - r * 17;
-          rid[u] = c < chunks ? rowid[r] : -1;
-        }
+      for (int u = 0; u < kStage; ++u) {
+        const int c = tid + kThreads * u;
+        const int r = c / 17, piece = c - r * 17;
+        const int rid = (c < kFp4Batch * 17 && r < nrows) ? rowid[r] : -1;
+        if (rid >= 0)
+          st[u] = *reinterpret_cast<const u32x4*>(piece < 16 ? a.lat_codes + (int64_t)rid * CSA2_LAT_CODE_BYTES + 16 * piece
+                                                           : a.lat_scales + (int64_t)rid * CSA2_LAT_SCALE_BYTES);
+      }
+    }
+  };
+  auto store_batch = [&](int k, const u32x4 (&st)[kStage]) {
+    uint8_t* buf = lds + kOffBuf + (k & 1) * kBufBytes;
+    if (k < n_wb) {
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int ins = i0 + u * kWaves;
-          if (ins < n_ins && rid[u] >= 0) {
-            const uint8_t* src = piece[u] < 16
-                                     ? a.lat_codes + (int64_t)rid[u] * CSA2_LAT_CODE_BYTES + 16 * piece[u]
-                                     : a.lat_scales + (int64_t)rid[u] * CSA2_LAT_SCALE_BYTES;
-            __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src), buf + ins * 1024, 16, 0, 0);
-          }
-        }
+      for (int u = 0; u < kWinBatch * 64 / kThreads; ++u) {
+        const int c = tid + kThreads * u;
+        *reinterpret_cast<u32x4*>(buf + (c >> 6) * kWinB + (c & 63) * 16) = st[u];
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < kStage; ++u) {
+        const int c = tid + kThreads * u;
+        if (c < kFp4Batch * 17) *reinterpret_cast<u32x4*>(buf + c * 16) = st[u];
       }
     }
   };
 
-  // ---- start: window copies first (no lookups); entry ids of the first two FP4
+  // ---- start: batch 0 (window rows need no lookups), entry ids of the first two FP4
   // batches (thread tid: batch tid/256, row tid%256) and q, all in flight at once ----
-  issue(0);
+  u32x4 st[kStage];
+  if (n_wb > 0) load_batch(0, st);
   const int pf_i = tid & (kFp4Batch - 1), pf_f = tid >> 8;
   const int pf_r = pf_f * kFp4Batch + pf_i;
   const int pf_e = (pf_f < n_fb && pf_r < a.topk) ? tk[pf_r] : -1;
@@ -323,6 +329,11 @@ __global__ __launch_bounds__(kThreads) void sparse_decode_kernel(DecArgs a) {
     for (int s = 0; s < 16; ++s) qf[s] = *reinterpret_cast<const u32x4*>(qp + 8 * s);
   }
   int pf_page = -1;
+  if (n_wb > 0) store_batch(0, st);
+  // q and the entry ids have arrived before the loop starts: the wait counts inside
+  // the loop then cover only the next batch's loads, which stay in flight until the
+  // batch is stored after PV.
+  __builtin_amdgcn_s_waitcnt(0);
 
   f32x4 acc[4];
 #pragma unroll
@@ -339,8 +350,7 @@ __global__ __launch_bounds__(kThreads) void sparse_decode_kernel(DecArgs a) {
     const int32_t* rowid = rowid_all + (f & 1) * kFp4Batch;
     const int ntl = (nrows + 31) >> 5;
 
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's copies of batch k
-    __syncthreads();                                    // everyone's; batch k-1 fully consumed
+    __syncthreads();   // batch k stored by every thread; batch k-1 fully consumed
     if (k == 0 && page_ok(pf_e)) pf_page = bt[pf_e >> 6];   // page lookups, consumed later
     if (k + 1 < nb) {
       const int f1 = k + 1 - n_wb;
@@ -351,19 +361,7 @@ __global__ __launch_bounds__(kThreads) void sparse_decode_kernel(DecArgs a) {
         resolve_rows(f1);
         __syncthreads();
       }
-      issue(k + 1);
-    }
-
-    // Rows that were not copied (absent ids, positions before 0, the padded tail of
-    // the last tile) hold stale bytes: their P is 0, but 0 * NaN is not, so they are
-    // zeroed before the PV pass (two barriers later).  Usually no row is.
-    if (tid < ntl * 32) {
-      const bool ok = is_win ? (tid < nrows && win_valid(a.W, t, w0 + tid)) : (tid < nrows && rowid[tid] >= 0);
-      if (!ok) {
-        const int pitch16 = is_win ? kWinB / 16 : kRowB / 16;
-        u32x4* rp = reinterpret_cast<u32x4*>(buf + tid * pitch16 * 16);
-        for (int c = 0; c < pitch16; ++c) rp[c] = u32x4{0u, 0u, 0u, 0u};
-      }
+      load_batch(k + 1, st);      // stored after this batch's PV
     }
 
     // ---- QK: wave w scores tile w ----
@@ -445,6 +443,7 @@ __global__ __launch_bounds__(kThreads) void sparse_decode_kernel(DecArgs a) {
       }
       pv4(acc, d01, d23, ph, pl);
     }
+    if (k + 1 < nb) store_batch(k + 1, st);   // into the other buffer, free since batch k began
   }
 
   // ---- softmax denominators, output ----
