@@ -29,10 +29,8 @@ constexpr int kScanThreads = 512;
 constexpr int kScanRound = 16;       // groups of 16 entries a wave loads before scoring them (4 pages)
 constexpr int kMergeThreads = 1024;
 constexpr int kMergeCap = 32768;     // keys the merge / pool workgroup selects from
-constexpr int kMergeKpt = kMergeCap / kMergeThreads;
 constexpr int kReindexThreads = 512;
 constexpr int kReindexCap = 16384;
-constexpr int kReindexKpt = kReindexCap / kReindexThreads;
 
 __device__ __forceinline__ int n_visible_entries(const int32_t* ctx_len, int b, int64_t max_ctx) {
   int64_t L = ctx_len[b];
@@ -208,14 +206,16 @@ struct MergeArgs {
 };
 
 // blockIdx.y == 0: top-K over the chunk candidates; == 1: HSI pool over block maxima.
+// KPT (keys per thread) is the smallest of 4/8/16/32 that covers both key sets.
+template <int KPT>
 __global__ __launch_bounds__(kMergeThreads) void index_merge_kernel(MergeArgs a) {
   __shared__ uint32_t hist[kSelectHist];
   __shared__ uint32_t scratch[kSelectScratch];
   const int b = blockIdx.x;
   const int n_vis = n_visible_entries(a.ctx_len, b, a.max_ctx);
   const int tid = threadIdx.x;
-  const int p0 = tid * kMergeKpt;
-  uint32_t kr[kMergeKpt];
+  const int p0 = tid * KPT;
+  uint32_t kr[KPT];
   if (blockIdx.y == 0) {
     // virtual position v = chunk * topk + i, in entry order
     const int nc = (n_vis + a.chunk - 1) / a.chunk;
@@ -227,7 +227,7 @@ __global__ __launch_bounds__(kMergeThreads) void index_merge_kernel(MergeArgs a)
       int cch = c0, j = j0;
       int cnt = (p0 < N) ? a.cand_cnt[(int64_t)b * a.n_chunks + cch] : 0;
 #pragma unroll
-      for (int i = 0; i < kMergeKpt; ++i) {
+      for (int i = 0; i < KPT; ++i) {
         kr[i] = (p0 + i < N && j < cnt) ? ckey[p0 + i] : 0u;
         if (++j == a.topk) {
           j = 0;
@@ -236,23 +236,23 @@ __global__ __launch_bounds__(kMergeThreads) void index_merge_kernel(MergeArgs a)
         }
       }
     }
-    const SelectResult sr = block_select<kMergeThreads, kMergeKpt>(kr, a.topk, hist, scratch);
+    const SelectResult sr = block_select<kMergeThreads, KPT>(kr, a.topk, hist, scratch);
     int32_t* out = a.topk_idx + (int64_t)b * a.topk;
     const int32_t* cidx = a.cand_idx + (int64_t)b * a.n_chunks * a.topk;
-    block_emit<kMergeThreads, kMergeKpt>(kr, sr, scratch, [&](int i, uint32_t pos) { out[pos] = cidx[p0 + i]; });
+    block_emit<kMergeThreads, KPT>(kr, sr, scratch, [&](int i, uint32_t pos) { out[pos] = cidx[p0 + i]; });
     for (int p = (int)sr.count + tid; p < a.topk; p += kMergeThreads) out[p] = -1;
   } else {
     const int cb = a.cand_block;
     const int nb = (n_vis + cb - 1) / cb;
     const uint32_t* bm = a.block_max + (int64_t)b * a.max_blocks;
 #pragma unroll
-    for (int i = 0; i < kMergeKpt; ++i) {
+    for (int i = 0; i < KPT; ++i) {
       const int v = p0 + i;
       kr[i] = v < nb ? (v == nb - 1 ? 0xffffffffu : bm[v]) : 0u;   // newest visible block: +inf
     }
-    const SelectResult sr = block_select<kMergeThreads, kMergeKpt>(kr, a.pool_blocks, hist, scratch);
+    const SelectResult sr = block_select<kMergeThreads, KPT>(kr, a.pool_blocks, hist, scratch);
     int32_t* out = a.pool + (int64_t)b * a.pool_blocks;
-    block_emit<kMergeThreads, kMergeKpt>(kr, sr, scratch, [&](int i, uint32_t pos) { out[pos] = p0 + i; });
+    block_emit<kMergeThreads, KPT>(kr, sr, scratch, [&](int i, uint32_t pos) { out[pos] = p0 + i; });
     for (int p = (int)sr.count + tid; p < a.pool_blocks; p += kMergeThreads) out[p] = -1;
   }
 }
@@ -272,10 +272,13 @@ struct ReindexArgs {
 
 // One workgroup per sequence: score the pool's entries (slot v = p*cb + i is entry
 // pool[p]*cb + i), keep the top-K.  The pool is ascending, so slot order is entry order.
+// KPT (keys per thread) is the smallest of 8/16/32 that covers the pool.
+template <int KPT>
 __global__ __launch_bounds__(kReindexThreads) void reindex_kernel(ReindexArgs a) {
+  constexpr int kCap = KPT * kReindexThreads;
   extern __shared__ uint32_t smem[];
-  uint32_t* keys = smem;                          // [kReindexCap]
-  uint32_t* hist = smem + kReindexCap;
+  uint32_t* keys = smem;                          // [kCap]
+  uint32_t* hist = smem + kCap;
   uint32_t* scratch = hist + kSelectHist;
   const int b = blockIdx.x;
   int64_t L = a.ctx_len[b];
@@ -339,21 +342,21 @@ __global__ __launch_bounds__(kReindexThreads) void reindex_kernel(ReindexArgs a)
     }
   }
   __syncthreads();
-  for (int i = N + threadIdx.x; i < kReindexCap; i += kReindexThreads) keys[i] = 0u;
+  for (int i = N + threadIdx.x; i < kCap; i += kReindexThreads) keys[i] = 0u;
   __syncthreads();
-  uint32_t kr[kReindexKpt];
-  const int p0 = threadIdx.x * kReindexKpt;
+  uint32_t kr[KPT];
+  const int p0 = threadIdx.x * KPT;
 #pragma unroll
-  for (int i = 0; i < kReindexKpt; i += 4) {
+  for (int i = 0; i < KPT; i += 4) {
     const u32x4 v = *reinterpret_cast<const u32x4*>(keys + p0 + i);
     kr[i] = v.x;
     kr[i + 1] = v.y;
     kr[i + 2] = v.z;
     kr[i + 3] = v.w;
   }
-  const SelectResult sr = block_select<kReindexThreads, kReindexKpt>(kr, a.topk, hist, scratch);
+  const SelectResult sr = block_select<kReindexThreads, KPT>(kr, a.topk, hist, scratch);
   int32_t* out = a.topk_idx + (int64_t)b * a.topk;
-  block_emit<kReindexThreads, kReindexKpt>(kr, sr, scratch, [&](int i, uint32_t pos) {
+  block_emit<kReindexThreads, KPT>(kr, sr, scratch, [&](int i, uint32_t pos) {
     const int v = p0 + i;
     out[pos] = pool[v / cb] * cb + (v % cb);
   });
@@ -369,7 +372,9 @@ bool lds_limits_set() {
     const void* ks[] = {reinterpret_cast<const void*>(index_scan_kernel<4096>),
                         reinterpret_cast<const void*>(index_scan_kernel<8192>),
                         reinterpret_cast<const void*>(index_scan_kernel<16384>),
-                        reinterpret_cast<const void*>(reindex_kernel)};
+                        reinterpret_cast<const void*>(reindex_kernel<8>),
+                        reinterpret_cast<const void*>(reindex_kernel<16>),
+                        reinterpret_cast<const void*>(reindex_kernel<32>)};
     bool r = true;
     for (const void* k : ks)
       r = r && hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) == hipSuccess;
@@ -465,7 +470,18 @@ int launch_index_full(const csa2_cache_t& c, int B, const int32_t* ctx_len, int6
   ma.block_max = sa.block_max;
   ma.topk_idx = topk_idx;
   ma.pool = pool;
-  hipLaunchKernelGGL(index_merge_kernel, dim3(B, pool_blocks > 0 ? 2 : 1), dim3(kMergeThreads), 0, s, ma);
+  const int64_t n_cand = (int64_t)p.n_chunks * topk;
+  const int64_t n_blk = pool_blocks > 0 ? (max_ctx / 2 + cand_block - 1) / cand_block : 0;
+  const int64_t need = n_cand > n_blk ? n_cand : n_blk;
+  const dim3 mgrid(B, pool_blocks > 0 ? 2 : 1);
+  if (need <= 4 * kMergeThreads)
+    hipLaunchKernelGGL(index_merge_kernel<4>, mgrid, dim3(kMergeThreads), 0, s, ma);
+  else if (need <= 8 * kMergeThreads)
+    hipLaunchKernelGGL(index_merge_kernel<8>, mgrid, dim3(kMergeThreads), 0, s, ma);
+  else if (need <= 16 * kMergeThreads)
+    hipLaunchKernelGGL(index_merge_kernel<16>, mgrid, dim3(kMergeThreads), 0, s, ma);
+  else
+    hipLaunchKernelGGL(index_merge_kernel<32>, mgrid, dim3(kMergeThreads), 0, s, ma);
   return hip_status();
 }
 
@@ -488,8 +504,15 @@ int launch_reindex(const csa2_cache_t& c, int B, const int32_t* ctx_len, const u
   ra.cand_block = cand_block;
   ra.topk = topk;
   ra.topk_idx = topk_idx;
-  const size_t lds = (size_t)(kReindexCap + kSelectHist + kSelectScratch) * 4;
-  hipLaunchKernelGGL(reindex_kernel, dim3(B), dim3(kReindexThreads), lds, s, ra);
+  const int N = pool_blocks * cand_block;
+  const int kpt = N <= 8 * kReindexThreads ? 8 : (N <= 16 * kReindexThreads ? 16 : 32);
+  const size_t lds = (size_t)(kpt * kReindexThreads + kSelectHist + kSelectScratch) * 4;
+  if (kpt == 8)
+    hipLaunchKernelGGL(reindex_kernel<8>, dim3(B), dim3(kReindexThreads), lds, s, ra);
+  else if (kpt == 16)
+    hipLaunchKernelGGL(reindex_kernel<16>, dim3(B), dim3(kReindexThreads), lds, s, ra);
+  else
+    hipLaunchKernelGGL(reindex_kernel<32>, dim3(B), dim3(kReindexThreads), lds, s, ra);
   return hip_status();
 }
 
