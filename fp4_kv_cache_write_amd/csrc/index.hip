@@ -257,6 +257,66 @@ __global__ __launch_bounds__(kMergeThreads) void index_merge_kernel(MergeArgs a)
   }
 }
 
+struct GroupArgs {
+  const int32_t* ctx_len;
+  int64_t max_ctx;
+  int topk, chunk, n_chunks, group, n_groups;
+  const uint32_t* cand_key;
+  const int32_t* cand_idx;
+  const int32_t* cand_cnt;
+  uint32_t* grp_key;
+  int32_t* grp_idx;
+  int32_t* grp_cnt;
+};
+
+// Long contexts: the candidates of `group` consecutive chunks are reduced to their
+// top-K first (one workgroup per sequence and group), in the chunk-candidate format,
+// so the final merge selects from n_groups * K keys instead of n_chunks * K.  Exact:
+// the global top-K is contained in the union of the groups' top-Ks, and the kept
+// keys stay in entry order.
+template <int KPT>
+__global__ __launch_bounds__(kMergeThreads) void index_group_kernel(GroupArgs a) {
+  __shared__ uint32_t hist[kSelectHist];
+  __shared__ uint32_t scratch[kSelectScratch];
+  const int b = blockIdx.x, grp = blockIdx.y;
+  const int n_vis = n_visible_entries(a.ctx_len, b, a.max_ctx);
+  const int nc = (n_vis + a.chunk - 1) / a.chunk;
+  const int c0 = grp * a.group;
+  const int64_t gslot = (int64_t)b * a.n_groups + grp;
+  if (c0 >= nc) {
+    if (threadIdx.x == 0) a.grp_cnt[gslot] = 0;
+    return;
+  }
+  const int N = min(a.group, nc - c0) * a.topk;
+  const int tid = threadIdx.x;
+  const int p0 = tid * KPT;
+  const int64_t cbase = (int64_t)b * a.n_chunks + c0;
+  const uint32_t* ckey = a.cand_key + cbase * a.topk;
+  uint32_t kr[KPT];
+  {
+    int cch = p0 / a.topk, j = p0 - (p0 / a.topk) * a.topk;
+    int cnt = (p0 < N) ? a.cand_cnt[cbase + cch] : 0;
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+      kr[i] = (p0 + i < N && j < cnt) ? ckey[p0 + i] : 0u;
+      if (++j == a.topk) {
+        j = 0;
+        ++cch;
+        cnt = (p0 + i + 1 < N) ? a.cand_cnt[cbase + cch] : 0;
+      }
+    }
+  }
+  const SelectResult sr = block_select<kMergeThreads, KPT>(kr, a.topk, hist, scratch);
+  uint32_t* gk = a.grp_key + gslot * a.topk;
+  int32_t* gi = a.grp_idx + gslot * a.topk;
+  const int32_t* cidx = a.cand_idx + cbase * a.topk;
+  block_emit<kMergeThreads, KPT>(kr, sr, scratch, [&](int i, uint32_t pos) {
+    gk[pos] = kr[i];
+    gi[pos] = cidx[p0 + i];
+  });
+  if (tid == 0) a.grp_cnt[gslot] = (int32_t)sr.count;
+}
+
 struct ReindexArgs {
   const uint8_t* idx_codes;
   const uint8_t* idx_scales;
@@ -404,6 +464,12 @@ IndexFullPlan plan_index_full(int B, int64_t max_ctx, int topk, int pool_blocks,
   p.chunk = ch;
   p.n_chunks = (int)nc;
   p.max_blocks = (int)max_blocks;
+  // group the chunks when the final merge would hold more than 4 keys per thread
+  const int64_t per_group = (4 * kMergeThreads) / topk;
+  if (nc * topk > 4 * kMergeThreads && per_group >= 2) {
+    p.group = (int)per_group;
+    p.n_groups = (int)((nc + per_group - 1) / per_group);
+  }
   size_t off = 0;
   p.off_cand_key = off;
   off = align256(off + (size_t)B * nc * topk * 4);
@@ -413,6 +479,12 @@ IndexFullPlan plan_index_full(int B, int64_t max_ctx, int topk, int pool_blocks,
   off = align256(off + (size_t)B * nc * 4);
   p.off_blockmax = off;
   off = align256(off + (size_t)B * max_blocks * 4);
+  p.off_grp_key = off;
+  off = align256(off + (size_t)B * p.n_groups * topk * 4);
+  p.off_grp_idx = off;
+  off = align256(off + (size_t)B * p.n_groups * topk * 4);
+  p.off_grp_cnt = off;
+  off = align256(off + (size_t)B * p.n_groups * 4);
   p.total = off;
   return p;
 }
@@ -461,16 +533,36 @@ int launch_index_full(const csa2_cache_t& c, int B, const int32_t* ctx_len, int6
   ma.topk = topk;
   ma.chunk = p.chunk;
   ma.n_chunks = p.n_chunks;
+  if (p.group > 0) {
+    GroupArgs ga;
+    ga.ctx_len = ctx_len;
+    ga.max_ctx = max_ctx;
+    ga.topk = topk;
+    ga.chunk = p.chunk;
+    ga.n_chunks = p.n_chunks;
+    ga.group = p.group;
+    ga.n_groups = p.n_groups;
+    ga.cand_key = sa.cand_key;
+    ga.cand_idx = sa.cand_idx;
+    ga.cand_cnt = sa.cand_cnt;
+    ga.grp_key = reinterpret_cast<uint32_t*>(w + p.off_grp_key);
+    ga.grp_idx = reinterpret_cast<int32_t*>(w + p.off_grp_idx);
+    ga.grp_cnt = reinterpret_cast<int32_t*>(w + p.off_grp_cnt);
+    hipLaunchKernelGGL(index_group_kernel<4>, dim3(B, p.n_groups), dim3(kMergeThreads), 0, s, ga);
+    if (hip_status() != CSA2_OK) return CSA2_EHIP;
+    ma.chunk = p.chunk * p.group;   // the final merge sees each group as one chunk
+    ma.n_chunks = p.n_groups;
+  }
   ma.cand_block = cand_block;
   ma.pool_blocks = pool_blocks;
   ma.max_blocks = p.max_blocks;
-  ma.cand_key = sa.cand_key;
-  ma.cand_idx = sa.cand_idx;
-  ma.cand_cnt = sa.cand_cnt;
+  ma.cand_key = p.group > 0 ? reinterpret_cast<uint32_t*>(w + p.off_grp_key) : sa.cand_key;
+  ma.cand_idx = p.group > 0 ? reinterpret_cast<int32_t*>(w + p.off_grp_idx) : sa.cand_idx;
+  ma.cand_cnt = p.group > 0 ? reinterpret_cast<int32_t*>(w + p.off_grp_cnt) : sa.cand_cnt;
   ma.block_max = sa.block_max;
   ma.topk_idx = topk_idx;
   ma.pool = pool;
-  const int64_t n_cand = (int64_t)p.n_chunks * topk;
+  const int64_t n_cand = (int64_t)ma.n_chunks * topk;
   const int64_t n_blk = pool_blocks > 0 ? (max_ctx / 2 + cand_block - 1) / cand_block : 0;
   const int64_t need = n_cand > n_blk ? n_cand : n_blk;
   const dim3 mgrid(B, pool_blocks > 0 ? 2 : 1);

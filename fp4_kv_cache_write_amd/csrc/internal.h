@@ -14,7 +14,10 @@ struct IndexFullPlan {
   int chunk;          // entries scored by one workgroup (power of two, >= topk)
   int n_chunks;       // chunks covering max_ctx/2 entries
   int max_blocks;     // candidate blocks covering max_ctx/2 entries
-  size_t off_cand_key, off_cand_idx, off_cand_cnt, off_blockmax, total;
+  int group;          // chunks merged per group before the final merge (0: no groups)
+  int n_groups;
+  size_t off_cand_key, off_cand_idx, off_cand_cnt, off_blockmax;
+  size_t off_grp_key, off_grp_idx, off_grp_cnt, total;
 };
 IndexFullPlan plan_index_full(int B, int64_t max_ctx, int topk, int pool_blocks, int cand_block);
 
