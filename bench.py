@@ -55,6 +55,9 @@ def parse():
     p.add_argument("--cpu-seqs", type=int, default=2, help="sequences in the oracle's timed sample")
     p.add_argument("--no-graph", action="store_true", help="time eager launches instead of graph replay")
     p.add_argument("--serial", action="store_true", help="issue every call of a step on one stream")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="first run one 256 MiB device-to-device copy, whose counter readings "
+                        "(rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE) scale those of the kernels")
     return p.parse_args()
 
 
@@ -108,6 +111,22 @@ def build_decode(case, fk, n_rep: int):
         reps.append(Replica(c, ls, wr))
     torch.cuda.synchronize()
     return reps
+
+
+def recorded_traffic(kernel: str):
+    """HBM bytes per launch of `kernel` from the committed counter summary, if the
+    summary was taken on the current source of that kernel (else None)."""
+    import hashlib
+    import re
+    path = os.path.join(ROOT, "profiles", "pmc_traffic_decode_b32_ctx64k.md")
+    src = os.path.join(ROOT, "fp4_kv_cache_write_amd", "csrc", "attention.hip")
+    if kernel != "sparse_decode" or not (os.path.exists(path) and os.path.exists(src)):
+        return None
+    m = re.search(r"sparse_decode_kernel traffic_bytes_per_launch=(\d+) attention_hip_sha256=([0-9a-f]+)",
+                  open(path).read())
+    if not m or m.group(2) != hashlib.sha256(open(src, "rb").read()).hexdigest():
+        return None
+    return int(m.group(1))
 
 
 def decode_bytes(case):
@@ -287,8 +306,9 @@ def bench_decode(fk, cfg_id: int, steps: int, warmup: int, n_rep: int, use_graph
         totals = {n: per_call[n] * count[n] for n in per_call}
         dom = max(totals, key=totals.get)
         achieved = per_bytes[dom] / (per_call[dom] / 1e3) / 1e9
+        traffic = recorded_traffic(dom) if cfg_id == 1 else None
         roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                    "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                    "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                     "bytes_per_launch": per_bytes[dom], "avg_launch_us": round(per_call[dom] * 1e3, 2),
                     "timing": "graph replay of that call, averaged per launch"}
     return dict(case=case, reps=reps, ms=ms, qps=qps, gbs=gbs, step_bytes=step_bytes, per_call=per_call,
@@ -373,6 +393,13 @@ def main() -> int:
     import fp4_kv_cache_write_amd as fk
     fk.lib()
     assert torch.cuda.is_available(), "no GPU visible"
+    if args.copy_calibration:
+        src = torch.ones(64 << 20, dtype=torch.float32, device="cuda")    # 256 MiB
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log("calibration copy: 268435456 bytes read, 268435456 bytes written")
+        del src, dst
 
     if args.workload == "c3":
         r = bench_prefill(fk, max(2, args.steps // 40), max(1, args.warmup // 10))
