@@ -476,9 +476,345 @@ __global__ __launch_bounds__(kThreads) void sparse_decode_kernel(DecArgs a) {
   }
 }
 
+
+// ---------------------------------------------------------------------------------
+// All 64 heads of a query in one workgroup (H a multiple of 64).  The 16-head
+// kernel above converts every FP4 element once per head group; here the PV operand
+// of a row is converted once and feeds the MFMAs of all four head groups, and every
+// row is read from memory once per query instead of four times.
+//   batches  window batches of 32 rows and FP4 batches of 128 rows (one 34 KB
+//            buffer each), double-buffered, staged through registers as above.
+//   QK       unit (tile t, head group h) = the scores of 16 heads x 32 rows; wave w
+//            takes head group w%4 (its q fragments stay in registers) and tiles
+//            w/4 and w/4 + 2 of the batch.
+//   max, P   per head group through LDS, as above; P of every unit is parked in LDS.
+//   PV       wave w accumulates O[64 heads][dims 64w..64w+63] (64 registers): per
+//            tile it converts its 8 rows x 4 dims once and runs the 2 x 4 MFMAs of
+//            each of the four head groups on them.
+// ---------------------------------------------------------------------------------
+constexpr int kG4 = 4;                                    // head groups per workgroup
+constexpr int64_t kH64MinQueries = 512;                   // launches with fewer queries use 16 heads
+constexpr int kFb64 = 128;                                // FP4 rows per batch (4 tiles)
+constexpr int kWb64 = 32;                                 // window rows per batch (1 tile)
+constexpr int kTiles64 = kFb64 / 32;
+constexpr int kBuf64 = kFb64 * kRowB;                     // 34816 >= kWb64 * kWinB
+constexpr int kStage64 = (kFb64 * 17 + kThreads - 1) / kThreads;
+constexpr int kPf64 = 4;                                  // FP4 batches whose ids are prefetched
+constexpr int kOff64P = 2 * kBuf64;                       // [4 tiles][4 groups][64 lanes][32 B]
+constexpr int kOff64RowId = kOff64P + kTiles64 * kG4 * 64 * kPBytes;   // [4][128] int32
+constexpr int kOff64Max = kOff64RowId + kPf64 * kFb64 * 4;           // [8 waves][16] float
+constexpr int kOff64L = kOff64Max + kWaves * 16 * 4;                  // [8 waves][16] float
+constexpr int kLds64 = kOff64L + kWaves * 16 * 4;
+static_assert(kWb64 * kWinB <= kBuf64, "window batch fits a buffer");
+static_assert(kPf64 * kFb64 == kThreads, "one prefetched row id per thread");
+static_assert(kTiles64 * kG4 == 2 * kWaves, "two QK units per wave");
+static_assert(kLds64 <= 160 * 1024, "LDS budget");
+
+__global__ __launch_bounds__(kThreads) void sparse_decode64_kernel(DecArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  uint8_t* plds = lds + kOff64P;
+  int32_t* rowid_all = reinterpret_cast<int32_t*>(lds + kOff64RowId);
+  float* m_part = reinterpret_cast<float*>(lds + kOff64Max);
+  float* l_w = reinterpret_cast<float*>(lds + kOff64L);
+
+  // XCD-aware mapping: XCD x takes the contiguous query range [x * q_per_xcd, ...).
+  const int xcd = blockIdx.x & 7;
+  const int li = blockIdx.x >> 3;
+  const int nhq = a.H / 64;                     // workgroups per query
+  const int ql = li / nhq;
+  const int hq = li - ql * nhq;                 // heads 64hq .. 64hq+63
+  const int64_t qi = (int64_t)xcd * a.q_per_xcd + ql;
+  if (ql >= a.q_per_xcd || qi >= (int64_t)a.B * a.C) return;
+  const int b = (int)(qi / a.C);
+  const int ci = (int)(qi - (int64_t)b * a.C);
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 15, g = lane >> 4;
+  const int my_hg = wid & 3;                    // head group of this wave's QK units
+
+  int64_t Lq = a.len[b];
+  if (Lq < 0) Lq = 0;
+  if (a.prefill) Lq += ci + 1;
+  const int n_vis = (int)(Lq >> 1);
+  const int t = (int)Lq - 1;
+  const uint16_t* win_b = a.win + (int64_t)b * (a.prefill ? a.W - 1 + a.C : a.W) * CSA2_D_LATENT;
+  const int32_t* tk = a.topk_idx + qi * a.topk;
+  const int32_t* bt = a.block_table + (int64_t)b * a.max_pages;
+
+  const int n_wb = (a.W + kWb64 - 1) / kWb64;
+  const int n_fb = a.topk > 0 ? (a.topk + kFb64 - 1) / kFb64 : 0;
+  const int nb = n_wb + n_fb;
+
+  auto row_of = [&](int e, int page) -> int {
+    return (e >= 0 && e < n_vis && page >= 0 && page < a.n_pages) ? page * CSA2_PAGE + (e & (CSA2_PAGE - 1)) : -1;
+  };
+  auto page_ok = [&](int e) { return e >= 0 && e < n_vis && (e >> 6) < a.max_pages; };
+  auto resolve_rows = [&](int f) {   // FP4 batch f >= kPf64, into slot f % kPf64
+    const int r0 = f * kFb64;
+    const int nrows = min(a.topk - r0, kFb64);
+    int32_t* rowid = rowid_all + (f % kPf64) * kFb64;
+    for (int i = tid; i < kFb64; i += kThreads) {
+      const int e = i < nrows ? tk[r0 + i] : -1;
+      rowid[i] = page_ok(e) ? row_of(e, bt[e >> 6]) : -1;
+    }
+  };
+  auto load_batch = [&](int k, u32x4 (&st)[kStage64]) {
+#pragma unroll
+    for (int u = 0; u < kStage64; ++u) st[u] = u32x4{0u, 0u, 0u, 0u};
+    if (k < n_wb) {
+      const int w0 = k * kWb64;
+      int slot0 = (t - (a.W - 1) + w0) % a.W;
+      if (slot0 < 0) slot0 += a.W;
+#pragma unroll
+      for (int u = 0; u < kWb64 * 64 / kThreads; ++u) {
+        const int c = tid + kThreads * u;
+        const int r = c >> 6, piece = c & 63;
+        if (win_valid(a.W, t, w0 + r)) {
+          int row;
+          if (a.prefill) {
+            row = ci + w0 + r;
+          } else {
+            row = slot0 + r;
+            if (row >= a.W) row -= a.W;
+          }
+          st[u] = *reinterpret_cast<const u32x4*>(win_b + (int64_t)row * CSA2_D_LATENT + 8 * piece);
+        }
+      }
+    } else {
+      const int f = k - n_wb;
+      const int nrows = min(a.topk - f * kFb64, kFb64);
+      const int32_t* rowid = rowid_all + (f % kPf64) * kFb64;
+#pragma unroll
+      for (int u = 0; u < kStage64; ++u) {
+        const int c = tid + kThreads * u;
+        const int r = c / 17, piece = c - r * 17;
+        const int rid = (c < kFb64 * 17 && r < nrows) ? rowid[r] : -1;
+        if (rid >= 0)
+          st[u] = *reinterpret_cast<const u32x4*>(piece < 16 ? a.lat_codes + (int64_t)rid * CSA2_LAT_CODE_BYTES + 16 * piece
+                                                           : a.lat_scales + (int64_t)rid * CSA2_LAT_SCALE_BYTES);
+      }
+    }
+  };
+  auto store_batch = [&](int k, const u32x4 (&st)[kStage64]) {
+    uint8_t* buf = lds + (k & 1) * kBuf64;
+    if (k < n_wb) {
+#pragma unroll
+      for (int u = 0; u < kWb64 * 64 / kThreads; ++u) {
+        const int c = tid + kThreads * u;
+        *reinterpret_cast<u32x4*>(buf + (c >> 6) * kWinB + (c & 63) * 16) = st[u];
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < kStage64; ++u) {
+        const int c = tid + kThreads * u;
+        if (c < kFb64 * 17) *reinterpret_cast<u32x4*>(buf + c * 16) = st[u];
+      }
+    }
+  };
+
+  // ---- start ----
+  u32x4 st[kStage64];
+  if (n_wb > 0) load_batch(0, st);
+  const int pf_f = tid / kFb64, pf_r = tid;     // prefetched id: FP4 batch tid/128, row tid%128
+  const int pf_e = (pf_f < n_fb && pf_r < a.topk) ? tk[pf_r] : -1;
+  u32x4 qf[16];   // q operand of head 64hq + 16*my_hg + n: dims 128g + 8s .. +7
+  {
+    const uint16_t* qp = a.q + (qi * a.H + 64 * hq + 16 * my_hg + n) * CSA2_D_LATENT + 128 * g;
+#pragma unroll
+    for (int s = 0; s < 16; ++s) qf[s] = *reinterpret_cast<const u32x4*>(qp + 8 * s);
+  }
+  int pf_page = -1;
+  if (n_wb > 0) store_batch(0, st);
+  __builtin_amdgcn_s_waitcnt(0);
+
+  f32x4 acc[kG4][4];
+#pragma unroll
+  for (int h = 0; h < kG4; ++h)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[h][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run[kG4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};   // head n of group h
+  float l_part = 0.f;                                                 // head n of my_hg
+
+#pragma unroll 1
+  for (int k = 0; k < nb; ++k) {
+    const bool is_win = k < n_wb;
+    uint8_t* buf = lds + (k & 1) * kBuf64;
+    const int f = k - n_wb;
+    const int w0 = k * kWb64;
+    const int nrows = is_win ? min(a.W - w0, kWb64) : min(a.topk - f * kFb64, kFb64);
+    const int32_t* rowid = rowid_all + (f % kPf64) * kFb64;
+    const int ntl = (nrows + 31) >> 5;
+
+    __syncthreads();   // batch k stored by every thread; batch k-1 fully consumed
+    if (k == 0 && page_ok(pf_e)) pf_page = bt[pf_e >> 6];
+    if (k + 1 < nb) {
+      const int f1 = k + 1 - n_wb;
+      if (f1 == 0) {
+        rowid_all[tid] = row_of(pf_e, pf_page);
+        __syncthreads();
+      } else if (f1 >= kPf64) {
+        resolve_rows(f1);
+        __syncthreads();
+      }
+      load_batch(k + 1, st);
+    }
+
+    // ---- QK: units (tile w/4, group w%4) and (tile w/4 + 2, group w%4) ----
+    const int t0 = wid >> 2, t1 = t0 + 2;
+    float z0[8], z1[8];
+    if (t0 < ntl) {
+      if (is_win)
+        win_qk(buf, a.W, t, w0, t0 * 32, qf, a.scale_log2, z0);
+      else
+        fp4_qk(buf, rowid, nrows, t0 * 32, qf, a.scale_log2, z0);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) z0[j] = -INFINITY;
+    }
+    if (t1 < ntl) {
+      fp4_qk(buf, rowid, nrows, t1 * 32, qf, a.scale_log2, z1);   // window batches hold one tile
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) z1[j] = -INFINITY;
+    }
+    float tmax = z0[0];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) tmax = fmaxf(tmax, fmaxf(z0[j], z1[j]));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, kWave));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
+    if (g == 0) m_part[wid * 16 + n] = tmax;
+    __syncthreads();
+
+    // ---- per-group batch max of head n, P of this wave's units ----
+    float fac[kG4];
+#pragma unroll
+    for (int h = 0; h < kG4; ++h) {
+      const float mb = fmaxf(m_part[h * 16 + n], m_part[(h + 4) * 16 + n]);
+      const float m_new = fmaxf(m_run[h], mb);
+      fac[h] = (m_run[h] == -INFINITY || m_new == m_run[h]) ? 1.f : exp2f(m_run[h] - m_new);
+      m_run[h] = m_new;
+    }
+    float my_fac = fac[0], my_m = m_run[0];
+#pragma unroll
+    for (int h = 1; h < kG4; ++h)
+      if (my_hg == h) {
+        my_fac = fac[h];
+        my_m = m_run[h];
+      }
+    l_part *= my_fac;
+    if (t0 < ntl) {
+      u32x4 ph, pl;
+      make_p(z0, my_m, l_part, ph, pl);
+      uint8_t* pp = plds + ((t0 * kG4 + my_hg) * 64 + lane) * kPBytes;
+      *reinterpret_cast<u32x4*>(pp) = ph;
+      *reinterpret_cast<u32x4*>(pp + 16) = pl;
+    }
+    if (t1 < ntl) {
+      u32x4 ph, pl;
+      make_p(z1, my_m, l_part, ph, pl);
+      uint8_t* pp = plds + ((t1 * kG4 + my_hg) * 64 + lane) * kPBytes;
+      *reinterpret_cast<u32x4*>(pp) = ph;
+      *reinterpret_cast<u32x4*>(pp + 16) = pl;
+    }
+    // rescale: acc[h][t][i] belongs to head 4g+i of group h, factor in lane 4g+i
+#pragma unroll
+    for (int h = 0; h < kG4; ++h) {
+      float fo[4];
+      bool any = false;
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        fo[ii] = __shfl(fac[h], 4 * g + ii, kWave);
+        any = any || fo[ii] != 1.f;
+      }
+      if (__any(any)) {
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+          for (int ii = 0; ii < 4; ++ii) acc[h][tt][ii] *= fo[ii];
+      }
+    }
+    __syncthreads();
+
+    // ---- PV: convert each tile's rows once, MFMAs for all four head groups ----
+#pragma unroll 1
+    for (int tile = 0; tile < ntl; ++tile) {
+      uint32_t d01[8], d23[8];
+      if (is_win) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const u32x2 v = lds_ld<u32x2>(buf + (tile * 32 + slot_row(g, j)) * kWinB + 128 * wid + 8 * n);
+          d01[j] = v.x;
+          d23[j] = v.y;
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const uint8_t* rp = buf + (tile * 32 + slot_row(g, j)) * kRowB;
+          const uint32_t c2 = lds_ld<uint16_t>(rp + 32 * wid + 2 * n);
+          const float sc = e8m0_scale(rp[256 + 2 * wid + (n >> 3)]);
+          d01[j] = fp4x2_to_bf16x2<0>(c2, sc);
+          d23[j] = fp4x2_to_bf16x2<1>(c2, sc);
+        }
+      }
+      bf16x8 bf[4];
+      bf[0] = __builtin_bit_cast(bf16x8, u32x4{pack_lo(d01[0], d01[1]), pack_lo(d01[2], d01[3]),
+                                               pack_lo(d01[4], d01[5]), pack_lo(d01[6], d01[7])});
+      bf[1] = __builtin_bit_cast(bf16x8, u32x4{pack_hi(d01[0], d01[1]), pack_hi(d01[2], d01[3]),
+                                               pack_hi(d01[4], d01[5]), pack_hi(d01[6], d01[7])});
+      bf[2] = __builtin_bit_cast(bf16x8, u32x4{pack_lo(d23[0], d23[1]), pack_lo(d23[2], d23[3]),
+                                               pack_lo(d23[4], d23[5]), pack_lo(d23[6], d23[7])});
+      bf[3] = __builtin_bit_cast(bf16x8, u32x4{pack_hi(d23[0], d23[1]), pack_hi(d23[2], d23[3]),
+                                               pack_hi(d23[4], d23[5]), pack_hi(d23[6], d23[7])});
+#pragma unroll
+      for (int h = 0; h < kG4; ++h) {
+        const uint8_t* pp = plds + ((tile * kG4 + h) * 64 + lane) * kPBytes;
+        const bf16x8 ph = __builtin_bit_cast(bf16x8, lds_ld<u32x4>(pp));
+        const bf16x8 pl = __builtin_bit_cast(bf16x8, lds_ld<u32x4>(pp + 16));
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt)
+          acc[h][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph, bf[tt], acc[h][tt], 0, 0, 0);
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt)
+          acc[h][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, bf[tt], acc[h][tt], 0, 0, 0);
+      }
+    }
+    if (k + 1 < nb) store_batch(k + 1, st);
+  }
+
+  // ---- softmax denominators (group h: waves h and h+4), output ----
+  float l_head = l_part;
+  l_head += __shfl_xor(l_head, 16, kWave);
+  l_head += __shfl_xor(l_head, 32, kWave);
+  if (g == 0) l_w[wid * 16 + n] = l_head;
+  __syncthreads();
+#pragma unroll
+  for (int h = 0; h < kG4; ++h) {
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) {
+      const float lh = l_w[h * 16 + 4 * g + ii] + l_w[(h + 4) * 16 + 4 * g + ii];
+      const float inv = lh > 0.f ? 1.f / lh : 0.f;
+      const uint32_t v0 = f32_to_bf16_rne(acc[h][0][ii] * inv), v1 = f32_to_bf16_rne(acc[h][1][ii] * inv);
+      const uint32_t v2 = f32_to_bf16_rne(acc[h][2][ii] * inv), v3 = f32_to_bf16_rne(acc[h][3][ii] * inv);
+      *reinterpret_cast<u32x2*>(a.out + (qi * a.H + 64 * hq + 16 * h + 4 * g + ii) * CSA2_D_LATENT + 64 * wid +
+                                4 * n) = u32x2{v0 | (v1 << 16), v2 | (v3 << 16)};
+    }
+  }
+  if (a.lse && wid < kG4 && g == 0) {
+    const float s = l_w[wid * 16 + n] + l_w[(wid + 4) * 16 + n];
+    a.lse[qi * a.H + 64 * hq + 16 * wid + n] = s > 0.f ? (m_run[0] * (wid == 0) + m_run[1] * (wid == 1) +
+                                                          m_run[2] * (wid == 2) + m_run[3] * (wid == 3) +
+                                                          log2f(s)) * kLn2
+                                                       : -INFINITY;
+  }
+}
+
 bool lds_limit_set() {
-  static const bool ok = hipFuncSetAttribute(reinterpret_cast<const void*>(sparse_decode_kernel),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes) == hipSuccess;
+  static const bool ok =
+      hipFuncSetAttribute(reinterpret_cast<const void*>(sparse_decode_kernel),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes) == hipSuccess &&
+      hipFuncSetAttribute(reinterpret_cast<const void*>(sparse_decode64_kernel),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, kLds64) == hipSuccess;
   return ok;
 }
 
@@ -516,10 +852,18 @@ int launch_gather_attention(const csa2_cache_t& c, int B, int C, int H, const in
   a.HG = H / 16;
   a.prefill = prefill ? 1 : 0;
   const int64_t per = ((int64_t)B * C + 7) / 8;
-  const int64_t grid = 8 * per * a.HG;
-  if (grid > 0x7fffffff) return CSA2_EUNSUPPORTED;
   a.q_per_xcd = (int)per;
-  hipLaunchKernelGGL(sparse_decode_kernel, dim3((unsigned)grid), dim3(kThreads), kLdsBytes, s, a);
+  // 64 heads per workgroup do more arithmetic per byte but four times the work per
+  // workgroup: worth it once the queries alone give every CU a couple of workgroups.
+  if (H % 64 == 0 && (int64_t)B * C >= kH64MinQueries) {
+    const int64_t grid = 8 * per * (H / 64);
+    if (grid > 0x7fffffff) return CSA2_EUNSUPPORTED;
+    hipLaunchKernelGGL(sparse_decode64_kernel, dim3((unsigned)grid), dim3(kThreads), kLds64, s, a);
+  } else {
+    const int64_t grid = 8 * per * a.HG;
+    if (grid > 0x7fffffff) return CSA2_EUNSUPPORTED;
+    hipLaunchKernelGGL(sparse_decode_kernel, dim3((unsigned)grid), dim3(kThreads), kLdsBytes, s, a);
+  }
   return hip_status();
 }
 

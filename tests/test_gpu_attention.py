@@ -59,6 +59,31 @@ def test_sparse_decode_matches_oracle(fk, ctx, H, topk, W):
     print(f"worst error / (2e-3 bar): {worst / 2e-3:.3f}")
 
 
+def test_sparse_decode_64_heads_per_workgroup(fk):
+    # 512 sequences with 64 heads: launched with all 64 heads of a query in one
+    # workgroup; short and ragged contexts cut the window at position 0
+    B = 512
+    ctx = tuple(40 + 2 * ((37 * b) % 400) for b in range(B))
+    cfg = small_decode(1, B=B, ctx=ctx, H=64, pages="random", heavy_frac=0.05, append=0, topk=96, window=128)
+    case = make_decode_case(cfg, "cpu")
+    oc = oracle_cache_for(case)
+    gc = gpu_cache_for(case)
+    L = case.layer(0)
+    tk = _oracle_topk(case, oc, L, 96)
+    ctx_len = torch.tensor(case.ctx_len, dtype=torch.int32, device="cuda")
+    out, lse = fk.sparse_decode(gc, ctx_len, L["q"].cuda(), torch.from_numpy(tk).cuda(), L["swa"].cuda())
+    torch.cuda.synchronize()
+    out_b, lse = bits(out.cpu()), lse.cpu().numpy()
+    worst = 0.0
+    for b in range(0, B, 7):
+        t = case.ctx_len[b] - 1
+        rows = gather_rows(oc, b, tk[b], bits(L["swa"][b]), t, 128)
+        o_ref, lse_ref = sparse_attention(bits(L["q"][b]), rows, 1 / math.sqrt(512))
+        worst = max(worst, check_attention_rows(out_b[b], o_ref))
+        assert np.allclose(lse[b], lse_ref, rtol=0, atol=1e-4), np.abs(lse[b] - lse_ref).max()
+    print(f"worst error / (2e-3 bar): {worst / 2e-3:.3f}")
+
+
 def test_reuse_reads_only_selected_and_ignores_bad_ids(fk):
     cfg = small_decode(1, B=2, ctx=(12000, 3000), H=16, pages="random", append=0)
     case = make_decode_case(cfg, "cpu")

@@ -72,6 +72,17 @@ def test_prefill_h64_topk512_long_prior():
     _compare(case, oc, ch, out, tk, q)
 
 
+def test_prefill_64_heads_per_workgroup():
+    # 2 x 300 chunk queries with 64 heads: all heads of a query in one workgroup
+    cfg = small_prefill(B=2, prior=1000, C=300, H=64, topk=128, pages="random", seed=1603)
+    case = make_prefill_case(cfg)
+    gc, oc, ch = prefill_caches(case, DEV, oracle_seqs=(0, 1))
+    out, tk = _run_gpu(gc, case, ch)
+    q = [(b, i) for b in range(2) for i in range(0, cfg.C, 5)]
+    compared, worst, near = _compare(case, oc, ch, out, tk, q)
+    print(f"compared {compared}/{len(q)}, worst {worst / 2e-3:.4f} of the bar, near-tie diffs {near}")
+
+
 def test_prefill_first_chunk_short_context():
     # prior 0: the first queries see fewer entries than K and a window cut at position 0
     cfg = small_prefill(B=1, prior=0, C=300, H=16, topk=64, seed=1303)
