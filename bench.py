@@ -171,6 +171,7 @@ def bench_decode(fk, cfg_id: int, steps: int, warmup: int, n_rep: int, use_graph
     max_ctx = max(case.ctx_len)
     pool_blocks = max([sp.pool_blocks for sp in cfg.layers] + [0])
     ws_full = fk.workspace(fk.FN_INDEX_FULL, device=dev, B=B, max_ctx=max_ctx, topk=topk, pool_blocks=pool_blocks)
+    ws_re = fk.workspace(fk.FN_REINDEX, device=dev, B=B, topk=topk, pool_blocks=max(pool_blocks, 1))
     tk_buf = [torch.empty((B, topk), dtype=torch.int32, device=dev) for _ in range(2)]
     pool = torch.empty((B, max(pool_blocks, 1)), dtype=torch.int32, device=dev)
     outs = [torch.empty((B, H, 512), dtype=torch.bfloat16, device=dev) for _ in cfg.layers]
@@ -197,7 +198,7 @@ def bench_decode(fk, cfg_id: int, steps: int, warmup: int, n_rep: int, use_graph
                 nxt ^= 1
                 out.append(("reindex", lambda L=L, tk=tk: fk.reindex(R.cache, ctx, L["q_idx"], L["w_idx"], pool,
                                                                      topk=topk, cand_block=cfg.cand_block,
-                                                                     topk_idx=tk)))
+                                                                     topk_idx=tk, ws=ws_re)))
                 cur = tk
             out.append(("sparse_decode", lambda L=L, tk=cur, l=l: fk.sparse_decode(
                 R.cache, ctx, L["q"], tk, L["swa"], out=outs[l], lse=lses[l])))

@@ -184,7 +184,8 @@ def index_full(cache: PagedCache, ctx_len: torch.Tensor, max_ctx: int, q_idx: to
 
 def reindex(cache: PagedCache, ctx_len: torch.Tensor, q_idx: torch.Tensor, w_idx: torch.Tensor,
             pool: torch.Tensor, topk: int = 512, cand_block: int = 8,
-            topk_idx: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+            topk_idx: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None,
+            split: bool = True, stream=None) -> torch.Tensor:
     B = ctx_len.shape[0]
     _need(ctx_len, torch.int32, "ctx_len", (B,))
     _bf16(q_idx, "q_idx", (B, H_INDEX, D_INDEX))
@@ -192,8 +193,11 @@ def reindex(cache: PagedCache, ctx_len: torch.Tensor, q_idx: torch.Tensor, w_idx
     _need(pool, torch.int32, "pool")
     if topk_idx is None:
         topk_idx = torch.empty((B, topk), dtype=torch.int32, device=q_idx.device)
+    if ws is None and split:
+        ws = workspace(FN_REINDEX, device=q_idx.device, B=B, topk=topk, pool_blocks=pool.shape[1])
+    wsb = ws.numel() if ws is not None else 0
     _check(lib().csa2_reindex(cache.ref, B, _ptr(ctx_len), _ptr(q_idx), _ptr(w_idx), _ptr(pool),
-                              pool.shape[1], cand_block, topk, _ptr(topk_idx), None, 0, _stream(stream)),
+                              pool.shape[1], cand_block, topk, _ptr(topk_idx), _ptr(ws), wsb, _stream(stream)),
            "csa2_reindex")
     return topk_idx
 

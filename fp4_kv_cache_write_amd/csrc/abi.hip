@@ -42,7 +42,7 @@ size_t csa2_workspace_size(int fn, int B, int H, int64_t max_ctx, int topk, int 
       if (max_ctx < 0 || topk < 1 || topk > CSA2_MAX_TOPK || pool_blocks < 0) return 0;
       return plan_index_full(B, max_ctx, topk, pool_blocks, 8).total;
     case CSA2_FN_REINDEX:
-      return 0;
+      return reindex_ws(B);
     case CSA2_FN_SPARSE_DECODE:
       if (H <= 0 || topk < 0) return 0;
       return sparse_decode_ws(B, H, topk);
@@ -82,15 +82,14 @@ int csa2_index_full(const csa2_cache_t* cache, int B, const int32_t* ctx_len, in
 int csa2_reindex(const csa2_cache_t* cache, int B, const int32_t* ctx_len, const uint16_t* q_idx,
                  const uint16_t* w_idx, const int32_t* pool, int pool_blocks, int cand_block,
                  int topk, int32_t* topk_idx, void* ws, size_t ws_bytes, void* stream) {
-  (void)ws;
-  (void)ws_bytes;
   if (!cache_ok(cache) || B <= 0 || !ctx_len || !q_idx || !w_idx || !pool || !topk_idx)
     return CSA2_EINVAL;
+  if (ws_bytes > 0 && !ws) return CSA2_EWORKSPACE;
   if (topk < 1 || topk > CSA2_MAX_TOPK || pool_blocks < 1) return CSA2_EINVAL;
   if (!pow2_in(cand_block, 1, 32)) return CSA2_EINVAL;
   if ((int64_t)pool_blocks * cand_block > 16384) return CSA2_EUNSUPPORTED;
   return launch_reindex(*cache, B, ctx_len, q_idx, w_idx, pool, pool_blocks, cand_block, topk,
-                        topk_idx, (hipStream_t)stream);
+                        topk_idx, ws, ws ? ws_bytes : 0, (hipStream_t)stream);
 }
 
 int csa2_sparse_decode(const csa2_cache_t* cache, int B, int H, const int32_t* ctx_len,

@@ -423,6 +423,106 @@ __global__ __launch_bounds__(kReindexThreads) void reindex_kernel(ReindexArgs a)
   for (int p = (int)sr.count + threadIdx.x; p < a.topk; p += kReindexThreads) out[p] = -1;
 }
 
+
+// Split Reindex, used when the caller passes a workspace.  One workgroup per sequence
+// leaves all but B CUs idle while it gathers the pool's keys, and a single CU pulls
+// scattered 272-byte pool blocks far slower than the GPU's bandwidth allows.  So the
+// scoring runs over (sequence, 512-slot slice) workgroups that write key images to
+// the workspace, and a second kernel selects the top-K of each sequence from them.
+constexpr int kReSlice = 512;
+constexpr int kReSelThreads = 1024;
+
+__global__ __launch_bounds__(256) void reindex_score_kernel(ReindexArgs a, uint32_t* __restrict__ keys_ws) {
+  const int b = blockIdx.x;
+  const int cb = a.cand_block;
+  const int N = a.pool_blocks * cb;
+  const int v0 = blockIdx.y * kReSlice;
+  if (v0 >= N) return;
+  int64_t L = a.ctx_len[b];
+  if (L < 0) L = 0;
+  const int64_t n_vis = L >> 1;
+  const int lane = threadIdx.x & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n = lane & 15, g = lane >> 4;
+  bf16x8 a0, a1;
+  load_q_frags(a.q_idx, b, a0, a1);
+  float wh[4];
+#pragma unroll
+  for (int h = 0; h < 4; ++h) wh[h] = bf16_to_f32(a.w_idx[b * CSA2_H_INDEX + h]);
+  const int32_t* pool = a.pool + (int64_t)b * a.pool_blocks;
+  constexpr int kGroups = kReSlice / 16 / 4;    // 16-slot groups per wave
+  // slot of group u for this lane: v0 + (wid * kGroups + u) * 16 + n
+  int blk[kGroups];
+#pragma unroll
+  for (int u = 0; u < kGroups; ++u) {
+    const int v = v0 + (wid * kGroups + u) * 16 + n;
+    blk[u] = v < N ? pool[v / cb] : -1;
+  }
+  int pg[kGroups];
+  int64_t ent[kGroups];
+#pragma unroll
+  for (int u = 0; u < kGroups; ++u) {
+    const int v = v0 + (wid * kGroups + u) * 16 + n;
+    ent[u] = (int64_t)blk[u] * cb + (v % cb);
+    pg[u] = (blk[u] >= 0 && ent[u] < n_vis) ? page_of(a.block_table, a.max_pages, a.n_pages, b, (int)ent[u]) : -1;
+  }
+  u32x2 cd[kGroups];
+  uint32_t sb[kGroups];
+#pragma unroll
+  for (int u = 0; u < kGroups; ++u) {
+    cd[u] = u32x2{0u, 0u};
+    sb[u] = 0u;
+    if (pg[u] >= 0) {
+      const int64_t row = (int64_t)pg[u] * CSA2_PAGE + (ent[u] & (CSA2_PAGE - 1));
+      cd[u] = *reinterpret_cast<const u32x2*>(a.idx_codes + row * CSA2_IDX_CODE_BYTES + 8 * g);
+      sb[u] = a.idx_scales[row * CSA2_IDX_SCALE_BYTES + (g >> 1)];
+    }
+  }
+  uint32_t* kout = keys_ws + (int64_t)b * kReindexCap;
+#pragma unroll
+  for (int u = 0; u < kGroups; ++u) {
+    const float s = score16(cd[u], sb[u], a0, a1, wh);
+    const int v = v0 + (wid * kGroups + u) * 16 + n;
+    if (lane < 16 && v < N) kout[v] = pg[u] >= 0 ? score_key(s) : 0u;
+  }
+}
+
+template <int KPT>
+__global__ __launch_bounds__(kReSelThreads) void reindex_select_kernel(ReindexArgs a, const uint32_t* __restrict__ keys_ws) {
+  __shared__ uint32_t hist[kSelectHist];
+  __shared__ uint32_t scratch[kSelectScratch];
+  const int b = blockIdx.x;
+  const int cb = a.cand_block;
+  const int N = a.pool_blocks * cb;
+  const int tid = threadIdx.x;
+  const int p0 = tid * KPT;
+  const int32_t* pool = a.pool + (int64_t)b * a.pool_blocks;
+  // this thread's slots p0..p0+KPT-1 span at most two pool blocks (KPT <= 2 * cb or
+  // the ids are re-read): fetch them before the select
+  const int blo = p0 < N ? pool[p0 / cb] : -1;
+  const int bhi = p0 + KPT - 1 < N ? pool[(p0 + KPT - 1) / cb] : -1;
+  const uint32_t* kin = keys_ws + (int64_t)b * kReindexCap;
+  uint32_t kr[KPT];
+#pragma unroll
+  for (int i = 0; i < KPT; i += 4) {
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (p0 + i < N) v = *reinterpret_cast<const u32x4*>(kin + p0 + i);
+    kr[i] = p0 + i < N ? v.x : 0u;
+    kr[i + 1] = p0 + i + 1 < N ? v.y : 0u;
+    kr[i + 2] = p0 + i + 2 < N ? v.z : 0u;
+    kr[i + 3] = p0 + i + 3 < N ? v.w : 0u;
+  }
+  const SelectResult sr = block_select<kReSelThreads, KPT>(kr, a.topk, hist, scratch);
+  int32_t* out = a.topk_idx + (int64_t)b * a.topk;
+  block_emit<kReSelThreads, KPT>(kr, sr, scratch, [&](int i, uint32_t pos) {
+    const int v = p0 + i;
+    const int bi = v / cb;
+    const int blk = bi == p0 / cb ? blo : (bi == (p0 + KPT - 1) / cb ? bhi : pool[bi]);
+    out[pos] = blk * cb + (v % cb);
+  });
+  for (int p = (int)sr.count + tid; p < a.topk; p += kReSelThreads) out[p] = -1;
+}
+
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Kernels here take up to ~80 KB of dynamic LDS (gfx950 has 160 KB per CU); raise
@@ -577,9 +677,11 @@ int launch_index_full(const csa2_cache_t& c, int B, const int32_t* ctx_len, int6
   return hip_status();
 }
 
+size_t reindex_ws(int B) { return align256((size_t)B * kReindexCap * 4); }
+
 int launch_reindex(const csa2_cache_t& c, int B, const int32_t* ctx_len, const uint16_t* q_idx,
                    const uint16_t* w_idx, const int32_t* pool, int pool_blocks, int cand_block,
-                   int topk, int32_t* topk_idx, hipStream_t s) {
+                   int topk, int32_t* topk_idx, void* ws, size_t ws_bytes, hipStream_t s) {
   if ((int64_t)pool_blocks * cand_block > kReindexCap) return CSA2_EUNSUPPORTED;
   if (!lds_limits_set()) return CSA2_EHIP;
   ReindexArgs ra;
@@ -597,6 +699,18 @@ int launch_reindex(const csa2_cache_t& c, int B, const int32_t* ctx_len, const u
   ra.topk = topk;
   ra.topk_idx = topk_idx;
   const int N = pool_blocks * cand_block;
+  if (ws && ws_bytes >= reindex_ws(B)) {
+    uint32_t* keys = static_cast<uint32_t*>(ws);
+    hipLaunchKernelGGL(reindex_score_kernel, dim3(B, (N + kReSlice - 1) / kReSlice), dim3(256), 0, s, ra, keys);
+    if (hip_status() != CSA2_OK) return CSA2_EHIP;
+    if (N <= 4 * kReSelThreads)
+      hipLaunchKernelGGL(reindex_select_kernel<4>, dim3(B), dim3(kReSelThreads), 0, s, ra, keys);
+    else if (N <= 8 * kReSelThreads)
+      hipLaunchKernelGGL(reindex_select_kernel<8>, dim3(B), dim3(kReSelThreads), 0, s, ra, keys);
+    else
+      hipLaunchKernelGGL(reindex_select_kernel<16>, dim3(B), dim3(kReSelThreads), 0, s, ra, keys);
+    return hip_status();
+  }
   const int kpt = N <= 8 * kReindexThreads ? 8 : (N <= 16 * kReindexThreads ? 16 : 32);
   const size_t lds = (size_t)(kpt * kReindexThreads + kSelectHist + kSelectScratch) * 4;
   if (kpt == 8)

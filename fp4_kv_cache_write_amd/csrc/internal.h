@@ -28,9 +28,13 @@ int launch_debug_gather(const csa2_cache_t& c, int B, const int32_t* idx, int n,
 int launch_index_full(const csa2_cache_t& c, int B, const int32_t* ctx_len, int64_t max_ctx,
                       const uint16_t* q_idx, const uint16_t* w_idx, int topk, int pool_blocks,
                       int cand_block, int32_t* topk_idx, int32_t* pool, void* ws, hipStream_t s);
+// Reindex: with a workspace of reindex_ws(B) bytes the pool is scored by many
+// workgroups per sequence and selected by a second kernel; without one, by one
+// workgroup per sequence.
+size_t reindex_ws(int B);
 int launch_reindex(const csa2_cache_t& c, int B, const int32_t* ctx_len, const uint16_t* q_idx,
                    const uint16_t* w_idx, const int32_t* pool, int pool_blocks, int cand_block,
-                   int topk, int32_t* topk_idx, hipStream_t s);
+                   int topk, int32_t* topk_idx, void* ws, size_t ws_bytes, hipStream_t s);
 size_t sparse_decode_ws(int B, int H, int topk);
 int launch_sparse_decode(const csa2_cache_t& c, int B, int H, const int32_t* ctx_len,
                          const uint16_t* q, const int32_t* topk_idx, int topk, const uint16_t* swa,

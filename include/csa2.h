@@ -138,8 +138,10 @@ int csa2_index_full(const csa2_cache_t *cache, int B, const int32_t *ctx_len, in
  *   ids, -1 entries ignored, each block covering cand_block entries), and writes the
  *   min(topk, pool size) best (ties: lower j) to topk_idx[b] in ascending order,
  *   padded with -1.  Shapes as in csa2_index_full; pool_blocks * cand_block <= 16384.
- *   ws: csa2_workspace_size(CSA2_FN_REINDEX, ...) bytes (0 in this build; ws may be
- *   NULL). */
+ *   ws: optional.  With ws_bytes >= csa2_workspace_size(CSA2_FN_REINDEX, B, 0, 0, topk,
+ *   pool_blocks, 0) (device memory) the pool is scored by many workgroups per
+ *   sequence and selected by a second pass; with ws == NULL by one workgroup per
+ *   sequence.  Results are the same. */
 int csa2_reindex(const csa2_cache_t *cache, int B, const int32_t *ctx_len, const uint16_t *q_idx,
                  const uint16_t *w_idx, const int32_t *pool, int pool_blocks, int cand_block,
                  int topk, int32_t *topk_idx, void *ws, size_t ws_bytes, void *stream);

@@ -89,9 +89,11 @@ def test_index_full_without_pool_and_repeatable(fk):
         check_topk_set(outs[0][b].numpy(), np.arange(n_vis), s, 512)
 
 
+@pytest.mark.parametrize("split", [True, False], ids=["split", "one-pass"])
 @pytest.mark.parametrize("ctx,pool_blocks,cb,topk", [((65536, 9000, 300), 512, 8, 512),
-                                                     ((20000,), 100, 4, 64), ((778,), 200, 8, 512)])
-def test_reindex_matches_oracle_on_oracle_pool(fk, ctx, pool_blocks, cb, topk):
+                                                     ((20000,), 100, 4, 64), ((778,), 200, 8, 512),
+                                                     ((60000,), 1024, 16, 300)])
+def test_reindex_matches_oracle_on_oracle_pool(fk, ctx, pool_blocks, cb, topk, split):
     cfg = small_decode(1, B=len(ctx), ctx=ctx, pages="random", heavy_frac=0.05, append=0)
     case = make_decode_case(cfg, "cpu")
     oc = oracle_cache_for(case)
@@ -104,7 +106,7 @@ def test_reindex_matches_oracle_on_oracle_pool(fk, ctx, pool_blocks, cb, topk):
         pools[b, :len(blocks)] = blocks
     ctx_len = torch.tensor(case.ctx_len, dtype=torch.int32, device="cuda")
     tk = fk.reindex(gc, ctx_len, L1["q_idx"].cuda(), L1["w_idx"].cuda(), torch.from_numpy(pools).cuda(),
-                    topk=topk, cand_block=cb)
+                    topk=topk, cand_block=cb, split=split)
     torch.cuda.synchronize()
     tk = tk.cpu().numpy()
     for b in range(case.B):
