@@ -58,9 +58,14 @@ __device__ __forceinline__ u32x4 fp4x8_to_bf16x8(uint32_t codes, float scale) {
 // -0 is folded onto +0 so that equal scores give equal keys.  Key 0 is reserved for
 // "no entry" (it would be a NaN pattern).
 __device__ __forceinline__ uint32_t score_key(float s) {
-  if (s == 0.0f) s = 0.0f;
-  uint32_t b = __float_as_uint(s);
-  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+  const uint32_t b = __float_as_uint(s + 0.0f);   // -0 + 0 = +0 under round-to-nearest
+  return b ^ ((uint32_t)((int32_t)b >> 31) | 0x80000000u);   // negative: ~b, else b | sign
+}
+
+// max(x, 0) for a non-NaN float, as one integer max on its bits: every negative
+// float (and -0) has a negative int32 pattern and maps to +0.
+__device__ __forceinline__ float relu0(float x) {
+  return __int_as_float(max(__float_as_int(x), 0));
 }
 
 __device__ __forceinline__ float key_score(uint32_t k) {

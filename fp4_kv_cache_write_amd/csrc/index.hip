@@ -73,8 +73,7 @@ __device__ __forceinline__ float score16(u32x2 codes, uint32_t scale_byte, bf16x
   acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, __builtin_bit_cast(bf16x8, lo), acc, 0, 0, 0);
   acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, __builtin_bit_cast(bf16x8, hi), acc, 0, 0, 0);
   // lanes 0..15: acc[i] = head i . key(l%16)
-  return wh[0] * fmaxf(acc[0], 0.f) + wh[1] * fmaxf(acc[1], 0.f) + wh[2] * fmaxf(acc[2], 0.f) +
-         wh[3] * fmaxf(acc[3], 0.f);
+  return wh[0] * relu0(acc[0]) + wh[1] * relu0(acc[1]) + wh[2] * relu0(acc[2]) + wh[3] * relu0(acc[3]);
 }
 
 struct ScanArgs {

@@ -50,6 +50,11 @@ struct PfIndexArgs {
   int n_units, per_xcd;
 };
 
+template <bool B>
+struct Check {
+  static constexpr bool value = B;
+};
+
 // Number of set bits of m at lanes below this one.
 __device__ __forceinline__ uint32_t lanes_below(uint64_t m) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
@@ -110,17 +115,20 @@ __device__ WaveSel wave_select(const uint32_t* kst, int cnt, uint32_t k, uint32_
 
 // Keep the selected pairs of list[0..cnt) in order -- back into the list (out ==
 // nullptr) or as entry ids into out -- and return how many were kept; *kmin gets
-// the smallest kept key.  sel_all keeps every pair.  The keys are copied into the
-// wave's LDS area kst with direct global->LDS loads (no registers held across the
-// scan); entry ids are read from the list only for the pairs kept.
-__device__ int list_keep(u32x2* list, int cnt, int topk, bool sel_all, uint32_t* kst, uint32_t* hist,
-                         int32_t* out, uint32_t* kmin) {
+// the smallest kept key.  sel_all keeps every pair.  Keys and entry ids are copied
+// into the wave's LDS areas kst and kid with direct global->LDS loads, all issued
+// before the one wait, so a compaction costs one memory round trip.
+__device__ int list_keep(u32x2* list, int cnt, int topk, bool sel_all, uint32_t* kst, uint32_t* kid,
+                         uint32_t* hist, int32_t* out, uint32_t* kmin) {
   const int lane = threadIdx.x & 63;
   const uint32_t* words = reinterpret_cast<const uint32_t*>(list);
   const int nr = (cnt + 63) >> 6;
   for (int r = 0; r < nr; ++r) {
     const int p = 64 * r + lane;
-    if (p < cnt) __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(words + 2 * p), kst + 64 * r, 4, 0, 0);
+    if (p < cnt) {
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(words + 2 * p), kst + 64 * r, 4, 0, 0);
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(words + 2 * p + 1), kid + 64 * r, 4, 0, 0);
+    }
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
@@ -135,9 +143,7 @@ __device__ int list_keep(u32x2* list, int cnt, int topk, bool sel_all, uint32_t*
     const bool sel = x != 0u && (x > s.thr || (eq && eq_before + lanes_below(meq) < s.krem));
     const uint64_t ms = __ballot(sel);
     const uint32_t dst = kept + lanes_below(ms);
-    // the row's ids are read before any of its kept pairs is written back (dst <= p,
-    // and earlier rows were written before this row was read)
-    const int32_t id = sel ? (int32_t)words[2 * p + 1] : -1;
+    const int32_t id = sel ? (int32_t)kid[p] : -1;
     if (sel) {
       if (out) {
         out[dst] = id;
@@ -160,6 +166,7 @@ __global__ __launch_bounds__(64) void prefill_index_kernel(PfIndexArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint32_t pf_lds[];
   uint32_t* hist = pf_lds;             // [256]
   uint32_t* kst = pf_lds + kPfHist;    // [cap] keys of the list being compacted
+  uint32_t* kid = kst + a.cap;         // [cap] its entry ids
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
   const int unit = xcd * a.per_xcd + slot;   // contiguous query groups per XCD
   if (slot >= a.per_xcd || unit >= a.n_units) return;
@@ -177,6 +184,8 @@ __global__ __launch_bounds__(64) void prefill_index_kernel(PfIndexArgs a) {
     return (int)(L >> 1);
   };
   const int nv = n_vis(i0 + g);                       // this lane's query
+  // fewest entries seen by any of the four queries (0 when the chunk ends inside the group)
+  const int nv_min = (i0 + kPfQ - 1 < a.C) ? n_vis(i0) : 0;
   const int nv_max = n_vis(min(i0 + kPfQ - 1, a.C - 1));
 
   // A operand: row m = l%16 is head m%4 of query i0 + m/4, dims 16g .. 16g+15.
@@ -232,6 +241,37 @@ __global__ __launch_bounds__(64) void prefill_index_kernel(PfIndexArgs a) {
       }
     }
   };
+  // Scores the 64 entries of a staged page for the wave's four queries and appends
+  // those above the query's threshold to its list.  Check<true> also tests each
+  // entry against the query's visible count.
+  auto score_page = [&](const Page& pg, int p, auto chk) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const float sc = e8m0_scale(pg.sb[t]);
+      u32x4 lo, hi;
+      lo.x = fp4x2_to_bf16x2<0>(pg.cd[t].x, sc);
+      lo.y = fp4x2_to_bf16x2<1>(pg.cd[t].x, sc);
+      lo.z = fp4x2_to_bf16x2<2>(pg.cd[t].x, sc);
+      lo.w = fp4x2_to_bf16x2<3>(pg.cd[t].x, sc);
+      hi.x = fp4x2_to_bf16x2<0>(pg.cd[t].y, sc);
+      hi.y = fp4x2_to_bf16x2<1>(pg.cd[t].y, sc);
+      hi.z = fp4x2_to_bf16x2<2>(pg.cd[t].y, sc);
+      hi.w = fp4x2_to_bf16x2<3>(pg.cd[t].y, sc);
+      f32x4 d = {0.f, 0.f, 0.f, 0.f};
+      d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, __builtin_bit_cast(bf16x8, lo), d, 0, 0, 0);
+      d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, __builtin_bit_cast(bf16x8, hi), d, 0, 0, 0);
+      // lane l: d[i] = head i of query l/16 against entry l%16 of the group
+      const float s = wh[0] * relu0(d[0]) + wh[1] * relu0(d[1]) + wh[2] * relu0(d[2]) + wh[3] * relu0(d[3]);
+      const int e = p * CSA2_PAGE + 16 * t + n;
+      const bool app = pg.ok && (!decltype(chk)::value || e < nv) && s > tau_s;
+      const uint64_t m = __builtin_amdgcn_ballot_w64(app);
+      if (m) {
+        const uint32_t mg = (uint32_t)(m >> (16 * g)) & 0xffffu;
+        if (app) lq[cnt + __builtin_popcount(mg & ((1u << n) - 1u))] = u32x2{score_key(s), (uint32_t)e};
+        cnt += __builtin_popcount(mg);
+      }
+    }
+  };
   Page p0, p1;
   load_page(0, __builtin_amdgcn_readlane(bt_cur, 0), p0);
   load_page(1, __builtin_amdgcn_readlane(bt_cur, 1), p1);
@@ -247,32 +287,11 @@ __global__ __launch_bounds__(64) void prefill_index_kernel(PfIndexArgs a) {
     Page p2;
     load_page(lp, __builtin_amdgcn_readlane(bt_cur, lp & 63), p2);
 
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const float sc = e8m0_scale(p0.sb[t]);
-      u32x4 lo, hi;
-      lo.x = fp4x2_to_bf16x2<0>(p0.cd[t].x, sc);
-      lo.y = fp4x2_to_bf16x2<1>(p0.cd[t].x, sc);
-      lo.z = fp4x2_to_bf16x2<2>(p0.cd[t].x, sc);
-      lo.w = fp4x2_to_bf16x2<3>(p0.cd[t].x, sc);
-      hi.x = fp4x2_to_bf16x2<0>(p0.cd[t].y, sc);
-      hi.y = fp4x2_to_bf16x2<1>(p0.cd[t].y, sc);
-      hi.z = fp4x2_to_bf16x2<2>(p0.cd[t].y, sc);
-      hi.w = fp4x2_to_bf16x2<3>(p0.cd[t].y, sc);
-      f32x4 d = {0.f, 0.f, 0.f, 0.f};
-      d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, __builtin_bit_cast(bf16x8, lo), d, 0, 0, 0);
-      d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, __builtin_bit_cast(bf16x8, hi), d, 0, 0, 0);
-      // lane l: d[i] = head i of query l/16 against entry l%16 of the group
-      const float s = wh[0] * fmaxf(d[0], 0.f) + wh[1] * fmaxf(d[1], 0.f) + wh[2] * fmaxf(d[2], 0.f) +
-                      wh[3] * fmaxf(d[3], 0.f);
-      const int e = p * CSA2_PAGE + 16 * t + n;
-      const bool app = p0.ok && e < nv && s > tau_s;
-      const uint64_t m = __ballot(app);
-      if (m) {
-        const uint32_t mg = (uint32_t)(m >> (16 * g)) & 0xffffu;
-        if (app) lq[cnt + __builtin_popcount(mg & ((1u << n) - 1u))] = u32x2{score_key(s), (uint32_t)e};
-        cnt += __builtin_popcount(mg);
-      }
+    // only the last pages hold entries that some of the four queries cannot see
+    if ((p + 1) * CSA2_PAGE <= nv_min) {
+      score_page(p0, p, Check<false>{});
+    } else {
+      score_page(p0, p, Check<true>{});
     }
     p0 = p1;
     p1 = p2;
@@ -285,7 +304,7 @@ __global__ __launch_bounds__(64) void prefill_index_kernel(PfIndexArgs a) {
         const int c = __builtin_amdgcn_readlane(cnt, 16 * qq);
         if (c <= a.cap - CSA2_PAGE) continue;
         uint32_t mn;
-        const int kept = list_keep(list0 + (int64_t)qq * a.cap, c, a.topk, false, kst, hist, nullptr, &mn);
+        const int kept = list_keep(list0 + (int64_t)qq * a.cap, c, a.topk, false, kst, kid, hist, nullptr, &mn);
         if (g == qq) {
           cnt = kept;
           tau = mn;
@@ -305,7 +324,7 @@ __global__ __launch_bounds__(64) void prefill_index_kernel(PfIndexArgs a) {
     const int c = __builtin_amdgcn_readlane(cnt, 16 * qq);
     int32_t* out = a.topk_idx + ((int64_t)b * a.C + i0 + qq) * a.topk;
     uint32_t mn;
-    const int kept = list_keep(list0 + (int64_t)qq * a.cap, c, a.topk, c <= a.topk, kst, hist, out, &mn);
+    const int kept = list_keep(list0 + (int64_t)qq * a.cap, c, a.topk, c <= a.topk, kst, kid, hist, out, &mn);
     for (int r = kept + lane; r < a.topk; r += 64) out[r] = -1;
   }
 }
@@ -353,7 +372,7 @@ int launch_prefill_chunk(const csa2_cache_t& c, int B, int H, const int32_t* pri
   if (units > 0x0fffffff) return CSA2_EUNSUPPORTED;
   a.n_units = (int)units;
   a.per_xcd = (int)((units + 7) / 8);
-  const size_t lds = (size_t)(kPfHist + a.cap) * 4;
+  const size_t lds = (size_t)(kPfHist + 2 * a.cap) * 4;
   hipLaunchKernelGGL(prefill_index_kernel, dim3(8u * (unsigned)a.per_xcd), dim3(64), lds, s, a);
   const int rc = hip_status();
   if (rc != CSA2_OK) return rc;
