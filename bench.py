@@ -54,7 +54,9 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seqs", type=int, default=2, help="sequences in the oracle's timed sample")
     p.add_argument("--no-graph", action="store_true", help="time eager launches instead of graph replay")
-    p.add_argument("--serial", action="store_true", help="issue every call of a step on one stream")
+    p.add_argument("--overlap-layers", action="store_true",
+                   help="fork each layer's attention onto its own stream (ignores that a layer's queries "
+                        "come from the previous layer's output; for reference only)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="first run one 256 MiB device-to-device copy, whose counter readings "
                         "(rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE) scale those of the kernels")
@@ -157,7 +159,7 @@ def decode_bytes(case):
 
 
 def bench_decode(fk, cfg_id: int, steps: int, warmup: int, n_rep: int, use_graph: bool, per_call_timing: bool,
-                 concurrent: bool = True):
+                 concurrent: bool = False):
     from synth import CONFIGS, make_decode_case
     cfg = CONFIGS[cfg_id]
     log(f"building {cfg.name} ({n_rep} replicas)")
@@ -172,6 +174,7 @@ def bench_decode(fk, cfg_id: int, steps: int, warmup: int, n_rep: int, use_graph
     pool_blocks = max([sp.pool_blocks for sp in cfg.layers] + [0])
     ws_full = fk.workspace(fk.FN_INDEX_FULL, device=dev, B=B, max_ctx=max_ctx, topk=topk, pool_blocks=pool_blocks)
     ws_re = fk.workspace(fk.FN_REINDEX, device=dev, B=B, topk=topk, pool_blocks=max(pool_blocks, 1))
+    ws_att = fk.workspace(fk.FN_SPARSE_DECODE, device=dev, B=B, H=H, topk=topk)
     tk_buf = [torch.empty((B, topk), dtype=torch.int32, device=dev) for _ in range(2)]
     pool = torch.empty((B, max(pool_blocks, 1)), dtype=torch.int32, device=dev)
     outs = [torch.empty((B, H, 512), dtype=torch.bfloat16, device=dev) for _ in cfg.layers]
@@ -201,13 +204,14 @@ def bench_decode(fk, cfg_id: int, steps: int, warmup: int, n_rep: int, use_graph
                                                                      topk_idx=tk, ws=ws_re)))
                 cur = tk
             out.append(("sparse_decode", lambda L=L, tk=cur, l=l: fk.sparse_decode(
-                R.cache, ctx, L["q"], tk, L["swa"], out=outs[l], lse=lses[l])))
+                R.cache, ctx, L["q"], tk, L["swa"], out=outs[l], lse=lses[l], ws=ws_att)))
         return out
 
-    # The selector calls (write, Full, Reindex) form one chain on the launching stream;
-    # each layer's attention needs only its selector's output, so it is forked onto a
-    # stream of its own and joined back at the end of the step.  Attention of layer l
-    # then runs beside the next layer's Reindex and beside the other layers' attention.
+    # Default: the step's calls run in layer order on one stream, as a model must run
+    # them (layer l+1's indexer and attention queries come from layer l's output).
+    # With concurrent=True the selector chain (write, Full, Reindex) stays on the
+    # launching stream and each layer's attention is forked onto a stream of its own;
+    # that overlaps layers a model cannot overlap and is kept only for reference.
     side = [torch.cuda.Stream() for _ in cfg.layers] if concurrent else []
 
     def run_step(r):
@@ -409,13 +413,13 @@ def main() -> int:
         return 0
 
     cfg_id = {"c1": 1, "c2": 2, "c4": 4}[args.workload]
-    d = bench_decode(fk, cfg_id, args.steps, args.warmup, args.replicas, not args.no_graph, True, not args.serial)
+    d = bench_decode(fk, cfg_id, args.steps, args.warmup, args.replicas, not args.no_graph, True, args.overlap_layers)
     case = d["case"]
     cfg = case.cfg
     secondary = {}
     if args.workload == "c1" and not args.no_secondary:
         c2 = bench_decode(fk, 2, max(20, args.steps // 4), max(5, args.warmup // 4), 4, not args.no_graph, True,
-                          not args.serial)
+                          args.overlap_layers)
         secondary["c2_b8_ctx1m"] = {
             "workload": c2["case"].cfg.name, "value": round(c2["qps"], 1), "unit": "queries/s",
             "ms_per_step": round(c2["ms"], 5), "achieved_gbs": round(c2["gbs"], 1),
@@ -448,7 +452,8 @@ def main() -> int:
                    "pool_blocks": max([sp.pool_blocks for sp in cfg.layers] + [0]), "cand_block": cfg.cand_block,
                    "layers": ",".join(sp.mode for sp in cfg.layers), "write_per_step": True,
                    "replicas": len(d["reps"]), "launch": ("hip-graph" if d["use_graph"] else "eager") +
-                   ("; each layer's attention on its own forked stream" if not args.serial else "; one stream")},
+                   ("; each layer's attention on its own forked stream (layers overlapped)" if args.overlap_layers
+                    else "; layers in order on one stream")},
         "algorithmic_bytes_per_step": d["step_bytes"],
         "achieved_gbs": round(d["gbs"], 1),
         "frac_hbm_peak": round(d["gbs"] / HBM_PEAK_GBS, 4),

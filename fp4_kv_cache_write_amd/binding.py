@@ -219,8 +219,9 @@ def sparse_decode(cache: PagedCache, ctx_len: torch.Tensor, q: torch.Tensor, top
         out = torch.empty((B, H, D_LATENT), dtype=torch.bfloat16, device=q.device)
     if lse is None and want_lse:
         lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
-    if ws is None:
-        ws = workspace(FN_SPARSE_DECODE, device=q.device, B=B, H=H, topk=topk)
+    if ws is None:   # split partials: every byte used is written first, no clearing needed
+        n = workspace_size(FN_SPARSE_DECODE, B=B, H=H, topk=topk)
+        ws = torch.empty(n, dtype=torch.uint8, device=q.device) if n > 0 else None
     wsb = ws.numel() if ws is not None else 0
     _check(lib().csa2_sparse_decode(cache.ref, B, H, _ptr(ctx_len), _ptr(q), _ptr(topk_idx), topk,
                                     _ptr(swa), W, sm_scale, _ptr(out), _ptr(lse), _ptr(ws), wsb,

@@ -99,10 +99,9 @@ int csa2_sparse_decode(const csa2_cache_t* cache, int B, int H, const int32_t* c
   if (!cache_ok(cache) || B <= 0 || !ctx_len || !q || !swa || !out) return CSA2_EINVAL;
   if (H <= 0 || (H % 16) != 0 || W < 1 || W > CSA2_MAX_WINDOW) return CSA2_EINVAL;
   if (topk < 0 || topk > CSA2_MAX_TOPK || (topk > 0 && !topk_idx)) return CSA2_EINVAL;
-  const size_t need = sparse_decode_ws(B, H, topk);
-  if (need > 0 && (!ws || ws_bytes < need)) return CSA2_EWORKSPACE;
+  if (ws_bytes > 0 && !ws) return CSA2_EWORKSPACE;   // the workspace is optional
   return launch_sparse_decode(*cache, B, H, ctx_len, q, topk_idx, topk, swa, W, sm_scale, out, lse,
-                              ws, (hipStream_t)stream);
+                              ws, ws_bytes, (hipStream_t)stream);
 }
 
 int csa2_prefill_chunk(const csa2_cache_t* cache, int B, int H, const int32_t* prior_len,

@@ -83,8 +83,35 @@ struct DecArgs {
   float scale_log2;        // sm_scale * log2(e)
   uint16_t* out;
   float* lse;
-  int B, C, H, HG, prefill, q_per_xcd;
+  float* part;             // split: [B*C*HG][nsplit][kPartFloats]
+  int B, C, H, HG, prefill, q_per_xcd, nsplit;
 };
+
+// Split launches: the rows of a (query, head group) are spread over nsplit
+// workgroups, each leaving a partial softmax state -- m[16] (running max, log2
+// units), l[16] (sum of 2^(z - m)) and the unnormalised O[16][512] -- that
+// attn_combine_kernel merges.
+constexpr int kPartFloats = 32 + 16 * CSA2_D_LATENT;
+constexpr int kMaxSplit = 8;
+constexpr int kSplitBelow = 256;   // launches with fewer workgroups than CUs split
+
+// Rows of split sp: the window tiles then the FP4 tiles (32 rows each) are cut into
+// nsplit contiguous runs of equal tile counts.  (A window tile needs no
+// dequantisation, but window batches hold only two tiles, so their fixed per-batch
+// cost makes the two kinds of tile cost about the same.)  Gives window rows
+// [w0, w1) and FP4 rows [f0, f1).
+__device__ __forceinline__ void split_rows(int W, int topk, int nsplit, int sp, int& w0, int& w1, int& f0,
+                                           int& f1) {
+  const int nwt = (W + 31) >> 5, nft = (topk + 31) >> 5;
+  auto cut = [&](int j) -> int {   // tile position (window tiles first) of boundary j
+    return (int)(((int64_t)j * (nwt + nft) + nsplit - 1) / nsplit);
+  };
+  const int p0 = cut(sp), p1 = cut(sp + 1);
+  w0 = min(32 * min(p0, nwt), W);
+  w1 = min(32 * min(p1, nwt), W);
+  f0 = min(32 * max(p0 - nwt, 0), topk);
+  f1 = min(32 * max(p1 - nwt, 0), topk);
+}
 
 // low halves of a and b -> (a.lo, b.lo); high halves -> (a.hi, b.hi)
 __device__ __forceinline__ uint32_t pack_lo(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x05040100u); }
@@ -217,10 +244,14 @@ __global__ __launch_bounds__(kThreads) void sparse_decode_kernel(DecArgs a) {
 
   // XCD-aware mapping: consecutive workgroup ids go to different XCDs; XCD x takes
   // the contiguous query range [x * q_per_xcd, (x+1) * q_per_xcd), all head groups.
+  // A split launch gives each (query, head group) nsplit consecutive workgroups.
   const int xcd = blockIdx.x & 7;
   const int li = blockIdx.x >> 3;
-  const int ql = li / a.HG;
-  const int hg = li - ql * a.HG;
+  const int per_q = a.HG * a.nsplit;
+  const int ql = li / per_q;
+  const int rem = li - ql * per_q;
+  const int hg = rem / a.nsplit;
+  const int sp = rem - hg * a.nsplit;
   const int64_t qi = (int64_t)xcd * a.q_per_xcd + ql;
   if (ql >= a.q_per_xcd || qi >= (int64_t)a.B * a.C) return;
   const int b = (int)(qi / a.C);
@@ -229,6 +260,10 @@ __global__ __launch_bounds__(kThreads) void sparse_decode_kernel(DecArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15, g = lane >> 4;
+
+  // this workgroup's rows: window rows [wr0, wr1), FP4 rows [fr0, fr1) of topk_idx
+  int wr0 = 0, wr1 = a.W, fr0 = 0, fr1 = a.topk;
+  if (a.nsplit > 1) split_rows(a.W, a.topk, a.nsplit, sp, wr0, wr1, fr0, fr1);
 
   int64_t Lq = a.len[b];
   if (Lq < 0) Lq = 0;
@@ -239,8 +274,8 @@ __global__ __launch_bounds__(kThreads) void sparse_decode_kernel(DecArgs a) {
   const int32_t* tk = a.topk_idx + qi * a.topk;
   const int32_t* bt = a.block_table + (int64_t)b * a.max_pages;
 
-  const int n_wb = (a.W + kWinBatch - 1) / kWinBatch;
-  const int n_fb = a.topk > 0 ? (a.topk + kFp4Batch - 1) / kFp4Batch : 0;
+  const int n_wb = (wr1 - wr0 + kWinBatch - 1) / kWinBatch;
+  const int n_fb = (fr1 - fr0 + kFp4Batch - 1) / kFp4Batch;
   const int nb = n_wb + n_fb;
 
   // row id of entry e (-1: invalid id, absent page)
@@ -250,8 +285,8 @@ __global__ __launch_bounds__(kThreads) void sparse_decode_kernel(DecArgs a) {
   auto page_ok = [&](int e) { return e >= 0 && e < n_vis && (e >> 6) < a.max_pages; };
   // FP4 batch f >= 2: ids resolved when the batch is issued
   auto resolve_rows = [&](int f) {
-    const int r0 = f * kFp4Batch;
-    const int nrows = min(a.topk - r0, kFp4Batch);
+    const int r0 = fr0 + f * kFp4Batch;
+    const int nrows = min(fr1 - r0, kFp4Batch);
     int32_t* rowid = rowid_all + (f & 1) * kFp4Batch;
     for (int i = tid; i < kFp4Batch; i += kThreads) {
       const int e = i < nrows ? tk[r0 + i] : -1;
@@ -265,14 +300,14 @@ __global__ __launch_bounds__(kThreads) void sparse_decode_kernel(DecArgs a) {
 #pragma unroll
     for (int u = 0; u < kStage; ++u) st[u] = u32x4{0u, 0u, 0u, 0u};
     if (k < n_wb) {
-      const int w0 = k * kWinBatch;
+      const int w0 = wr0 + k * kWinBatch;
       int slot0 = (t - (a.W - 1) + w0) % a.W;   // ring slot of the batch's first position
       if (slot0 < 0) slot0 += a.W;
 #pragma unroll
       for (int u = 0; u < kWinBatch * 64 / kThreads; ++u) {
         const int c = tid + kThreads * u;
         const int r = c >> 6, piece = c & 63;
-        if (win_valid(a.W, t, w0 + r)) {
+        if (w0 + r < wr1 && win_valid(a.W, t, w0 + r)) {
           int row;
           if (a.prefill) {
             row = ci + w0 + r;
@@ -285,7 +320,7 @@ __global__ __launch_bounds__(kThreads) void sparse_decode_kernel(DecArgs a) {
       }
     } else {
       const int f = k - n_wb;
-      const int nrows = min(a.topk - f * kFp4Batch, kFp4Batch);
+      const int nrows = min(fr1 - fr0 - f * kFp4Batch, kFp4Batch);
       const int32_t* rowid = rowid_all + (f & 1) * kFp4Batch;
 #pragma unroll
       for (int u = 0; u < kStage; ++u) {
@@ -320,8 +355,8 @@ __global__ __launch_bounds__(kThreads) void sparse_decode_kernel(DecArgs a) {
   u32x4 st[kStage];
   if (n_wb > 0) load_batch(0, st);
   const int pf_i = tid & (kFp4Batch - 1), pf_f = tid >> 8;
-  const int pf_r = pf_f * kFp4Batch + pf_i;
-  const int pf_e = (pf_f < n_fb && pf_r < a.topk) ? tk[pf_r] : -1;
+  const int pf_r = fr0 + pf_f * kFp4Batch + pf_i;
+  const int pf_e = (pf_f < n_fb && pf_r < fr1) ? tk[pf_r] : -1;
   u32x4 qf[16];   // q operand of head hg*16+n: dims 128g + 8s .. +7 for k-step s
   {
     const uint16_t* qp = a.q + (qi * a.H + hg * 16 + n) * CSA2_D_LATENT + 128 * g;
@@ -329,7 +364,16 @@ __global__ __launch_bounds__(kThreads) void sparse_decode_kernel(DecArgs a) {
     for (int s = 0; s < 16; ++s) qf[s] = *reinterpret_cast<const u32x4*>(qp + 8 * s);
   }
   int pf_page = -1;
-  if (n_wb > 0) store_batch(0, st);
+  if (n_wb > 0) {
+    store_batch(0, st);
+  } else if (n_fb > 0) {
+    // the run starts with FP4 rows (split launches): resolve the prefetched ids now
+    if (page_ok(pf_e)) pf_page = bt[pf_e >> 6];
+    rowid_all[tid] = row_of(pf_e, pf_page);
+    __syncthreads();
+    load_batch(0, st);
+    store_batch(0, st);
+  }
   // q and the entry ids have arrived before the loop starts: the wait counts inside
   // the loop then cover only the next batch's loads, which stay in flight until the
   // batch is stored after PV.
@@ -345,13 +389,13 @@ __global__ __launch_bounds__(kThreads) void sparse_decode_kernel(DecArgs a) {
     const bool is_win = k < n_wb;
     uint8_t* buf = lds + kOffBuf + (k & 1) * kBufBytes;
     const int f = k - n_wb;
-    const int w0 = k * kWinBatch;
-    const int nrows = is_win ? min(a.W - w0, kWinBatch) : min(a.topk - f * kFp4Batch, kFp4Batch);
+    const int w0 = wr0 + k * kWinBatch;
+    const int nrows = is_win ? min(wr1 - w0, kWinBatch) : min(fr1 - fr0 - f * kFp4Batch, kFp4Batch);
     const int32_t* rowid = rowid_all + (f & 1) * kFp4Batch;
     const int ntl = (nrows + 31) >> 5;
 
     __syncthreads();   // batch k stored by every thread; batch k-1 fully consumed
-    if (k == 0 && page_ok(pf_e)) pf_page = bt[pf_e >> 6];   // page lookups, consumed later
+    if (k == 0 && n_wb > 0 && page_ok(pf_e)) pf_page = bt[pf_e >> 6];   // page lookups, consumed later
     if (k + 1 < nb) {
       const int f1 = k + 1 - n_wb;
       if (f1 == 0) {              // first FP4 batch: row ids of the two prefetched batches
@@ -452,6 +496,21 @@ __global__ __launch_bounds__(kThreads) void sparse_decode_kernel(DecArgs a) {
   l_head += __shfl_xor(l_head, 32, kWave);
   if (g == 0) l_w[wid * 16 + n] = l_head;
   __syncthreads();
+  if (a.nsplit > 1) {   // partial state of this run of rows
+    float* part = a.part + ((qi * a.HG + hg) * a.nsplit + sp) * (int64_t)kPartFloats;
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii)
+      *reinterpret_cast<f32x4*>(part + 32 + (4 * g + ii) * CSA2_D_LATENT + 64 * wid + 4 * n) =
+          f32x4{acc[0][ii], acc[1][ii], acc[2][ii], acc[3][ii]};
+    if (wid == 0 && g == 0) {
+      float sl = 0.f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) sl += l_w[w * 16 + n];
+      part[n] = m_run;
+      part[16 + n] = sl;
+    }
+    return;
+  }
   float lh[4];
 #pragma unroll
   for (int ii = 0; ii < 4; ++ii) {
@@ -818,18 +877,90 @@ bool lds_limit_set() {
   return ok;
 }
 
+// Merge the split partials of one (query, head group): with m* the largest partial
+// maximum, weights 2^(m_s - m*) scale each partial's sum and output, as in the
+// log-sum-exp merge of softmax blocks.  Thread t: head t/32, dims 16(t%32) .. +15.
+// Every load is issued before the first is used (one memory round trip).
+__global__ __launch_bounds__(512) void attn_combine_kernel(const float* __restrict__ part, int nsplit,
+                                                          int64_t n_pairs, uint16_t* __restrict__ out,
+                                                          float* __restrict__ lse) {
+  const int64_t qh = blockIdx.x;
+  if (qh >= n_pairs) return;
+  const int tid = threadIdx.x, h = tid >> 5, d0 = (tid & 31) * 16;
+  const float* p0 = part + qh * nsplit * (int64_t)kPartFloats;
+  float ms[kMaxSplit], ls[kMaxSplit];
+  f32x4 os[kMaxSplit][4];
+#pragma unroll
+  for (int s = 0; s < kMaxSplit; ++s) {
+    ms[s] = -INFINITY;
+    ls[s] = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) os[s][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (s < nsplit) {
+      const float* ps = p0 + s * kPartFloats;
+      ms[s] = ps[h];
+      ls[s] = ps[16 + h];
+      const f32x4* src = reinterpret_cast<const f32x4*>(ps + 32 + h * CSA2_D_LATENT + d0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) os[s][i] = src[i];
+    }
+  }
+  float m = -INFINITY;
+#pragma unroll
+  for (int s = 0; s < kMaxSplit; ++s) m = fmaxf(m, ms[s]);
+  float l = 0.f;
+  f32x4 o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < kMaxSplit; ++s) {
+    const float w = ms[s] == -INFINITY ? 0.f : exp2f(ms[s] - m);   // runs with no valid row drop out
+    l += w * ls[s];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) o[i][j] += w * os[s][i][j];
+    }
+  }
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+  uint32_t wv[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    wv[2 * i] = f32_to_bf16_rne(o[i][0] * inv) | (f32_to_bf16_rne(o[i][1] * inv) << 16);
+    wv[2 * i + 1] = f32_to_bf16_rne(o[i][2] * inv) | (f32_to_bf16_rne(o[i][3] * inv) << 16);
+  }
+  u32x4* dst = reinterpret_cast<u32x4*>(out + (qh * 16 + h) * CSA2_D_LATENT + d0);
+  dst[0] = u32x4{wv[0], wv[1], wv[2], wv[3]};
+  dst[1] = u32x4{wv[4], wv[5], wv[6], wv[7]};
+  if (lse && (tid & 31) == 0) lse[qh * 16 + h] = l > 0.f ? (m + log2f(l)) * kLn2 : -INFINITY;
+}
+
+// Workgroups per (query, head group): enough to give every CU one, at most
+// kMaxSplit, and at least two 32-row tiles each.
+int split_count(int64_t nq, int HG, int W, int topk) {
+  const int64_t pairs = nq * HG;
+  if (pairs <= 0 || pairs >= kSplitBelow) return 1;
+  int s = (int)std::min<int64_t>(kMaxSplit, kSplitBelow / pairs);
+  const int tiles = (W + 31) / 32 + (topk + 31) / 32;
+  s = min(s, max(1, tiles / 2));   // at least two tiles per run
+  return max(s, 1);
+}
+
 }  // namespace
 
 size_t sparse_decode_ws(int B, int H, int topk) {
-  (void)B;
-  (void)H;
   (void)topk;
-  return 0;
+  const int HG = H / 16;
+  const int64_t pairs = (int64_t)B * HG;
+  if (pairs <= 0 || pairs >= kSplitBelow) return 0;
+  const int64_t s = std::min<int64_t>(kMaxSplit, kSplitBelow / pairs);
+  return (size_t)(pairs * s * kPartFloats * 4);
 }
 
 int launch_gather_attention(const csa2_cache_t& c, int B, int C, int H, const int32_t* len, bool prefill,
                             const uint16_t* q, const int32_t* topk_idx, int topk, const uint16_t* win,
-                            int W, float sm_scale, uint16_t* out, float* lse, hipStream_t s) {
+                            int W, float sm_scale, uint16_t* out, float* lse, hipStream_t s, void* ws,
+                            size_t ws_bytes) {
   if (!lds_limit_set()) return CSA2_EHIP;
   DecArgs a;
   a.lat_codes = c.lat_codes;
@@ -851,27 +982,42 @@ int launch_gather_attention(const csa2_cache_t& c, int B, int C, int H, const in
   a.H = H;
   a.HG = H / 16;
   a.prefill = prefill ? 1 : 0;
-  const int64_t per = ((int64_t)B * C + 7) / 8;
+  a.part = nullptr;
+  a.nsplit = 1;
+  const int64_t nq = (int64_t)B * C;
+  const int64_t per = (nq + 7) / 8;
   a.q_per_xcd = (int)per;
   // 64 heads per workgroup do more arithmetic per byte but four times the work per
   // workgroup: worth it once the queries alone give every CU a couple of workgroups.
-  if (H % 64 == 0 && (int64_t)B * C >= kH64MinQueries) {
+  if (H % 64 == 0 && nq >= kH64MinQueries) {
     const int64_t grid = 8 * per * (H / 64);
     if (grid > 0x7fffffff) return CSA2_EUNSUPPORTED;
     hipLaunchKernelGGL(sparse_decode64_kernel, dim3((unsigned)grid), dim3(kThreads), kLds64, s, a);
-  } else {
-    const int64_t grid = 8 * per * a.HG;
-    if (grid > 0x7fffffff) return CSA2_EUNSUPPORTED;
-    hipLaunchKernelGGL(sparse_decode_kernel, dim3((unsigned)grid), dim3(kThreads), kLdsBytes, s, a);
+    return hip_status();
+  }
+  const int ns = split_count(nq, a.HG, W, topk);
+  if (ns > 1 && ws && ws_bytes >= (size_t)(nq * a.HG * ns * kPartFloats * 4)) {
+    a.part = static_cast<float*>(ws);
+    a.nsplit = ns;
+  }
+  const int64_t grid = 8 * per * a.HG * a.nsplit;
+  if (grid > 0x7fffffff) return CSA2_EUNSUPPORTED;
+  hipLaunchKernelGGL(sparse_decode_kernel, dim3((unsigned)grid), dim3(kThreads), kLdsBytes, s, a);
+  if (a.nsplit > 1) {
+    const int rc = hip_status();
+    if (rc != CSA2_OK) return rc;
+    hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)(nq * a.HG)), dim3(512), 0, s, a.part, a.nsplit,
+                       nq * a.HG, out, lse);
   }
   return hip_status();
 }
 
 int launch_sparse_decode(const csa2_cache_t& c, int B, int H, const int32_t* ctx_len,
                          const uint16_t* q, const int32_t* topk_idx, int topk, const uint16_t* swa,
-                         int W, float sm_scale, uint16_t* out, float* lse, void* ws, hipStream_t s) {
-  (void)ws;
-  return launch_gather_attention(c, B, 1, H, ctx_len, false, q, topk_idx, topk, swa, W, sm_scale, out, lse, s);
+                         int W, float sm_scale, uint16_t* out, float* lse, void* ws, size_t ws_bytes,
+                         hipStream_t s) {
+  return launch_gather_attention(c, B, 1, H, ctx_len, false, q, topk_idx, topk, swa, W, sm_scale, out, lse, s,
+                                 ws, ws_bytes);
 }
 
 }  // namespace csa2

@@ -157,8 +157,12 @@ int csa2_reindex(const csa2_cache_t *cache, int B, const int32_t *ctx_len, const
  *   Reuse mode ([P1] §2.3.2) is this call with an earlier layer's topk_idx.
  *   q: [B][H][512] bf16; topk_idx: [B][topk] int32; swa: [B][W][512] bf16;
  *   out: [B][H][512] bf16; lse: [B][H] float or NULL (all device).  H a multiple of
- *   16; 1 <= W <= 1024; 0 <= topk <= 2048.  ws: csa2_workspace_size(
- *   CSA2_FN_SPARSE_DECODE, B, H, 0, topk, 0, 0) bytes. */
+ *   16; 1 <= W <= 1024; 0 <= topk <= 2048.  ws (optional, device): with
+ *   csa2_workspace_size(CSA2_FN_SPARSE_DECODE, B, H, 0, topk, 0, 0) bytes, a call
+ *   with fewer (sequence, 16-head group) pairs than the GPU has CUs spreads each
+ *   pair's rows over several workgroups and merges their partial softmax states
+ *   (same result up to fp32 rounding order); NULL with ws_bytes = 0 runs one
+ *   workgroup per pair.  ws_bytes > 0 with ws NULL: CSA2_EWORKSPACE. */
 int csa2_sparse_decode(const csa2_cache_t *cache, int B, int H, const int32_t *ctx_len,
                        const uint16_t *q, const int32_t *topk_idx, int topk, const uint16_t *swa,
                        int W, float sm_scale, uint16_t *out, float *lse, void *ws, size_t ws_bytes,

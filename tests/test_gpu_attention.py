@@ -30,6 +30,12 @@ def _oracle_topk(case, oc, layer, topk):
     return out
 
 
+def _no_ws():
+    """A zero-byte workspace: one workgroup per (sequence, head group), no split."""
+    return torch.empty(0, dtype=torch.uint8, device="cuda")
+
+
+@pytest.mark.parametrize("split", [True, False], ids=["split", "whole"])
 @pytest.mark.parametrize("ctx,H,topk,W", [
     ((2048,), 16, 512, 128),                    # config-0 shape
     ((65536, 300, 4000, 100), 64, 512, 128),    # config-1 length, short contexts, ragged tiles
@@ -37,7 +43,7 @@ def _oracle_topk(case, oc, layer, topk):
     ((5000,), 16, 2048, 128),                   # eight FP4 batches
     ((700, 3000), 16, 512, 1024),               # long window: 16 window batches
 ])
-def test_sparse_decode_matches_oracle(fk, ctx, H, topk, W):
+def test_sparse_decode_matches_oracle(fk, ctx, H, topk, W, split):
     cfg = small_decode(1, B=len(ctx), ctx=ctx, H=H, pages="random", heavy_frac=0.05, append=0,
                        topk=topk, window=W)
     case = make_decode_case(cfg, "cpu")
@@ -46,7 +52,8 @@ def test_sparse_decode_matches_oracle(fk, ctx, H, topk, W):
     L = case.layer(0)
     tk = _oracle_topk(case, oc, L, topk)
     ctx_len = torch.tensor(case.ctx_len, dtype=torch.int32, device="cuda")
-    out, lse = fk.sparse_decode(gc, ctx_len, L["q"].cuda(), torch.from_numpy(tk).cuda(), L["swa"].cuda())
+    out, lse = fk.sparse_decode(gc, ctx_len, L["q"].cuda(), torch.from_numpy(tk).cuda(), L["swa"].cuda(),
+                                ws=None if split else _no_ws())
     torch.cuda.synchronize()
     out_b, lse = bits(out.cpu()), lse.cpu().numpy()
     worst = 0.0
@@ -136,3 +143,26 @@ def test_window_only_and_single_row(fk):
         check_attention_rows(out_b[b], o_ref)
     # ctx 2 -> t = 1: two window rows; ctx 1 impossible (even), so check the row count
     assert gather_rows(oc, 0, np.zeros(0, np.int64), bits(L["swa"][0]), 1, 128).shape[0] == 2
+
+
+def test_split_runs_without_valid_rows(fk):
+    # window only (no FP4 rows), a 1024-row window cut into eight runs, and contexts so
+    # short that most runs hold no valid row: those runs must drop out of the merge
+    cfg = small_decode(1, B=3, ctx=(2, 40, 2000), H=16, pages="identity", append=0, window=1024)
+    case = make_decode_case(cfg, "cpu")
+    oc = oracle_cache_for(case)
+    gc = gpu_cache_for(case)
+    L = case.layer(0)
+    ctx_len = torch.tensor(case.ctx_len, dtype=torch.int32, device="cuda")
+    tk = torch.full((case.B, 0), -1, dtype=torch.int32, device="cuda")
+    out, lse = fk.sparse_decode(gc, ctx_len, L["q"].cuda(), tk, L["swa"].cuda())
+    whole, lse_w = fk.sparse_decode(gc, ctx_len, L["q"].cuda(), tk, L["swa"].cuda(), ws=_no_ws())
+    torch.cuda.synchronize()
+    out_b, lse = bits(out.cpu()), lse.cpu().numpy()
+    for b in range(case.B):
+        t = case.ctx_len[b] - 1
+        rows = gather_rows(oc, b, np.zeros(0, np.int64), bits(L["swa"][b]), t, 1024)
+        o_ref, lse_ref = sparse_attention(bits(L["q"][b]), rows, 1 / math.sqrt(512))
+        check_attention_rows(out_b[b], o_ref)
+        assert np.allclose(lse[b], lse_ref, rtol=0, atol=1e-4), np.abs(lse[b] - lse_ref).max()
+    assert np.allclose(lse, lse_w.cpu().numpy(), rtol=0, atol=1e-5)
