@@ -116,15 +116,16 @@ def build_decode(case, fk, n_rep: int):
 
 
 def recorded_traffic(kernel: str):
-    """HBM bytes per launch of `kernel` from the committed counter summary, if the
-    summary was taken on the current source of that kernel (else None)."""
+    """HBM bytes per call of `kernel` (for the attention: split kernel plus combine)
+    from the committed counter summary, if the summary was taken on the current
+    source of that kernel (else None)."""
     import hashlib
     import re
     path = os.path.join(ROOT, "profiles", "pmc_traffic_decode_b32_ctx64k.md")
     src = os.path.join(ROOT, "fp4_kv_cache_write_amd", "csrc", "attention.hip")
     if kernel != "sparse_decode" or not (os.path.exists(path) and os.path.exists(src)):
         return None
-    m = re.search(r"sparse_decode_kernel traffic_bytes_per_launch=(\d+) attention_hip_sha256=([0-9a-f]+)",
+    m = re.search(r"sparse_decode_call traffic_bytes_per_launch=(\d+) attention_hip_sha256=([0-9a-f]+)",
                   open(path).read())
     if not m or m.group(2) != hashlib.sha256(open(src, "rb").read()).hexdigest():
         return None
