@@ -95,22 +95,17 @@ constexpr int kPartFloats = 32 + 16 * CSA2_D_LATENT;
 constexpr int kMaxSplit = 8;
 constexpr int kSplitBelow = 256;   // launches with fewer workgroups than CUs split
 
-// Rows of split sp: the window tiles then the FP4 tiles (32 rows each) are cut into
-// nsplit contiguous runs of equal tile counts.  (A window tile needs no
-// dequantisation, but window batches hold only two tiles, so their fixed per-batch
-// cost makes the two kinds of tile cost about the same.)  Gives window rows
-// [w0, w1) and FP4 rows [f0, f1).
+// Rows of split sp: run sp takes the sp-th of nsplit equal shares (in 32-row tiles)
+// of the window rows and, separately, of the FP4 rows.  Every run then starts with
+// window rows, which need no lookups, while the ids of its FP4 rows resolve, and
+// all runs do the same mix of work.  Gives window rows [w0, w1), FP4 rows [f0, f1).
 __device__ __forceinline__ void split_rows(int W, int topk, int nsplit, int sp, int& w0, int& w1, int& f0,
                                            int& f1) {
   const int nwt = (W + 31) >> 5, nft = (topk + 31) >> 5;
-  auto cut = [&](int j) -> int {   // tile position (window tiles first) of boundary j
-    return (int)(((int64_t)j * (nwt + nft) + nsplit - 1) / nsplit);
-  };
-  const int p0 = cut(sp), p1 = cut(sp + 1);
-  w0 = min(32 * min(p0, nwt), W);
-  w1 = min(32 * min(p1, nwt), W);
-  f0 = min(32 * max(p0 - nwt, 0), topk);
-  f1 = min(32 * max(p1 - nwt, 0), topk);
+  w0 = min(32 * (sp * nwt / nsplit), W);
+  w1 = min(32 * ((sp + 1) * nwt / nsplit), W);
+  f0 = min(32 * (sp * nft / nsplit), topk);
+  f1 = min(32 * ((sp + 1) * nft / nsplit), topk);
 }
 
 // low halves of a and b -> (a.lo, b.lo); high halves -> (a.hi, b.hi)
@@ -879,14 +874,15 @@ bool lds_limit_set() {
 
 // Merge the split partials of one (query, head group): with m* the largest partial
 // maximum, weights 2^(m_s - m*) scale each partial's sum and output, as in the
-// log-sum-exp merge of softmax blocks.  Thread t: head t/32, dims 16(t%32) .. +15.
-// Every load is issued before the first is used (one memory round trip).
-__global__ __launch_bounds__(512) void attn_combine_kernel(const float* __restrict__ part, int nsplit,
+// log-sum-exp merge of softmax blocks.  Workgroup x: pair x/4, heads 4(x%4) .. +3;
+// thread t: head 4(x%4) + t/32, dims 16(t%32) .. +15.  Every load is issued before
+// the first is used (one memory round trip).
+__global__ __launch_bounds__(128) void attn_combine_kernel(const float* __restrict__ part, int nsplit,
                                                           int64_t n_pairs, uint16_t* __restrict__ out,
                                                           float* __restrict__ lse) {
-  const int64_t qh = blockIdx.x;
+  const int64_t qh = blockIdx.x >> 2;
   if (qh >= n_pairs) return;
-  const int tid = threadIdx.x, h = tid >> 5, d0 = (tid & 31) * 16;
+  const int tid = threadIdx.x, h = 4 * (blockIdx.x & 3) + (tid >> 5), d0 = (tid & 31) * 16;
   const float* p0 = part + qh * nsplit * (int64_t)kPartFloats;
   float ms[kMaxSplit], ls[kMaxSplit];
   f32x4 os[kMaxSplit][4];
@@ -1006,8 +1002,8 @@ int launch_gather_attention(const csa2_cache_t& c, int B, int C, int H, const in
   if (a.nsplit > 1) {
     const int rc = hip_status();
     if (rc != CSA2_OK) return rc;
-    hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)(nq * a.HG)), dim3(512), 0, s, a.part, a.nsplit,
-                       nq * a.HG, out, lse);
+    hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)(4 * nq * a.HG)), dim3(128), 0, s, a.part,
+                       a.nsplit, nq * a.HG, out, lse);
   }
   return hip_status();
 }

@@ -189,6 +189,8 @@ __global__ __launch_bounds__(kScanThreads) void index_scan_kernel(ScanArgs a) {
     ck[pos] = kr[i];
     ci[pos] = e0 + p0 + i;
   });
+  // unused slots hold key 0 ("no entry"), so readers need not wait for the count
+  for (int p = (int)sr.count + threadIdx.x; p < a.topk; p += kScanThreads) ck[p] = 0u;
   if (threadIdx.x == 0) a.cand_cnt[slot] = (int32_t)sr.count;
 }
 
@@ -219,26 +221,19 @@ __global__ __launch_bounds__(kMergeThreads) void index_merge_kernel(MergeArgs a)
     // virtual position v = chunk * topk + i, in entry order
     const int nc = (n_vis + a.chunk - 1) / a.chunk;
     const int N = nc * a.topk;
-    // slot v = chunk * topk + j, walked incrementally from this thread's first slot
-    const int c0 = p0 / a.topk, j0 = p0 - c0 * a.topk;
+    // unused candidate slots hold key 0; keys and ids are loaded together, one round trip
     const uint32_t* ckey = a.cand_key + (int64_t)b * a.n_chunks * a.topk;
-    {
-      int cch = c0, j = j0;
-      int cnt = (p0 < N) ? a.cand_cnt[(int64_t)b * a.n_chunks + cch] : 0;
+    const int32_t* cidx = a.cand_idx + (int64_t)b * a.n_chunks * a.topk;
+    int32_t id[KPT];
 #pragma unroll
-      for (int i = 0; i < KPT; ++i) {
-        kr[i] = (p0 + i < N && j < cnt) ? ckey[p0 + i] : 0u;
-        if (++j == a.topk) {
-          j = 0;
-          ++cch;
-          cnt = (p0 + i + 1 < N) ? a.cand_cnt[(int64_t)b * a.n_chunks + cch] : 0;
-        }
-      }
+    for (int i = 0; i < KPT; ++i) {
+      const bool in = p0 + i < N;
+      kr[i] = in ? ckey[p0 + i] : 0u;
+      id[i] = in ? cidx[p0 + i] : -1;
     }
     const SelectResult sr = block_select<kMergeThreads, KPT>(kr, a.topk, hist, scratch);
     int32_t* out = a.topk_idx + (int64_t)b * a.topk;
-    const int32_t* cidx = a.cand_idx + (int64_t)b * a.n_chunks * a.topk;
-    block_emit<kMergeThreads, KPT>(kr, sr, scratch, [&](int i, uint32_t pos) { out[pos] = cidx[p0 + i]; });
+    block_emit<kMergeThreads, KPT>(kr, sr, scratch, [&](int i, uint32_t pos) { out[pos] = id[i]; });
     for (int p = (int)sr.count + tid; p < a.topk; p += kMergeThreads) out[p] = -1;
   } else {
     const int cb = a.cand_block;
@@ -291,28 +286,24 @@ __global__ __launch_bounds__(kMergeThreads) void index_group_kernel(GroupArgs a)
   const int p0 = tid * KPT;
   const int64_t cbase = (int64_t)b * a.n_chunks + c0;
   const uint32_t* ckey = a.cand_key + cbase * a.topk;
+  // unused candidate slots hold key 0; keys and ids are loaded together, one round trip
+  const int32_t* cidx = a.cand_idx + cbase * a.topk;
   uint32_t kr[KPT];
-  {
-    int cch = p0 / a.topk, j = p0 - (p0 / a.topk) * a.topk;
-    int cnt = (p0 < N) ? a.cand_cnt[cbase + cch] : 0;
+  int32_t id[KPT];
 #pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      kr[i] = (p0 + i < N && j < cnt) ? ckey[p0 + i] : 0u;
-      if (++j == a.topk) {
-        j = 0;
-        ++cch;
-        cnt = (p0 + i + 1 < N) ? a.cand_cnt[cbase + cch] : 0;
-      }
-    }
+  for (int i = 0; i < KPT; ++i) {
+    const bool in = p0 + i < N;
+    kr[i] = in ? ckey[p0 + i] : 0u;
+    id[i] = in ? cidx[p0 + i] : -1;
   }
   const SelectResult sr = block_select<kMergeThreads, KPT>(kr, a.topk, hist, scratch);
   uint32_t* gk = a.grp_key + gslot * a.topk;
   int32_t* gi = a.grp_idx + gslot * a.topk;
-  const int32_t* cidx = a.cand_idx + cbase * a.topk;
   block_emit<kMergeThreads, KPT>(kr, sr, scratch, [&](int i, uint32_t pos) {
     gk[pos] = kr[i];
-    gi[pos] = cidx[p0 + i];
+    gi[pos] = id[i];
   });
+  for (int p = (int)sr.count + tid; p < a.topk; p += kMergeThreads) gk[p] = 0u;   // key 0: no entry
   if (tid == 0) a.grp_cnt[gslot] = (int32_t)sr.count;
 }
 
