@@ -31,9 +31,14 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
   return b >> 16;
 }
 
-// Scale 2^(u-127) of an e8m0 byte as an fp32 multiplier (u = 0 is the subnormal 2^-127).
+// Scale operand of the FP4 convert for an e8m0 byte u (scale 2^(u-127)).  The
+// convert reads only the exponent field of its fp32 scale operand, exponent field 0
+// standing for 2^-127 as in e8m0, so the byte shifted into that field is the scale:
+// one shift, no special case for u = 0.  (Checked against the exact multiplier,
+// 2^-127 being the subnormal 0x00400000, on all 256 scale bytes x 256 code bytes.)
+// Only valid as the convert's operand, not as an arithmetic multiplier.
 __device__ __forceinline__ float e8m0_scale(uint32_t u) {
-  return __uint_as_float(u ? (u << 23) : 0x00400000u);
+  return __uint_as_float(u << 23);
 }
 
 // Two e2m1 codes (byte SEL of `codes`: low nibble -> element 0) times `scale`, as bf16.
