@@ -373,6 +373,8 @@ __global__ __launch_bounds__(kThreads) void sparse_decode_kernel(DecArgs a) {
   // the loop then cover only the next batch's loads, which stay in flight until the
   // batch is stored after PV.
   __builtin_amdgcn_s_waitcnt(0);
+  // page lookups of the prefetched FP4 ids: in flight during the first window batch
+  if (n_wb > 0 && page_ok(pf_e)) pf_page = bt[pf_e >> 6];
 
   f32x4 acc[4];
 #pragma unroll
@@ -390,18 +392,13 @@ __global__ __launch_bounds__(kThreads) void sparse_decode_kernel(DecArgs a) {
     const int ntl = (nrows + 31) >> 5;
 
     __syncthreads();   // batch k stored by every thread; batch k-1 fully consumed
-    if (k == 0 && n_wb > 0 && page_ok(pf_e)) pf_page = bt[pf_e >> 6];   // page lookups, consumed later
-    if (k + 1 < nb) {
-      const int f1 = k + 1 - n_wb;
-      if (f1 == 0) {              // first FP4 batch: row ids of the two prefetched batches
-        rowid_all[tid] = row_of(pf_e, pf_page);
-        __syncthreads();
-      } else if (f1 >= 2) {
-        resolve_rows(f1);
-        __syncthreads();
-      }
-      load_batch(k + 1, st);      // stored after this batch's PV
-    }
+    // Batch k+1 is loaded now if its rows are known (a window batch, or the second FP4
+    // batch whose ids came with the first); otherwise its row ids are resolved after
+    // this batch's QK, which hides the lookups, and it is loaded after the next barrier.
+    const int f1 = k + 1 - n_wb;
+    const bool has_next = k + 1 < nb;
+    const bool ids_later = has_next && (f1 == 0 || f1 >= 2);
+    if (has_next && !ids_later) load_batch(k + 1, st);   // stored after this batch's PV
 
     // ---- QK: wave w scores tile w ----
     float z[8];
@@ -420,7 +417,14 @@ __global__ __launch_bounds__(kThreads) void sparse_decode_kernel(DecArgs a) {
     tmax = fmaxf(tmax, __shfl_xor(tmax, 16, kWave));
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
     if (g == 0) m_part[wid * 16 + n] = tmax;
+    if (ids_later) {
+      if (f1 == 0)
+        rowid_all[tid] = row_of(pf_e, pf_page);   // the two prefetched FP4 batches
+      else
+        resolve_rows(f1);
+    }
     __syncthreads();
+    if (ids_later) load_batch(k + 1, st);
 
     // ---- batch max of head n (identical in every wave), P for the scored tile ----
     float mb = m_part[n];
