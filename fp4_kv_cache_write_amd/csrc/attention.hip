@@ -499,8 +499,8 @@ __global__ __launch_bounds__(kThreads) void sparse_decode_kernel(DecArgs a) {
     float* part = a.part + ((qi * a.HG + hg) * a.nsplit + sp) * (int64_t)kPartFloats;
 #pragma unroll
     for (int ii = 0; ii < 4; ++ii)
-      *reinterpret_cast<f32x4*>(part + 32 + (4 * g + ii) * CSA2_D_LATENT + 64 * wid + 4 * n) =
-          f32x4{acc[0][ii], acc[1][ii], acc[2][ii], acc[3][ii]};
+      __builtin_nontemporal_store(f32x4{acc[0][ii], acc[1][ii], acc[2][ii], acc[3][ii]},
+                                  reinterpret_cast<f32x4*>(part + 32 + (4 * g + ii) * CSA2_D_LATENT + 64 * wid + 4 * n));
     if (wid == 0 && g == 0) {
       float sl = 0.f;
 #pragma unroll
