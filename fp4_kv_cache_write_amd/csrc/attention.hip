@@ -56,8 +56,9 @@ constexpr int kBufBytes = kFp4Batch * kRowB;              // 69632 >= kWinBatch 
 constexpr int kPBytes = 32;                               // per lane and tile: P head + residual
 constexpr int kStage = (kFp4Batch * 17 + kThreads - 1) / kThreads;   // 16-byte chunks per thread
 constexpr int kOffBuf = 0;
-constexpr int kOffP = 2 * kBufBytes;                      // [8 tiles][64 lanes][32 B]
-constexpr int kOffRowId = kOffP + kMaxTiles * 64 * kPBytes;   // [2][256] int32
+constexpr int kPSlots = kMaxTiles + kWinBatch / 32;        // FP4 tiles, then a window batch's tiles
+constexpr int kOffP = 2 * kBufBytes;                      // [10 slots][64 lanes][32 B]
+constexpr int kOffRowId = kOffP + kPSlots * 64 * kPBytes;   // [2][256] int32
 constexpr int kOffMax = kOffRowId + 2 * kFp4Batch * 4;    // [8 waves][16] float
 constexpr int kOffL = kOffMax + kWaves * 16 * 4;          // [8 waves][16] float
 constexpr int kLdsBytes = kOffL + kWaves * 16 * 4;
@@ -381,6 +382,79 @@ __global__ __launch_bounds__(kThreads) void sparse_decode_kernel(DecArgs a) {
   for (int i = 0; i < 4; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_part = 0.f;
 
+  // PV of one 32-row tile of a batch in LDS (window rows: bf16; else FP4), this wave's
+  // 64 dims, with the P operand from P slot ps.
+  auto pv_tile = [&](const uint8_t* buf, bool win, int tile, int ps) {
+    const uint8_t* pp = plds + (ps * 64 + lane) * kPBytes;
+    const bf16x8 ph = __builtin_bit_cast(bf16x8, lds_ld<u32x4>(pp));
+    const bf16x8 pl = __builtin_bit_cast(bf16x8, lds_ld<u32x4>(pp + 16));
+    uint32_t d01[8], d23[8];
+    if (win) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const u32x2 v = lds_ld<u32x2>(buf + (tile * 32 + slot_row(g, j)) * kWinB + 128 * wid + 8 * n);
+        d01[j] = v.x;
+        d23[j] = v.y;
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const uint8_t* rp = buf + (tile * 32 + slot_row(g, j)) * kRowB;
+        const uint32_t c2 = lds_ld<uint16_t>(rp + 32 * wid + 2 * n);
+        const float sc = e8m0_scale(rp[256 + 2 * wid + (n >> 3)]);
+        d01[j] = fp4x2_to_bf16x2<0>(c2, sc);
+        d23[j] = fp4x2_to_bf16x2<1>(c2, sc);
+      }
+    }
+    pv4(acc, d01, d23, ph, pl);
+  };
+  auto put_p = [&](const float (&z)[8], float m, int ps) {
+    u32x4 ph, pl;
+    make_p(z, m, l_part, ph, pl);
+    uint8_t* pp = plds + (ps * 64 + lane) * kPBytes;
+    *reinterpret_cast<u32x4*>(pp) = ph;
+    *reinterpret_cast<u32x4*>(pp + 16) = pl;
+  };
+
+  if (n_wb == 1 && n_fb == 1) {
+    // One window batch (buffer 0, stored in the prologue) and one FP4 batch (buffer 1)
+    // in a single pass: the window tiles are scored while the FP4 rows' pages are
+    // looked up and their rows loaded, then one softmax and one PV cover all tiles.
+    uint8_t* bufw = lds + kOffBuf;
+    uint8_t* buff = lds + kOffBuf + kBufBytes;
+    const int ntl_w = (min(wr1 - wr0, kWinBatch) + 31) >> 5;
+    const int nrows_f = min(fr1 - fr0, kFp4Batch);
+    const int ntl_f = (nrows_f + 31) >> 5;
+    __syncthreads();   // window rows stored by every thread
+    float zw[8], zf[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) zw[j] = zf[j] = -INFINITY;
+    if (wid < ntl_w) win_qk(bufw, a.W, t, wr0, wid * 32, qf, a.scale_log2, zw);
+    rowid_all[tid] = row_of(pf_e, pf_page);
+    __syncthreads();
+    load_batch(1, st);
+    store_batch(1, st);
+    __syncthreads();   // FP4 rows stored by every thread
+    if (wid < ntl_f) fp4_qk(buff, rowid_all, nrows_f, wid * 32, qf, a.scale_log2, zf);
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) tmax = fmaxf(tmax, fmaxf(zw[j], zf[j]));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, kWave));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
+    if (g == 0) m_part[wid * 16 + n] = tmax;
+    __syncthreads();
+    float mb = m_part[n];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) mb = fmaxf(mb, m_part[w * 16 + n]);
+    if (wid < ntl_f) put_p(zf, mb, wid);
+    if (wid < ntl_w) put_p(zw, mb, kMaxTiles + wid);
+    m_run = mb;
+    __syncthreads();
+#pragma unroll 1
+    for (int tile = 0; tile < ntl_w; ++tile) pv_tile(bufw, true, tile, kMaxTiles + tile);
+#pragma unroll 1
+    for (int tile = 0; tile < ntl_f; ++tile) pv_tile(buff, false, tile, tile);
+  } else {
 #pragma unroll 1
   for (int k = 0; k < nb; ++k) {
     const bool is_win = k < n_wb;
@@ -433,13 +507,7 @@ __global__ __launch_bounds__(kThreads) void sparse_decode_kernel(DecArgs a) {
     const float m_new = fmaxf(m_run, mb);
     const float fac = (m_run == -INFINITY || m_new == m_run) ? 1.f : exp2f(m_run - m_new);
     l_part *= fac;
-    if (wid < ntl) {
-      u32x4 ph, pl;
-      make_p(z, m_new, l_part, ph, pl);
-      uint8_t* pp = plds + (wid * 64 + lane) * kPBytes;
-      *reinterpret_cast<u32x4*>(pp) = ph;
-      *reinterpret_cast<u32x4*>(pp + 16) = pl;
-    }
+    if (wid < ntl) put_p(z, m_new, wid);
     // rescale: acc[t][i] belongs to head 4g+i, whose factor lives in lane 4g+i
     {
       float fo[4];
@@ -462,31 +530,9 @@ __global__ __launch_bounds__(kThreads) void sparse_decode_kernel(DecArgs a) {
 
     // ---- PV over every tile of the batch, this wave's 64 dims ----
 #pragma unroll 1
-    for (int tile = 0; tile < ntl; ++tile) {
-      const uint8_t* pp = plds + (tile * 64 + lane) * kPBytes;
-      const bf16x8 ph = __builtin_bit_cast(bf16x8, lds_ld<u32x4>(pp));
-      const bf16x8 pl = __builtin_bit_cast(bf16x8, lds_ld<u32x4>(pp + 16));
-      uint32_t d01[8], d23[8];
-      if (is_win) {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const u32x2 v = lds_ld<u32x2>(buf + (tile * 32 + slot_row(g, j)) * kWinB + 128 * wid + 8 * n);
-          d01[j] = v.x;
-          d23[j] = v.y;
-        }
-      } else {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const uint8_t* rp = buf + (tile * 32 + slot_row(g, j)) * kRowB;
-          const uint32_t c2 = lds_ld<uint16_t>(rp + 32 * wid + 2 * n);
-          const float sc = e8m0_scale(rp[256 + 2 * wid + (n >> 3)]);
-          d01[j] = fp4x2_to_bf16x2<0>(c2, sc);
-          d23[j] = fp4x2_to_bf16x2<1>(c2, sc);
-        }
-      }
-      pv4(acc, d01, d23, ph, pl);
-    }
+    for (int tile = 0; tile < ntl; ++tile) pv_tile(buf, is_win, tile, tile);
     if (k + 1 < nb) store_batch(k + 1, st);   // into the other buffer, free since batch k began
+  }
   }
 
   // ---- softmax denominators, output ----
