@@ -346,13 +346,14 @@ __global__ __launch_bounds__(kThreads) void sparse_decode_kernel(DecArgs a) {
     }
   };
 
-  // ---- start: batch 0 (window rows need no lookups), entry ids of the first two FP4
-  // batches (thread tid: batch tid/256, row tid%256) and q, all in flight at once ----
+  // ---- start: the entry ids of the first two FP4 batches (thread tid: batch tid/256,
+  // row tid%256) go out first, then batch 0 (window rows need no lookups) and q.  The
+  // ids' page lookups are issued as soon as the ids land, while the rest is in flight.
   u32x4 st[kStage];
-  if (n_wb > 0) load_batch(0, st);
   const int pf_i = tid & (kFp4Batch - 1), pf_f = tid >> 8;
   const int pf_r = fr0 + pf_f * kFp4Batch + pf_i;
   const int pf_e = (pf_f < n_fb && pf_r < fr1) ? tk[pf_r] : -1;
+  if (n_wb > 0) load_batch(0, st);
   u32x4 qf[16];   // q operand of head hg*16+n: dims 128g + 8s .. +7 for k-step s
   {
     const uint16_t* qp = a.q + (qi * a.H + hg * 16 + n) * CSA2_D_LATENT + 128 * g;
@@ -361,6 +362,7 @@ __global__ __launch_bounds__(kThreads) void sparse_decode_kernel(DecArgs a) {
   }
   int pf_page = -1;
   if (n_wb > 0) {
+    if (page_ok(pf_e)) pf_page = bt[pf_e >> 6];
     store_batch(0, st);
   } else if (n_fb > 0) {
     // the run starts with FP4 rows (split launches): resolve the prefetched ids now
@@ -374,8 +376,6 @@ __global__ __launch_bounds__(kThreads) void sparse_decode_kernel(DecArgs a) {
   // the loop then cover only the next batch's loads, which stay in flight until the
   // batch is stored after PV.
   __builtin_amdgcn_s_waitcnt(0);
-  // page lookups of the prefetched FP4 ids: in flight during the first window batch
-  if (n_wb > 0 && page_ok(pf_e)) pf_page = bt[pf_e >> 6];
 
   f32x4 acc[4];
 #pragma unroll
@@ -418,21 +418,20 @@ __global__ __launch_bounds__(kThreads) void sparse_decode_kernel(DecArgs a) {
 
   if (n_wb == 1 && n_fb == 1) {
     // One window batch (buffer 0, stored in the prologue) and one FP4 batch (buffer 1)
-    // in a single pass: the window tiles are scored while the FP4 rows' pages are
-    // looked up and their rows loaded, then one softmax and one PV cover all tiles.
+    // in a single pass: the window tiles are scored while the FP4 rows load, then one
+    // softmax and one PV cover all tiles.
     uint8_t* bufw = lds + kOffBuf;
     uint8_t* buff = lds + kOffBuf + kBufBytes;
     const int ntl_w = (min(wr1 - wr0, kWinBatch) + 31) >> 5;
     const int nrows_f = min(fr1 - fr0, kFp4Batch);
     const int ntl_f = (nrows_f + 31) >> 5;
-    __syncthreads();   // window rows stored by every thread
+    rowid_all[tid] = row_of(pf_e, pf_page);
+    __syncthreads();   // window rows and the FP4 row ids stored by every thread
+    load_batch(1, st);   // FP4 rows: in flight while the window tiles are scored
     float zw[8], zf[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) zw[j] = zf[j] = -INFINITY;
     if (wid < ntl_w) win_qk(bufw, a.W, t, wr0, wid * 32, qf, a.scale_log2, zw);
-    rowid_all[tid] = row_of(pf_e, pf_page);
-    __syncthreads();
-    load_batch(1, st);
     store_batch(1, st);
     __syncthreads();   // FP4 rows stored by every thread
     if (wid < ntl_f) fp4_qk(buff, rowid_all, nrows_f, wid * 32, qf, a.scale_log2, zf);
