@@ -7,9 +7,10 @@ layer that searches the Full layer's candidate pool.  [P3]
 ("選ぶ位置は同じでも、情報の混ぜ方は変わる"): Reuse keeps the positions while the
 query, and so the weights, change.
 
-Visibility ([P3], causal mask): entry j merges tokens 2j and 2j+1, so a query
-at token t sees entries with 2j+1 <= t, i.e. floor((t+1)/2) of them; a decode
-query for a context of L tokens sits at t = L-1.
+Visibility ([P3], causal mask): at ratio 2 entry j merges tokens 2j and 2j+1, so
+a query at token t sees entries with 2j+1 <= t, i.e. floor((t+1)/2) of them; at
+ratio 1 ([P1] §2.3.1, the decoder) entry j is token j and t sees t+1 entries.  A
+decode query for a context of L tokens sits at t = L-1.
 """
 from __future__ import annotations
 
@@ -21,8 +22,8 @@ from .attention import gather_rows, sparse_attention
 from .indexer import full_layer, index_scores, reindex_layer, topk_select
 
 
-def n_visible(t: int) -> int:
-    return (t + 1) // 2
+def n_visible(t: int, ratio: int = 2) -> int:
+    return (t + 1) // ratio
 
 
 def run_decode(cache, ctx_len, layers, topk: int = 512, W: int = 128, cand_block: int = 8,
@@ -45,7 +46,7 @@ def run_decode(cache, ctx_len, layers, topk: int = 512, W: int = 128, cand_block
         res = {"topk": {}, "pool": {}, "o": {}, "lse": {}}
         for b in seqs:
             t = ctx_len[b] - 1
-            nv = n_visible(t)
+            nv = n_visible(t, getattr(cache, "ratio", 2))
             if spec["mode"] == "full":
                 tk, pool, _ = full_layer(cache, b, nv, spec["q_idx"][b], spec["w_idx"][b], topk,
                                          spec.get("pool_blocks", 0), cand_block)
@@ -80,6 +81,7 @@ def run_prefill(cache, prior_len, C: int, q, q_idx, w_idx, local, topk: int = 51
     """
     if sm_scale is None:
         sm_scale = 1.0 / math.sqrt(512.0)
+    assert getattr(cache, "ratio", 2) == 2, "chunked prefill is the encoder's (ratio 2) path"
     B = len(prior_len)
     if queries is None:
         queries = [(b, i) for b in range(B) for i in range(C)]
