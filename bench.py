@@ -48,7 +48,7 @@ def parse():
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--replicas", type=int, default=8)
-    p.add_argument("--workload", choices=("c1", "c2", "c3", "c4"), default="c1",
+    p.add_argument("--workload", choices=("c1", "c2", "c3", "c4", "c5"), default="c1",
                    help="c1 = headline decode line (+ secondary c2, c3); others alone")
     p.add_argument("--no-secondary", action="store_true")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -78,38 +78,39 @@ class Replica:
 
 def build_decode(case, fk, n_rep: int):
     """Cache with every sequence's pre-built tokens; the step's write re-submits the
-    newest pair (no append) or submits the appended tokens."""
+    newest entry's tokens (a pair at ratio 2, one token at ratio 1) when nothing is
+    appended, or submits the appended tokens."""
     dev = "cuda"
     cfg = case.cfg
-    cache = fk.PagedCache.allocate(case.n_pages, case.block_table, device=dev)
-    bt_rows = case.block_table.to(dev)
-    pair_x, pair_w, pair_k = [], [], []
+    r = cfg.ratio
+    cache = fk.PagedCache.allocate(case.n_pages, case.block_table, device=dev, ratio=r)
+    last_x, last_w, last_k = [], [], []
     for b in range(case.B):
         x, w, k = case.seq_tokens(b)
         T = x.shape[0]
-        sub = fk.PagedCache(cache.lat_codes, cache.lat_scales, cache.idx_codes, cache.idx_scales,
-                            bt_rows[b:b + 1].contiguous())
-        fk.write_kv(sub, torch.zeros(1, dtype=torch.int32, device=dev), x[None].contiguous(),
-                    w[None].contiguous(), k[None].contiguous())
+        fk.write_kv(cache.rows(b, b + 1), torch.zeros(1, dtype=torch.int32, device=dev), x[None].contiguous(),
+                    None if w is None else w[None].contiguous(), k[None].contiguous())
         if cfg.append == 0:
-            pair_x.append(x[T - 2:].clone())
-            pair_w.append(w[T - 2:].clone())
-            pair_k.append(k[T // 2 - 1:].clone())
+            last_x.append(x[T - r:].clone())
+            last_w.append(None if w is None else w[T - r:].clone())
+            last_k.append(k[T // r - 1:].clone())
         del x, w, k
     torch.cuda.synchronize()
     if cfg.append == 0:
-        write = dict(x=torch.stack(pair_x).contiguous(), w=torch.stack(pair_w).contiguous(),
-                     k=torch.stack(pair_k).contiguous(),
-                     start=torch.tensor([L - 2 for L in case.ctx_len], dtype=torch.int32, device=dev))
+        write = dict(x=torch.stack(last_x).contiguous(),
+                     w=None if r == 1 else torch.stack(last_w).contiguous(),
+                     k=torch.stack(last_k).contiguous(),
+                     start=torch.tensor([L - r for L in case.ctx_len], dtype=torch.int32, device=dev))
     else:
         xa, wa, ka, start = case.append_tokens()
-        write = dict(x=xa.contiguous(), w=wa.contiguous(), k=ka.contiguous(), start=start.to(dev))
+        write = dict(x=xa.contiguous(), w=None if wa is None else wa.contiguous(), k=ka.contiguous(),
+                     start=start.to(dev))
     layers = [case.layer(l) for l in range(cfg.n_layers)]
     reps = []
     for r in range(n_rep):
         c = cache if r == 0 else cache.clone()
         ls = [{k: (v if r == 0 else v.clone()) for k, v in L.items()} for L in layers]
-        wr = {k: (v if r == 0 else v.clone()) for k, v in write.items()}
+        wr = {k: (v if r == 0 or v is None else v.clone()) for k, v in write.items()}
         reps.append(Replica(c, ls, wr))
     torch.cuda.synchronize()
     return reps
@@ -141,9 +142,10 @@ def decode_bytes(case):
     n_t = [min(topk, v) for v in n_vis]
     n_pool = [min(pool_blocks * cfg.cand_block, v) for v in n_vis]
     n_win = [min(W, L) for L in case.ctx_len]
-    T_w = 2 if cfg.append == 0 else cfg.append
-    per = {
-        "write_kv": B * (T_w * 2 * 1024 + (T_w // 2) * 128 + 4 + (T_w // 2) * 306),
+    r = cfg.ratio
+    T_w = r if cfg.append == 0 else cfg.append
+    per = {   # write reads x (and w at ratio 2) per token and a key per entry, stores 306 B per entry
+        "write_kv": B * (T_w * r * 1024 + (T_w // r) * 128 + 4 + (T_w // r) * 306),
         "index_full": sum(v * BYTES_IDX + 520 + 4 * topk + 4 * pool_blocks for v in n_vis),
         "reindex": sum(p * BYTES_IDX + 520 + 4 * pool_blocks + 4 * topk for p in n_pool),
         "sparse_decode": sum(t * BYTES_LAT + w * 1024 + 2 * H * 1024 + 4 * t + 4 * H for t, w in zip(n_t, n_win)),
@@ -173,8 +175,10 @@ def bench_decode(fk, cfg_id: int, steps: int, warmup: int, n_rep: int, use_graph
     ctx = torch.tensor(case.ctx_len, dtype=torch.int32, device=dev)
     max_ctx = max(case.ctx_len)
     pool_blocks = max([sp.pool_blocks for sp in cfg.layers] + [0])
-    ws_full = fk.workspace(fk.FN_INDEX_FULL, device=dev, B=B, max_ctx=max_ctx, topk=topk, pool_blocks=pool_blocks)
-    ws_re = fk.workspace(fk.FN_REINDEX, device=dev, B=B, topk=topk, pool_blocks=max(pool_blocks, 1))
+    ws_full = fk.workspace(fk.FN_INDEX_FULL, device=dev, B=B, max_ctx=max_ctx, topk=topk, pool_blocks=pool_blocks,
+                           ratio=cfg.ratio)
+    ws_re = fk.workspace(fk.FN_REINDEX, device=dev, B=B, topk=topk, pool_blocks=max(pool_blocks, 1),
+                         ratio=cfg.ratio)
     ws_att = fk.workspace(fk.FN_SPARSE_DECODE, device=dev, B=B, H=H, topk=topk)
     tk_buf = [torch.empty((B, topk), dtype=torch.int32, device=dev) for _ in range(2)]
     pool = torch.empty((B, max(pool_blocks, 1)), dtype=torch.int32, device=dev)
@@ -413,7 +417,7 @@ def main() -> int:
                               config={"workload": r["workload"]})), flush=True)
         return 0
 
-    cfg_id = {"c1": 1, "c2": 2, "c4": 4}[args.workload]
+    cfg_id = {"c1": 1, "c2": 2, "c4": 4, "c5": 5}[args.workload]
     d = bench_decode(fk, cfg_id, args.steps, args.warmup, args.replicas, not args.no_graph, True, args.overlap_layers)
     case = d["case"]
     cfg = case.cfg
@@ -429,6 +433,16 @@ def main() -> int:
         del c2
         torch.cuda.empty_cache()
         secondary["c3_prefill"] = bench_prefill(fk, 5, 2)
+        torch.cuda.empty_cache()
+        # the decoder's ratio-1 cache with the 2048-block HSI pool
+        c5 = bench_decode(fk, 5, max(20, args.steps // 4), max(5, args.warmup // 4), 4, not args.no_graph, True,
+                          args.overlap_layers)
+        secondary["c5_decoder_ratio1"] = {
+            "workload": c5["case"].cfg.name, "value": round(c5["qps"], 1), "unit": "queries/s",
+            "ms_per_step": round(c5["ms"], 5), "achieved_gbs": round(c5["gbs"], 1),
+            "frac_hbm_peak": round(c5["gbs"] / HBM_PEAK_GBS, 4), "algorithmic_bytes_per_step": c5["step_bytes"],
+            "per_call_us": {n: round(v * 1e3, 2) for n, v in c5["per_call"].items()}, "roofline": c5["roofline"]}
+        del c5
         torch.cuda.empty_cache()
 
     cpu = None

@@ -31,7 +31,7 @@ class CacheT(ctypes.Structure):
     _fields_ = [("lat_codes", ctypes.c_void_p), ("lat_scales", ctypes.c_void_p),
                 ("idx_codes", ctypes.c_void_p), ("idx_scales", ctypes.c_void_p),
                 ("n_pages", ctypes.c_int32), ("block_table", ctypes.c_void_p),
-                ("max_pages", ctypes.c_int32)]
+                ("max_pages", ctypes.c_int32), ("ratio", ctypes.c_int32)]
 
 
 _lib = None
@@ -54,7 +54,7 @@ def lib() -> ctypes.CDLL:
         L.csa2_strerror.restype = ctypes.c_char_p
         L.csa2_strerror.argtypes = [I]
         L.csa2_workspace_size.restype = SZ
-        L.csa2_workspace_size.argtypes = [I, I, I, I64, I, I, I]
+        L.csa2_workspace_size.argtypes = [I, I, I, I64, I, I, I, I]
         L.csa2_write_kv.restype = I
         L.csa2_write_kv.argtypes = [C, I, P, I, P, P, P, I, P]
         L.csa2_index_full.restype = I
@@ -100,9 +100,15 @@ def _bf16(t: torch.Tensor, name: str, shape=None) -> None:
 
 
 class PagedCache:
-    """Device byte arrays of the paged FP4 cache plus its block table (see csa2.h)."""
+    """Device byte arrays of the paged FP4 cache plus its block table (see csa2.h).
 
-    def __init__(self, lat_codes, lat_scales, idx_codes, idx_scales, block_table):
+    ratio: tokens per entry, 2 (encoder: token pairs merged) or 1 (decoder: one entry
+    per token)."""
+
+    def __init__(self, lat_codes, lat_scales, idx_codes, idx_scales, block_table, ratio: int = 2):
+        if ratio not in (1, 2):
+            raise Csa2Error(f"ratio must be 1 or 2, got {ratio}")
+        self.ratio = ratio
         self.lat_codes, self.lat_scales = lat_codes, lat_scales
         self.idx_codes, self.idx_scales = idx_codes, idx_scales
         self.block_table = block_table
@@ -113,18 +119,23 @@ class PagedCache:
         self.max_pages = block_table.shape[1]
         self._struct = CacheT(lat_codes.data_ptr(), lat_scales.data_ptr(), idx_codes.data_ptr(),
                               idx_scales.data_ptr(), self.n_pages, block_table.data_ptr(),
-                              self.max_pages)
+                              self.max_pages, ratio)
 
     @classmethod
-    def allocate(cls, n_pages: int, block_table: torch.Tensor, device="cuda", fill: int = 0):
+    def allocate(cls, n_pages: int, block_table: torch.Tensor, device="cuda", fill: int = 0, ratio: int = 2):
         mk = lambda *s: torch.full(s, fill, dtype=torch.uint8, device=device)
         return cls(mk(n_pages, PAGE, D_LATENT // 2), mk(n_pages, PAGE, D_LATENT // 32),
                    mk(n_pages, PAGE, D_INDEX // 2), mk(n_pages, PAGE, D_INDEX // 32),
-                   block_table.to(device=device, dtype=torch.int32).contiguous())
+                   block_table.to(device=device, dtype=torch.int32).contiguous(), ratio)
 
     def clone(self) -> "PagedCache":
         return PagedCache(self.lat_codes.clone(), self.lat_scales.clone(), self.idx_codes.clone(),
-                          self.idx_scales.clone(), self.block_table.clone())
+                          self.idx_scales.clone(), self.block_table.clone(), self.ratio)
+
+    def rows(self, b0: int, b1: int) -> "PagedCache":
+        """The same cache with the block-table rows of sequences b0 .. b1-1 only."""
+        return PagedCache(self.lat_codes, self.lat_scales, self.idx_codes, self.idx_scales,
+                          self.block_table[b0:b1].contiguous(), self.ratio)
 
     @property
     def ref(self):
@@ -140,8 +151,8 @@ def bytes_per_entry() -> int:
 
 
 def workspace_size(fn: int, B: int, H: int = 0, max_ctx: int = 0, topk: int = 512,
-                   pool_blocks: int = 0, C: int = 0) -> int:
-    return lib().csa2_workspace_size(fn, B, H, max_ctx, topk, pool_blocks, C)
+                   pool_blocks: int = 0, C: int = 0, ratio: int = 2) -> int:
+    return lib().csa2_workspace_size(fn, B, H, max_ctx, topk, pool_blocks, C, ratio)
 
 
 def workspace(fn: int, device="cuda", **kw) -> Optional[torch.Tensor]:
@@ -149,12 +160,16 @@ def workspace(fn: int, device="cuda", **kw) -> Optional[torch.Tensor]:
     return torch.zeros(max(n, 1), dtype=torch.uint8, device=device) if n > 0 else None
 
 
-def write_kv(cache: PagedCache, start_tok: torch.Tensor, x: torch.Tensor, w: torch.Tensor,
-             k_idx: torch.Tensor, ratio: int = 2, stream=None) -> None:
+def write_kv(cache: PagedCache, start_tok: torch.Tensor, x: torch.Tensor, w: Optional[torch.Tensor],
+             k_idx: torch.Tensor, ratio: Optional[int] = None, stream=None) -> None:
+    """Write tokens start_tok .. start_tok+T-1 of every sequence.  ratio defaults to the
+    cache's; at ratio 1 w is unused (None) and k_idx has one key per token."""
+    ratio = cache.ratio if ratio is None else ratio
     B, T = x.shape[0], x.shape[1]
     _bf16(x, "x", (B, T, D_LATENT))
-    _bf16(w, "w", (B, T, D_LATENT))
-    _bf16(k_idx, "k_idx", (B, T // 2, D_INDEX))
+    if ratio == 2 or w is not None:
+        _bf16(w, "w", (B, T, D_LATENT))
+    _bf16(k_idx, "k_idx", (B, T // ratio, D_INDEX))
     _need(start_tok, torch.int32, "start_tok", (B,))
     _check(lib().csa2_write_kv(cache.ref, B, _ptr(start_tok), T, _ptr(x), _ptr(w), _ptr(k_idx), ratio,
                                _stream(stream)), "csa2_write_kv")
@@ -174,7 +189,8 @@ def index_full(cache: PagedCache, ctx_len: torch.Tensor, max_ctx: int, q_idx: to
     if pool_blocks > 0 and pool is None:
         pool = torch.empty((B, pool_blocks), dtype=torch.int32, device=dev)
     if ws is None:
-        ws = workspace(FN_INDEX_FULL, device=dev, B=B, max_ctx=max_ctx, topk=topk, pool_blocks=pool_blocks)
+        ws = workspace(FN_INDEX_FULL, device=dev, B=B, max_ctx=max_ctx, topk=topk, pool_blocks=pool_blocks,
+                       ratio=cache.ratio)
     wsb = ws.numel() if ws is not None else 0
     _check(lib().csa2_index_full(cache.ref, B, _ptr(ctx_len), max_ctx, _ptr(q_idx), _ptr(w_idx), topk,
                                  pool_blocks, cand_block, _ptr(topk_idx), _ptr(pool), _ptr(ws), wsb,
@@ -194,7 +210,8 @@ def reindex(cache: PagedCache, ctx_len: torch.Tensor, q_idx: torch.Tensor, w_idx
     if topk_idx is None:
         topk_idx = torch.empty((B, topk), dtype=torch.int32, device=q_idx.device)
     if ws is None and split:
-        ws = workspace(FN_REINDEX, device=q_idx.device, B=B, topk=topk, pool_blocks=pool.shape[1])
+        ws = workspace(FN_REINDEX, device=q_idx.device, B=B, topk=topk, pool_blocks=pool.shape[1],
+                       ratio=cache.ratio)
     wsb = ws.numel() if ws is not None else 0
     _check(lib().csa2_reindex(cache.ref, B, _ptr(ctx_len), _ptr(q_idx), _ptr(w_idx), _ptr(pool),
                               pool.shape[1], cand_block, topk, _ptr(topk_idx), _ptr(ws), wsb, _stream(stream)),

@@ -11,7 +11,7 @@ namespace {
 
 bool cache_ok(const csa2_cache_t* c) {
   return c && c->lat_codes && c->lat_scales && c->idx_codes && c->idx_scales && c->block_table &&
-         c->n_pages > 0 && c->max_pages > 0;
+         c->n_pages > 0 && c->max_pages > 0 && c->ratio >= 0 && c->ratio <= 2;
 }
 
 bool pow2_in(int v, int lo, int hi) { return v >= lo && v <= hi && (v & (v - 1)) == 0; }
@@ -35,12 +35,14 @@ const char* csa2_strerror(int code) {
   }
 }
 
-size_t csa2_workspace_size(int fn, int B, int H, int64_t max_ctx, int topk, int pool_blocks, int C) {
-  if (B <= 0) return 0;
+size_t csa2_workspace_size(int fn, int B, int H, int64_t max_ctx, int topk, int pool_blocks, int C,
+                           int ratio) {
+  if (B <= 0 || ratio < 0 || ratio > 2) return 0;
+  const int vs = ratio == 1 ? 0 : 1;
   switch (fn) {
     case CSA2_FN_INDEX_FULL:
       if (max_ctx < 0 || topk < 1 || topk > CSA2_MAX_TOPK || pool_blocks < 0) return 0;
-      return plan_index_full(B, max_ctx, topk, pool_blocks, 8).total;
+      return plan_index_full(B, max_ctx >> vs, topk, pool_blocks, 8).total;
     case CSA2_FN_REINDEX:
       return reindex_ws(B);
     case CSA2_FN_SPARSE_DECODE:
@@ -57,9 +59,10 @@ size_t csa2_workspace_size(int fn, int B, int H, int64_t max_ctx, int topk, int 
 int csa2_write_kv(const csa2_cache_t* cache, int B, const int32_t* start_tok, int T_new,
                   const uint16_t* x, const uint16_t* w, const uint16_t* k_idx, int ratio,
                   void* stream) {
-  if (!cache_ok(cache) || B <= 0 || !start_tok || !x || !w || !k_idx) return CSA2_EINVAL;
-  if (T_new <= 0 || (T_new & 1)) return CSA2_EINVAL;
-  if (ratio != 2) return ratio == 1 ? CSA2_EUNSUPPORTED : CSA2_EINVAL;
+  if (!cache_ok(cache) || B <= 0 || !start_tok || !x || !k_idx) return CSA2_EINVAL;
+  if (ratio != cache_ratio(*cache)) return CSA2_EINVAL;
+  if (ratio == 2 && (!w || T_new <= 0 || (T_new & 1))) return CSA2_EINVAL;
+  if (ratio == 1 && T_new <= 0) return CSA2_EINVAL;
   return launch_write_kv(*cache, B, start_tok, T_new, x, w, k_idx, (hipStream_t)stream);
 }
 
@@ -71,8 +74,9 @@ int csa2_index_full(const csa2_cache_t* cache, int B, const int32_t* ctx_len, in
   if (topk < 1 || topk > CSA2_MAX_TOPK || pool_blocks < 0 || max_ctx < 0) return CSA2_EINVAL;
   if (!pow2_in(cand_block, 1, 32)) return CSA2_EINVAL;
   if (pool_blocks > 0 && !pool) return CSA2_EINVAL;
-  if (max_ctx / 2 > (int64_t)cache->max_pages * CSA2_PAGE) return CSA2_EINVAL;
-  const IndexFullPlan p = plan_index_full(B, max_ctx, topk, pool_blocks, cand_block);
+  const int64_t max_nvis = max_ctx >> vis_shift(*cache);
+  if (max_nvis > (int64_t)cache->max_pages * CSA2_PAGE) return CSA2_EINVAL;
+  const IndexFullPlan p = plan_index_full(B, max_nvis, topk, pool_blocks, cand_block);
   if (p.chunk == 0) return CSA2_EUNSUPPORTED;
   if (p.total > 0 && (!ws || ws_bytes < p.total)) return CSA2_EWORKSPACE;
   return launch_index_full(*cache, B, ctx_len, max_ctx, q_idx, w_idx, topk, pool_blocks, cand_block,
@@ -113,6 +117,7 @@ int csa2_prefill_chunk(const csa2_cache_t* cache, int B, int H, const int32_t* p
     return CSA2_EINVAL;
   if (H <= 0 || (H % 16) != 0 || C <= 0 || W < 1 || W > CSA2_MAX_WINDOW) return CSA2_EINVAL;
   if (topk < 1 || topk > CSA2_MAX_TOPK || max_ctx < C) return CSA2_EINVAL;
+  if (cache_ratio(*cache) != 2) return CSA2_EUNSUPPORTED;   // the encoder's path
   if (max_ctx / 2 > (int64_t)cache->max_pages * CSA2_PAGE) return CSA2_EINVAL;
   const size_t need = prefill_ws(B, H, max_ctx, topk, C);
   if (need > 0 && (!ws || ws_bytes < need)) return CSA2_EWORKSPACE;

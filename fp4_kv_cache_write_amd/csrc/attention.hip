@@ -84,6 +84,7 @@ struct DecArgs {
   float scale_log2;        // sm_scale * log2(e)
   uint16_t* out;
   float* lse;
+  int vshift;              // token count -> visible entries: >> vshift
   float* part;             // split: [B*C*HG][nsplit][kPartFloats]
   int B, C, H, HG, prefill, q_per_xcd, nsplit;
 };
@@ -264,7 +265,7 @@ __global__ __launch_bounds__(kThreads) void sparse_decode_kernel(DecArgs a) {
   int64_t Lq = a.len[b];
   if (Lq < 0) Lq = 0;
   if (a.prefill) Lq += ci + 1;   // chunk query ci sits at position prior + ci
-  const int n_vis = (int)(Lq >> 1);
+  const int n_vis = (int)(Lq >> a.vshift);
   const int t = (int)Lq - 1;
   const uint16_t* win_b = a.win + (int64_t)b * (a.prefill ? a.W - 1 + a.C : a.W) * CSA2_D_LATENT;
   const int32_t* tk = a.topk_idx + qi * a.topk;
@@ -639,7 +640,7 @@ __global__ __launch_bounds__(kThreads) void sparse_decode64_kernel(DecArgs a) {
   int64_t Lq = a.len[b];
   if (Lq < 0) Lq = 0;
   if (a.prefill) Lq += ci + 1;
-  const int n_vis = (int)(Lq >> 1);
+  const int n_vis = (int)(Lq >> a.vshift);
   const int t = (int)Lq - 1;
   const uint16_t* win_b = a.win + (int64_t)b * (a.prefill ? a.W - 1 + a.C : a.W) * CSA2_D_LATENT;
   const int32_t* tk = a.topk_idx + qi * a.topk;
@@ -1027,6 +1028,7 @@ int launch_gather_attention(const csa2_cache_t& c, int B, int C, int H, const in
   a.H = H;
   a.HG = H / 16;
   a.prefill = prefill ? 1 : 0;
+  a.vshift = vis_shift(c);
   a.part = nullptr;
   a.nsplit = 1;
   const int64_t nq = (int64_t)B * C;

@@ -32,11 +32,13 @@ constexpr int kMergeCap = 32768;     // keys the merge / pool workgroup selects 
 constexpr int kReindexThreads = 512;
 constexpr int kReindexCap = 16384;
 
-__device__ __forceinline__ int n_visible_entries(const int32_t* ctx_len, int b, int64_t max_ctx) {
+// Entries visible to a decode query of ctx_len[b] tokens: one per `ratio` tokens,
+// given as the shift vshift (1 for ratio 2, 0 for ratio 1).
+__device__ __forceinline__ int n_visible_entries(const int32_t* ctx_len, int b, int64_t max_ctx, int vshift) {
   int64_t L = ctx_len[b];
   if (L < 0) L = 0;
   if (L > max_ctx) L = max_ctx;
-  return (int)(L >> 1);
+  return (int)(L >> vshift);
 }
 
 // A-operand of the indexer MFMA: lane (m = l%16, g = l/16) holds head m's dims
@@ -83,6 +85,7 @@ struct ScanArgs {
   int n_pages, max_pages;
   const int32_t* ctx_len;
   int64_t max_ctx;
+  int vshift;            // token count -> visible entries: >> vshift
   const uint16_t* q_idx;
   const uint16_t* w_idx;
   int topk, n_chunks, cand_block, want_blocks, max_blocks;
@@ -102,7 +105,7 @@ __global__ __launch_bounds__(kScanThreads) void index_scan_kernel(ScanArgs a) {
   uint32_t* scratch = hist + kSelectHist;         // [kSelectScratch]
   const int b = blockIdx.x / a.n_chunks;
   const int c = blockIdx.x - b * a.n_chunks;
-  const int n_vis = n_visible_entries(a.ctx_len, b, a.max_ctx);
+  const int n_vis = n_visible_entries(a.ctx_len, b, a.max_ctx, a.vshift);
   const int e0 = c * CHUNK;
   const int64_t slot = (int64_t)b * a.n_chunks + c;
   if (e0 >= n_vis) {
@@ -197,6 +200,7 @@ __global__ __launch_bounds__(kScanThreads) void index_scan_kernel(ScanArgs a) {
 struct MergeArgs {
   const int32_t* ctx_len;
   int64_t max_ctx;
+  int vshift;            // token count -> visible entries: >> vshift
   int topk, chunk, n_chunks, cand_block, pool_blocks, max_blocks;
   const uint32_t* cand_key;
   const int32_t* cand_idx;
@@ -213,7 +217,7 @@ __global__ __launch_bounds__(kMergeThreads) void index_merge_kernel(MergeArgs a)
   __shared__ uint32_t hist[kSelectHist];
   __shared__ uint32_t scratch[kSelectScratch];
   const int b = blockIdx.x;
-  const int n_vis = n_visible_entries(a.ctx_len, b, a.max_ctx);
+  const int n_vis = n_visible_entries(a.ctx_len, b, a.max_ctx, a.vshift);
   const int tid = threadIdx.x;
   const int p0 = tid * KPT;
   uint32_t kr[KPT];
@@ -254,6 +258,7 @@ __global__ __launch_bounds__(kMergeThreads) void index_merge_kernel(MergeArgs a)
 struct GroupArgs {
   const int32_t* ctx_len;
   int64_t max_ctx;
+  int vshift;            // token count -> visible entries: >> vshift
   int topk, chunk, n_chunks, group, n_groups;
   const uint32_t* cand_key;
   const int32_t* cand_idx;
@@ -273,7 +278,7 @@ __global__ __launch_bounds__(kMergeThreads) void index_group_kernel(GroupArgs a)
   __shared__ uint32_t hist[kSelectHist];
   __shared__ uint32_t scratch[kSelectScratch];
   const int b = blockIdx.x, grp = blockIdx.y;
-  const int n_vis = n_visible_entries(a.ctx_len, b, a.max_ctx);
+  const int n_vis = n_visible_entries(a.ctx_len, b, a.max_ctx, a.vshift);
   const int nc = (n_vis + a.chunk - 1) / a.chunk;
   const int c0 = grp * a.group;
   const int64_t gslot = (int64_t)b * a.n_groups + grp;
@@ -318,6 +323,7 @@ struct ReindexArgs {
   const int32_t* pool;
   int pool_blocks, cand_block, topk;
   int32_t* topk_idx;
+  int vshift;            // token count -> visible entries: >> vshift
 };
 
 // One workgroup per sequence: score the pool's entries (slot v = p*cb + i is entry
@@ -333,7 +339,7 @@ __global__ __launch_bounds__(kReindexThreads) void reindex_kernel(ReindexArgs a)
   const int b = blockIdx.x;
   int64_t L = a.ctx_len[b];
   if (L < 0) L = 0;
-  const int64_t n_vis = L >> 1;
+  const int64_t n_vis = L >> a.vshift;
   const int cb = a.cand_block;
   const int N = a.pool_blocks * cb;
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
@@ -430,7 +436,7 @@ __global__ __launch_bounds__(256) void reindex_score_kernel(ReindexArgs a, uint3
   if (v0 >= N) return;
   int64_t L = a.ctx_len[b];
   if (L < 0) L = 0;
-  const int64_t n_vis = L >> 1;
+  const int64_t n_vis = L >> a.vshift;
   const int lane = threadIdx.x & 63;
   const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15, g = lane >> 4;
@@ -535,10 +541,9 @@ bool lds_limits_set() {
 
 }  // namespace
 
-IndexFullPlan plan_index_full(int B, int64_t max_ctx, int topk, int pool_blocks, int cand_block) {
+IndexFullPlan plan_index_full(int B, int64_t max_nvis, int topk, int pool_blocks, int cand_block) {
   (void)cand_block;
   IndexFullPlan p{};
-  const int64_t max_nvis = max_ctx / 2;
   int ch = 4096;
   while (ch < topk) ch *= 2;
   int64_t nc = (max_nvis + ch - 1) / ch;
@@ -582,9 +587,11 @@ IndexFullPlan plan_index_full(int B, int64_t max_ctx, int topk, int pool_blocks,
 int launch_index_full(const csa2_cache_t& c, int B, const int32_t* ctx_len, int64_t max_ctx,
                       const uint16_t* q_idx, const uint16_t* w_idx, int topk, int pool_blocks,
                       int cand_block, int32_t* topk_idx, int32_t* pool, void* ws, hipStream_t s) {
-  const IndexFullPlan p = plan_index_full(B, max_ctx, topk, pool_blocks, cand_block);
+  const int vs = vis_shift(c);
+  const int64_t max_nvis = max_ctx >> vs;
+  const IndexFullPlan p = plan_index_full(B, max_nvis, topk, pool_blocks, cand_block);
   if (p.chunk == 0) return CSA2_EUNSUPPORTED;
-  if (pool_blocks > 0 && (max_ctx / 2 + cand_block - 1) / cand_block > kMergeCap) return CSA2_EUNSUPPORTED;
+  if (pool_blocks > 0 && (max_nvis + cand_block - 1) / cand_block > kMergeCap) return CSA2_EUNSUPPORTED;
   if (!lds_limits_set()) return CSA2_EHIP;
   uint8_t* w = static_cast<uint8_t*>(ws);
   ScanArgs sa;
@@ -595,6 +602,7 @@ int launch_index_full(const csa2_cache_t& c, int B, const int32_t* ctx_len, int6
   sa.max_pages = c.max_pages;
   sa.ctx_len = ctx_len;
   sa.max_ctx = max_ctx;
+  sa.vshift = vs;
   sa.q_idx = q_idx;
   sa.w_idx = w_idx;
   sa.topk = topk;
@@ -620,6 +628,7 @@ int launch_index_full(const csa2_cache_t& c, int B, const int32_t* ctx_len, int6
   MergeArgs ma;
   ma.ctx_len = ctx_len;
   ma.max_ctx = max_ctx;
+  ma.vshift = vs;
   ma.topk = topk;
   ma.chunk = p.chunk;
   ma.n_chunks = p.n_chunks;
@@ -627,6 +636,7 @@ int launch_index_full(const csa2_cache_t& c, int B, const int32_t* ctx_len, int6
     GroupArgs ga;
     ga.ctx_len = ctx_len;
     ga.max_ctx = max_ctx;
+    ga.vshift = vs;
     ga.topk = topk;
     ga.chunk = p.chunk;
     ga.n_chunks = p.n_chunks;
@@ -653,7 +663,7 @@ int launch_index_full(const csa2_cache_t& c, int B, const int32_t* ctx_len, int6
   ma.topk_idx = topk_idx;
   ma.pool = pool;
   const int64_t n_cand = (int64_t)ma.n_chunks * topk;
-  const int64_t n_blk = pool_blocks > 0 ? (max_ctx / 2 + cand_block - 1) / cand_block : 0;
+  const int64_t n_blk = pool_blocks > 0 ? (max_nvis + cand_block - 1) / cand_block : 0;
   const int64_t need = n_cand > n_blk ? n_cand : n_blk;
   const dim3 mgrid(B, pool_blocks > 0 ? 2 : 1);
   if (need <= 4 * kMergeThreads)
@@ -688,6 +698,7 @@ int launch_reindex(const csa2_cache_t& c, int B, const int32_t* ctx_len, const u
   ra.cand_block = cand_block;
   ra.topk = topk;
   ra.topk_idx = topk_idx;
+  ra.vshift = vis_shift(c);
   const int N = pool_blocks * cand_block;
   if (ws && ws_bytes >= reindex_ws(B)) {
     uint32_t* keys = static_cast<uint32_t*>(ws);

@@ -9,17 +9,23 @@
 
 namespace csa2 {
 
+// Tokens per entry of a cache (0 in the descriptor means 2), and the shift that
+// turns a token count into the visible entry count: n_vis = tokens >> shift.
+inline int cache_ratio(const csa2_cache_t& c) { return c.ratio == 1 ? 1 : 2; }
+inline int vis_shift(const csa2_cache_t& c) { return c.ratio == 1 ? 0 : 1; }
+
 // Workspace layout of csa2_index_full, shared by the size query and the launcher.
 struct IndexFullPlan {
   int chunk;          // entries scored by one workgroup (power of two, >= topk)
-  int n_chunks;       // chunks covering max_ctx/2 entries
-  int max_blocks;     // candidate blocks covering max_ctx/2 entries
+  int n_chunks;       // chunks covering max_nvis entries
+  int max_blocks;     // candidate blocks covering max_nvis entries
   int group;          // chunks merged per group before the final merge (0: no groups)
   int n_groups;
   size_t off_cand_key, off_cand_idx, off_cand_cnt, off_blockmax;
   size_t off_grp_key, off_grp_idx, off_grp_cnt, total;
 };
-IndexFullPlan plan_index_full(int B, int64_t max_ctx, int topk, int pool_blocks, int cand_block);
+// max_nvis: the most entries any sequence has visible (max_ctx >> vis_shift).
+IndexFullPlan plan_index_full(int B, int64_t max_nvis, int topk, int pool_blocks, int cand_block);
 
 int launch_write_kv(const csa2_cache_t& c, int B, const int32_t* start_tok, int T_new,
                     const uint16_t* x, const uint16_t* w, const uint16_t* k_idx, hipStream_t s);

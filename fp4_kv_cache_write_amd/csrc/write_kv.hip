@@ -1,10 +1,12 @@
-// Write path: pairwise merge of two tokens into one entry, MXFP4 quantisation of the
-// 512-d latent and the 64-d indexer key, scatter into the paged cache.
+// Write path: pairwise merge of two tokens into one entry (ratio 2) or one token per
+// entry (ratio 1), MXFP4 quantisation of the 512-d latent and the 64-d indexer key,
+// scatter into the paged cache.
 //
 // [P1] "DeepSeek-v4.1 Flash: KVキャッシュ圧縮の限界を押し広げる" §1.1 (the encoder
 // merges two adjacent positions with learned per-channel weights) and §2.3.1 (no
 // window overlap, no absolute position embedding; the indexer key is derived from
-// the entry).  FP4 block format and rounding: see csa2.h.
+// the entry; the ratio-1 special case leaves the decoder's entries unmerged).  FP4
+// block format and rounding: see csa2.h.
 //
 // One wavefront per entry.  Lane l owns channels 8l..8l+7: four 16-byte loads
 // (x and w of both tokens), one fused multiply-add per channel, an MX block of 32
@@ -52,30 +54,41 @@ __global__ __launch_bounds__(256) void write_kv_kernel(
     uint8_t* __restrict__ idx_codes, uint8_t* __restrict__ idx_scales, int n_pages,
     const int32_t* __restrict__ block_table, int max_pages, const int32_t* __restrict__ start_tok,
     int half, int64_t total, const uint16_t* __restrict__ x, const uint16_t* __restrict__ w,
-    const uint16_t* __restrict__ k_idx) {
+    const uint16_t* __restrict__ k_idx, int ratio) {
+  // half: entries per sequence (tokens / ratio)
   const int64_t e = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (e >= total) return;
   const int lane = threadIdx.x & 63;
   const int b = (int)(e / half);
   const int i = (int)(e - (int64_t)b * half);
   const int st = start_tok[b];
-  if (st < 0 || (st & 1)) return;                        // caller contract: even start
-  const int j = (st >> 1) + i;
+  if (st < 0 || (ratio == 2 && (st & 1))) return;       // caller contract: even start at ratio 2
+  const int j = (ratio == 2 ? (st >> 1) : st) + i;
   const int page = page_of(block_table, max_pages, n_pages, b, j);
   if (page < 0) return;
   const int64_t row = (int64_t)page * CSA2_PAGE + (j & (CSA2_PAGE - 1));
 
-  // ---- latent: y = w0*x0 + w1*x1 with one rounding (w1*x1 is exact in fp32) ----
-  const int64_t tok0 = ((int64_t)b * 2 * half + 2 * i) * CSA2_D_LATENT + lane * 8;
-  const u32x4 xa = *reinterpret_cast<const u32x4*>(x + tok0);
-  const u32x4 xb = *reinterpret_cast<const u32x4*>(x + tok0 + CSA2_D_LATENT);
-  const u32x4 wa = *reinterpret_cast<const u32x4*>(w + tok0);
-  const u32x4 wb = *reinterpret_cast<const u32x4*>(w + tok0 + CSA2_D_LATENT);
   float y[8];
+  if (ratio == 2) {
+    // ---- latent: y = w0*x0 + w1*x1 with one rounding (w1*x1 is exact in fp32) ----
+    const int64_t tok0 = ((int64_t)b * 2 * half + 2 * i) * CSA2_D_LATENT + lane * 8;
+    const u32x4 xa = *reinterpret_cast<const u32x4*>(x + tok0);
+    const u32x4 xb = *reinterpret_cast<const u32x4*>(x + tok0 + CSA2_D_LATENT);
+    const u32x4 wa = *reinterpret_cast<const u32x4*>(w + tok0);
+    const u32x4 wb = *reinterpret_cast<const u32x4*>(w + tok0 + CSA2_D_LATENT);
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    y[2 * q] = fmaf(lo_bf16(wa[q]), lo_bf16(xa[q]), lo_bf16(wb[q]) * lo_bf16(xb[q]));
-    y[2 * q + 1] = fmaf(hi_bf16(wa[q]), hi_bf16(xa[q]), hi_bf16(wb[q]) * hi_bf16(xb[q]));
+    for (int q = 0; q < 4; ++q) {
+      y[2 * q] = fmaf(lo_bf16(wa[q]), lo_bf16(xa[q]), lo_bf16(wb[q]) * lo_bf16(xb[q]));
+      y[2 * q + 1] = fmaf(hi_bf16(wa[q]), hi_bf16(xa[q]), hi_bf16(wb[q]) * hi_bf16(xb[q]));
+    }
+  } else {
+    // ---- latent: the token itself (bf16 is exact in fp32) ----
+    const u32x4 xa = *reinterpret_cast<const u32x4*>(x + ((int64_t)b * half + i) * CSA2_D_LATENT + lane * 8);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      y[2 * q] = lo_bf16(xa[q]);
+      y[2 * q + 1] = hi_bf16(xa[q]);
+    }
   }
   uint32_t codes, u;
   mx_quant8(y, codes, u);
@@ -157,14 +170,15 @@ __global__ __launch_bounds__(256) void debug_gather_kernel(
 
 int launch_write_kv(const csa2_cache_t& c, int B, const int32_t* start_tok, int T_new,
                     const uint16_t* x, const uint16_t* w, const uint16_t* k_idx, hipStream_t s) {
-  const int half = T_new / 2;
+  const int ratio = cache_ratio(c);
+  const int half = T_new / ratio;   // entries per sequence
   const int64_t total = (int64_t)B * half;
   if (total == 0) return CSA2_OK;
   const int64_t grid = (total + 3) / 4;
   if (grid > 0x7fffffff) return CSA2_EUNSUPPORTED;
   hipLaunchKernelGGL(write_kv_kernel, dim3((unsigned)grid), dim3(256), 0, s, c.lat_codes,
                      c.lat_scales, c.idx_codes, c.idx_scales, c.n_pages, c.block_table,
-                     c.max_pages, start_tok, half, total, x, w, k_idx);
+                     c.max_pages, start_tok, half, total, x, w, k_idx, ratio);
   return hip_status();
 }
 

@@ -67,8 +67,12 @@ enum {
   CSA2_FN_PREFILL_CHUNK = 4
 };
 
-/* Paged cache of merged entries.  Entry j of sequence b lives in slot j % 64 of
- * page block_table[b * max_pages + j / 64].  Per entry:
+/* Paged cache of entries.  Entry j of sequence b lives in slot j % 64 of
+ * page block_table[b * max_pages + j / 64].  ratio ([P1] §2.3.1) is the number of
+ * tokens per entry: 2 for the encoder's cache (entry j merges tokens 2j, 2j+1) and
+ * 1 for the decoder's (entry j is token j, uncompressed in the sequence dimension);
+ * 0 means 2.  A query at token t sees floor((t+1)/ratio) entries, so a context of
+ * L tokens has floor(L/ratio).  Per entry:
  *   lat_codes  [n_pages][64][256]  512 e2m1 codes, channel 2i in the low nibble
  *   lat_scales [n_pages][64][16]   e8m0 scale byte of channels 32k..32k+31
  *   idx_codes  [n_pages][64][32]   64 e2m1 indexer-key codes
@@ -83,6 +87,7 @@ typedef struct csa2_cache_t {
   int32_t n_pages;
   const int32_t *block_table; /* [B][max_pages] int32 (device) */
   int32_t max_pages;
+  int32_t ratio;              /* tokens per entry: 2 (or 0) or 1 */
 } csa2_cache_t;
 
 /* Bytes one merged entry occupies: 272 latent + 34 indexer = 306. */
@@ -92,12 +97,17 @@ int csa2_bytes_per_entry(void);
 const char *csa2_strerror(int code);
 
 /* Workspace bytes `fn` needs for these sizes (0 if none).  max_ctx bounds every
- * ctx_len / prior_len + C (tokens); pool_blocks is the Full layer's pool quota. */
-size_t csa2_workspace_size(int fn, int B, int H, int64_t max_ctx, int topk, int pool_blocks, int C);
+ * ctx_len / prior_len + C (tokens); pool_blocks is the Full layer's pool quota;
+ * ratio is the cache's (2, or 0 meaning 2, or 1). */
+size_t csa2_workspace_size(int fn, int B, int H, int64_t max_ctx, int topk, int pool_blocks, int C,
+                           int ratio);
 
-/* csa2_write_kv — encoder write path ([P1] §1.1 sequence dimension, §2.3.1
- * compressor): merge token pairs with per-channel weights, quantise to FP4, store.
- *   For each sequence b and i < T_new/2, entry j = start_tok[b]/2 + i is
+/* csa2_write_kv — write path ([P1] §1.1 sequence dimension, §2.3.1 compressor).
+ *   ratio must equal the cache's.  Ratio 2 (encoder): merge token pairs with
+ *   per-channel weights, quantise to FP4, store.  Ratio 1 (decoder): entry
+ *   j = start_tok[b] + i is token i quantised as it is (y = x[b][i]; w unused, may
+ *   be NULL); k_idx: [B][T_new][64]; any start_tok >= 0 and T_new >= 1.
+ *   Ratio 2: for each sequence b and i < T_new/2, entry j = start_tok[b]/2 + i is
  *     y_c = fp32_rne(w[b][2i][c] * x[b][2i][c] + w[b][2i+1][c] * x[b][2i+1][c])
  *   (exact products and sum, one rounding; no normalisation), then every block of
  *   32 channels is quantised: scale exponent e = clamp(floor(log2 max|y|) - 2,
@@ -107,15 +117,14 @@ size_t csa2_workspace_size(int fn, int B, int H, int64_t max_ctx, int topk, int 
  *   trained weight the caller applies, [P1] §2.3.1) is quantised the same way.
  *   x, w: [B][T_new][512] bf16 (device); k_idx: [B][T_new/2][64] bf16 (device);
  *   start_tok: [B] int32 (device), even.  T_new must be even (> 0); an unpaired last
- *   token is the caller's to resubmit with the next one.  ratio must be 2 (the
- *   decoder's ratio 1 is not built: CSA2_EUNSUPPORTED).  The table must already hold
- *   pages for every written entry. */
+ *   token is the caller's to resubmit with the next one.  The table must already
+ *   hold pages for every written entry. */
 int csa2_write_kv(const csa2_cache_t *cache, int B, const int32_t *start_tok, int T_new,
                   const uint16_t *x, const uint16_t *w, const uint16_t *k_idx, int ratio,
                   void *stream);
 
 /* csa2_index_full — Full-mode indexer ([P1] §2.3.2 Full mode, §2.3.4 HSI).
- *   For every sequence b with n = floor(ctx_len[b]/2) visible entries:
+ *   For every sequence b with n = floor(ctx_len[b]/ratio) visible entries:
  *     s_j = sum_{h<4} w_idx[b][h] * max(0, q_idx[b][h] . k_j)   (k_j dequantised)
  *   topk_idx[b] = the min(topk, n) entries with the largest s (ties: lower j), in
  *   ascending j order, padded with -1.  If pool_blocks > 0: block maxima over blocks
@@ -125,8 +134,8 @@ int csa2_write_kv(const csa2_cache_t *cache, int B, const int32_t *start_tok, in
  *   ctx_len: [B] int32 tokens (device), each <= max_ctx; q_idx: [B][4][64] bf16;
  *   w_idx: [B][4] bf16; topk_idx: [B][topk] int32; pool: [B][pool_blocks] int32 or
  *   NULL when pool_blocks == 0 (all device).  1 <= topk <= 2048; cand_block in
- *   {1,2,4,8,16,32}; max_ctx/2 <= 64 * max_pages.  ws: csa2_workspace_size(
- *   CSA2_FN_INDEX_FULL, B, 0, max_ctx, topk, pool_blocks, 0) bytes (device). */
+ *   {1,2,4,8,16,32}; max_ctx/ratio <= 64 * max_pages.  ws: csa2_workspace_size(
+ *   CSA2_FN_INDEX_FULL, B, 0, max_ctx, topk, pool_blocks, 0, ratio) bytes (device). */
 int csa2_index_full(const csa2_cache_t *cache, int B, const int32_t *ctx_len, int64_t max_ctx,
                     const uint16_t *q_idx, const uint16_t *w_idx, int topk, int pool_blocks,
                     int cand_block, int32_t *topk_idx, int32_t *pool, void *ws, size_t ws_bytes,
@@ -134,12 +143,12 @@ int csa2_index_full(const csa2_cache_t *cache, int B, const int32_t *ctx_len, in
 
 /* csa2_reindex — Reindex mode ([P1] §2.3.2 Reindex mode, §2.3.4: later indexers
  *   score only the candidate pool).  Scores, with this layer's q_idx / w_idx, the
- *   visible entries j < floor(ctx_len[b]/2) of the blocks listed in pool[b] (block
+ *   visible entries j < floor(ctx_len[b]/ratio) of the blocks listed in pool[b] (block
  *   ids, -1 entries ignored, each block covering cand_block entries), and writes the
  *   min(topk, pool size) best (ties: lower j) to topk_idx[b] in ascending order,
  *   padded with -1.  Shapes as in csa2_index_full; pool_blocks * cand_block <= 16384.
  *   ws: optional.  With ws_bytes >= csa2_workspace_size(CSA2_FN_REINDEX, B, 0, 0, topk,
- *   pool_blocks, 0) (device memory) the pool is scored by many workgroups per
+ *   pool_blocks, 0, ratio) (device memory) the pool is scored by many workgroups per
  *   sequence and selected by a second pass; with ws == NULL by one workgroup per
  *   sequence.  Results are the same. */
 int csa2_reindex(const csa2_cache_t *cache, int B, const int32_t *ctx_len, const uint16_t *q_idx,
@@ -150,7 +159,7 @@ int csa2_reindex(const csa2_cache_t *cache, int B, const int32_t *ctx_len, const
  *   ([P1] §2.3.1: each query attends to the selected entries and the layer's window
  *   KV together; [P3]: scores -> weights summing to 1 -> weighted sum of values).
  *   Rows R = dequantised latent of every valid topk_idx[b][i] (valid: 0 <= j <
- *   floor(ctx_len[b]/2)) followed by the window rows of positions max(0, t-W+1)..t,
+ *   floor(ctx_len[b]/ratio)) followed by the window rows of positions max(0, t-W+1)..t,
  *   t = ctx_len[b]-1, taken from swa[b][pos % W].  For every head h:
  *     z_r = sm_scale * q[b][h] . R_r,  p = softmax(z),  out[b][h] = sum_r p_r R_r
  *   (K = V = the 512-d latent), rounded to bf16; lse[b][h] = log sum_r exp(z_r).
@@ -158,7 +167,7 @@ int csa2_reindex(const csa2_cache_t *cache, int B, const int32_t *ctx_len, const
  *   q: [B][H][512] bf16; topk_idx: [B][topk] int32; swa: [B][W][512] bf16;
  *   out: [B][H][512] bf16; lse: [B][H] float or NULL (all device).  H a multiple of
  *   16; 1 <= W <= 1024; 0 <= topk <= 2048.  ws (optional, device): with
- *   csa2_workspace_size(CSA2_FN_SPARSE_DECODE, B, H, 0, topk, 0, 0) bytes, a call
+ *   csa2_workspace_size(CSA2_FN_SPARSE_DECODE, B, H, 0, topk, 0, 0, ratio) bytes, a call
  *   with fewer (sequence, 16-head group) pairs than the GPU has CUs spreads each
  *   pair's rows over several workgroups and merges their partial softmax states
  *   (same result up to fp32 rounding order); NULL with ws_bytes = 0 runs one
@@ -179,7 +188,8 @@ int csa2_sparse_decode(const csa2_cache_t *cache, int B, int H, const int32_t *c
  *   (bf16, device); out: [B][C][H][512] bf16; topk_idx: [B][C][topk] int32 or NULL
  *   (then the lists live in the workspace).  prior_len: [B] int32 (device),
  *   prior_len[b] + C <= max_ctx.  H a multiple of 16; 1 <= W <= 1024; 1 <= topk <= 2048.
- *   ws: csa2_workspace_size(CSA2_FN_PREFILL_CHUNK, B, H, max_ctx, topk, 0, C) bytes
+ *   Chunked prefill is the encoder's path: a ratio-1 cache gives CSA2_EUNSUPPORTED.
+ *   ws: csa2_workspace_size(CSA2_FN_PREFILL_CHUNK, B, H, max_ctx, topk, 0, C, 2) bytes
  *   (device): per-query candidate lists, and the top-K lists when topk_idx is NULL. */
 int csa2_prefill_chunk(const csa2_cache_t *cache, int B, int H, const int32_t *prior_len,
                        int64_t max_ctx, int C, const uint16_t *q, const uint16_t *q_idx,

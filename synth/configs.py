@@ -48,6 +48,7 @@ class DecodeConfig:
     window: int = WINDOW
     cand_block: int = CAND_BLOCK
     seed: int = 1000
+    ratio: int = RATIO                 # tokens per entry: 2 (encoder) or 1 (decoder)
 
     @property
     def n_layers(self) -> int:
@@ -83,6 +84,12 @@ CONFIGS = {
                     layers=(LayerSpec("full", 512), LayerSpec("reuse"), LayerSpec("reindex"),
                             LayerSpec("reuse")),
                     pages="fragmented", append=64, seed=1004),
+    # The decoder's ratio-1 cache (one entry per token) with the pages' HSI setting of
+    # 2048 candidate blocks of 8 positions (16384 candidates); 32K tokens per sequence
+    # give the same 32768 entries as config 1.
+    5: DecodeConfig("c5_b32_ctx32k_h64_ratio1_pool2048", B=32, H=64, ctx=(32768,) * 32,
+                    layers=(LayerSpec("full", 2048), LayerSpec("reindex"), LayerSpec("reuse")),
+                    heavy_frac=0.05, seed=1005, ratio=1),
 }
 
 
@@ -100,7 +107,7 @@ def small_decode(base: int, B: int, ctx: Tuple[int, ...] | None = None, H: int |
         pages=kw.pop("pages", c.pages), heavy_frac=kw.pop("heavy_frac", c.heavy_frac),
         append=kw.pop("append", c.append), ctx_range=ctx_range, topk=kw.pop("topk", c.topk),
         window=kw.pop("window", c.window), cand_block=kw.pop("cand_block", c.cand_block),
-        seed=seed if seed is not None else c.seed + 100)
+        seed=seed if seed is not None else c.seed + 100, ratio=kw.pop("ratio", c.ratio))
 
 
 def small_prefill(B: int = 2, prior: int = 3000, C: int = 96, H: int = 16, seed: int = 1103,

@@ -13,7 +13,10 @@ Recipes (all bf16 values are the round-to-nearest-even image of an fp32 draw):
   * indexer keys, queries, indexer queries, indexer head weights, window rows:
     N(0,1).
   * heavy tail: a seeded uniform choice of round(frac * n) entries whose two
-    source tokens and indexer key are multiplied by 4 (exact in bf16).
+    source tokens (one at ratio 1) and indexer key are multiplied by 4 (exact in
+    bf16).
+  * ratio-1 (decoder) caches: one entry per token, the token's x and indexer key
+    as drawn (no merge weights).
   * page tables: identity, a random permutation of all pages, or a random
     permutation of exactly the pages the batch needs ("fragmented").
   * log-uniform lengths: L = even(round(exp(U(ln lo, ln hi)))).
@@ -123,29 +126,38 @@ class DecodeCase:
         return self.cfg.B
 
     @property
-    def n_vis(self) -> List[int]:
-        return [L // RATIO for L in self.ctx_len]
+    def ratio(self) -> int:
+        return self.cfg.ratio
 
-    def seq_tokens(self, b: int, recipe: str = "l2") -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
-        """Merge inputs of the pre-built part of sequence b: x, w [T,512], k_idx [T/2,64]."""
+    @property
+    def n_vis(self) -> List[int]:
+        return [L // self.cfg.ratio for L in self.ctx_len]
+
+    def seq_tokens(self, b: int, recipe: str = "l2"):
+        """Write inputs of the pre-built part of sequence b: x [T,512], w [T,512] (None at
+        ratio 1), k_idx [T/ratio, 64]."""
         T = self.prebuilt[b]
+        r = self.cfg.ratio
         x = self.gen.normal_bf16((T, D_LATENT), "x", b)
-        w = self.gen.merge_weights(T, recipe, "w", b)
-        k = self.gen.normal_bf16((T // 2, D_INDEX), "kidx", b)
-        n_heavy = int(round(self.cfg.heavy_frac * (T // 2)))
+        w = self.gen.merge_weights(T, recipe, "w", b) if r == 2 else None
+        k = self.gen.normal_bf16((T // r, D_INDEX), "kidx", b)
+        n_heavy = int(round(self.cfg.heavy_frac * (T // r)))
         if n_heavy > 0:
-            sel = self.gen.randperm(T // 2, "heavy", b)[:n_heavy]
-            tok = torch.cat([2 * sel, 2 * sel + 1])
+            sel = self.gen.randperm(T // r, "heavy", b)[:n_heavy]
+            tok = torch.cat([2 * sel, 2 * sel + 1]) if r == 2 else sel
             x[tok] = x[tok] * 4
             k[sel] = k[sel] * 4
         return x, w, k
 
-    def append_tokens(self) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor, torch.Tensor]:
-        """Tokens the step appends: x, w [B, A, 512], k_idx [B, A/2, 64], start_tok int32 [B]."""
+    def append_tokens(self):
+        """Tokens the step appends: x, w [B, A, 512] (w None at ratio 1), k_idx
+        [B, A/ratio, 64], start_tok int32 [B]."""
         A = self.cfg.append
+        r = self.cfg.ratio
         x = self.gen.normal_bf16((self.B, A, D_LATENT), "x_app")
-        w = torch.stack([self.gen.merge_weights(A, "sum", "w_app", b) for b in range(self.B)])
-        k = self.gen.normal_bf16((self.B, A // 2, D_INDEX), "kidx_app")
+        w = (torch.stack([self.gen.merge_weights(A, "sum", "w_app", b) for b in range(self.B)])
+             if r == 2 else None)
+        k = self.gen.normal_bf16((self.B, A // r, D_INDEX), "kidx_app")
         start = torch.tensor(self.prebuilt, dtype=torch.int32)
         return x, w, k, start
 
@@ -172,9 +184,10 @@ def make_decode_case(cfg: DecodeConfig, device: str | torch.device = "cpu",
     else:
         assert len(cfg.ctx) == cfg.B
         ctx = list(cfg.ctx)
-    assert all(L % 2 == 0 for L in ctx) and cfg.append % 2 == 0
+    assert cfg.ratio in (1, 2)
+    assert all(L % cfg.ratio == 0 for L in ctx) and cfg.append % cfg.ratio == 0
     prebuilt = [L - cfg.append for L in ctx]
-    pages = [(L // RATIO + PAGE - 1) // PAGE for L in ctx]
+    pages = [(L // cfg.ratio + PAGE - 1) // PAGE for L in ctx]
     bt, n_pages = _block_table(gen, cfg.pages, pages)
     return DecodeCase(cfg=cfg, gen=gen, ctx_len=ctx, prebuilt=prebuilt, block_table=bt, n_pages=n_pages)
 

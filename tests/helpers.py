@@ -19,30 +19,30 @@ def gpu_available() -> bool:
 
 def oracle_cache_for(case, recipe: str = "l2", seqs=None) -> OracleCache:
     """Oracle cache holding the pre-built part of every sequence of a DecodeCase."""
-    oc = OracleCache(case.n_pages, case.block_table.numpy())
+    ratio = getattr(case.cfg, "ratio", 2)
+    oc = OracleCache(case.n_pages, case.block_table.numpy(), ratio=ratio)
     for b in (range(case.B) if seqs is None else seqs):
         if case.prebuilt[b] == 0:
             continue
         x, w, k = case.seq_tokens(b, recipe)
-        oc.write(b, 0, bits(x), bits(w), bits(k))
+        oc.write(b, 0, bits(x), None if w is None else bits(w), bits(k))
     return oc
 
 
 def gpu_cache_for(case, recipe: str = "l2", device="cuda"):
     """PagedCache filled by csa2_write_kv with the same pre-built tokens, one sequence at a time."""
     import fp4_kv_cache_write_amd as fk
-    cache = fk.PagedCache.allocate(case.n_pages, case.block_table, device=device)
-    full = torch.from_numpy(np.ascontiguousarray(case.block_table.numpy()))
+    ratio = getattr(case.cfg, "ratio", 2)
+    cache = fk.PagedCache.allocate(case.n_pages, case.block_table, device=device, ratio=ratio)
     for b in range(case.B):
         T = case.prebuilt[b]
         if T == 0:
             continue
         x, w, k = case.seq_tokens(b, recipe)
-        sub = fk.PagedCache(cache.lat_codes, cache.lat_scales, cache.idx_codes, cache.idx_scales,
-                            full[b:b + 1].to(device))
+        sub = cache.rows(b, b + 1)
         start = torch.zeros(1, dtype=torch.int32, device=device)
-        fk.write_kv(sub, start, x.to(device)[None].contiguous(), w.to(device)[None].contiguous(),
-                    k.to(device)[None].contiguous())
+        fk.write_kv(sub, start, x.to(device)[None].contiguous(),
+                    None if w is None else w.to(device)[None].contiguous(), k.to(device)[None].contiguous())
     torch.cuda.synchronize()
     return cache
 

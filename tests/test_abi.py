@@ -40,15 +40,19 @@ def test_workspace_sizes_are_consistent():
     b = fk.workspace_size(fk.FN_INDEX_FULL, B=32, max_ctx=65536, topk=512, pool_blocks=0)
     assert a > 0 and b > 0 and a >= b
     assert fk.workspace_size(fk.FN_INDEX_FULL, B=0, max_ctx=100) == 0
+    # a ratio-1 cache has twice the entries for the same tokens: at least as much workspace
+    r1 = fk.workspace_size(fk.FN_INDEX_FULL, B=32, max_ctx=65536, topk=512, pool_blocks=512, ratio=1)
+    assert r1 >= a
+    assert fk.workspace_size(fk.FN_INDEX_FULL, B=32, max_ctx=65536, topk=512, ratio=3) == 0
     assert fk.workspace_size(99, B=1) == 0
 
 
-def _fake_cache(max_pages=4):
+def _fake_cache(max_pages=4, ratio=0):
     # Non-null host addresses: validation must reject the call before anything
     # dereferences them or launches a kernel.
     buf = (ctypes.c_uint8 * 64)()
     addr = ctypes.addressof(buf)
-    return binding.CacheT(addr, addr, addr, addr, 4, addr, max_pages), buf
+    return binding.CacheT(addr, addr, addr, addr, 4, addr, max_pages, ratio), buf
 
 
 def test_host_argument_errors_return_before_launch():
@@ -60,8 +64,9 @@ def test_host_argument_errors_return_before_launch():
     assert L.csa2_write_kv(None, 1, p, 2, p, p, p, 2, None) == EINVAL
     assert L.csa2_write_kv(ref, 1, p, 3, p, p, p, 2, None) == EINVAL        # odd token count
     assert L.csa2_write_kv(ref, 1, p, 0, p, p, p, 2, None) == EINVAL
-    assert L.csa2_write_kv(ref, 1, p, 2, p, p, p, 1, None) == EUNS         # ratio 1 not built
+    assert L.csa2_write_kv(ref, 1, p, 2, p, p, p, 1, None) == EINVAL       # ratio differs from the cache's
     assert L.csa2_write_kv(ref, 1, None, 2, p, p, p, 2, None) == EINVAL
+    assert L.csa2_write_kv(ref, 1, p, 2, p, None, p, 2, None) == EINVAL    # ratio 2 needs w
     assert L.csa2_index_full(ref, 1, p, 128, p, p, 0, 0, 8, p, None, None, 0, None) == EINVAL  # topk 0
     assert L.csa2_index_full(ref, 1, p, 128, p, p, 4096, 0, 8, p, None, None, 0, None) == EINVAL
     assert L.csa2_index_full(ref, 1, p, 128, p, p, 16, 4, 8, p, None, None, 0, None) == EINVAL  # pool NULL
@@ -75,6 +80,16 @@ def test_host_argument_errors_return_before_launch():
     assert L.csa2_sparse_decode(ref, 1, 16, p, p, None, 16, p, 128, 0.1, p, None, None, 0, None) == EINVAL
     assert L.csa2_prefill_chunk(ref, 1, 16, p, 128, 0, p, p, p, p, 128, 16, 0.1, p, None, None, 0, None) == EINVAL
     assert L.csa2_debug_gather(ref, 1, p, 4, None, None, None) == EINVAL
+    # a ratio-1 (decoder) cache: one entry per token
+    c1, keep1 = _fake_cache(ratio=1)
+    r1 = ctypes.byref(c1)
+    assert L.csa2_write_kv(r1, 1, p, 0, p, None, p, 1, None) == EINVAL      # no tokens
+    assert L.csa2_write_kv(r1, 1, p, 3, p, None, p, 2, None) == EINVAL      # ratio differs
+    assert L.csa2_index_full(r1, 1, p, 300, p, p, 16, 0, 8, p, None, None, 0, None) == EINVAL  # 300 entries > 256
+    assert L.csa2_index_full(r1, 1, p, 200, p, p, 16, 0, 8, p, None, None, 0, None) == EWS
+    assert L.csa2_prefill_chunk(r1, 1, 16, p, 128, 64, p, p, p, p, 128, 16, 0.1, p, None, None, 0, None) == EUNS
+    bad, keep2 = _fake_cache(ratio=3)
+    assert L.csa2_write_kv(ctypes.byref(bad), 1, p, 2, p, p, p, 2, None) == EINVAL
 
 
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):
