@@ -325,6 +325,49 @@ def bench_decode(fk, cfg_id: int, steps: int, warmup: int, n_rep: int, use_graph
                 roofline=roofline, use_graph=use_graph, count=count, per_bytes=per_bytes)
 
 
+def bench_schedule(fk, cfg_id: int, schedule, steps: int, warmup: int, n_rep: int = 4):
+    """One decode step of a whole layer schedule through the native runner
+    (csa2_schedule_*: the step's write plus every layer captured as one HIP graph),
+    replayed over n_rep cache replicas."""
+    import dataclasses
+    from synth import CONFIGS, make_decode_case
+    cfg = dataclasses.replace(CONFIGS[cfg_id], layers=tuple(schedule),
+                              name=CONFIGS[cfg_id].name + f"_schedule{len(schedule)}")
+    log(f"building {cfg.name} ({n_rep} replicas, native schedule runner)")
+    case = make_decode_case(cfg, device="cuda")
+    reps = build_decode(case, fk, n_rep)
+    dev = "cuda"
+    B, H = case.B, cfg.H
+    ctx = torch.tensor(case.ctx_len, dtype=torch.int32, device=dev)
+    outs = [torch.empty((B, H, 512), dtype=torch.bfloat16, device=dev) for _ in cfg.layers]
+    scheds = []
+    for R in reps:
+        layers = [dict(mode=sp.mode, pool_blocks=sp.pool_blocks, q=R.layers[l]["q"], q_idx=R.layers[l]["q_idx"],
+                       w_idx=R.layers[l]["w_idx"], swa=R.layers[l]["swa"], out=outs[l])
+                  for l, sp in enumerate(cfg.layers)]
+        scheds.append(fk.Schedule(R.cache, ctx, max(case.ctx_len), layers, W=cfg.window, topk=cfg.topk,
+                                  cand_block=cfg.cand_block, write=R.write))
+    for i in range(warmup):
+        scheds[i % n_rep].launch()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record()
+    for i in range(steps):
+        scheds[i % n_rep].launch()
+    ev1.record()
+    torch.cuda.synchronize()
+    ms = max(ev0.elapsed_time(ev1) / steps, (time.perf_counter() - t0) * 1e3 / steps)
+    _, count, step_bytes = decode_bytes(case)
+    for sc in scheds:
+        sc.close()
+    log(f"{cfg.name}: {ms * 1e3:.1f} us/step ({len(cfg.layers)} layers), {B / (ms / 1e3):.0f} queries/s")
+    return {"workload": cfg.name, "value": round(B / (ms / 1e3), 1), "unit": "queries/s",
+            "ms_per_step": round(ms, 5), "layers": len(cfg.layers), "us_per_layer": round(ms * 1e3 / len(cfg.layers), 2),
+            "achieved_gbs": round(step_bytes / (ms / 1e3) / 1e9, 1), "algorithmic_bytes_per_step": step_bytes,
+            "launch": "native schedule runner: write + all layers as one HIP graph"}
+
+
 # ----------------------------------------------------------------------------------
 # chunked prefill
 # ----------------------------------------------------------------------------------
@@ -443,6 +486,11 @@ def main() -> int:
             "frac_hbm_peak": round(c5["gbs"] / HBM_PEAK_GBS, 4), "algorithmic_bytes_per_step": c5["step_bytes"],
             "per_call_us": {n: round(v * 1e3, 2) for n, v in c5["per_call"].items()}, "roofline": c5["roofline"]}
         del c5
+        torch.cuda.empty_cache()
+        # the pages' whole decoder schedule (20 layers) at that size, through the native runner
+        from synth.configs import DECODER_SCHEDULE
+        secondary["c5_decoder_schedule20"] = bench_schedule(fk, 5, DECODER_SCHEDULE, max(10, args.steps // 10),
+                                                            max(3, args.warmup // 4))
         torch.cuda.empty_cache()
 
     cpu = None

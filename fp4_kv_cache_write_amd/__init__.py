@@ -5,10 +5,10 @@ include/csa2.h); this package is its ctypes binding.  There is no CPU or
 PyTorch fallback.
 """
 from . import binding
-from .binding import (Csa2Error, PagedCache, bytes_per_entry, debug_gather, index_full, lib,
+from .binding import (Csa2Error, PagedCache, Schedule, bytes_per_entry, debug_gather, index_full, lib,
                       prefill_chunk, reindex, sparse_decode, workspace, workspace_size, write_kv,
                       FN_INDEX_FULL, FN_REINDEX, FN_SPARSE_DECODE, FN_PREFILL_CHUNK)
 
-__all__ = ["binding", "Csa2Error", "PagedCache", "bytes_per_entry", "debug_gather", "index_full", "lib",
+__all__ = ["binding", "Csa2Error", "PagedCache", "Schedule", "bytes_per_entry", "debug_gather", "index_full", "lib",
            "prefill_chunk", "reindex", "sparse_decode", "workspace", "workspace_size", "write_kv",
            "FN_INDEX_FULL", "FN_REINDEX", "FN_SPARSE_DECODE", "FN_PREFILL_CHUNK"]

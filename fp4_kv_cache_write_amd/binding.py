@@ -20,11 +20,19 @@ FN_INDEX_FULL, FN_REINDEX, FN_SPARSE_DECODE, FN_PREFILL_CHUNK = 1, 2, 3, 4
 
 EXPORTS = ("csa2_bytes_per_entry", "csa2_strerror", "csa2_workspace_size", "csa2_write_kv",
            "csa2_index_full", "csa2_reindex", "csa2_sparse_decode", "csa2_prefill_chunk",
-           "csa2_debug_gather")
+           "csa2_debug_gather", "csa2_schedule_workspace_size", "csa2_schedule_create",
+           "csa2_schedule_launch", "csa2_schedule_destroy")
+LAYER_MODES = {"full": 0, "reindex": 1, "reuse": 2}
 
 
 class Csa2Error(RuntimeError):
     pass
+
+
+class LayerT(ctypes.Structure):
+    _fields_ = [("mode", ctypes.c_int32), ("pool_blocks", ctypes.c_int32), ("q", ctypes.c_void_p),
+                ("q_idx", ctypes.c_void_p), ("w_idx", ctypes.c_void_p), ("swa", ctypes.c_void_p),
+                ("out", ctypes.c_void_p), ("lse", ctypes.c_void_p)]
 
 
 class CacheT(ctypes.Structure):
@@ -67,6 +75,16 @@ def lib() -> ctypes.CDLL:
         L.csa2_prefill_chunk.argtypes = [C, I, I, P, I64, I, P, P, P, P, I, I, F, P, P, P, SZ, P]
         L.csa2_debug_gather.restype = I
         L.csa2_debug_gather.argtypes = [C, I, P, I, P, P, P]
+        LP = ctypes.POINTER(LayerT)
+        L.csa2_schedule_workspace_size.restype = SZ
+        L.csa2_schedule_workspace_size.argtypes = [I, I, I64, I, I, LP, I]
+        L.csa2_schedule_create.restype = I
+        L.csa2_schedule_create.argtypes = [C, I, I, P, I64, I, I, I, F, P, I, P, P, P, I, LP, P, SZ,
+                                           ctypes.POINTER(P)]
+        L.csa2_schedule_launch.restype = I
+        L.csa2_schedule_launch.argtypes = [P, P]
+        L.csa2_schedule_destroy.restype = None
+        L.csa2_schedule_destroy.argtypes = [P]
         _lib = L
     return _lib
 
@@ -284,3 +302,64 @@ def debug_gather(cache: PagedCache, idx: torch.Tensor, stream=None) -> Tuple[tor
     _check(lib().csa2_debug_gather(cache.ref, B, _ptr(idx), n, _ptr(lat), _ptr(key), _stream(stream)),
            "csa2_debug_gather")
     return lat, key
+
+
+class Schedule:
+    """One decode step of a layer schedule captured into a HIP graph (csa2_schedule_*).
+
+    layers: list of dicts with mode ("full" | "reindex" | "reuse"), pool_blocks (Full),
+    q, q_idx, w_idx (Full, Reindex), swa, out and optional lse tensors.  write: optional
+    dict (start, x, w, k) of the step's write.  The tensors are kept alive with the
+    schedule; their contents are read when launch() runs the graph.
+    """
+
+    def __init__(self, cache: PagedCache, ctx_len: torch.Tensor, max_ctx: int, layers, W: int,
+                 topk: int = 512, cand_block: int = 8, sm_scale: Optional[float] = None, write=None,
+                 ws: Optional[torch.Tensor] = None):
+        B = ctx_len.shape[0]
+        _need(ctx_len, torch.int32, "ctx_len", (B,))
+        H = layers[0]["q"].shape[1]
+        if sm_scale is None:
+            sm_scale = D_LATENT ** -0.5
+        arr = (LayerT * len(layers))()
+        keep = [cache, ctx_len]
+        for i, L in enumerate(layers):
+            _bf16(L["q"], "q", (B, H, D_LATENT))
+            _bf16(L["swa"], "swa", (B, W, D_LATENT))
+            _bf16(L["out"], "out", (B, H, D_LATENT))
+            if L["mode"] != "reuse":
+                _bf16(L["q_idx"], "q_idx", (B, H_INDEX, D_INDEX))
+                _bf16(L["w_idx"], "w_idx", (B, H_INDEX))
+            arr[i] = LayerT(LAYER_MODES[L["mode"]], L.get("pool_blocks", 0), _ptr(L["q"]), _ptr(L.get("q_idx")),
+                            _ptr(L.get("w_idx")), _ptr(L["swa"]), _ptr(L["out"]), _ptr(L.get("lse")))
+            keep += [v for v in L.values() if isinstance(v, torch.Tensor)]
+        n = lib().csa2_schedule_workspace_size(B, H, max_ctx, topk, len(layers), arr, cache.ratio)
+        if n == 0:
+            raise Csa2Error("csa2_schedule_workspace_size: invalid schedule")
+        if ws is None:
+            ws = torch.zeros(n, dtype=torch.uint8, device=ctx_len.device)
+        keep.append(ws)
+        wr = write or {}
+        x, w, k, start = wr.get("x"), wr.get("w"), wr.get("k"), wr.get("start")
+        T = x.shape[1] if x is not None else 0
+        keep += [t for t in (x, w, k, start) if t is not None]
+        handle = ctypes.c_void_p()
+        _check(lib().csa2_schedule_create(cache.ref, B, H, _ptr(ctx_len), max_ctx, topk, cand_block, W, sm_scale,
+                                          _ptr(start), T, _ptr(x), _ptr(w), _ptr(k), len(layers), arr, _ptr(ws),
+                                          ws.numel(), ctypes.byref(handle)), "csa2_schedule_create")
+        self._handle = handle
+        self._keep = keep
+
+    def launch(self, stream=None) -> None:
+        _check(lib().csa2_schedule_launch(self._handle, _stream(stream)), "csa2_schedule_launch")
+
+    def close(self) -> None:
+        if getattr(self, "_handle", None) is not None and self._handle.value:
+            lib().csa2_schedule_destroy(self._handle)
+        self._handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -994,6 +994,8 @@ int split_count(int64_t nq, int HG, int W, int topk) {
 
 }  // namespace
 
+bool attention_kernels_ready() { return lds_limit_set(); }
+
 size_t sparse_decode_ws(int B, int H, int topk) {
   (void)topk;
   const int HG = H / 16;

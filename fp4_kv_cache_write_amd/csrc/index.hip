@@ -541,6 +541,8 @@ bool lds_limits_set() {
 
 }  // namespace
 
+bool index_kernels_ready() { return lds_limits_set(); }
+
 IndexFullPlan plan_index_full(int B, int64_t max_nvis, int topk, int pool_blocks, int cand_block) {
   (void)cand_block;
   IndexFullPlan p{};

@@ -63,6 +63,11 @@ int launch_prefill_chunk(const csa2_cache_t& c, int B, int H, const int32_t* pri
                          const uint16_t* w_idx, const uint16_t* local, int W, int topk,
                          float sm_scale, uint16_t* out, int32_t* topk_idx, void* ws, hipStream_t s);
 
+// Kernel attributes (dynamic LDS limits) set once per process; the schedule runner
+// calls these before a stream capture so that no attribute call happens inside it.
+bool index_kernels_ready();
+bool attention_kernels_ready();
+
 inline int hip_status() {
   return hipGetLastError() == hipSuccess ? CSA2_OK : CSA2_EHIP;
 }

@@ -197,6 +197,54 @@ int csa2_prefill_chunk(const csa2_cache_t *cache, int B, int H, const int32_t *p
                        float sm_scale, uint16_t *out, int32_t *topk_idx, void *ws,
                        size_t ws_bytes, void *stream);
 
+/* Layer schedules ([P1] §2.3.2 modes, §2.3.3 schedules: an encoder block is one
+ * Full layer then five Reuse layers; the decoder runs [Full + 3 Reuse] then four
+ * blocks of [Reindex + 3 Reuse]). */
+enum { CSA2_LAYER_FULL = 0, CSA2_LAYER_REINDEX = 1, CSA2_LAYER_REUSE = 2 };
+
+/* One layer of a schedule.  All pointers device memory. */
+typedef struct csa2_layer_t {
+  int32_t mode;             /* CSA2_LAYER_* */
+  int32_t pool_blocks;      /* Full: candidate blocks kept for later Reindex layers (0: none) */
+  const uint16_t *q;        /* [B][H][512] bf16 */
+  const uint16_t *q_idx;    /* [B][4][64] bf16 (Full and Reindex layers) */
+  const uint16_t *w_idx;    /* [B][4] bf16 (Full and Reindex layers) */
+  const uint16_t *swa;      /* [B][W][512] bf16, ring slot pos % W */
+  uint16_t *out;            /* [B][H][512] bf16 */
+  float *lse;               /* [B][H] or NULL */
+} csa2_layer_t;
+
+typedef struct csa2_schedule csa2_schedule_t;   /* opaque: a captured HIP graph */
+
+/* Workspace bytes of csa2_schedule_create for these sizes and layers (0 if the
+ *   schedule is invalid).  ratio: the cache's. */
+size_t csa2_schedule_workspace_size(int B, int H, int64_t max_ctx, int topk, int n_layers,
+                                    const csa2_layer_t *layers, int ratio);
+
+/* csa2_schedule_create — capture one decode step of a layer schedule into a HIP
+ *   graph: the step's write (csa2_write_kv of T_new tokens at start_tok; skipped when
+ *   x is NULL), then per layer its selection (Full: csa2_index_full with the layer's
+ *   pool_blocks; Reindex: csa2_reindex over the pool of the latest Full layer that
+ *   kept one; Reuse: none) and csa2_sparse_decode with the latest selection.  The
+ *   graph runs exactly those calls on the buffers given here, so its results equal
+ *   theirs; every pointer and the workspace must stay valid while the schedule
+ *   exists, and their contents are read when the graph runs.  The first layer must
+ *   be Full; a Reindex layer needs an earlier Full layer with pool_blocks > 0.
+ *   Other arguments as in the single calls.  ws: csa2_schedule_workspace_size(...)
+ *   bytes (device), zero-filled once before the schedule's first launch (it holds
+ *   the split attention's state); calls that run at the same time need separate
+ *   workspaces.  On success *out receives the schedule; on failure *out is NULL. */
+int csa2_schedule_create(const csa2_cache_t *cache, int B, int H, const int32_t *ctx_len, int64_t max_ctx,
+                         int topk, int cand_block, int W, float sm_scale, const int32_t *start_tok, int T_new,
+                         const uint16_t *x, const uint16_t *w, const uint16_t *k_idx, int n_layers,
+                         const csa2_layer_t *layers, void *ws, size_t ws_bytes, csa2_schedule_t **out);
+
+/* Run the captured step on `stream` (asynchronous). */
+int csa2_schedule_launch(csa2_schedule_t *schedule, void *stream);
+
+/* Free the graph (host objects of the HIP runtime).  NULL is a no-op. */
+void csa2_schedule_destroy(csa2_schedule_t *schedule);
+
 /* csa2_debug_gather — test hook: dequantise entries through the page table with the
  *   same FP4 decode the kernels use.  idx: [B][n] int32 entry ids (device);
  *   out_lat: [B][n][512] float, out_idx: [B][n][64] float (device; either may be

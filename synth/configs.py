@@ -70,6 +70,13 @@ class PrefillConfig:
 
 FULL = LayerSpec("full")
 
+# The pages' schedules ([P1] §2.3.3): the decoder runs a Full block ([Full + 3 Reuse],
+# the Full layer keeping the 2048-block HSI pool of §2.3.4) and four Reindex blocks
+# ([Reindex + 3 Reuse]); an encoder block is [Full + 5 Reuse], three of them.
+DECODER_SCHEDULE = ((LayerSpec("full", 2048),) + (LayerSpec("reuse"),) * 3 +
+                    ((LayerSpec("reindex"),) + (LayerSpec("reuse"),) * 3) * 4)
+ENCODER_SCHEDULE = ((LayerSpec("full"),) + (LayerSpec("reuse"),) * 5) * 3
+
 CONFIGS = {
     0: DecodeConfig("c0_b1_ctx2k_h16_full", B=1, H=16, ctx=(2048,),
                     layers=(LayerSpec("full", 256),), seed=1000),

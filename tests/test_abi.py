@@ -97,3 +97,32 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(binding, "_LIB_PATH", str(tmp_path / "nope.so"))
     with pytest.raises(binding.Csa2Error):
         binding.lib()
+
+
+def test_schedule_validation_before_capture():
+    # invalid schedules are rejected on the host: no stream, capture or launch happens
+    L = fk.lib()
+    c, keep = _fake_cache()
+    p = ctypes.c_void_p(ctypes.addressof(keep))
+    EINVAL, EWS = -1, -2
+
+    def layers(*modes, pool=0):
+        arr = (binding.LayerT * len(modes))()
+        for i, m in enumerate(modes):
+            arr[i] = binding.LayerT(binding.LAYER_MODES[m], pool if m == "full" else 0, p, p, p, p, p, None)
+        return arr
+
+    ok = layers("full", "reuse", "reindex", "reuse", pool=64)
+    assert L.csa2_schedule_workspace_size(2, 16, 4096, 64, 4, ok, 2) > 0
+    assert L.csa2_schedule_workspace_size(2, 16, 4096, 64, 1, layers("reuse"), 2) == 0        # no selection yet
+    assert L.csa2_schedule_workspace_size(2, 16, 4096, 64, 2, layers("full", "reindex"), 2) == 0  # no pool
+    assert L.csa2_schedule_workspace_size(2, 12, 4096, 64, 4, ok, 2) == 0                      # H % 16
+    assert L.csa2_schedule_workspace_size(2, 16, 4096, 64, 4, ok, 3) == 0                      # ratio
+    out = ctypes.c_void_p()
+    ref = ctypes.byref(c)
+    args = (ref, 2, 16, p, 400, 64, 8, 128, 0.1, None, 0, None, None, None)   # 200 entries fit 4 pages
+    assert L.csa2_schedule_create(*args, 4, ok, p, 0, ctypes.byref(out)) == EWS and not out.value
+    assert L.csa2_schedule_create(*args, 1, layers("reuse"), p, 1 << 30, ctypes.byref(out)) == EINVAL
+    assert L.csa2_schedule_create(*args, 4, ok, p, 1 << 30, None) == EINVAL
+    assert L.csa2_schedule_launch(None, None) == EINVAL
+    L.csa2_schedule_destroy(None)
