@@ -337,7 +337,7 @@ class Schedule:
         if n == 0:
             raise Csa2Error("csa2_schedule_workspace_size: invalid schedule")
         if ws is None:
-            ws = torch.zeros(n, dtype=torch.uint8, device=ctx_len.device)
+            ws = torch.empty(n, dtype=torch.uint8, device=ctx_len.device)
         keep.append(ws)
         wr = write or {}
         x, w, k, start = wr.get("x"), wr.get("w"), wr.get("k"), wr.get("start")

@@ -231,8 +231,8 @@ size_t csa2_schedule_workspace_size(int B, int H, int64_t max_ctx, int topk, int
  *   exists, and their contents are read when the graph runs.  The first layer must
  *   be Full; a Reindex layer needs an earlier Full layer with pool_blocks > 0.
  *   Other arguments as in the single calls.  ws: csa2_schedule_workspace_size(...)
- *   bytes (device), zero-filled once before the schedule's first launch (it holds
- *   the split attention's state); calls that run at the same time need separate
+ *   bytes (device; no initialisation needed: every byte a launch reads was written
+ *   earlier in the same launch); schedules that run at the same time need separate
  *   workspaces.  On success *out receives the schedule; on failure *out is NULL. */
 int csa2_schedule_create(const csa2_cache_t *cache, int B, int H, const int32_t *ctx_len, int64_t max_ctx,
                          int topk, int cand_block, int W, float sm_scale, const int32_t *start_tok, int T_new,
