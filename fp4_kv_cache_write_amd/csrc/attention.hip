@@ -66,6 +66,7 @@ static_assert(kWinBatch * kWinB <= kBufBytes, "window batch fits a buffer");
 static_assert(kMaxTiles == kWaves, "one FP4 tile per wave");
 static_assert(2 * kFp4Batch == kThreads, "one prefetched row id per thread (two FP4 batches)");
 static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
+static_assert(16 * kWinB <= kPSlots * 64 * kPBytes, "q of 16 heads fits the P slots");
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -354,13 +355,16 @@ __global__ __launch_bounds__(kThreads) void sparse_decode_kernel(DecArgs a) {
   const int pf_i = tid & (kFp4Batch - 1), pf_f = tid >> 8;
   const int pf_r = fr0 + pf_f * kFp4Batch + pf_i;
   const int pf_e = (pf_f < n_fb && pf_r < fr1) ? tk[pf_r] : -1;
-  if (n_wb > 0) load_batch(0, st);
-  u32x4 qf[16];   // q operand of head hg*16+n: dims 128g + 8s .. +7 for k-step s
+  // q of the 16 heads is read from memory once per workgroup -- thread tid: head
+  // tid/32, dims 16(tid%32) .. +15 -- and handed to the waves through the P slots,
+  // which are free until the first P (rows at the window pitch, as win_qk reads them).
+  u32x4 qs[2];
   {
-    const uint16_t* qp = a.q + (qi * a.H + hg * 16 + n) * CSA2_D_LATENT + 128 * g;
-#pragma unroll
-    for (int s = 0; s < 16; ++s) qf[s] = *reinterpret_cast<const u32x4*>(qp + 8 * s);
+    const uint16_t* qp = a.q + (qi * a.H + hg * 16 + (tid >> 5)) * CSA2_D_LATENT + 16 * (tid & 31);
+    qs[0] = *reinterpret_cast<const u32x4*>(qp);
+    qs[1] = *reinterpret_cast<const u32x4*>(qp + 8);
   }
+  if (n_wb > 0) load_batch(0, st);
   int pf_page = -1;
   if (n_wb > 0) {
     if (page_ok(pf_e)) pf_page = bt[pf_e >> 6];
@@ -377,6 +381,17 @@ __global__ __launch_bounds__(kThreads) void sparse_decode_kernel(DecArgs a) {
   // the loop then cover only the next batch's loads, which stay in flight until the
   // batch is stored after PV.
   __builtin_amdgcn_s_waitcnt(0);
+  {
+    uint8_t* qd = plds + (tid >> 5) * kWinB + 32 * (tid & 31);
+    *reinterpret_cast<u32x4*>(qd) = qs[0];
+    *reinterpret_cast<u32x4*>(qd + 16) = qs[1];
+  }
+  u32x4 qf[16];   // q operand of head hg*16+n: dims 128g + 8s .. +7 for k-step s
+  auto read_q = [&]() {   // after a barrier that follows the stores above
+    const uint8_t* qp = plds + n * kWinB + 256 * g;
+#pragma unroll
+    for (int s = 0; s < 16; ++s) qf[s] = lds_ld<u32x4>(qp + 16 * s);
+  };
 
   f32x4 acc[4];
 #pragma unroll
@@ -427,8 +442,9 @@ __global__ __launch_bounds__(kThreads) void sparse_decode_kernel(DecArgs a) {
     const int nrows_f = min(fr1 - fr0, kFp4Batch);
     const int ntl_f = (nrows_f + 31) >> 5;
     rowid_all[tid] = row_of(pf_e, pf_page);
-    __syncthreads();   // window rows and the FP4 row ids stored by every thread
+    __syncthreads();   // window rows, q and the FP4 row ids stored by every thread
     load_batch(1, st);   // FP4 rows: in flight while the window tiles are scored
+    read_q();
     float zw[8], zf[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) zw[j] = zf[j] = -INFINITY;
@@ -455,6 +471,8 @@ __global__ __launch_bounds__(kThreads) void sparse_decode_kernel(DecArgs a) {
 #pragma unroll 1
     for (int tile = 0; tile < ntl_f; ++tile) pv_tile(buff, false, tile, tile);
   } else {
+  __syncthreads();   // q stored by every thread
+  read_q();
 #pragma unroll 1
   for (int k = 0; k < nb; ++k) {
     const bool is_win = k < n_wb;
