@@ -78,6 +78,33 @@ __device__ __forceinline__ float score16(u32x2 codes, uint32_t scale_byte, bf16x
   return wh[0] * relu0(acc[0]) + wh[1] * relu0(acc[1]) + wh[2] * relu0(acc[2]) + wh[3] * relu0(acc[3]);
 }
 
+// Maxima of blocks of CB consecutive keys, from the keys in registers (thread t holds
+// positions t*KPT .. +KPT-1): a thread holds KPT/CB whole blocks, or a block spans
+// CB/KPT adjacent lanes.  Block k goes to bm[k] for k < nb.
+template <int KPT, int CB>
+__device__ __forceinline__ void block_maxima(const uint32_t (&kr)[KPT], uint32_t* __restrict__ bm, int nb) {
+  if constexpr (CB <= KPT) {
+#pragma unroll
+    for (int j = 0; j < KPT; j += CB) {
+      uint32_t m = kr[j];
+#pragma unroll
+      for (int i = 1; i < CB; ++i) m = max(m, kr[j + i]);
+      const int k = (int)(threadIdx.x * (KPT / CB)) + j / CB;
+      if (k < nb) bm[k] = m;
+    }
+  } else {
+    constexpr int R = CB / KPT;   // lanes per block
+    static_assert(R <= 64, "a block lies within a wave");
+    uint32_t m = kr[0];
+#pragma unroll
+    for (int i = 1; i < KPT; ++i) m = max(m, kr[i]);
+#pragma unroll
+    for (int o = 1; o < R; o <<= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o, kWave));
+    const int k = (int)threadIdx.x / R;
+    if ((threadIdx.x & (R - 1)) == 0 && k < nb) bm[k] = m;
+  }
+}
+
 struct ScanArgs {
   const uint8_t* idx_codes;
   const uint8_t* idx_scales;
@@ -162,19 +189,6 @@ __global__ __launch_bounds__(kScanThreads) void index_scan_kernel(ScanArgs a) {
   for (int i = ((n_in + 15) & ~15) + threadIdx.x; i < CHUNK; i += kScanThreads) keys[i] = 0u;
   __syncthreads();
 
-  // HSI block maxima of this chunk (as keys): block k covers entries k*cb .. +cb-1.
-  if (a.want_blocks) {
-    const int cb = a.cand_block;
-    const int nb = (n_in + cb - 1) / cb;
-    const int blk0 = e0 / cb;
-    for (int k = threadIdx.x; k < nb; k += kScanThreads) {
-      uint32_t m = 0u;
-      const int lo = k * cb, hi = min(n_in, lo + cb);
-      for (int e = lo; e < hi; ++e) m = max(m, keys[e]);
-      a.block_max[(int64_t)b * a.max_blocks + blk0 + k] = m;
-    }
-  }
-
   uint32_t kr[KPT];
 #pragma unroll
   for (int i = 0; i < KPT; i += 4) {
@@ -183,6 +197,20 @@ __global__ __launch_bounds__(kScanThreads) void index_scan_kernel(ScanArgs a) {
     kr[i + 1] = v.y;
     kr[i + 2] = v.z;
     kr[i + 3] = v.w;
+  }
+  // HSI block maxima of this chunk (as keys): block k covers entries k*cb .. +cb-1;
+  // keys past the chunk's entries are 0 and leave the maxima unchanged.
+  if (a.want_blocks) {
+    uint32_t* bm = a.block_max + (int64_t)b * a.max_blocks + e0 / a.cand_block;
+    const int nb = (n_in + a.cand_block - 1) / a.cand_block;
+    switch (a.cand_block) {
+      case 1: block_maxima<KPT, 1>(kr, bm, nb); break;
+      case 2: block_maxima<KPT, 2>(kr, bm, nb); break;
+      case 4: block_maxima<KPT, 4>(kr, bm, nb); break;
+      case 8: block_maxima<KPT, 8>(kr, bm, nb); break;
+      case 16: block_maxima<KPT, 16>(kr, bm, nb); break;
+      default: block_maxima<KPT, 32>(kr, bm, nb); break;
+    }
   }
   const SelectResult sr = block_select<kScanThreads, KPT>(kr, a.topk, hist, scratch);
   uint32_t* ck = a.cand_key + slot * a.topk;

@@ -113,3 +113,54 @@ def test_reindex_matches_oracle_on_oracle_pool(fk, ctx, pool_blocks, cb, topk, s
         pos = pool_positions(pools[b][pools[b] >= 0], case.n_vis[b], cb)
         s = index_scores(bits(L1["q_idx"][b]), bits(L1["w_idx"][b]), oc.index_keys(b, pos))
         check_topk_set(tk[b], pos, s, topk)
+
+
+def _tied_caches(fk, ctx, factor_of, seed):
+    """Caches whose indexer keys are entry 0's key of each sequence times factor_of(n)[j]
+    (powers of two): the FP4 codes are equal and the scales shift, so every score is
+    exactly factor x the base score on both sides, and the selections are fully
+    decided by the lower-index rule among equal scores."""
+    from oracle import OracleCache
+    cfg = small_decode(1, B=len(ctx), ctx=ctx, H=16, pages="random", heavy_frac=0.0, append=0, seed=seed)
+    case = make_decode_case(cfg, "cpu")
+    gc = fk.PagedCache.allocate(case.n_pages, case.block_table, device="cuda", ratio=2)
+    oc = OracleCache(case.n_pages, case.block_table.numpy(), ratio=2)
+    for b in range(case.B):
+        x, w, k = case.seq_tokens(b)
+        f = torch.as_tensor(factor_of(k.shape[0]), dtype=torch.float32)[:, None]
+        k = (k[:1].float() * f).to(torch.bfloat16)
+        fk.write_kv(gc.rows(b, b + 1), torch.zeros(1, dtype=torch.int32, device="cuda"), x.cuda()[None].contiguous(),
+                    w.cuda()[None].contiguous(), k.cuda()[None].contiguous())
+        oc.write(b, 0, None, None, bits(k), latent=False)
+    torch.cuda.synchronize()
+    return case, gc, oc
+
+
+@pytest.mark.parametrize("kind", ["all_equal", "three_values"])
+def test_tied_scores_resolve_to_lowest_entries(fk, kind):
+    # Full top-K, HSI pool and Reindex must equal the oracle exactly: with scores tied
+    # in large groups, lower entry indices (and lower block indices) win.
+    ctx = (40000, 6000, 900, 2)
+    rng = np.random.default_rng(5)
+    if kind == "all_equal":
+        factor_of = lambda n: np.ones(n)
+    else:
+        factor_of = lambda n: rng.choice([1.0, 2.0, 4.0], size=n)
+    case, gc, oc = _tied_caches(fk, ctx, factor_of, seed=1207 if kind == "all_equal" else 1208)
+    L0, L1 = case.layer(0), case.layer(1)
+    ctx_len = torch.tensor(case.ctx_len, dtype=torch.int32, device="cuda")
+    topk, P, cb = 512, 300, 8
+    tk, pool = fk.index_full(gc, ctx_len, max(case.ctx_len), L0["q_idx"].cuda(), L0["w_idx"].cuda(), topk=topk,
+                             pool_blocks=P, cand_block=cb)
+    tk2 = fk.reindex(gc, ctx_len, L1["q_idx"].cuda(), L1["w_idx"].cuda(), pool, topk=topk, cand_block=cb)
+    torch.cuda.synchronize()
+    tk, pool, tk2 = tk.cpu().numpy(), pool.cpu().numpy(), tk2.cpu().numpy()
+    for b in range(case.B):
+        n_vis = case.n_vis[b]
+        t, p, _ = full_layer(oc, b, n_vis, bits(L0["q_idx"][b]), bits(L0["w_idx"][b]), topk, P, cb)
+        assert np.array_equal(tk[b][tk[b] >= 0], t), f"seq {b}: top-K"
+        assert np.array_equal(pool[b][pool[b] >= 0], np.sort(p)), f"seq {b}: pool"
+        t2, _ = reindex_layer(oc, b, n_vis, bits(L1["q_idx"][b]), bits(L1["w_idx"][b]), np.sort(p), cb, topk)
+        assert np.array_equal(tk2[b][tk2[b] >= 0], t2), f"seq {b}: Reindex"
+        if kind == "all_equal" and n_vis > topk:
+            assert np.array_equal(t, np.arange(topk))
