@@ -26,7 +26,7 @@ namespace csa2 {
 namespace {
 
 constexpr int kScanThreads = 512;
-constexpr int kScanRound = 16;       // groups of 16 entries a wave loads before scoring them (4 pages)
+constexpr int kScanRound = 8;        // groups of 16 entries a wave loads before scoring them (2 pages)
 constexpr int kMergeThreads = 1024;
 constexpr int kMergeCap = 32768;     // keys the merge / pool workgroup selects from
 constexpr int kReindexThreads = 512;
@@ -150,40 +150,65 @@ __global__ __launch_bounds__(kScanThreads) void index_scan_kernel(ScanArgs a) {
 #pragma unroll
   for (int h = 0; h < 4; ++h) wh[h] = bf16_to_f32(a.w_idx[b * CSA2_H_INDEX + h]);
 
-  // Wave w streams groups [w*GPW, (w+1)*GPW) of 16 entries.  A round covers 4
-  // pages: their ids are fetched first with scalar loads, then all code and scale
-  // loads of the round are issued before the first one is consumed.
+  // Wave w streams groups [w*GPW, (w+1)*GPW) of 16 entries in rounds of kScanRound
+  // groups (2 pages).  A round's page ids are fetched with scalar loads, then all its
+  // code and scale loads are issued; the next round is issued before this one is
+  // scored, so its memory latency overlaps the scoring.
   const int32_t* bt = a.block_table + (int64_t)b * a.max_pages;
-  for (int r0 = 0; r0 < GPW; r0 += kScanRound) {
-    const int eb0 = e0 + (wid * GPW + r0) * 16;               // wave-uniform round start
+  struct Round {
     int pg[kScanRound / 4];
+    u32x2 cd[kScanRound];
+    uint32_t sp[kScanRound / 4];   // lane l: the two scale bytes of entry l of page q
+  };
+  auto load_round = [&](int r0, Round& R) {
+    const int eb0 = e0 + (wid * GPW + r0) * 16;               // wave-uniform round start
 #pragma unroll
     for (int q = 0; q < kScanRound / 4; ++q) {
       const int pi = (eb0 >> 6) + q;
       int p = (eb0 + 64 * q < n_vis && pi < a.max_pages) ? bt[pi] : -1;
-      pg[q] = (p >= 0 && p < a.n_pages) ? p : -1;
+      R.pg[q] = (p >= 0 && p < a.n_pages) ? p : -1;
     }
-    u32x2 cd[kScanRound];
-    uint32_t sb[kScanRound];
+    // Every lane loads (lanes without an entry read row 0, which every cache has, and
+    // drop the value): no branch splits the loads, so the wait counts before each
+    // group's scoring stay exact while the later loads are in flight.  A page's 64
+    // entries keep their scales contiguous: one 2-byte load per lane covers them.
+#pragma unroll
+    for (int q = 0; q < kScanRound / 4; ++q) {
+      const int e = eb0 + 64 * q + lane;
+      const bool ok = R.pg[q] >= 0 && e < n_vis;
+      const int64_t row = ok ? (int64_t)R.pg[q] * CSA2_PAGE + lane : 0;
+      const uint32_t sv = *reinterpret_cast<const uint16_t*>(a.idx_scales + row * CSA2_IDX_SCALE_BYTES);
+      R.sp[q] = ok ? sv : 0u;
+    }
 #pragma unroll
     for (int u = 0; u < kScanRound; ++u) {
       const int e = eb0 + u * 16 + n;
-      const int page = pg[u >> 2];
-      cd[u] = u32x2{0u, 0u};
-      sb[u] = 0u;
-      if (page >= 0 && e < n_vis) {
-        const int64_t row = (int64_t)page * CSA2_PAGE + (e & (CSA2_PAGE - 1));
-        cd[u] = *reinterpret_cast<const u32x2*>(a.idx_codes + row * CSA2_IDX_CODE_BYTES + 8 * g);
-        sb[u] = a.idx_scales[row * CSA2_IDX_SCALE_BYTES + (g >> 1)];
-      }
+      const int page = R.pg[u >> 2];
+      const bool ok = page >= 0 && e < n_vis;
+      const int64_t row = ok ? (int64_t)page * CSA2_PAGE + (e & (CSA2_PAGE - 1)) : 0;
+      const u32x2 cv = *reinterpret_cast<const u32x2*>(a.idx_codes + row * CSA2_IDX_CODE_BYTES + 8 * g);
+      R.cd[u] = ok ? cv : u32x2{0u, 0u};
     }
+  };
+  auto score_round = [&](int r0, const Round& R) {
 #pragma unroll
     for (int u = 0; u < kScanRound; ++u) {
       const int le = (wid * GPW + r0 + u) * 16;
       if (e0 + le >= n_vis) break;                        // wave-uniform
-      const float s = score16(cd[u], sb[u], a0, a1, wh);
-      if (lane < 16) keys[le + n] = (le + n < n_in && pg[u >> 2] >= 0) ? score_key(s) : 0u;   // absent page: no entry
+      // scale byte g/2 of entry n of this group: lane 16(u%4) + n of the page's load
+      const uint32_t sw = (uint32_t)__shfl((int)R.sp[u >> 2], 16 * (u & 3) + n, kWave);
+      const float s = score16(R.cd[u], (sw >> (8 * (g >> 1))) & 0xffu, a0, a1, wh);
+      if (lane < 16) keys[le + n] = (le + n < n_in && R.pg[u >> 2] >= 0) ? score_key(s) : 0u;   // absent page: no entry
     }
+  };
+  static_assert(GPW % kScanRound == 0, "whole rounds per wave");
+  constexpr int NR = GPW / kScanRound;
+  Round rr[2];
+  load_round(0, rr[0]);
+#pragma unroll
+  for (int i = 0; i < NR; ++i) {
+    if (i + 1 < NR) load_round((i + 1) * kScanRound, rr[(i + 1) & 1]);
+    score_round(i * kScanRound, rr[i & 1]);
   }
   // tail of a partial chunk: keys of absent entries are 0
   for (int i = ((n_in + 15) & ~15) + threadIdx.x; i < CHUNK; i += kScanThreads) keys[i] = 0u;
