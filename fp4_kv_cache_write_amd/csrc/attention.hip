@@ -293,10 +293,11 @@ __global__ __launch_bounds__(kThreads) void sparse_decode_kernel(DecArgs a) {
   };
   // Batch k in registers: thread tid holds chunks c = tid + 512u (16 bytes each) of
   // the batch image -- FP4: piece c%17 of row c/17 (16 code pieces, then the scales);
-  // window: piece c%64 of row c/64 -- zeros where no row is.
+  // window: piece c%64 of row c/64 -- zeros where no row is.  Every chunk is loaded
+  // (one with no row reads window row 0 of the sequence or cache row 0, and is
+  // dropped), so no branch splits the loads: they issue back to back.
   auto load_batch = [&](int k, u32x4 (&st)[kStage]) {
-#pragma unroll
-    for (int u = 0; u < kStage; ++u) st[u] = u32x4{0u, 0u, 0u, 0u};
+    const u32x4 zero = {0u, 0u, 0u, 0u};
     if (k < n_wb) {
       const int w0 = wr0 + k * kWinBatch;
       int slot0 = (t - (a.W - 1) + w0) % a.W;   // ring slot of the batch's first position
@@ -305,29 +306,34 @@ __global__ __launch_bounds__(kThreads) void sparse_decode_kernel(DecArgs a) {
       for (int u = 0; u < kWinBatch * 64 / kThreads; ++u) {
         const int c = tid + kThreads * u;
         const int r = c >> 6, piece = c & 63;
-        if (w0 + r < wr1 && win_valid(a.W, t, w0 + r)) {
-          int row;
-          if (a.prefill) {
-            row = ci + w0 + r;
-          } else {
-            row = slot0 + r;
-            if (row >= a.W) row -= a.W;
-          }
-          st[u] = *reinterpret_cast<const u32x4*>(win_b + (int64_t)row * CSA2_D_LATENT + 8 * piece);
-        }
+        const bool ok = w0 + r < wr1 && win_valid(a.W, t, w0 + r);
+        int row = a.prefill ? ci + w0 + r : (slot0 + r >= a.W ? slot0 + r - a.W : slot0 + r);
+        row = ok ? row : 0;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(win_b + (int64_t)row * CSA2_D_LATENT + 8 * piece);
+        st[u] = ok ? v : zero;
       }
+#pragma unroll
+      for (int u = kWinBatch * 64 / kThreads; u < kStage; ++u) st[u] = zero;
     } else {
       const int f = k - n_wb;
       const int nrows = min(fr1 - fr0 - f * kFp4Batch, kFp4Batch);
       const int32_t* rowid = rowid_all + (f & 1) * kFp4Batch;
+      int rid[kStage];
+#pragma unroll
+      for (int u = 0; u < kStage; ++u) {
+        const int c = tid + kThreads * u;
+        rid[u] = rowid[min(c / 17, kFp4Batch - 1)];
+      }
 #pragma unroll
       for (int u = 0; u < kStage; ++u) {
         const int c = tid + kThreads * u;
         const int r = c / 17, piece = c - r * 17;
-        const int rid = (c < kFp4Batch * 17 && r < nrows) ? rowid[r] : -1;
-        if (rid >= 0)
-          st[u] = *reinterpret_cast<const u32x4*>(piece < 16 ? a.lat_codes + (int64_t)rid * CSA2_LAT_CODE_BYTES + 16 * piece
-                                                           : a.lat_scales + (int64_t)rid * CSA2_LAT_SCALE_BYTES);
+        const bool ok = c < kFp4Batch * 17 && r < nrows && rid[u] >= 0;
+        const int64_t rw = ok ? rid[u] : 0;
+        const uint8_t* src = piece < 16 ? a.lat_codes + rw * CSA2_LAT_CODE_BYTES + 16 * piece
+                                        : a.lat_scales + rw * CSA2_LAT_SCALE_BYTES;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(src);
+        st[u] = ok ? v : zero;
       }
     }
   };

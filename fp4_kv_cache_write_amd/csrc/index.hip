@@ -499,13 +499,18 @@ __global__ __launch_bounds__(256) void reindex_score_kernel(ReindexArgs a, uint3
 #pragma unroll
   for (int h = 0; h < 4; ++h) wh[h] = bf16_to_f32(a.w_idx[b * CSA2_H_INDEX + h]);
   const int32_t* pool = a.pool + (int64_t)b * a.pool_blocks;
+  const int32_t* bt = a.block_table + (int64_t)b * a.max_pages;
   constexpr int kGroups = kReSlice / 16 / 4;    // 16-slot groups per wave
-  // slot of group u for this lane: v0 + (wid * kGroups + u) * 16 + n
+  // Slot of group u for this lane: v0 + (wid * kGroups + u) * 16 + n.  Three rounds of
+  // loads (pool blocks, page ids, keys), each issued whole: lanes without a slot or an
+  // entry load element 0 / row 0 (which exist whenever this workgroup runs) and drop
+  // the value, so no branch splits a round and each round costs one wait.
   int blk[kGroups];
 #pragma unroll
   for (int u = 0; u < kGroups; ++u) {
     const int v = v0 + (wid * kGroups + u) * 16 + n;
-    blk[u] = v < N ? pool[v / cb] : -1;
+    const int bv = pool[v < N ? v / cb : 0];
+    blk[u] = v < N ? bv : -1;
   }
   int pg[kGroups];
   int64_t ent[kGroups];
@@ -513,19 +518,19 @@ __global__ __launch_bounds__(256) void reindex_score_kernel(ReindexArgs a, uint3
   for (int u = 0; u < kGroups; ++u) {
     const int v = v0 + (wid * kGroups + u) * 16 + n;
     ent[u] = (int64_t)blk[u] * cb + (v % cb);
-    pg[u] = (blk[u] >= 0 && ent[u] < n_vis) ? page_of(a.block_table, a.max_pages, a.n_pages, b, (int)ent[u]) : -1;
+    const bool ok = blk[u] >= 0 && ent[u] < n_vis && (ent[u] >> 6) < a.max_pages;
+    const int p = bt[ok ? (int)(ent[u] >> 6) : 0];
+    pg[u] = (ok && p >= 0 && p < a.n_pages) ? p : -1;
   }
   u32x2 cd[kGroups];
   uint32_t sb[kGroups];
 #pragma unroll
   for (int u = 0; u < kGroups; ++u) {
-    cd[u] = u32x2{0u, 0u};
-    sb[u] = 0u;
-    if (pg[u] >= 0) {
-      const int64_t row = (int64_t)pg[u] * CSA2_PAGE + (ent[u] & (CSA2_PAGE - 1));
-      cd[u] = *reinterpret_cast<const u32x2*>(a.idx_codes + row * CSA2_IDX_CODE_BYTES + 8 * g);
-      sb[u] = a.idx_scales[row * CSA2_IDX_SCALE_BYTES + (g >> 1)];
-    }
+    const int64_t row = pg[u] >= 0 ? (int64_t)pg[u] * CSA2_PAGE + (ent[u] & (CSA2_PAGE - 1)) : 0;
+    const u32x2 cv = *reinterpret_cast<const u32x2*>(a.idx_codes + row * CSA2_IDX_CODE_BYTES + 8 * g);
+    const uint32_t sv = a.idx_scales[row * CSA2_IDX_SCALE_BYTES + (g >> 1)];
+    cd[u] = pg[u] >= 0 ? cv : u32x2{0u, 0u};
+    sb[u] = pg[u] >= 0 ? sv : 0u;
   }
   uint32_t* kout = keys_ws + (int64_t)b * kReindexCap;
 #pragma unroll
