@@ -687,9 +687,9 @@ __global__ __launch_bounds__(kThreads) void sparse_decode64_kernel(DecArgs a) {
       rowid[i] = page_ok(e) ? row_of(e, bt[e >> 6]) : -1;
     }
   };
+  // Every chunk is loaded, as in the 16-head kernel: no branch splits the loads.
   auto load_batch = [&](int k, u32x4 (&st)[kStage64]) {
-#pragma unroll
-    for (int u = 0; u < kStage64; ++u) st[u] = u32x4{0u, 0u, 0u, 0u};
+    const u32x4 zero = {0u, 0u, 0u, 0u};
     if (k < n_wb) {
       const int w0 = k * kWb64;
       int slot0 = (t - (a.W - 1) + w0) % a.W;
@@ -698,29 +698,34 @@ __global__ __launch_bounds__(kThreads) void sparse_decode64_kernel(DecArgs a) {
       for (int u = 0; u < kWb64 * 64 / kThreads; ++u) {
         const int c = tid + kThreads * u;
         const int r = c >> 6, piece = c & 63;
-        if (win_valid(a.W, t, w0 + r)) {
-          int row;
-          if (a.prefill) {
-            row = ci + w0 + r;
-          } else {
-            row = slot0 + r;
-            if (row >= a.W) row -= a.W;
-          }
-          st[u] = *reinterpret_cast<const u32x4*>(win_b + (int64_t)row * CSA2_D_LATENT + 8 * piece);
-        }
+        const bool ok = win_valid(a.W, t, w0 + r);
+        int row = a.prefill ? ci + w0 + r : (slot0 + r >= a.W ? slot0 + r - a.W : slot0 + r);
+        row = ok ? row : 0;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(win_b + (int64_t)row * CSA2_D_LATENT + 8 * piece);
+        st[u] = ok ? v : zero;
       }
+#pragma unroll
+      for (int u = kWb64 * 64 / kThreads; u < kStage64; ++u) st[u] = zero;
     } else {
       const int f = k - n_wb;
       const int nrows = min(a.topk - f * kFb64, kFb64);
       const int32_t* rowid = rowid_all + (f % kPf64) * kFb64;
+      int rid[kStage64];
+#pragma unroll
+      for (int u = 0; u < kStage64; ++u) {
+        const int c = tid + kThreads * u;
+        rid[u] = rowid[min(c / 17, kFb64 - 1)];
+      }
 #pragma unroll
       for (int u = 0; u < kStage64; ++u) {
         const int c = tid + kThreads * u;
         const int r = c / 17, piece = c - r * 17;
-        const int rid = (c < kFb64 * 17 && r < nrows) ? rowid[r] : -1;
-        if (rid >= 0)
-          st[u] = *reinterpret_cast<const u32x4*>(piece < 16 ? a.lat_codes + (int64_t)rid * CSA2_LAT_CODE_BYTES + 16 * piece
-                                                           : a.lat_scales + (int64_t)rid * CSA2_LAT_SCALE_BYTES);
+        const bool ok = c < kFb64 * 17 && r < nrows && rid[u] >= 0;
+        const int64_t rw = ok ? rid[u] : 0;
+        const uint8_t* src = piece < 16 ? a.lat_codes + rw * CSA2_LAT_CODE_BYTES + 16 * piece
+                                        : a.lat_scales + rw * CSA2_LAT_SCALE_BYTES;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(src);
+        st[u] = ok ? v : zero;
       }
     }
   };
