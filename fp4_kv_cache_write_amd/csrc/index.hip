@@ -126,7 +126,7 @@ template <int CHUNK>
 __global__ __launch_bounds__(kScanThreads) void index_scan_kernel(ScanArgs a) {
   constexpr int KPT = CHUNK / kScanThreads;
   constexpr int GPW = CHUNK / 16 / (kScanThreads / 64);   // groups per wave
-  extern __shared__ uint32_t smem[];
+  extern __shared__ __align__(16) uint32_t smem[];
   uint32_t* keys = smem;                          // [CHUNK]
   uint32_t* hist = smem + CHUNK;                  // [kSelectHist]
   uint32_t* scratch = hist + kSelectHist;         // [kSelectScratch]
@@ -267,7 +267,7 @@ struct MergeArgs {
 // KPT (keys per thread) is the smallest of 4/8/16/32 that covers both key sets.
 template <int KPT>
 __global__ __launch_bounds__(kMergeThreads) void index_merge_kernel(MergeArgs a) {
-  __shared__ uint32_t hist[kSelectHist];
+  __shared__ __align__(16) uint32_t hist[kSelectHist];
   __shared__ uint32_t scratch[kSelectScratch];
   const int b = blockIdx.x;
   const int n_vis = n_visible_entries(a.ctx_len, b, a.max_ctx, a.vshift);
@@ -328,7 +328,7 @@ struct GroupArgs {
 // keys stay in entry order.
 template <int KPT>
 __global__ __launch_bounds__(kMergeThreads) void index_group_kernel(GroupArgs a) {
-  __shared__ uint32_t hist[kSelectHist];
+  __shared__ __align__(16) uint32_t hist[kSelectHist];
   __shared__ uint32_t scratch[kSelectScratch];
   const int b = blockIdx.x, grp = blockIdx.y;
   const int n_vis = n_visible_entries(a.ctx_len, b, a.max_ctx, a.vshift);
@@ -385,7 +385,7 @@ struct ReindexArgs {
 template <int KPT>
 __global__ __launch_bounds__(kReindexThreads) void reindex_kernel(ReindexArgs a) {
   constexpr int kCap = KPT * kReindexThreads;
-  extern __shared__ uint32_t smem[];
+  extern __shared__ __align__(16) uint32_t smem[];
   uint32_t* keys = smem;                          // [kCap]
   uint32_t* hist = smem + kCap;
   uint32_t* scratch = hist + kSelectHist;
@@ -543,7 +543,7 @@ __global__ __launch_bounds__(256) void reindex_score_kernel(ReindexArgs a, uint3
 
 template <int KPT>
 __global__ __launch_bounds__(kReSelThreads) void reindex_select_kernel(ReindexArgs a, const uint32_t* __restrict__ keys_ws) {
-  __shared__ uint32_t hist[kSelectHist];
+  __shared__ __align__(16) uint32_t hist[kSelectHist];
   __shared__ uint32_t scratch[kSelectScratch];
   const int b = blockIdx.x;
   const int cb = a.cand_block;
