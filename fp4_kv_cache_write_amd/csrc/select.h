@@ -100,13 +100,45 @@ __device__ SelectResult block_select(const uint32_t (&key)[KPT], int K, uint32_t
     const int shift = left - width;
     const uint32_t dmask = (1u << width) - 1u;
     uint32_t* H = hist + (pass & 1) * kHistStride;
+    // Tied scores (e.g. the exact zeros ReLU produces) put many keys on one digit,
+    // and 64 same-address LDS atomics in one instruction serialise.  A wave whose
+    // first key slot shows 16 or more lanes on one digit therefore counts, per slot,
+    // the lanes that share the first active lane's digit with a single atomic; other
+    // waves add every key on its own.
+    bool agg;
+    {
+      const uint32_t x = key[0];
+      const bool in = x != 0u && ((x - kmin) & mask) == prefix;
+      const uint32_t d = ((x - kmin) >> shift) & dmask;
+      const uint64_t vm = __ballot(in);
+      const uint32_t hot = __builtin_amdgcn_readlane(d, vm ? __builtin_ctzll(vm) : 0);
+      agg = __popcll(__ballot(in && d == hot)) >= 16;
+    }
+    if (agg) {
 #pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      const uint32_t x = key[i];
-      const uint32_t v = x - kmin;
-      if (x != 0u && (v & mask) == prefix) {
-        const uint32_t d = (v >> shift) & dmask;
-        atomicAdd(&H[d + 4 * (d >> 5)], 1u);
+      for (int i = 0; i < KPT; ++i) {
+        const uint32_t x = key[i];
+        const uint32_t v = x - kmin;
+        if (x != 0u && (v & mask) == prefix) {
+          const uint32_t d = (v >> shift) & dmask;
+          const uint32_t hot = __builtin_amdgcn_readfirstlane(d);
+          const uint64_t same = __ballot(d == hot);
+          if (d != hot) {
+            atomicAdd(&H[d + 4 * (d >> 5)], 1u);
+          } else if (lane == __builtin_ctzll(same)) {
+            atomicAdd(&H[hot + 4 * (hot >> 5)], (uint32_t)__popcll(same));
+          }
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < KPT; ++i) {
+        const uint32_t x = key[i];
+        const uint32_t v = x - kmin;
+        if (x != 0u && (v & mask) == prefix) {
+          const uint32_t d = (v >> shift) & dmask;
+          atomicAdd(&H[d + 4 * (d >> 5)], 1u);
+        }
       }
     }
     __syncthreads();
