@@ -293,18 +293,27 @@ __global__ __launch_bounds__(kMergeThreads) void index_merge_kernel(MergeArgs a)
     block_emit<kMergeThreads, KPT>(kr, sr, scratch, [&](int i, uint32_t pos) { out[pos] = id[i]; });
     for (int p = (int)sr.count + tid; p < a.topk; p += kMergeThreads) out[p] = -1;
   } else {
+    // The newest visible block ranks first (its maximum counts as +inf) and has the
+    // largest id, so it is the last entry of the ascending pool; the other
+    // pool_blocks - 1 slots are the best of the older blocks.
     const int cb = a.cand_block;
     const int nb = (n_vis + cb - 1) / cb;
     const uint32_t* bm = a.block_max + (int64_t)b * a.max_blocks;
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
       const int v = p0 + i;
-      kr[i] = v < nb ? (v == nb - 1 ? 0xffffffffu : bm[v]) : 0u;   // newest visible block: +inf
+      kr[i] = v < nb - 1 ? bm[v] : 0u;
     }
-    const SelectResult sr = block_select<kMergeThreads, KPT>(kr, a.pool_blocks, hist, scratch);
     int32_t* out = a.pool + (int64_t)b * a.pool_blocks;
-    block_emit<kMergeThreads, KPT>(kr, sr, scratch, [&](int i, uint32_t pos) { out[pos] = p0 + i; });
-    for (int p = (int)sr.count + tid; p < a.pool_blocks; p += kMergeThreads) out[p] = -1;
+    uint32_t n_old = 0;
+    if (nb > 1 && a.pool_blocks > 1) {                                // uniform over the block
+      const SelectResult sr = block_select<kMergeThreads, KPT>(kr, a.pool_blocks - 1, hist, scratch);
+      block_emit<kMergeThreads, KPT>(kr, sr, scratch, [&](int i, uint32_t pos) { out[pos] = p0 + i; });
+      n_old = sr.count;
+    }
+    const int n_out = nb > 0 ? (int)n_old + 1 : 0;
+    if (tid == 0 && nb > 0) out[n_old] = nb - 1;
+    for (int p = n_out + tid; p < a.pool_blocks; p += kMergeThreads) out[p] = -1;
   }
 }
 

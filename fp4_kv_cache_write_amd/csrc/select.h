@@ -16,7 +16,8 @@
 
 namespace csa2 {
 
-// LDS the select needs: two histogram buffers + scratch [64 + 8].  A buffer holds
+// LDS the select needs: two histogram buffers + scratch [64 + 8] (per-wave values,
+// then the search results and the count of keys tied at the top).  A buffer holds
 // 2048 bins with four pad words after every 32 (bin d lives at d + 4*(d/32)): the
 // search wave's lane l reads bins 32l..32l+31 as eight aligned 16-byte loads, and
 // any 8 consecutive lanes of such a load cover the 32 banks once.
@@ -82,6 +83,7 @@ __device__ SelectResult block_select(const uint32_t (&key)[KPT], int K, uint32_t
     scratch[wid] = kl;
     scratch[32 + wid] = kh;
   }
+  if (tid == 0) res[4] = 0u;                                      // keys equal to the largest key
   for (int i = tid; i < kSelectHist; i += NT) hist[i] = 0u;
   __syncthreads();
   uint32_t kmin = 0xffffffffu, kmax = 0u;
@@ -100,35 +102,38 @@ __device__ SelectResult block_select(const uint32_t (&key)[KPT], int K, uint32_t
     const int shift = left - width;
     const uint32_t dmask = (1u << width) - 1u;
     uint32_t* H = hist + (pass & 1) * kHistStride;
-    // Tied scores (e.g. the exact zeros ReLU produces) put many keys on one digit,
-    // and 64 same-address LDS atomics in one instruction serialise.  A wave whose
-    // first key slot shows 16 or more lanes on one digit therefore counts, per slot,
-    // the lanes that share the first active lane's digit with a single atomic; other
-    // waves add every key on its own.
+    // Many keys tied at the largest key (a sequence whose indexer weights are all
+    // negative scores every entry <= 0, and the entries whose head dots are all <= 0
+    // tie at exactly 0) put one digit on most lanes, and 64 same-address LDS atomics
+    // in one instruction serialise.  A wave whose first key slot has 16 or more lanes
+    // on the largest key's digit counts that digit with one atomic per slot; every
+    // other key (and every key of other waves) is added on its own.
+    const uint32_t vmax = kmax - kmin;
+    const bool top_in = (vmax & mask) == prefix;
+    const uint32_t hotd = (vmax >> shift) & dmask;
     bool agg;
     {
       const uint32_t x = key[0];
       const bool in = x != 0u && ((x - kmin) & mask) == prefix;
-      const uint32_t d = ((x - kmin) >> shift) & dmask;
-      const uint64_t vm = __ballot(in);
-      const uint32_t hot = __builtin_amdgcn_readlane(d, vm ? __builtin_ctzll(vm) : 0);
-      agg = __popcll(__ballot(in && d == hot)) >= 16;
+      agg = top_in && __popcll(__ballot(in && (((x - kmin) >> shift) & dmask) == hotd)) >= 16;
+    }
+    if (pass == 0) {
+      // keys equal to kmax: if there are K of them, they alone are the top K
+      uint32_t ctop = 0;
+#pragma unroll
+      for (int i = 0; i < KPT; ++i) ctop += (uint32_t)__popcll(__ballot(key[i] == kmax));
+      if (lane == 0 && ctop != 0u) atomicAdd(&res[4], ctop);
     }
     if (agg) {
 #pragma unroll
       for (int i = 0; i < KPT; ++i) {
         const uint32_t x = key[i];
         const uint32_t v = x - kmin;
-        if (x != 0u && (v & mask) == prefix) {
-          const uint32_t d = (v >> shift) & dmask;
-          const uint32_t hot = __builtin_amdgcn_readfirstlane(d);
-          const uint64_t same = __ballot(d == hot);
-          if (d != hot) {
-            atomicAdd(&H[d + 4 * (d >> 5)], 1u);
-          } else if (lane == __builtin_ctzll(same)) {
-            atomicAdd(&H[hot + 4 * (hot >> 5)], (uint32_t)__popcll(same));
-          }
-        }
+        const bool in = x != 0u && (v & mask) == prefix;
+        const uint32_t d = (v >> shift) & dmask;
+        const uint64_t same = __ballot(in && d == hotd);
+        if (in && d != hotd) atomicAdd(&H[d + 4 * (d >> 5)], 1u);
+        if (same != 0ull && lane == __builtin_ctzll(same)) atomicAdd(&H[hotd + 4 * (hotd >> 5)], (uint32_t)__popcll(same));
       }
     } else {
 #pragma unroll
@@ -178,6 +183,7 @@ __device__ SelectResult block_select(const uint32_t (&key)[KPT], int K, uint32_t
     }
     __syncthreads();
     if (pass == 0 && res[3] <= (uint32_t)K) return SelectResult{0u, 0u, res[3]};   // take every valid key
+    if (pass == 0 && res[4] >= (uint32_t)K) return SelectResult{kmax, (uint32_t)K, (uint32_t)K};   // K tied at the top
     const uint32_t d = res[0], knew = res[1], in_bin = res[2];
     const uint32_t lo = prefix | (d << shift);                  // smallest v of the bin
     if (knew == in_bin) return SelectResult{kmin + lo - 1u, 0u, (uint32_t)K};   // the whole bin is in
