@@ -386,6 +386,7 @@ struct ReindexArgs {
   int pool_blocks, cand_block, topk;
   int32_t* topk_idx;
   int vshift;            // token count -> visible entries: >> vshift
+  int cb_shift;          // log2(cand_block): slot v lies in pool block v >> cb_shift
 };
 
 // One workgroup per sequence: score the pool's entries (slot v = p*cb + i is entry
@@ -416,8 +417,8 @@ __global__ __launch_bounds__(kReindexThreads) void reindex_kernel(ReindexArgs a)
   // Resolve every pool slot to its cache row (or -1) first, into the key array.
   int32_t* rowid = reinterpret_cast<int32_t*>(keys);
   for (int v = threadIdx.x; v < N; v += kReindexThreads) {
-    const int blk = pool[v / cb];
-    const int64_t e = (int64_t)blk * cb + (v % cb);
+    const int blk = pool[v >> a.cb_shift];
+    const int64_t e = (int64_t)blk * cb + (v & (cb - 1));
     int32_t rid = -1;
     if (blk >= 0 && e < n_vis) {
       const int page = page_of(a.block_table, a.max_pages, a.n_pages, b, (int)e);
@@ -476,7 +477,7 @@ __global__ __launch_bounds__(kReindexThreads) void reindex_kernel(ReindexArgs a)
   int32_t* out = a.topk_idx + (int64_t)b * a.topk;
   block_emit<kReindexThreads, KPT>(kr, sr, scratch, [&](int i, uint32_t pos) {
     const int v = p0 + i;
-    out[pos] = pool[v / cb] * cb + (v % cb);
+    out[pos] = pool[v >> a.cb_shift] * cb + (v & (cb - 1));
   });
   for (int p = (int)sr.count + threadIdx.x; p < a.topk; p += kReindexThreads) out[p] = -1;
 }
@@ -518,7 +519,7 @@ __global__ __launch_bounds__(256) void reindex_score_kernel(ReindexArgs a, uint3
 #pragma unroll
   for (int u = 0; u < kGroups; ++u) {
     const int v = v0 + (wid * kGroups + u) * 16 + n;
-    const int bv = pool[v < N ? v / cb : 0];
+    const int bv = pool[v < N ? v >> a.cb_shift : 0];
     blk[u] = v < N ? bv : -1;
   }
   int pg[kGroups];
@@ -526,7 +527,7 @@ __global__ __launch_bounds__(256) void reindex_score_kernel(ReindexArgs a, uint3
 #pragma unroll
   for (int u = 0; u < kGroups; ++u) {
     const int v = v0 + (wid * kGroups + u) * 16 + n;
-    ent[u] = (int64_t)blk[u] * cb + (v % cb);
+    ent[u] = (int64_t)blk[u] * cb + (v & (cb - 1));
     const bool ok = blk[u] >= 0 && ent[u] < n_vis && (ent[u] >> 6) < a.max_pages;
     const int p = bt[ok ? (int)(ent[u] >> 6) : 0];
     pg[u] = (ok && p >= 0 && p < a.n_pages) ? p : -1;
@@ -562,8 +563,8 @@ __global__ __launch_bounds__(kReSelThreads) void reindex_select_kernel(ReindexAr
   const int32_t* pool = a.pool + (int64_t)b * a.pool_blocks;
   // this thread's slots p0..p0+KPT-1 span at most two pool blocks (KPT <= 2 * cb or
   // the ids are re-read): fetch them before the select
-  const int blo = p0 < N ? pool[p0 / cb] : -1;
-  const int bhi = p0 + KPT - 1 < N ? pool[(p0 + KPT - 1) / cb] : -1;
+  const int blo = p0 < N ? pool[p0 >> a.cb_shift] : -1;
+  const int bhi = p0 + KPT - 1 < N ? pool[(p0 + KPT - 1) >> a.cb_shift] : -1;
   const uint32_t* kin = keys_ws + (int64_t)b * kReindexCap;
   uint32_t kr[KPT];
 #pragma unroll
@@ -579,9 +580,9 @@ __global__ __launch_bounds__(kReSelThreads) void reindex_select_kernel(ReindexAr
   int32_t* out = a.topk_idx + (int64_t)b * a.topk;
   block_emit<kReSelThreads, KPT>(kr, sr, scratch, [&](int i, uint32_t pos) {
     const int v = p0 + i;
-    const int bi = v / cb;
-    const int blk = bi == p0 / cb ? blo : (bi == (p0 + KPT - 1) / cb ? bhi : pool[bi]);
-    out[pos] = blk * cb + (v % cb);
+    const int bi = v >> a.cb_shift;
+    const int blk = bi == (p0 >> a.cb_shift) ? blo : (bi == ((p0 + KPT - 1) >> a.cb_shift) ? bhi : pool[bi]);
+    out[pos] = blk * cb + (v & (cb - 1));
   });
   for (int p = (int)sr.count + tid; p < a.topk; p += kReSelThreads) out[p] = -1;
 }
@@ -768,6 +769,7 @@ int launch_reindex(const csa2_cache_t& c, int B, const int32_t* ctx_len, const u
   ra.topk = topk;
   ra.topk_idx = topk_idx;
   ra.vshift = vis_shift(c);
+  ra.cb_shift = __builtin_ctz((unsigned)cand_block);   // cand_block: a power of two (checked at the boundary)
   const int N = pool_blocks * cand_block;
   if (ws && ws_bytes >= reindex_ws(B)) {
     uint32_t* keys = static_cast<uint32_t*>(ws);
