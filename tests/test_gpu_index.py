@@ -164,3 +164,74 @@ def test_tied_scores_resolve_to_lowest_entries(fk, kind):
         assert np.array_equal(tk2[b][tk2[b] >= 0], t2), f"seq {b}: Reindex"
         if kind == "all_equal" and n_vis > topk:
             assert np.array_equal(t, np.arange(topk))
+
+
+def _lowest_index_rule(sel, zero, amb, what):
+    """sel: selected ids; zero: ids tied at score 0 (the top); amb: ids whose sign of some
+    head dot is within rounding of 0, so either side may count them as tied or not.
+    Selected ids outside amb must be tied, and no unselected tie below the largest
+    selected id may be skipped (the lower index wins among equal scores)."""
+    sel = set(int(x) for x in sel)
+    assert not (sel - amb) - zero, f"{what}: an id below the tied top was selected"
+    top = max(sel)
+    skipped = [j for j in zero - amb if j < top and j not in sel]
+    assert not skipped, f"{what}: tied ids skipped for higher ones: {skipped[:5]}"
+
+
+def test_all_negative_head_weights_tie_at_zero(fk):
+    # All four indexer head weights negative: every score is <= 0, and the entries whose
+    # four head dots are all <= 0 (1 in 16) score exactly -0, the largest value.  Those
+    # ties fill the top-K and the pool; the lowest entries and blocks must win, in Full,
+    # in the HSI pool and in Reindex (tied pool entries under the second layer's weights).
+    ctx = (40000, 65536, 3000)
+    cfg = small_decode(1, B=len(ctx), ctx=ctx, pages="random", heavy_frac=0.05, append=0, seed=1209)
+    case = make_decode_case(cfg, "cpu")
+    oc = oracle_cache_for(case)
+    gc = gpu_cache_for(case)
+    L0, L1 = case.layer(0), case.layer(1)
+    w0, w1 = -L0["w_idx"].abs(), -L1["w_idx"].abs()
+    ctx_len = torch.tensor(case.ctx_len, dtype=torch.int32, device="cuda")
+    topk, P, cb = 512, 300, 8
+    tk, pool = fk.index_full(gc, ctx_len, max(case.ctx_len), L0["q_idx"].cuda(), w0.cuda(), topk=topk,
+                             pool_blocks=P, cand_block=cb)
+    tk2 = fk.reindex(gc, ctx_len, L1["q_idx"].cuda(), w1.cuda(), pool, topk=topk, cand_block=cb)
+    torch.cuda.synchronize()
+    tk, pool, tk2 = tk.cpu().numpy(), pool.cpu().numpy(), tk2.cpu().numpy()
+
+    def ties(q, w, keys):
+        s = index_scores(bits(q), bits(w), keys)
+        dots = keys @ q.double().numpy().T                       # [n, 4] exact head dots
+        amb = (np.abs(dots).min(axis=1) < 1e-5) | ((s < 0) & (s > -1e-5))
+        return s, s == 0, amb
+
+    n_tied_top = []
+    for b in range(case.B):
+        n_vis = case.n_vis[b]
+        keys = oc.index_keys(b, np.arange(n_vis))
+        s, z, amb = ties(L0["q_idx"][b], w0[b], keys)
+        assert s.max() <= 0
+        check_topk_set(tk[b], np.arange(n_vis), s, topk)
+        sel = tk[b][tk[b] >= 0]
+        if z.sum() >= topk:
+            n_tied_top.append(b)
+            _lowest_index_rule(sel, set(np.flatnonzero(z).tolist()), set(np.flatnonzero(amb).tolist()),
+                               f"seq {b} top-K")
+        # pool: the newest block last, older blocks by block maximum, lowest block first among ties
+        _check_pool(pool[b], s, n_vis, cb, P)
+        pv = pool[b][pool[b] >= 0]
+        nb = (n_vis + cb - 1) // cb
+        assert pv[-1] == nb - 1
+        pad = (-n_vis) % cb
+        zb = np.concatenate([z, np.zeros(pad, bool)]).reshape(-1, cb).any(axis=1)[:nb - 1]
+        ab = np.concatenate([amb, np.zeros(pad, bool)]).reshape(-1, cb).any(axis=1)[:nb - 1]
+        if len(pv) > 1 and zb.sum() >= len(pv) - 1:
+            _lowest_index_rule(pv[:-1], set(np.flatnonzero(zb).tolist()), set(np.flatnonzero(ab).tolist()),
+                               f"seq {b} pool")
+        # Reindex over the GPU's pool with the second layer's (negative) weights
+        pos = pool_positions(pv, n_vis, cb)
+        s2, z2, amb2 = ties(L1["q_idx"][b], w1[b], oc.index_keys(b, pos))
+        check_topk_set(tk2[b], pos, s2, topk)
+        if z2.sum() >= topk:
+            _lowest_index_rule(tk2[b][tk2[b] >= 0], set(pos[z2].tolist()), set(pos[amb2].tolist()),
+                               f"seq {b} Reindex")
+    assert n_tied_top, "no sequence had K entries tied at the top"
