@@ -11,9 +11,11 @@ path) before the Full layer reads it.  Inputs are seeded synthetic data already
 resident in HBM; timed steps rotate over cache replicas so the 256 MB Infinity
 Cache cannot serve a step from the previous one.  Steps are replayed as HIP graphs.
 
-The same JSON line carries, under "secondary", the 1M-token decode (8 sequences,
-Full scan + attention) and the chunked prefill (4 x 4,096 queries against 131,072
-prior tokens) measured the same way.  `--workload` runs one of them alone instead.
+The same JSON line carries, under "secondary", the single 2K-token query, the 1M-token
+decode (8 sequences, Full scan + attention), the chunked prefill (4 x 4,096 queries
+against 131,072 prior tokens), the mixed serving batch (128 sequences of 1K-256K
+tokens with a 64-token append), the decoder's ratio-1 cache and its 20-layer schedule,
+measured the same way.  `--workload` runs one of them alone instead.
 
 Prints one JSON line.
 """
@@ -48,8 +50,8 @@ def parse():
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--replicas", type=int, default=8)
-    p.add_argument("--workload", choices=("c1", "c2", "c3", "c4", "c5"), default="c1",
-                   help="c1 = headline decode line (+ secondary c2, c3); others alone")
+    p.add_argument("--workload", choices=("c0", "c1", "c2", "c3", "c4", "c5"), default="c1",
+                   help="c1 = headline decode line (+ secondary c0, c2, c3, c4, c5); others alone")
     p.add_argument("--no-secondary", action="store_true")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seqs", type=int, default=2, help="sequences in the oracle's timed sample")
@@ -460,32 +462,32 @@ def main() -> int:
                               config={"workload": r["workload"]})), flush=True)
         return 0
 
-    cfg_id = {"c1": 1, "c2": 2, "c4": 4, "c5": 5}[args.workload]
+    cfg_id = {"c0": 0, "c1": 1, "c2": 2, "c4": 4, "c5": 5}[args.workload]
     d = bench_decode(fk, cfg_id, args.steps, args.warmup, args.replicas, not args.no_graph, True, args.overlap_layers)
     case = d["case"]
     cfg = case.cfg
     secondary = {}
     if args.workload == "c1" and not args.no_secondary:
-        c2 = bench_decode(fk, 2, max(20, args.steps // 4), max(5, args.warmup // 4), 4, not args.no_graph, True,
-                          args.overlap_layers)
-        secondary["c2_b8_ctx1m"] = {
-            "workload": c2["case"].cfg.name, "value": round(c2["qps"], 1), "unit": "queries/s",
-            "ms_per_step": round(c2["ms"], 5), "achieved_gbs": round(c2["gbs"], 1),
-            "frac_hbm_peak": round(c2["gbs"] / HBM_PEAK_GBS, 4), "algorithmic_bytes_per_step": c2["step_bytes"],
-            "per_call_us": {n: round(v * 1e3, 2) for n, v in c2["per_call"].items()}, "roofline": c2["roofline"]}
-        del c2
-        torch.cuda.empty_cache()
+        def decode_line(cid, n_rep):
+            r = bench_decode(fk, cid, max(20, args.steps // 4), max(5, args.warmup // 4), n_rep, not args.no_graph,
+                             True, args.overlap_layers)
+            out = {"workload": r["case"].cfg.name, "value": round(r["qps"], 1), "unit": "queries/s",
+                   "ms_per_step": round(r["ms"], 5), "achieved_gbs": round(r["gbs"], 1),
+                   "frac_hbm_peak": round(r["gbs"] / HBM_PEAK_GBS, 4), "algorithmic_bytes_per_step": r["step_bytes"],
+                   "per_call_us": {n: round(v * 1e3, 2) for n, v in r["per_call"].items()}, "roofline": r["roofline"]}
+            del r
+            torch.cuda.empty_cache()
+            return out
+
+        # a single 2K-token query: launch-latency bound, reported for completeness
+        secondary["c0_b1_ctx2k"] = decode_line(0, 8)
+        secondary["c2_b8_ctx1m"] = decode_line(2, 4)
         secondary["c3_prefill"] = bench_prefill(fk, 5, 2)
         torch.cuda.empty_cache()
+        # mixed serving batch: 128 sequences of log-uniform length, 64-token append per step
+        secondary["c4_b128_mixed"] = decode_line(4, 2)
         # the decoder's ratio-1 cache with the 2048-block HSI pool
-        c5 = bench_decode(fk, 5, max(20, args.steps // 4), max(5, args.warmup // 4), 4, not args.no_graph, True,
-                          args.overlap_layers)
-        secondary["c5_decoder_ratio1"] = {
-            "workload": c5["case"].cfg.name, "value": round(c5["qps"], 1), "unit": "queries/s",
-            "ms_per_step": round(c5["ms"], 5), "achieved_gbs": round(c5["gbs"], 1),
-            "frac_hbm_peak": round(c5["gbs"] / HBM_PEAK_GBS, 4), "algorithmic_bytes_per_step": c5["step_bytes"],
-            "per_call_us": {n: round(v * 1e3, 2) for n, v in c5["per_call"].items()}, "roofline": c5["roofline"]}
-        del c5
+        secondary["c5_decoder_ratio1"] = decode_line(5, 4)
         torch.cuda.empty_cache()
         # the pages' whole decoder schedule (20 layers) at that size, through the native runner
         from synth.configs import DECODER_SCHEDULE
