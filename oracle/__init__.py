@@ -21,6 +21,7 @@ against closed forms, brute force, invariants or numbers the pages print.
 from .fp4 import (E2M1_VALUES, bf16_bits_to_f64, f64_to_bf16_bits, e2m1_decode, e8m0_decode,
                   quantise_blocks, dequantise_blocks, pack_nibbles, unpack_nibbles)
 from .merge import merge_pair_f32
+from .project import project_key_f32
 from .cache import OracleCache, BYTES_LATENT, BYTES_INDEX, BYTES_PER_ENTRY
 from .indexer import (index_scores, topk_select, hsi_pool, full_layer, reindex_layer)
 from .attention import sparse_attention, gather_rows
@@ -29,6 +30,7 @@ from .schedule import run_decode, run_prefill
 __all__ = [
     "E2M1_VALUES", "bf16_bits_to_f64", "f64_to_bf16_bits", "e2m1_decode", "e8m0_decode",
     "quantise_blocks", "dequantise_blocks", "pack_nibbles", "unpack_nibbles", "merge_pair_f32",
+    "project_key_f32",
     "OracleCache", "BYTES_LATENT", "BYTES_INDEX", "BYTES_PER_ENTRY", "index_scores", "topk_select",
     "hsi_pool", "full_layer", "reindex_layer", "sparse_attention", "gather_rows", "run_decode",
     "run_prefill",

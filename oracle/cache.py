@@ -21,6 +21,7 @@ import numpy as np
 
 from .fp4 import (bf16_bits_to_f64, dequantise_blocks, pack_nibbles, quantise_blocks, unpack_nibbles)
 from .merge import merge_pair_f32
+from .project import project_key_f32
 
 PAGE = 64
 D_LATENT = 512
@@ -92,6 +93,33 @@ class OracleCache:
                 self.lat_codes[pg, sl] = pack_nibbles(lc)
                 self.lat_scales[pg, sl] = lu
             ic, iu = quantise_blocks(bf16_bits_to_f64(k[i0:i1]))
+            self.idx_codes[pg, sl] = pack_nibbles(ic)
+            self.idx_scales[pg, sl] = iu
+
+    def write_projected(self, b: int, start_tok: int, x_bits, w_bits, p_bits, chunk: int = 1024) -> None:
+        """Store the entries of tokens start_tok .. start_tok+T-1 with indexer keys projected
+        from the entries themselves (project.py) by the bf16 weights p_bits [64][512]
+        instead of keys supplied per entry.  Ratio 2: x_bits, w_bits [T, 512], T and
+        start_tok even; ratio 1: x_bits [T, 512], w_bits unused."""
+        x = np.asarray(x_bits)
+        p = bf16_bits_to_f64(np.asarray(p_bits))
+        r = self.ratio
+        T = x.shape[0]
+        assert T % r == 0 and start_tok % r == 0
+        n = T // r
+        for i0 in range(0, n, chunk):
+            i1 = min(n, i0 + chunk)
+            pg, sl = self.slots(b, np.arange(start_tok // r + i0, start_tok // r + i1))
+            if r == 2:
+                xs = bf16_bits_to_f64(x[2 * i0: 2 * i1])
+                ws = bf16_bits_to_f64(np.asarray(w_bits)[2 * i0: 2 * i1])
+                y = merge_pair_f32(xs[0::2], xs[1::2], ws[0::2], ws[1::2])
+            else:
+                y = bf16_bits_to_f64(x[i0:i1]).astype(np.float32)
+            lc, lu = quantise_blocks(y.astype(np.float64))
+            self.lat_codes[pg, sl] = pack_nibbles(lc)
+            self.lat_scales[pg, sl] = lu
+            ic, iu = quantise_blocks(project_key_f32(y, p).astype(np.float64))
             self.idx_codes[pg, sl] = pack_nibbles(ic)
             self.idx_scales[pg, sl] = iu
 
