@@ -420,6 +420,32 @@ def bench_prefill(fk, steps: int, warmup: int):
         t_a += e[1].elapsed_time(e[2])
     ms_w, ms_a = t_w / steps, t_a / steps
     ms = ms_w + ms_a
+
+    # The same chunk written with its indexer keys projected from the entries by a
+    # seeded bf16 [64][512] weight matrix (csa2_write_kv_proj), timed on its own.
+    gen = torch.Generator().manual_seed(cfg.seed + 77)
+    w_proj = (torch.randn((64, 512), generator=gen) / 512 ** 0.5).to(torch.bfloat16).to(dev)
+
+    def write_proj():
+        fk.write_kv_proj(gc, start, ch["x"], ch["w"], w_proj)
+
+    for _ in range(3):
+        write_proj()
+    torch.cuda.synchronize()
+    e[0].record()
+    for _ in range(steps):
+        write_proj()
+    e[1].record()
+    torch.cuda.synchronize()
+    ms_wp = e[0].elapsed_time(e[1]) / steps
+    n_ent = case.B * cfg.C // 2
+    wp_bytes = n_ent * (4 * 1024 + 306) + 64 * 512 * 2       # x, w of two tokens in; entry out; weights once
+    write_proj_line = {"us": round(ms_wp * 1e3, 2), "entries": n_ent,
+                       "achieved_gbs": round(wp_bytes / (ms_wp / 1e3) / 1e9, 1),
+                       "fp64_gflops": round(n_ent * 64 * 512 * 2 / (ms_wp / 1e3) / 1e9, 1),
+                       "write_with_supplied_keys_us": round(ms_w * 1e3, 2)}
+    log(f"{cfg.name}: write with projected keys {ms_wp * 1e3:.1f} us for {n_ent} entries "
+        f"(supplied keys: {ms_w * 1e3:.1f} us)")
     nv = (cfg.prior + np.arange(cfg.C) + 1) // 2
     n_win = np.minimum(cfg.window, cfg.prior + np.arange(cfg.C) + 1)
     fl_idx = case.B * float(np.sum(nv)) * 4 * 64 * 2
@@ -433,7 +459,7 @@ def bench_prefill(fk, steps: int, warmup: int):
             "ms_index_attention": round(ms_a, 4), "flop_indexer": fl_idx, "flop_attention": fl_att,
             "roofline": {"bound": "mfma", "achieved": round(tfs, 2), "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
                          "frac": round(tfs / MFMA_BF16_PEAK_TFS, 4), "traffic": None},
-            "dtype": "bf16", "steps": steps, "warmup": warmup}
+            "write_proj": write_proj_line, "dtype": "bf16", "steps": steps, "warmup": warmup}
 
 
 # ----------------------------------------------------------------------------------

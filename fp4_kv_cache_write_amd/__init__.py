@@ -6,9 +6,9 @@ PyTorch fallback.
 """
 from . import binding
 from .binding import (Csa2Error, PagedCache, Schedule, bytes_per_entry, debug_gather, index_full, lib,
-                      prefill_chunk, reindex, sparse_decode, workspace, workspace_size, write_kv,
+                      prefill_chunk, reindex, sparse_decode, workspace, workspace_size, write_kv, write_kv_proj,
                       FN_INDEX_FULL, FN_REINDEX, FN_SPARSE_DECODE, FN_PREFILL_CHUNK)
 
 __all__ = ["binding", "Csa2Error", "PagedCache", "Schedule", "bytes_per_entry", "debug_gather", "index_full", "lib",
-           "prefill_chunk", "reindex", "sparse_decode", "workspace", "workspace_size", "write_kv",
+           "prefill_chunk", "reindex", "sparse_decode", "workspace", "workspace_size", "write_kv", "write_kv_proj",
            "FN_INDEX_FULL", "FN_REINDEX", "FN_SPARSE_DECODE", "FN_PREFILL_CHUNK"]

@@ -18,7 +18,7 @@ _LIB_PATH = os.environ.get("CSA2_LIB") or os.path.join(os.path.dirname(os.path.a
 D_LATENT, D_INDEX, H_INDEX, PAGE = 512, 64, 4, 64
 FN_INDEX_FULL, FN_REINDEX, FN_SPARSE_DECODE, FN_PREFILL_CHUNK = 1, 2, 3, 4
 
-EXPORTS = ("csa2_bytes_per_entry", "csa2_strerror", "csa2_workspace_size", "csa2_write_kv",
+EXPORTS = ("csa2_bytes_per_entry", "csa2_strerror", "csa2_workspace_size", "csa2_write_kv", "csa2_write_kv_proj",
            "csa2_index_full", "csa2_reindex", "csa2_sparse_decode", "csa2_prefill_chunk",
            "csa2_debug_gather", "csa2_schedule_workspace_size", "csa2_schedule_create",
            "csa2_schedule_launch", "csa2_schedule_destroy")
@@ -65,6 +65,8 @@ def lib() -> ctypes.CDLL:
         L.csa2_workspace_size.argtypes = [I, I, I, I64, I, I, I, I]
         L.csa2_write_kv.restype = I
         L.csa2_write_kv.argtypes = [C, I, P, I, P, P, P, I, P]
+        L.csa2_write_kv_proj.restype = I
+        L.csa2_write_kv_proj.argtypes = [C, I, P, I, P, P, P, I, P]
         L.csa2_index_full.restype = I
         L.csa2_index_full.argtypes = [C, I, P, I64, P, P, I, I, I, P, P, P, SZ, P]
         L.csa2_reindex.restype = I
@@ -192,6 +194,21 @@ def write_kv(cache: PagedCache, start_tok: torch.Tensor, x: torch.Tensor, w: Opt
     _check(lib().csa2_write_kv(cache.ref, B, _ptr(start_tok), T, _ptr(x), _ptr(w), _ptr(k_idx), ratio,
                                _stream(stream)), "csa2_write_kv")
 
+
+
+def write_kv_proj(cache: PagedCache, start_tok: torch.Tensor, x: torch.Tensor, w: Optional[torch.Tensor],
+                  w_proj: torch.Tensor, ratio: Optional[int] = None, stream=None) -> None:
+    """Write tokens start_tok .. start_tok+T-1 of every sequence with each entry's indexer
+    key projected from the entry by w_proj [64][512] (bf16) inside the kernel."""
+    ratio = cache.ratio if ratio is None else ratio
+    B, T = x.shape[0], x.shape[1]
+    _bf16(x, "x", (B, T, D_LATENT))
+    if ratio == 2 or w is not None:
+        _bf16(w, "w", (B, T, D_LATENT))
+    _bf16(w_proj, "w_proj", (D_INDEX, D_LATENT))
+    _need(start_tok, torch.int32, "start_tok", (B,))
+    _check(lib().csa2_write_kv_proj(cache.ref, B, _ptr(start_tok), T, _ptr(x), _ptr(w), _ptr(w_proj), ratio,
+                                    _stream(stream)), "csa2_write_kv_proj")
 
 def index_full(cache: PagedCache, ctx_len: torch.Tensor, max_ctx: int, q_idx: torch.Tensor,
                w_idx: torch.Tensor, topk: int = 512, pool_blocks: int = 0, cand_block: int = 8,

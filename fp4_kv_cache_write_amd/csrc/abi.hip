@@ -66,6 +66,15 @@ int csa2_write_kv(const csa2_cache_t* cache, int B, const int32_t* start_tok, in
   return launch_write_kv(*cache, B, start_tok, T_new, x, w, k_idx, (hipStream_t)stream);
 }
 
+int csa2_write_kv_proj(const csa2_cache_t* cache, int B, const int32_t* start_tok, int T_new,
+                       const uint16_t* x, const uint16_t* w, const uint16_t* w_proj, int ratio, void* stream) {
+  if (!cache_ok(cache) || B <= 0 || !start_tok || !x || !w_proj) return CSA2_EINVAL;
+  if (ratio != cache_ratio(*cache)) return CSA2_EINVAL;
+  if (ratio == 2 && (!w || T_new <= 0 || (T_new & 1))) return CSA2_EINVAL;
+  if (ratio == 1 && T_new <= 0) return CSA2_EINVAL;
+  return launch_write_kv_proj(*cache, B, start_tok, T_new, x, w, w_proj, (hipStream_t)stream);
+}
+
 int csa2_index_full(const csa2_cache_t* cache, int B, const int32_t* ctx_len, int64_t max_ctx,
                     const uint16_t* q_idx, const uint16_t* w_idx, int topk, int pool_blocks,
                     int cand_block, int32_t* topk_idx, int32_t* pool, void* ws, size_t ws_bytes,

@@ -29,6 +29,10 @@ IndexFullPlan plan_index_full(int B, int64_t max_nvis, int topk, int pool_blocks
 
 int launch_write_kv(const csa2_cache_t& c, int B, const int32_t* start_tok, int T_new,
                     const uint16_t* x, const uint16_t* w, const uint16_t* k_idx, hipStream_t s);
+// The write with the indexer key projected from each entry by the bf16 weights
+// w_proj [64][512] instead of taken from the caller.
+int launch_write_kv_proj(const csa2_cache_t& c, int B, const int32_t* start_tok, int T_new,
+                         const uint16_t* x, const uint16_t* w, const uint16_t* w_proj, hipStream_t s);
 int launch_debug_gather(const csa2_cache_t& c, int B, const int32_t* idx, int n, float* out_lat,
                         float* out_idx, hipStream_t s);
 int launch_index_full(const csa2_cache_t& c, int B, const int32_t* ctx_len, int64_t max_ctx,

@@ -13,6 +13,8 @@
 // channels spans 4 adjacent lanes (max via two lane swaps), and the lane stores one
 // dword of codes, so a wave writes the entry's 256 code bytes in one coalesced
 // store.  The kernel is HBM-bound: 4 KB read and 306 B written per entry.
+#include <algorithm>
+
 #include "common.h"
 #include "internal.h"
 
@@ -49,6 +51,33 @@ __device__ __forceinline__ void mx_quant8(const float (&y)[8], uint32_t& codes, 
 __device__ __forceinline__ float lo_bf16(uint32_t d) { return __uint_as_float(d << 16); }
 __device__ __forceinline__ float hi_bf16(uint32_t d) { return __uint_as_float(d & 0xffff0000u); }
 
+// Channels 8l..8l+7 (lane l) of entry i of sequence b before quantisation: the fp32
+// merge of its two tokens (ratio 2) or the token itself (ratio 1).
+__device__ __forceinline__ void entry_latent(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, int b,
+                                             int i, int half, int ratio, int lane, float (&y)[8]) {
+  if (ratio == 2) {
+    // y = w0*x0 + w1*x1 with one rounding (w1*x1 is exact in fp32)
+    const int64_t tok0 = ((int64_t)b * 2 * half + 2 * i) * CSA2_D_LATENT + lane * 8;
+    const u32x4 xa = *reinterpret_cast<const u32x4*>(x + tok0);
+    const u32x4 xb = *reinterpret_cast<const u32x4*>(x + tok0 + CSA2_D_LATENT);
+    const u32x4 wa = *reinterpret_cast<const u32x4*>(w + tok0);
+    const u32x4 wb = *reinterpret_cast<const u32x4*>(w + tok0 + CSA2_D_LATENT);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      y[2 * q] = fmaf(lo_bf16(wa[q]), lo_bf16(xa[q]), lo_bf16(wb[q]) * lo_bf16(xb[q]));
+      y[2 * q + 1] = fmaf(hi_bf16(wa[q]), hi_bf16(xa[q]), hi_bf16(wb[q]) * hi_bf16(xb[q]));
+    }
+  } else {
+    // the token itself (bf16 is exact in fp32)
+    const u32x4 xa = *reinterpret_cast<const u32x4*>(x + ((int64_t)b * half + i) * CSA2_D_LATENT + lane * 8);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      y[2 * q] = lo_bf16(xa[q]);
+      y[2 * q + 1] = hi_bf16(xa[q]);
+    }
+  }
+}
+
 __global__ __launch_bounds__(256) void write_kv_kernel(
     uint8_t* __restrict__ lat_codes, uint8_t* __restrict__ lat_scales,
     uint8_t* __restrict__ idx_codes, uint8_t* __restrict__ idx_scales, int n_pages,
@@ -69,27 +98,7 @@ __global__ __launch_bounds__(256) void write_kv_kernel(
   const int64_t row = (int64_t)page * CSA2_PAGE + (j & (CSA2_PAGE - 1));
 
   float y[8];
-  if (ratio == 2) {
-    // ---- latent: y = w0*x0 + w1*x1 with one rounding (w1*x1 is exact in fp32) ----
-    const int64_t tok0 = ((int64_t)b * 2 * half + 2 * i) * CSA2_D_LATENT + lane * 8;
-    const u32x4 xa = *reinterpret_cast<const u32x4*>(x + tok0);
-    const u32x4 xb = *reinterpret_cast<const u32x4*>(x + tok0 + CSA2_D_LATENT);
-    const u32x4 wa = *reinterpret_cast<const u32x4*>(w + tok0);
-    const u32x4 wb = *reinterpret_cast<const u32x4*>(w + tok0 + CSA2_D_LATENT);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      y[2 * q] = fmaf(lo_bf16(wa[q]), lo_bf16(xa[q]), lo_bf16(wb[q]) * lo_bf16(xb[q]));
-      y[2 * q + 1] = fmaf(hi_bf16(wa[q]), hi_bf16(xa[q]), hi_bf16(wb[q]) * hi_bf16(xb[q]));
-    }
-  } else {
-    // ---- latent: the token itself (bf16 is exact in fp32) ----
-    const u32x4 xa = *reinterpret_cast<const u32x4*>(x + ((int64_t)b * half + i) * CSA2_D_LATENT + lane * 8);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      y[2 * q] = lo_bf16(xa[q]);
-      y[2 * q + 1] = hi_bf16(xa[q]);
-    }
-  }
+  entry_latent(x, w, b, i, half, ratio, lane, y);
   uint32_t codes, u;
   mx_quant8(y, codes, u);
   *reinterpret_cast<uint32_t*>(lat_codes + row * CSA2_LAT_CODE_BYTES + lane * 4) = codes;
@@ -113,6 +122,84 @@ __global__ __launch_bounds__(256) void write_kv_kernel(
   if (lane < 8) {
     *reinterpret_cast<uint32_t*>(idx_codes + row * CSA2_IDX_CODE_BYTES + lane * 4) = codes;
     if ((lane & 3) == 0) idx_scales[row * CSA2_IDX_SCALE_BYTES + (lane >> 2)] = (uint8_t)u;
+  }
+}
+
+
+// Write with the indexer key projected from the entry ([P1] §2.3.1: the indexer key
+// is a projection of the compressed entry; the weights are the caller's).  The key
+// is k_o = fp32(s_512), s_{d+1} = fp64(s_d + P[o][d] * y[d]) over channels d = 0..511
+// in order: a bf16 x fp32 product has at most 32 significant bits, so each fma below
+// rounds exactly where that sum does, and the bytes match a plain evaluation of it.
+//
+// The 64 KB weight matrix is staged in LDS once per workgroup, rows padded by one
+// dword so that 64 lanes reading one column of their rows spread over the banks; the
+// workgroup's four waves then take entries in a grid-stride loop.  Per entry a wave
+// merges and stores the latent as write_kv_kernel does, parks y in its LDS slot,
+// lane o runs output o's 512-step chain, and lanes 0..7 quantise the 64 outputs.
+constexpr int kProjRowWords = CSA2_D_LATENT / 2 + 1;            // bf16 pairs per padded row
+constexpr int kProjWaves = 4;
+constexpr size_t kProjLds = (size_t)CSA2_D_INDEX * kProjRowWords * 4 +
+                            (size_t)kProjWaves * (CSA2_D_LATENT + CSA2_D_INDEX) * 4;
+
+__global__ __launch_bounds__(256) void write_kv_proj_kernel(
+    uint8_t* __restrict__ lat_codes, uint8_t* __restrict__ lat_scales,
+    uint8_t* __restrict__ idx_codes, uint8_t* __restrict__ idx_scales, int n_pages,
+    const int32_t* __restrict__ block_table, int max_pages, const int32_t* __restrict__ start_tok,
+    int half, int64_t total, const uint16_t* __restrict__ x, const uint16_t* __restrict__ w,
+    const uint16_t* __restrict__ w_proj, int ratio) {
+  extern __shared__ __attribute__((aligned(16))) uint32_t plds[];
+  uint32_t* pw = plds;                                            // [64][257] bf16 pairs
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  float* ys = reinterpret_cast<float*>(plds + CSA2_D_INDEX * kProjRowWords) + wid * (CSA2_D_LATENT + CSA2_D_INDEX);
+  float* ks = ys + CSA2_D_LATENT;
+  for (int t = threadIdx.x; t < CSA2_D_INDEX * (CSA2_D_LATENT / 2); t += blockDim.x) {
+    const int o = t / (CSA2_D_LATENT / 2), c = t - o * (CSA2_D_LATENT / 2);
+    pw[o * kProjRowWords + c] = reinterpret_cast<const uint32_t*>(w_proj)[t];
+  }
+  __syncthreads();
+  const uint32_t* prow = pw + lane * kProjRowWords;
+  for (int64_t e = (int64_t)blockIdx.x * kProjWaves + wid; e < total; e += (int64_t)gridDim.x * kProjWaves) {
+    const int b = (int)(e / half);
+    const int i = (int)(e - (int64_t)b * half);
+    const int st = start_tok[b];
+    if (st < 0 || (ratio == 2 && (st & 1))) continue;             // caller contract: even start at ratio 2
+    const int j = (ratio == 2 ? (st >> 1) : st) + i;
+    const int page = page_of(block_table, max_pages, n_pages, b, j);
+    if (page < 0) continue;
+    const int64_t row = (int64_t)page * CSA2_PAGE + (j & (CSA2_PAGE - 1));
+
+    float y[8];
+    entry_latent(x, w, b, i, half, ratio, lane, y);
+    uint32_t codes, u;
+    mx_quant8(y, codes, u);
+    *reinterpret_cast<uint32_t*>(lat_codes + row * CSA2_LAT_CODE_BYTES + lane * 4) = codes;
+    if ((lane & 3) == 0) lat_scales[row * CSA2_LAT_SCALE_BYTES + (lane >> 2)] = (uint8_t)u;
+
+    *reinterpret_cast<f32x4*>(ys + lane * 8) = f32x4{y[0], y[1], y[2], y[3]};
+    *reinterpret_cast<f32x4*>(ys + lane * 8 + 4) = f32x4{y[4], y[5], y[6], y[7]};
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");            // the wave's y is in LDS
+    double s = 0.0;
+#pragma unroll 4
+    for (int d = 0; d < CSA2_D_LATENT; d += 4) {
+      const f32x4 yv = *reinterpret_cast<const f32x4*>(ys + d);  // same address in every lane
+      const uint32_t p01 = prow[d >> 1], p23 = prow[(d >> 1) + 1];
+      s = fma((double)lo_bf16(p01), (double)yv[0], s);
+      s = fma((double)hi_bf16(p01), (double)yv[1], s);
+      s = fma((double)lo_bf16(p23), (double)yv[2], s);
+      s = fma((double)hi_bf16(p23), (double)yv[3], s);
+    }
+    ks[lane] = (float)s;
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");            // all 64 outputs are in LDS
+    float kv[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) kv[q] = lane < 8 ? ks[lane * 8 + q] : 0.0f;
+    mx_quant8(kv, codes, u);
+    if (lane < 8) {
+      *reinterpret_cast<uint32_t*>(idx_codes + row * CSA2_IDX_CODE_BYTES + lane * 4) = codes;
+      if ((lane & 3) == 0) idx_scales[row * CSA2_IDX_SCALE_BYTES + (lane >> 2)] = (uint8_t)u;
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");            // y and k slots free for the next entry
   }
 }
 
@@ -179,6 +266,24 @@ int launch_write_kv(const csa2_cache_t& c, int B, const int32_t* start_tok, int 
   hipLaunchKernelGGL(write_kv_kernel, dim3((unsigned)grid), dim3(256), 0, s, c.lat_codes,
                      c.lat_scales, c.idx_codes, c.idx_scales, c.n_pages, c.block_table,
                      c.max_pages, start_tok, half, total, x, w, k_idx, ratio);
+  return hip_status();
+}
+
+int launch_write_kv_proj(const csa2_cache_t& c, int B, const int32_t* start_tok, int T_new,
+                         const uint16_t* x, const uint16_t* w, const uint16_t* w_proj, hipStream_t s) {
+  static const bool lds_ok = hipFuncSetAttribute(reinterpret_cast<const void*>(write_kv_proj_kernel),
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                 (int)kProjLds) == hipSuccess;
+  if (!lds_ok) return CSA2_EHIP;
+  const int ratio = cache_ratio(c);
+  const int half = T_new / ratio;   // entries per sequence
+  const int64_t total = (int64_t)B * half;
+  if (total == 0) return CSA2_OK;
+  // two workgroups per CU stay resident (75 KB of LDS each); at most one entry per wave
+  const int64_t grid = std::min<int64_t>((total + kProjWaves - 1) / kProjWaves, 2 * 256);
+  hipLaunchKernelGGL(write_kv_proj_kernel, dim3((unsigned)grid), dim3(64 * kProjWaves), kProjLds, s, c.lat_codes,
+                     c.lat_scales, c.idx_codes, c.idx_scales, c.n_pages, c.block_table,
+                     c.max_pages, start_tok, half, total, x, w, w_proj, ratio);
   return hip_status();
 }
 

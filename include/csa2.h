@@ -123,6 +123,22 @@ int csa2_write_kv(const csa2_cache_t *cache, int B, const int32_t *start_tok, in
                   const uint16_t *x, const uint16_t *w, const uint16_t *k_idx, int ratio,
                   void *stream);
 
+/* csa2_write_kv_proj — the write path with the indexer key projected from the entry
+ *   ([P1] §2.3.1: the indexer key is a projection of the compressed main entry).
+ *   Same arguments, layout and latent as csa2_write_kv, but instead of k_idx the
+ *   caller passes the projection weights w_proj: [64][512] bf16 (device, row o =
+ *   output channel o).  With y the entry's fp32 latent before quantisation (the
+ *   merge above at ratio 2, the token at ratio 1), key channel o is
+ *     k_o = fp32_rne(s_512),  s_0 = 0,  s_{d+1} = fp64_rne(s_d + w_proj[o][d] * y[d])
+ *   accumulated over d = 0..511 in that order (each product is exact in fp64), then
+ *   quantised like any indexer key.  The pages give no precision for the projection;
+ *   this one fixes every rounding, so the stored codes are reproducible bit for bit.
+ *   Returns CSA2_EINVAL for a null w_proj or the csa2_write_kv conditions; allocates
+ *   nothing (75 KB of LDS per workgroup). */
+int csa2_write_kv_proj(const csa2_cache_t *cache, int B, const int32_t *start_tok, int T_new,
+                       const uint16_t *x, const uint16_t *w, const uint16_t *w_proj, int ratio,
+                       void *stream);
+
 /* csa2_index_full — Full-mode indexer ([P1] §2.3.2 Full mode, §2.3.4 HSI).
  *   For every sequence b with n = floor(ctx_len[b]/ratio) visible entries:
  *     s_j = sum_{h<4} w_idx[b][h] * max(0, q_idx[b][h] . k_j)   (k_j dequantised)
