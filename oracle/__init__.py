@@ -24,6 +24,7 @@ from .merge import merge_pair_f32
 from .project import project_key_f32
 from .cache import OracleCache, BYTES_LATENT, BYTES_INDEX, BYTES_PER_ENTRY
 from .indexer import (index_scores, topk_select, hsi_pool, full_layer, reindex_layer)
+from .hisa import block_summaries, hisa_layer
 from .attention import sparse_attention, gather_rows
 from .schedule import run_decode, run_prefill
 
@@ -32,6 +33,6 @@ __all__ = [
     "quantise_blocks", "dequantise_blocks", "pack_nibbles", "unpack_nibbles", "merge_pair_f32",
     "project_key_f32",
     "OracleCache", "BYTES_LATENT", "BYTES_INDEX", "BYTES_PER_ENTRY", "index_scores", "topk_select",
-    "hsi_pool", "full_layer", "reindex_layer", "sparse_attention", "gather_rows", "run_decode",
+    "hsi_pool", "full_layer", "reindex_layer", "block_summaries", "hisa_layer", "sparse_attention", "gather_rows", "run_decode",
     "run_prefill",
 ]
