@@ -18,7 +18,7 @@ _LIB_PATH = os.environ.get("CSA2_LIB") or os.path.join(os.path.dirname(os.path.a
 D_LATENT, D_INDEX, H_INDEX, PAGE = 512, 64, 4, 64
 FN_INDEX_FULL, FN_REINDEX, FN_SPARSE_DECODE, FN_PREFILL_CHUNK = 1, 2, 3, 4
 
-EXPORTS = ("csa2_bytes_per_entry", "csa2_strerror", "csa2_workspace_size", "csa2_write_kv", "csa2_write_kv_proj",
+EXPORTS = ("csa2_bytes_per_entry", "csa2_strerror", "csa2_workspace_size", "csa2_write_kv", "csa2_write_kv_proj", "csa2_block_keys",
            "csa2_index_full", "csa2_reindex", "csa2_sparse_decode", "csa2_prefill_chunk",
            "csa2_debug_gather", "csa2_schedule_workspace_size", "csa2_schedule_create",
            "csa2_schedule_launch", "csa2_schedule_destroy")
@@ -67,6 +67,8 @@ def lib() -> ctypes.CDLL:
         L.csa2_write_kv.argtypes = [C, I, P, I, P, P, P, I, P]
         L.csa2_write_kv_proj.restype = I
         L.csa2_write_kv_proj.argtypes = [C, I, P, I, P, P, P, I, P]
+        L.csa2_block_keys.restype = I
+        L.csa2_block_keys.argtypes = [C, C, I, P, I64, I, P, I, P, P]
         L.csa2_index_full.restype = I
         L.csa2_index_full.argtypes = [C, I, P, I64, P, P, I, I, I, P, P, P, SZ, P]
         L.csa2_reindex.restype = I
@@ -209,6 +211,35 @@ def write_kv_proj(cache: PagedCache, start_tok: torch.Tensor, x: torch.Tensor, w
     _need(start_tok, torch.int32, "start_tok", (B,))
     _check(lib().csa2_write_kv_proj(cache.ref, B, _ptr(start_tok), T, _ptr(x), _ptr(w), _ptr(w_proj), ratio,
                                     _stream(stream)), "csa2_write_kv_proj")
+
+
+def block_keys(cache: PagedCache, blocks: PagedCache, ctx_len: torch.Tensor, max_ctx: int, cand_block: int = 8,
+               blk_first: Optional[torch.Tensor] = None, n_span: int = 1, n_blocks: Optional[torch.Tensor] = None,
+               stream=None) -> torch.Tensor:
+    """HISA block summaries of cache's indexer keys into `blocks` (a ratio-1 cache whose
+    slot k holds block k); all blocks, or per sequence blk_first[b] .. +n_span-1.
+    Returns the per-sequence block counts (the context to index `blocks` with)."""
+    B = ctx_len.shape[0]
+    _need(ctx_len, torch.int32, "ctx_len", (B,))
+    if blk_first is not None:
+        _need(blk_first, torch.int32, "blk_first", (B,))
+    if n_blocks is None:
+        n_blocks = torch.empty((B,), dtype=torch.int32, device=ctx_len.device)
+    _check(lib().csa2_block_keys(cache.ref, blocks.ref, B, _ptr(ctx_len), max_ctx, cand_block, _ptr(blk_first),
+                                 n_span, _ptr(n_blocks), _stream(stream)), "csa2_block_keys")
+    return n_blocks
+
+
+def index_hisa(cache: PagedCache, blocks: PagedCache, n_blocks: torch.Tensor, max_blocks: int, ctx_len: torch.Tensor,
+               q_idx: torch.Tensor, w_idx: torch.Tensor, keep_blocks: int, topk: int = 512, cand_block: int = 8,
+               ws_blocks: Optional[torch.Tensor] = None, ws_reindex: Optional[torch.Tensor] = None,
+               stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """HISA selection: the keep_blocks best block summaries (csa2_index_full on `blocks`),
+    then the top-K of their entries (csa2_reindex on `cache`).  Returns (top-K, pool)."""
+    pool, _ = index_full(blocks, n_blocks, max_blocks, q_idx, w_idx, topk=keep_blocks, pool_blocks=0,
+                         cand_block=cand_block, ws=ws_blocks, stream=stream)
+    tk = reindex(cache, ctx_len, q_idx, w_idx, pool, topk=topk, cand_block=cand_block, ws=ws_reindex, stream=stream)
+    return tk, pool
 
 def index_full(cache: PagedCache, ctx_len: torch.Tensor, max_ctx: int, q_idx: torch.Tensor,
                w_idx: torch.Tensor, topk: int = 512, pool_blocks: int = 0, cand_block: int = 8,

@@ -75,6 +75,16 @@ int csa2_write_kv_proj(const csa2_cache_t* cache, int B, const int32_t* start_to
   return launch_write_kv_proj(*cache, B, start_tok, T_new, x, w, w_proj, (hipStream_t)stream);
 }
 
+int csa2_block_keys(const csa2_cache_t* cache, const csa2_cache_t* blocks, int B, const int32_t* ctx_len,
+                    int64_t max_ctx, int cand_block, const int32_t* blk_first, int n_span, int32_t* n_blocks,
+                    void* stream) {
+  if (!cache_ok(cache) || !cache_ok(blocks) || B <= 0 || !ctx_len || max_ctx < 0) return CSA2_EINVAL;
+  if (blocks->ratio != 1 || !pow2_in(cand_block, 1, 32)) return CSA2_EINVAL;
+  if (blk_first && n_span < 1) return CSA2_EINVAL;
+  return launch_block_keys(*cache, *blocks, B, ctx_len, max_ctx, cand_block, blk_first, n_span, n_blocks,
+                           (hipStream_t)stream);
+}
+
 int csa2_index_full(const csa2_cache_t* cache, int B, const int32_t* ctx_len, int64_t max_ctx,
                     const uint16_t* q_idx, const uint16_t* w_idx, int topk, int pool_blocks,
                     int cand_block, int32_t* topk_idx, int32_t* pool, void* ws, size_t ws_bytes,

@@ -33,6 +33,12 @@ int launch_write_kv(const csa2_cache_t& c, int B, const int32_t* start_tok, int 
 // w_proj [64][512] instead of taken from the caller.
 int launch_write_kv_proj(const csa2_cache_t& c, int B, const int32_t* start_tok, int T_new,
                          const uint16_t* x, const uint16_t* w, const uint16_t* w_proj, hipStream_t s);
+// HISA block summaries of c's indexer keys into blocks' key arrays (blocks of
+// cand_block entries): per sequence, blocks blk_first[b] .. +n_span-1, or all of them
+// (n_span from max_ctx) when blk_first is null.
+int launch_block_keys(const csa2_cache_t& c, const csa2_cache_t& blocks, int B, const int32_t* ctx_len,
+                      int64_t max_ctx, int cand_block, const int32_t* blk_first, int n_span, int32_t* n_blocks_out,
+                      hipStream_t s);
 int launch_debug_gather(const csa2_cache_t& c, int B, const int32_t* idx, int n, float* out_lat,
                         float* out_idx, hipStream_t s);
 int launch_index_full(const csa2_cache_t& c, int B, const int32_t* ctx_len, int64_t max_ctx,

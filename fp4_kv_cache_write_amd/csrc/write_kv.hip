@@ -203,6 +203,70 @@ __global__ __launch_bounds__(256) void write_kv_proj_kernel(
   }
 }
 
+
+// HISA block summaries ([P1] §2.3.4, HISA): block k of a sequence covers entries
+// k*cb .. k*cb+cb-1; its summary is the mean of the dequantised indexer keys of the
+// entries that are visible and present, summed in float32 in entry order and divided
+// once by their count (zero key for an empty block), stored as an MXFP4 indexer key
+// in slot k of the block-key cache.  One wave per (sequence, block): lane l sums
+// dimension l (each e2m1 x 2^(u-127) term is exact in float32); the 64 means are
+// regrouped through LDS so that lanes 0..7 quantise 8 each, as for any key.
+__device__ __forceinline__ float e2m1_times_scale(uint32_t c, uint32_t u) {
+  const uint32_t eb = (c >> 1) & 3u, mb = c & 1u;
+  const float mag = eb == 0u ? 0.5f * (float)mb : ldexpf(1.0f + 0.5f * (float)mb, (int)eb - 1);
+  const float v = ldexpf(mag, (int)u - 127);                     // exact: at most 2 significant bits
+  return (c & 8u) ? -v : v;
+}
+
+__global__ __launch_bounds__(256) void block_keys_kernel(
+    const uint8_t* __restrict__ idx_codes, const uint8_t* __restrict__ idx_scales, int n_pages,
+    const int32_t* __restrict__ block_table, int max_pages, const int32_t* __restrict__ ctx_len, int64_t max_ctx,
+    int vshift, int cb_shift, const int32_t* __restrict__ blk_first, int n_span, int B,
+    uint8_t* __restrict__ bk_codes, uint8_t* __restrict__ bk_scales, int bk_n_pages,
+    const int32_t* __restrict__ bk_table, int bk_max_pages, int32_t* __restrict__ n_blocks_out) {
+  __shared__ float means[4][CSA2_D_INDEX];
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int64_t wv = (int64_t)blockIdx.x * 4 + wid;
+  if (wv >= (int64_t)B * n_span) return;                         // whole wave
+  const int b = (int)(wv / n_span);
+  const int r = (int)(wv - (int64_t)b * n_span);
+  int64_t L = ctx_len[b];
+  L = L < 0 ? 0 : (L > max_ctx ? max_ctx : L);
+  const int n_vis = (int)(L >> vshift);
+  const int cb = 1 << cb_shift;
+  const int nb = (n_vis + cb - 1) >> cb_shift;
+  if (r == 0 && n_blocks_out && lane == 0) n_blocks_out[b] = nb;
+  const int first = blk_first ? max(blk_first[b], 0) : 0;
+  const int k = first + r;
+  if (k >= nb) return;
+  const int j0 = k << cb_shift;
+  const int page = page_of(block_table, max_pages, n_pages, b, j0);   // cb divides 64: one page per block
+  float sum = 0.0f;
+  int cnt = 0;
+  if (page >= 0) {
+    for (int i = 0; i < cb && j0 + i < n_vis; ++i) {
+      const int64_t row = (int64_t)page * CSA2_PAGE + ((j0 + i) & (CSA2_PAGE - 1));
+      const uint32_t byte = idx_codes[row * CSA2_IDX_CODE_BYTES + (lane >> 1)];
+      const uint32_t u = idx_scales[row * CSA2_IDX_SCALE_BYTES + (lane >> 5)];
+      sum += e2m1_times_scale((byte >> (4 * (lane & 1))) & 15u, u);
+      ++cnt;
+    }
+  }
+  means[wid][lane] = cnt > 0 ? __fdiv_rn(sum, (float)cnt) : 0.0f;
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");            // the wave's 64 means are in LDS
+  float kv[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) kv[q] = lane < 8 ? means[wid][lane * 8 + q] : 0.0f;
+  uint32_t codes, u;
+  mx_quant8(kv, codes, u);
+  const int bpage = page_of(bk_table, bk_max_pages, bk_n_pages, b, k);
+  if (lane < 8 && bpage >= 0) {
+    const int64_t brow = (int64_t)bpage * CSA2_PAGE + (k & (CSA2_PAGE - 1));
+    *reinterpret_cast<uint32_t*>(bk_codes + brow * CSA2_IDX_CODE_BYTES + lane * 4) = codes;
+    if ((lane & 3) == 0) bk_scales[brow * CSA2_IDX_SCALE_BYTES + (lane >> 2)] = (uint8_t)u;
+  }
+}
+
 // Dequantise entries through the page table with the kernels' own FP4 decode.
 __global__ __launch_bounds__(256) void debug_gather_kernel(
     const uint8_t* __restrict__ lat_codes, const uint8_t* __restrict__ lat_scales,
@@ -284,6 +348,22 @@ int launch_write_kv_proj(const csa2_cache_t& c, int B, const int32_t* start_tok,
   hipLaunchKernelGGL(write_kv_proj_kernel, dim3((unsigned)grid), dim3(64 * kProjWaves), kProjLds, s, c.lat_codes,
                      c.lat_scales, c.idx_codes, c.idx_scales, c.n_pages, c.block_table,
                      c.max_pages, start_tok, half, total, x, w, w_proj, ratio);
+  return hip_status();
+}
+
+int launch_block_keys(const csa2_cache_t& c, const csa2_cache_t& blocks, int B, const int32_t* ctx_len,
+                      int64_t max_ctx, int cand_block, const int32_t* blk_first, int n_span, int32_t* n_blocks_out,
+                      hipStream_t s) {
+  const int cb_shift = __builtin_ctz((unsigned)cand_block);
+  if (blk_first == nullptr) n_span = (int)(((max_ctx >> vis_shift(c)) + cand_block - 1) >> cb_shift);
+  const int64_t waves = (int64_t)B * n_span;
+  if (waves == 0) return CSA2_OK;
+  const int64_t grid = (waves + 3) / 4;
+  if (grid > 0x7fffffff) return CSA2_EUNSUPPORTED;
+  hipLaunchKernelGGL(block_keys_kernel, dim3((unsigned)grid), dim3(256), 0, s, c.idx_codes, c.idx_scales, c.n_pages,
+                     c.block_table, c.max_pages, ctx_len, max_ctx, vis_shift(c), cb_shift, blk_first, n_span, B,
+                     blocks.idx_codes, blocks.idx_scales, blocks.n_pages, blocks.block_table, blocks.max_pages,
+                     n_blocks_out);
   return hip_status();
 }
 

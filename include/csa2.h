@@ -139,6 +139,28 @@ int csa2_write_kv_proj(const csa2_cache_t *cache, int B, const int32_t *start_to
                        const uint16_t *x, const uint16_t *w, const uint16_t *w_proj, int ratio,
                        void *stream);
 
+/* csa2_block_keys — HISA block summaries ([P1] §2.3.4, the HISA scheme it builds on:
+ *   each block of positions keeps the mean of its indexer keys; during decoding only
+ *   the current block changes).  Block k of sequence b covers entries k*cand_block ..
+ *   k*cand_block + cand_block - 1 of `cache`; its summary is the mean of the
+ *   dequantised keys of those entries that are visible (j < ctx_len[b] >> (ratio-1))
+ *   and present, summed in float32 in entry order and divided once by their count (the
+ *   zero key for a block with none), quantised like an indexer key and stored in slot k
+ *   of `blocks` (its idx_codes / idx_scales through its own block table, 64 blocks per
+ *   page; its latent arrays are not touched; blocks->ratio must be 1).
+ *   Blocks written: per sequence blk_first[b] .. min(blk_first[b] + n_span, nb) - 1
+ *   with nb = ceil(visible entries / cand_block) (decode: blk_first = the newest block,
+ *   n_span = 1), or every block when blk_first is NULL (n_span ignored).  n_blocks
+ *   ([B] int32, device, optional) receives nb, the context to give csa2_index_full on
+ *   `blocks`.  The HISA selection is then csa2_index_full(blocks, B, n_blocks, ...,
+ *   topk = the number of blocks to keep, pool_blocks = 0), whose ascending block ids
+ *   are the pool of csa2_reindex(cache, ..., that pool, cand_block, K).
+ *   cand_block: a power of two in [1, 32].  Returns CSA2_EINVAL for bad arguments;
+ *   allocates nothing. */
+int csa2_block_keys(const csa2_cache_t *cache, const csa2_cache_t *blocks, int B, const int32_t *ctx_len,
+                    int64_t max_ctx, int cand_block, const int32_t *blk_first, int n_span, int32_t *n_blocks,
+                    void *stream);
+
 /* csa2_index_full — Full-mode indexer ([P1] §2.3.2 Full mode, §2.3.4 HSI).
  *   For every sequence b with n = floor(ctx_len[b]/ratio) visible entries:
  *     s_j = sum_{h<4} w_idx[b][h] * max(0, q_idx[b][h] . k_j)   (k_j dequantised)

@@ -72,6 +72,8 @@ def test_host_argument_errors_return_before_launch():
     assert L.csa2_write_kv_proj(ref, 1, p, 2, p, None, p, 2, None) == EINVAL  # ratio 2 needs w
     assert L.csa2_write_kv_proj(ref, 1, p, 2, p, p, p, 1, None) == EINVAL     # ratio differs from the cache's
     assert L.csa2_write_kv_proj(None, 1, p, 2, p, p, p, 2, None) == EINVAL
+    assert L.csa2_block_keys(ref, ref, 1, p, 128, 8, None, 1, None, None) == EINVAL   # block cache not ratio 1
+    assert L.csa2_block_keys(ref, None, 1, p, 128, 8, None, 1, None, None) == EINVAL
     assert L.csa2_index_full(ref, 1, p, 128, p, p, 0, 0, 8, p, None, None, 0, None) == EINVAL  # topk 0
     assert L.csa2_index_full(ref, 1, p, 128, p, p, 4096, 0, 8, p, None, None, 0, None) == EINVAL
     assert L.csa2_index_full(ref, 1, p, 128, p, p, 16, 4, 8, p, None, None, 0, None) == EINVAL  # pool NULL
