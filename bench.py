@@ -462,6 +462,79 @@ def bench_prefill(fk, steps: int, warmup: int):
             "write_proj": write_proj_line, "dtype": "bf16", "steps": steps, "warmup": warmup}
 
 
+def bench_hisa(fk, steps: int, warmup: int, n_rep: int = 4, cfg_id: int = 1):
+    """HISA selection at a decode workload's size (blocks of 8 entries): per
+    step, the newest block's summary is refreshed (csa2_block_keys) and the 512 best
+    block summaries are expanded and re-scored to the top-512 (csa2_index_full on the
+    block cache, then csa2_reindex); timed beside the Full layer's selection with its
+    HSI pool of the same size, as HIP-graph replays over cache replicas."""
+    from synth import CONFIGS, make_decode_case
+    cfg = CONFIGS[cfg_id]
+    dev = "cuda"
+    case = make_decode_case(cfg, device=dev)
+    reps = build_decode(case, fk, n_rep)
+    B, topk, cb, keep = case.B, cfg.topk, cfg.cand_block, 512
+    ctx = torch.tensor(case.ctx_len, dtype=torch.int32, device=dev)
+    max_ctx = max(case.ctx_len)
+    nb_max = -(-(max_ctx // 2) // cb)
+    P = -(-nb_max // 64)
+    bt = torch.arange(B * P, dtype=torch.int32, device=dev).reshape(B, P)
+    blocks = [fk.PagedCache.allocate(B * P, bt, device=dev, ratio=1) for _ in reps]
+    nbs = [fk.block_keys(R.cache, bk, ctx, max_ctx, cand_block=cb) for R, bk in zip(reps, blocks)]
+    newest = torch.tensor([(L // 2 - 1) // cb for L in case.ctx_len], dtype=torch.int32, device=dev)
+    ws_b = fk.workspace(fk.FN_INDEX_FULL, device=dev, B=B, max_ctx=nb_max, topk=keep, pool_blocks=0, ratio=1)
+    ws_r = fk.workspace(fk.FN_REINDEX, device=dev, B=B, topk=topk, pool_blocks=keep, ratio=2)
+    # the Full layer's own HSI pool ranks up to 32768 blocks; past that it selects without one
+    pb = keep if -(-(max_ctx // 2) // cb) <= 32768 else 0
+    ws_f = fk.workspace(fk.FN_INDEX_FULL, device=dev, B=B, max_ctx=max_ctx, topk=topk, pool_blocks=pb, ratio=2)
+    tk = torch.empty((B, topk), dtype=torch.int32, device=dev)
+    pool = torch.empty((B, keep), dtype=torch.int32, device=dev)
+
+    def hisa(r):
+        L = reps[r].layers[0]
+        fk.block_keys(reps[r].cache, blocks[r], ctx, max_ctx, cand_block=cb, blk_first=newest, n_span=1,
+                      n_blocks=nbs[r])
+        fk.index_hisa(reps[r].cache, blocks[r], nbs[r], nb_max, ctx, L["q_idx"], L["w_idx"], keep_blocks=keep,
+                      topk=topk, cand_block=cb, ws_blocks=ws_b, ws_reindex=ws_r)
+
+    def full(r):
+        L = reps[r].layers[0]
+        fk.index_full(reps[r].cache, ctx, max_ctx, L["q_idx"], L["w_idx"], topk=topk, pool_blocks=pb,
+                      cand_block=cb, ws=ws_f, topk_idx=tk, pool=pool if pb else None)
+
+    out = {}
+    for name, f in (("hisa", hisa), ("full", full)):
+        for r in range(n_rep):
+            f(r)
+        torch.cuda.synchronize()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            for r in range(n_rep):
+                f(r)
+        torch.cuda.current_stream().wait_stream(s)
+        for _ in range(max(1, warmup)):
+            g.replay()
+        torch.cuda.synchronize()
+        a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a0.record()
+        for _ in range(steps):
+            g.replay()
+        a1.record()
+        torch.cuda.synchronize()
+        out[name] = a0.elapsed_time(a1) / (steps * n_rep) * 1e3
+    n_vis = case.n_vis
+    hisa_bytes = sum((-(-v // cb)) * BYTES_IDX + keep * cb * BYTES_IDX + 2 * 520 + 4 * topk for v in n_vis)
+    log(f"{cfg.name} HISA selection {out['hisa']:.1f} us/step vs Full{' + HSI pool' if pb else ''} {out['full']:.1f} us")
+    return {"workload": f"{cfg.name.split('_h64')[0]}_hisa_blocks{cb}_keep{keep}", "us_per_step": round(out["hisa"], 2),
+            "full_selection_us": round(out["full"], 2), "full_selection_has_pool": bool(pb),
+            "value": round(B / (out["hisa"] / 1e6), 1),
+            "unit": "selections/s", "algorithmic_bytes_per_step": hisa_bytes,
+            "achieved_gbs": round(hisa_bytes / (out["hisa"] / 1e6) / 1e9, 1),
+            "launch": "hip-graph; block_keys (newest block) + index_full over block summaries + reindex"}
+
+
 # ----------------------------------------------------------------------------------
 
 def main() -> int:
@@ -514,6 +587,11 @@ def main() -> int:
         secondary["c4_b128_mixed"] = decode_line(4, 2)
         # the decoder's ratio-1 cache with the 2048-block HSI pool
         secondary["c5_decoder_ratio1"] = decode_line(5, 4)
+        # HISA's block-mean pool as the selection, beside the Full layer's
+        secondary["c1_hisa"] = bench_hisa(fk, max(20, args.steps // 4), max(5, args.warmup // 4))
+        torch.cuda.empty_cache()
+        secondary["c2_hisa"] = bench_hisa(fk, max(20, args.steps // 4), max(5, args.warmup // 4), n_rep=2, cfg_id=2)
+        torch.cuda.empty_cache()
         torch.cuda.empty_cache()
         # the pages' whole decoder schedule (20 layers) at that size, through the native runner
         from synth.configs import DECODER_SCHEDULE
