@@ -132,15 +132,18 @@ __global__ __launch_bounds__(256) void write_kv_kernel(
 // in order: a bf16 x fp32 product has at most 32 significant bits, so each fma below
 // rounds exactly where that sum does, and the bytes match a plain evaluation of it.
 //
-// The 64 KB weight matrix is staged in LDS once per workgroup, rows padded by one
-// dword so that 64 lanes reading one column of their rows spread over the banks; the
-// workgroup's four waves then take entries in a grid-stride loop.  Per entry a wave
-// merges and stores the latent as write_kv_kernel does, parks y in its LDS slot,
-// lane o runs output o's 512-step chain, and lanes 0..7 quantise the 64 outputs.
-constexpr int kProjRowWords = CSA2_D_LATENT / 2 + 1;            // bf16 pairs per padded row
+// The 64 KB weight matrix is staged transposed in LDS once per workgroup (pt[d][o]),
+// and each wave takes groups of 8 entries in a grid-stride loop.  The wave merges and
+// stores the 8 latents one by one as write_kv_kernel does and parks their y in padded
+// LDS rows; then lane (e, g) = (lane / 8, lane % 8) runs the 8 chains of outputs
+// 8g..8g+7 of entry e side by side -- one 16-byte weight read and one y value per
+// channel feed 8 independent fmas -- and those 8 outputs are exactly the channels the
+// MX quantiser expects in that lane, so the key is quantised and stored in place.
 constexpr int kProjWaves = 4;
-constexpr size_t kProjLds = (size_t)CSA2_D_INDEX * kProjRowWords * 4 +
-                            (size_t)kProjWaves * (CSA2_D_LATENT + CSA2_D_INDEX) * 4;
+constexpr int kProjEntries = 8;                                  // entries per wave pass
+constexpr int kProjYPitch = CSA2_D_LATENT + 4;                   // floats per y row (bank offset 4)
+constexpr size_t kProjLds = (size_t)CSA2_D_LATENT * CSA2_D_INDEX * 2 +
+                            (size_t)kProjWaves * kProjEntries * kProjYPitch * 4;
 
 __global__ __launch_bounds__(256) void write_kv_proj_kernel(
     uint8_t* __restrict__ lat_codes, uint8_t* __restrict__ lat_scales,
@@ -149,60 +152,82 @@ __global__ __launch_bounds__(256) void write_kv_proj_kernel(
     int half, int64_t total, const uint16_t* __restrict__ x, const uint16_t* __restrict__ w,
     const uint16_t* __restrict__ w_proj, int ratio) {
   extern __shared__ __attribute__((aligned(16))) uint32_t plds[];
-  uint32_t* pw = plds;                                            // [64][257] bf16 pairs
+  uint16_t* pt = reinterpret_cast<uint16_t*>(plds);               // [512][64]: pt[d*64 + o] = P[o][d]
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  float* ys = reinterpret_cast<float*>(plds + CSA2_D_INDEX * kProjRowWords) + wid * (CSA2_D_LATENT + CSA2_D_INDEX);
-  float* ks = ys + CSA2_D_LATENT;
-  for (int t = threadIdx.x; t < CSA2_D_INDEX * (CSA2_D_LATENT / 2); t += blockDim.x) {
-    const int o = t / (CSA2_D_LATENT / 2), c = t - o * (CSA2_D_LATENT / 2);
-    pw[o * kProjRowWords + c] = reinterpret_cast<const uint32_t*>(w_proj)[t];
+  float* ys = reinterpret_cast<float*>(plds + CSA2_D_LATENT * CSA2_D_INDEX / 2) + wid * kProjEntries * kProjYPitch;
+  // staging: thread (o = t % 64, channels 8c..8c+7) reads 16 bytes of row o and writes
+  // 8 weights; the 64 lanes of a store write 64 adjacent weights
+  for (int t = threadIdx.x; t < CSA2_D_INDEX * (CSA2_D_LATENT / 8); t += blockDim.x) {
+    const int o = t & (CSA2_D_INDEX - 1), c = t / CSA2_D_INDEX;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(w_proj + o * CSA2_D_LATENT + 8 * c);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      pt[(8 * c + 2 * q) * CSA2_D_INDEX + o] = (uint16_t)(v[q] & 0xffffu);
+      pt[(8 * c + 2 * q + 1) * CSA2_D_INDEX + o] = (uint16_t)(v[q] >> 16);
+    }
   }
   __syncthreads();
-  const uint32_t* prow = pw + lane * kProjRowWords;
-  for (int64_t e = (int64_t)blockIdx.x * kProjWaves + wid; e < total; e += (int64_t)gridDim.x * kProjWaves) {
-    const int b = (int)(e / half);
-    const int i = (int)(e - (int64_t)b * half);
+  // cache row of entry e, or -1 (past the end, bad start, absent page)
+  auto entry_row = [&](int64_t e, int& b, int& i) -> int64_t {
+    if (e >= total) return -1;
+    b = (int)(e / half);
+    i = (int)(e - (int64_t)b * half);
     const int st = start_tok[b];
-    if (st < 0 || (ratio == 2 && (st & 1))) continue;             // caller contract: even start at ratio 2
+    if (st < 0 || (ratio == 2 && (st & 1))) return -1;           // caller contract: even start at ratio 2
     const int j = (ratio == 2 ? (st >> 1) : st) + i;
     const int page = page_of(block_table, max_pages, n_pages, b, j);
-    if (page < 0) continue;
-    const int64_t row = (int64_t)page * CSA2_PAGE + (j & (CSA2_PAGE - 1));
-
-    float y[8];
-    entry_latent(x, w, b, i, half, ratio, lane, y);
-    uint32_t codes, u;
-    mx_quant8(y, codes, u);
-    *reinterpret_cast<uint32_t*>(lat_codes + row * CSA2_LAT_CODE_BYTES + lane * 4) = codes;
-    if ((lane & 3) == 0) lat_scales[row * CSA2_LAT_SCALE_BYTES + (lane >> 2)] = (uint8_t)u;
-
-    *reinterpret_cast<f32x4*>(ys + lane * 8) = f32x4{y[0], y[1], y[2], y[3]};
-    *reinterpret_cast<f32x4*>(ys + lane * 8 + 4) = f32x4{y[4], y[5], y[6], y[7]};
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");            // the wave's y is in LDS
-    double s = 0.0;
-#pragma unroll 4
-    for (int d = 0; d < CSA2_D_LATENT; d += 4) {
-      const f32x4 yv = *reinterpret_cast<const f32x4*>(ys + d);  // same address in every lane
-      const uint32_t p01 = prow[d >> 1], p23 = prow[(d >> 1) + 1];
-      s = fma((double)lo_bf16(p01), (double)yv[0], s);
-      s = fma((double)hi_bf16(p01), (double)yv[1], s);
-      s = fma((double)lo_bf16(p23), (double)yv[2], s);
-      s = fma((double)hi_bf16(p23), (double)yv[3], s);
+    return page < 0 ? -1 : (int64_t)page * CSA2_PAGE + (j & (CSA2_PAGE - 1));
+  };
+  const int es = lane >> 3, og = lane & 7;
+  const int64_t n_groups = (total + kProjEntries - 1) / kProjEntries;
+  for (int64_t gi = (int64_t)blockIdx.x * kProjWaves + wid; gi < n_groups; gi += (int64_t)gridDim.x * kProjWaves) {
+    for (int q = 0; q < kProjEntries; ++q) {                      // latents, one entry at a time
+      int b = 0, i = 0;
+      const int64_t row = entry_row(gi * kProjEntries + q, b, i);   // wave-uniform
+      float y[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      if (row >= 0) entry_latent(x, w, b, i, half, ratio, lane, y);
+      uint32_t codes, u;
+      mx_quant8(y, codes, u);
+      if (row >= 0) {
+        *reinterpret_cast<uint32_t*>(lat_codes + row * CSA2_LAT_CODE_BYTES + lane * 4) = codes;
+        if ((lane & 3) == 0) lat_scales[row * CSA2_LAT_SCALE_BYTES + (lane >> 2)] = (uint8_t)u;
+      }
+      float* yr = ys + q * kProjYPitch + lane * 8;
+      *reinterpret_cast<f32x4*>(yr) = f32x4{y[0], y[1], y[2], y[3]};
+      *reinterpret_cast<f32x4*>(yr + 4) = f32x4{y[4], y[5], y[6], y[7]};
     }
-    ks[lane] = (float)s;
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");            // all 64 outputs are in LDS
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");            // the 8 y rows are in LDS
+    double acc[8] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
+    const float* yrow = ys + es * kProjYPitch;
+    const uint16_t* pcol = pt + og * 8;
+#pragma unroll 2
+    for (int d = 0; d < CSA2_D_LATENT; d += 4) {
+      const f32x4 yv = *reinterpret_cast<const f32x4*>(yrow + d);
+#pragma unroll
+      for (int dd = 0; dd < 4; ++dd) {
+        const u32x4 pv = *reinterpret_cast<const u32x4*>(pcol + (d + dd) * CSA2_D_INDEX);
+        const double yd = (double)yv[dd];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          acc[2 * r] = fma((double)lo_bf16(pv[r]), yd, acc[2 * r]);
+          acc[2 * r + 1] = fma((double)hi_bf16(pv[r]), yd, acc[2 * r + 1]);
+        }
+      }
+    }
     float kv[8];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) kv[q] = lane < 8 ? ks[lane * 8 + q] : 0.0f;
-    mx_quant8(kv, codes, u);
-    if (lane < 8) {
-      *reinterpret_cast<uint32_t*>(idx_codes + row * CSA2_IDX_CODE_BYTES + lane * 4) = codes;
-      if ((lane & 3) == 0) idx_scales[row * CSA2_IDX_SCALE_BYTES + (lane >> 2)] = (uint8_t)u;
+    for (int r = 0; r < 8; ++r) kv[r] = (float)acc[r];
+    uint32_t codes, u;
+    mx_quant8(kv, codes, u);                                      // block = lanes 8e..8e+3 / 8e+4..8e+7
+    int b = 0, i = 0;
+    const int64_t row = entry_row(gi * kProjEntries + es, b, i);
+    if (row >= 0) {
+      *reinterpret_cast<uint32_t*>(idx_codes + row * CSA2_IDX_CODE_BYTES + og * 4) = codes;
+      if ((og & 3) == 0) idx_scales[row * CSA2_IDX_SCALE_BYTES + (og >> 2)] = (uint8_t)u;
     }
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");            // y and k slots free for the next entry
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");            // y rows free for the next group
   }
 }
-
 
 // HISA block summaries ([P1] §2.3.4, HISA): block k of a sequence covers entries
 // k*cb .. k*cb+cb-1; its summary is the mean of the dequantised indexer keys of the
@@ -343,8 +368,9 @@ int launch_write_kv_proj(const csa2_cache_t& c, int B, const int32_t* start_tok,
   const int half = T_new / ratio;   // entries per sequence
   const int64_t total = (int64_t)B * half;
   if (total == 0) return CSA2_OK;
-  // two workgroups per CU stay resident (75 KB of LDS each); at most one entry per wave
-  const int64_t grid = std::min<int64_t>((total + kProjWaves - 1) / kProjWaves, 2 * 256);
+  // one workgroup per CU (129 KB of LDS); at most one group of 8 entries per wave
+  const int64_t groups = (total + kProjEntries - 1) / kProjEntries;
+  const int64_t grid = std::min<int64_t>((groups + kProjWaves - 1) / kProjWaves, 256);
   hipLaunchKernelGGL(write_kv_proj_kernel, dim3((unsigned)grid), dim3(64 * kProjWaves), kProjLds, s, c.lat_codes,
                      c.lat_scales, c.idx_codes, c.idx_scales, c.n_pages, c.block_table,
                      c.max_pages, start_tok, half, total, x, w, w_proj, ratio);
