@@ -541,7 +541,7 @@ def main() -> int:
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py: this build runs on one GPU only (the path has no multi-GPU sharding); "
+        print("bench.py: this library runs on one GPU only (the path has no multi-GPU sharding); "
               f"got --gpus {args.gpus}, WORLD_SIZE={world}", file=sys.stderr)
         return 2
     import fp4_kv_cache_write_amd as fk
