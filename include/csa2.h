@@ -13,6 +13,8 @@
  *     The caller allocates and frees all memory: cache pages, tables, inputs, outputs
  *     and workspace.  The library allocates nothing and keeps no mutable global state.
  *   - bf16 values travel as uint16_t bit patterns.
+ *   - Alignment: every device array starts on a 16-byte boundary (the kernels load
+ *     rows with 16-byte vector loads); torch and hipMalloc allocations satisfy this.
  *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL = default
  *     stream).  A return of CSA2_OK means the launch was accepted; results are ready
  *     once the stream is synchronised.
@@ -55,7 +57,7 @@ enum {
   CSA2_OK = 0,
   CSA2_EINVAL = -1,       /* null pointer, bad size, odd token count, ... */
   CSA2_EWORKSPACE = -2,   /* workspace missing or smaller than csa2_workspace_size() */
-  CSA2_EUNSUPPORTED = -3, /* a valid request this build does not implement */
+  CSA2_EUNSUPPORTED = -3, /* a valid request this library does not implement */
   CSA2_EHIP = -4          /* the HIP runtime refused a launch */
 };
 
