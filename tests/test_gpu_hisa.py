@@ -118,3 +118,49 @@ def test_one_entry_blocks_reproduce_the_full_top_k(fk):
     full, _ = fk.index_full(gc, ctx_len, max(ctx), q, w, topk=512)
     torch.cuda.synchronize()
     assert torch.equal(tk.cpu(), full.cpu())
+
+
+def test_hisa_at_full_size_on_sampled_sequences(fk):
+    # The headline shape (32 sequences x 65,536 tokens, 5% heavy-tailed keys): every
+    # block summary of the sampled sequences is bit-exact, and both selection stages
+    # agree with the oracle's scores; the whole batch is launched as one call.
+    from oracle import OracleCache
+    from synth import CONFIGS
+    cfg = CONFIGS[1]
+    cb, keep, topk = cfg.cand_block, 512, cfg.topk
+    case = make_decode_case(cfg, "cuda")
+    seqs = (0, 17, 31)
+    gc = fk.PagedCache.allocate(case.n_pages, case.block_table, device="cuda")
+    bt = case.block_table.to("cuda")
+    oc = OracleCache(case.n_pages, case.block_table.numpy())
+    for b in range(case.B):
+        x, w, k = case.seq_tokens(b)
+        sub = fk.PagedCache(gc.lat_codes, gc.lat_scales, gc.idx_codes, gc.idx_scales, bt[b:b + 1].contiguous())
+        fk.write_kv(sub, torch.zeros(1, dtype=torch.int32, device="cuda"), x[None].contiguous(), w[None].contiguous(),
+                    k[None].contiguous())
+        if b in seqs:
+            oc.write(b, 0, None, None, bits(k), latent=False)
+        del x, w, k
+    max_ctx = max(case.ctx_len)
+    blocks, max_blocks = _block_cache(fk, case.B, max_ctx, cb)
+    ctx_len = torch.tensor(case.ctx_len, dtype=torch.int32, device="cuda")
+    nb = fk.block_keys(gc, blocks, ctx_len, max_ctx, cand_block=cb)
+    L = case.layer(0)
+    tk, pool = fk.index_hisa(gc, blocks, nb, max_blocks, ctx_len, L["q_idx"], L["w_idx"], keep_blocks=keep,
+                             topk=topk, cand_block=cb)
+    torch.cuda.synchronize()
+    bi, bs = blocks.idx_codes.cpu().numpy(), blocks.idx_scales.cpu().numpy()
+    btb = blocks.block_table.cpu().numpy()
+    tk, pool = tk.cpu().numpy(), pool.cpu().numpy()
+    for b in seqs:
+        n_vis = case.n_vis[b]
+        codes, scales = block_summaries(oc, b, n_vis, cb)
+        ks = np.arange(codes.shape[0])
+        assert np.array_equal(bi[btb[b, ks // 64], ks % 64], pack_nibbles(codes)), f"seq {b}: block codes"
+        assert np.array_equal(bs[btb[b, ks // 64], ks % 64], scales), f"seq {b}: block scales"
+        q, w = bits(L["q_idx"][b]), bits(L["w_idx"][b])
+        _, _, S = hisa_layer(oc, b, n_vis, q, w, cb, keep, topk)
+        check_topk_set(pool[b], np.arange(len(S)), S, keep)
+        pos = pool_positions(pool[b][pool[b] >= 0], n_vis, cb)
+        check_topk_set(tk[b], pos, index_scores(q, w, oc.index_keys(b, pos)), topk)
+    assert np.all((tk >= -1) & (tk < max(case.n_vis)))
