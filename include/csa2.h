@@ -15,6 +15,10 @@
  *   - bf16 values travel as uint16_t bit patterns.
  *   - Alignment: every device array starts on a 16-byte boundary (the kernels load
  *     rows with 16-byte vector loads); torch and hipMalloc allocations satisfy this.
+ *   - Graph capture: the launches can be recorded into a HIP graph.  A function's
+ *     first call in a process raises its kernels' dynamic-LDS limit (a runtime call
+ *     that a stream capture may refuse), so make that first call outside a capture;
+ *     csa2_schedule_create does this itself.
  *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL = default
  *     stream).  A return of CSA2_OK means the launch was accepted; results are ready
  *     once the stream is synchronised.
