@@ -122,10 +122,12 @@ struct ScanArgs {
   uint32_t* block_max;
 };
 
-template <int CHUNK>
-__global__ __launch_bounds__(kScanThreads) void index_scan_kernel(ScanArgs a) {
-  constexpr int KPT = CHUNK / kScanThreads;
-  constexpr int GPW = CHUNK / 16 / (kScanThreads / 64);   // groups per wave
+// NT threads stream one chunk: 512, or 1024 when the grid leaves one workgroup per
+// CU (twice the waves, so twice the key loads in flight per CU, for the same chunk).
+template <int CHUNK, int NT = kScanThreads>
+__global__ __launch_bounds__(NT) void index_scan_kernel(ScanArgs a) {
+  constexpr int KPT = CHUNK / NT;
+  constexpr int GPW = CHUNK / 16 / (NT / 64);   // groups per wave
   extern __shared__ __align__(16) uint32_t smem[];
   uint32_t* keys = smem;                          // [CHUNK]
   uint32_t* hist = smem + CHUNK;                  // [kSelectHist]
@@ -211,7 +213,7 @@ __global__ __launch_bounds__(kScanThreads) void index_scan_kernel(ScanArgs a) {
     score_round(i * kScanRound, rr[i & 1]);
   }
   // tail of a partial chunk: keys of absent entries are 0
-  for (int i = ((n_in + 15) & ~15) + threadIdx.x; i < CHUNK; i += kScanThreads) keys[i] = 0u;
+  for (int i = ((n_in + 15) & ~15) + threadIdx.x; i < CHUNK; i += NT) keys[i] = 0u;
   __syncthreads();
 
   uint32_t kr[KPT];
@@ -237,16 +239,16 @@ __global__ __launch_bounds__(kScanThreads) void index_scan_kernel(ScanArgs a) {
       default: block_maxima<KPT, 32>(kr, bm, nb); break;
     }
   }
-  const SelectResult sr = block_select<kScanThreads, KPT>(kr, a.topk, hist, scratch);
+  const SelectResult sr = block_select<NT, KPT>(kr, a.topk, hist, scratch);
   uint32_t* ck = a.cand_key + slot * a.topk;
   int32_t* ci = a.cand_idx + slot * a.topk;
   const int p0 = threadIdx.x * KPT;
-  block_emit<kScanThreads, KPT>(kr, sr, scratch, [&](int i, uint32_t pos) {
+  block_emit<NT, KPT>(kr, sr, scratch, [&](int i, uint32_t pos) {
     ck[pos] = kr[i];
     ci[pos] = e0 + p0 + i;
   });
   // unused slots hold key 0 ("no entry"), so readers need not wait for the count
-  for (int p = (int)sr.count + threadIdx.x; p < a.topk; p += kScanThreads) ck[p] = 0u;
+  for (int p = (int)sr.count + threadIdx.x; p < a.topk; p += NT) ck[p] = 0u;
   if (threadIdx.x == 0) a.cand_cnt[slot] = (int32_t)sr.count;
 }
 
@@ -593,7 +595,8 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 // each kernel's limit once per process.
 bool lds_limits_set() {
   static const bool ok = [] {
-    const void* ks[] = {reinterpret_cast<const void*>(index_scan_kernel<4096>),
+    const void* ks[] = {reinterpret_cast<const void*>(index_scan_kernel<4096, 1024>),
+                        reinterpret_cast<const void*>(index_scan_kernel<4096>),
                         reinterpret_cast<const void*>(index_scan_kernel<8192>),
                         reinterpret_cast<const void*>(index_scan_kernel<16384>),
                         reinterpret_cast<const void*>(reindex_kernel<8>),
@@ -687,7 +690,9 @@ int launch_index_full(const csa2_cache_t& c, int B, const int32_t* ctx_len, int6
   const size_t scan_lds = (size_t)(p.chunk + kSelectHist + kSelectScratch) * 4;
   const int64_t grid = (int64_t)B * p.n_chunks;
   if (grid > 0x7fffffff) return CSA2_EUNSUPPORTED;
-  if (p.chunk == 4096)
+  if (p.chunk == 4096 && grid <= 256)
+    hipLaunchKernelGGL((index_scan_kernel<4096, 1024>), dim3((unsigned)grid), dim3(1024), scan_lds, s, sa);
+  else if (p.chunk == 4096)
     hipLaunchKernelGGL(index_scan_kernel<4096>, dim3((unsigned)grid), dim3(kScanThreads), scan_lds, s, sa);
   else if (p.chunk == 8192)
     hipLaunchKernelGGL(index_scan_kernel<8192>, dim3((unsigned)grid), dim3(kScanThreads), scan_lds, s, sa);
