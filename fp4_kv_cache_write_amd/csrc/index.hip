@@ -632,9 +632,10 @@ IndexFullPlan plan_index_full(int B, int64_t max_nvis, int topk, int pool_blocks
   p.chunk = ch;
   p.n_chunks = (int)nc;
   p.max_blocks = (int)max_blocks;
-  // group the chunks when the final merge would hold more than 4 keys per thread
+  // group the chunks when the final merge would hold more than 16 keys per thread
+  // (16 is faster than grouping for the mixed batch's longest sequences; 32 is not)
   const int64_t per_group = (4 * kMergeThreads) / topk;
-  if (nc * topk > 4 * kMergeThreads && per_group >= 2) {
+  if (nc * topk > 16 * kMergeThreads && per_group >= 2) {
     p.group = (int)per_group;
     p.n_groups = (int)((nc + per_group - 1) / per_group);
   }
