@@ -26,7 +26,9 @@ namespace csa2 {
 namespace {
 
 constexpr int kScanThreads = 512;
-constexpr int kScanRound = 8;        // groups of 16 entries a wave loads before scoring them (2 pages)
+constexpr int kScanRound = 4;        // groups of 16 entries a scan wave loads before scoring them (1 page)
+constexpr int kReindexRound = 8;     // groups of 16 pool slots a reindex wave loads before scoring them
+static_assert(kScanRound % 4 == 0, "a scan round covers whole 64-entry pages");
 constexpr int kMergeThreads = 1024;
 constexpr int kMergeCap = 32768;     // keys the merge / pool workgroup selects from
 constexpr int kReindexThreads = 512;
@@ -153,7 +155,7 @@ __global__ __launch_bounds__(NT) void index_scan_kernel(ScanArgs a) {
   for (int h = 0; h < 4; ++h) wh[h] = bf16_to_f32(a.w_idx[b * CSA2_H_INDEX + h]);
 
   // Wave w streams groups [w*GPW, (w+1)*GPW) of 16 entries in rounds of kScanRound
-  // groups (2 pages).  A round's page ids are fetched with scalar loads, then all its
+  // groups (1 page).  A round's page ids are fetched with scalar loads, then all its
   // code and scale loads are issued; the next round is issued before this one is
   // scored, so its memory latency overlaps the scoring.
   const int32_t* bt = a.block_table + (int64_t)b * a.max_pages;
@@ -433,17 +435,17 @@ __global__ __launch_bounds__(kReindexThreads) void reindex_kernel(ReindexArgs a)
   const int wv = __builtin_amdgcn_readfirstlane(wid);
   const int gpw = (n_grp + NW - 1) / NW;
   const int g0 = wv * gpw, g1 = min(n_grp, g0 + gpw);
-  for (int r0 = g0; r0 < g1; r0 += kScanRound) {
-    u32x2 cd[kScanRound];
-    uint32_t sb[kScanRound];
-    int32_t rid[kScanRound];
+  for (int r0 = g0; r0 < g1; r0 += kReindexRound) {
+    u32x2 cd[kReindexRound];
+    uint32_t sb[kReindexRound];
+    int32_t rid[kReindexRound];
 #pragma unroll
-    for (int u = 0; u < kScanRound; ++u) {
+    for (int u = 0; u < kReindexRound; ++u) {
       const int v = (r0 + u) * 16 + n;
       rid[u] = (r0 + u < g1 && v < N) ? rowid[v] : -1;
     }
 #pragma unroll
-    for (int u = 0; u < kScanRound; ++u) {
+    for (int u = 0; u < kReindexRound; ++u) {
       cd[u] = u32x2{0u, 0u};
       sb[u] = 0u;
       if (rid[u] >= 0) {
@@ -454,7 +456,7 @@ __global__ __launch_bounds__(kReindexThreads) void reindex_kernel(ReindexArgs a)
     // slot v's row id and key share a word; both are touched only by this wave,
     // in program order, so the read above precedes the write below
 #pragma unroll
-    for (int u = 0; u < kScanRound; ++u) {
+    for (int u = 0; u < kReindexRound; ++u) {
       if (r0 + u >= g1) break;                    // wave-uniform
       const float s = score16(cd[u], sb[u], a0, a1, wh);
       const int v = (r0 + u) * 16 + n;
