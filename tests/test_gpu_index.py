@@ -46,6 +46,9 @@ CASES = [
     ((65536, 3000), 512, 512, 8, "random"),                               # config-1 length
     ((5000,), 2048, 300, 16, "identity"),
     ((16390,), 100, 5, 1, "random"),
+    # 133,000 entries at K = 2048: 16384-entry chunks, the chunk groups' pre-merge, and a
+    # final merge of 32 keys per thread; the shorter sequence leaves four of five groups empty
+    ((266000, 40002), 2048, 64, 8, "random"),
 ]
 
 
