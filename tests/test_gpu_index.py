@@ -49,6 +49,9 @@ CASES = [
     # 133,000 entries at K = 2048: 16384-entry chunks, the chunk groups' pre-merge, and a
     # final merge of 32 keys per thread; the shorter sequence leaves four of five groups empty
     ((266000, 40002), 2048, 64, 8, "random"),
+    # 65 sequences: a 5-chunk grid of 325 scan workgroups (the 8-wave scan workgroup),
+    # with short and empty sequences whose chunks hold nothing
+    (tuple([35000] + [2 * ((i * 97) % 1500) for i in range(64)]), 512, 64, 8, "random"),
 ]
 
 
@@ -95,7 +98,8 @@ def test_index_full_without_pool_and_repeatable(fk):
 @pytest.mark.parametrize("split", [True, False], ids=["split", "one-pass"])
 @pytest.mark.parametrize("ctx,pool_blocks,cb,topk", [((65536, 9000, 300), 512, 8, 512),
                                                      ((20000,), 100, 4, 64), ((778,), 200, 8, 512),
-                                                     ((60000,), 1024, 16, 300)])
+                                                     ((60000,), 1024, 16, 300),
+                                                     ((50000,), 700, 8, 512)])   # 5,600 slots
 def test_reindex_matches_oracle_on_oracle_pool(fk, ctx, pool_blocks, cb, topk, split):
     cfg = small_decode(1, B=len(ctx), ctx=ctx, pages="random", heavy_frac=0.05, append=0)
     case = make_decode_case(cfg, "cpu")
