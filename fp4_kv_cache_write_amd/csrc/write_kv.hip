@@ -52,30 +52,49 @@ __device__ __forceinline__ float lo_bf16(uint32_t d) { return __uint_as_float(d 
 __device__ __forceinline__ float hi_bf16(uint32_t d) { return __uint_as_float(d & 0xffff0000u); }
 
 // Channels 8l..8l+7 (lane l) of entry i of sequence b before quantisation: the fp32
-// merge of its two tokens (ratio 2) or the token itself (ratio 1).
-__device__ __forceinline__ void entry_latent(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, int b,
-                                             int i, int half, int ratio, int lane, float (&y)[8]) {
+// merge of its two tokens (ratio 2) or the token itself (ratio 1).  The raw bf16 words
+// are loaded first (entry_words) and combined later (latent_of), so a caller can issue
+// the loads before work that does not depend on them.
+struct EntryWords {
+  u32x4 xa, xb, wa, wb;   // ratio 1: xa only
+};
+
+__device__ __forceinline__ void entry_words(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, int b,
+                                            int i, int half, int ratio, int lane, EntryWords& t) {
+  if (ratio == 2) {
+    const int64_t tok0 = ((int64_t)b * 2 * half + 2 * i) * CSA2_D_LATENT + lane * 8;
+    t.xa = *reinterpret_cast<const u32x4*>(x + tok0);
+    t.xb = *reinterpret_cast<const u32x4*>(x + tok0 + CSA2_D_LATENT);
+    t.wa = *reinterpret_cast<const u32x4*>(w + tok0);
+    t.wb = *reinterpret_cast<const u32x4*>(w + tok0 + CSA2_D_LATENT);
+  } else {
+    t.xa = *reinterpret_cast<const u32x4*>(x + ((int64_t)b * half + i) * CSA2_D_LATENT + lane * 8);
+  }
+}
+
+__device__ __forceinline__ void latent_of(const EntryWords& t, int ratio, float (&y)[8]) {
   if (ratio == 2) {
     // y = w0*x0 + w1*x1 with one rounding (w1*x1 is exact in fp32)
-    const int64_t tok0 = ((int64_t)b * 2 * half + 2 * i) * CSA2_D_LATENT + lane * 8;
-    const u32x4 xa = *reinterpret_cast<const u32x4*>(x + tok0);
-    const u32x4 xb = *reinterpret_cast<const u32x4*>(x + tok0 + CSA2_D_LATENT);
-    const u32x4 wa = *reinterpret_cast<const u32x4*>(w + tok0);
-    const u32x4 wb = *reinterpret_cast<const u32x4*>(w + tok0 + CSA2_D_LATENT);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      y[2 * q] = fmaf(lo_bf16(wa[q]), lo_bf16(xa[q]), lo_bf16(wb[q]) * lo_bf16(xb[q]));
-      y[2 * q + 1] = fmaf(hi_bf16(wa[q]), hi_bf16(xa[q]), hi_bf16(wb[q]) * hi_bf16(xb[q]));
+      y[2 * q] = fmaf(lo_bf16(t.wa[q]), lo_bf16(t.xa[q]), lo_bf16(t.wb[q]) * lo_bf16(t.xb[q]));
+      y[2 * q + 1] = fmaf(hi_bf16(t.wa[q]), hi_bf16(t.xa[q]), hi_bf16(t.wb[q]) * hi_bf16(t.xb[q]));
     }
   } else {
     // the token itself (bf16 is exact in fp32)
-    const u32x4 xa = *reinterpret_cast<const u32x4*>(x + ((int64_t)b * half + i) * CSA2_D_LATENT + lane * 8);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      y[2 * q] = lo_bf16(xa[q]);
-      y[2 * q + 1] = hi_bf16(xa[q]);
+      y[2 * q] = lo_bf16(t.xa[q]);
+      y[2 * q + 1] = hi_bf16(t.xa[q]);
     }
   }
+}
+
+__device__ __forceinline__ void entry_latent(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, int b,
+                                             int i, int half, int ratio, int lane, float (&y)[8]) {
+  EntryWords t;
+  entry_words(x, w, b, i, half, ratio, lane, t);
+  latent_of(t, ratio, y);
 }
 
 __global__ __launch_bounds__(256) void write_kv_kernel(
@@ -90,6 +109,12 @@ __global__ __launch_bounds__(256) void write_kv_kernel(
   const int lane = threadIdx.x & 63;
   const int b = (int)(e / half);
   const int i = (int)(e - (int64_t)b * half);
+  // The entry's inputs do not depend on where it is stored: their loads are issued
+  // first and are in flight during the page lookup (start_tok, then the block table).
+  EntryWords t;
+  entry_words(x, w, b, i, half, ratio, lane, t);
+  u32x4 ka = u32x4{0u, 0u, 0u, 0u};   // lanes 0..7: channels 8l..8l+7 of the indexer key
+  if (lane < 8) ka = *reinterpret_cast<const u32x4*>(k_idx + ((int64_t)b * half + i) * CSA2_D_INDEX + lane * 8);
   const int st = start_tok[b];
   if (st < 0 || (ratio == 2 && (st & 1))) return;       // caller contract: even start at ratio 2
   const int j = (ratio == 2 ? (st >> 1) : st) + i;
@@ -98,7 +123,7 @@ __global__ __launch_bounds__(256) void write_kv_kernel(
   const int64_t row = (int64_t)page * CSA2_PAGE + (j & (CSA2_PAGE - 1));
 
   float y[8];
-  entry_latent(x, w, b, i, half, ratio, lane, y);
+  latent_of(t, ratio, y);
   uint32_t codes, u;
   mx_quant8(y, codes, u);
   *reinterpret_cast<uint32_t*>(lat_codes + row * CSA2_LAT_CODE_BYTES + lane * 4) = codes;
@@ -106,17 +131,10 @@ __global__ __launch_bounds__(256) void write_kv_kernel(
 
   // ---- indexer key: lanes 0..7 own 8 channels each (two MX blocks) ----
   float kv[8];
-  if (lane < 8) {
-    const u32x4 ka = *reinterpret_cast<const u32x4*>(
-        k_idx + ((int64_t)b * half + i) * CSA2_D_INDEX + lane * 8);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      kv[2 * q] = lo_bf16(ka[q]);
-      kv[2 * q + 1] = hi_bf16(ka[q]);
-    }
-  } else {
-#pragma unroll
-    for (int q = 0; q < 8; ++q) kv[q] = 0.0f;
+  for (int q = 0; q < 4; ++q) {   // lanes 8..63 hold zeros
+    kv[2 * q] = lo_bf16(ka[q]);
+    kv[2 * q + 1] = hi_bf16(ka[q]);
   }
   mx_quant8(kv, codes, u);
   if (lane < 8) {
