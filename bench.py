@@ -136,7 +136,12 @@ def recorded_traffic(kernel: str):
 
 
 def decode_bytes(case):
-    """Algorithmic HBM bytes of every call type for one step (formulas in the design doc)."""
+    """Algorithmic HBM bytes of every call type for one step: each byte a call must
+    read or write, counted once.  Full: every visible indexer key (BYTES_IDX each), the
+    520 B of indexer query and head weights, the top-K and pool written.  Reindex: the
+    pool's keys, the query, the pool read and the top-K written.  Attention: each
+    selected latent row (BYTES_LAT), each window row (1 KiB of bf16), the query read and
+    the output written (1 KiB per head each), the ids and the per-head log-sum-exp."""
     cfg = case.cfg
     B, H, topk, W = case.B, cfg.H, cfg.topk, cfg.window
     n_vis = case.n_vis
