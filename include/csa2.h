@@ -179,7 +179,12 @@ int csa2_block_keys(const csa2_cache_t *cache, const csa2_cache_t *blocks, int B
  *   w_idx: [B][4] bf16; topk_idx: [B][topk] int32; pool: [B][pool_blocks] int32 or
  *   NULL when pool_blocks == 0 (all device).  1 <= topk <= 2048; cand_block in
  *   {1,2,4,8,16,32}; max_ctx/ratio <= 64 * max_pages.  ws: csa2_workspace_size(
- *   CSA2_FN_INDEX_FULL, B, 0, max_ctx, topk, pool_blocks, 0, ratio) bytes (device). */
+ *   CSA2_FN_INDEX_FULL, B, 0, max_ctx, topk, pool_blocks, 0, ratio) bytes (device).
+ *   Capacity, with n = max_ctx / ratio: ceil(n / 16384) * topk <= 32768 (1,048,576
+ *   entries at topk 512), and with pool_blocks > 0 also ceil(n / min(cand_block, 8))
+ *   <= 32768 (262,144 entries at cand_block 8).  Past these the call returns
+ *   CSA2_EUNSUPPORTED, and the workspace size query returns 0 (it assumes
+ *   cand_block 8). */
 int csa2_index_full(const csa2_cache_t *cache, int B, const int32_t *ctx_len, int64_t max_ctx,
                     const uint16_t *q_idx, const uint16_t *w_idx, int topk, int pool_blocks,
                     int cand_block, int32_t *topk_idx, int32_t *pool, void *ws, size_t ws_bytes,

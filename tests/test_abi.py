@@ -47,6 +47,17 @@ def test_workspace_sizes_are_consistent():
     assert fk.workspace_size(99, B=1) == 0
 
 
+def test_index_full_capacity_boundaries():
+    # the Full selection merges at most 32,768 candidates (16384-entry chunks x topk) and,
+    # with a pool, at most 32,768 block maxima of 8 entries: one entry more is unsupported
+    ws = lambda max_ctx, topk, pool_blocks, ratio=2: fk.workspace_size(
+        fk.FN_INDEX_FULL, B=1, max_ctx=max_ctx, topk=topk, pool_blocks=pool_blocks, ratio=ratio)
+    assert ws(2 * 1048576, 512, 0) > 0 and ws(2 * 1048576 + 2, 512, 0) == 0
+    assert ws(1048576, 512, 0, ratio=1) > 0 and ws(1048577, 512, 0, ratio=1) == 0
+    assert ws(2 * 16 * 16384, 2048, 0) > 0 and ws(2 * 16 * 16384 + 2, 2048, 0) == 0
+    assert ws(2 * 262144, 512, 512) > 0 and ws(2 * 262144 + 2, 512, 512) == 0
+
+
 def _fake_cache(max_pages=4, ratio=0):
     # Non-null host addresses: validation must reject the call before anything
     # dereferences them or launches a kernel.
