@@ -76,7 +76,7 @@ def _run(fk, cfg_layers, ratio, ctx, write_last):
     layers = _layers(case, 16)
     sch = fk.Schedule(gc, ctx_len, max(case.ctx_len), layers, W=cfg.window, write=write)
     outs = []
-    for _ in range(2):
+    for _ in range(3):   # each replay checked; eager fills and a sync between replays
         for L in layers:
             L["out"].zero_()
             L["lse"].zero_()
