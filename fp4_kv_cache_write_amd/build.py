@@ -22,8 +22,11 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, 
 
 
 # Per-source flags.  The prefill indexer reads each MFMA result once with plain VALU
-# ops; the VGPR form of its MFMAs saves the accumulator-to-VGPR copies.
-EXTRA = {"prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# ops; the VGPR form of its MFMAs saves the accumulator-to-VGPR copies.  The attention
+# kernel runs two waves per SIMD (256 registers each): in the VGPR form its
+# accumulators, q and staging share one budget instead of a fixed 128/128 split.
+EXTRA = {"prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+         "attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def sources():

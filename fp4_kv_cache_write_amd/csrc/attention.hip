@@ -8,70 +8,78 @@
 // entries and the layer's window KV together); [P3] "DeepSeek V4.1 Flash
 // architecture..." (scores -> weights summing to 1 -> weighted sum of values).
 //
-// Decomposition: one workgroup per (query, group of 16 heads), 8 waves (two per
-// SIMD).  blockIdx is mapped so that the head groups of a query, and neighbouring
-// queries of a sequence, run on one XCD and share its L2 for the gathered rows.
+// Decomposition.  One workgroup of 8 waves (two per SIMD) per (query, group of 16
+// heads, half or quarter of the output dims).  The window is cut into 16-row units
+// and the FP4 rows into 32-row tiles, each dealt round robin to the waves; a wave
+// takes whole units and tiles: it scores all 512 dims of its rows for the 16 heads,
+// keeps its own online softmax state and accumulates its own O[16 heads][its dims].
+// Nothing is shared between waves until the end, so the row loop has no workgroup
+// barrier; the eight states are merged once through LDS.  The output dims of a
+// (query, head group) are split over 2 workgroups (4 when pairs are few): each part
+// scores all rows and writes its own dims, so no partial state goes through HBM and
+// a launch of 128 pairs fills 256 CUs.
 //
-// Rows are processed in batches that live in one of two 68 KB LDS buffers: window
-// batches of 64 bf16 rows (pitch 1040 B), then FP4 batches of 256 rows (256 code
-// bytes + 16 scale bytes, pitch 272 B).  Batch k+1 is loaded into registers (9 x 16 B
-// per thread) when batch k starts and written to the free buffer after batch k's PV,
-// so the loads overlap batch k's arithmetic.  (Direct global->LDS loads would not:
-// the compiler cannot tell their destination from the buffer being read and waits
-// for them before every LDS read.)  Chunks of rows that are absent are written as
-// zeros, so stale bytes never meet a zero weight (0 * NaN is not 0).  The selected
-// entries' page lookups are loads issued at the start and consumed only when the
-// first FP4 batch is loaded, so they hide behind the window batches.
-// Per batch:
-//   QK  wave w scores 32-row tile w: D[row][head] via 16x16x32 bf16 MFMAs, A = rows
-//       (lane: row l%16, dims 128g+8s..+7 at k-step s, g = l/16; FP4 rows become
+// Costs measured on the MI355X set the shape: a 16x16x32 bf16 MFMA takes ~7.4 ns
+// of a SIMD, VALU work adds to it rather than overlapping, and one wave per SIMD
+// reaches only half the VALU rate of two.  Hence two waves per SIMD (a wave fits in
+// 256 registers with half the dims), and VALU work is kept to the FP4 converts, the
+// row pairing of the value operand and a short softmax.
+//
+// Data path.  Rows are copied from HBM straight into a private LDS region of the
+// wave (global_load_lds, 16 bytes per lane); the wave waits for them with an explicit
+// vmcnt, so its two FP4 tiles are in flight together.  From LDS:
+//   QK  D[row][head] with 16x16x32 bf16 MFMAs.  A = rows (lane: row l%16; at k-step
+//       s = 4c + u lane group g holds dims 128c + 32g + 8u .. +7; FP4 codes become
 //       bf16 through the hardware convert with the e8m0 scale folded in, exact),
-//       B = q (lane: head l%16, same dims; q stays in registers).
-//   max the batch maximum of every head goes through LDS, so all waves hold the
-//       same running maximum; accumulators are rescaled once per batch.
-//   P   the scoring wave turns its 32 scores per head into the P operand of the PV
-//       MFMA -- a bf16 head plus a bf16 residual, since plain bf16 weights would use
-//       most of the 2e-3 error budget on flat softmaxes -- and parks it in LDS.  The
-//       lane's scores are already the K-slots of that operand (rows 4g..4g+3 and
-//       16+4g..16+4g+3 of head l%16), so no lane exchange is needed.
-//   PV  every wave accumulates O[16 heads][its 64 dims] over all tiles of the batch:
-//       n-tile t of lane column n is dim 64w + 4n + t, so a lane reads 4 adjacent
-//       dims (2 FP4 bytes or 8 bf16 bytes) of each of its 8 rows and v_perm pairs
-//       rows into the B operand.  Dims are split across waves, so no wave merges
-//       accumulators with another and each wave writes its own slice of the output.
+//       B = q (lane: head l%16, the same dims; q stays in registers).
+//   P   each lane ends with the scores of head l%16 for rows 4g..4g+3 (and
+//       16+4g..16+4g+3 in an FP4 tile): exactly the K-slots of the value MFMA's A
+//       operand, so P never leaves the lane.  P enters that MFMA as a bf16 head plus
+//       a bf16 residual, since plain bf16 weights use most of the 2e-3 error budget
+//       on flat softmaxes.
+//   PV  n-tile t of lane column n is dim 32n + t: per row a lane reads the 16 bytes
+//       of FP4 codes (or 16 bytes of bf16 per 8 dims) of its 32 dims; the convert
+//       gives pairs of dims of one row and v_perm pairs rows into the B operand.  A
+//       window unit has 16 rows, so its value MFMAs are the 16x16x16 ones.
+//   The running maximum is lazy: it moves only when a tile's maximum passes it by
+//   more than 2^8 (weights up to 256 are exact in the bf16 split and fp32 sums), so
+//   the accumulator is rescaled almost never.
+// LDS layouts are swizzled (XOR of the 16-byte chunk index with the row) so that
+// both the QK reads (16 rows, same chunk) and the PV reads (one row, 16 chunks) hit
+// distinct banks.
 #include "common.h"
 #include "internal.h"
 
 namespace csa2 {
 namespace {
 
-constexpr int kWaves = 8;
-constexpr int kThreads = kWaves * 64;
-constexpr int kRowB = 272;           // FP4 row in LDS: 256 code bytes then 16 scale bytes
-constexpr int kWinB = 1040;          // window row in LDS: 1024 bytes + 16 pad
-constexpr int kFp4Batch = 256;       // FP4 rows per batch (8 tiles)
-constexpr int kWinBatch = 64;        // window rows per batch (2 tiles)
-constexpr int kMaxTiles = kFp4Batch / 32;
-constexpr int kBufBytes = kFp4Batch * kRowB;              // 69632 >= kWinBatch * kWinB
-constexpr int kPBytes = 32;                               // per lane and tile: P head + residual
-constexpr int kStage = (kFp4Batch * 17 + kThreads - 1) / kThreads;   // 16-byte chunks per thread
-constexpr int kOffBuf = 0;
-constexpr int kPSlots = kMaxTiles + kWinBatch / 32;        // FP4 tiles, then a window batch's tiles
-constexpr int kOffP = 2 * kBufBytes;                      // [10 slots][64 lanes][32 B]
-constexpr int kOffRowId = kOffP + kPSlots * 64 * kPBytes;   // [2][256] int32
-constexpr int kOffMax = kOffRowId + 2 * kFp4Batch * 4;    // [8 waves][16] float
-constexpr int kOffL = kOffMax + kWaves * 16 * 4;          // [8 waves][16] float
-constexpr int kLdsBytes = kOffL + kWaves * 16 * 4;
-static_assert(kWinBatch * kWinB <= kBufBytes, "window batch fits a buffer");
-static_assert(kMaxTiles == kWaves, "one FP4 tile per wave");
-static_assert(2 * kFp4Batch == kThreads, "one prefetched row id per thread (two FP4 batches)");
-static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
-static_assert(16 * kWinB <= kPSlots * 64 * kPBytes, "q of 16 heads fits the P slots");
+constexpr int kWavesA = 8;
+constexpr int kThreadsA = kWavesA * 64;
+constexpr int kTile = 32;                              // FP4 rows per tile
+constexpr int kUnit = 16;                              // window rows per unit
+constexpr int kCodeB = kTile * CSA2_LAT_CODE_BYTES;    // 8192: FP4 codes of a tile
+constexpr int kSlotB = kCodeB + kTile * CSA2_LAT_SCALE_BYTES;   // 8704: + scales
+constexpr int kSlots = 2;                              // FP4 tiles in flight per wave
+constexpr int kRegionB = kSlots * kSlotB;              // 17408 per wave
+constexpr int kWinRowB = 2 * CSA2_D_LATENT;            // 1024: a bf16 window row
+constexpr int kMaxFtWave = CSA2_MAX_TOPK / kTile / kWavesA;   // 8 FP4 tiles per wave at most
+constexpr int kOffQ = kWavesA * kRegionB;              // q of the 16 heads: [16][512] bf16
+constexpr int kOffMask = kOffQ + 16 * kWinRowB;        // [8 waves][8] uint32
+constexpr int kOffMl = kOffMask + kWavesA * kMaxFtWave * 4;           // m[8][16], l[8][16]
+constexpr int kLdsA = kOffMl + 2 * kWavesA * 16 * 4;
+constexpr int kDmaFp4 = 8 + 2;                         // DMA instructions per FP4 tile
+constexpr float kLazy = 8.0f;                          // log2 headroom of the lazy maximum
+constexpr int64_t kBatchPairs = 512;                   // from here on, the batched kernels
+static_assert(kUnit * kWinRowB <= kRegionB, "a window unit fits the region");
+static_assert(16 * 256 * 4 <= kRegionB, "the merge's O[16][256] fits a region");
+static_assert(kLdsA <= 160 * 1024, "LDS budget");
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
-struct DecArgs {
+typedef __attribute__((ext_vector_type(4))) short s16x4;
+
+struct AttnArgs {
   const uint8_t* lat_codes;
   const uint8_t* lat_scales;
   const int32_t* block_table;
@@ -86,30 +94,26 @@ struct DecArgs {
   uint16_t* out;
   float* lse;
   int vshift;              // token count -> visible entries: >> vshift
-  float* part;             // split: [B*C*HG][nsplit][kPartFloats]
-  int B, C, H, HG, prefill, q_per_xcd, nsplit;
+  int B, C, H, HG, prefill, q_per_xcd;
 };
 
-// Split launches: the rows of a (query, head group) are spread over nsplit
-// workgroups, each leaving a partial softmax state -- m[16] (running max, log2
-// units), l[16] (sum of 2^(z - m)) and the unnormalised O[16][512] -- that
-// attn_combine_kernel merges.
-constexpr int kPartFloats = 32 + 16 * CSA2_D_LATENT;
-constexpr int kMaxSplit = 8;
-constexpr int kSplitBelow = 256;   // launches with fewer workgroups than CUs split
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-// Rows of split sp: run sp takes the sp-th of nsplit equal shares (in 32-row tiles)
-// of the window rows and, separately, of the FP4 rows.  Every run then starts with
-// window rows, which need no lookups, while the ids of its FP4 rows resolve, and
-// all runs do the same mix of work.  Gives window rows [w0, w1), FP4 rows [f0, f1).
-__device__ __forceinline__ void split_rows(int W, int topk, int nsplit, int sp, int& w0, int& w1, int& f0,
-                                           int& f1) {
-  const int nwt = (W + 31) >> 5, nft = (topk + 31) >> 5;
-  w0 = min(32 * (sp * nwt / nsplit), W);
-  w1 = min(32 * ((sp + 1) * nwt / nsplit), W);
-  f0 = min(32 * (sp * nft / nsplit), topk);
-  f1 = min(32 * ((sp + 1) * nft / nsplit), topk);
+// 16 bytes per lane from global memory into LDS: lane l's bytes land at dst + 16 l.
+__device__ __forceinline__ void dma16(const void* src, uint8_t* dst) {
+  __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)dst, 16, 0, 0);
 }
+// 4 bytes per lane: lane l's bytes land at dst + 4 l.
+__device__ __forceinline__ void dma4(const void* src, uint8_t* dst) {
+  __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)dst, 4, 0, 0);
+}
+// Wait until at most N vector-memory operations of this wave are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x3f70);
+}
+__device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xc07f); }   // lgkmcnt(0)
 
 // low halves of a and b -> (a.lo, b.lo); high halves -> (a.hi, b.hi)
 __device__ __forceinline__ uint32_t pack_lo(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x05040100u); }
@@ -118,928 +122,535 @@ __device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) { return __b
 template <class T>
 __device__ __forceinline__ T lds_ld(const uint8_t* p) { return *reinterpret_cast<const T*>(p); }
 
-// Row of K-slot j for lane group g: rows 4g..4g+3, then 16+4g..16+4g+3.
+// Row of K-slot j of an FP4 tile for lane group g: rows 4g..4g+3, then 16+4g..16+4g+3.
 __device__ __forceinline__ int slot_row(int g, int j) { return j < 4 ? 4 * g + j : 16 + 4 * g + (j - 4); }
 
-// Window slot w (position t-W+1+w) holds a row, i.e. w < W and the position is >= 0.
-__device__ __forceinline__ bool win_valid(int W, int t, int w) { return w < W && t - (W - 1) + w >= 0; }
+// LDS position of 16-byte chunk k of row r.  FP4 rows have 16 chunks, window and q
+// rows 64; only the low four bits of the chunk index move (each map is its own
+// inverse).
+__device__ __forceinline__ int swz_fp4(int k, int r) { return k ^ (r & 15); }
+__device__ __forceinline__ int swz_win(int k, int r) { return k ^ (((k >> 4) & 3) ^ (r & 15)); }
+__device__ __forceinline__ int swz_q(int k, int h) { return k ^ (h & 15); }
 
-// P operand (bf16 head + bf16 residual) of this lane's 8 scores (log2 units, -inf =
-// absent) against the running max m; adds the weights to l_part.
-__device__ __forceinline__ void make_p(const float (&z)[8], float m, float& l_part, u32x4& phi, u32x4& plo) {
-  const float mb = (m == -INFINITY) ? 0.f : m;
-  uint32_t h[4], r[4];
-#pragma unroll
-  for (int j = 0; j < 8; j += 2) {
-    const float p0 = exp2f(z[j] - mb), p1 = exp2f(z[j + 1] - mb);
-    l_part += p0 + p1;
-    const uint32_t h0 = f32_to_bf16_rne(p0), h1 = f32_to_bf16_rne(p1);
-    const uint32_t r0 = f32_to_bf16_rne(p0 - bf16_to_f32(h0));
-    const uint32_t r1 = f32_to_bf16_rne(p1 - bf16_to_f32(h1));
-    h[j >> 1] = h0 | (h1 << 16);
-    r[j >> 1] = r0 | (r1 << 16);
-  }
-  phi = u32x4{h[0], h[1], h[2], h[3]};
-  plo = u32x4{r[0], r[1], r[2], r[3]};
+// Window slot s (position t-W+1+s) holds a row: s < W and the position is >= 0.
+__device__ __forceinline__ bool win_valid(int W, int t, int s) { return s < W && t - (W - 1) + s >= 0; }
+
+// bf16 head and residual of two weights, packed (first weight in the low half).
+__device__ __forceinline__ void split_pair(float p0, float p1, uint32_t& hi, uint32_t& lo) {
+  typedef __attribute__((ext_vector_type(2))) __bf16 bf2;
+  const bf2 h = {(__bf16)p0, (__bf16)p1};
+  hi = __builtin_bit_cast(uint32_t, h);
+  const float r0 = p0 - __uint_as_float(hi << 16), r1 = p1 - __uint_as_float(hi & 0xffff0000u);
+  const bf2 l = {(__bf16)r0, (__bf16)r1};
+  lo = __builtin_bit_cast(uint32_t, l);
 }
 
-// Scores of the FP4 tile at row `base` of the batch in LDS.
-__device__ __forceinline__ void fp4_qk(const uint8_t* rows, const int32_t* rowid, int nrows, int base,
-                                       const u32x4 (&qf)[16], float scale_log2, float (&z)[8]) {
-  const int lane = threadIdx.x & 63;
-  const int n = lane & 15, g = lane >> 4;
-  u32x4 cd0[4], cd1[4];
-  const uint8_t* r0p = rows + (base + n) * kRowB;
-  const uint8_t* r1p = rows + (base + 16 + n) * kRowB;
+// The wave's state: O accumulators of its dim quarters (n-tile t = 8*quarter + tt,
+// lane (n, g): heads 4g..4g+3 of dim 32n + 8*quarter + tt), the lazy running maximum
+// of head n (identical in the 4 lanes of a head) and the lane's share of the sum.
+template <int NQ>
+struct WaveState {
+  f32x4 acc[NQ * 8];
+  float m_run, l_part;
+};
+
+// J scores of head n (log2 units, -inf = absent) -> lazy max -> P operands (bf16
+// head and residual, J/2 dwords each); rescales the state when the max moves.
+template <int NQ, int J>
+__device__ __forceinline__ void softmax_scores(WaveState<NQ>& S, const float (&z)[J], int g, uint32_t (&ph)[J / 2],
+                                               uint32_t (&pl)[J / 2]) {
+  float tmax = z[0];
 #pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    cd0[c] = lds_ld<u32x4>(r0p + 64 * g + 16 * c);
-    cd1[c] = lds_ld<u32x4>(r1p + 64 * g + 16 * c);
-  }
-  const uint32_t sb0 = lds_ld<uint32_t>(r0p + 256 + 4 * g);
-  const uint32_t sb1 = lds_ld<uint32_t>(r1p + 256 + 4 * g);
-  f32x4 sa[4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+  for (int j = 1; j < J; ++j) tmax = fmaxf(tmax, z[j]);
+  tmax = fmaxf(tmax, __shfl_xor(tmax, 16, kWave));
+  tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
+  const bool move = tmax > S.m_run + kLazy;   // also true for the first row seen
+  if (__any(move)) {
+    const float m_new = move ? tmax : S.m_run;
+    const float fac = move ? (S.m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(S.m_run - m_new)) : 1.f;
+    S.l_part *= fac;
+    // acc[t][i] belongs to head 4g+i, whose factor lives in lane 4g+i
+    float fo[4];
+    bool any = false;
 #pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    const float sc0 = e8m0_scale((sb0 >> (8 * c)) & 0xffu);
-    const float sc1 = e8m0_scale((sb1 >> (8 * c)) & 0xffu);
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const bf16x8 qv = __builtin_bit_cast(bf16x8, qf[4 * c + k]);
-      const int e = k & 1;   // two partial sums per row half keep four MFMA chains in flight
-      sa[e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, fp4x8_to_bf16x8(cd0[c][k], sc0)),
-                                                      qv, sa[e], 0, 0, 0);
-      sa[2 + e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-          __builtin_bit_cast(bf16x8, fp4x8_to_bf16x8(cd1[c][k], sc1)), qv, sa[2 + e], 0, 0, 0);
+    for (int ii = 0; ii < 4; ++ii) {
+      fo[ii] = __shfl(fac, 4 * g + ii, kWave);
+      any = any || fo[ii] != 1.f;
     }
-  }
-  const f32x4 s0 = sa[0] + sa[1], s1 = sa[2] + sa[3];
+    if (__any(any)) {
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int r0 = base + slot_row(g, j), r1 = base + slot_row(g, 4 + j);
-    z[j] = (r0 < nrows && rowid[r0] >= 0) ? s0[j] * scale_log2 : -INFINITY;
-    z[4 + j] = (r1 < nrows && rowid[r1] >= 0) ? s1[j] * scale_log2 : -INFINITY;
-  }
-}
-
-// Scores of the window tile at row `base` of the batch in LDS (window slots w0 + row).
-__device__ __forceinline__ void win_qk(const uint8_t* wrows, int W, int t, int w0, int base, const u32x4 (&qf)[16],
-                                       float scale_log2, float (&z)[8]) {
-  const int lane = threadIdx.x & 63;
-  const int n = lane & 15, g = lane >> 4;
-  const uint8_t* r0p = wrows + (base + n) * kWinB + 256 * g;
-  const uint8_t* r1p = wrows + (base + 16 + n) * kWinB + 256 * g;
-  f32x4 sa[4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+      for (int t = 0; t < NQ * 8; ++t)
 #pragma unroll
-  for (int half = 0; half < 2; ++half) {
-    u32x4 r0[8], r1[8];
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      r0[s] = lds_ld<u32x4>(r0p + 16 * (8 * half + s));
-      r1[s] = lds_ld<u32x4>(r1p + 16 * (8 * half + s));
+        for (int ii = 0; ii < 4; ++ii) S.acc[t][ii] *= fo[ii];
     }
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      const bf16x8 qv = __builtin_bit_cast(bf16x8, qf[8 * half + s]);
-      const int e = s & 1;
-      sa[e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, r0[s]), qv, sa[e], 0, 0, 0);
-      sa[2 + e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, r1[s]), qv, sa[2 + e], 0, 0, 0);
-    }
+    S.m_run = m_new;
   }
-  const f32x4 s0 = sa[0] + sa[1], s1 = sa[2] + sa[3];
+  const float mb = S.m_run == -INFINITY ? 0.f : S.m_run;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    z[j] = win_valid(W, t, w0 + base + slot_row(g, j)) ? s0[j] * scale_log2 : -INFINITY;
-    z[4 + j] = win_valid(W, t, w0 + base + slot_row(g, 4 + j)) ? s1[j] * scale_log2 : -INFINITY;
+  for (int j = 0; j < J; j += 2) {
+    const float p0 = __builtin_amdgcn_exp2f(z[j] - mb), p1 = __builtin_amdgcn_exp2f(z[j + 1] - mb);
+    S.l_part += p0 + p1;
+    split_pair(p0, p1, ph[j >> 1], pl[j >> 1]);
   }
 }
 
-// PV for this wave's 64 dims from 8 rows given as pairs d01[j] = dims (4n, 4n+1),
-// d23[j] = dims (4n+2, 4n+3) of row slot j: n-tile t holds dim 4n + t.
-__device__ __forceinline__ void pv4(f32x4 (&acc)[4], const uint32_t (&d01)[8], const uint32_t (&d23)[8], bf16x8 ph,
-                                    bf16x8 pl) {
-  bf16x8 bf[4];
-  bf[0] = __builtin_bit_cast(bf16x8, u32x4{pack_lo(d01[0], d01[1]), pack_lo(d01[2], d01[3]),
-                                           pack_lo(d01[4], d01[5]), pack_lo(d01[6], d01[7])});
-  bf[1] = __builtin_bit_cast(bf16x8, u32x4{pack_hi(d01[0], d01[1]), pack_hi(d01[2], d01[3]),
-                                           pack_hi(d01[4], d01[5]), pack_hi(d01[6], d01[7])});
-  bf[2] = __builtin_bit_cast(bf16x8, u32x4{pack_lo(d23[0], d23[1]), pack_lo(d23[2], d23[3]),
-                                           pack_lo(d23[4], d23[5]), pack_lo(d23[6], d23[7])});
-  bf[3] = __builtin_bit_cast(bf16x8, u32x4{pack_hi(d23[0], d23[1]), pack_hi(d23[2], d23[3]),
-                                           pack_hi(d23[4], d23[5]), pack_hi(d23[6], d23[7])});
-#pragma unroll
-  for (int t = 0; t < 4; ++t) acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph, bf[t], acc[t], 0, 0, 0);
-#pragma unroll
-  for (int t = 0; t < 4; ++t) acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, bf[t], acc[t], 0, 0, 0);
+// Value MFMAs of n-tiles 2m and 2m+1 of quarter qi for an FP4 tile (K = 32 rows):
+// c[j] = dims (8q + 2m, 8q + 2m + 1) of the row in K-slot j, as a bf16 pair.
+template <int NQ>
+__device__ __forceinline__ void pv_pair32(WaveState<NQ>& S, int qi, int m, const uint32_t (&c)[8], bf16x8 ph,
+                                          bf16x8 pl) {
+  const bf16x8 b0 = __builtin_bit_cast(
+      bf16x8, u32x4{pack_lo(c[0], c[1]), pack_lo(c[2], c[3]), pack_lo(c[4], c[5]), pack_lo(c[6], c[7])});
+  const bf16x8 b1 = __builtin_bit_cast(
+      bf16x8, u32x4{pack_hi(c[0], c[1]), pack_hi(c[2], c[3]), pack_hi(c[4], c[5]), pack_hi(c[6], c[7])});
+  f32x4& a0 = S.acc[qi * 8 + 2 * m];
+  f32x4& a1 = S.acc[qi * 8 + 2 * m + 1];
+  a0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph, b0, a0, 0, 0, 0);
+  a1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph, b1, a1, 0, 0, 0);
+  a0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, b0, a0, 0, 0, 0);
+  a1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, b1, a1, 0, 0, 0);
 }
 
-__global__ __launch_bounds__(kThreads) void sparse_decode_kernel(DecArgs a) {
+// The same for a window unit (K = 16 rows, K-slot j = row 4g + j).
+template <int NQ>
+__device__ __forceinline__ void pv_pair16(WaveState<NQ>& S, int qi, int m, const uint32_t (&c)[4], s16x4 ph,
+                                          s16x4 pl) {
+  const s16x4 b0 = __builtin_bit_cast(s16x4, u32x2{pack_lo(c[0], c[1]), pack_lo(c[2], c[3])});
+  const s16x4 b1 = __builtin_bit_cast(s16x4, u32x2{pack_hi(c[0], c[1]), pack_hi(c[2], c[3])});
+  f32x4& a0 = S.acc[qi * 8 + 2 * m];
+  f32x4& a1 = S.acc[qi * 8 + 2 * m + 1];
+  a0 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ph, b0, a0, 0, 0, 0);
+  a1 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ph, b1, a1, 0, 0, 0);
+  a0 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pl, b0, a0, 0, 0, 0);
+  a1 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pl, b1, a1, 0, 0, 0);
+}
+
+// Two FP4 codes (byte m of `codes`) as a bf16 pair.
+__device__ __forceinline__ uint32_t fp4_pair(uint32_t codes, float scale, int m) {
+  switch (m) {
+    case 0: return fp4x2_to_bf16x2<0>(codes, scale);
+    case 1: return fp4x2_to_bf16x2<1>(codes, scale);
+    case 2: return fp4x2_to_bf16x2<2>(codes, scale);
+    default: return fp4x2_to_bf16x2<3>(codes, scale);
+  }
+}
+
+struct Slot0 { static constexpr int value = 0; };
+struct Slot1 { static constexpr int value = 1; };
+
+template <int NQ>
+__global__ __launch_bounds__(kThreadsA) void attn_kernel(AttnArgs a) {
+  static_assert(NQ == 1 || NQ == 2, "one or two dim quarters per workgroup");
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-  uint8_t* plds = lds + kOffP;
-  int32_t* rowid_all = reinterpret_cast<int32_t*>(lds + kOffRowId);
-  float* m_part = reinterpret_cast<float*>(lds + kOffMax);
-  float* l_w = reinterpret_cast<float*>(lds + kOffL);
+  constexpr int ND = 4 / NQ;   // workgroups per (query, head group)
 
   // XCD-aware mapping: consecutive workgroup ids go to different XCDs; XCD x takes
-  // the contiguous query range [x * q_per_xcd, (x+1) * q_per_xcd), all head groups.
-  // A split launch gives each (query, head group) nsplit consecutive workgroups.
+  // the contiguous query range [x * q_per_xcd, (x+1) * q_per_xcd), all head groups
+  // and dim parts, so the workgroups reading the same rows share one L2.
   const int xcd = blockIdx.x & 7;
   const int li = blockIdx.x >> 3;
-  const int per_q = a.HG * a.nsplit;
+  const int per_q = a.HG * ND;
   const int ql = li / per_q;
   const int rem = li - ql * per_q;
-  const int hg = rem / a.nsplit;
-  const int sp = rem - hg * a.nsplit;
+  const int hg = rem / ND;
+  const int qd0 = (rem - hg * ND) * NQ;   // first dim quarter of this workgroup
   const int64_t qi = (int64_t)xcd * a.q_per_xcd + ql;
   if (ql >= a.q_per_xcd || qi >= (int64_t)a.B * a.C) return;
   const int b = (int)(qi / a.C);
   const int ci = (int)(qi - (int64_t)b * a.C);
 
   const int tid = threadIdx.x, lane = tid & 63;
-  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15, g = lane >> 4;
-
-  // this workgroup's rows: window rows [wr0, wr1), FP4 rows [fr0, fr1) of topk_idx
-  int wr0 = 0, wr1 = a.W, fr0 = 0, fr1 = a.topk;
-  if (a.nsplit > 1) split_rows(a.W, a.topk, a.nsplit, sp, wr0, wr1, fr0, fr1);
+  uint8_t* region = lds + w * kRegionB;
+  const uint8_t* qlds = lds + kOffQ;
+  uint32_t* vmask = reinterpret_cast<uint32_t*>(lds + kOffMask) + w * kMaxFtWave;
 
   int64_t Lq = a.len[b];
   if (Lq < 0) Lq = 0;
   if (a.prefill) Lq += ci + 1;   // chunk query ci sits at position prior + ci
   const int n_vis = (int)(Lq >> a.vshift);
   const int t = (int)Lq - 1;
-  const uint16_t* win_b = a.win + (int64_t)b * (a.prefill ? a.W - 1 + a.C : a.W) * CSA2_D_LATENT;
+  const int W = a.W;
+  const uint16_t* win_b = a.win + (int64_t)b * (a.prefill ? W - 1 + a.C : W) * CSA2_D_LATENT;
   const int32_t* tk = a.topk_idx + qi * a.topk;
   const int32_t* bt = a.block_table + (int64_t)b * a.max_pages;
 
-  const int n_wb = (wr1 - wr0 + kWinBatch - 1) / kWinBatch;
-  const int n_fb = (fr1 - fr0 + kFp4Batch - 1) / kFp4Batch;
-  const int nb = n_wb + n_fb;
+  const int n_wu = (W + kUnit - 1) / kUnit;       // window units; this wave's: w, w + 8, ...
+  const int n_ft = (a.topk + kTile - 1) / kTile;  // FP4 tiles; this wave's: w, w + 8, ...
+  const int nk = n_ft > w ? (n_ft - w + kWavesA - 1) / kWavesA : 0;
 
-  // row id of entry e (-1: invalid id, absent page)
-  auto row_of = [&](int e, int page) -> int {
-    return (e >= 0 && e < n_vis && page >= 0 && page < a.n_pages) ? page * CSA2_PAGE + (e & (CSA2_PAGE - 1)) : -1;
-  };
-  auto page_ok = [&](int e) { return e >= 0 && e < n_vis && (e >> 6) < a.max_pages; };
-  // FP4 batch f >= 2: ids resolved when the batch is issued
-  auto resolve_rows = [&](int f) {
-    const int r0 = fr0 + f * kFp4Batch;
-    const int nrows = min(fr1 - r0, kFp4Batch);
-    int32_t* rowid = rowid_all + (f & 1) * kFp4Batch;
-    for (int i = tid; i < kFp4Batch; i += kThreads) {
-      const int e = i < nrows ? tk[r0 + i] : -1;
-      rowid[i] = page_ok(e) ? row_of(e, bt[e >> 6]) : -1;
+  // ---- prologue: entry ids of this wave's FP4 tiles (lane: tile 2u + lane/32, row
+  // lane%32), q, and the first window unit's rows; page lookups follow the ids.
+  int ids[kMaxFtWave / 2];
+#pragma unroll
+  for (int u = 0; u < kMaxFtWave / 2; ++u) {
+    ids[u] = -1;
+    if (2 * u < nk) {
+      const int k = 2 * u + (lane >> 5);
+      const int i = kTile * (w + kWavesA * k) + (lane & 31);
+      if (k < nk && i < a.topk) ids[u] = tk[i];
     }
-  };
-  // Batch k in registers: thread tid holds chunks c = tid + 512u (16 bytes each) of
-  // the batch image -- FP4: piece c%17 of row c/17 (16 code pieces, then the scales);
-  // window: piece c%64 of row c/64 -- zeros where no row is.  Every chunk is loaded
-  // (one with no row reads window row 0 of the sequence or cache row 0, and is
-  // dropped), so no branch splits the loads: they issue back to back.
-  auto load_batch = [&](int k, u32x4 (&st)[kStage]) {
-    const u32x4 zero = {0u, 0u, 0u, 0u};
-    if (k < n_wb) {
-      const int w0 = wr0 + k * kWinBatch;
-      int slot0 = (t - (a.W - 1) + w0) % a.W;   // ring slot of the batch's first position
-      if (slot0 < 0) slot0 += a.W;
-#pragma unroll
-      for (int u = 0; u < kWinBatch * 64 / kThreads; ++u) {
-        const int c = tid + kThreads * u;
-        const int r = c >> 6, piece = c & 63;
-        const bool ok = w0 + r < wr1 && win_valid(a.W, t, w0 + r);
-        int row = a.prefill ? ci + w0 + r : (slot0 + r >= a.W ? slot0 + r - a.W : slot0 + r);
-        row = ok ? row : 0;
-        const u32x4 v = *reinterpret_cast<const u32x4*>(win_b + (int64_t)row * CSA2_D_LATENT + 8 * piece);
-        st[u] = ok ? v : zero;
-      }
-#pragma unroll
-      for (int u = kWinBatch * 64 / kThreads; u < kStage; ++u) st[u] = zero;
-    } else {
-      const int f = k - n_wb;
-      const int nrows = min(fr1 - fr0 - f * kFp4Batch, kFp4Batch);
-      const int32_t* rowid = rowid_all + (f & 1) * kFp4Batch;
-      int rid[kStage];
-#pragma unroll
-      for (int u = 0; u < kStage; ++u) {
-        const int c = tid + kThreads * u;
-        rid[u] = rowid[min(c / 17, kFp4Batch - 1)];
-      }
-#pragma unroll
-      for (int u = 0; u < kStage; ++u) {
-        const int c = tid + kThreads * u;
-        const int r = c / 17, piece = c - r * 17;
-        const bool ok = c < kFp4Batch * 17 && r < nrows && rid[u] >= 0;
-        const int64_t rw = ok ? rid[u] : 0;
-        const uint8_t* src = piece < 16 ? a.lat_codes + rw * CSA2_LAT_CODE_BYTES + 16 * piece
-                                        : a.lat_scales + rw * CSA2_LAT_SCALE_BYTES;
-        const u32x4 v = *reinterpret_cast<const u32x4*>(src);
-        st[u] = ok ? v : zero;
-      }
-    }
-  };
-  auto store_batch = [&](int k, const u32x4 (&st)[kStage]) {
-    uint8_t* buf = lds + kOffBuf + (k & 1) * kBufBytes;
-    if (k < n_wb) {
-#pragma unroll
-      for (int u = 0; u < kWinBatch * 64 / kThreads; ++u) {
-        const int c = tid + kThreads * u;
-        *reinterpret_cast<u32x4*>(buf + (c >> 6) * kWinB + (c & 63) * 16) = st[u];
-      }
-    } else {
-#pragma unroll
-      for (int u = 0; u < kStage; ++u) {
-        const int c = tid + kThreads * u;
-        if (c < kFp4Batch * 17) *reinterpret_cast<u32x4*>(buf + c * 16) = st[u];
-      }
-    }
-  };
-
-  // ---- start: the entry ids of the first two FP4 batches (thread tid: batch tid/256,
-  // row tid%256) go out first, then batch 0 (window rows need no lookups) and q.  The
-  // ids' page lookups are issued as soon as the ids land, while the rest is in flight.
-  u32x4 st[kStage];
-  const int pf_i = tid & (kFp4Batch - 1), pf_f = tid >> 8;
-  const int pf_r = fr0 + pf_f * kFp4Batch + pf_i;
-  const int pf_e = (pf_f < n_fb && pf_r < fr1) ? tk[pf_r] : -1;
-  // q of the 16 heads is read from memory once per workgroup -- thread tid: head
-  // tid/32, dims 16(tid%32) .. +15 -- and handed to the waves through the P slots,
-  // which are free until the first P (rows at the window pitch, as win_qk reads them).
-  u32x4 qs[2];
-  {
-    const uint16_t* qp = a.q + (qi * a.H + hg * 16 + (tid >> 5)) * CSA2_D_LATENT + 16 * (tid & 31);
-    qs[0] = *reinterpret_cast<const u32x4*>(qp);
-    qs[1] = *reinterpret_cast<const u32x4*>(qp + 8);
   }
-  if (n_wb > 0) load_batch(0, st);
-  int pf_page = -1;
-  if (n_wb > 0) {
-    if (page_ok(pf_e)) pf_page = bt[pf_e >> 6];
-    store_batch(0, st);
-  } else if (n_fb > 0) {
-    // the run starts with FP4 rows (split launches): resolve the prefetched ids now
-    if (page_ok(pf_e)) pf_page = bt[pf_e >> 6];
-    rowid_all[tid] = row_of(pf_e, pf_page);
-    __syncthreads();
-    load_batch(0, st);
-    store_batch(0, st);
+  // q of heads 2w, 2w+1 into LDS (row = head, chunk k of 8 dims at swz_q(k, head));
+  // every wave reads all 16 heads from there after the barrier below.
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh) {
+    const int head = 2 * w + hh;
+    dma16(a.q + (qi * a.H + hg * 16 + head) * CSA2_D_LATENT + 8 * swz_q(lane, head),
+          lds + kOffQ + head * kWinRowB);
   }
-  // q and the entry ids have arrived before the loop starts: the wait counts inside
-  // the loop then cover only the next batch's loads, which stay in flight until the
-  // batch is stored after PV.
-  __builtin_amdgcn_s_waitcnt(0);
-  {
-    uint8_t* qd = plds + (tid >> 5) * kWinB + 32 * (tid & 31);
-    *reinterpret_cast<u32x4*>(qd) = qs[0];
-    *reinterpret_cast<u32x4*>(qd + 16) = qs[1];
+  // B operand of k-step 4c+u: head n, dims 128c + 32g + 8u .. +7
+  auto q_op = [&](int c, int u) __attribute__((always_inline)) {
+    return __builtin_bit_cast(bf16x8, lds_ld<u32x4>(qlds + n * kWinRowB + 16 * swz_q(16 * c + 4 * g + u, n)));
+  };
+  // Window unit wu into the region: row r = slot 16wu + r.  A slot with no token
+  // reads the row of position t (always present) and is masked in the scores.
+  auto dma_window = [&](int wu) __attribute__((always_inline)) {
+    const int s0 = kUnit * wu;
+    const int row_t = a.prefill ? ci + W - 1 : (t < 0 ? 0 : t % W);
+    int ring = 0;   // ring row of slot s0 (decode), advanced by one per slot
+    if (!a.prefill) {
+      ring = (t - (W - 1) + s0) % W;
+      if (ring < 0) ring += W;
+    }
+#pragma unroll 4
+    for (int r = 0; r < kUnit; ++r) {
+      const int s = s0 + r;
+      const int row = win_valid(W, t, s) ? (a.prefill ? ci + s : ring) : row_t;
+      dma16(win_b + (int64_t)row * CSA2_D_LATENT + 8 * swz_win(lane, r), region + r * kWinRowB);
+      ring = ring + 1 == W ? 0 : ring + 1;
+    }
+  };
+  // Waves w and w+4 share a SIMD.  Waves 0-3 take their window unit first and waves
+  // 4-7 their FP4 tiles first, so one of each pair computes while the other waits for
+  // its rows.
+  const bool win_first = w < 4;
+  const bool has_win = w < n_wu;
+  if (has_win && win_first) dma_window(w);
+  wait_vm<0>();   // ids, q and the first window unit
+  __syncthreads();   // q of every head is in LDS
+
+  // page lookups of the ids
+  int pg[kMaxFtWave / 2];
+#pragma unroll
+  for (int u = 0; u < kMaxFtWave / 2; ++u) {
+    pg[u] = -1;
+    if (2 * u < nk) {
+      const int e = ids[u];
+      if (e >= 0 && e < n_vis && (e >> 6) < a.max_pages) pg[u] = bt[e >> 6];
+    }
   }
-  u32x4 qf[16];   // q operand of head hg*16+n: dims 128g + 8s .. +7 for k-step s
-  auto read_q = [&]() {   // after a barrier that follows the stores above
-    const uint8_t* qp = plds + n * kWinB + 256 * g;
-#pragma unroll
-    for (int s = 0; s < 16; ++s) qf[s] = lds_ld<u32x4>(qp + 16 * s);
-  };
 
-  f32x4 acc[4];
+  WaveState<NQ> S;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_part = 0.f;
+  for (int i = 0; i < NQ * 8; ++i) S.acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  S.m_run = -INFINITY;
+  S.l_part = 0.f;
 
-  // PV of one 32-row tile of a batch in LDS (window rows: bf16; else FP4), this wave's
-  // 64 dims, with the P operand from P slot ps.
-  auto pv_tile = [&](const uint8_t* buf, bool win, int tile, int ps) {
-    const uint8_t* pp = plds + (ps * 64 + lane) * kPBytes;
-    const bf16x8 ph = __builtin_bit_cast(bf16x8, lds_ld<u32x4>(pp));
-    const bf16x8 pl = __builtin_bit_cast(bf16x8, lds_ld<u32x4>(pp + 16));
-    uint32_t d01[8], d23[8];
-    if (win) {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const u32x2 v = lds_ld<u32x2>(buf + (tile * 32 + slot_row(g, j)) * kWinB + 128 * wid + 8 * n);
-        d01[j] = v.x;
-        d23[j] = v.y;
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const uint8_t* rp = buf + (tile * 32 + slot_row(g, j)) * kRowB;
-        const uint32_t c2 = lds_ld<uint16_t>(rp + 32 * wid + 2 * n);
-        const float sc = e8m0_scale(rp[256 + 2 * wid + (n >> 3)]);
-        d01[j] = fp4x2_to_bf16x2<0>(c2, sc);
-        d23[j] = fp4x2_to_bf16x2<1>(c2, sc);
-      }
-    }
-    pv4(acc, d01, d23, ph, pl);
-  };
-  auto put_p = [&](const float (&z)[8], float m, int ps) {
-    u32x4 ph, pl;
-    make_p(z, m, l_part, ph, pl);
-    uint8_t* pp = plds + (ps * 64 + lane) * kPBytes;
-    *reinterpret_cast<u32x4*>(pp) = ph;
-    *reinterpret_cast<u32x4*>(pp + 16) = pl;
-  };
-
-  if (n_wb == 1 && n_fb == 1) {
-    // One window batch (buffer 0, stored in the prologue) and one FP4 batch (buffer 1)
-    // in a single pass: the window tiles are scored while the FP4 rows load, then one
-    // softmax and one PV cover all tiles.
-    uint8_t* bufw = lds + kOffBuf;
-    uint8_t* buff = lds + kOffBuf + kBufBytes;
-    const int ntl_w = (min(wr1 - wr0, kWinBatch) + 31) >> 5;
-    const int nrows_f = min(fr1 - fr0, kFp4Batch);
-    const int ntl_f = (nrows_f + 31) >> 5;
-    rowid_all[tid] = row_of(pf_e, pf_page);
-    __syncthreads();   // window rows, q and the FP4 row ids stored by every thread
-    load_batch(1, st);   // FP4 rows: in flight while the window tiles are scored
-    read_q();
-    float zw[8], zf[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) zw[j] = zf[j] = -INFINITY;
-    if (wid < ntl_w) win_qk(bufw, a.W, t, wr0, wid * 32, qf, a.scale_log2, zw);
-    store_batch(1, st);
-    __syncthreads();   // FP4 rows stored by every thread
-    if (wid < ntl_f) fp4_qk(buff, rowid_all, nrows_f, wid * 32, qf, a.scale_log2, zf);
-    float tmax = -INFINITY;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) tmax = fmaxf(tmax, fmaxf(zw[j], zf[j]));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, kWave));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
-    if (g == 0) m_part[wid * 16 + n] = tmax;
-    __syncthreads();
-    float mb = m_part[n];
-#pragma unroll
-    for (int w = 1; w < kWaves; ++w) mb = fmaxf(mb, m_part[w * 16 + n]);
-    if (wid < ntl_f) put_p(zf, mb, wid);
-    if (wid < ntl_w) put_p(zw, mb, kMaxTiles + wid);
-    m_run = mb;
-    __syncthreads();
-#pragma unroll 1
-    for (int tile = 0; tile < ntl_w; ++tile) pv_tile(bufw, true, tile, kMaxTiles + tile);
-#pragma unroll 1
-    for (int tile = 0; tile < ntl_f; ++tile) pv_tile(buff, false, tile, tile);
-  } else {
-  __syncthreads();   // q stored by every thread
-  read_q();
-#pragma unroll 1
-  for (int k = 0; k < nb; ++k) {
-    const bool is_win = k < n_wb;
-    uint8_t* buf = lds + kOffBuf + (k & 1) * kBufBytes;
-    const int f = k - n_wb;
-    const int w0 = wr0 + k * kWinBatch;
-    const int nrows = is_win ? min(wr1 - w0, kWinBatch) : min(fr1 - fr0 - f * kFp4Batch, kFp4Batch);
-    const int32_t* rowid = rowid_all + (f & 1) * kFp4Batch;
-    const int ntl = (nrows + 31) >> 5;
-
-    __syncthreads();   // batch k stored by every thread; batch k-1 fully consumed
-    // Batch k+1 is loaded now if its rows are known (a window batch, or the second FP4
-    // batch whose ids came with the first); otherwise its row ids are resolved after
-    // this batch's QK, which hides the lookups, and it is loaded after the next barrier.
-    const int f1 = k + 1 - n_wb;
-    const bool has_next = k + 1 < nb;
-    const bool ids_later = has_next && (f1 == 0 || f1 >= 2);
-    if (has_next && !ids_later) load_batch(k + 1, st);   // stored after this batch's PV
-
-    // ---- QK: wave w scores tile w ----
-    float z[8];
-    if (wid < ntl) {
-      if (is_win)
-        win_qk(buf, a.W, t, w0, wid * 32, qf, a.scale_log2, z);
-      else
-        fp4_qk(buf, rowid, nrows, wid * 32, qf, a.scale_log2, z);
-    } else {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) z[j] = -INFINITY;
-    }
-    float tmax = z[0];
-#pragma unroll
-    for (int j = 1; j < 8; ++j) tmax = fmaxf(tmax, z[j]);
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, kWave));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
-    if (g == 0) m_part[wid * 16 + n] = tmax;
-    if (ids_later) {
-      if (f1 == 0)
-        rowid_all[tid] = row_of(pf_e, pf_page);   // the two prefetched FP4 batches
-      else
-        resolve_rows(f1);
-    }
-    __syncthreads();
-    if (ids_later) load_batch(k + 1, st);
-
-    // ---- batch max of head n (identical in every wave), P for the scored tile ----
-    float mb = m_part[n];
-#pragma unroll
-    for (int w = 1; w < kWaves; ++w) mb = fmaxf(mb, m_part[w * 16 + n]);
-    const float m_new = fmaxf(m_run, mb);
-    const float fac = (m_run == -INFINITY || m_new == m_run) ? 1.f : exp2f(m_run - m_new);
-    l_part *= fac;
-    if (wid < ntl) put_p(z, m_new, wid);
-    // rescale: acc[t][i] belongs to head 4g+i, whose factor lives in lane 4g+i
+  // ---- a window unit: 16 rows, QK with 16 MFMAs, value MFMAs with K = 16 ----
+  auto window_unit = [&](int wu) __attribute__((always_inline)) {
+    const int s0 = kUnit * wu;
+    float z[4];
     {
-      float fo[4];
-      bool any = false;
+      f32x4 sa[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+      const uint8_t* rp = region + n * kWinRowB;
 #pragma unroll
-      for (int ii = 0; ii < 4; ++ii) {
-        fo[ii] = __shfl(fac, 4 * g + ii, kWave);
-        any = any || fo[ii] != 1.f;
+      for (int c = 0; c < 4; ++c) {
+        u32x4 v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) v[u] = lds_ld<u32x4>(rp + 16 * swz_win(16 * c + 4 * g + u, n));
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          sa[u & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, v[u]), q_op(c, u),
+                                                              sa[u & 1], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);   // one chunk's rows live at a time (register budget)
       }
-      if (__any(any)) {
+      const f32x4 sv = sa[0] + sa[1];
 #pragma unroll
-        for (int tt = 0; tt < 4; ++tt) {
+      for (int j = 0; j < 4; ++j) z[j] = win_valid(W, t, s0 + 4 * g + j) ? sv[j] * a.scale_log2 : -INFINITY;
+    }
+    uint32_t ph[2], pl[2];
+    softmax_scores<NQ, 4>(S, z, g, ph, pl);
+    const s16x4 phv = __builtin_bit_cast(s16x4, u32x2{ph[0], ph[1]});
+    const s16x4 plv = __builtin_bit_cast(s16x4, u32x2{pl[0], pl[1]});
 #pragma unroll
-          for (int ii = 0; ii < 4; ++ii) acc[tt][ii] *= fo[ii];
+    for (int qi2 = 0; qi2 < NQ; ++qi2) {
+      const int qd = qd0 + qi2;
+      u32x4 v[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int r = 4 * g + j;
+        v[j] = lds_ld<u32x4>(region + r * kWinRowB + 16 * swz_win(4 * n + qd, r));
+      }
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const uint32_t c[4] = {v[0][m], v[1][m], v[2][m], v[3][m]};
+        pv_pair16<NQ>(S, qi2, m, c, phv, plv);
+      }
+    }
+  };
+  if (has_win && win_first) window_unit(w);
+
+  // row ids of the FP4 tiles stay in registers (lane: tile 2u + lane/32, row
+  // lane%32); vmask[k] bit r = row r of tile k valid
+  int rowv[kMaxFtWave / 2];
+#pragma unroll
+  for (int u = 0; u < kMaxFtWave / 2; ++u) {
+    rowv[u] = -1;
+    if (2 * u < nk) {
+      const int e = ids[u], p = pg[u];
+      rowv[u] = (e >= 0 && e < n_vis && p >= 0 && p < a.n_pages) ? p * CSA2_PAGE + (e & (CSA2_PAGE - 1)) : -1;
+      const uint64_t bal = __ballot(rowv[u] >= 0);
+      if (lane == 0) {
+        vmask[2 * u] = (uint32_t)bal;
+        if (2 * u + 1 < nk) vmask[2 * u + 1] = (uint32_t)(bal >> 32);
+      }
+    }
+  }
+  // The page lookups have all been consumed; saying so here keeps the compiler from
+  // waiting for every load in flight (the FP4 tiles' DMAs) at the FP4 loop's entry.
+  wait_vm<0>();
+  // the window units this wave has not done yet (all of them for waves 4-7; beyond
+  // the first for windows longer than 128)
+  auto rest_of_window = [&]() __attribute__((always_inline)) {
+    for (int wu = win_first ? w + kWavesA : w; wu < n_wu; wu += kWavesA) {
+      wait_lds();
+      dma_window(wu);
+      wait_vm<0>();
+      window_unit(wu);
+    }
+  };
+  if (win_first) rest_of_window();
+  wait_lds();   // the region is free, the validity masks are stored
+
+  // ---- FP4 tiles: two slots, each refilled two tiles ahead ----
+  // A row with no entry reads q's first bytes (always present) and is masked: its
+  // score is -inf and its value scale is replaced by 0, so its codes stay finite.
+  auto dma_fp4 = [&](int k, uint8_t* slot) __attribute__((always_inline)) {
+    const int u = k >> 1, hk = 32 * (k & 1);
+    int rw = rowv[0];
+#pragma unroll
+    for (int uu = 1; uu < kMaxFtWave / 2; ++uu) rw = u == uu ? rowv[uu] : rw;
+    const int h = lane >> 4;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int r = 4 * i + h;
+      const int rr = __shfl(rw, hk + r, kWave);
+      const void* src = rr >= 0 ? (const void*)(a.lat_codes + (int64_t)rr * CSA2_LAT_CODE_BYTES + 16 * swz_fp4(lane & 15, r))
+                                : (const void*)a.q;
+      dma16(src, slot + 1024 * i);
+    }
+    // scales: 4 bytes per lane, rows 16i + lane/4
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int rr = __shfl(rw, hk + 16 * i + (lane >> 2), kWave);
+      const void* src = rr >= 0 ? (const void*)(a.lat_scales + (int64_t)rr * CSA2_LAT_SCALE_BYTES + 4 * (lane & 3))
+                                : (const void*)a.q;
+      dma4(src, slot + kCodeB + 256 * i);
+    }
+  };
+  if (nk > 0) dma_fp4(0, region);
+  if (nk > 1) dma_fp4(1, region + kSlotB);
+
+  // one FP4 tile from slot SL (a compile-time constant, so LDS offsets are immediates)
+  auto fp4_tile = [&](int k, auto slot_c) __attribute__((always_inline)) {
+    constexpr int SL = decltype(slot_c)::value;
+    const uint8_t* slot = region + SL * kSlotB;
+    // validity of rows 4g + j (bit j) and 16 + 4g + j (bit 16 + j)
+    const uint32_t vmg = __builtin_amdgcn_readfirstlane(vmask[k]) >> (4 * g);
+    float z[8];
+    {
+      f32x4 sa[4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        // rows n and 16+n: 16 code bytes (dims 128c + 32g .. +31) and the scale byte of
+        // that block (byte g of scale dword c)
+        const u32x4 c0 = lds_ld<u32x4>(slot + n * CSA2_LAT_CODE_BYTES + 16 * swz_fp4(4 * c + g, n));
+        const u32x4 c1 = lds_ld<u32x4>(slot + (16 + n) * CSA2_LAT_CODE_BYTES + 16 * swz_fp4(4 * c + g, n));
+        const uint32_t s0w = lds_ld<uint32_t>(slot + kCodeB + n * CSA2_LAT_SCALE_BYTES + 4 * c);
+        const uint32_t s1w = lds_ld<uint32_t>(slot + kCodeB + (16 + n) * CSA2_LAT_SCALE_BYTES + 4 * c);
+        const float sc0 = e8m0_scale(__builtin_amdgcn_ubfe(s0w, 8 * g, 8));
+        const float sc1 = e8m0_scale(__builtin_amdgcn_ubfe(s1w, 8 * g, 8));
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const bf16x8 qv = q_op(c, u);
+          sa[u & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, fp4x8_to_bf16x8(c0[u], sc0)),
+                                                              qv, sa[u & 1], 0, 0, 0);
+          sa[2 + (u & 1)] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              __builtin_bit_cast(bf16x8, fp4x8_to_bf16x8(c1[u], sc1)), qv, sa[2 + (u & 1)], 0, 0, 0);
         }
       }
-    }
-    m_run = m_new;
-    __syncthreads();
-
-    // ---- PV over every tile of the batch, this wave's 64 dims ----
-#pragma unroll 1
-    for (int tile = 0; tile < ntl; ++tile) pv_tile(buf, is_win, tile, tile);
-    if (k + 1 < nb) store_batch(k + 1, st);   // into the other buffer, free since batch k began
-  }
-  }
-
-  // ---- softmax denominators, output ----
-  float l_head = l_part;
-  l_head += __shfl_xor(l_head, 16, kWave);
-  l_head += __shfl_xor(l_head, 32, kWave);
-  if (g == 0) l_w[wid * 16 + n] = l_head;
-  __syncthreads();
-  if (a.nsplit > 1) {   // partial state of this run of rows
-    float* part = a.part + ((qi * a.HG + hg) * a.nsplit + sp) * (int64_t)kPartFloats;
+      const f32x4 s0v = sa[0] + sa[1], s1v = sa[2] + sa[3];
 #pragma unroll
-    for (int ii = 0; ii < 4; ++ii)
-      __builtin_nontemporal_store(f32x4{acc[0][ii], acc[1][ii], acc[2][ii], acc[3][ii]},
-                                  reinterpret_cast<f32x4*>(part + 32 + (4 * g + ii) * CSA2_D_LATENT + 64 * wid + 4 * n));
-    if (wid == 0 && g == 0) {
-      float sl = 0.f;
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) sl += l_w[w * 16 + n];
-      part[n] = m_run;
-      part[16 + n] = sl;
-    }
-    return;
-  }
-  float lh[4];
-#pragma unroll
-  for (int ii = 0; ii < 4; ++ii) {
-    float s = 0.f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) s += l_w[w * 16 + 4 * g + ii];
-    lh[ii] = s;
-  }
-#pragma unroll
-  for (int ii = 0; ii < 4; ++ii) {
-    const float inv = lh[ii] > 0.f ? 1.f / lh[ii] : 0.f;
-    const uint32_t v0 = f32_to_bf16_rne(acc[0][ii] * inv), v1 = f32_to_bf16_rne(acc[1][ii] * inv);
-    const uint32_t v2 = f32_to_bf16_rne(acc[2][ii] * inv), v3 = f32_to_bf16_rne(acc[3][ii] * inv);
-    *reinterpret_cast<u32x2*>(a.out + (qi * a.H + hg * 16 + 4 * g + ii) * CSA2_D_LATENT + 64 * wid + 4 * n) =
-        u32x2{v0 | (v1 << 16), v2 | (v3 << 16)};
-  }
-  if (a.lse && wid == 0 && g == 0) {
-    float s = 0.f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) s += l_w[w * 16 + n];
-    a.lse[qi * a.H + hg * 16 + n] = s > 0.f ? (m_run + log2f(s)) * kLn2 : -INFINITY;
-  }
-}
-
-
-// ---------------------------------------------------------------------------------
-// All 64 heads of a query in one workgroup (H a multiple of 64).  The 16-head
-// kernel above converts every FP4 element once per head group; here the PV operand
-// of a row is converted once and feeds the MFMAs of all four head groups, and every
-// row is read from memory once per query instead of four times.
-//   batches  window batches of 32 rows and FP4 batches of 128 rows (one 34 KB
-//            buffer each), double-buffered, staged through registers as above.
-//   QK       unit (tile t, head group h) = the scores of 16 heads x 32 rows; wave w
-//            takes head group w%4 (its q fragments stay in registers) and tiles
-//            w/4 and w/4 + 2 of the batch.
-//   max, P   per head group through LDS, as above; P of every unit is parked in LDS.
-//   PV       wave w accumulates O[64 heads][dims 64w..64w+63] (64 registers): per
-//            tile it converts its 8 rows x 4 dims once and runs the 2 x 4 MFMAs of
-//            each of the four head groups on them.
-// ---------------------------------------------------------------------------------
-constexpr int kG4 = 4;                                    // head groups per workgroup
-constexpr int64_t kH64MinQueries = 512;                   // launches with fewer queries use 16 heads
-constexpr int kFb64 = 128;                                // FP4 rows per batch (4 tiles)
-constexpr int kWb64 = 32;                                 // window rows per batch (1 tile)
-constexpr int kTiles64 = kFb64 / 32;
-constexpr int kBuf64 = kFb64 * kRowB;                     // 34816 >= kWb64 * kWinB
-constexpr int kStage64 = (kFb64 * 17 + kThreads - 1) / kThreads;
-constexpr int kPf64 = 4;                                  // FP4 batches whose ids are prefetched
-constexpr int kOff64P = 2 * kBuf64;                       // [4 tiles][4 groups][64 lanes][32 B]
-constexpr int kOff64RowId = kOff64P + kTiles64 * kG4 * 64 * kPBytes;   // [4][128] int32
-constexpr int kOff64Max = kOff64RowId + kPf64 * kFb64 * 4;           // [8 waves][16] float
-constexpr int kOff64L = kOff64Max + kWaves * 16 * 4;                  // [8 waves][16] float
-constexpr int kLds64 = kOff64L + kWaves * 16 * 4;
-static_assert(kWb64 * kWinB <= kBuf64, "window batch fits a buffer");
-static_assert(kPf64 * kFb64 == kThreads, "one prefetched row id per thread");
-static_assert(kTiles64 * kG4 == 2 * kWaves, "two QK units per wave");
-static_assert(kLds64 <= 160 * 1024, "LDS budget");
-
-__global__ __launch_bounds__(kThreads) void sparse_decode64_kernel(DecArgs a) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-  uint8_t* plds = lds + kOff64P;
-  int32_t* rowid_all = reinterpret_cast<int32_t*>(lds + kOff64RowId);
-  float* m_part = reinterpret_cast<float*>(lds + kOff64Max);
-  float* l_w = reinterpret_cast<float*>(lds + kOff64L);
-
-  // XCD-aware mapping: XCD x takes the contiguous query range [x * q_per_xcd, ...).
-  const int xcd = blockIdx.x & 7;
-  const int li = blockIdx.x >> 3;
-  const int nhq = a.H / 64;                     // workgroups per query
-  const int ql = li / nhq;
-  const int hq = li - ql * nhq;                 // heads 64hq .. 64hq+63
-  const int64_t qi = (int64_t)xcd * a.q_per_xcd + ql;
-  if (ql >= a.q_per_xcd || qi >= (int64_t)a.B * a.C) return;
-  const int b = (int)(qi / a.C);
-  const int ci = (int)(qi - (int64_t)b * a.C);
-
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int n = lane & 15, g = lane >> 4;
-  const int my_hg = wid & 3;                    // head group of this wave's QK units
-
-  int64_t Lq = a.len[b];
-  if (Lq < 0) Lq = 0;
-  if (a.prefill) Lq += ci + 1;
-  const int n_vis = (int)(Lq >> a.vshift);
-  const int t = (int)Lq - 1;
-  const uint16_t* win_b = a.win + (int64_t)b * (a.prefill ? a.W - 1 + a.C : a.W) * CSA2_D_LATENT;
-  const int32_t* tk = a.topk_idx + qi * a.topk;
-  const int32_t* bt = a.block_table + (int64_t)b * a.max_pages;
-
-  const int n_wb = (a.W + kWb64 - 1) / kWb64;
-  const int n_fb = a.topk > 0 ? (a.topk + kFb64 - 1) / kFb64 : 0;
-  const int nb = n_wb + n_fb;
-
-  auto row_of = [&](int e, int page) -> int {
-    return (e >= 0 && e < n_vis && page >= 0 && page < a.n_pages) ? page * CSA2_PAGE + (e & (CSA2_PAGE - 1)) : -1;
-  };
-  auto page_ok = [&](int e) { return e >= 0 && e < n_vis && (e >> 6) < a.max_pages; };
-  auto resolve_rows = [&](int f) {   // FP4 batch f >= kPf64, into slot f % kPf64
-    const int r0 = f * kFb64;
-    const int nrows = min(a.topk - r0, kFb64);
-    int32_t* rowid = rowid_all + (f % kPf64) * kFb64;
-    for (int i = tid; i < kFb64; i += kThreads) {
-      const int e = i < nrows ? tk[r0 + i] : -1;
-      rowid[i] = page_ok(e) ? row_of(e, bt[e >> 6]) : -1;
-    }
-  };
-  // Every chunk is loaded, as in the 16-head kernel: no branch splits the loads.
-  auto load_batch = [&](int k, u32x4 (&st)[kStage64]) {
-    const u32x4 zero = {0u, 0u, 0u, 0u};
-    if (k < n_wb) {
-      const int w0 = k * kWb64;
-      int slot0 = (t - (a.W - 1) + w0) % a.W;
-      if (slot0 < 0) slot0 += a.W;
-#pragma unroll
-      for (int u = 0; u < kWb64 * 64 / kThreads; ++u) {
-        const int c = tid + kThreads * u;
-        const int r = c >> 6, piece = c & 63;
-        const bool ok = win_valid(a.W, t, w0 + r);
-        int row = a.prefill ? ci + w0 + r : (slot0 + r >= a.W ? slot0 + r - a.W : slot0 + r);
-        row = ok ? row : 0;
-        const u32x4 v = *reinterpret_cast<const u32x4*>(win_b + (int64_t)row * CSA2_D_LATENT + 8 * piece);
-        st[u] = ok ? v : zero;
-      }
-#pragma unroll
-      for (int u = kWb64 * 64 / kThreads; u < kStage64; ++u) st[u] = zero;
-    } else {
-      const int f = k - n_wb;
-      const int nrows = min(a.topk - f * kFb64, kFb64);
-      const int32_t* rowid = rowid_all + (f % kPf64) * kFb64;
-      int rid[kStage64];
-#pragma unroll
-      for (int u = 0; u < kStage64; ++u) {
-        const int c = tid + kThreads * u;
-        rid[u] = rowid[min(c / 17, kFb64 - 1)];
-      }
-#pragma unroll
-      for (int u = 0; u < kStage64; ++u) {
-        const int c = tid + kThreads * u;
-        const int r = c / 17, piece = c - r * 17;
-        const bool ok = c < kFb64 * 17 && r < nrows && rid[u] >= 0;
-        const int64_t rw = ok ? rid[u] : 0;
-        const uint8_t* src = piece < 16 ? a.lat_codes + rw * CSA2_LAT_CODE_BYTES + 16 * piece
-                                        : a.lat_scales + rw * CSA2_LAT_SCALE_BYTES;
-        const u32x4 v = *reinterpret_cast<const u32x4*>(src);
-        st[u] = ok ? v : zero;
+      for (int j = 0; j < 4; ++j) {
+        z[j] = ((vmg >> j) & 1u) ? s0v[j] * a.scale_log2 : -INFINITY;
+        z[4 + j] = ((vmg >> (16 + j)) & 1u) ? s1v[j] * a.scale_log2 : -INFINITY;
       }
     }
-  };
-  auto store_batch = [&](int k, const u32x4 (&st)[kStage64]) {
-    uint8_t* buf = lds + (k & 1) * kBuf64;
-    if (k < n_wb) {
-#pragma unroll
-      for (int u = 0; u < kWb64 * 64 / kThreads; ++u) {
-        const int c = tid + kThreads * u;
-        *reinterpret_cast<u32x4*>(buf + (c >> 6) * kWinB + (c & 63) * 16) = st[u];
-      }
-    } else {
-#pragma unroll
-      for (int u = 0; u < kStage64; ++u) {
-        const int c = tid + kThreads * u;
-        if (c < kFb64 * 17) *reinterpret_cast<u32x4*>(buf + c * 16) = st[u];
-      }
-    }
-  };
+    uint32_t ph[4], pl[4];
+    softmax_scores<NQ, 8>(S, z, g, ph, pl);
+    const bf16x8 phv = __builtin_bit_cast(bf16x8, u32x4{ph[0], ph[1], ph[2], ph[3]});
+    const bf16x8 plv = __builtin_bit_cast(bf16x8, u32x4{pl[0], pl[1], pl[2], pl[3]});
 
-  // ---- start ----
-  u32x4 st[kStage64];
-  if (n_wb > 0) load_batch(0, st);
-  const int pf_f = tid / kFb64, pf_r = tid;     // prefetched id: FP4 batch tid/128, row tid%128
-  const int pf_e = (pf_f < n_fb && pf_r < a.topk) ? tk[pf_r] : -1;
-  u32x4 qf[16];   // q operand of head 64hq + 16*my_hg + n: dims 128g + 8s .. +7
-  {
-    const uint16_t* qp = a.q + (qi * a.H + 64 * hq + 16 * my_hg + n) * CSA2_D_LATENT + 128 * g;
+    // value operand: the lane's code dwords of its dims 32n + 8*qd0 .. + 8*NQ in each
+    // of its 8 rows (dword qi of row j = dims 32n + 8(qd0 + qi) .. +7)
+    uint32_t v[8][NQ];
+    float scf[8];
 #pragma unroll
-    for (int s = 0; s < 16; ++s) qf[s] = *reinterpret_cast<const u32x4*>(qp + 8 * s);
-  }
-  int pf_page = -1;
-  if (n_wb > 0) store_batch(0, st);
-  __builtin_amdgcn_s_waitcnt(0);
-
-  f32x4 acc[kG4][4];
-#pragma unroll
-  for (int h = 0; h < kG4; ++h)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) acc[h][i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run[kG4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};   // head n of group h
-  float l_part = 0.f;                                                 // head n of my_hg
-
-#pragma unroll 1
-  for (int k = 0; k < nb; ++k) {
-    const bool is_win = k < n_wb;
-    uint8_t* buf = lds + (k & 1) * kBuf64;
-    const int f = k - n_wb;
-    const int w0 = k * kWb64;
-    const int nrows = is_win ? min(a.W - w0, kWb64) : min(a.topk - f * kFb64, kFb64);
-    const int32_t* rowid = rowid_all + (f % kPf64) * kFb64;
-    const int ntl = (nrows + 31) >> 5;
-
-    __syncthreads();   // batch k stored by every thread; batch k-1 fully consumed
-    if (k == 0 && page_ok(pf_e)) pf_page = bt[pf_e >> 6];
-    if (k + 1 < nb) {
-      const int f1 = k + 1 - n_wb;
-      if (f1 == 0) {
-        rowid_all[tid] = row_of(pf_e, pf_page);
-        __syncthreads();
-      } else if (f1 >= kPf64) {
-        resolve_rows(f1);
-        __syncthreads();
-      }
-      load_batch(k + 1, st);
-    }
-
-    // ---- QK: units (tile w/4, group w%4) and (tile w/4 + 2, group w%4) ----
-    const int t0 = wid >> 2, t1 = t0 + 2;
-    float z0[8], z1[8];
-    if (t0 < ntl) {
-      if (is_win)
-        win_qk(buf, a.W, t, w0, t0 * 32, qf, a.scale_log2, z0);
-      else
-        fp4_qk(buf, rowid, nrows, t0 * 32, qf, a.scale_log2, z0);
-    } else {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) z0[j] = -INFINITY;
-    }
-    if (t1 < ntl) {
-      fp4_qk(buf, rowid, nrows, t1 * 32, qf, a.scale_log2, z1);   // window batches hold one tile
-    } else {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) z1[j] = -INFINITY;
-    }
-    float tmax = z0[0];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) tmax = fmaxf(tmax, fmaxf(z0[j], z1[j]));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, kWave));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
-    if (g == 0) m_part[wid * 16 + n] = tmax;
-    __syncthreads();
-
-    // ---- per-group batch max of head n, P of this wave's units ----
-    float fac[kG4];
-#pragma unroll
-    for (int h = 0; h < kG4; ++h) {
-      const float mb = fmaxf(m_part[h * 16 + n], m_part[(h + 4) * 16 + n]);
-      const float m_new = fmaxf(m_run[h], mb);
-      fac[h] = (m_run[h] == -INFINITY || m_new == m_run[h]) ? 1.f : exp2f(m_run[h] - m_new);
-      m_run[h] = m_new;
-    }
-    float my_fac = fac[0], my_m = m_run[0];
-#pragma unroll
-    for (int h = 1; h < kG4; ++h)
-      if (my_hg == h) {
-        my_fac = fac[h];
-        my_m = m_run[h];
-      }
-    l_part *= my_fac;
-    if (t0 < ntl) {
-      u32x4 ph, pl;
-      make_p(z0, my_m, l_part, ph, pl);
-      uint8_t* pp = plds + ((t0 * kG4 + my_hg) * 64 + lane) * kPBytes;
-      *reinterpret_cast<u32x4*>(pp) = ph;
-      *reinterpret_cast<u32x4*>(pp + 16) = pl;
-    }
-    if (t1 < ntl) {
-      u32x4 ph, pl;
-      make_p(z1, my_m, l_part, ph, pl);
-      uint8_t* pp = plds + ((t1 * kG4 + my_hg) * 64 + lane) * kPBytes;
-      *reinterpret_cast<u32x4*>(pp) = ph;
-      *reinterpret_cast<u32x4*>(pp + 16) = pl;
-    }
-    // rescale: acc[h][t][i] belongs to head 4g+i of group h, factor in lane 4g+i
-#pragma unroll
-    for (int h = 0; h < kG4; ++h) {
-      float fo[4];
-      bool any = false;
-#pragma unroll
-      for (int ii = 0; ii < 4; ++ii) {
-        fo[ii] = __shfl(fac[h], 4 * g + ii, kWave);
-        any = any || fo[ii] != 1.f;
-      }
-      if (__any(any)) {
-#pragma unroll
-        for (int tt = 0; tt < 4; ++tt)
-#pragma unroll
-          for (int ii = 0; ii < 4; ++ii) acc[h][tt][ii] *= fo[ii];
-      }
-    }
-    __syncthreads();
-
-    // ---- PV: convert each tile's rows once, MFMAs for all four head groups ----
-#pragma unroll 1
-    for (int tile = 0; tile < ntl; ++tile) {
-      uint32_t d01[8], d23[8];
-      if (is_win) {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const u32x2 v = lds_ld<u32x2>(buf + (tile * 32 + slot_row(g, j)) * kWinB + 128 * wid + 8 * n);
-          d01[j] = v.x;
-          d23[j] = v.y;
-        }
+    for (int j = 0; j < 8; ++j) {
+      const int r = slot_row(g, j);
+      const uint8_t* cp = slot + r * CSA2_LAT_CODE_BYTES + 16 * swz_fp4(n, r) + 4 * qd0;
+      if constexpr (NQ == 1) {
+        v[j][0] = lds_ld<uint32_t>(cp);
       } else {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const uint8_t* rp = buf + (tile * 32 + slot_row(g, j)) * kRowB;
-          const uint32_t c2 = lds_ld<uint16_t>(rp + 32 * wid + 2 * n);
-          const float sc = e8m0_scale(rp[256 + 2 * wid + (n >> 3)]);
-          d01[j] = fp4x2_to_bf16x2<0>(c2, sc);
-          d23[j] = fp4x2_to_bf16x2<1>(c2, sc);
-        }
+        const u32x2 d = lds_ld<u32x2>(cp);
+        v[j][0] = d.x;
+        v[j][1] = d.y;
       }
-      bf16x8 bf[4];
-      bf[0] = __builtin_bit_cast(bf16x8, u32x4{pack_lo(d01[0], d01[1]), pack_lo(d01[2], d01[3]),
-                                               pack_lo(d01[4], d01[5]), pack_lo(d01[6], d01[7])});
-      bf[1] = __builtin_bit_cast(bf16x8, u32x4{pack_hi(d01[0], d01[1]), pack_hi(d01[2], d01[3]),
-                                               pack_hi(d01[4], d01[5]), pack_hi(d01[6], d01[7])});
-      bf[2] = __builtin_bit_cast(bf16x8, u32x4{pack_lo(d23[0], d23[1]), pack_lo(d23[2], d23[3]),
-                                               pack_lo(d23[4], d23[5]), pack_lo(d23[6], d23[7])});
-      bf[3] = __builtin_bit_cast(bf16x8, u32x4{pack_hi(d23[0], d23[1]), pack_hi(d23[2], d23[3]),
-                                               pack_hi(d23[4], d23[5]), pack_hi(d23[6], d23[7])});
+      const uint32_t u8 = slot[kCodeB + r * CSA2_LAT_SCALE_BYTES + n];
+      const uint32_t ok = (vmg >> (j < 4 ? j : 12 + j)) & 1u;
+      scf[j] = e8m0_scale(u8 & (0u - ok));   // absent row: scale byte 0, finite, weight 0
+    }
 #pragma unroll
-      for (int h = 0; h < kG4; ++h) {
-        const uint8_t* pp = plds + ((tile * kG4 + h) * 64 + lane) * kPBytes;
-        const bf16x8 ph = __builtin_bit_cast(bf16x8, lds_ld<u32x4>(pp));
-        const bf16x8 pl = __builtin_bit_cast(bf16x8, lds_ld<u32x4>(pp + 16));
+    for (int qi2 = 0; qi2 < NQ; ++qi2) {
 #pragma unroll
-        for (int tt = 0; tt < 4; ++tt)
-          acc[h][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph, bf[tt], acc[h][tt], 0, 0, 0);
+      for (int m = 0; m < 4; ++m) {
+        uint32_t c[8];
 #pragma unroll
-        for (int tt = 0; tt < 4; ++tt)
-          acc[h][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, bf[tt], acc[h][tt], 0, 0, 0);
+        for (int j = 0; j < 8; ++j) c[j] = fp4_pair(v[j][qi2], scf[j], m);
+        pv_pair32<NQ>(S, qi2, m, c, phv, plv);
       }
     }
-    if (k + 1 < nb) store_batch(k + 1, st);
+  };
+  for (int k = 0; k < nk; k += 2) {
+    if (k + 1 < nk) wait_vm<kDmaFp4>(); else wait_vm<0>();   // tile k landed; k+1 may be in flight
+    fp4_tile(k, Slot0{});
+    if (k + 2 < nk) {
+      wait_lds();   // every read of slot 0 has returned
+      dma_fp4(k + 2, region);
+    }
+    if (k + 1 < nk) {
+      if (k + 2 < nk) wait_vm<kDmaFp4>(); else wait_vm<0>();
+      fp4_tile(k + 1, Slot1{});
+      if (k + 3 < nk) {
+        wait_lds();
+        dma_fp4(k + 3, region + kSlotB);
+      }
+    }
   }
 
-  // ---- softmax denominators (group h: waves h and h+4), output ----
-  float l_head = l_part;
+  if (!win_first) rest_of_window();
+
+  // ---- merge the eight waves: m, l to LDS; O into the wave's own region ----
+  float l_head = S.l_part;
   l_head += __shfl_xor(l_head, 16, kWave);
   l_head += __shfl_xor(l_head, 32, kWave);
-  if (g == 0) l_w[wid * 16 + n] = l_head;
+  float* m_all = reinterpret_cast<float*>(lds + kOffMl);
+  float* l_all = m_all + kWavesA * 16;
+  if (g == 0) {
+    m_all[w * 16 + n] = S.m_run;
+    l_all[w * 16 + n] = l_head;
+  }
+  wait_lds();
+  float* ow = reinterpret_cast<float*>(region);   // [16 heads][NQ*128 dims of this part]
+  constexpr int kDimsP = NQ * 128;
+#pragma unroll
+  for (int ii = 0; ii < 4; ++ii)
+#pragma unroll
+    for (int qi2 = 0; qi2 < NQ; ++qi2) {
+      float* dst = ow + (4 * g + ii) * kDimsP + (n * NQ + qi2) * 8;
+      *reinterpret_cast<f32x4*>(dst) = f32x4{S.acc[qi2 * 8 + 0][ii], S.acc[qi2 * 8 + 1][ii],
+                                             S.acc[qi2 * 8 + 2][ii], S.acc[qi2 * 8 + 3][ii]};
+      *reinterpret_cast<f32x4*>(dst + 4) = f32x4{S.acc[qi2 * 8 + 4][ii], S.acc[qi2 * 8 + 5][ii],
+                                                 S.acc[qi2 * 8 + 6][ii], S.acc[qi2 * 8 + 7][ii]};
+    }
   __syncthreads();
+
+  // wave w writes heads 2w, 2w+1: lane (m = lane%32, head 2w + lane/32) covers local
+  // dims [4*NQ*m, 4*NQ*(m+1)) = output dims 32(m/2) + 8*qd0 + 4*NQ*(m%2) .. + 4*NQ
+  constexpr int kPer = 4 * NQ;
+  const int head = 2 * w + (lane >> 5), m = lane & 31;
+  f32x4 part[kWavesA][kPer / 4];   // every read issued before the first is used
 #pragma unroll
-  for (int h = 0; h < kG4; ++h) {
+  for (int v2 = 0; v2 < kWavesA; ++v2) {
+    const float* src = reinterpret_cast<const float*>(lds + v2 * kRegionB) + head * kDimsP + kPer * m;
 #pragma unroll
-    for (int ii = 0; ii < 4; ++ii) {
-      const float lh = l_w[h * 16 + 4 * g + ii] + l_w[(h + 4) * 16 + 4 * g + ii];
-      const float inv = lh > 0.f ? 1.f / lh : 0.f;
-      const uint32_t v0 = f32_to_bf16_rne(acc[h][0][ii] * inv), v1 = f32_to_bf16_rne(acc[h][1][ii] * inv);
-      const uint32_t v2 = f32_to_bf16_rne(acc[h][2][ii] * inv), v3 = f32_to_bf16_rne(acc[h][3][ii] * inv);
-      *reinterpret_cast<u32x2*>(a.out + (qi * a.H + 64 * hq + 16 * h + 4 * g + ii) * CSA2_D_LATENT + 64 * wid +
-                                4 * n) = u32x2{v0 | (v1 << 16), v2 | (v3 << 16)};
+    for (int i = 0; i < kPer / 4; ++i) part[v2][i] = *reinterpret_cast<const f32x4*>(src + 4 * i);
+  }
+  float mw[kWavesA], lw[kWavesA], M = -INFINITY;
+#pragma unroll
+  for (int v2 = 0; v2 < kWavesA; ++v2) {
+    mw[v2] = m_all[v2 * 16 + head];
+    lw[v2] = l_all[v2 * 16 + head];
+    M = fmaxf(M, mw[v2]);
+  }
+  float o[kPer], L = 0.f;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) o[i] = 0.f;
+#pragma unroll
+  for (int v2 = 0; v2 < kWavesA; ++v2) {
+    const float fw = mw[v2] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw[v2] - M);
+    L += fw * lw[v2];
+#pragma unroll
+    for (int i = 0; i < kPer / 4; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[4 * i + e] += fw * part[v2][i][e];
+  }
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  uint16_t* op = a.out + (qi * a.H + hg * 16 + head) * CSA2_D_LATENT + 32 * (m >> 1) + 8 * qd0 + kPer * (m & 1);
+  if constexpr (kPer == 4) {
+    *reinterpret_cast<u32x2*>(op) = u32x2{f32_to_bf16_rne(o[0] * inv) | (f32_to_bf16_rne(o[1] * inv) << 16),
+                                          f32_to_bf16_rne(o[2] * inv) | (f32_to_bf16_rne(o[3] * inv) << 16)};
+  } else {
+#pragma unroll
+    for (int i = 0; i < kPer / 8; ++i) {
+      u32x4 pk;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        pk[e] = f32_to_bf16_rne(o[8 * i + 2 * e] * inv) | (f32_to_bf16_rne(o[8 * i + 2 * e + 1] * inv) << 16);
+      *reinterpret_cast<u32x4*>(op + 8 * i) = pk;
     }
   }
-  if (a.lse && wid < kG4 && g == 0) {
-    const float s = l_w[wid * 16 + n] + l_w[(wid + 4) * 16 + n];
-    a.lse[qi * a.H + 64 * hq + 16 * wid + n] = s > 0.f ? (m_run[0] * (wid == 0) + m_run[1] * (wid == 1) +
-                                                          m_run[2] * (wid == 2) + m_run[3] * (wid == 3) +
-                                                          log2f(s)) * kLn2
-                                                       : -INFINITY;
-  }
+  if (a.lse && qd0 == 0 && m == 0)
+    a.lse[qi * a.H + hg * 16 + head] = L > 0.f ? (M + log2f(L)) * kLn2 : -INFINITY;
 }
 
 bool lds_limit_set() {
   static const bool ok =
-      hipFuncSetAttribute(reinterpret_cast<const void*>(sparse_decode_kernel),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes) == hipSuccess &&
-      hipFuncSetAttribute(reinterpret_cast<const void*>(sparse_decode64_kernel),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, kLds64) == hipSuccess;
+      hipFuncSetAttribute(reinterpret_cast<const void*>(attn_kernel<1>), hipFuncAttributeMaxDynamicSharedMemorySize,
+                          kLdsA) == hipSuccess &&
+      hipFuncSetAttribute(reinterpret_cast<const void*>(attn_kernel<2>), hipFuncAttributeMaxDynamicSharedMemorySize,
+                          kLdsA) == hipSuccess;
   return ok;
-}
-
-// Merge the split partials of one (query, head group): with m* the largest partial
-// maximum, weights 2^(m_s - m*) scale each partial's sum and output, as in the
-// log-sum-exp merge of softmax blocks.  Workgroup x: pair x/4, heads 4(x%4) .. +3;
-// thread t: head 4(x%4) + t/32, dims 16(t%32) .. +15.  Every load is issued before
-// the first is used (one memory round trip).
-__global__ __launch_bounds__(128) void attn_combine_kernel(const float* __restrict__ part, int nsplit,
-                                                          int64_t n_pairs, uint16_t* __restrict__ out,
-                                                          float* __restrict__ lse) {
-  const int64_t qh = blockIdx.x >> 2;
-  if (qh >= n_pairs) return;
-  const int tid = threadIdx.x, h = 4 * (blockIdx.x & 3) + (tid >> 5), d0 = (tid & 31) * 16;
-  const float* p0 = part + qh * nsplit * (int64_t)kPartFloats;
-  float ms[kMaxSplit], ls[kMaxSplit];
-  f32x4 os[kMaxSplit][4];
-#pragma unroll
-  for (int s = 0; s < kMaxSplit; ++s) {
-    ms[s] = -INFINITY;
-    ls[s] = 0.f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) os[s][i] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (s < nsplit) {
-      const float* ps = p0 + s * kPartFloats;
-      ms[s] = ps[h];
-      ls[s] = ps[16 + h];
-      const f32x4* src = reinterpret_cast<const f32x4*>(ps + 32 + h * CSA2_D_LATENT + d0);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) os[s][i] = src[i];
-    }
-  }
-  float m = -INFINITY;
-#pragma unroll
-  for (int s = 0; s < kMaxSplit; ++s) m = fmaxf(m, ms[s]);
-  float l = 0.f;
-  f32x4 o[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int s = 0; s < kMaxSplit; ++s) {
-    const float w = ms[s] == -INFINITY ? 0.f : exp2f(ms[s] - m);   // runs with no valid row drop out
-    l += w * ls[s];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) o[i][j] += w * os[s][i][j];
-    }
-  }
-  const float inv = l > 0.f ? 1.f / l : 0.f;
-  uint32_t wv[8];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    wv[2 * i] = f32_to_bf16_rne(o[i][0] * inv) | (f32_to_bf16_rne(o[i][1] * inv) << 16);
-    wv[2 * i + 1] = f32_to_bf16_rne(o[i][2] * inv) | (f32_to_bf16_rne(o[i][3] * inv) << 16);
-  }
-  u32x4* dst = reinterpret_cast<u32x4*>(out + (qh * 16 + h) * CSA2_D_LATENT + d0);
-  dst[0] = u32x4{wv[0], wv[1], wv[2], wv[3]};
-  dst[1] = u32x4{wv[4], wv[5], wv[6], wv[7]};
-  if (lse && (tid & 31) == 0) lse[qh * 16 + h] = l > 0.f ? (m + log2f(l)) * kLn2 : -INFINITY;
-}
-
-// Workgroups per (query, head group): enough to give every CU one, at most
-// kMaxSplit, and at least two 32-row tiles each.
-int split_count(int64_t nq, int HG, int W, int topk) {
-  const int64_t pairs = nq * HG;
-  if (pairs <= 0 || pairs >= kSplitBelow) return 1;
-  int s = (int)std::min<int64_t>(kMaxSplit, kSplitBelow / pairs);
-  const int tiles = (W + 31) / 32 + (topk + 31) / 32;
-  s = min(s, max(1, tiles / 2));   // at least two tiles per run
-  return max(s, 1);
 }
 
 }  // namespace
 
-bool attention_kernels_ready() { return lds_limit_set(); }
+bool attention_kernels_ready() { return lds_limit_set() && attention_batch_ready(); }
 
 size_t sparse_decode_ws(int B, int H, int topk) {
+  (void)B;
+  (void)H;
   (void)topk;
-  const int HG = H / 16;
-  const int64_t pairs = (int64_t)B * HG;
-  if (pairs <= 0 || pairs >= kSplitBelow) return 0;
-  const int64_t s = std::min<int64_t>(kMaxSplit, kSplitBelow / pairs);
-  return (size_t)(pairs * s * kPartFloats * 4);
+  return 0;
 }
 
 int launch_gather_attention(const csa2_cache_t& c, int B, int C, int H, const int32_t* len, bool prefill,
                             const uint16_t* q, const int32_t* topk_idx, int topk, const uint16_t* win,
                             int W, float sm_scale, uint16_t* out, float* lse, hipStream_t s, void* ws,
                             size_t ws_bytes) {
+  (void)ws;
+  (void)ws_bytes;
   if (!lds_limit_set()) return CSA2_EHIP;
-  DecArgs a;
+  if (topk > CSA2_MAX_TOPK || W < 1 || W > CSA2_MAX_WINDOW) return CSA2_EINVAL;
+  // Launches with 512 or more (query, head group) pairs fill every CU for several
+  // rounds: there the batched kernels' throughput wins over the short latency
+  // chain of the kernel below (measured: 128 x 64-head decode 54 against 67 us,
+  // 16384-query prefill attention about 2.5x faster).
+  if ((int64_t)B * C * (H / 16) >= kBatchPairs)
+    return launch_attention_batch(c, B, C, H, len, prefill, q, topk_idx, topk, win, W, sm_scale, out, lse, s);
+  AttnArgs a;
   a.lat_codes = c.lat_codes;
   a.lat_scales = c.lat_scales;
   a.block_table = c.block_table;
@@ -1060,33 +671,19 @@ int launch_gather_attention(const csa2_cache_t& c, int B, int C, int H, const in
   a.HG = H / 16;
   a.prefill = prefill ? 1 : 0;
   a.vshift = vis_shift(c);
-  a.part = nullptr;
-  a.nsplit = 1;
   const int64_t nq = (int64_t)B * C;
   const int64_t per = (nq + 7) / 8;
   a.q_per_xcd = (int)per;
-  // 64 heads per workgroup do more arithmetic per byte but four times the work per
-  // workgroup: worth it once the queries alone give every CU a couple of workgroups.
-  if (H % 64 == 0 && nq >= kH64MinQueries) {
-    const int64_t grid = 8 * per * (H / 64);
-    if (grid > 0x7fffffff) return CSA2_EUNSUPPORTED;
-    hipLaunchKernelGGL(sparse_decode64_kernel, dim3((unsigned)grid), dim3(kThreads), kLds64, s, a);
-    return hip_status();
-  }
-  const int ns = split_count(nq, a.HG, W, topk);
-  if (ns > 1 && ws && ws_bytes >= (size_t)(nq * a.HG * ns * kPartFloats * 4)) {
-    a.part = static_cast<float*>(ws);
-    a.nsplit = ns;
-  }
-  const int64_t grid = 8 * per * a.HG * a.nsplit;
+  // The output dims of a (query, head group) go to 2 workgroups, or to 4 while the
+  // pairs alone would leave most CUs idle.
+  const int64_t pairs = nq * a.HG;
+  const int nqrt = pairs >= 128 ? 2 : 1;
+  const int64_t grid = 8 * per * a.HG * (4 / nqrt);
   if (grid > 0x7fffffff) return CSA2_EUNSUPPORTED;
-  hipLaunchKernelGGL(sparse_decode_kernel, dim3((unsigned)grid), dim3(kThreads), kLdsBytes, s, a);
-  if (a.nsplit > 1) {
-    const int rc = hip_status();
-    if (rc != CSA2_OK) return rc;
-    hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)(4 * nq * a.HG)), dim3(128), 0, s, a.part,
-                       a.nsplit, nq * a.HG, out, lse);
-  }
+  if (nqrt == 2)
+    hipLaunchKernelGGL(attn_kernel<2>, dim3((unsigned)grid), dim3(kThreadsA), kLdsA, s, a);
+  else
+    hipLaunchKernelGGL(attn_kernel<1>, dim3((unsigned)grid), dim3(kThreadsA), kLdsA, s, a);
   return hip_status();
 }
 

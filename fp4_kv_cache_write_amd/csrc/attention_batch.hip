@@ -1,0 +1,950 @@
+// Sparse gather-attention for launches with many (query, head group) pairs: the
+// mixed serving batch and chunked prefill, where the work keeps every CU busy for
+// several rounds and throughput, not the length of one workgroup's latency chain,
+// sets the time.  Same computation as attention.hip (one softmax over the top-K FP4
+// latent rows plus the bf16 window, K = V = the 512-d latent, fp32 accumulation,
+// bf16 output); that file holds the kernel for small launches.
+//
+// [P1] "DeepSeek-v4.1 Flash: KVキャッシュ圧縮の限界を押し広げる" §1.2 (window 128,
+// every head shares one 512-d latent) and §2.3.1 (each query attends to the selected
+// entries and the layer's window KV together); [P3] "DeepSeek V4.1 Flash
+// architecture..." (scores -> weights summing to 1 -> weighted sum of values).
+//
+// Two kernels:
+//   sparse_decode_kernel    one workgroup per (query, 16 heads), 8 waves, all rows;
+//   sparse_decode64_kernel  one workgroup per (query, 64 heads) when H is a multiple
+//                           of 64 and there are >= 512 queries: each FP4 tile is
+//                           converted once for four head groups.
+// Rows are processed in batches that live in one of two LDS buffers: window
+// batches of bf16 rows (pitch 1040 B), then FP4 batches (256 code bytes + 16 scale
+// bytes, pitch 272 B).  Batch k+1 is loaded into registers when batch k starts and
+// written to the free buffer after batch k's PV, so the loads overlap batch k's
+// arithmetic.  Chunks of rows that are absent are written as zeros, so stale bytes
+// never meet a zero weight (0 * NaN is not 0).  The selected entries' page lookups
+// are loads issued at the start and consumed only when the first FP4 batch is
+// loaded, so they hide behind the window batches.
+// Per batch (16-head kernel):
+//   QK  wave w scores 32-row tile w: D[row][head] via 16x16x32 bf16 MFMAs, A = rows
+//       (lane: row l%16, dims 128g+8s..+7 at k-step s, g = l/16; FP4 rows become
+//       bf16 through the hardware convert with the e8m0 scale folded in, exact),
+//       B = q (lane: head l%16, same dims; q stays in registers).
+//   max the batch maximum of every head goes through LDS, so all waves hold the
+//       same running maximum; accumulators are rescaled once per batch.
+//   P   the scoring wave turns its 32 scores per head into the P operand of the PV
+//       MFMA -- a bf16 head plus a bf16 residual -- and parks it in LDS.  The lane's
+//       scores are already the K-slots of that operand (rows 4g..4g+3 and
+//       16+4g..16+4g+3 of head l%16), so no lane exchange is needed.
+//   PV  every wave accumulates O[16 heads][its 64 dims] over all tiles of the batch:
+//       n-tile t of lane column n is dim 64w + 4n + t, so a lane reads 4 adjacent
+//       dims (2 FP4 bytes or 8 bf16 bytes) of each of its 8 rows and v_perm pairs
+//       rows into the B operand.
+#include "common.h"
+#include "internal.h"
+
+namespace csa2 {
+namespace {
+
+constexpr int kWaves = 8;
+constexpr int kThreads = kWaves * 64;
+constexpr int kRowB = 272;           // FP4 row in LDS: 256 code bytes then 16 scale bytes
+constexpr int kWinB = 1040;          // window row in LDS: 1024 bytes + 16 pad
+constexpr int kFp4Batch = 256;       // FP4 rows per batch (8 tiles)
+constexpr int kWinBatch = 64;        // window rows per batch (2 tiles)
+constexpr int kMaxTiles = kFp4Batch / 32;
+constexpr int kBufBytes = kFp4Batch * kRowB;              // 69632 >= kWinBatch * kWinB
+constexpr int kPBytes = 32;                               // per lane and tile: P head + residual
+constexpr int kStage = (kFp4Batch * 17 + kThreads - 1) / kThreads;   // 16-byte chunks per thread
+constexpr int kOffBuf = 0;
+constexpr int kPSlots = kMaxTiles + kWinBatch / 32;        // FP4 tiles, then a window batch's tiles
+constexpr int kOffP = 2 * kBufBytes;                      // [10 slots][64 lanes][32 B]
+constexpr int kOffRowId = kOffP + kPSlots * 64 * kPBytes;   // [2][256] int32
+constexpr int kOffMax = kOffRowId + 2 * kFp4Batch * 4;    // [8 waves][16] float
+constexpr int kOffL = kOffMax + kWaves * 16 * 4;          // [8 waves][16] float
+constexpr int kLdsBytes = kOffL + kWaves * 16 * 4;
+static_assert(kWinBatch * kWinB <= kBufBytes, "window batch fits a buffer");
+static_assert(kMaxTiles == kWaves, "one FP4 tile per wave");
+static_assert(2 * kFp4Batch == kThreads, "one prefetched row id per thread (two FP4 batches)");
+static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
+static_assert(16 * kWinB <= kPSlots * 64 * kPBytes, "q of 16 heads fits the P slots");
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+struct DecArgs {
+  const uint8_t* lat_codes;
+  const uint8_t* lat_scales;
+  const int32_t* block_table;
+  int n_pages, max_pages;
+  const int32_t* len;      // decode: context length; prefill: tokens before the chunk
+  const uint16_t* q;
+  const int32_t* topk_idx;
+  int topk;
+  const uint16_t* win;     // decode: ring [B][W][512]; prefill: [B][W-1+C][512]
+  int W;
+  float scale_log2;        // sm_scale * log2(e)
+  uint16_t* out;
+  float* lse;
+  int vshift;              // token count -> visible entries: >> vshift
+  int B, C, H, HG, prefill, q_per_xcd;
+};
+
+// low halves of a and b -> (a.lo, b.lo); high halves -> (a.hi, b.hi)
+__device__ __forceinline__ uint32_t pack_lo(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x05040100u); }
+__device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x07060302u); }
+
+template <class T>
+__device__ __forceinline__ T lds_ld(const uint8_t* p) { return *reinterpret_cast<const T*>(p); }
+
+// Row of K-slot j for lane group g: rows 4g..4g+3, then 16+4g..16+4g+3.
+__device__ __forceinline__ int slot_row(int g, int j) { return j < 4 ? 4 * g + j : 16 + 4 * g + (j - 4); }
+
+// Window slot w (position t-W+1+w) holds a row, i.e. w < W and the position is >= 0.
+__device__ __forceinline__ bool win_valid(int W, int t, int w) { return w < W && t - (W - 1) + w >= 0; }
+
+// P operand (bf16 head + bf16 residual) of this lane's 8 scores (log2 units, -inf =
+// absent) against the running max m; adds the weights to l_part.
+__device__ __forceinline__ void make_p(const float (&z)[8], float m, float& l_part, u32x4& phi, u32x4& plo) {
+  const float mb = (m == -INFINITY) ? 0.f : m;
+  uint32_t h[4], r[4];
+#pragma unroll
+  for (int j = 0; j < 8; j += 2) {
+    const float p0 = exp2f(z[j] - mb), p1 = exp2f(z[j + 1] - mb);
+    l_part += p0 + p1;
+    const uint32_t h0 = f32_to_bf16_rne(p0), h1 = f32_to_bf16_rne(p1);
+    const uint32_t r0 = f32_to_bf16_rne(p0 - bf16_to_f32(h0));
+    const uint32_t r1 = f32_to_bf16_rne(p1 - bf16_to_f32(h1));
+    h[j >> 1] = h0 | (h1 << 16);
+    r[j >> 1] = r0 | (r1 << 16);
+  }
+  phi = u32x4{h[0], h[1], h[2], h[3]};
+  plo = u32x4{r[0], r[1], r[2], r[3]};
+}
+
+// Scores of the FP4 tile at row `base` of the batch in LDS.
+__device__ __forceinline__ void fp4_qk(const uint8_t* rows, const int32_t* rowid, int nrows, int base,
+                                       const u32x4 (&qf)[16], float scale_log2, float (&z)[8]) {
+  const int lane = threadIdx.x & 63;
+  const int n = lane & 15, g = lane >> 4;
+  u32x4 cd0[4], cd1[4];
+  const uint8_t* r0p = rows + (base + n) * kRowB;
+  const uint8_t* r1p = rows + (base + 16 + n) * kRowB;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    cd0[c] = lds_ld<u32x4>(r0p + 64 * g + 16 * c);
+    cd1[c] = lds_ld<u32x4>(r1p + 64 * g + 16 * c);
+  }
+  const uint32_t sb0 = lds_ld<uint32_t>(r0p + 256 + 4 * g);
+  const uint32_t sb1 = lds_ld<uint32_t>(r1p + 256 + 4 * g);
+  f32x4 sa[4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const float sc0 = e8m0_scale((sb0 >> (8 * c)) & 0xffu);
+    const float sc1 = e8m0_scale((sb1 >> (8 * c)) & 0xffu);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const bf16x8 qv = __builtin_bit_cast(bf16x8, qf[4 * c + k]);
+      const int e = k & 1;   // two partial sums per row half keep four MFMA chains in flight
+      sa[e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, fp4x8_to_bf16x8(cd0[c][k], sc0)),
+                                                      qv, sa[e], 0, 0, 0);
+      sa[2 + e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+          __builtin_bit_cast(bf16x8, fp4x8_to_bf16x8(cd1[c][k], sc1)), qv, sa[2 + e], 0, 0, 0);
+    }
+  }
+  const f32x4 s0 = sa[0] + sa[1], s1 = sa[2] + sa[3];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int r0 = base + slot_row(g, j), r1 = base + slot_row(g, 4 + j);
+    z[j] = (r0 < nrows && rowid[r0] >= 0) ? s0[j] * scale_log2 : -INFINITY;
+    z[4 + j] = (r1 < nrows && rowid[r1] >= 0) ? s1[j] * scale_log2 : -INFINITY;
+  }
+}
+
+// Scores of the window tile at row `base` of the batch in LDS (window slots w0 + row).
+__device__ __forceinline__ void win_qk(const uint8_t* wrows, int W, int t, int w0, int base, const u32x4 (&qf)[16],
+                                       float scale_log2, float (&z)[8]) {
+  const int lane = threadIdx.x & 63;
+  const int n = lane & 15, g = lane >> 4;
+  const uint8_t* r0p = wrows + (base + n) * kWinB + 256 * g;
+  const uint8_t* r1p = wrows + (base + 16 + n) * kWinB + 256 * g;
+  f32x4 sa[4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    u32x4 r0[8], r1[8];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      r0[s] = lds_ld<u32x4>(r0p + 16 * (8 * half + s));
+      r1[s] = lds_ld<u32x4>(r1p + 16 * (8 * half + s));
+    }
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const bf16x8 qv = __builtin_bit_cast(bf16x8, qf[8 * half + s]);
+      const int e = s & 1;
+      sa[e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, r0[s]), qv, sa[e], 0, 0, 0);
+      sa[2 + e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, r1[s]), qv, sa[2 + e], 0, 0, 0);
+    }
+  }
+  const f32x4 s0 = sa[0] + sa[1], s1 = sa[2] + sa[3];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    z[j] = win_valid(W, t, w0 + base + slot_row(g, j)) ? s0[j] * scale_log2 : -INFINITY;
+    z[4 + j] = win_valid(W, t, w0 + base + slot_row(g, 4 + j)) ? s1[j] * scale_log2 : -INFINITY;
+  }
+}
+
+// PV for this wave's 64 dims from 8 rows given as pairs d01[j] = dims (4n, 4n+1),
+// d23[j] = dims (4n+2, 4n+3) of row slot j: n-tile t holds dim 4n + t.
+__device__ __forceinline__ void pv4(f32x4 (&acc)[4], const uint32_t (&d01)[8], const uint32_t (&d23)[8], bf16x8 ph,
+                                    bf16x8 pl) {
+  bf16x8 bf[4];
+  bf[0] = __builtin_bit_cast(bf16x8, u32x4{pack_lo(d01[0], d01[1]), pack_lo(d01[2], d01[3]),
+                                           pack_lo(d01[4], d01[5]), pack_lo(d01[6], d01[7])});
+  bf[1] = __builtin_bit_cast(bf16x8, u32x4{pack_hi(d01[0], d01[1]), pack_hi(d01[2], d01[3]),
+                                           pack_hi(d01[4], d01[5]), pack_hi(d01[6], d01[7])});
+  bf[2] = __builtin_bit_cast(bf16x8, u32x4{pack_lo(d23[0], d23[1]), pack_lo(d23[2], d23[3]),
+                                           pack_lo(d23[4], d23[5]), pack_lo(d23[6], d23[7])});
+  bf[3] = __builtin_bit_cast(bf16x8, u32x4{pack_hi(d23[0], d23[1]), pack_hi(d23[2], d23[3]),
+                                           pack_hi(d23[4], d23[5]), pack_hi(d23[6], d23[7])});
+#pragma unroll
+  for (int t = 0; t < 4; ++t) acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph, bf[t], acc[t], 0, 0, 0);
+#pragma unroll
+  for (int t = 0; t < 4; ++t) acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, bf[t], acc[t], 0, 0, 0);
+}
+
+__global__ __launch_bounds__(kThreads) void sparse_decode_kernel(DecArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  uint8_t* plds = lds + kOffP;
+  int32_t* rowid_all = reinterpret_cast<int32_t*>(lds + kOffRowId);
+  float* m_part = reinterpret_cast<float*>(lds + kOffMax);
+  float* l_w = reinterpret_cast<float*>(lds + kOffL);
+
+  // XCD-aware mapping: consecutive workgroup ids go to different XCDs; XCD x takes
+  // the contiguous query range [x * q_per_xcd, (x+1) * q_per_xcd), all head groups.
+  const int xcd = blockIdx.x & 7;
+  const int li = blockIdx.x >> 3;
+  const int ql = li / a.HG;
+  const int hg = li - ql * a.HG;
+  const int64_t qi = (int64_t)xcd * a.q_per_xcd + ql;
+  if (ql >= a.q_per_xcd || qi >= (int64_t)a.B * a.C) return;
+  const int b = (int)(qi / a.C);
+  const int ci = (int)(qi - (int64_t)b * a.C);
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 15, g = lane >> 4;
+
+  // the workgroup's rows: window rows [wr0, wr1), FP4 rows [fr0, fr1) of topk_idx
+  const int wr0 = 0, wr1 = a.W, fr0 = 0, fr1 = a.topk;
+
+  int64_t Lq = a.len[b];
+  if (Lq < 0) Lq = 0;
+  if (a.prefill) Lq += ci + 1;   // chunk query ci sits at position prior + ci
+  const int n_vis = (int)(Lq >> a.vshift);
+  const int t = (int)Lq - 1;
+  const uint16_t* win_b = a.win + (int64_t)b * (a.prefill ? a.W - 1 + a.C : a.W) * CSA2_D_LATENT;
+  const int32_t* tk = a.topk_idx + qi * a.topk;
+  const int32_t* bt = a.block_table + (int64_t)b * a.max_pages;
+
+  const int n_wb = (wr1 - wr0 + kWinBatch - 1) / kWinBatch;
+  const int n_fb = (fr1 - fr0 + kFp4Batch - 1) / kFp4Batch;
+  const int nb = n_wb + n_fb;
+
+  // row id of entry e (-1: invalid id, absent page)
+  auto row_of = [&](int e, int page) -> int {
+    return (e >= 0 && e < n_vis && page >= 0 && page < a.n_pages) ? page * CSA2_PAGE + (e & (CSA2_PAGE - 1)) : -1;
+  };
+  auto page_ok = [&](int e) { return e >= 0 && e < n_vis && (e >> 6) < a.max_pages; };
+  // FP4 batch f >= 2: ids resolved when the batch is issued
+  auto resolve_rows = [&](int f) {
+    const int r0 = fr0 + f * kFp4Batch;
+    const int nrows = min(fr1 - r0, kFp4Batch);
+    int32_t* rowid = rowid_all + (f & 1) * kFp4Batch;
+    for (int i = tid; i < kFp4Batch; i += kThreads) {
+      const int e = i < nrows ? tk[r0 + i] : -1;
+      rowid[i] = page_ok(e) ? row_of(e, bt[e >> 6]) : -1;
+    }
+  };
+  // Batch k in registers: thread tid holds chunks c = tid + 512u (16 bytes each) of
+  // the batch image -- FP4: piece c%17 of row c/17 (16 code pieces, then the scales);
+  // window: piece c%64 of row c/64 -- zeros where no row is.  Every chunk is loaded
+  // (one with no row reads window row 0 of the sequence or cache row 0, and is
+  // dropped), so no branch splits the loads: they issue back to back.
+  auto load_batch = [&](int k, u32x4 (&st)[kStage]) {
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+    if (k < n_wb) {
+      const int w0 = wr0 + k * kWinBatch;
+      int slot0 = (t - (a.W - 1) + w0) % a.W;   // ring slot of the batch's first position
+      if (slot0 < 0) slot0 += a.W;
+#pragma unroll
+      for (int u = 0; u < kWinBatch * 64 / kThreads; ++u) {
+        const int c = tid + kThreads * u;
+        const int r = c >> 6, piece = c & 63;
+        const bool ok = w0 + r < wr1 && win_valid(a.W, t, w0 + r);
+        int row = a.prefill ? ci + w0 + r : (slot0 + r >= a.W ? slot0 + r - a.W : slot0 + r);
+        row = ok ? row : 0;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(win_b + (int64_t)row * CSA2_D_LATENT + 8 * piece);
+        st[u] = ok ? v : zero;
+      }
+#pragma unroll
+      for (int u = kWinBatch * 64 / kThreads; u < kStage; ++u) st[u] = zero;
+    } else {
+      const int f = k - n_wb;
+      const int nrows = min(fr1 - fr0 - f * kFp4Batch, kFp4Batch);
+      const int32_t* rowid = rowid_all + (f & 1) * kFp4Batch;
+      int rid[kStage];
+#pragma unroll
+      for (int u = 0; u < kStage; ++u) {
+        const int c = tid + kThreads * u;
+        rid[u] = rowid[min(c / 17, kFp4Batch - 1)];
+      }
+#pragma unroll
+      for (int u = 0; u < kStage; ++u) {
+        const int c = tid + kThreads * u;
+        const int r = c / 17, piece = c - r * 17;
+        const bool ok = c < kFp4Batch * 17 && r < nrows && rid[u] >= 0;
+        const int64_t rw = ok ? rid[u] : 0;
+        const uint8_t* src = piece < 16 ? a.lat_codes + rw * CSA2_LAT_CODE_BYTES + 16 * piece
+                                        : a.lat_scales + rw * CSA2_LAT_SCALE_BYTES;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(src);
+        st[u] = ok ? v : zero;
+      }
+    }
+  };
+  auto store_batch = [&](int k, const u32x4 (&st)[kStage]) {
+    uint8_t* buf = lds + kOffBuf + (k & 1) * kBufBytes;
+    if (k < n_wb) {
+#pragma unroll
+      for (int u = 0; u < kWinBatch * 64 / kThreads; ++u) {
+        const int c = tid + kThreads * u;
+        *reinterpret_cast<u32x4*>(buf + (c >> 6) * kWinB + (c & 63) * 16) = st[u];
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < kStage; ++u) {
+        const int c = tid + kThreads * u;
+        if (c < kFp4Batch * 17) *reinterpret_cast<u32x4*>(buf + c * 16) = st[u];
+      }
+    }
+  };
+
+  // ---- start: the entry ids of the first two FP4 batches (thread tid: batch tid/256,
+  // row tid%256) go out first, then batch 0 (window rows need no lookups) and q.  The
+  // ids' page lookups are issued as soon as the ids land, while the rest is in flight.
+  u32x4 st[kStage];
+  const int pf_i = tid & (kFp4Batch - 1), pf_f = tid >> 8;
+  const int pf_r = fr0 + pf_f * kFp4Batch + pf_i;
+  const int pf_e = (pf_f < n_fb && pf_r < fr1) ? tk[pf_r] : -1;
+  // q of the 16 heads is read from memory once per workgroup -- thread tid: head
+  // tid/32, dims 16(tid%32) .. +15 -- and handed to the waves through the P slots,
+  // which are free until the first P (rows at the window pitch, as win_qk reads them).
+  u32x4 qs[2];
+  {
+    const uint16_t* qp = a.q + (qi * a.H + hg * 16 + (tid >> 5)) * CSA2_D_LATENT + 16 * (tid & 31);
+    qs[0] = *reinterpret_cast<const u32x4*>(qp);
+    qs[1] = *reinterpret_cast<const u32x4*>(qp + 8);
+  }
+  // W >= 1 (checked by the launcher), so the run starts with a window batch, which
+  // needs no lookups; the ids' page lookups are issued behind it.
+  load_batch(0, st);
+  int pf_page = -1;
+  if (page_ok(pf_e)) pf_page = bt[pf_e >> 6];
+  store_batch(0, st);
+  // q and the entry ids have arrived before the loop starts: the wait counts inside
+  // the loop then cover only the next batch's loads, which stay in flight until the
+  // batch is stored after PV.
+  __builtin_amdgcn_s_waitcnt(0);
+  {
+    uint8_t* qd = plds + (tid >> 5) * kWinB + 32 * (tid & 31);
+    *reinterpret_cast<u32x4*>(qd) = qs[0];
+    *reinterpret_cast<u32x4*>(qd + 16) = qs[1];
+  }
+  u32x4 qf[16];   // q operand of head hg*16+n: dims 128g + 8s .. +7 for k-step s
+  auto read_q = [&]() {   // after a barrier that follows the stores above
+    const uint8_t* qp = plds + n * kWinB + 256 * g;
+#pragma unroll
+    for (int s = 0; s < 16; ++s) qf[s] = lds_ld<u32x4>(qp + 16 * s);
+  };
+
+  f32x4 acc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_part = 0.f;
+
+  // PV of one 32-row tile of a batch in LDS (window rows: bf16; else FP4), this wave's
+  // 64 dims, with the P operand from P slot ps.
+  auto pv_tile = [&](const uint8_t* buf, bool win, int tile, int ps) {
+    const uint8_t* pp = plds + (ps * 64 + lane) * kPBytes;
+    const bf16x8 ph = __builtin_bit_cast(bf16x8, lds_ld<u32x4>(pp));
+    const bf16x8 pl = __builtin_bit_cast(bf16x8, lds_ld<u32x4>(pp + 16));
+    uint32_t d01[8], d23[8];
+    if (win) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const u32x2 v = lds_ld<u32x2>(buf + (tile * 32 + slot_row(g, j)) * kWinB + 128 * wid + 8 * n);
+        d01[j] = v.x;
+        d23[j] = v.y;
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const uint8_t* rp = buf + (tile * 32 + slot_row(g, j)) * kRowB;
+        const uint32_t c2 = lds_ld<uint16_t>(rp + 32 * wid + 2 * n);
+        const float sc = e8m0_scale(rp[256 + 2 * wid + (n >> 3)]);
+        d01[j] = fp4x2_to_bf16x2<0>(c2, sc);
+        d23[j] = fp4x2_to_bf16x2<1>(c2, sc);
+      }
+    }
+    pv4(acc, d01, d23, ph, pl);
+  };
+  auto put_p = [&](const float (&z)[8], float m, int ps) {
+    u32x4 ph, pl;
+    make_p(z, m, l_part, ph, pl);
+    uint8_t* pp = plds + (ps * 64 + lane) * kPBytes;
+    *reinterpret_cast<u32x4*>(pp) = ph;
+    *reinterpret_cast<u32x4*>(pp + 16) = pl;
+  };
+
+  if (n_wb == 1 && n_fb == 1) {
+    // One window batch (buffer 0, stored in the prologue) and one FP4 batch (buffer 1)
+    // in a single pass: the window tiles are scored while the FP4 rows load, then one
+    // softmax and one PV cover all tiles.
+    uint8_t* bufw = lds + kOffBuf;
+    uint8_t* buff = lds + kOffBuf + kBufBytes;
+    const int ntl_w = (min(wr1 - wr0, kWinBatch) + 31) >> 5;
+    const int nrows_f = min(fr1 - fr0, kFp4Batch);
+    const int ntl_f = (nrows_f + 31) >> 5;
+    rowid_all[tid] = row_of(pf_e, pf_page);
+    __syncthreads();   // window rows, q and the FP4 row ids stored by every thread
+    load_batch(1, st);   // FP4 rows: in flight while the window tiles are scored
+    read_q();
+    float zw[8], zf[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) zw[j] = zf[j] = -INFINITY;
+    if (wid < ntl_w) win_qk(bufw, a.W, t, wr0, wid * 32, qf, a.scale_log2, zw);
+    store_batch(1, st);
+    __syncthreads();   // FP4 rows stored by every thread
+    if (wid < ntl_f) fp4_qk(buff, rowid_all, nrows_f, wid * 32, qf, a.scale_log2, zf);
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) tmax = fmaxf(tmax, fmaxf(zw[j], zf[j]));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, kWave));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
+    if (g == 0) m_part[wid * 16 + n] = tmax;
+    __syncthreads();
+    float mb = m_part[n];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) mb = fmaxf(mb, m_part[w * 16 + n]);
+    if (wid < ntl_f) put_p(zf, mb, wid);
+    if (wid < ntl_w) put_p(zw, mb, kMaxTiles + wid);
+    m_run = mb;
+    __syncthreads();
+#pragma unroll 1
+    for (int tile = 0; tile < ntl_w; ++tile) pv_tile(bufw, true, tile, kMaxTiles + tile);
+#pragma unroll 1
+    for (int tile = 0; tile < ntl_f; ++tile) pv_tile(buff, false, tile, tile);
+  } else {
+  __syncthreads();   // q stored by every thread
+  read_q();
+#pragma unroll 1
+  for (int k = 0; k < nb; ++k) {
+    const bool is_win = k < n_wb;
+    uint8_t* buf = lds + kOffBuf + (k & 1) * kBufBytes;
+    const int f = k - n_wb;
+    const int w0 = wr0 + k * kWinBatch;
+    const int nrows = is_win ? min(wr1 - w0, kWinBatch) : min(fr1 - fr0 - f * kFp4Batch, kFp4Batch);
+    const int32_t* rowid = rowid_all + (f & 1) * kFp4Batch;
+    const int ntl = (nrows + 31) >> 5;
+
+    __syncthreads();   // batch k stored by every thread; batch k-1 fully consumed
+    // Batch k+1 is loaded now if its rows are known (a window batch, or the second FP4
+    // batch whose ids came with the first); otherwise its row ids are resolved after
+    // this batch's QK, which hides the lookups, and it is loaded after the next barrier.
+    const int f1 = k + 1 - n_wb;
+    const bool has_next = k + 1 < nb;
+    const bool ids_later = has_next && (f1 == 0 || f1 >= 2);
+    if (has_next && !ids_later) load_batch(k + 1, st);   // stored after this batch's PV
+
+    // ---- QK: wave w scores tile w ----
+    float z[8];
+    if (wid < ntl) {
+      if (is_win)
+        win_qk(buf, a.W, t, w0, wid * 32, qf, a.scale_log2, z);
+      else
+        fp4_qk(buf, rowid, nrows, wid * 32, qf, a.scale_log2, z);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) z[j] = -INFINITY;
+    }
+    float tmax = z[0];
+#pragma unroll
+    for (int j = 1; j < 8; ++j) tmax = fmaxf(tmax, z[j]);
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, kWave));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
+    if (g == 0) m_part[wid * 16 + n] = tmax;
+    if (ids_later) {
+      if (f1 == 0)
+        rowid_all[tid] = row_of(pf_e, pf_page);   // the two prefetched FP4 batches
+      else
+        resolve_rows(f1);
+    }
+    __syncthreads();
+    if (ids_later) load_batch(k + 1, st);
+
+    // ---- batch max of head n (identical in every wave), P for the scored tile ----
+    float mb = m_part[n];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) mb = fmaxf(mb, m_part[w * 16 + n]);
+    const float m_new = fmaxf(m_run, mb);
+    const float fac = (m_run == -INFINITY || m_new == m_run) ? 1.f : exp2f(m_run - m_new);
+    l_part *= fac;
+    if (wid < ntl) put_p(z, m_new, wid);
+    // rescale: acc[t][i] belongs to head 4g+i, whose factor lives in lane 4g+i
+    {
+      float fo[4];
+      bool any = false;
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        fo[ii] = __shfl(fac, 4 * g + ii, kWave);
+        any = any || fo[ii] != 1.f;
+      }
+      if (__any(any)) {
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+#pragma unroll
+          for (int ii = 0; ii < 4; ++ii) acc[tt][ii] *= fo[ii];
+        }
+      }
+    }
+    m_run = m_new;
+    __syncthreads();
+
+    // ---- PV over every tile of the batch, this wave's 64 dims ----
+#pragma unroll 1
+    for (int tile = 0; tile < ntl; ++tile) pv_tile(buf, is_win, tile, tile);
+    if (k + 1 < nb) store_batch(k + 1, st);   // into the other buffer, free since batch k began
+  }
+  }
+
+  // ---- softmax denominators, output ----
+  float l_head = l_part;
+  l_head += __shfl_xor(l_head, 16, kWave);
+  l_head += __shfl_xor(l_head, 32, kWave);
+  if (g == 0) l_w[wid * 16 + n] = l_head;
+  __syncthreads();
+  float lh[4];
+#pragma unroll
+  for (int ii = 0; ii < 4; ++ii) {
+    float s = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) s += l_w[w * 16 + 4 * g + ii];
+    lh[ii] = s;
+  }
+#pragma unroll
+  for (int ii = 0; ii < 4; ++ii) {
+    const float inv = lh[ii] > 0.f ? 1.f / lh[ii] : 0.f;
+    const uint32_t v0 = f32_to_bf16_rne(acc[0][ii] * inv), v1 = f32_to_bf16_rne(acc[1][ii] * inv);
+    const uint32_t v2 = f32_to_bf16_rne(acc[2][ii] * inv), v3 = f32_to_bf16_rne(acc[3][ii] * inv);
+    *reinterpret_cast<u32x2*>(a.out + (qi * a.H + hg * 16 + 4 * g + ii) * CSA2_D_LATENT + 64 * wid + 4 * n) =
+        u32x2{v0 | (v1 << 16), v2 | (v3 << 16)};
+  }
+  if (a.lse && wid == 0 && g == 0) {
+    float s = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) s += l_w[w * 16 + n];
+    a.lse[qi * a.H + hg * 16 + n] = s > 0.f ? (m_run + log2f(s)) * kLn2 : -INFINITY;
+  }
+}
+
+
+// ---------------------------------------------------------------------------------
+// All 64 heads of a query in one workgroup (H a multiple of 64).  The 16-head
+// kernel above converts every FP4 element once per head group; here the PV operand
+// of a row is converted once and feeds the MFMAs of all four head groups, and every
+// row is read from memory once per query instead of four times.
+//   batches  window batches of 32 rows and FP4 batches of 128 rows (one 34 KB
+//            buffer each), double-buffered, staged through registers as above.
+//   QK       unit (tile t, head group h) = the scores of 16 heads x 32 rows; wave w
+//            takes head group w%4 (its q fragments stay in registers) and tiles
+//            w/4 and w/4 + 2 of the batch.
+//   max, P   per head group through LDS, as above; P of every unit is parked in LDS.
+//   PV       wave w accumulates O[64 heads][dims 64w..64w+63] (64 registers): per
+//            tile it converts its 8 rows x 4 dims once and runs the 2 x 4 MFMAs of
+//            each of the four head groups on them.
+// ---------------------------------------------------------------------------------
+constexpr int kG4 = 4;                                    // head groups per workgroup
+constexpr int64_t kH64MinQueries = 512;                   // launches with fewer queries use 16 heads
+constexpr int kFb64 = 128;                                // FP4 rows per batch (4 tiles)
+constexpr int kWb64 = 32;                                 // window rows per batch (1 tile)
+constexpr int kTiles64 = kFb64 / 32;
+constexpr int kBuf64 = kFb64 * kRowB;                     // 34816 >= kWb64 * kWinB
+constexpr int kStage64 = (kFb64 * 17 + kThreads - 1) / kThreads;
+constexpr int kPf64 = 4;                                  // FP4 batches whose ids are prefetched
+constexpr int kOff64P = 2 * kBuf64;                       // [4 tiles][4 groups][64 lanes][32 B]
+constexpr int kOff64RowId = kOff64P + kTiles64 * kG4 * 64 * kPBytes;   // [4][128] int32
+constexpr int kOff64Max = kOff64RowId + kPf64 * kFb64 * 4;           // [8 waves][16] float
+constexpr int kOff64L = kOff64Max + kWaves * 16 * 4;                  // [8 waves][16] float
+constexpr int kLds64 = kOff64L + kWaves * 16 * 4;
+static_assert(kWb64 * kWinB <= kBuf64, "window batch fits a buffer");
+static_assert(kPf64 * kFb64 == kThreads, "one prefetched row id per thread");
+static_assert(kTiles64 * kG4 == 2 * kWaves, "two QK units per wave");
+static_assert(kLds64 <= 160 * 1024, "LDS budget");
+
+__global__ __launch_bounds__(kThreads) void sparse_decode64_kernel(DecArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  uint8_t* plds = lds + kOff64P;
+  int32_t* rowid_all = reinterpret_cast<int32_t*>(lds + kOff64RowId);
+  float* m_part = reinterpret_cast<float*>(lds + kOff64Max);
+  float* l_w = reinterpret_cast<float*>(lds + kOff64L);
+
+  // XCD-aware mapping: XCD x takes the contiguous query range [x * q_per_xcd, ...).
+  const int xcd = blockIdx.x & 7;
+  const int li = blockIdx.x >> 3;
+  const int nhq = a.H / 64;                     // workgroups per query
+  const int ql = li / nhq;
+  const int hq = li - ql * nhq;                 // heads 64hq .. 64hq+63
+  const int64_t qi = (int64_t)xcd * a.q_per_xcd + ql;
+  if (ql >= a.q_per_xcd || qi >= (int64_t)a.B * a.C) return;
+  const int b = (int)(qi / a.C);
+  const int ci = (int)(qi - (int64_t)b * a.C);
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 15, g = lane >> 4;
+  const int my_hg = wid & 3;                    // head group of this wave's QK units
+
+  int64_t Lq = a.len[b];
+  if (Lq < 0) Lq = 0;
+  if (a.prefill) Lq += ci + 1;
+  const int n_vis = (int)(Lq >> a.vshift);
+  const int t = (int)Lq - 1;
+  const uint16_t* win_b = a.win + (int64_t)b * (a.prefill ? a.W - 1 + a.C : a.W) * CSA2_D_LATENT;
+  const int32_t* tk = a.topk_idx + qi * a.topk;
+  const int32_t* bt = a.block_table + (int64_t)b * a.max_pages;
+
+  const int n_wb = (a.W + kWb64 - 1) / kWb64;
+  const int n_fb = a.topk > 0 ? (a.topk + kFb64 - 1) / kFb64 : 0;
+  const int nb = n_wb + n_fb;
+
+  auto row_of = [&](int e, int page) -> int {
+    return (e >= 0 && e < n_vis && page >= 0 && page < a.n_pages) ? page * CSA2_PAGE + (e & (CSA2_PAGE - 1)) : -1;
+  };
+  auto page_ok = [&](int e) { return e >= 0 && e < n_vis && (e >> 6) < a.max_pages; };
+  auto resolve_rows = [&](int f) {   // FP4 batch f >= kPf64, into slot f % kPf64
+    const int r0 = f * kFb64;
+    const int nrows = min(a.topk - r0, kFb64);
+    int32_t* rowid = rowid_all + (f % kPf64) * kFb64;
+    for (int i = tid; i < kFb64; i += kThreads) {
+      const int e = i < nrows ? tk[r0 + i] : -1;
+      rowid[i] = page_ok(e) ? row_of(e, bt[e >> 6]) : -1;
+    }
+  };
+  // Every chunk is loaded, as in the 16-head kernel: no branch splits the loads.
+  auto load_batch = [&](int k, u32x4 (&st)[kStage64]) {
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+    if (k < n_wb) {
+      const int w0 = k * kWb64;
+      int slot0 = (t - (a.W - 1) + w0) % a.W;
+      if (slot0 < 0) slot0 += a.W;
+#pragma unroll
+      for (int u = 0; u < kWb64 * 64 / kThreads; ++u) {
+        const int c = tid + kThreads * u;
+        const int r = c >> 6, piece = c & 63;
+        const bool ok = win_valid(a.W, t, w0 + r);
+        int row = a.prefill ? ci + w0 + r : (slot0 + r >= a.W ? slot0 + r - a.W : slot0 + r);
+        row = ok ? row : 0;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(win_b + (int64_t)row * CSA2_D_LATENT + 8 * piece);
+        st[u] = ok ? v : zero;
+      }
+#pragma unroll
+      for (int u = kWb64 * 64 / kThreads; u < kStage64; ++u) st[u] = zero;
+    } else {
+      const int f = k - n_wb;
+      const int nrows = min(a.topk - f * kFb64, kFb64);
+      const int32_t* rowid = rowid_all + (f % kPf64) * kFb64;
+      int rid[kStage64];
+#pragma unroll
+      for (int u = 0; u < kStage64; ++u) {
+        const int c = tid + kThreads * u;
+        rid[u] = rowid[min(c / 17, kFb64 - 1)];
+      }
+#pragma unroll
+      for (int u = 0; u < kStage64; ++u) {
+        const int c = tid + kThreads * u;
+        const int r = c / 17, piece = c - r * 17;
+        const bool ok = c < kFb64 * 17 && r < nrows && rid[u] >= 0;
+        const int64_t rw = ok ? rid[u] : 0;
+        const uint8_t* src = piece < 16 ? a.lat_codes + rw * CSA2_LAT_CODE_BYTES + 16 * piece
+                                        : a.lat_scales + rw * CSA2_LAT_SCALE_BYTES;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(src);
+        st[u] = ok ? v : zero;
+      }
+    }
+  };
+  auto store_batch = [&](int k, const u32x4 (&st)[kStage64]) {
+    uint8_t* buf = lds + (k & 1) * kBuf64;
+    if (k < n_wb) {
+#pragma unroll
+      for (int u = 0; u < kWb64 * 64 / kThreads; ++u) {
+        const int c = tid + kThreads * u;
+        *reinterpret_cast<u32x4*>(buf + (c >> 6) * kWinB + (c & 63) * 16) = st[u];
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < kStage64; ++u) {
+        const int c = tid + kThreads * u;
+        if (c < kFb64 * 17) *reinterpret_cast<u32x4*>(buf + c * 16) = st[u];
+      }
+    }
+  };
+
+  // ---- start ----
+  u32x4 st[kStage64];
+  if (n_wb > 0) load_batch(0, st);
+  const int pf_f = tid / kFb64, pf_r = tid;     // prefetched id: FP4 batch tid/128, row tid%128
+  const int pf_e = (pf_f < n_fb && pf_r < a.topk) ? tk[pf_r] : -1;
+  u32x4 qf[16];   // q operand of head 64hq + 16*my_hg + n: dims 128g + 8s .. +7
+  {
+    const uint16_t* qp = a.q + (qi * a.H + 64 * hq + 16 * my_hg + n) * CSA2_D_LATENT + 128 * g;
+#pragma unroll
+    for (int s = 0; s < 16; ++s) qf[s] = *reinterpret_cast<const u32x4*>(qp + 8 * s);
+  }
+  int pf_page = -1;
+  if (n_wb > 0) store_batch(0, st);
+  __builtin_amdgcn_s_waitcnt(0);
+
+  f32x4 acc[kG4][4];
+#pragma unroll
+  for (int h = 0; h < kG4; ++h)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[h][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run[kG4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};   // head n of group h
+  float l_part = 0.f;                                                 // head n of my_hg
+
+#pragma unroll 1
+  for (int k = 0; k < nb; ++k) {
+    const bool is_win = k < n_wb;
+    uint8_t* buf = lds + (k & 1) * kBuf64;
+    const int f = k - n_wb;
+    const int w0 = k * kWb64;
+    const int nrows = is_win ? min(a.W - w0, kWb64) : min(a.topk - f * kFb64, kFb64);
+    const int32_t* rowid = rowid_all + (f % kPf64) * kFb64;
+    const int ntl = (nrows + 31) >> 5;
+
+    __syncthreads();   // batch k stored by every thread; batch k-1 fully consumed
+    if (k == 0 && page_ok(pf_e)) pf_page = bt[pf_e >> 6];
+    if (k + 1 < nb) {
+      const int f1 = k + 1 - n_wb;
+      if (f1 == 0) {
+        rowid_all[tid] = row_of(pf_e, pf_page);
+        __syncthreads();
+      } else if (f1 >= kPf64) {
+        resolve_rows(f1);
+        __syncthreads();
+      }
+      load_batch(k + 1, st);
+    }
+
+    // ---- QK: units (tile w/4, group w%4) and (tile w/4 + 2, group w%4) ----
+    const int t0 = wid >> 2, t1 = t0 + 2;
+    float z0[8], z1[8];
+    if (t0 < ntl) {
+      if (is_win)
+        win_qk(buf, a.W, t, w0, t0 * 32, qf, a.scale_log2, z0);
+      else
+        fp4_qk(buf, rowid, nrows, t0 * 32, qf, a.scale_log2, z0);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) z0[j] = -INFINITY;
+    }
+    if (t1 < ntl) {
+      fp4_qk(buf, rowid, nrows, t1 * 32, qf, a.scale_log2, z1);   // window batches hold one tile
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) z1[j] = -INFINITY;
+    }
+    float tmax = z0[0];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) tmax = fmaxf(tmax, fmaxf(z0[j], z1[j]));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, kWave));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
+    if (g == 0) m_part[wid * 16 + n] = tmax;
+    __syncthreads();
+
+    // ---- per-group batch max of head n, P of this wave's units ----
+    float fac[kG4];
+#pragma unroll
+    for (int h = 0; h < kG4; ++h) {
+      const float mb = fmaxf(m_part[h * 16 + n], m_part[(h + 4) * 16 + n]);
+      const float m_new = fmaxf(m_run[h], mb);
+      fac[h] = (m_run[h] == -INFINITY || m_new == m_run[h]) ? 1.f : exp2f(m_run[h] - m_new);
+      m_run[h] = m_new;
+    }
+    float my_fac = fac[0], my_m = m_run[0];
+#pragma unroll
+    for (int h = 1; h < kG4; ++h)
+      if (my_hg == h) {
+        my_fac = fac[h];
+        my_m = m_run[h];
+      }
+    l_part *= my_fac;
+    if (t0 < ntl) {
+      u32x4 ph, pl;
+      make_p(z0, my_m, l_part, ph, pl);
+      uint8_t* pp = plds + ((t0 * kG4 + my_hg) * 64 + lane) * kPBytes;
+      *reinterpret_cast<u32x4*>(pp) = ph;
+      *reinterpret_cast<u32x4*>(pp + 16) = pl;
+    }
+    if (t1 < ntl) {
+      u32x4 ph, pl;
+      make_p(z1, my_m, l_part, ph, pl);
+      uint8_t* pp = plds + ((t1 * kG4 + my_hg) * 64 + lane) * kPBytes;
+      *reinterpret_cast<u32x4*>(pp) = ph;
+      *reinterpret_cast<u32x4*>(pp + 16) = pl;
+    }
+    // rescale: acc[h][t][i] belongs to head 4g+i of group h, factor in lane 4g+i
+#pragma unroll
+    for (int h = 0; h < kG4; ++h) {
+      float fo[4];
+      bool any = false;
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        fo[ii] = __shfl(fac[h], 4 * g + ii, kWave);
+        any = any || fo[ii] != 1.f;
+      }
+      if (__any(any)) {
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+          for (int ii = 0; ii < 4; ++ii) acc[h][tt][ii] *= fo[ii];
+      }
+    }
+    __syncthreads();
+
+    // ---- PV: convert each tile's rows once, MFMAs for all four head groups ----
+#pragma unroll 1
+    for (int tile = 0; tile < ntl; ++tile) {
+      uint32_t d01[8], d23[8];
+      if (is_win) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const u32x2 v = lds_ld<u32x2>(buf + (tile * 32 + slot_row(g, j)) * kWinB + 128 * wid + 8 * n);
+          d01[j] = v.x;
+          d23[j] = v.y;
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const uint8_t* rp = buf + (tile * 32 + slot_row(g, j)) * kRowB;
+          const uint32_t c2 = lds_ld<uint16_t>(rp + 32 * wid + 2 * n);
+          const float sc = e8m0_scale(rp[256 + 2 * wid + (n >> 3)]);
+          d01[j] = fp4x2_to_bf16x2<0>(c2, sc);
+          d23[j] = fp4x2_to_bf16x2<1>(c2, sc);
+        }
+      }
+      bf16x8 bf[4];
+      bf[0] = __builtin_bit_cast(bf16x8, u32x4{pack_lo(d01[0], d01[1]), pack_lo(d01[2], d01[3]),
+                                               pack_lo(d01[4], d01[5]), pack_lo(d01[6], d01[7])});
+      bf[1] = __builtin_bit_cast(bf16x8, u32x4{pack_hi(d01[0], d01[1]), pack_hi(d01[2], d01[3]),
+                                               pack_hi(d01[4], d01[5]), pack_hi(d01[6], d01[7])});
+      bf[2] = __builtin_bit_cast(bf16x8, u32x4{pack_lo(d23[0], d23[1]), pack_lo(d23[2], d23[3]),
+                                               pack_lo(d23[4], d23[5]), pack_lo(d23[6], d23[7])});
+      bf[3] = __builtin_bit_cast(bf16x8, u32x4{pack_hi(d23[0], d23[1]), pack_hi(d23[2], d23[3]),
+                                               pack_hi(d23[4], d23[5]), pack_hi(d23[6], d23[7])});
+#pragma unroll
+      for (int h = 0; h < kG4; ++h) {
+        const uint8_t* pp = plds + ((tile * kG4 + h) * 64 + lane) * kPBytes;
+        const bf16x8 ph = __builtin_bit_cast(bf16x8, lds_ld<u32x4>(pp));
+        const bf16x8 pl = __builtin_bit_cast(bf16x8, lds_ld<u32x4>(pp + 16));
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt)
+          acc[h][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph, bf[tt], acc[h][tt], 0, 0, 0);
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt)
+          acc[h][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, bf[tt], acc[h][tt], 0, 0, 0);
+      }
+    }
+    if (k + 1 < nb) store_batch(k + 1, st);
+  }
+
+  // ---- softmax denominators (group h: waves h and h+4), output ----
+  float l_head = l_part;
+  l_head += __shfl_xor(l_head, 16, kWave);
+  l_head += __shfl_xor(l_head, 32, kWave);
+  if (g == 0) l_w[wid * 16 + n] = l_head;
+  __syncthreads();
+#pragma unroll
+  for (int h = 0; h < kG4; ++h) {
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) {
+      const float lh = l_w[h * 16 + 4 * g + ii] + l_w[(h + 4) * 16 + 4 * g + ii];
+      const float inv = lh > 0.f ? 1.f / lh : 0.f;
+      const uint32_t v0 = f32_to_bf16_rne(acc[h][0][ii] * inv), v1 = f32_to_bf16_rne(acc[h][1][ii] * inv);
+      const uint32_t v2 = f32_to_bf16_rne(acc[h][2][ii] * inv), v3 = f32_to_bf16_rne(acc[h][3][ii] * inv);
+      *reinterpret_cast<u32x2*>(a.out + (qi * a.H + 64 * hq + 16 * h + 4 * g + ii) * CSA2_D_LATENT + 64 * wid +
+                                4 * n) = u32x2{v0 | (v1 << 16), v2 | (v3 << 16)};
+    }
+  }
+  if (a.lse && wid < kG4 && g == 0) {
+    const float s = l_w[wid * 16 + n] + l_w[(wid + 4) * 16 + n];
+    a.lse[qi * a.H + 64 * hq + 16 * wid + n] = s > 0.f ? (m_run[0] * (wid == 0) + m_run[1] * (wid == 1) +
+                                                          m_run[2] * (wid == 2) + m_run[3] * (wid == 3) +
+                                                          log2f(s)) * kLn2
+                                                       : -INFINITY;
+  }
+}
+
+bool lds_limit_set() {
+  static const bool ok =
+      hipFuncSetAttribute(reinterpret_cast<const void*>(sparse_decode_kernel),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes) == hipSuccess &&
+      hipFuncSetAttribute(reinterpret_cast<const void*>(sparse_decode64_kernel),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, kLds64) == hipSuccess;
+  return ok;
+}
+
+}  // namespace
+
+bool attention_batch_ready() { return lds_limit_set(); }
+
+int launch_attention_batch(const csa2_cache_t& c, int B, int C, int H, const int32_t* len, bool prefill,
+                           const uint16_t* q, const int32_t* topk_idx, int topk, const uint16_t* win, int W,
+                           float sm_scale, uint16_t* out, float* lse, hipStream_t s) {
+  if (!lds_limit_set()) return CSA2_EHIP;
+  DecArgs a;
+  a.lat_codes = c.lat_codes;
+  a.lat_scales = c.lat_scales;
+  a.block_table = c.block_table;
+  a.n_pages = c.n_pages;
+  a.max_pages = c.max_pages;
+  a.len = len;
+  a.q = q;
+  a.topk_idx = topk_idx;
+  a.topk = topk;
+  a.win = win;
+  a.W = W;
+  a.scale_log2 = sm_scale * kLog2e;
+  a.out = out;
+  a.lse = lse;
+  a.B = B;
+  a.C = C;
+  a.H = H;
+  a.HG = H / 16;
+  a.prefill = prefill ? 1 : 0;
+  a.vshift = vis_shift(c);
+  const int64_t nq = (int64_t)B * C;
+  const int64_t per = (nq + 7) / 8;
+  a.q_per_xcd = (int)per;
+  // 64 heads per workgroup do more arithmetic per byte but four times the work per
+  // workgroup: worth it once the queries alone give every CU a couple of workgroups.
+  if (H % 64 == 0 && nq >= kH64MinQueries) {
+    const int64_t grid = 8 * per * (H / 64);
+    if (grid > 0x7fffffff) return CSA2_EUNSUPPORTED;
+    hipLaunchKernelGGL(sparse_decode64_kernel, dim3((unsigned)grid), dim3(kThreads), kLds64, s, a);
+    return hip_status();
+  }
+  const int64_t grid = 8 * per * a.HG;
+  if (grid > 0x7fffffff) return CSA2_EUNSUPPORTED;
+  hipLaunchKernelGGL(sparse_decode_kernel, dim3((unsigned)grid), dim3(kThreads), kLdsBytes, s, a);
+  return hip_status();
+}
+
+}  // namespace csa2

@@ -51,10 +51,9 @@ size_t reindex_ws(int B);
 int launch_reindex(const csa2_cache_t& c, int B, const int32_t* ctx_len, const uint16_t* q_idx,
                    const uint16_t* w_idx, const int32_t* pool, int pool_blocks, int cand_block,
                    int topk, int32_t* topk_idx, void* ws, size_t ws_bytes, hipStream_t s);
-// Sparse decode: with a workspace of sparse_decode_ws(B, H, topk) bytes, launches
-// with fewer (query, head group) pairs than CUs spread each pair's rows over several
-// workgroups and merge their partial softmax states; without one, one workgroup per
-// pair.
+// Sparse decode needs no workspace (sparse_decode_ws returns 0; the ABI keeps the
+// argument): launches with few (query, head group) pairs split the output dims, not
+// the rows, over several workgroups.
 size_t sparse_decode_ws(int B, int H, int topk);
 int launch_sparse_decode(const csa2_cache_t& c, int B, int H, const int32_t* ctx_len,
                          const uint16_t* q, const int32_t* topk_idx, int topk, const uint16_t* swa,
@@ -62,11 +61,17 @@ int launch_sparse_decode(const csa2_cache_t& c, int B, int H, const int32_t* ctx
                          hipStream_t s);
 // The attention kernel for B*C queries: C = 1 and prefill = false is the decode
 // call; prefill = true reads query positions as len[b] + chunk index and window
-// rows from a [B][W-1+C][512] array.  ws (optional) holds split partials.
+// rows from a [B][W-1+C][512] array.  ws is unused.
 int launch_gather_attention(const csa2_cache_t& c, int B, int C, int H, const int32_t* len, bool prefill,
                             const uint16_t* q, const int32_t* topk_idx, int topk, const uint16_t* win,
                             int W, float sm_scale, uint16_t* out, float* lse, hipStream_t s,
                             void* ws = nullptr, size_t ws_bytes = 0);
+// The batched attention kernels (attention_batch.hip), for launches with many
+// (query, head group) pairs; same arguments and result as launch_gather_attention.
+int launch_attention_batch(const csa2_cache_t& c, int B, int C, int H, const int32_t* len, bool prefill,
+                           const uint16_t* q, const int32_t* topk_idx, int topk, const uint16_t* win, int W,
+                           float sm_scale, uint16_t* out, float* lse, hipStream_t s);
+bool attention_batch_ready();
 size_t prefill_ws(int B, int H, int64_t max_ctx, int topk, int C);
 int launch_prefill_chunk(const csa2_cache_t& c, int B, int H, const int32_t* prior_len,
                          int64_t max_ctx, int C, const uint16_t* q, const uint16_t* q_idx,

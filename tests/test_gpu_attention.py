@@ -30,20 +30,22 @@ def _oracle_topk(case, oc, layer, topk):
     return out
 
 
-def _no_ws():
-    """A zero-byte workspace: one workgroup per (sequence, head group), no split."""
-    return torch.empty(0, dtype=torch.uint8, device="cuda")
-
-
-@pytest.mark.parametrize("split", [True, False], ids=["split", "whole"])
+# The launcher picks the kernel instance from the number of (sequence, 16-head
+# group) pairs: under 128 pairs each pair's output dims go to four workgroups, from
+# 128 to two, from 512 on the batched kernels run (64 heads per workgroup with >= 512
+# queries).  A wave holds two FP4 tiles at a time; top-K 2048 makes it refill its
+# slots, and a window of 1024 gives every wave several window units.
 @pytest.mark.parametrize("ctx,H,topk,W", [
     ((2048,), 16, 512, 128),                    # config-0 shape
     ((65536, 300, 4000, 100), 64, 512, 128),    # config-1 length, short contexts, ragged tiles
     ((9000, 18), 32, 100, 37),                  # ragged top-K and window
-    ((5000,), 16, 2048, 128),                   # eight FP4 batches
-    ((700, 3000), 16, 512, 1024),               # long window: 16 window batches
-])
-def test_sparse_decode_matches_oracle(fk, ctx, H, topk, W, split):
+    ((5000,), 16, 2048, 128),                   # eight FP4 tiles per wave: slot refills
+    ((700, 3000), 16, 512, 1024),               # long window: several window units per wave
+    (tuple(600 + 2 * ((53 * b) % 4000) for b in range(40)), 64, 512, 128),    # 160 pairs: dims split in two
+    (tuple(60 + 2 * ((97 * b) % 3000) for b in range(34)), 64, 2048, 1024),  # 136 pairs, refills, long window
+    (tuple(40 + 2 * ((37 * b) % 700) for b in range(130)), 64, 96, 128),     # 520 pairs: batched 16-head kernel
+], ids=["c0", "c1len", "ragged", "topk2048", "win1024", "pairs160", "pairs136_long", "pairs520"])
+def test_sparse_decode_matches_oracle(fk, ctx, H, topk, W):
     cfg = small_decode(1, B=len(ctx), ctx=ctx, H=H, pages="random", heavy_frac=0.05, append=0,
                        topk=topk, window=W)
     case = make_decode_case(cfg, "cpu")
@@ -52,8 +54,7 @@ def test_sparse_decode_matches_oracle(fk, ctx, H, topk, W, split):
     L = case.layer(0)
     tk = _oracle_topk(case, oc, L, topk)
     ctx_len = torch.tensor(case.ctx_len, dtype=torch.int32, device="cuda")
-    out, lse = fk.sparse_decode(gc, ctx_len, L["q"].cuda(), torch.from_numpy(tk).cuda(), L["swa"].cuda(),
-                                ws=None if split else _no_ws())
+    out, lse = fk.sparse_decode(gc, ctx_len, L["q"].cuda(), torch.from_numpy(tk).cuda(), L["swa"].cuda())
     torch.cuda.synchronize()
     out_b, lse = bits(out.cpu()), lse.cpu().numpy()
     worst = 0.0
@@ -145,9 +146,9 @@ def test_window_only_and_single_row(fk):
     assert gather_rows(oc, 0, np.zeros(0, np.int64), bits(L["swa"][0]), 1, 128).shape[0] == 2
 
 
-def test_split_runs_without_valid_rows(fk):
-    # window only (no FP4 rows), a 1024-row window cut into eight runs, and contexts so
-    # short that most runs hold no valid row: those runs must drop out of the merge
+def test_waves_without_valid_rows(fk):
+    # window only (no FP4 rows), a 1024-row window over eight waves, and contexts so
+    # short that most waves hold no valid row: those waves must drop out of the merge
     cfg = small_decode(1, B=3, ctx=(2, 40, 2000), H=16, pages="identity", append=0, window=1024)
     case = make_decode_case(cfg, "cpu")
     oc = oracle_cache_for(case)
@@ -156,7 +157,6 @@ def test_split_runs_without_valid_rows(fk):
     ctx_len = torch.tensor(case.ctx_len, dtype=torch.int32, device="cuda")
     tk = torch.full((case.B, 0), -1, dtype=torch.int32, device="cuda")
     out, lse = fk.sparse_decode(gc, ctx_len, L["q"].cuda(), tk, L["swa"].cuda())
-    whole, lse_w = fk.sparse_decode(gc, ctx_len, L["q"].cuda(), tk, L["swa"].cuda(), ws=_no_ws())
     torch.cuda.synchronize()
     out_b, lse = bits(out.cpu()), lse.cpu().numpy()
     for b in range(case.B):
@@ -165,4 +165,3 @@ def test_split_runs_without_valid_rows(fk):
         o_ref, lse_ref = sparse_attention(bits(L["q"][b]), rows, 1 / math.sqrt(512))
         check_attention_rows(out_b[b], o_ref)
         assert np.allclose(lse[b], lse_ref, rtol=0, atol=1e-4), np.abs(lse[b] - lse_ref).max()
-    assert np.allclose(lse, lse_w.cpu().numpy(), rtol=0, atol=1e-5)
