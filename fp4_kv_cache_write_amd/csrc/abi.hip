@@ -42,7 +42,9 @@ size_t csa2_workspace_size(int fn, int B, int H, int64_t max_ctx, int topk, int 
   switch (fn) {
     case CSA2_FN_INDEX_FULL:
       if (max_ctx < 0 || topk < 1 || topk > CSA2_MAX_TOPK || pool_blocks < 0) return 0;
-      return plan_index_full(B, max_ctx >> vs, topk, pool_blocks, 8).total;
+      // the size does not depend on cand_block; the capacity check here takes the
+      // most permissive block size (32), csa2_index_full the caller's
+      return plan_index_full(B, max_ctx >> vs, topk, pool_blocks, 32).total;
     case CSA2_FN_REINDEX:
       return reindex_ws(B);
     case CSA2_FN_SPARSE_DECODE:

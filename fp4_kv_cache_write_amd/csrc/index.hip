@@ -617,8 +617,8 @@ bool lds_limits_set() {
 bool index_kernels_ready() { return lds_limits_set(); }
 
 IndexFullPlan plan_index_full(int B, int64_t max_nvis, int topk, int pool_blocks, int cand_block) {
-  (void)cand_block;
   IndexFullPlan p{};
+  if (cand_block < 1) return p;
   int ch = 4096;
   while (ch < topk) ch *= 2;
   int64_t nc = (max_nvis + ch - 1) / ch;
@@ -628,9 +628,11 @@ IndexFullPlan plan_index_full(int B, int64_t max_nvis, int topk, int pool_blocks
   }
   if (nc < 1) nc = 1;
   if (nc * topk > kMergeCap || ch > 16384) return p;      // chunk = 0: unsupported
-  // pool: block maxima sized for the smallest block (1 entry) so any cand_block fits
+  // pool: the pool workgroup ranks at most kMergeCap block maxima of cand_block
+  // entries (the only capacity check of the pool); their storage is sized for 1-entry
+  // blocks, so the size does not depend on cand_block
+  if (pool_blocks > 0 && (max_nvis + cand_block - 1) / cand_block > kMergeCap) return p;
   const int64_t max_blocks = pool_blocks > 0 ? std::max<int64_t>(max_nvis, 1) : 0;
-  if (pool_blocks > 0 && (max_nvis + 7) / 8 > kMergeCap) return p;
   p.chunk = ch;
   p.n_chunks = (int)nc;
   p.max_blocks = (int)max_blocks;
@@ -667,7 +669,6 @@ int launch_index_full(const csa2_cache_t& c, int B, const int32_t* ctx_len, int6
   const int64_t max_nvis = max_ctx >> vs;
   const IndexFullPlan p = plan_index_full(B, max_nvis, topk, pool_blocks, cand_block);
   if (p.chunk == 0) return CSA2_EUNSUPPORTED;
-  if (pool_blocks > 0 && (max_nvis + cand_block - 1) / cand_block > kMergeCap) return CSA2_EUNSUPPORTED;
   if (!lds_limits_set()) return CSA2_EHIP;
   uint8_t* w = static_cast<uint8_t*>(ws);
   ScanArgs sa;

@@ -181,10 +181,10 @@ int csa2_block_keys(const csa2_cache_t *cache, const csa2_cache_t *blocks, int B
  *   {1,2,4,8,16,32}; max_ctx/ratio <= 64 * max_pages.  ws: csa2_workspace_size(
  *   CSA2_FN_INDEX_FULL, B, 0, max_ctx, topk, pool_blocks, 0, ratio) bytes (device).
  *   Capacity, with n = max_ctx / ratio: ceil(n / 16384) * topk <= 32768 (1,048,576
- *   entries at topk 512), and with pool_blocks > 0 also ceil(n / min(cand_block, 8))
- *   <= 32768 (262,144 entries at cand_block 8).  Past these the call returns
- *   CSA2_EUNSUPPORTED, and the workspace size query returns 0 (it assumes
- *   cand_block 8). */
+ *   entries at topk 512), and with pool_blocks > 0 also ceil(n / cand_block) <= 32768
+ *   (262,144 entries at cand_block 8, 1,048,576 at 32).  Past these the call returns
+ *   CSA2_EUNSUPPORTED.  The workspace size does not depend on cand_block; the size
+ *   query returns 0 only when no cand_block fits (it checks with cand_block 32). */
 int csa2_index_full(const csa2_cache_t *cache, int B, const int32_t *ctx_len, int64_t max_ctx,
                     const uint16_t *q_idx, const uint16_t *w_idx, int topk, int pool_blocks,
                     int cand_block, int32_t *topk_idx, int32_t *pool, void *ws, size_t ws_bytes,
@@ -215,12 +215,12 @@ int csa2_reindex(const csa2_cache_t *cache, int B, const int32_t *ctx_len, const
  *   Reuse mode ([P1] §2.3.2) is this call with an earlier layer's topk_idx.
  *   q: [B][H][512] bf16; topk_idx: [B][topk] int32; swa: [B][W][512] bf16;
  *   out: [B][H][512] bf16; lse: [B][H] float or NULL (all device).  H a multiple of
- *   16; 1 <= W <= 1024; 0 <= topk <= 2048.  ws (optional, device): with
- *   csa2_workspace_size(CSA2_FN_SPARSE_DECODE, B, H, 0, topk, 0, 0, ratio) bytes, a call
- *   with fewer (sequence, 16-head group) pairs than the GPU has CUs spreads each
- *   pair's rows over several workgroups and merges their partial softmax states
- *   (same result up to fp32 rounding order); NULL with ws_bytes = 0 runs one
- *   workgroup per pair.  ws_bytes > 0 with ws NULL: CSA2_EWORKSPACE. */
+ *   16; 1 <= W <= 1024; 0 <= topk <= 2048.  ws, ws_bytes: kept for callers of the
+ *   workspace-sized interface; the call needs no workspace (csa2_workspace_size(
+ *   CSA2_FN_SPARSE_DECODE, ...) returns 0) and ignores them, except that ws_bytes > 0
+ *   with ws NULL is CSA2_EWORKSPACE.  No state goes through memory between kernels:
+ *   small batches split each (sequence, 16-head group)'s output dims over several
+ *   workgroups, not its rows. */
 int csa2_sparse_decode(const csa2_cache_t *cache, int B, int H, const int32_t *ctx_len,
                        const uint16_t *q, const int32_t *topk_idx, int topk, const uint16_t *swa,
                        int W, float sm_scale, uint16_t *out, float *lse, void *ws, size_t ws_bytes,

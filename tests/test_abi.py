@@ -49,13 +49,24 @@ def test_workspace_sizes_are_consistent():
 
 def test_index_full_capacity_boundaries():
     # the Full selection merges at most 32,768 candidates (16384-entry chunks x topk) and,
-    # with a pool, at most 32,768 block maxima of 8 entries: one entry more is unsupported
+    # with a pool, ranks at most 32,768 block maxima: one entry more is unsupported
     ws = lambda max_ctx, topk, pool_blocks, ratio=2: fk.workspace_size(
         fk.FN_INDEX_FULL, B=1, max_ctx=max_ctx, topk=topk, pool_blocks=pool_blocks, ratio=ratio)
     assert ws(2 * 1048576, 512, 0) > 0 and ws(2 * 1048576 + 2, 512, 0) == 0
     assert ws(1048576, 512, 0, ratio=1) > 0 and ws(1048577, 512, 0, ratio=1) == 0
     assert ws(2 * 16 * 16384, 2048, 0) > 0 and ws(2 * 16 * 16384 + 2, 2048, 0) == 0
-    assert ws(2 * 262144, 512, 512) > 0 and ws(2 * 262144 + 2, 512, 512) == 0
+    # the pool's block count depends on cand_block: the size query checks with the
+    # most permissive (32); the call checks the caller's (EUNSUPPORTED before any launch)
+    assert ws(2 * 1048576, 512, 512) > 0 and ws(2 * 1048576 + 2, 512, 512) == 0
+    L = fk.lib()
+    c, keep = _fake_cache(max_pages=20000)
+    p = ctypes.c_void_p(ctypes.addressof(keep))
+    call = lambda max_ctx, cand_block: L.csa2_index_full(ctypes.byref(c), 1, p, max_ctx, p, p, 512, 512,
+                                                         cand_block, p, p, None, 0, None)
+    EWS, EUNS = -2, -3
+    assert call(2 * 262144, 8) == EWS and call(2 * 262144 + 2, 8) == EUNS
+    assert call(2 * 262144 + 2, 16) == EWS and call(2 * 524288 + 2, 16) == EUNS
+    assert call(2 * 32768, 1) == EWS and call(2 * 32768 + 2, 1) == EUNS
 
 
 def _fake_cache(max_pages=4, ratio=0):
