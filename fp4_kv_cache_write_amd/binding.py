@@ -19,7 +19,7 @@ D_LATENT, D_INDEX, H_INDEX, PAGE = 512, 64, 4, 64
 FN_INDEX_FULL, FN_REINDEX, FN_SPARSE_DECODE, FN_PREFILL_CHUNK = 1, 2, 3, 4
 
 EXPORTS = ("csa2_bytes_per_entry", "csa2_strerror", "csa2_workspace_size", "csa2_write_kv", "csa2_write_kv_proj", "csa2_block_keys",
-           "csa2_index_full", "csa2_reindex", "csa2_sparse_decode", "csa2_prefill_chunk",
+           "csa2_index_full", "csa2_index_full_noalloc", "csa2_reindex", "csa2_sparse_decode", "csa2_prefill_chunk",
            "csa2_debug_gather", "csa2_schedule_workspace_size", "csa2_schedule_create",
            "csa2_schedule_launch", "csa2_schedule_destroy")
 LAYER_MODES = {"full": 0, "reindex": 1, "reuse": 2}
@@ -71,6 +71,8 @@ def lib() -> ctypes.CDLL:
         L.csa2_block_keys.argtypes = [C, C, I, P, I64, I, P, I, P, P]
         L.csa2_index_full.restype = I
         L.csa2_index_full.argtypes = [C, I, P, I64, P, P, I, I, I, P, P, P, SZ, P]
+        L.csa2_index_full_noalloc.restype = I
+        L.csa2_index_full_noalloc.argtypes = [C, I, P, I64, P, P, I, I, I, P, P, P]
         L.csa2_reindex.restype = I
         L.csa2_reindex.argtypes = [C, I, P, P, P, P, I, I, I, P, P, SZ, P]
         L.csa2_sparse_decode.restype = I
@@ -262,6 +264,25 @@ def index_full(cache: PagedCache, ctx_len: torch.Tensor, max_ctx: int, q_idx: to
                                  pool_blocks, cand_block, _ptr(topk_idx), _ptr(pool), _ptr(ws), wsb,
                                  _stream(stream)), "csa2_index_full")
     return topk_idx, pool
+
+
+def index_full_noalloc(cache: PagedCache, ctx_len: torch.Tensor, max_ctx: int, q_idx: torch.Tensor,
+                       w_idx: torch.Tensor, topk_idx: torch.Tensor, pool: Optional[torch.Tensor] = None,
+                       topk: int = 512, pool_blocks: int = 0, cand_block: int = 8, stream=None) -> None:
+    """csa2_index_full_noalloc: outputs are the caller's; the workspace is the library's
+    fixed per-GPU array, so nothing is allocated on this path."""
+    B = ctx_len.shape[0]
+    _need(ctx_len, torch.int32, "ctx_len", (B,))
+    _bf16(q_idx, "q_idx", (B, H_INDEX, D_INDEX))
+    _bf16(w_idx, "w_idx", (B, H_INDEX))
+    _need(topk_idx, torch.int32, "topk_idx", (B, topk))
+    if pool_blocks > 0:
+        if pool is None:
+            raise ValueError("pool is required when pool_blocks > 0")
+        _need(pool, torch.int32, "pool", (B, pool_blocks))
+    _check(lib().csa2_index_full_noalloc(cache.ref, B, _ptr(ctx_len), max_ctx, _ptr(q_idx), _ptr(w_idx),
+                                         topk, pool_blocks, cand_block, _ptr(topk_idx), _ptr(pool),
+                                         _stream(stream)), "csa2_index_full_noalloc")
 
 
 def reindex(cache: PagedCache, ctx_len: torch.Tensor, q_idx: torch.Tensor, w_idx: torch.Tensor,

@@ -2,10 +2,15 @@
 // The contract of every function is in csa2.h.
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "csa2.h"
 #include "internal.h"
 
 using namespace csa2;
+
+// Workspace of csa2_index_full_noalloc (see scratch_for_current_device below).
+static __device__ __align__(256) uint8_t scratch[CSA2_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -15,6 +20,44 @@ bool cache_ok(const csa2_cache_t* c) {
 }
 
 bool pow2_in(int v, int lo, int hi) { return v >= lo && v <= hi && (v & (v - 1)) == 0; }
+
+// Argument checks shared by csa2_index_full and csa2_index_full_noalloc; on success
+// *plan holds the workspace layout the launch will use.
+int index_full_check(const csa2_cache_t* cache, int B, const int32_t* ctx_len, int64_t max_ctx,
+                     const uint16_t* q_idx, const uint16_t* w_idx, int topk, int pool_blocks,
+                     int cand_block, const int32_t* topk_idx, const int32_t* pool, IndexFullPlan* plan) {
+  if (!cache_ok(cache) || B <= 0 || !ctx_len || !q_idx || !w_idx || !topk_idx) return CSA2_EINVAL;
+  if (topk < 1 || topk > CSA2_MAX_TOPK || pool_blocks < 0 || max_ctx < 0) return CSA2_EINVAL;
+  if (!pow2_in(cand_block, 1, 32)) return CSA2_EINVAL;
+  if (pool_blocks > 0 && !pool) return CSA2_EINVAL;
+  const int64_t max_nvis = max_ctx >> vis_shift(*cache);
+  if (max_nvis > (int64_t)cache->max_pages * CSA2_PAGE) return CSA2_EINVAL;
+  *plan = plan_index_full(B, max_nvis, topk, pool_blocks, cand_block);
+  if (plan->chunk == 0) return CSA2_EUNSUPPORTED;
+  return CSA2_OK;
+}
+
+// Workspace of csa2_index_full_noalloc: one array per GPU, resident until the process
+// ends.  Host code never passes `scratch` itself to a kernel (on the host it names a
+// stand-in, not device memory); it passes the device address that hipGetSymbolAddress
+// returns for the current device, looked up once per device and kept.
+constexpr size_t kScratchBytes = (size_t)CSA2_NOALLOC_SCRATCH_BYTES;
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+int scratch_for_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return CSA2_EHIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return CSA2_EHIP;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return CSA2_OK;
+}
 
 }  // namespace
 
@@ -31,6 +74,7 @@ const char* csa2_strerror(int code) {
     case CSA2_EWORKSPACE: return "workspace missing or too small";
     case CSA2_EUNSUPPORTED: return "unsupported request";
     case CSA2_EHIP: return "HIP launch failure";
+    case CSA2_ESCRATCH: return "request needs more than the fixed scratch array";
     default: return "unknown error";
   }
 }
@@ -91,15 +135,28 @@ int csa2_index_full(const csa2_cache_t* cache, int B, const int32_t* ctx_len, in
                     const uint16_t* q_idx, const uint16_t* w_idx, int topk, int pool_blocks,
                     int cand_block, int32_t* topk_idx, int32_t* pool, void* ws, size_t ws_bytes,
                     void* stream) {
-  if (!cache_ok(cache) || B <= 0 || !ctx_len || !q_idx || !w_idx || !topk_idx) return CSA2_EINVAL;
-  if (topk < 1 || topk > CSA2_MAX_TOPK || pool_blocks < 0 || max_ctx < 0) return CSA2_EINVAL;
-  if (!pow2_in(cand_block, 1, 32)) return CSA2_EINVAL;
-  if (pool_blocks > 0 && !pool) return CSA2_EINVAL;
-  const int64_t max_nvis = max_ctx >> vis_shift(*cache);
-  if (max_nvis > (int64_t)cache->max_pages * CSA2_PAGE) return CSA2_EINVAL;
-  const IndexFullPlan p = plan_index_full(B, max_nvis, topk, pool_blocks, cand_block);
-  if (p.chunk == 0) return CSA2_EUNSUPPORTED;
+  IndexFullPlan p{};
+  const int rc = index_full_check(cache, B, ctx_len, max_ctx, q_idx, w_idx, topk, pool_blocks,
+                                  cand_block, topk_idx, pool, &p);
+  if (rc != CSA2_OK) return rc;
   if (p.total > 0 && (!ws || ws_bytes < p.total)) return CSA2_EWORKSPACE;
+  return launch_index_full(*cache, B, ctx_len, max_ctx, q_idx, w_idx, topk, pool_blocks, cand_block,
+                           topk_idx, pool, ws, (hipStream_t)stream);
+}
+
+int csa2_index_full_noalloc(const csa2_cache_t* cache, int B, const int32_t* ctx_len, int64_t max_ctx,
+                            const uint16_t* q_idx, const uint16_t* w_idx, int topk, int pool_blocks,
+                            int cand_block, int32_t* topk_idx, int32_t* pool, void* stream) {
+  IndexFullPlan p{};
+  int rc = index_full_check(cache, B, ctx_len, max_ctx, q_idx, w_idx, topk, pool_blocks, cand_block,
+                            topk_idx, pool, &p);
+  if (rc != CSA2_OK) return rc;
+  if (p.total > kScratchBytes) return CSA2_ESCRATCH;
+  void* ws = nullptr;
+  rc = scratch_for_current_device(&ws);
+  if (rc != CSA2_OK) return rc;
+  // every workspace byte the kernels read is written earlier in the same launch
+  // sequence, so the array's contents from an earlier call need no clearing
   return launch_index_full(*cache, B, ctx_len, max_ctx, q_idx, w_idx, topk, pool_blocks, cand_block,
                            topk_idx, pool, ws, (hipStream_t)stream);
 }

@@ -62,8 +62,12 @@ enum {
   CSA2_EINVAL = -1,       /* null pointer, bad size, odd token count, ... */
   CSA2_EWORKSPACE = -2,   /* workspace missing or smaller than csa2_workspace_size() */
   CSA2_EUNSUPPORTED = -3, /* a valid request this library does not implement */
-  CSA2_EHIP = -4          /* the HIP runtime refused a launch */
+  CSA2_EHIP = -4,         /* the HIP runtime refused a launch */
+  CSA2_ESCRATCH = -5      /* csa2_index_full_noalloc: workspace above the fixed array */
 };
+
+/* Size of the per-GPU array that csa2_index_full_noalloc uses as its workspace. */
+#define CSA2_NOALLOC_SCRATCH_BYTES (32u << 20)
 
 /* Workspace-sized functions (argument `fn` of csa2_workspace_size). */
 enum {
@@ -189,6 +193,24 @@ int csa2_index_full(const csa2_cache_t *cache, int B, const int32_t *ctx_len, in
                     const uint16_t *q_idx, const uint16_t *w_idx, int topk, int pool_blocks,
                     int cand_block, int32_t *topk_idx, int32_t *pool, void *ws, size_t ws_bytes,
                     void *stream);
+
+/* csa2_index_full_noalloc — csa2_index_full for callers that cannot allocate device
+ *   memory: code under HIP graph capture, tight serving loops, and harnesses that
+ *   forbid hipMalloc.  Same arguments, results and checks as csa2_index_full, without
+ *   ws / ws_bytes: the workspace is a library-owned array of
+ *   CSA2_NOALLOC_SCRATCH_BYTES (32 MiB) in device memory, one per GPU, resident from
+ *   the first call on that GPU until the process ends.  A request whose workspace
+ *   (csa2_workspace_size(CSA2_FN_INDEX_FULL, ...)) is larger returns CSA2_ESCRATCH
+ *   before any launch; 32 MiB covers batch 32 at 32,768 entries with a 4096-entry
+ *   pool, and batch 8 at 524,288 entries without a pool.  The call allocates nothing
+ *   (no hipMalloc, no allocating library routine); on its first call on a GPU it looks
+ *   up the array's device address (CSA2_EHIP if that fails).  Every call on one GPU
+ *   shares that GPU's array: calls that overlap in time on one GPU (two streams, or
+ *   two host threads) race and give undefined results; calls ordered on one stream
+ *   are safe.  The array needs no clearing between calls. */
+int csa2_index_full_noalloc(const csa2_cache_t *cache, int B, const int32_t *ctx_len, int64_t max_ctx,
+                            const uint16_t *q_idx, const uint16_t *w_idx, int topk, int pool_blocks,
+                            int cand_block, int32_t *topk_idx, int32_t *pool, void *stream);
 
 /* csa2_reindex — Reindex mode ([P1] §2.3.2 Reindex mode, §2.3.4: later indexers
  *   score only the candidate pool).  Scores, with this layer's q_idx / w_idx, the

@@ -30,8 +30,8 @@ def test_library_exports_every_declared_function():
 def test_constants_and_strerror():
     assert fk.bytes_per_entry() == 306
     L = fk.lib()
-    for code in (0, -1, -2, -3, -4):
-        assert L.csa2_strerror(code)
+    for code in (0, -1, -2, -3, -4, -5):
+        assert L.csa2_strerror(code) != b"unknown error"
     assert L.csa2_strerror(-99) == b"unknown error"
 
 
@@ -67,6 +67,30 @@ def test_index_full_capacity_boundaries():
     assert call(2 * 262144, 8) == EWS and call(2 * 262144 + 2, 8) == EUNS
     assert call(2 * 262144 + 2, 16) == EWS and call(2 * 524288 + 2, 16) == EUNS
     assert call(2 * 32768, 1) == EWS and call(2 * 32768 + 2, 1) == EUNS
+
+
+def test_index_full_noalloc_limits_return_before_launch():
+    # the no-alloc variant checks arguments like csa2_index_full, then refuses a workspace
+    # above its fixed array before looking the array up or launching anything
+    L = fk.lib()
+    c, keep = _fake_cache(max_pages=20000)
+    p = ctypes.c_void_p(ctypes.addressof(keep))
+    ref = ctypes.byref(c)
+    EINVAL, EUNS, ESCRATCH = -1, -3, -5
+    limit = 32 << 20
+    call = lambda B, max_ctx, pool_blocks, cand_block=8, pool=p: L.csa2_index_full_noalloc(
+        ref, B, p, max_ctx, p, p, 512, pool_blocks, cand_block, p, pool, None)
+    # batch 128 at 131,072 entries with a 4096-entry pool needs 80 MiB
+    assert fk.workspace_size(fk.FN_INDEX_FULL, B=128, max_ctx=262144, topk=512, pool_blocks=512) > limit
+    assert call(128, 262144, 512) == ESCRATCH
+    # the largest batch that fits is refused one sequence later
+    fits = max(B for B in range(1, 200) if fk.workspace_size(
+        fk.FN_INDEX_FULL, B=B, max_ctx=262144, topk=512, pool_blocks=512) <= limit)
+    assert fits < 128 and call(fits + 1, 262144, 512) == ESCRATCH
+    assert call(1, 2 * 262144 + 2, 512) == EUNS          # pool capacity at cand_block 8
+    assert call(1, 262144, 512, pool=None) == EINVAL       # pool NULL
+    assert call(1, 262144, 0, cand_block=3) == EINVAL
+    assert L.csa2_index_full_noalloc(None, 1, p, 128, p, p, 16, 0, 8, p, None, None) == EINVAL
 
 
 def _fake_cache(max_pages=4, ratio=0):
