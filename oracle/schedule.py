@@ -27,13 +27,18 @@ def n_visible(t: int, ratio: int = 2) -> int:
 
 
 def run_decode(cache, ctx_len, layers, topk: int = 512, W: int = 128, cand_block: int = 8,
-               sm_scale: float | None = None, seqs=None):
+               sm_scale: float | None = None, seqs=None, attend_on=None):
     """Decode one query per sequence through `layers`.
 
     layers: list of dicts with mode ("full"|"reindex"|"reuse"), pool_blocks and
     the layer's bf16-bit inputs q [B,H,512], q_idx [B,4,64], w_idx [B,4],
     swa [B,W,512].  Returns per layer a dict with topk[b], pool[b] (block ids),
     o[b] (float64 [H,512]) and lse[b] for every b in seqs.
+    attend_on: optional, per layer a dict b -> entry ids.  Where given, that
+    layer's attention for b reads those entries instead of the layer's own
+    selection (a selection that differs only by near-tied scores is as correct,
+    and its attention output is then compared on equal terms); topk[b] and
+    pool[b] stay this function's own selections.
     """
     if sm_scale is None:
         sm_scale = 1.0 / math.sqrt(512.0)
@@ -61,7 +66,10 @@ def run_decode(cache, ctx_len, layers, topk: int = 512, W: int = 128, cand_block
                 assert cur_t[b] is not None, "Reuse needs an earlier Full or Reindex layer"
             else:
                 raise ValueError(spec["mode"])
-            rows = gather_rows(cache, b, cur_t[b], spec["swa"][b], t, W)
+            sel = cur_t[b]
+            if attend_on is not None and b in attend_on[len(out)]:
+                sel = attend_on[len(out)][b]
+            rows = gather_rows(cache, b, sel, spec["swa"][b], t, W)
             o, lse = sparse_attention(spec["q"][b], rows, sm_scale)
             res["topk"][b] = cur_t[b]
             res["pool"][b] = cur_pool[b]
@@ -72,12 +80,15 @@ def run_decode(cache, ctx_len, layers, topk: int = 512, W: int = 128, cand_block
 
 
 def run_prefill(cache, prior_len, C: int, q, q_idx, w_idx, local, topk: int = 512, W: int = 128,
-                sm_scale: float | None = None, queries=None):
+                sm_scale: float | None = None, queries=None, attend_on=None):
     """Chunked prefill after the chunk's entries were written.
 
     q [B,C,H,512], q_idx [B,C,4,64], w_idx [B,C,4], local [B,W-1+C,512] (window
     rows for positions prior-W+1 .. prior+C-1) as bf16 bits.  queries: list of
     (b, i) pairs to evaluate (default: all).  Returns dict (b,i) -> (topk, o, lse).
+    attend_on: optional dict (b, i) -> entry ids; where given, the query's
+    attention reads those entries instead of its own top-K (which is still the
+    returned topk), as in run_decode.
     """
     if sm_scale is None:
         sm_scale = 1.0 / math.sqrt(512.0)
@@ -99,7 +110,8 @@ def run_prefill(cache, prior_len, C: int, q, q_idx, w_idx, local, topk: int = 51
         ring = np.zeros((W, local.shape[-1]), dtype=np.uint16)
         for pos in range(max(0, t - W + 1), t + 1):
             ring[pos % W] = local[b, pos - (prior_len[b] - W + 1)]
-        rows = gather_rows(cache, b, tk, ring, t, W)
+        sel = tk if attend_on is None or (b, i) not in attend_on else attend_on[(b, i)]
+        rows = gather_rows(cache, b, sel, ring, t, W)
         o, lse = sparse_attention(q[b, i], rows, sm_scale)
         out[(b, i)] = (tk, o, lse)
     return out

@@ -1,8 +1,11 @@
 """GPU tests of the layer-schedule runner (csa2_schedule_*).
 
 The captured graph must give, bit for bit, what the same calls give one by one
-(it runs the same kernels on the same buffers), on every replay; against the
-oracle, layers whose selection equals the oracle's meet the attention bar.
+(it runs the same kernels on the same buffers), on every replay.  Against the
+oracle's run_decode, for every layer of every sequence checked: Full selections
+and pools up to near-ties, Reindex selections over the GPU's own pool, Reuse
+keeping the previous selection, and attention on the GPU's own selection within
+the 2e-3 bar (lse within 1e-4).
 Schedules from [P1] §2.3.3: the decoder's [Full + 3 Reuse] + 4 x [Reindex + 3 Reuse]
 (ratio 1, pool 2048 x 8) and the encoder's [Full + 5 Reuse] x 3 (ratio 2).
 """
@@ -10,10 +13,12 @@ import numpy as np
 import pytest
 import torch
 
+from oracle.indexer import index_scores, pool_positions
 from oracle.schedule import run_decode
 from synth import make_decode_case, small_decode
 from synth.configs import DECODER_SCHEDULE as DECODER, ENCODER_SCHEDULE as ENCODER
-from tests.helpers import bits, check_attention_rows, gpu_cache_for, oracle_cache_for
+from tests.helpers import (AttentionReport, bits, check_pool_set, check_topk_set, gpu_cache_for,
+                           oracle_cache_for)
 
 pytestmark = pytest.mark.gpu
 
@@ -51,7 +56,7 @@ def _eager(fk, gc, case, ctx_len, layers, write):
         elif L["mode"] == "reindex":
             sel = fk.reindex(gc, ctx_len, L["q_idx"], L["w_idx"], pool, topk=512, cand_block=8)
         o, lse = fk.sparse_decode(gc, ctx_len, L["q"], sel, L["swa"])
-        res.append((o.clone(), lse.clone(), sel.clone()))
+        res.append((o.clone(), lse.clone(), sel.clone(), None if pool is None else pool.clone()))
     torch.cuda.synchronize()
     return res
 
@@ -92,20 +97,48 @@ def _run(fk, cfg_layers, ratio, ctx, write_last):
     return case, layers, eager
 
 
-def test_decoder_schedule_equals_calls_and_oracle(fk):
-    case, layers, eager = _run(fk, DECODER, 1, (9000, 20000), write_last=True)
-    oc = oracle_cache_for(case, seqs=(1,))
+def _check_oracle(case, layers, eager, seqs, cand_block=8, topk=512):
+    """Every layer of every sequence in seqs against the oracle (module docstring)."""
+    oc = oracle_cache_for(case, seqs=seqs)
     specs = [dict(mode=L["mode"], pool_blocks=L["pool_blocks"], q=bits(L["q"].cpu()), q_idx=bits(L["q_idx"].cpu()),
                   w_idx=bits(L["w_idx"].cpu()), swa=bits(L["swa"].cpu())) for L in layers]
-    ref = run_decode(oc, case.ctx_len, specs, topk=512, W=case.cfg.window, cand_block=8, seqs=(1,))
-    compared = 0
-    for l, (o, _, sel) in enumerate(eager):
-        g = sel[1].cpu().numpy()
-        if np.array_equal(g[g >= 0], ref[l]["topk"][1]):
-            check_attention_rows(bits(o[1].cpu()), ref[l]["o"][1])
-            compared += 1
-    assert compared >= len(eager) // 2, f"only {compared}/{len(eager)} layers had the oracle's selection"
+    sels = [e[2].cpu().numpy() for e in eager]
+    attend = [{b: sels[l][b][sels[l][b] >= 0] for b in seqs} for l in range(len(layers))]
+    ref = run_decode(oc, case.ctx_len, specs, topk=topk, W=case.cfg.window, cand_block=cand_block, seqs=seqs,
+                     attend_on=attend)
+    rep, same = AttentionReport(), 0
+    for b in seqs:
+        nv = case.n_vis[b]
+        g_pool = None
+        for l, (o, lse, sel, pool) in enumerate(eager):
+            g = sels[l][b]
+            sp = specs[l]
+            if sp["mode"] == "full":
+                s = index_scores(sp["q_idx"][b], sp["w_idx"][b], oc.index_keys(b, np.arange(nv)))
+                check_topk_set(g, np.arange(nv), s, topk)
+                if sp["pool_blocks"] > 0:
+                    p = pool[b].cpu().numpy()
+                    check_pool_set(p, s, nv, cand_block, sp["pool_blocks"])
+                    g_pool = p[p >= 0]
+            elif sp["mode"] == "reindex":
+                pos = pool_positions(g_pool, nv, cand_block)
+                s2 = index_scores(sp["q_idx"][b], sp["w_idx"][b], oc.index_keys(b, pos))
+                check_topk_set(g, pos, s2, topk)
+            else:
+                assert np.array_equal(g, sels[l - 1][b]), f"layer {l}: Reuse changed the selection"
+            rep.check(bits(o[b].cpu()), ref[l]["o"][b], lse[b].cpu().numpy(), ref[l]["lse"][b])
+            same += int(np.array_equal(g[g >= 0], ref[l]["topk"][b]))
+    assert rep.n == len(seqs) * len(eager)
+    return rep, same
 
 
-def test_encoder_schedule_equals_calls(fk):
-    _run(fk, ENCODER, 2, (4000, 12000), write_last=True)
+def test_decoder_schedule_equals_calls_and_oracle(fk):
+    case, layers, eager = _run(fk, DECODER, 1, (9000, 20000), write_last=True)
+    rep, same = _check_oracle(case, layers, eager, seqs=(0, 1))
+    print(f"decoder schedule: {rep}; {same}/{rep.n} selections identical to the oracle's")
+
+
+def test_encoder_schedule_equals_calls_and_oracle(fk):
+    case, layers, eager = _run(fk, ENCODER, 2, (4000, 12000), write_last=True)
+    rep, same = _check_oracle(case, layers, eager, seqs=(0, 1))
+    print(f"encoder schedule: {rep}; {same}/{rep.n} selections identical to the oracle's")

@@ -137,3 +137,44 @@ def test_prefill_query_ignores_later_chunk_tokens():
     assert np.array_equal(r1[(0, i)][1], r2[(0, i)][1])
     assert np.array_equal(r1[(0, i)][0], r2[(0, i)][0])
     assert r1[(0, i)][0].max() < n_visible(prior + i)
+
+
+def test_attend_on_reads_the_given_selection():
+    # attend_on evaluates a layer's attention on another selection (a GPU's, which may
+    # differ by near-tied scores); the returned selection stays the oracle's own
+    rng = np.random.default_rng(5)
+    n = 300
+    cache = _rand_cache(rng, n)
+    W, H, K = 16, 2, 24
+    L = 2 * n
+    spec = dict(mode="full", pool_blocks=0, q=bits(rng.standard_normal((1, H, 512))),
+                q_idx=bits(rng.standard_normal((1, 4, 64))), w_idx=bits(rng.standard_normal((1, 4))),
+                swa=bits(rng.standard_normal((1, W, 512))))
+    own = run_decode(cache, [L], [spec], topk=K, W=W)
+    sel = own[0]["topk"][0]
+    same = run_decode(cache, [L], [spec], topk=K, W=W, attend_on=[{0: sel}])
+    assert np.array_equal(same[0]["o"][0], own[0]["o"][0])
+    # swap the last selected entry for one outside the selection
+    other = np.sort(np.concatenate([sel[:-1], [np.setdiff1d(np.arange(n), sel)[0]]]))
+    alt = run_decode(cache, [L], [spec], topk=K, W=W, attend_on=[{0: other}])
+    assert np.array_equal(alt[0]["topk"][0], sel)
+    rows = np.concatenate([cache.latent(0, other),
+                           bf16_bits_to_f64(spec["swa"][0])[window_positions(L - 1, W) % W]])
+    dense = _dense_attention_loops(bf16_bits_to_f64(spec["q"][0]), rows, 1 / math.sqrt(512))
+    assert np.allclose(alt[0]["o"][0], dense, rtol=1e-12, atol=1e-12)
+    assert not np.allclose(alt[0]["o"][0], own[0]["o"][0], rtol=0, atol=1e-9)
+    # chunked prefill: the same option per query
+    prior, C = 200, 6
+    q = bits(rng.standard_normal((1, C, H, 512)))
+    qi = bits(rng.standard_normal((1, C, 4, 64)))
+    wi = bits(rng.standard_normal((1, C, 4)))
+    local = bits(rng.standard_normal((1, W - 1 + C, 512)))
+    r1 = run_prefill(cache, [prior], C, q, qi, wi, local, topk=K, W=W, queries=[(0, 3)])
+    tk = r1[(0, 3)][0]
+    swap = np.sort(np.concatenate([tk[1:], [np.setdiff1d(np.arange(n_visible(prior + 3)), tk)[-1]]]))
+    r2 = run_prefill(cache, [prior], C, q, qi, wi, local, topk=K, W=W, queries=[(0, 3)],
+                     attend_on={(0, 3): tk})
+    r3 = run_prefill(cache, [prior], C, q, qi, wi, local, topk=K, W=W, queries=[(0, 3)],
+                     attend_on={(0, 3): swap})
+    assert np.array_equal(r2[(0, 3)][1], r1[(0, 3)][1])
+    assert np.array_equal(r3[(0, 3)][0], tk) and not np.allclose(r3[(0, 3)][1], r1[(0, 3)][1], rtol=0, atol=1e-9)
