@@ -54,7 +54,9 @@ def parse():
                    help="c1 = headline decode line (+ secondary c0, c2, c3, c4, c5); others alone")
     p.add_argument("--no-secondary", action="store_true")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-seqs", type=int, default=2, help="sequences in the oracle's timed sample")
+    p.add_argument("--cpu-seqs", type=int, default=2, help="sequences in the headline oracle sample")
+    p.add_argument("--cpu-seconds", type=float, default=10.0,
+                   help="oracle time for the headline line (secondary lines take half)")
     p.add_argument("--no-graph", action="store_true", help="time eager launches instead of graph replay")
     p.add_argument("--overlap-layers", action="store_true",
                    help="fork each layer's attention onto its own stream (ignores that a layer's queries "
@@ -332,7 +334,8 @@ def bench_decode(fk, cfg_id: int, steps: int, warmup: int, n_rep: int, use_graph
                 roofline=roofline, use_graph=use_graph, count=count, per_bytes=per_bytes)
 
 
-def bench_schedule(fk, cfg_id: int, schedule, steps: int, warmup: int, n_rep: int = 4):
+def bench_schedule(fk, cfg_id: int, schedule, steps: int, warmup: int, n_rep: int = 4, cpu_seqs=(),
+                   cpu_seconds=5.0):
     """One decode step of a whole layer schedule through the native runner
     (csa2_schedule_*: the step's write plus every layer captured as one HIP graph),
     replayed over n_rep cache replicas."""
@@ -369,17 +372,19 @@ def bench_schedule(fk, cfg_id: int, schedule, steps: int, warmup: int, n_rep: in
     for sc in scheds:
         sc.close()
     log(f"{cfg.name}: {ms * 1e3:.1f} us/step ({len(cfg.layers)} layers), {B / (ms / 1e3):.0f} queries/s")
+    cpu = (cpu_baseline_decode(case, reps[0], cpu_seqs, cpu_seconds, f"{len(cpu_seqs)} of {B} sequences")
+           if cpu_seqs else None)
     return {"workload": cfg.name, "value": round(B / (ms / 1e3), 1), "unit": "queries/s",
             "ms_per_step": round(ms, 5), "layers": len(cfg.layers), "us_per_layer": round(ms * 1e3 / len(cfg.layers), 2),
             "achieved_gbs": round(step_bytes / (ms / 1e3) / 1e9, 1), "algorithmic_bytes_per_step": step_bytes,
-            "launch": "native schedule runner: write + all layers as one HIP graph"}
+            "launch": "native schedule runner: write + all layers as one HIP graph", "cpu_baseline": cpu}
 
 
 # ----------------------------------------------------------------------------------
 # chunked prefill
 # ----------------------------------------------------------------------------------
 
-def bench_prefill(fk, steps: int, warmup: int):
+def bench_prefill(fk, steps: int, warmup: int, cpu_seqs=()):
     from synth import CONFIGS, make_prefill_case
     cfg = CONFIGS[3]
     dev = "cuda"
@@ -459,15 +464,20 @@ def bench_prefill(fk, steps: int, warmup: int):
     toks = case.B * cfg.C / (ms / 1e3)
     log(f"{cfg.name}: write {ms_w * 1e3:.0f} us + prefill {ms_a * 1e3:.0f} us; {toks:.0f} tokens/s, "
         f"{tfs:.1f} TFLOP/s")
+    cpu = None
+    if cpu_seqs:
+        cpu = cpu_baseline_prefill(case, ch, cpu_seqs, 64, f"{len(cpu_seqs)} of {case.B} chunks")
+        log(f"{cfg.name}: oracle {cpu['value']} tokens/s (extrapolated)")
     return {"workload": cfg.name, "metric": "prefill query tokens/s", "value": round(toks, 1),
             "unit": "tokens/s", "ms_per_step": round(ms, 4), "ms_write": round(ms_w, 4),
             "ms_index_attention": round(ms_a, 4), "flop_indexer": fl_idx, "flop_attention": fl_att,
             "roofline": {"bound": "mfma", "achieved": round(tfs, 2), "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
                          "frac": round(tfs / MFMA_BF16_PEAK_TFS, 4), "traffic": None},
-            "write_proj": write_proj_line, "dtype": "bf16", "steps": steps, "warmup": warmup}
+            "write_proj": write_proj_line, "dtype": "bf16", "steps": steps, "warmup": warmup,
+            "cpu_baseline": cpu}
 
 
-def bench_hisa(fk, steps: int, warmup: int, n_rep: int = 4, cfg_id: int = 1):
+def bench_hisa(fk, steps: int, warmup: int, n_rep: int = 4, cfg_id: int = 1, cpu_seqs=(), cpu_seconds=5.0):
     """HISA selection at a decode workload's size (blocks of 8 entries): per
     step, the newest block's summary is refreshed (csa2_block_keys) and the 512 best
     block summaries are expanded and re-scored to the top-512 (csa2_index_full on the
@@ -532,12 +542,14 @@ def bench_hisa(fk, steps: int, warmup: int, n_rep: int = 4, cfg_id: int = 1):
     n_vis = case.n_vis
     hisa_bytes = sum((-(-v // cb)) * BYTES_IDX + keep * cb * BYTES_IDX + 2 * 520 + 4 * topk for v in n_vis)
     log(f"{cfg.name} HISA selection {out['hisa']:.1f} us/step vs Full{' + HSI pool' if pb else ''} {out['full']:.1f} us")
+    cpu = cpu_baseline_hisa(case, cpu_seqs, reps[0].layers[0], keep, cpu_seconds) if cpu_seqs else None
     return {"workload": f"{cfg.name.split('_h64')[0]}_hisa_blocks{cb}_keep{keep}", "us_per_step": round(out["hisa"], 2),
             "full_selection_us": round(out["full"], 2), "full_selection_has_pool": bool(pb),
             "value": round(B / (out["hisa"] / 1e6), 1),
             "unit": "selections/s", "algorithmic_bytes_per_step": hisa_bytes,
             "achieved_gbs": round(hisa_bytes / (out["hisa"] / 1e6) / 1e9, 1),
-            "launch": "hip-graph; block_keys (newest block) + index_full over block summaries + reindex"}
+            "launch": "hip-graph; block_keys (newest block) + index_full over block summaries + reindex",
+            "cpu_baseline": cpu}
 
 
 # ----------------------------------------------------------------------------------
@@ -561,7 +573,8 @@ def main() -> int:
         del src, dst
 
     if args.workload == "c3":
-        r = bench_prefill(fk, max(2, args.steps // 40), max(1, args.warmup // 10))
+        r = bench_prefill(fk, max(2, args.steps // 40), max(1, args.warmup // 10),
+                          cpu_seqs=() if args.no_cpu_baseline else (0, 3))
         print(json.dumps(dict(r, n_gpus=1, higher_is_better=True, data="synthetic", vs_baseline=None,
                               config={"workload": r["workload"]})), flush=True)
         return 0
@@ -571,42 +584,58 @@ def main() -> int:
     case = d["case"]
     cfg = case.cfg
     secondary = {}
+    want_cpu = not args.no_cpu_baseline
+    sec_s = args.cpu_seconds / 2
     if args.workload == "c1" and not args.no_secondary:
-        def decode_line(cid, n_rep):
+        def decode_line(cid, n_rep, cpu_seqs):
             r = bench_decode(fk, cid, max(20, args.steps // 4), max(5, args.warmup // 4), n_rep, not args.no_graph,
                              True, args.overlap_layers)
-            out = {"workload": r["case"].cfg.name, "value": round(r["qps"], 1), "unit": "queries/s",
+            c = r["case"]
+            out = {"workload": c.cfg.name, "value": round(r["qps"], 1), "unit": "queries/s",
                    "ms_per_step": round(r["ms"], 5), "achieved_gbs": round(r["gbs"], 1),
                    "frac_hbm_peak": round(r["gbs"] / HBM_PEAK_GBS, 4), "algorithmic_bytes_per_step": r["step_bytes"],
-                   "per_call_us": {n: round(v * 1e3, 2) for n, v in r["per_call"].items()}, "roofline": r["roofline"]}
+                   "per_call_us": {n: round(v * 1e3, 2) for n, v in r["per_call"].items()}, "roofline": r["roofline"],
+                   "cpu_baseline": None}
+            if want_cpu:
+                seqs = cpu_seqs(c)
+                out["cpu_baseline"] = cpu_baseline_decode(c, r["reps"][0], seqs, sec_s,
+                                                          f"{len(seqs)} of {c.B} sequences")
             del r
             torch.cuda.empty_cache()
             return out
 
+        def seeded(n, seed):
+            return lambda c: tuple(sorted(np.random.default_rng(seed).choice(c.B, size=n, replace=False).tolist()))
+
         # a single 2K-token query: launch-latency bound, reported for completeness
-        secondary["c0_b1_ctx2k"] = decode_line(0, 8)
-        secondary["c2_b8_ctx1m"] = decode_line(2, 4)
-        secondary["c3_prefill"] = bench_prefill(fk, 5, 2)
+        secondary["c0_b1_ctx2k"] = decode_line(0, 8, lambda c: (0,))
+        secondary["c2_b8_ctx1m"] = decode_line(2, 4, seeded(1, 2002))
+        secondary["c3_prefill"] = bench_prefill(fk, 5, 2, cpu_seqs=(0, 3) if want_cpu else ())
         torch.cuda.empty_cache()
-        # mixed serving batch: 128 sequences of log-uniform length, 64-token append per step
-        secondary["c4_b128_mixed"] = decode_line(4, 2)
+        # mixed serving batch: 128 sequences of log-uniform length, 64-token append per step;
+        # the oracle's sample is 8 sequences drawn uniformly, so its queries/s is unbiased
+        secondary["c4_b128_mixed"] = decode_line(4, 2, seeded(8, 2004))
         # the decoder's ratio-1 cache with the 2048-block HSI pool
-        secondary["c5_decoder_ratio1"] = decode_line(5, 4)
+        secondary["c5_decoder_ratio1"] = decode_line(5, 4, seeded(2, 2005))
         # HISA's block-mean pool as the selection, beside the Full layer's
-        secondary["c1_hisa"] = bench_hisa(fk, max(20, args.steps // 4), max(5, args.warmup // 4))
+        secondary["c1_hisa"] = bench_hisa(fk, max(20, args.steps // 4), max(5, args.warmup // 4),
+                                          cpu_seqs=(0, 31) if want_cpu else (), cpu_seconds=sec_s)
         torch.cuda.empty_cache()
-        secondary["c2_hisa"] = bench_hisa(fk, max(20, args.steps // 4), max(5, args.warmup // 4), n_rep=2, cfg_id=2)
-        torch.cuda.empty_cache()
+        secondary["c2_hisa"] = bench_hisa(fk, max(20, args.steps // 4), max(5, args.warmup // 4), n_rep=2, cfg_id=2,
+                                          cpu_seqs=(5,) if want_cpu else (), cpu_seconds=sec_s)
         torch.cuda.empty_cache()
         # the pages' whole decoder schedule (20 layers) at that size, through the native runner
         from synth.configs import DECODER_SCHEDULE
         secondary["c5_decoder_schedule20"] = bench_schedule(fk, 5, DECODER_SCHEDULE, max(10, args.steps // 10),
-                                                            max(3, args.warmup // 4))
+                                                            max(3, args.warmup // 4),
+                                                            cpu_seqs=(7,) if want_cpu else (), cpu_seconds=sec_s)
         torch.cuda.empty_cache()
 
     cpu = None
-    if args.workload == "c1" and not args.no_cpu_baseline:
-        cpu = cpu_baseline(case, d["reps"][0], cfg.topk, cfg.window, args.cpu_seqs)
+    if want_cpu and args.workload != "c3":
+        n = max(1, min(args.cpu_seqs, case.B))
+        seqs = tuple(sorted({int(round(i * (case.B - 1) / max(n - 1, 1))) for i in range(n)}))
+        cpu = cpu_baseline_decode(case, d["reps"][0], seqs, args.cpu_seconds, f"{len(seqs)} of {case.B} sequences")
 
     line = {
         "metric": METRIC,
@@ -640,56 +669,186 @@ def main() -> int:
     return 0
 
 
-def cpu_baseline(case, rep, topk, W, n_seqs, min_seconds=10.0):
-    """Time the NumPy oracle on `n_seqs` sequences of the same inputs (host cores)."""
-    from oracle import OracleCache
-    from oracle.schedule import run_decode
+# ----------------------------------------------------------------------------------
+# the CPU oracle as a reported baseline (bounded samples of the same workloads)
+# ----------------------------------------------------------------------------------
 
-    def bits(t):
-        return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+def _host_bits(t):
+    return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
 
+
+def _host_threads():
+    """(cpus this process may run on, BLAS threads numpy uses)."""
     try:
         from threadpoolctl import threadpool_info
         blas = [i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"]
         blas_threads = max(blas) if blas else 1
     except Exception:
         blas_threads = 1
-    seqs = list(range(min(n_seqs, case.B)))
-    log(f"cpu baseline: building oracle caches for {len(seqs)} sequence(s) (untimed)")
-    caches = {}
+    return len(os.sched_getaffinity(0)), blas_threads
+
+
+def _seq_table(case, b, n_entries=None):
+    """Sequence b's own pages renumbered 0..P-1 in the same relative order, so that an
+    oracle cache for one sequence holds only that sequence's pages."""
+    row = case.block_table[b].numpy()
+    if n_entries is None:
+        n_entries = case.ctx_len[b] // case.cfg.ratio
+    P = -(-n_entries // 64)
+    row = row[:max(P, 1)]
+    return np.argsort(np.argsort(row))[None, :], max(P, 1)
+
+
+def _oracle_decode_caches(case, rep, seqs, specs):
+    """Per sampled sequence, an oracle cache ready for the timed step (untimed set-up):
+    every indexer key before the step's write, then, from a dry run of the oracle's own
+    layers, the latent rows those layers read.  The step's write is re-done when timed."""
+    from oracle import OracleCache
+    from oracle.schedule import run_decode
+    cfg = case.cfg
+    r = cfg.ratio
+    Wr = rep.write
+    out = {}
     for b in seqs:
+        bt, P = _seq_table(case, b)
+        oc = OracleCache(P, bt, ratio=r)
         x, w, k = case.seq_tokens(b)
-        bt = case.block_table[b:b + 1].numpy()
-        oc = OracleCache(case.n_pages, bt)
-        T = x.shape[0]
-        oc.write(0, 0, bits(x[:T - 2]), bits(w[:T - 2]), bits(k[:T // 2 - 1]))
-        caches[b] = (oc, bits(x[T - 2:]), bits(w[T - 2:]), bits(k[T // 2 - 1:]))
-    specs = []
-    for l, spec in enumerate(case.cfg.layers):
-        L = rep.layers[l]
-        specs.append(dict(mode=spec.mode, pool_blocks=spec.pool_blocks, q=bits(L["q"]), q_idx=bits(L["q_idx"]),
-                          w_idx=bits(L["w_idx"]), swa=bits(L["swa"])))
-    log("cpu baseline: timing the oracle")
+        start = int(Wr["start"][b])
+        n_pre = start // r
+        oc.write(0, 0, None, None, _host_bits(k[:n_pre]), latent=False)
+        wx = _host_bits(Wr["x"][b])
+        ww = None if Wr["w"] is None else _host_bits(Wr["w"][b])
+        wk = _host_bits(Wr["k"][b])
+        oc.write(0, start, wx, ww, wk)
+        sub = [dict(s, q=s["q"][b:b + 1], q_idx=s["q_idx"][b:b + 1], w_idx=s["w_idx"][b:b + 1],
+                    swa=s["swa"][b:b + 1]) for s in specs]
+        dry = run_decode(oc, [case.ctx_len[b]], sub, topk=cfg.topk, W=cfg.window, cand_block=cfg.cand_block)
+        need = np.unique(np.concatenate([d["topk"][0] for d in dry] + [np.zeros(0, np.int64)]))
+        need = need[need < n_pre].astype(np.int64)
+        tok = torch.as_tensor((r * need[:, None] + np.arange(r)[None]).reshape(-1), device=x.device)
+        xs = _host_bits(x[tok])
+        ws = None if w is None else _host_bits(w[tok])
+        kb = _host_bits(k[:n_pre])
+        for i, j in enumerate(need.tolist()):
+            oc.write(0, r * j, xs[r * i:r * i + r], None if ws is None else ws[r * i:r * i + r], kb[j:j + 1])
+        out[b] = (oc, start, wx, ww, wk, sub)
+        del x, w, k
+    return out
+
+
+def cpu_baseline_decode(case, rep, seqs, min_seconds: float, sample_note: str):
+    """The oracle's decode step (the step's write, then every layer: selection and
+    attention) timed on sampled sequences of the workload, on the host cores."""
+    from oracle.schedule import run_decode
+    cfg = case.cfg
+    specs = [dict(mode=sp.mode, pool_blocks=sp.pool_blocks, q=_host_bits(L["q"]), q_idx=_host_bits(L["q_idx"]),
+                  w_idx=_host_bits(L["w_idx"]), swa=_host_bits(L["swa"])) for sp, L in zip(cfg.layers, rep.layers)]
+    log(f"cpu baseline {cfg.name}: oracle caches for sequences {list(seqs)} (untimed)")
+    caches = _oracle_decode_caches(case, rep, seqs, specs)
+    log(f"cpu baseline {cfg.name}: timing the oracle")
     t0 = time.perf_counter()
     done = 0
     while True:
         for b in seqs:
-            oc, px, pw, pk = caches[b]
-            L = case.ctx_len[b]
-            oc.write(0, L - 2, px, pw, pk)                   # the step's pair write
-            sub = [dict(s, q=s["q"][b:b + 1], q_idx=s["q_idx"][b:b + 1], w_idx=s["w_idx"][b:b + 1],
-                        swa=s["swa"][b:b + 1]) for s in specs]
-            run_decode(oc, [L], sub, topk=topk, W=W, cand_block=case.cfg.cand_block)
+            oc, start, wx, ww, wk, sub = caches[b]
+            oc.write(0, start, wx, ww, wk)
+            run_decode(oc, [case.ctx_len[b]], sub, topk=cfg.topk, W=cfg.window, cand_block=cfg.cand_block)
             done += 1
         if time.perf_counter() - t0 >= min_seconds:
             break
     dt = time.perf_counter() - t0
-    return {"value": round(done / dt, 3), "unit": "queries/s", "cores": blas_threads,
+    cores, blas = _host_threads()
+    return {"value": round(done / dt, 3), "unit": "queries/s", "cores": cores, "blas_threads": blas,
             "kind": "oracle",
-            "sample": f"sequences {seqs} of {case.B} decoded {done // len(seqs)}x each ({done} queries), "
-                      f"full 3-layer step incl. pair write, oracle cache pre-built untimed; {dt:.2f}s; "
-                      f"numpy float64, BLAS threads={blas_threads}, elementwise single-threaded; "
-                      f"host cpus={len(os.sched_getaffinity(0))}"}
+            "sample": f"{sample_note}: sequences {list(seqs)} of {case.B} (lengths "
+                      f"{[case.ctx_len[b] for b in seqs]}), {done} queries in {dt:.2f}s; each query is the "
+                      f"oracle's whole step for its sequence (the step's write, then {len(cfg.layers)} layers of "
+                      f"selection and attention); oracle cache set up untimed; numpy float64, BLAS on "
+                      f"{blas} threads, elementwise work on one"}
+
+
+def cpu_baseline_hisa(case, seqs, layer, keep: int, min_seconds: float):
+    """The oracle's HISA selection (block summaries, their top blocks, the top-K
+    within them) timed on sampled sequences."""
+    from oracle import OracleCache
+    from oracle.hisa import hisa_layer
+    cfg = case.cfg
+    caches = {}
+    for b in seqs:
+        bt, P = _seq_table(case, b)
+        oc = OracleCache(P, bt)
+        _, _, k = case.seq_tokens(b)
+        oc.write(0, 0, None, None, _host_bits(k), latent=False)
+        caches[b] = (oc, _host_bits(layer["q_idx"][b]), _host_bits(layer["w_idx"][b]))
+        del k
+    t0 = time.perf_counter()
+    done = 0
+    while True:
+        for b in seqs:
+            oc, qi, wi = caches[b]
+            hisa_layer(oc, 0, case.n_vis[b], qi, wi, cfg.cand_block, keep, cfg.topk)
+            done += 1
+        if time.perf_counter() - t0 >= min_seconds:
+            break
+    dt = time.perf_counter() - t0
+    cores, blas = _host_threads()
+    return {"value": round(done / dt, 3), "unit": "selections/s", "cores": cores, "blas_threads": blas,
+            "kind": "oracle",
+            "sample": f"sequences {list(seqs)} of {case.B}, {done} selections in {dt:.2f}s; the oracle recomputes "
+                      f"every block summary per selection; oracle keys set up untimed; numpy float64"}
+
+
+def cpu_baseline_prefill(case, ch, seqs, n_queries: int, sample_note: str):
+    """The oracle's chunked prefill, extrapolated from a sample: per sampled sequence the
+    chunk's write (2,048 merged entries) is timed whole, and n_queries evenly spaced
+    chunk queries (first and last included) are timed; the chunk's time is the write
+    plus C times the mean query time.  Untimed set-up: every indexer key, and the
+    latent rows the sampled queries read (from a dry run of their selection)."""
+    from oracle import OracleCache
+    from oracle.indexer import index_scores, topk_select
+    from oracle.schedule import n_visible, run_prefill
+    cfg = case.cfg
+    C = cfg.C
+    qs = np.unique(np.linspace(0, C - 1, n_queries).round().astype(int)).tolist()
+    q_all, qi_all, wi_all, loc_all = (_host_bits(ch[n]) for n in ("q", "q_idx", "w_idx", "local"))
+    t_write = t_query = 0.0
+    n_q = 0
+    for b in seqs:
+        bt, P = _seq_table(case, b, (cfg.prior + C) // 2)
+        x, w, k = case.prior_tokens(b)
+        xb, wb, kb = _host_bits(x), _host_bits(w), _host_bits(k)
+        cx, cw, ck = _host_bits(ch["x"][b]), _host_bits(ch["w"][b]), _host_bits(ch["k_idx"][b])
+        oc = OracleCache(P, bt)
+        oc.write(0, 0, None, None, kb, latent=False)
+        oc.write(0, cfg.prior, None, None, ck, latent=False)
+        keys = oc.index_keys(0, np.arange(n_visible(cfg.prior + C - 1)))
+        need = set()
+        for i in qs:
+            nv = n_visible(cfg.prior + i)
+            need.update(topk_select(index_scores(qi_all[b, i], wi_all[b, i], keys[:nv]), cfg.topk).tolist())
+        need = np.array(sorted(j for j in need if 2 * j < cfg.prior), dtype=np.int64)
+        for run in np.split(need, np.nonzero(np.diff(need) != 1)[0] + 1) if need.size else []:
+            j0, j1 = int(run[0]), int(run[-1]) + 1
+            oc.write(0, 2 * j0, xb[2 * j0:2 * j1], wb[2 * j0:2 * j1], kb[j0:j1])
+        del x, w, k, xb, wb
+        t0 = time.perf_counter()
+        oc.write(0, cfg.prior, cx, cw, ck)                    # the chunk's write path
+        t1 = time.perf_counter()
+        run_prefill(oc, [cfg.prior], C, q_all[b:b + 1], qi_all[b:b + 1], wi_all[b:b + 1], loc_all[b:b + 1],
+                    topk=cfg.topk, W=cfg.window, queries=[(0, i) for i in qs])
+        t2 = time.perf_counter()
+        t_write += t1 - t0
+        t_query += t2 - t1
+        n_q += len(qs)
+    per_query = t_query / n_q
+    per_chunk = t_write / len(seqs) + C * per_query
+    cores, blas = _host_threads()
+    return {"value": round(C / per_chunk, 3), "unit": "tokens/s", "cores": cores, "blas_threads": blas,
+            "kind": "oracle", "extrapolated": True,
+            "sample": f"{sample_note}: sequences {list(seqs)} of {case.B}; per sequence the chunk's write "
+                      f"({C // 2} entries, timed whole: {t_write / len(seqs):.2f}s) and {len(qs)} evenly spaced "
+                      f"chunk queries incl. first and last ({per_query * 1e3:.1f} ms each); the chunk's time is "
+                      f"extrapolated as write + {C} x mean query time = {per_chunk:.1f}s; numpy float64"}
 
 
 if __name__ == "__main__":
