@@ -47,6 +47,17 @@
 // LDS layouts are swizzled (XOR of the 16-byte chunk index with the row) so that
 // both the QK reads (16 rows, same chunk) and the PV reads (one row, 16 chunks) hit
 // distinct banks.
+//
+// Order of loads.  Waves 0-3 load their window unit at once and their FP4 rows after
+// computing it; waves 4-7 the other way round.  Whatever a wave loads late is first
+// warmed into L2 with a few dword loads (window rows at the start, FP4 rows right
+// after the page lookups), and the late window unit is loaded in halves, each into an
+// FP4 slot as soon as that slot's last tile is done.  The row ids of a tile's DMAs are
+// gathered from the lanes holding them before any of the DMAs is issued, and the
+// operands of the next 128-dim chunk are read from LDS while the current one is
+// multiplied.  Measured on the MI355X, the kernel is bound by how fast a CU can pull
+// rows from L2 (about 16 bytes per clock per CU for 256-byte rows at full load) more
+// than by its arithmetic: every workgroup of a query reads all of the query's rows.
 #include "common.h"
 #include "internal.h"
 
@@ -66,11 +77,13 @@ constexpr int kMaxFtWave = CSA2_MAX_TOPK / kTile / kWavesA;   // 8 FP4 tiles per
 constexpr int kOffQ = kWavesA * kRegionB;              // q of the 16 heads: [16][512] bf16
 constexpr int kOffMask = kOffQ + 16 * kWinRowB;        // [8 waves][8] uint32
 constexpr int kOffMl = kOffMask + kWavesA * kMaxFtWave * 4;           // m[8][16], l[8][16]
-constexpr int kLdsA = kOffMl + 2 * kWavesA * 16 * 4;
+constexpr int kOffPf = kOffMl + 2 * kWavesA * 16 * 4;    // [8 waves][256 B]: landing area of L2 warm-ups
+constexpr int kLdsA = kOffPf + kWavesA * 256;
 constexpr int kDmaFp4 = 8 + 2;                         // DMA instructions per FP4 tile
 constexpr float kLazy = 8.0f;                          // log2 headroom of the lazy maximum
 constexpr int64_t kBatchPairs = 512;                   // from here on, the batched kernels
 static_assert(kUnit * kWinRowB <= kRegionB, "a window unit fits the region");
+static_assert(kSlotB >= (kUnit / 2) * kWinRowB, "half a window unit fits an FP4 slot");
 static_assert(16 * 256 * 4 <= kRegionB, "the merge's O[16][256] fits a region");
 static_assert(kLdsA <= 160 * 1024, "LDS budget");
 
@@ -131,6 +144,16 @@ __device__ __forceinline__ int slot_row(int g, int j) { return j < 4 ? 4 * g + j
 __device__ __forceinline__ int swz_fp4(int k, int r) { return k ^ (r & 15); }
 __device__ __forceinline__ int swz_win(int k, int r) { return k ^ (((k >> 4) & 3) ^ (r & 15)); }
 __device__ __forceinline__ int swz_q(int k, int h) { return k ^ (h & 15); }
+
+// LDS offset of row r of a window unit in a wave's region: rows 0-7 fill FP4 slot 0
+// and rows 8-15 start at slot 1, so each half of a unit can be loaded into one slot
+// as soon as that slot's last FP4 tile is done.
+__device__ __forceinline__ int win_row_off(int r) { return r * kWinRowB + (r >> 3) * (kSlotB - 8 * kWinRowB); }
+
+// 16-byte chunk c of head h's row in the merge's O area: the bits above the 16 bank
+// positions and the head's bits 2-3 are folded into the position, so the stores of a
+// wave (16 chunks x 4 heads) and the reads (32 consecutive chunks) spread over all banks.
+__device__ __forceinline__ int swz_o(int c, int h) { return c ^ ((c >> 4) & 3) ^ (h & 12); }
 
 // Window slot s (position t-W+1+s) holds a row: s < W and the position is >= 0.
 __device__ __forceinline__ bool win_valid(int W, int t, int s) { return s < W && t - (W - 1) + s >= 0; }
@@ -304,22 +327,36 @@ __global__ __launch_bounds__(kThreadsA) void attn_kernel(AttnArgs a) {
   auto q_op = [&](int c, int u) __attribute__((always_inline)) {
     return __builtin_bit_cast(bf16x8, lds_ld<u32x4>(qlds + n * kWinRowB + 16 * swz_q(16 * c + 4 * g + u, n)));
   };
-  // Window unit wu into the region: row r = slot 16wu + r.  A slot with no token
-  // reads the row of position t (always present) and is masked in the scores.
-  auto dma_window = [&](int wu) __attribute__((always_inline)) {
-    const int s0 = kUnit * wu;
-    const int row_t = a.prefill ? ci + W - 1 : (t < 0 ? 0 : t % W);
-    int ring = 0;   // ring row of slot s0 (decode), advanced by one per slot
-    if (!a.prefill) {
-      ring = (t - (W - 1) + s0) % W;
-      if (ring < 0) ring += W;
-    }
+  // Window unit wu into the region: row r = slot 16wu + r at win_row_off(r).  A slot
+  // with no token reads the row of position t (always present) and is masked in the
+  // scores.  Rows r0 .. r0+nr-1 of the unit.
+  const int row_t = a.prefill ? ci + W - 1 : (t < 0 ? 0 : t % W);
+  auto ring_row = [&](int s) __attribute__((always_inline)) {   // array row of slot s if it holds a token
+    if (a.prefill) return ci + s;
+    const int ring = (t - (W - 1) + s) % W;
+    return ring < 0 ? ring + W : ring;
+  };
+  auto win_row = [&](int s) __attribute__((always_inline)) { return win_valid(W, t, s) ? ring_row(s) : row_t; };
+  auto dma_window_rows = [&](int wu, int r0, int nr) __attribute__((always_inline)) {
+    const int s0 = kUnit * wu + r0;
+    int row = ring_row(s0);   // advanced by one per slot
 #pragma unroll 4
-    for (int r = 0; r < kUnit; ++r) {
+    for (int r = 0; r < nr; ++r) {
       const int s = s0 + r;
-      const int row = win_valid(W, t, s) ? (a.prefill ? ci + s : ring) : row_t;
-      dma16(win_b + (int64_t)row * CSA2_D_LATENT + 8 * swz_win(lane, r), region + r * kWinRowB);
-      ring = ring + 1 == W ? 0 : ring + 1;
+      const int rw = win_valid(W, t, s) ? row : row_t;
+      dma16(win_b + (int64_t)rw * CSA2_D_LATENT + 8 * swz_win(lane, r0 + r), region + win_row_off(r0 + r));
+      row = a.prefill ? row + 1 : (row + 1 == W ? 0 : row + 1);
+    }
+  };
+  auto dma_window = [&](int wu) __attribute__((always_inline)) { dma_window_rows(wu, 0, kUnit); };
+  // L2 warm-up of window unit wu (128 lines of 128 bytes; two dword loads per lane whose
+  // bytes land in this wave's scratch area, which nothing reads)
+  auto warm_window = [&](int wu) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int line = 64 * i + lane;
+      dma4(win_b + (int64_t)win_row(kUnit * wu + (line >> 3)) * CSA2_D_LATENT + 64 * (line & 7),
+           lds + kOffPf + 256 * w);
     }
   };
   // Waves w and w+4 share a SIMD.  Waves 0-3 take their window unit first and waves
@@ -327,7 +364,9 @@ __global__ __launch_bounds__(kThreadsA) void attn_kernel(AttnArgs a) {
   // its rows.
   const bool win_first = w < 4;
   const bool has_win = w < n_wu;
+  const bool late_win = has_win && !win_first;   // unit w is done after the FP4 tiles
   if (has_win && win_first) dma_window(w);
+  if (late_win) warm_window(w);
   wait_vm<0>();   // ids, q and the first window unit
   __syncthreads();   // q of every head is in LDS
 
@@ -354,38 +393,59 @@ __global__ __launch_bounds__(kThreadsA) void attn_kernel(AttnArgs a) {
     float z[4];
     {
       f32x4 sa[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-      const uint8_t* rp = region + n * kWinRowB;
+      const uint8_t* rp = region + win_row_off(n);
+      // chunk c: row n's dims 128c + 32g + 8u .. +7 and q's k-steps; chunk c+1's reads
+      // are issued before chunk c's products (the unit often runs with its SIMD's other
+      // wave idle, so nothing else hides the LDS latency)
+      struct WinIn {
+        u32x4 v[4], q[4];
+      };
+      auto win_load = [&](int c) __attribute__((always_inline)) {
+        WinIn in;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          in.v[u] = lds_ld<u32x4>(rp + 16 * swz_win(16 * c + 4 * g + u, n));
+          in.q[u] = __builtin_bit_cast(u32x4, q_op(c, u));
+        }
+        return in;
+      };
+      WinIn cur = win_load(0);
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        u32x4 v[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) v[u] = lds_ld<u32x4>(rp + 16 * swz_win(16 * c + 4 * g + u, n));
+        WinIn nxt;
+        if (c < 3) nxt = win_load(c + 1);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int u = 0; u < 4; ++u)
-          sa[u & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, v[u]), q_op(c, u),
-                                                              sa[u & 1], 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);   // one chunk's rows live at a time (register budget)
+          sa[u & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, cur.v[u]),
+                                                              __builtin_bit_cast(bf16x8, cur.q[u]), sa[u & 1], 0, 0, 0);
+        if (c < 3) cur = nxt;
+        __builtin_amdgcn_sched_barrier(0);
       }
       const f32x4 sv = sa[0] + sa[1];
 #pragma unroll
       for (int j = 0; j < 4; ++j) z[j] = win_valid(W, t, s0 + 4 * g + j) ? sv[j] * a.scale_log2 : -INFINITY;
     }
+    // value operands (rows 4g..4g+3, this lane's dims of each quarter), read before the
+    // softmax so their latency overlaps it
+    u32x4 v[NQ][4];
+#pragma unroll
+    for (int qi2 = 0; qi2 < NQ; ++qi2)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int r = 4 * g + j;
+        v[qi2][j] = lds_ld<u32x4>(region + win_row_off(r) + 16 * swz_win(4 * n + qd0 + qi2, r));
+      }
+    __builtin_amdgcn_sched_barrier(0);
     uint32_t ph[2], pl[2];
     softmax_scores<NQ, 4>(S, z, g, ph, pl);
     const s16x4 phv = __builtin_bit_cast(s16x4, u32x2{ph[0], ph[1]});
     const s16x4 plv = __builtin_bit_cast(s16x4, u32x2{pl[0], pl[1]});
 #pragma unroll
     for (int qi2 = 0; qi2 < NQ; ++qi2) {
-      const int qd = qd0 + qi2;
-      u32x4 v[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int r = 4 * g + j;
-        v[j] = lds_ld<u32x4>(region + r * kWinRowB + 16 * swz_win(4 * n + qd, r));
-      }
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
-        const uint32_t c[4] = {v[0][m], v[1][m], v[2][m], v[3][m]};
+        const uint32_t c[4] = {v[qi2][0][m], v[qi2][1][m], v[qi2][2][m], v[qi2][3][m]};
         pv_pair16<NQ>(S, qi2, m, c, phv, plv);
       }
     }
@@ -411,10 +471,25 @@ __global__ __launch_bounds__(kThreadsA) void attn_kernel(AttnArgs a) {
   // The page lookups have all been consumed; saying so here keeps the compiler from
   // waiting for every load in flight (the FP4 tiles' DMAs) at the FP4 loop's entry.
   wait_vm<0>();
-  // the window units this wave has not done yet (all of them for waves 4-7; beyond
-  // the first for windows longer than 128)
+  // Waves 0-3 load their FP4 rows only after their window unit: warm those rows' lines
+  // into L2 now (codes: two lines per row, scales: one).
+  if (win_first) {
+#pragma unroll
+    for (int u = 0; u < kMaxFtWave / 2; ++u) {
+      if (2 * u < nk) {
+        const int rr = rowv[u];
+        const uint8_t* cp = rr >= 0 ? a.lat_codes + (int64_t)rr * CSA2_LAT_CODE_BYTES : (const uint8_t*)a.q;
+        const uint8_t* sp = rr >= 0 ? a.lat_scales + (int64_t)rr * CSA2_LAT_SCALE_BYTES : (const uint8_t*)a.q;
+        dma4(cp, lds + kOffPf + 256 * w);
+        dma4(cp + 128, lds + kOffPf + 256 * w);
+        dma4(sp, lds + kOffPf + 256 * w);
+      }
+    }
+  }
+  // the window units this wave has not done yet: beyond the first, for windows longer
+  // than 128 (waves 4-7 load their first unit in halves as their FP4 slots free up)
   auto rest_of_window = [&]() __attribute__((always_inline)) {
-    for (int wu = win_first ? w + kWavesA : w; wu < n_wu; wu += kWavesA) {
+    for (int wu = w + kWavesA; wu < n_wu; wu += kWavesA) {
       wait_lds();
       dma_window(wu);
       wait_vm<0>();
@@ -427,31 +502,54 @@ __global__ __launch_bounds__(kThreadsA) void attn_kernel(AttnArgs a) {
   // ---- FP4 tiles: two slots, each refilled two tiles ahead ----
   // A row with no entry reads q's first bytes (always present) and is masked: its
   // score is -inf and its value scale is replaced by 0, so its codes stay finite.
-  auto dma_fp4 = [&](int k, uint8_t* slot) __attribute__((always_inline)) {
+  // The row of each of tile k's ten DMAs, fetched from the lanes holding them (all
+  // shuffles first, then the DMAs, so their latencies are not paid one by one).
+  struct Fp4Rows {
+    int r[10];
+  };
+  auto fp4_rows = [&](int k) __attribute__((always_inline)) {
     const int u = k >> 1, hk = 32 * (k & 1);
     int rw = rowv[0];
 #pragma unroll
     for (int uu = 1; uu < kMaxFtWave / 2; ++uu) rw = u == uu ? rowv[uu] : rw;
-    const int h = lane >> 4;
+    Fp4Rows fr;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) fr.r[i] = __shfl(rw, hk + 4 * i + (lane >> 4), kWave);   // codes: rows 4i + lane/16
+#pragma unroll
+    for (int i = 0; i < 2; ++i) fr.r[8 + i] = __shfl(rw, hk + 16 * i + (lane >> 2), kWave);   // scales: 16i + lane/4
+    return fr;
+  };
+  auto fp4_dma = [&](const Fp4Rows& fr, uint8_t* slot) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const int r = 4 * i + h;
-      const int rr = __shfl(rw, hk + r, kWave);
+      const int r = 4 * i + (lane >> 4), rr = fr.r[i];
       const void* src = rr >= 0 ? (const void*)(a.lat_codes + (int64_t)rr * CSA2_LAT_CODE_BYTES + 16 * swz_fp4(lane & 15, r))
                                 : (const void*)a.q;
       dma16(src, slot + 1024 * i);
     }
-    // scales: 4 bytes per lane, rows 16i + lane/4
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const int rr = __shfl(rw, hk + 16 * i + (lane >> 2), kWave);
+      const int rr = fr.r[8 + i];
       const void* src = rr >= 0 ? (const void*)(a.lat_scales + (int64_t)rr * CSA2_LAT_SCALE_BYTES + 4 * (lane & 3))
                                 : (const void*)a.q;
       dma4(src, slot + kCodeB + 256 * i);
     }
   };
-  if (nk > 0) dma_fp4(0, region);
-  if (nk > 1) dma_fp4(1, region + kSlotB);
+  auto dma_fp4 = [&](int k, uint8_t* slot) __attribute__((always_inline)) {
+    const Fp4Rows fr = fp4_rows(k);
+    __builtin_amdgcn_sched_barrier(0);
+    fp4_dma(fr, slot);
+  };
+  if (nk > 1) {   // both tiles' shuffles, then both tiles' DMAs
+    const Fp4Rows f0 = fp4_rows(0), f1 = fp4_rows(1);
+    __builtin_amdgcn_sched_barrier(0);
+    fp4_dma(f0, region);
+    fp4_dma(f1, region + kSlotB);
+  } else if (nk == 1) {
+    dma_fp4(0, region);
+  }
+  if (nk <= 1 && late_win) dma_window_rows(w, kUnit / 2, kUnit / 2);   // slot 1 holds no tile
+  if (nk == 0 && late_win) dma_window_rows(w, 0, kUnit / 2);
 
   // one FP4 tile from slot SL (a compile-time constant, so LDS offsets are immediates)
   auto fp4_tile = [&](int k, auto slot_c) __attribute__((always_inline)) {
@@ -462,24 +560,41 @@ __global__ __launch_bounds__(kThreadsA) void attn_kernel(AttnArgs a) {
     float z[8];
     {
       f32x4 sa[4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+      // operands of chunk c: rows n and 16+n, 16 code bytes each (dims 128c + 32g .. +31),
+      // the scale dwords holding that block's byte (byte g of dword c), and q's four
+      // k-steps; chunk c+1's are read while chunk c is multiplied
+      struct QkIn {
+        u32x4 c0, c1, q[4];
+        uint32_t s0w, s1w;
+      };
+      auto qk_load = [&](int c) __attribute__((always_inline)) {
+        QkIn in;
+        in.c0 = lds_ld<u32x4>(slot + n * CSA2_LAT_CODE_BYTES + 16 * swz_fp4(4 * c + g, n));
+        in.c1 = lds_ld<u32x4>(slot + (16 + n) * CSA2_LAT_CODE_BYTES + 16 * swz_fp4(4 * c + g, n));
+        in.s0w = lds_ld<uint32_t>(slot + kCodeB + n * CSA2_LAT_SCALE_BYTES + 4 * c);
+        in.s1w = lds_ld<uint32_t>(slot + kCodeB + (16 + n) * CSA2_LAT_SCALE_BYTES + 4 * c);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) in.q[u] = __builtin_bit_cast(u32x4, q_op(c, u));
+        return in;
+      };
+      QkIn cur = qk_load(0);
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        // rows n and 16+n: 16 code bytes (dims 128c + 32g .. +31) and the scale byte of
-        // that block (byte g of scale dword c)
-        const u32x4 c0 = lds_ld<u32x4>(slot + n * CSA2_LAT_CODE_BYTES + 16 * swz_fp4(4 * c + g, n));
-        const u32x4 c1 = lds_ld<u32x4>(slot + (16 + n) * CSA2_LAT_CODE_BYTES + 16 * swz_fp4(4 * c + g, n));
-        const uint32_t s0w = lds_ld<uint32_t>(slot + kCodeB + n * CSA2_LAT_SCALE_BYTES + 4 * c);
-        const uint32_t s1w = lds_ld<uint32_t>(slot + kCodeB + (16 + n) * CSA2_LAT_SCALE_BYTES + 4 * c);
-        const float sc0 = e8m0_scale(__builtin_amdgcn_ubfe(s0w, 8 * g, 8));
-        const float sc1 = e8m0_scale(__builtin_amdgcn_ubfe(s1w, 8 * g, 8));
+        QkIn nxt;
+        if (c < 3) nxt = qk_load(c + 1);
+        __builtin_amdgcn_sched_barrier(0);   // keep chunk c+1's reads ahead of chunk c's products
+        const float sc0 = e8m0_scale(__builtin_amdgcn_ubfe(cur.s0w, 8 * g, 8));
+        const float sc1 = e8m0_scale(__builtin_amdgcn_ubfe(cur.s1w, 8 * g, 8));
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          const bf16x8 qv = q_op(c, u);
-          sa[u & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, fp4x8_to_bf16x8(c0[u], sc0)),
+          const bf16x8 qv = __builtin_bit_cast(bf16x8, cur.q[u]);
+          sa[u & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, fp4x8_to_bf16x8(cur.c0[u], sc0)),
                                                               qv, sa[u & 1], 0, 0, 0);
           sa[2 + (u & 1)] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              __builtin_bit_cast(bf16x8, fp4x8_to_bf16x8(c1[u], sc1)), qv, sa[2 + (u & 1)], 0, 0, 0);
+              __builtin_bit_cast(bf16x8, fp4x8_to_bf16x8(cur.c1[u], sc1)), qv, sa[2 + (u & 1)], 0, 0, 0);
         }
+        if (c < 3) cur = nxt;
+        __builtin_amdgcn_sched_barrier(0);
       }
       const f32x4 s0v = sa[0] + sa[1], s1v = sa[2] + sa[3];
 #pragma unroll
@@ -523,21 +638,41 @@ __global__ __launch_bounds__(kThreadsA) void attn_kernel(AttnArgs a) {
       }
     }
   };
+  // Wait for tile j: the only loads issued after tile j's are the next tile's, or a
+  // half window unit loaded into a slot whose tiles are done (waves 4-7).
+  auto wait_tile = [&](int j) __attribute__((always_inline)) {
+    if (j + 1 < nk)
+      wait_vm<kDmaFp4>();
+    else if (late_win && (j >= 1 || nk == 1))
+      wait_vm<kUnit / 2>();
+    else
+      wait_vm<0>();
+  };
   for (int k = 0; k < nk; k += 2) {
-    if (k + 1 < nk) wait_vm<kDmaFp4>(); else wait_vm<0>();   // tile k landed; k+1 may be in flight
+    wait_tile(k);   // tile k landed; k+1 may be in flight
     fp4_tile(k, Slot0{});
     if (k + 2 < nk) {
       wait_lds();   // every read of slot 0 has returned
       dma_fp4(k + 2, region);
+    } else if (late_win) {
+      wait_lds();
+      dma_window_rows(w, 0, kUnit / 2);
     }
     if (k + 1 < nk) {
-      if (k + 2 < nk) wait_vm<kDmaFp4>(); else wait_vm<0>();
+      wait_tile(k + 1);
       fp4_tile(k + 1, Slot1{});
       if (k + 3 < nk) {
         wait_lds();
         dma_fp4(k + 3, region + kSlotB);
+      } else if (late_win) {
+        wait_lds();
+        dma_window_rows(w, kUnit / 2, kUnit / 2);
       }
     }
+  }
+  if (late_win) {
+    wait_vm<0>();
+    window_unit(w);
   }
 
   if (!win_first) rest_of_window();
@@ -559,11 +694,12 @@ __global__ __launch_bounds__(kThreadsA) void attn_kernel(AttnArgs a) {
   for (int ii = 0; ii < 4; ++ii)
 #pragma unroll
     for (int qi2 = 0; qi2 < NQ; ++qi2) {
-      float* dst = ow + (4 * g + ii) * kDimsP + (n * NQ + qi2) * 8;
-      *reinterpret_cast<f32x4*>(dst) = f32x4{S.acc[qi2 * 8 + 0][ii], S.acc[qi2 * 8 + 1][ii],
-                                             S.acc[qi2 * 8 + 2][ii], S.acc[qi2 * 8 + 3][ii]};
-      *reinterpret_cast<f32x4*>(dst + 4) = f32x4{S.acc[qi2 * 8 + 4][ii], S.acc[qi2 * 8 + 5][ii],
-                                                 S.acc[qi2 * 8 + 6][ii], S.acc[qi2 * 8 + 7][ii]};
+      const int h = 4 * g + ii, c = 2 * (n * NQ + qi2);   // local dims 4c .. 4c+7
+      float* row = ow + h * kDimsP;
+      *reinterpret_cast<f32x4*>(row + 4 * swz_o(c, h)) = f32x4{S.acc[qi2 * 8 + 0][ii], S.acc[qi2 * 8 + 1][ii],
+                                                             S.acc[qi2 * 8 + 2][ii], S.acc[qi2 * 8 + 3][ii]};
+      *reinterpret_cast<f32x4*>(row + 4 * swz_o(c + 1, h)) = f32x4{S.acc[qi2 * 8 + 4][ii], S.acc[qi2 * 8 + 5][ii],
+                                                                 S.acc[qi2 * 8 + 6][ii], S.acc[qi2 * 8 + 7][ii]};
     }
   __syncthreads();
 
@@ -574,9 +710,10 @@ __global__ __launch_bounds__(kThreadsA) void attn_kernel(AttnArgs a) {
   f32x4 part[kWavesA][kPer / 4];   // every read issued before the first is used
 #pragma unroll
   for (int v2 = 0; v2 < kWavesA; ++v2) {
-    const float* src = reinterpret_cast<const float*>(lds + v2 * kRegionB) + head * kDimsP + kPer * m;
+    const float* src = reinterpret_cast<const float*>(lds + v2 * kRegionB) + head * kDimsP;
 #pragma unroll
-    for (int i = 0; i < kPer / 4; ++i) part[v2][i] = *reinterpret_cast<const f32x4*>(src + 4 * i);
+    for (int i = 0; i < kPer / 4; ++i)
+      part[v2][i] = *reinterpret_cast<const f32x4*>(src + 4 * swz_o((kPer / 4) * m + i, head));
   }
   float mw[kWavesA], lw[kWavesA], M = -INFINITY;
 #pragma unroll
