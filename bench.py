@@ -120,21 +120,54 @@ def build_decode(case, fk, n_rep: int):
     return reps
 
 
-def recorded_traffic(kernel: str):
-    """HBM bytes per call of `kernel` (for the attention: split kernel plus combine)
-    from the committed counter summary, if the summary was taken on the current
-    source of that kernel (else None)."""
+def recorded_traffic(workload: str, call: str):
+    """HBM bytes per `call` (FETCH_SIZE + WRITE_SIZE, scaled by the calibration copy) of
+    `workload` from the committed counter summaries under profiles/, if they were taken
+    on the current sources of that call's kernels (else None)."""
+    import glob
     import hashlib
     import re
-    path = os.path.join(ROOT, "profiles", "pmc_traffic_decode_b32_ctx64k.md")
-    src = os.path.join(ROOT, "fp4_kv_cache_write_amd", "csrc", "attention.hip")
-    if kernel != "sparse_decode" or not (os.path.exists(path) and os.path.exists(src)):
-        return None
-    m = re.search(r"sparse_decode_call traffic_bytes_per_launch=(\d+) attention_hip_sha256=([0-9a-f]+)",
-                  open(path).read())
-    if not m or m.group(2) != hashlib.sha256(open(src, "rb").read()).hexdigest():
-        return None
-    return int(m.group(1))
+    pat = re.compile(r"traffic workload=(\S+) call=(\S+) bytes_per_launch=(\d+) sources=(\S+) sha256=([0-9a-f]+)")
+    csrc = os.path.join(ROOT, "fp4_kv_cache_write_amd", "csrc")
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "pmc_traffic_*.md"))):
+        for m in pat.finditer(open(path).read()):
+            if m.group(1) != workload or m.group(2) != call:
+                continue
+            h = hashlib.sha256()
+            for f in m.group(4).split(","):
+                fp = os.path.join(csrc, f)
+                if not os.path.exists(fp):
+                    return None
+                h.update(open(fp, "rb").read())
+            return int(m.group(3)) if h.hexdigest() == m.group(5) else None
+    return None
+
+
+def recorded_mfma_busy(workload: str):
+    """MFMA busy % per kernel of `workload` from the committed counter summary under
+    profiles/ (SQ_VALU_MFMA_BUSY_CYCLES over active cycles x SIMDs), for kernels whose
+    sources still have the recorded hash."""
+    import glob
+    import hashlib
+    import re
+    pat = re.compile(r"mfma workload=(\S+) kernel=(\S+) busy_pct=([0-9.]+) sources=(\S+) sha256=([0-9a-f]+)")
+    csrc = os.path.join(ROOT, "fp4_kv_cache_write_amd", "csrc")
+    out = {}
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "pmc_mfma_*.md"))):
+        for m in pat.finditer(open(path).read()):
+            if m.group(1) != workload:
+                continue
+            h = hashlib.sha256()
+            ok = True
+            for f in m.group(4).split(","):
+                fp = os.path.join(csrc, f)
+                if not os.path.exists(fp):
+                    ok = False
+                    break
+                h.update(open(fp, "rb").read())
+            if ok and h.hexdigest() == m.group(5):
+                out[m.group(2)] = float(m.group(3))
+    return out or None
 
 
 def decode_bytes(case):
@@ -325,7 +358,7 @@ def bench_decode(fk, cfg_id: int, steps: int, warmup: int, n_rep: int, use_graph
         totals = {n: per_call[n] * count[n] for n in per_call}
         dom = max(totals, key=totals.get)
         achieved = per_bytes[dom] / (per_call[dom] / 1e3) / 1e9
-        traffic = recorded_traffic(dom) if cfg_id == 1 else None
+        traffic = recorded_traffic(cfg.name, dom)
         roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                     "bytes_per_launch": per_bytes[dom], "avg_launch_us": round(per_call[dom] * 1e3, 2),
@@ -472,7 +505,8 @@ def bench_prefill(fk, steps: int, warmup: int, cpu_seqs=()):
             "unit": "tokens/s", "ms_per_step": round(ms, 4), "ms_write": round(ms_w, 4),
             "ms_index_attention": round(ms_a, 4), "flop_indexer": fl_idx, "flop_attention": fl_att,
             "roofline": {"bound": "mfma", "achieved": round(tfs, 2), "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
-                         "frac": round(tfs / MFMA_BF16_PEAK_TFS, 4), "traffic": None},
+                         "frac": round(tfs / MFMA_BF16_PEAK_TFS, 4), "traffic": None,
+                         "mfma_busy_pct_counters": recorded_mfma_busy(cfg.name)},
             "write_proj": write_proj_line, "dtype": "bf16", "steps": steps, "warmup": warmup,
             "cpu_baseline": cpu}
 
