@@ -9,12 +9,17 @@
 // ReLU(q_h . k_j) over 4 heads (the pages give no formula; this is the library's).
 //
 // Full scan (index_scan_kernel): one workgroup per (sequence, chunk of CH entries).
-// Each wave streams 16-entry groups of FP4 keys straight from the paged cache
-// (8 bytes per lane, a wave covers 512 contiguous bytes), converts them to bf16
-// with the hardware FP4 convert (scale folded in, exact) and scores the group with
-// two 16x16x32 bf16 MFMAs: A = the 4 indexer heads (rows 4..15 zero), B = 16 keys.
-// Lanes 0..15 then hold the 4 head dots of one entry each and form the score
-// without any cross-lane reduction.  Scores never leave LDS: after the chunk is
+// Each wave streams whole 64-entry pages of FP4 keys straight from the paged cache
+// with buffer loads off a per-page descriptor (8 bytes per lane and group of 16
+// entries, a wave covers 512 contiguous bytes), converts them to bf16 with the
+// hardware FP4 convert (scale folded in, exact) and scores a page with eight
+// 16x16x32 bf16 MFMAs into one accumulator: group u of the page meets the 4
+// indexer heads placed in rows 4u..4u+3 (the other rows zero), so lane l ends with
+// the 4 head dots of entry l and forms its score without any cross-lane reduction,
+// and the ReLU, weighting and key conversion run once per page, not once per group.
+// Measured on the MI355X at 8 x 524,288 entries, this cut the vector ALU work of
+// the stream by two thirds, which had bound it as much as the HBM reads.
+// Scores never leave LDS: after the chunk is
 // scored, the workgroup writes the block maxima (for the pool) and an exact local
 // top-K (select.h) as (key, entry) candidates in entry order.  The global top-K is
 // a subset of the union of the local top-Ks, so the merge is exact.
@@ -26,9 +31,8 @@ namespace csa2 {
 namespace {
 
 constexpr int kScanThreads = 512;
-constexpr int kScanRound = 4;        // groups of 16 entries a scan wave loads before scoring them (1 page)
+constexpr int kScanAhead = 2;        // pages a scan wave keeps in flight beyond the one it scores
 constexpr int kReindexRound = 8;     // groups of 16 pool slots a reindex wave loads before scoring them
-static_assert(kScanRound % 4 == 0, "a scan round covers whole 64-entry pages");
 constexpr int kMergeThreads = 1024;
 constexpr int kMergeCap = 32768;     // keys the merge / pool workgroup selects from
 constexpr int kReindexThreads = 512;
@@ -80,6 +84,58 @@ __device__ __forceinline__ float score16(u32x2 codes, uint32_t scale_byte, bf16x
   return wh[0] * relu0(acc[0]) + wh[1] * relu0(acc[1]) + wh[2] * relu0(acc[2]) + wh[3] * relu0(acc[3]);
 }
 
+// A-operands that score a whole 64-entry page with one accumulator: group u (entries
+// 16u..16u+15) is multiplied with the 4 heads placed in rows 4u..4u+3 and zero rows
+// elsewhere, so the eight MFMAs of a page add into one register set and each group
+// fills only its own 16 lanes.  Lane (m = l%16, g = l/16) of a[u][s] holds head m%4's
+// dims 8*(2g+s) .. +7 when m/4 == u, zero otherwise.
+__device__ __forceinline__ void load_q_frags_page(const uint16_t* __restrict__ q_idx, int b,
+                                                  bf16x8 (&a)[4][2]) {
+  static_assert(CSA2_H_INDEX == 4, "four groups of four heads fill the 16 rows");
+  const int lane = threadIdx.x & 63;
+  const int m = lane & 15, g = lane >> 4;
+  const uint16_t* q = q_idx + ((int64_t)b * CSA2_H_INDEX + (m & 3)) * CSA2_D_INDEX + 16 * g;
+  const u32x4 v0 = *reinterpret_cast<const u32x4*>(q);
+  const u32x4 v1 = *reinterpret_cast<const u32x4*>(q + 8);
+  const u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    a[u][0] = __builtin_bit_cast(bf16x8, (m >> 2) == u ? v0 : z);
+    a[u][1] = __builtin_bit_cast(bf16x8, (m >> 2) == u ? v1 : z);
+  }
+}
+
+// Scores of the 64 entries of a page: cd[u] holds the 8 code bytes at dims
+// 16g..16g+15 of entry 16u + l%16 and sb[u] that entry's scale byte for those dims.
+// Lane l returns the score of entry l.  A lane's own group adds its two products to
+// an accumulator that holds +0, and the other groups add exact zeros, so the score
+// is the one a separate 16-entry product gives, bit for bit.
+__device__ __forceinline__ float score_page(const u32x2 (&cd)[4], const uint32_t (&sb)[4],
+                                            const bf16x8 (&a)[4][2], const float (&wh)[4]) {
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const float sc = e8m0_scale(sb[u]);
+    u32x4 lo, hi;
+    lo.x = fp4x2_to_bf16x2<0>(cd[u].x, sc);
+    lo.y = fp4x2_to_bf16x2<1>(cd[u].x, sc);
+    lo.z = fp4x2_to_bf16x2<2>(cd[u].x, sc);
+    lo.w = fp4x2_to_bf16x2<3>(cd[u].x, sc);
+    hi.x = fp4x2_to_bf16x2<0>(cd[u].y, sc);
+    hi.y = fp4x2_to_bf16x2<1>(cd[u].y, sc);
+    hi.z = fp4x2_to_bf16x2<2>(cd[u].y, sc);
+    hi.w = fp4x2_to_bf16x2<3>(cd[u].y, sc);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u][0], __builtin_bit_cast(bf16x8, lo), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u][1], __builtin_bit_cast(bf16x8, hi), acc, 0, 0, 0);
+  }
+  return wh[0] * relu0(acc[0]) + wh[1] * relu0(acc[1]) + wh[2] * relu0(acc[2]) + wh[3] * relu0(acc[3]);
+}
+
+// Buffer descriptor of one page's bytes (raw buffer, dword 3 as gfx9 wants it).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t page_rsrc(const uint8_t* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), 0, bytes, 0x00020000);
+}
+
 // Maxima of blocks of CB consecutive keys, from the keys in registers (thread t holds
 // positions t*KPT .. +KPT-1): a thread holds KPT/CB whole blocks, or a block spans
 // CB/KPT adjacent lanes.  Block k goes to bm[k] for k < nb.
@@ -129,7 +185,6 @@ struct ScanArgs {
 template <int CHUNK, int NT = kScanThreads>
 __global__ __launch_bounds__(NT) void index_scan_kernel(ScanArgs a) {
   constexpr int KPT = CHUNK / NT;
-  constexpr int GPW = CHUNK / 16 / (NT / 64);   // groups per wave
   extern __shared__ __align__(16) uint32_t smem[];
   uint32_t* keys = smem;                          // [CHUNK]
   uint32_t* hist = smem + CHUNK;                  // [kSelectHist]
@@ -148,71 +203,67 @@ __global__ __launch_bounds__(NT) void index_scan_kernel(ScanArgs a) {
   const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
   const int n = lane & 15, g = lane >> 4;
 
-  bf16x8 a0, a1;
-  load_q_frags(a.q_idx, b, a0, a1);
+  bf16x8 aq[4][2];
+  load_q_frags_page(a.q_idx, b, aq);
   float wh[4];
 #pragma unroll
   for (int h = 0; h < 4; ++h) wh[h] = bf16_to_f32(a.w_idx[b * CSA2_H_INDEX + h]);
 
-  // Wave w streams groups [w*GPW, (w+1)*GPW) of 16 entries in rounds of kScanRound
-  // groups (1 page).  A round's page ids are fetched with scalar loads, then all its
-  // code and scale loads are issued; the next round is issued before this one is
-  // scored, so its memory latency overlaps the scoring.
+  // Wave w streams the NPW pages [w*NPW, (w+1)*NPW) of the chunk, one page a round.
+  // The page ids come first, with one vector load (lane k: the wave's page k).  A
+  // round's loads are buffer loads from a descriptor of its page: the page base sits
+  // in scalar registers and every lane's offsets are constants, so issuing a round
+  // takes no vector ALU work.  LA rounds are in flight while one is scored.
+  constexpr int NPW = CHUNK / CSA2_PAGE / (NT / 64);   // pages per wave
+  static_assert(NPW <= kWave && NPW * (NT / 64) * CSA2_PAGE == CHUNK, "one page id per lane");
   const int32_t* bt = a.block_table + (int64_t)b * a.max_pages;
+  int pgv;
+  {
+    const int ew0 = e0 + wid * NPW * CSA2_PAGE;   // wave-uniform
+    const int pi = (ew0 >> 6) + lane;
+    const int p = bt[min(pi, a.max_pages - 1)];
+    pgv = (lane < NPW && ew0 + CSA2_PAGE * lane < n_vis && pi < a.max_pages && p >= 0 && p < a.n_pages) ? p : -1;
+  }
+  // lane (n, g): code bytes 8g.. of entry 16u + n, scale byte g/2 of that entry
+  const int voff_code = n * CSA2_IDX_CODE_BYTES + 8 * g;
+  const int voff_scale = n * CSA2_IDX_SCALE_BYTES + (g >> 1);
   struct Round {
-    int pg[kScanRound / 4];
-    u32x2 cd[kScanRound];
-    uint32_t sp[kScanRound / 4];   // lane l: the two scale bytes of entry l of page q
+    u32x2 cd[4];
+    uint32_t sb[4];
   };
-  auto load_round = [&](int r0, Round& R) {
-    const int eb0 = e0 + (wid * GPW + r0) * 16;               // wave-uniform round start
+  auto load_round = [&](int r, Round& R) {
+    const int pg = __builtin_amdgcn_readlane(pgv, r);
+    const int64_t pc = pg >= 0 ? pg : 0;   // absent page: page 0 is read, its keys dropped
+    const __amdgpu_buffer_rsrc_t rc = page_rsrc(a.idx_codes + pc * (CSA2_PAGE * CSA2_IDX_CODE_BYTES),
+                                                CSA2_PAGE * CSA2_IDX_CODE_BYTES);
+    const __amdgpu_buffer_rsrc_t rs = page_rsrc(a.idx_scales + pc * (CSA2_PAGE * CSA2_IDX_SCALE_BYTES),
+                                                CSA2_PAGE * CSA2_IDX_SCALE_BYTES);
 #pragma unroll
-    for (int q = 0; q < kScanRound / 4; ++q) {
-      const int pi = (eb0 >> 6) + q;
-      int p = (eb0 + 64 * q < n_vis && pi < a.max_pages) ? bt[pi] : -1;
-      R.pg[q] = (p >= 0 && p < a.n_pages) ? p : -1;
-    }
-    // Every lane loads (lanes without an entry read row 0, which every cache has, and
-    // drop the value): no branch splits the loads, so the wait counts before each
-    // group's scoring stay exact while the later loads are in flight.  A page's 64
-    // entries keep their scales contiguous: one 2-byte load per lane covers them.
+    for (int u = 0; u < 4; ++u)
+      R.cd[u] = __builtin_amdgcn_raw_buffer_load_b64(rc, voff_code + u * 16 * CSA2_IDX_CODE_BYTES, 0, 0);
 #pragma unroll
-    for (int q = 0; q < kScanRound / 4; ++q) {
-      const int e = eb0 + 64 * q + lane;
-      const bool ok = R.pg[q] >= 0 && e < n_vis;
-      const int64_t row = ok ? (int64_t)R.pg[q] * CSA2_PAGE + lane : 0;
-      const uint32_t sv = *reinterpret_cast<const uint16_t*>(a.idx_scales + row * CSA2_IDX_SCALE_BYTES);
-      R.sp[q] = ok ? sv : 0u;
-    }
-#pragma unroll
-    for (int u = 0; u < kScanRound; ++u) {
-      const int e = eb0 + u * 16 + n;
-      const int page = R.pg[u >> 2];
-      const bool ok = page >= 0 && e < n_vis;
-      const int64_t row = ok ? (int64_t)page * CSA2_PAGE + (e & (CSA2_PAGE - 1)) : 0;
-      const u32x2 cv = *reinterpret_cast<const u32x2*>(a.idx_codes + row * CSA2_IDX_CODE_BYTES + 8 * g);
-      R.cd[u] = ok ? cv : u32x2{0u, 0u};
-    }
+    for (int u = 0; u < 4; ++u)
+      R.sb[u] = __builtin_amdgcn_raw_buffer_load_b8(rs, voff_scale + u * 16 * CSA2_IDX_SCALE_BYTES, 0, 0);
   };
-  auto score_round = [&](int r0, const Round& R) {
-#pragma unroll
-    for (int u = 0; u < kScanRound; ++u) {
-      const int le = (wid * GPW + r0 + u) * 16;
-      if (e0 + le >= n_vis) break;                        // wave-uniform
-      // scale byte g/2 of entry n of this group: lane 16(u%4) + n of the page's load
-      const uint32_t sw = (uint32_t)__shfl((int)R.sp[u >> 2], 16 * (u & 3) + n, kWave);
-      const float s = score16(R.cd[u], (sw >> (8 * (g >> 1))) & 0xffu, a0, a1, wh);
-      if (lane < 16) keys[le + n] = (le + n < n_in && R.pg[u >> 2] >= 0) ? score_key(s) : 0u;   // absent page: no entry
-    }
+  auto score_round = [&](int r, const Round& R) {
+    const int le = (wid * NPW + r) * CSA2_PAGE;   // chunk position of the page's entry 0
+    const bool present = __builtin_amdgcn_readlane(pgv, r) >= 0;
+    const float s = score_page(R.cd, R.sb, aq, wh);
+    keys[le + lane] = (present && le + lane < n_in) ? score_key(s) : 0u;   // absent page: no entry
   };
-  static_assert(GPW % kScanRound == 0, "whole rounds per wave");
-  constexpr int NR = GPW / kScanRound;
-  Round rr[2];
-  load_round(0, rr[0]);
+  constexpr int LA = kScanAhead;                 // rounds in flight beyond the one scored
+  // A wave with no visible entry skips the stream (its keys are cleared below with the
+  // chunk's tail).  Any other wave streams all its pages with no branch between a
+  // round's loads and its scoring (entries past the end score to key 0).
+  if (e0 + wid * NPW * CSA2_PAGE < n_vis) {
+    Round rr[LA + 1];
 #pragma unroll
-  for (int i = 0; i < NR; ++i) {
-    if (i + 1 < NR) load_round((i + 1) * kScanRound, rr[(i + 1) & 1]);
-    score_round(i * kScanRound, rr[i & 1]);
+    for (int i = 0; i < LA && i < NPW; ++i) load_round(i, rr[i]);
+#pragma unroll
+    for (int i = 0; i < NPW; ++i) {
+      if (i + LA < NPW) load_round(i + LA, rr[(i + LA) % (LA + 1)]);
+      score_round(i, rr[i % (LA + 1)]);
+    }
   }
   // tail of a partial chunk: keys of absent entries are 0
   for (int i = ((n_in + 15) & ~15) + threadIdx.x; i < CHUNK; i += NT) keys[i] = 0u;
