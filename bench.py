@@ -58,6 +58,8 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="oracle time for the headline line (secondary lines take half)")
     p.add_argument("--no-graph", action="store_true", help="time eager launches instead of graph replay")
+    p.add_argument("--unfused-write", action="store_true",
+                   help="run the step's write as its own call instead of inside the first Full layer's scan")
     p.add_argument("--overlap-layers", action="store_true",
                    help="fork each layer's attention onto its own stream (ignores that a layer's queries "
                         "come from the previous layer's output; for reference only)")
@@ -170,7 +172,7 @@ def recorded_mfma_busy(workload: str):
     return out or None
 
 
-def decode_bytes(case):
+def decode_bytes(case, fused_write: bool = False):
     """Algorithmic HBM bytes of every call type for one step: each byte a call must
     read or write, counted once.  Full: every visible indexer key (BYTES_IDX each), the
     520 B of indexer query and head weights, the top-K and pool written.  Reindex: the
@@ -199,12 +201,18 @@ def decode_bytes(case):
             count["index_full"] += 1
         elif sp.mode == "reindex":
             count["reindex"] += 1
-    step = sum(per[n] * count[n] for n in per)
+    if fused_write and cfg.layers[0].mode == "full":
+        # the step's write runs inside the first Full layer's scan (csa2_write_index_full)
+        per["write_index_full"] = per["write_kv"] + per["index_full"]
+        count["write_index_full"] = 1
+        count["write_kv"] = 0
+        count["index_full"] -= 1
+    step = sum(per[n] * count.get(n, 0) for n in per)
     return per, count, step
 
 
 def bench_decode(fk, cfg_id: int, steps: int, warmup: int, n_rep: int, use_graph: bool, per_call_timing: bool,
-                 concurrent: bool = False):
+                 concurrent: bool = False, fused_write: bool = True):
     from synth import CONFIGS, make_decode_case
     cfg = CONFIGS[cfg_id]
     log(f"building {cfg.name} ({n_rep} replicas)")
@@ -230,12 +238,22 @@ def bench_decode(fk, cfg_id: int, steps: int, warmup: int, n_rep: int, use_graph
     def calls(r):
         R = reps[r]
         Wr = R.write
-        out = [("write_kv", lambda: fk.write_kv(R.cache, Wr["start"], Wr["x"], Wr["w"], Wr["k"]))]
+        fuse = fused_write and cfg.layers[0].mode == "full"
+        out = [] if fuse else [("write_kv", lambda: fk.write_kv(R.cache, Wr["start"], Wr["x"], Wr["w"], Wr["k"]))]
         cur = None
         nxt = 0
         for l, sp in enumerate(cfg.layers):
             L = R.layers[l]
-            if sp.mode == "full":
+            if sp.mode == "full" and l == 0 and fuse:
+                tk = tk_buf[nxt]
+                nxt ^= 1
+                pb = sp.pool_blocks
+                out.append(("write_index_full", lambda L=L, tk=tk, pb=pb: fk.write_index_full(
+                    R.cache, Wr["start"], Wr["x"], Wr["w"], Wr["k"], ctx, max_ctx, L["q_idx"], L["w_idx"],
+                    topk=topk, pool_blocks=pb, cand_block=cfg.cand_block, ws=ws_full, topk_idx=tk,
+                    pool=pool if pb > 0 else None)))
+                cur = tk
+            elif sp.mode == "full":
                 tk = tk_buf[nxt]
                 nxt ^= 1
                 pb = sp.pool_blocks
@@ -284,7 +302,7 @@ def bench_decode(fk, cfg_id: int, steps: int, warmup: int, n_rep: int, use_graph
         run_step(r)
     torch.cuda.synchronize()
 
-    per_bytes, count, step_bytes = decode_bytes(case)
+    per_bytes, count, step_bytes = decode_bytes(case, fused_write)
     graphs = []
     if use_graph:
         try:
@@ -329,7 +347,8 @@ def bench_decode(fk, cfg_id: int, steps: int, warmup: int, n_rep: int, use_graph
     if per_call_timing:
         # each call type alone: a graph holding that call once per replica, replayed 8 times
         # (launched and timed on the current stream)
-        for name in [n for n in ("write_kv", "index_full", "reindex", "sparse_decode") if count[n] > 0]:
+        for name in [n for n in ("write_kv", "write_index_full", "index_full", "reindex", "sparse_decode")
+                     if count.get(n, 0) > 0]:
             try:
                 s = torch.cuda.Stream()
                 s.wait_stream(torch.cuda.current_stream())
@@ -614,7 +633,9 @@ def main() -> int:
         return 0
 
     cfg_id = {"c0": 0, "c1": 1, "c2": 2, "c4": 4, "c5": 5}[args.workload]
-    d = bench_decode(fk, cfg_id, args.steps, args.warmup, args.replicas, not args.no_graph, True, args.overlap_layers)
+    fused = not args.unfused_write
+    d = bench_decode(fk, cfg_id, args.steps, args.warmup, args.replicas, not args.no_graph, True, args.overlap_layers,
+                     fused)
     case = d["case"]
     cfg = case.cfg
     secondary = {}
@@ -623,7 +644,7 @@ def main() -> int:
     if args.workload == "c1" and not args.no_secondary:
         def decode_line(cid, n_rep, cpu_seqs):
             r = bench_decode(fk, cid, max(20, args.steps // 4), max(5, args.warmup // 4), n_rep, not args.no_graph,
-                             True, args.overlap_layers)
+                             True, args.overlap_layers, fused)
             c = r["case"]
             out = {"workload": c.cfg.name, "value": round(r["qps"], 1), "unit": "queries/s",
                    "ms_per_step": round(r["ms"], 5), "achieved_gbs": round(r["gbs"], 1),
@@ -688,6 +709,8 @@ def main() -> int:
                    "entries_per_seq": max(case.n_vis), "H": cfg.H, "topk": cfg.topk, "window": cfg.window,
                    "pool_blocks": max([sp.pool_blocks for sp in cfg.layers] + [0]), "cand_block": cfg.cand_block,
                    "layers": ",".join(sp.mode for sp in cfg.layers), "write_per_step": True,
+                   "write": ("inside the first Full layer's scan (csa2_write_index_full)"
+                             if fused and cfg.layers[0].mode == "full" else "its own call (csa2_write_kv)"),
                    "replicas": len(d["reps"]), "launch": ("hip-graph" if d["use_graph"] else "eager") +
                    ("; each layer's attention on its own forked stream (layers overlapped)" if args.overlap_layers
                     else "; layers in order on one stream")},

@@ -19,7 +19,7 @@ D_LATENT, D_INDEX, H_INDEX, PAGE = 512, 64, 4, 64
 FN_INDEX_FULL, FN_REINDEX, FN_SPARSE_DECODE, FN_PREFILL_CHUNK = 1, 2, 3, 4
 
 EXPORTS = ("csa2_bytes_per_entry", "csa2_strerror", "csa2_workspace_size", "csa2_write_kv", "csa2_write_kv_proj", "csa2_block_keys",
-           "csa2_index_full", "csa2_index_full_noalloc", "csa2_reindex", "csa2_sparse_decode", "csa2_prefill_chunk",
+           "csa2_index_full", "csa2_write_index_full", "csa2_index_full_noalloc", "csa2_reindex", "csa2_sparse_decode", "csa2_prefill_chunk",
            "csa2_debug_gather", "csa2_schedule_workspace_size", "csa2_schedule_create",
            "csa2_schedule_launch", "csa2_schedule_destroy")
 LAYER_MODES = {"full": 0, "reindex": 1, "reuse": 2}
@@ -71,6 +71,8 @@ def lib() -> ctypes.CDLL:
         L.csa2_block_keys.argtypes = [C, C, I, P, I64, I, P, I, P, P]
         L.csa2_index_full.restype = I
         L.csa2_index_full.argtypes = [C, I, P, I64, P, P, I, I, I, P, P, P, SZ, P]
+        L.csa2_write_index_full.restype = I
+        L.csa2_write_index_full.argtypes = [C, I, P, I, P, P, P, I, P, I64, P, P, I, I, I, P, P, P, SZ, P]
         L.csa2_index_full_noalloc.restype = I
         L.csa2_index_full_noalloc.argtypes = [C, I, P, I64, P, P, I, I, I, P, P, P]
         L.csa2_reindex.restype = I
@@ -263,6 +265,39 @@ def index_full(cache: PagedCache, ctx_len: torch.Tensor, max_ctx: int, q_idx: to
     _check(lib().csa2_index_full(cache.ref, B, _ptr(ctx_len), max_ctx, _ptr(q_idx), _ptr(w_idx), topk,
                                  pool_blocks, cand_block, _ptr(topk_idx), _ptr(pool), _ptr(ws), wsb,
                                  _stream(stream)), "csa2_index_full")
+    return topk_idx, pool
+
+
+def write_index_full(cache: PagedCache, start_tok: torch.Tensor, x: torch.Tensor, w: Optional[torch.Tensor],
+                     k_idx: torch.Tensor, ctx_len: torch.Tensor, max_ctx: int, q_idx: torch.Tensor,
+                     w_idx: torch.Tensor, topk: int = 512, pool_blocks: int = 0, cand_block: int = 8,
+                     ws: Optional[torch.Tensor] = None, topk_idx: Optional[torch.Tensor] = None,
+                     pool: Optional[torch.Tensor] = None, stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """csa2_write_index_full: write_kv(cache, start_tok, x, w, k_idx) then index_full(...),
+    in one launch sequence with the same results."""
+    ratio = cache.ratio
+    B, T = x.shape[0], x.shape[1]
+    _bf16(x, "x", (B, T, D_LATENT))
+    if ratio == 2 or w is not None:
+        _bf16(w, "w", (B, T, D_LATENT))
+    _bf16(k_idx, "k_idx", (B, T // ratio, D_INDEX))
+    _need(start_tok, torch.int32, "start_tok", (B,))
+    _need(ctx_len, torch.int32, "ctx_len", (B,))
+    _bf16(q_idx, "q_idx", (B, H_INDEX, D_INDEX))
+    _bf16(w_idx, "w_idx", (B, H_INDEX))
+    dev = q_idx.device
+    if topk_idx is None:
+        topk_idx = torch.empty((B, topk), dtype=torch.int32, device=dev)
+    if pool_blocks > 0 and pool is None:
+        pool = torch.empty((B, pool_blocks), dtype=torch.int32, device=dev)
+    if ws is None:
+        ws = workspace(FN_INDEX_FULL, device=dev, B=B, max_ctx=max_ctx, topk=topk, pool_blocks=pool_blocks,
+                       ratio=ratio)
+    wsb = ws.numel() if ws is not None else 0
+    _check(lib().csa2_write_index_full(cache.ref, B, _ptr(start_tok), T, _ptr(x), _ptr(w), _ptr(k_idx), ratio,
+                                       _ptr(ctx_len), max_ctx, _ptr(q_idx), _ptr(w_idx), topk, pool_blocks,
+                                       cand_block, _ptr(topk_idx), _ptr(pool), _ptr(ws), wsb, _stream(stream)),
+           "csa2_write_index_full")
     return topk_idx, pool
 
 

@@ -144,6 +144,24 @@ int csa2_index_full(const csa2_cache_t* cache, int B, const int32_t* ctx_len, in
                            topk_idx, pool, ws, (hipStream_t)stream);
 }
 
+int csa2_write_index_full(const csa2_cache_t* cache, int B, const int32_t* start_tok, int T_new,
+                          const uint16_t* x, const uint16_t* w, const uint16_t* k_idx, int ratio,
+                          const int32_t* ctx_len, int64_t max_ctx, const uint16_t* q_idx, const uint16_t* w_idx,
+                          int topk, int pool_blocks, int cand_block, int32_t* topk_idx, int32_t* pool, void* ws,
+                          size_t ws_bytes, void* stream) {
+  if (!cache_ok(cache) || B <= 0 || !start_tok || !x || !k_idx) return CSA2_EINVAL;
+  if (ratio != cache_ratio(*cache)) return CSA2_EINVAL;
+  if (ratio == 2 && (!w || T_new <= 0 || (T_new & 1))) return CSA2_EINVAL;
+  if (ratio == 1 && T_new <= 0) return CSA2_EINVAL;
+  IndexFullPlan p{};
+  const int rc = index_full_check(cache, B, ctx_len, max_ctx, q_idx, w_idx, topk, pool_blocks,
+                                  cand_block, topk_idx, pool, &p);
+  if (rc != CSA2_OK) return rc;
+  if (p.total > 0 && (!ws || ws_bytes < p.total)) return CSA2_EWORKSPACE;
+  return launch_write_index_full(*cache, B, start_tok, T_new, x, w, k_idx, ctx_len, max_ctx, q_idx, w_idx, topk,
+                                 pool_blocks, cand_block, topk_idx, pool, ws, (hipStream_t)stream);
+}
+
 int csa2_index_full_noalloc(const csa2_cache_t* cache, int B, const int32_t* ctx_len, int64_t max_ctx,
                             const uint16_t* q_idx, const uint16_t* w_idx, int topk, int pool_blocks,
                             int cand_block, int32_t* topk_idx, int32_t* pool, void* stream) {

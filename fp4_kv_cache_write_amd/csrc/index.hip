@@ -24,6 +24,7 @@
 // top-K (select.h) as (key, entry) candidates in entry order.  The global top-K is
 // a subset of the union of the local top-Ks, so the merge is exact.
 #include "common.h"
+#include "entry_write.h"
 #include "internal.h"
 #include "select.h"
 
@@ -178,6 +179,7 @@ struct ScanArgs {
   int32_t* cand_idx;
   int32_t* cand_cnt;
   uint32_t* block_max;
+  WriteArgs wr;          // the step's write, done by this launch (wr.x == nullptr: none)
 };
 
 // NT threads stream one chunk: 512, or 1024 when the grid leaves one workgroup per
@@ -194,14 +196,38 @@ __global__ __launch_bounds__(NT) void index_scan_kernel(ScanArgs a) {
   const int n_vis = n_visible_entries(a.ctx_len, b, a.max_ctx, a.vshift);
   const int e0 = c * CHUNK;
   const int64_t slot = (int64_t)b * a.n_chunks + c;
+  const int lane = threadIdx.x & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
+  constexpr int NW = NT / 64;
+  constexpr int NPW = CHUNK / CSA2_PAGE / NW;   // pages per wave
+
+  // The step's write, when this launch performs it (the scan then sees the written
+  // keys, as if the write had run first).  Entry j = j0 + i of sequence b's write is
+  // stored by the wave that streams j's page, before that wave reads the page, when
+  // j is visible; the entries no chunk streams are spread over all waves of the
+  // sequence's workgroups here.
+  int wj0 = -1;
+  if (a.wr.x != nullptr) {
+    wj0 = write_first_entry(a.wr, b);
+    if (wj0 >= 0) {
+      const int stride = a.n_chunks * NW;
+      for (int i = max(0, n_vis - wj0) + c * NW + wid; i < a.wr.half; i += stride)
+        write_entry_wave(a.wr, b, i, lane);
+    }
+  }
   if (e0 >= n_vis) {
     if (threadIdx.x == 0) a.cand_cnt[slot] = 0;
     return;
   }
   const int n_in = min(CHUNK, n_vis - e0);
-  const int lane = threadIdx.x & 63;
-  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
   const int n = lane & 15, g = lane >> 4;
+  if (wj0 >= 0) {
+    const int lo = max(wj0, e0 + wid * NPW * CSA2_PAGE);
+    const int hi = min(min(wj0 + a.wr.half, e0 + (wid + 1) * NPW * CSA2_PAGE), n_vis);
+    for (int j = lo; j < hi; ++j) write_entry_wave(a.wr, b, j - wj0, lane);
+    // the stores are complete before this wave's loads of the same rows are issued
+    if (lo < hi) __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+  }
 
   bf16x8 aq[4][2];
   load_q_frags_page(a.q_idx, b, aq);
@@ -214,8 +240,7 @@ __global__ __launch_bounds__(NT) void index_scan_kernel(ScanArgs a) {
   // round's loads are buffer loads from a descriptor of its page: the page base sits
   // in scalar registers and every lane's offsets are constants, so issuing a round
   // takes no vector ALU work.  LA rounds are in flight while one is scored.
-  constexpr int NPW = CHUNK / CSA2_PAGE / (NT / 64);   // pages per wave
-  static_assert(NPW <= kWave && NPW * (NT / 64) * CSA2_PAGE == CHUNK, "one page id per lane");
+  static_assert(NPW <= kWave && NPW * NW * CSA2_PAGE == CHUNK, "one page id per lane");
   const int32_t* bt = a.block_table + (int64_t)b * a.max_pages;
   int pgv;
   {
@@ -713,9 +738,12 @@ IndexFullPlan plan_index_full(int B, int64_t max_nvis, int topk, int pool_blocks
   return p;
 }
 
-int launch_index_full(const csa2_cache_t& c, int B, const int32_t* ctx_len, int64_t max_ctx,
-                      const uint16_t* q_idx, const uint16_t* w_idx, int topk, int pool_blocks,
-                      int cand_block, int32_t* topk_idx, int32_t* pool, void* ws, hipStream_t s) {
+namespace {
+
+int index_full_impl(const csa2_cache_t& c, int B, const int32_t* ctx_len, int64_t max_ctx,
+                    const uint16_t* q_idx, const uint16_t* w_idx, int topk, int pool_blocks,
+                    int cand_block, int32_t* topk_idx, int32_t* pool, void* ws, const WriteArgs& wr,
+                    hipStream_t s) {
   const int vs = vis_shift(c);
   const int64_t max_nvis = max_ctx >> vs;
   const IndexFullPlan p = plan_index_full(B, max_nvis, topk, pool_blocks, cand_block);
@@ -742,6 +770,7 @@ int launch_index_full(const csa2_cache_t& c, int B, const int32_t* ctx_len, int6
   sa.cand_idx = reinterpret_cast<int32_t*>(w + p.off_cand_idx);
   sa.cand_cnt = reinterpret_cast<int32_t*>(w + p.off_cand_cnt);
   sa.block_max = reinterpret_cast<uint32_t*>(w + p.off_blockmax);
+  sa.wr = wr;
   const size_t scan_lds = (size_t)(p.chunk + kSelectHist + kSelectScratch) * 4;
   const int64_t grid = (int64_t)B * p.n_chunks;
   if (grid > 0x7fffffff) return CSA2_EUNSUPPORTED;
@@ -805,6 +834,26 @@ int launch_index_full(const csa2_cache_t& c, int B, const int32_t* ctx_len, int6
   else
     hipLaunchKernelGGL(index_merge_kernel<32>, mgrid, dim3(kMergeThreads), 0, s, ma);
   return hip_status();
+}
+
+}  // namespace
+
+int launch_index_full(const csa2_cache_t& c, int B, const int32_t* ctx_len, int64_t max_ctx,
+                      const uint16_t* q_idx, const uint16_t* w_idx, int topk, int pool_blocks,
+                      int cand_block, int32_t* topk_idx, int32_t* pool, void* ws, hipStream_t s) {
+  WriteArgs none{};
+  return index_full_impl(c, B, ctx_len, max_ctx, q_idx, w_idx, topk, pool_blocks, cand_block, topk_idx, pool, ws,
+                         none, s);
+}
+
+int launch_write_index_full(const csa2_cache_t& c, int B, const int32_t* start_tok, int T_new, const uint16_t* x,
+                            const uint16_t* w, const uint16_t* k_idx, const int32_t* ctx_len, int64_t max_ctx,
+                            const uint16_t* q_idx, const uint16_t* w_idx, int topk, int pool_blocks,
+                            int cand_block, int32_t* topk_idx, int32_t* pool, void* ws, hipStream_t s) {
+  const int ratio = cache_ratio(c);
+  const WriteArgs wr = write_args(c, start_tok, T_new / ratio, x, w, k_idx, ratio);
+  return index_full_impl(c, B, ctx_len, max_ctx, q_idx, w_idx, topk, pool_blocks, cand_block, topk_idx, pool, ws,
+                         wr, s);
 }
 
 size_t reindex_ws(int B) { return align256((size_t)B * kReindexCap * 4); }

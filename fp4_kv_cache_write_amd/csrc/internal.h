@@ -44,6 +44,13 @@ int launch_debug_gather(const csa2_cache_t& c, int B, const int32_t* idx, int n,
 int launch_index_full(const csa2_cache_t& c, int B, const int32_t* ctx_len, int64_t max_ctx,
                       const uint16_t* q_idx, const uint16_t* w_idx, int topk, int pool_blocks,
                       int cand_block, int32_t* topk_idx, int32_t* pool, void* ws, hipStream_t s);
+// The step's write (as launch_write_kv) and the Full selection (as launch_index_full)
+// in one launch: the scan stores each written entry that it streams before reading
+// it, so the selection is the one the two calls give in that order.
+int launch_write_index_full(const csa2_cache_t& c, int B, const int32_t* start_tok, int T_new, const uint16_t* x,
+                            const uint16_t* w, const uint16_t* k_idx, const int32_t* ctx_len, int64_t max_ctx,
+                            const uint16_t* q_idx, const uint16_t* w_idx, int topk, int pool_blocks,
+                            int cand_block, int32_t* topk_idx, int32_t* pool, void* ws, hipStream_t s);
 // Reindex: with a workspace of reindex_ws(B) bytes the pool is scored by many
 // workgroups per sequence and selected by a second kernel; without one, by one
 // workgroup per sequence.

@@ -9,8 +9,9 @@
 // layers).
 //
 // Host code only.  The calls are the library's own launchers, issued in layer order
-// on a private capture stream: the graph holds exactly the kernels the separate
-// calls would run, on the same buffers, so its results are those calls' results.
+// on a private capture stream, on the same buffers the separate calls would use; a
+// step whose first layer is Full runs its write inside that layer's scan (the launch
+// of csa2_write_index_full), so the graph's results are those of the separate calls.
 // Intermediates (the current selection, the pool, the workspaces of the index,
 // Reindex and attention calls) live in one caller workspace; the graph and its
 // executable are the only allocations (host-side objects of the HIP runtime).
@@ -139,11 +140,17 @@ int csa2_schedule_create(const csa2_cache_t* cache, int B, int H, const int32_t*
     return CSA2_EHIP;
   }
   int err = CSA2_OK;
-  if (x) err = launch_write_kv(*cache, B, start_tok, T_new, x, w, k_idx, st);
+  const bool fused_write = x && layers[0].mode == CSA2_LAYER_FULL;
+  if (x && !fused_write) err = launch_write_kv(*cache, B, start_tok, T_new, x, w, k_idx, st);
   int cur_pool_blocks = 0;
   for (int l = 0; l < n_layers && err == CSA2_OK; ++l) {
     const csa2_layer_t& L = layers[l];
-    if (L.mode == CSA2_LAYER_FULL) {
+    if (L.mode == CSA2_LAYER_FULL && l == 0 && fused_write) {
+      cur_pool_blocks = L.pool_blocks;
+      err = launch_write_index_full(*cache, B, start_tok, T_new, x, w, k_idx, ctx_len, max_ctx, L.q_idx, L.w_idx,
+                                    topk, L.pool_blocks, cand_block, topk_idx, L.pool_blocks > 0 ? pool : nullptr,
+                                    ws_full, st);
+    } else if (L.mode == CSA2_LAYER_FULL) {
       cur_pool_blocks = L.pool_blocks;
       err = launch_index_full(*cache, B, ctx_len, max_ctx, L.q_idx, L.w_idx, topk, L.pool_blocks, cand_block,
                               topk_idx, L.pool_blocks > 0 ? pool : nullptr, ws_full, st);

@@ -16,131 +16,17 @@
 #include <algorithm>
 
 #include "common.h"
+#include "entry_write.h"
 #include "internal.h"
 
 namespace csa2 {
 namespace {
 
-// Quantise the lane's 8 values; the 32-value block is lanes 4q..4q+3.
-__device__ __forceinline__ void mx_quant8(const float (&y)[8], uint32_t& codes, uint32_t& u) {
-  float a = 0.0f;
-#pragma unroll
-  for (int k = 0; k < 8; ++k) a = fmaxf(a, fabsf(y[k]));
-  a = fmaxf(a, __shfl_xor(a, 1, kWave));
-  a = fmaxf(a, __shfl_xor(a, 2, kWave));
-  // scale exponent e = floor(log2 a) - 2 clamped at -127  ->  byte u = e + 127
-  const uint32_t bexp = (__float_as_uint(a) >> 23) & 0xffu;
-  u = bexp > 2u ? bexp - 2u : 0u;
-  const float inv = __uint_as_float((254u - u) << 23);   // 2^-e, exact
-  const bool zero = (a == 0.0f);
-  codes = 0u;
-#pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    const float v = fabsf(y[k]) * inv;                   // in [0, 8), exact
-    // nearest e2m1 magnitude, ties to the even code: 0.25->0 0.75->2 1.25->2
-    // 1.75->4 2.5->4 3.5->6 5->6, saturating at 6 (code 7)
-    uint32_t m = (uint32_t)(v > 0.25f) + (uint32_t)(v >= 0.75f) + (uint32_t)(v > 1.25f) +
-                 (uint32_t)(v >= 1.75f) + (uint32_t)(v > 2.5f) + (uint32_t)(v >= 3.5f) +
-                 (uint32_t)(v > 5.0f);
-    const uint32_t s = __float_as_uint(y[k]) >> 31;
-    const uint32_t c = zero ? 0u : (m | (s << 3));
-    codes |= c << (4 * k);
-  }
-}
-
-__device__ __forceinline__ float lo_bf16(uint32_t d) { return __uint_as_float(d << 16); }
-__device__ __forceinline__ float hi_bf16(uint32_t d) { return __uint_as_float(d & 0xffff0000u); }
-
-// Channels 8l..8l+7 (lane l) of entry i of sequence b before quantisation: the fp32
-// merge of its two tokens (ratio 2) or the token itself (ratio 1).  The raw bf16 words
-// are loaded first (entry_words) and combined later (latent_of), so a caller can issue
-// the loads before work that does not depend on them.
-struct EntryWords {
-  u32x4 xa, xb, wa, wb;   // ratio 1: xa only
-};
-
-__device__ __forceinline__ void entry_words(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, int b,
-                                            int i, int half, int ratio, int lane, EntryWords& t) {
-  if (ratio == 2) {
-    const int64_t tok0 = ((int64_t)b * 2 * half + 2 * i) * CSA2_D_LATENT + lane * 8;
-    t.xa = *reinterpret_cast<const u32x4*>(x + tok0);
-    t.xb = *reinterpret_cast<const u32x4*>(x + tok0 + CSA2_D_LATENT);
-    t.wa = *reinterpret_cast<const u32x4*>(w + tok0);
-    t.wb = *reinterpret_cast<const u32x4*>(w + tok0 + CSA2_D_LATENT);
-  } else {
-    t.xa = *reinterpret_cast<const u32x4*>(x + ((int64_t)b * half + i) * CSA2_D_LATENT + lane * 8);
-  }
-}
-
-__device__ __forceinline__ void latent_of(const EntryWords& t, int ratio, float (&y)[8]) {
-  if (ratio == 2) {
-    // y = w0*x0 + w1*x1 with one rounding (w1*x1 is exact in fp32)
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      y[2 * q] = fmaf(lo_bf16(t.wa[q]), lo_bf16(t.xa[q]), lo_bf16(t.wb[q]) * lo_bf16(t.xb[q]));
-      y[2 * q + 1] = fmaf(hi_bf16(t.wa[q]), hi_bf16(t.xa[q]), hi_bf16(t.wb[q]) * hi_bf16(t.xb[q]));
-    }
-  } else {
-    // the token itself (bf16 is exact in fp32)
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      y[2 * q] = lo_bf16(t.xa[q]);
-      y[2 * q + 1] = hi_bf16(t.xa[q]);
-    }
-  }
-}
-
-__device__ __forceinline__ void entry_latent(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w, int b,
-                                             int i, int half, int ratio, int lane, float (&y)[8]) {
-  EntryWords t;
-  entry_words(x, w, b, i, half, ratio, lane, t);
-  latent_of(t, ratio, y);
-}
-
-__global__ __launch_bounds__(256) void write_kv_kernel(
-    uint8_t* __restrict__ lat_codes, uint8_t* __restrict__ lat_scales,
-    uint8_t* __restrict__ idx_codes, uint8_t* __restrict__ idx_scales, int n_pages,
-    const int32_t* __restrict__ block_table, int max_pages, const int32_t* __restrict__ start_tok,
-    int half, int64_t total, const uint16_t* __restrict__ x, const uint16_t* __restrict__ w,
-    const uint16_t* __restrict__ k_idx, int ratio) {
-  // half: entries per sequence (tokens / ratio)
+__global__ __launch_bounds__(256) void write_kv_kernel(WriteArgs a, int64_t total) {
   const int64_t e = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (e >= total) return;
-  const int lane = threadIdx.x & 63;
-  const int b = (int)(e / half);
-  const int i = (int)(e - (int64_t)b * half);
-  // The entry's inputs do not depend on where it is stored: their loads are issued
-  // first and are in flight during the page lookup (start_tok, then the block table).
-  EntryWords t;
-  entry_words(x, w, b, i, half, ratio, lane, t);
-  u32x4 ka = u32x4{0u, 0u, 0u, 0u};   // lanes 0..7: channels 8l..8l+7 of the indexer key
-  if (lane < 8) ka = *reinterpret_cast<const u32x4*>(k_idx + ((int64_t)b * half + i) * CSA2_D_INDEX + lane * 8);
-  const int st = start_tok[b];
-  if (st < 0 || (ratio == 2 && (st & 1))) return;       // caller contract: even start at ratio 2
-  const int j = (ratio == 2 ? (st >> 1) : st) + i;
-  const int page = page_of(block_table, max_pages, n_pages, b, j);
-  if (page < 0) return;
-  const int64_t row = (int64_t)page * CSA2_PAGE + (j & (CSA2_PAGE - 1));
-
-  float y[8];
-  latent_of(t, ratio, y);
-  uint32_t codes, u;
-  mx_quant8(y, codes, u);
-  *reinterpret_cast<uint32_t*>(lat_codes + row * CSA2_LAT_CODE_BYTES + lane * 4) = codes;
-  if ((lane & 3) == 0) lat_scales[row * CSA2_LAT_SCALE_BYTES + (lane >> 2)] = (uint8_t)u;
-
-  // ---- indexer key: lanes 0..7 own 8 channels each (two MX blocks) ----
-  float kv[8];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {   // lanes 8..63 hold zeros
-    kv[2 * q] = lo_bf16(ka[q]);
-    kv[2 * q + 1] = hi_bf16(ka[q]);
-  }
-  mx_quant8(kv, codes, u);
-  if (lane < 8) {
-    *reinterpret_cast<uint32_t*>(idx_codes + row * CSA2_IDX_CODE_BYTES + lane * 4) = codes;
-    if ((lane & 3) == 0) idx_scales[row * CSA2_IDX_SCALE_BYTES + (lane >> 2)] = (uint8_t)u;
-  }
+  const int b = (int)(e / a.half);
+  write_entry_wave(a, b, (int)(e - (int64_t)b * a.half), threadIdx.x & 63);
 }
 
 
@@ -370,9 +256,8 @@ int launch_write_kv(const csa2_cache_t& c, int B, const int32_t* start_tok, int 
   if (total == 0) return CSA2_OK;
   const int64_t grid = (total + 3) / 4;
   if (grid > 0x7fffffff) return CSA2_EUNSUPPORTED;
-  hipLaunchKernelGGL(write_kv_kernel, dim3((unsigned)grid), dim3(256), 0, s, c.lat_codes,
-                     c.lat_scales, c.idx_codes, c.idx_scales, c.n_pages, c.block_table,
-                     c.max_pages, start_tok, half, total, x, w, k_idx, ratio);
+  hipLaunchKernelGGL(write_kv_kernel, dim3((unsigned)grid), dim3(256), 0, s,
+                     write_args(c, start_tok, half, x, w, k_idx, ratio), total);
   return hip_status();
 }
 

@@ -194,6 +194,25 @@ int csa2_index_full(const csa2_cache_t *cache, int B, const int32_t *ctx_len, in
                     int cand_block, int32_t *topk_idx, int32_t *pool, void *ws, size_t ws_bytes,
                     void *stream);
 
+/* csa2_write_index_full — the step's write followed by the Full selection, in one
+ *   launch sequence ([P1] §2.3.1: a decode step appends the new entry, then the
+ *   indexer scores every visible entry, the new one included; §2.3.2 Full mode).
+ *   Results, outputs and workspace are exactly those of csa2_write_kv(cache, B,
+ *   start_tok, T_new, x, w, k_idx, ratio) followed on the same stream by
+ *   csa2_index_full(cache, B, ctx_len, max_ctx, q_idx, w_idx, topk, pool_blocks,
+ *   cand_block, topk_idx, pool, ws, ws_bytes): the same cache bytes and the same
+ *   selections, bit for bit.  The write is done by the scan itself (each written entry
+ *   that a chunk streams is stored by the wave that reads it, just before it reads it),
+ *   which saves the write's launch.  Arguments, layouts, ownership and error codes are
+ *   those of the two calls; any argument either call rejects is rejected here before
+ *   anything runs.  Meant for decode steps (a few entries per sequence): every written
+ *   entry costs the wave that stores it one dependent round of loads. */
+int csa2_write_index_full(const csa2_cache_t *cache, int B, const int32_t *start_tok, int T_new,
+                          const uint16_t *x, const uint16_t *w, const uint16_t *k_idx, int ratio,
+                          const int32_t *ctx_len, int64_t max_ctx, const uint16_t *q_idx, const uint16_t *w_idx,
+                          int topk, int pool_blocks, int cand_block, int32_t *topk_idx, int32_t *pool, void *ws,
+                          size_t ws_bytes, void *stream);
+
 /* csa2_index_full_noalloc — csa2_index_full for callers that cannot allocate device
  *   memory: code under HIP graph capture, tight serving loops, and harnesses that
  *   forbid hipMalloc.  Same arguments, results and checks as csa2_index_full, without

@@ -179,3 +179,31 @@ def test_schedule_validation_before_capture():
     assert L.csa2_schedule_create(*args, 4, ok, p, 1 << 30, None) == EINVAL
     assert L.csa2_schedule_launch(None, None) == EINVAL
     L.csa2_schedule_destroy(None)
+
+
+def test_write_index_full_rejects_what_either_call_rejects():
+    L = fk.lib()
+    c, keep = _fake_cache()
+    p = ctypes.c_void_p(ctypes.addressof(keep))
+    ref = ctypes.byref(c)
+    EINVAL, EWS, EUNS = -1, -2, -3
+
+    def call(T_new=2, x=p, w=p, k=p, ratio=2, ctx=p, max_ctx=128, q=p, topk=16, pool_blocks=0, cand_block=8,
+             pool=None, ws=None, ws_bytes=0, cache=ref, start=p):
+        return L.csa2_write_index_full(cache, 1, start, T_new, x, w, k, ratio, ctx, max_ctx, q, p, topk,
+                                       pool_blocks, cand_block, p, pool, ws, ws_bytes, None)
+
+    assert call() == EWS                      # valid arguments, no workspace: nothing launched
+    assert call(cache=None) == EINVAL
+    assert call(start=None) == EINVAL
+    assert call(T_new=3) == EINVAL            # odd token count at ratio 2
+    assert call(T_new=0) == EINVAL
+    assert call(ratio=1) == EINVAL            # ratio differs from the cache's
+    assert call(w=None) == EINVAL             # ratio 2 needs w
+    assert call(k=None) == EINVAL
+    assert call(q=None) == EINVAL
+    assert call(ctx=None) == EINVAL
+    assert call(topk=0) == EINVAL
+    assert call(cand_block=3) == EINVAL
+    assert call(pool_blocks=4) == EINVAL      # pool NULL
+    assert call(max_ctx=2 * 4 * 64 + 2) == EINVAL   # beyond the table's pages
