@@ -33,6 +33,7 @@ namespace {
 
 constexpr int kScanThreads = 512;
 constexpr int kScanAhead = 2;        // pages a scan wave keeps in flight beyond the one it scores
+constexpr int kScanMaxWrites = 2;    // entries per sequence up to which the scan does the step's write
 constexpr int kReindexRound = 8;     // groups of 16 pool slots a reindex wave loads before scoring them
 constexpr int kMergeThreads = 1024;
 constexpr int kMergeCap = 32768;     // keys the merge / pool workgroup selects from
@@ -202,10 +203,9 @@ __global__ __launch_bounds__(NT) void index_scan_kernel(ScanArgs a) {
   constexpr int NPW = CHUNK / CSA2_PAGE / NW;   // pages per wave
 
   // The step's write, when this launch performs it (the scan then sees the written
-  // keys, as if the write had run first).  Entry j = j0 + i of sequence b's write is
-  // stored by the wave that streams j's page, before that wave reads the page, when
-  // j is visible; the entries no chunk streams are spread over all waves of the
-  // sequence's workgroups here.
+  // keys, as if the write had run first).  A visible written entry is stored by the
+  // workgroup that streams it before its rows are read (below); the entries no chunk
+  // streams are spread over all waves of the sequence's workgroups here.
   int wj0 = -1;
   if (a.wr.x != nullptr) {
     wj0 = write_first_entry(a.wr, b);
@@ -222,10 +222,11 @@ __global__ __launch_bounds__(NT) void index_scan_kernel(ScanArgs a) {
   const int n_in = min(CHUNK, n_vis - e0);
   const int n = lane & 15, g = lane >> 4;
   if (wj0 >= 0) {
+    // the wave that streams a written entry's page stores the entry, and only that
+    // wave waits for its stores before it issues its loads of those rows
     const int lo = max(wj0, e0 + wid * NPW * CSA2_PAGE);
     const int hi = min(min(wj0 + a.wr.half, e0 + (wid + 1) * NPW * CSA2_PAGE), n_vis);
     for (int j = lo; j < hi; ++j) write_entry_wave(a.wr, b, j - wj0, lane);
-    // the stores are complete before this wave's loads of the same rows are issued
     if (lo < hi) __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
   }
 
@@ -851,7 +852,16 @@ int launch_write_index_full(const csa2_cache_t& c, int B, const int32_t* start_t
                             const uint16_t* q_idx, const uint16_t* w_idx, int topk, int pool_blocks,
                             int cand_block, int32_t* topk_idx, int32_t* pool, void* ws, hipStream_t s) {
   const int ratio = cache_ratio(c);
-  const WriteArgs wr = write_args(c, start_tok, T_new / ratio, x, w, k_idx, ratio);
+  const int half = T_new / ratio;
+  if (half > kScanMaxWrites) {
+    // a wave stores its entries one after another, each a dependent round of loads:
+    // past a decode step's few entries the write kernel's one wave per entry is faster
+    const int rc = launch_write_kv(c, B, start_tok, T_new, x, w, k_idx, s);
+    if (rc != CSA2_OK) return rc;
+    return launch_index_full(c, B, ctx_len, max_ctx, q_idx, w_idx, topk, pool_blocks, cand_block, topk_idx, pool,
+                             ws, s);
+  }
+  const WriteArgs wr = write_args(c, start_tok, half, x, w, k_idx, ratio);
   return index_full_impl(c, B, ctx_len, max_ctx, q_idx, w_idx, topk, pool_blocks, cand_block, topk_idx, pool, ws,
                          wr, s);
 }

@@ -203,10 +203,11 @@ int csa2_index_full(const csa2_cache_t *cache, int B, const int32_t *ctx_len, in
  *   cand_block, topk_idx, pool, ws, ws_bytes): the same cache bytes and the same
  *   selections, bit for bit.  The write is done by the scan itself (each written entry
  *   that a chunk streams is stored by the wave that reads it, just before it reads it),
- *   which saves the write's launch.  Arguments, layouts, ownership and error codes are
- *   those of the two calls; any argument either call rejects is rejected here before
- *   anything runs.  Meant for decode steps (a few entries per sequence): every written
- *   entry costs the wave that stores it one dependent round of loads. */
+ *   which saves the write's launch.  That holds for writes of up to 2 entries per
+ *   sequence (a decode step); a larger write runs as the two launches, since a wave
+ *   stores its entries one after another.  Arguments, layouts, ownership and error
+ *   codes are those of the two calls; any argument either call rejects is rejected here
+ *   before anything runs. */
 int csa2_write_index_full(const csa2_cache_t *cache, int B, const int32_t *start_tok, int T_new,
                           const uint16_t *x, const uint16_t *w, const uint16_t *k_idx, int ratio,
                           const int32_t *ctx_len, int64_t max_ctx, const uint16_t *q_idx, const uint16_t *w_idx,

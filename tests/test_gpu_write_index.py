@@ -3,9 +3,9 @@ stream: the same cache bytes and the same selections (top-K and pool), bit for b
 
 The cases put the written entries where the fused scan must store them before it reads
 them: the last entry of a chunk, the first of the next, a page's first entry, entry 0,
-a write crossing a chunk and several page boundaries, written entries past the visible
-context (stored, not scored), an odd start at ratio 2 (nothing written), and an absent
-page under a written entry.
+writes crossing a chunk or a page boundary, written entries past the visible context
+(stored, not scored), an odd start at ratio 2 (nothing written), and an absent page
+under a written entry; a 70-entry write, which the call runs as two launches, too.
 """
 import pytest
 import torch
@@ -72,8 +72,26 @@ def test_decoder_ratio1_single_token_write(fk):
     _compare(fk, case, start, torch.tensor(case.ctx_len, dtype=torch.int32))
 
 
-def test_multi_entry_write_across_chunks_with_invisible_odd_and_absent(fk):
-    # 70 entries per sequence.  Seq 0: entries 4060..4129 (chunk 0 -> 1, pages 63..64);
+def test_two_entry_write_across_edges_with_invisible_odd_and_absent(fk):
+    # 2 entries per sequence, the most the scan writes itself.  Seq 0: entries 4095, 4096
+    # (one in each chunk); seq 1: 63, 64 (one in each page); seq 2: the context stops
+    # after the first (the second is stored, not scored); seq 3: odd start (nothing
+    # written); seq 4: its second entry's page is unmapped; seq 5: entries 0, 1.
+    A = 4
+    ctx = (8190 + A, 126 + A, 2000 + A, 5000 + A, 126 + A, A)
+    cfg = small_decode(1, B=len(ctx), ctx=ctx, H=16, pages="random", append=A, topk=128,
+                       layers=(LayerSpec("full", 40),))
+    case = make_decode_case(cfg, "cpu")
+    _, _, _, start = case.append_tokens()
+    start = start.clone()
+    start[3] += 1
+    ctx_t = torch.tensor(case.ctx_len, dtype=torch.int32)
+    ctx_t[2] -= 2
+    _compare(fk, case, start, ctx_t, absent=(4, 1))
+
+
+def test_multi_entry_write_runs_as_two_launches(fk):
+    # 70 entries per sequence (more than the scan writes itself).  Seq 0: entries 4060..4129 (chunk 0 -> 1, pages 63..64);
     # seq 1: same, but the context stops 40 entries into the write (the rest is stored,
     # not scored); seq 2: odd start (nothing written); seq 3: short sequence whose
     # written page 1 is unmapped; seq 4: a write far from the end of its chunk.
