@@ -48,11 +48,14 @@
 // both the QK reads (16 rows, same chunk) and the PV reads (one row, 16 chunks) hit
 // distinct banks.
 //
-// Order of loads.  Waves 0-3 load their window unit at once and their FP4 rows after
-// computing it; waves 4-7 the other way round.  Whatever a wave loads late is first
-// warmed into L2 with a few dword loads (window rows at the start, FP4 rows right
-// after the page lookups), and the late window unit is loaded in halves, each into an
-// FP4 slot as soon as that slot's last tile is done.  The row ids of a tile's DMAs are
+// Order of loads.  The window's first eight units all go to waves 0-3: wave w loads
+// unit w at once, computes it, then its FP4 tiles, then unit w+4; waves 4-7 take
+// only FP4 tiles.  (Waves 0-3 issue first on their SIMDs and so run ahead of waves
+// 4-7; measured on the MI355X, dealing them the extra work ends the two waves of a
+// SIMD closer together, about 1 us sooner per call at 32 x 64 heads.)  Whatever a
+// wave loads late is first warmed into L2 with a few dword loads (window rows at the
+// start, FP4 rows right after the page lookups), and the late window unit is loaded
+// in halves, each into an FP4 slot as soon as that slot's last tile is done.  The row ids of a tile's DMAs are
 // gathered from the lanes holding them before any of the DMAs is issued, and the
 // operands of the next 128-dim chunk are read from LDS while the current one is
 // multiplied.  Measured on the MI355X, the kernel is bound by how fast a CU can pull
@@ -359,14 +362,15 @@ __global__ __launch_bounds__(kThreadsA) void attn_kernel(AttnArgs a) {
            lds + kOffPf + 256 * w);
     }
   };
-  // Waves w and w+4 share a SIMD.  Waves 0-3 take their window unit first and waves
-  // 4-7 their FP4 tiles first, so one of each pair computes while the other waits for
-  // its rows.
+  // Waves w and w+4 share a SIMD.  Waves 0-3 take window unit w first and waves 4-7
+  // their FP4 tiles, so one of each pair computes while the other waits for its rows;
+  // waves 0-3 also take unit w+4 after their tiles.
   const bool win_first = w < 4;
-  const bool has_win = w < n_wu;
-  const bool late_win = has_win && !win_first;   // unit w is done after the FP4 tiles
-  if (has_win && win_first) dma_window(w);
-  if (late_win) warm_window(w);
+  const bool has_win = win_first && w < n_wu;    // unit w before the FP4 tiles
+  const int late_wu = w + 4;                     // and unit w + 4 after them
+  const bool late_win = win_first && late_wu < n_wu;
+  if (has_win) dma_window(w);
+  if (late_win) warm_window(late_wu);
   wait_vm<0>();   // ids, q and the first window unit
   __syncthreads();   // q of every head is in LDS
 
@@ -450,7 +454,7 @@ __global__ __launch_bounds__(kThreadsA) void attn_kernel(AttnArgs a) {
       }
     }
   };
-  if (has_win && win_first) window_unit(w);
+  if (has_win) window_unit(w);
 
   // row ids of the FP4 tiles stay in registers (lane: tile 2u + lane/32, row
   // lane%32); vmask[k] bit r = row r of tile k valid
@@ -548,8 +552,8 @@ __global__ __launch_bounds__(kThreadsA) void attn_kernel(AttnArgs a) {
   } else if (nk == 1) {
     dma_fp4(0, region);
   }
-  if (nk <= 1 && late_win) dma_window_rows(w, kUnit / 2, kUnit / 2);   // slot 1 holds no tile
-  if (nk == 0 && late_win) dma_window_rows(w, 0, kUnit / 2);
+  if (nk <= 1 && late_win) dma_window_rows(late_wu, kUnit / 2, kUnit / 2);   // slot 1 holds no tile
+  if (nk == 0 && late_win) dma_window_rows(late_wu, 0, kUnit / 2);
 
   // one FP4 tile from slot SL (a compile-time constant, so LDS offsets are immediates)
   auto fp4_tile = [&](int k, auto slot_c) __attribute__((always_inline)) {
@@ -656,7 +660,7 @@ __global__ __launch_bounds__(kThreadsA) void attn_kernel(AttnArgs a) {
       dma_fp4(k + 2, region);
     } else if (late_win) {
       wait_lds();
-      dma_window_rows(w, 0, kUnit / 2);
+      dma_window_rows(late_wu, 0, kUnit / 2);
     }
     if (k + 1 < nk) {
       wait_tile(k + 1);
@@ -666,13 +670,13 @@ __global__ __launch_bounds__(kThreadsA) void attn_kernel(AttnArgs a) {
         dma_fp4(k + 3, region + kSlotB);
       } else if (late_win) {
         wait_lds();
-        dma_window_rows(w, kUnit / 2, kUnit / 2);
+        dma_window_rows(late_wu, kUnit / 2, kUnit / 2);
       }
     }
   }
   if (late_win) {
     wait_vm<0>();
-    window_unit(w);
+    window_unit(late_wu);
   }
 
   if (!win_first) rest_of_window();
