@@ -371,17 +371,45 @@ __global__ __launch_bounds__(kThreadsA) void attn_kernel(AttnArgs a) {
   const bool late_win = win_first && late_wu < n_wu;
   if (has_win) dma_window(w);
   if (late_win) warm_window(late_wu);
-  wait_vm<0>();   // ids, q and the first window unit
-  __syncthreads();   // q of every head is in LDS
+  // ids and q have landed; the window rows and warm-ups issued after them may still be
+  // in flight (the barrier does not wait for waves 0-3's window rows)
+  if (has_win && late_win)
+    wait_vm<kUnit + 2>();
+  else if (has_win)
+    wait_vm<kUnit>();
+  else if (late_win)
+    wait_vm<2>();
+  else
+    wait_vm<0>();
+  // q of every head is in LDS.  A bare barrier: the fence of __syncthreads would wait
+  // for every load in flight, the window rows included.
+  asm volatile("s_barrier" ::: "memory");
 
-  // page lookups of the ids
-  int pg[kMaxFtWave / 2];
+  // page lookups of the ids: one load per pair of tiles, issued whatever the lanes
+  // hold (an invalid id reads the table's first slot and is dropped), so their number
+  // is known to the waits below
+  int pg[kMaxFtWave / 2];   // the raw table slot; validity is applied where it is used
+  int n_pl = 0;
 #pragma unroll
   for (int u = 0; u < kMaxFtWave / 2; ++u) {
     pg[u] = -1;
     if (2 * u < nk) {
       const int e = ids[u];
-      if (e >= 0 && e < n_vis && (e >> 6) < a.max_pages) pg[u] = bt[e >> 6];
+      const bool ok = e >= 0 && e < n_vis && (e >> 6) < a.max_pages;
+      pg[u] = bt[ok ? e >> 6 : 0];
+      ++n_pl;
+    }
+  }
+  // waves 0-3: their window unit's rows (issued before the warm-ups and the lookups)
+  if (has_win) {
+    switch (n_pl + (late_win ? 2 : 0)) {
+      case 0: wait_vm<0>(); break;
+      case 1: wait_vm<1>(); break;
+      case 2: wait_vm<2>(); break;
+      case 3: wait_vm<3>(); break;
+      case 4: wait_vm<4>(); break;
+      case 5: wait_vm<5>(); break;
+      default: wait_vm<6>(); break;
     }
   }
 
@@ -464,7 +492,8 @@ __global__ __launch_bounds__(kThreadsA) void attn_kernel(AttnArgs a) {
     rowv[u] = -1;
     if (2 * u < nk) {
       const int e = ids[u], p = pg[u];
-      rowv[u] = (e >= 0 && e < n_vis && p >= 0 && p < a.n_pages) ? p * CSA2_PAGE + (e & (CSA2_PAGE - 1)) : -1;
+      const bool ok = e >= 0 && e < n_vis && (e >> 6) < a.max_pages && p >= 0 && p < a.n_pages;
+      rowv[u] = ok ? p * CSA2_PAGE + (e & (CSA2_PAGE - 1)) : -1;
       const uint64_t bal = __ballot(rowv[u] >= 0);
       if (lane == 0) {
         vmask[2 * u] = (uint32_t)bal;
