@@ -268,6 +268,9 @@ __global__ __launch_bounds__(64) void prefill_index_kernel(PfIndexArgs a) {
   // the keys serves every set) and appends those above a query's threshold to its
   // list.  Check<true> also tests each entry against the query's visible count.
   auto score_page = [&](const Page& pg, int p, auto chk) {
+    // all of the page's products first, then the scores: the MFMAs of the later groups
+    // cover the latency of the earlier ones' results
+    f32x4 dd[4][kPfSets];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const float sc = e8m0_scale(pg.sb[t]);
@@ -280,12 +283,19 @@ __global__ __launch_bounds__(64) void prefill_index_kernel(PfIndexArgs a) {
       hi.y = fp4x2_to_bf16x2<1>(pg.cd[t].y, sc);
       hi.z = fp4x2_to_bf16x2<2>(pg.cd[t].y, sc);
       hi.w = fp4x2_to_bf16x2<3>(pg.cd[t].y, sc);
-      const int e = p * CSA2_PAGE + 16 * t + n;
 #pragma unroll
       for (int st = 0; st < kPfSets; ++st) {
         f32x4 d = {0.f, 0.f, 0.f, 0.f};
         d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[st][0], __builtin_bit_cast(bf16x8, lo), d, 0, 0, 0);
-        d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[st][1], __builtin_bit_cast(bf16x8, hi), d, 0, 0, 0);
+        dd[t][st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[st][1], __builtin_bit_cast(bf16x8, hi), d, 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int e = p * CSA2_PAGE + 16 * t + n;
+#pragma unroll
+      for (int st = 0; st < kPfSets; ++st) {
+        const f32x4 d = dd[t][st];
         // lane l: d[i] = head i of query i0 + 4st + l/16 against entry l%16 of the group
         const float s = wh[st][0] * relu0(d[0]) + wh[st][1] * relu0(d[1]) + wh[st][2] * relu0(d[2]) +
                         wh[st][3] * relu0(d[3]);
