@@ -161,16 +161,6 @@ __device__ __forceinline__ int swz_o(int c, int h) { return c ^ ((c >> 4) & 3) ^
 // Window slot s (position t-W+1+s) holds a row: s < W and the position is >= 0.
 __device__ __forceinline__ bool win_valid(int W, int t, int s) { return s < W && t - (W - 1) + s >= 0; }
 
-// bf16 head and residual of two weights, packed (first weight in the low half).
-__device__ __forceinline__ void split_pair(float p0, float p1, uint32_t& hi, uint32_t& lo) {
-  typedef __attribute__((ext_vector_type(2))) __bf16 bf2;
-  const bf2 h = {(__bf16)p0, (__bf16)p1};
-  hi = __builtin_bit_cast(uint32_t, h);
-  const float r0 = p0 - __uint_as_float(hi << 16), r1 = p1 - __uint_as_float(hi & 0xffff0000u);
-  const bf2 l = {(__bf16)r0, (__bf16)r1};
-  lo = __builtin_bit_cast(uint32_t, l);
-}
-
 // The wave's state: O accumulators of its dim quarters (n-tile t = 8*quarter + tt,
 // lane (n, g): heads 4g..4g+3 of dim 32n + 8*quarter + tt), the lazy running maximum
 // of head n (identical in the 4 lanes of a head) and the lane's share of the sum.

@@ -11,10 +11,14 @@
 // architecture..." (scores -> weights summing to 1 -> weighted sum of values).
 //
 // Two kernels:
-//   sparse_decode_kernel    one workgroup per (query, 16 heads), 8 waves, all rows;
-//   sparse_decode64_kernel  one workgroup per (query, 64 heads) when H is a multiple
-//                           of 64 and there are >= 512 queries: each FP4 tile is
-//                           converted once for four head groups.
+//   sparse_decode_wide_kernel<G>  one workgroup (8 waves) per (query, 16G heads):
+//                           G = 4 when H is a multiple of 64 and there are >= 512
+//                           queries, else G = 2 when H is a multiple of 32.  Each
+//                           row is read once per workgroup and each FP4 tile is
+//                           converted once for G head groups;
+//   sparse_decode_kernel<NW>  one workgroup of NW = 4 waves per (query, 16 heads)
+//                           for the remaining head counts; at 81 KB of LDS two
+//                           workgroups share a CU.
 // Rows are processed in batches that live in one of two LDS buffers: window
 // batches of bf16 rows (pitch 1040 B), then FP4 batches (256 code bytes + 16 scale
 // bytes, pitch 272 B).  Batch k+1 is loaded into registers when batch k starts and
@@ -22,14 +26,18 @@
 // arithmetic.  Chunks of rows that are absent are written as zeros, so stale bytes
 // never meet a zero weight (0 * NaN is not 0).  The selected entries' page lookups
 // are loads issued at the start and consumed only when the first FP4 batch is
-// loaded, so they hide behind the window batches.
+// loaded, so they hide behind the window batches.  Per-wave timestamps on the
+// MI355X (the mixed batch) put the time in each batch's vector ALU work and its
+// three barriers, not in waiting for the next batch's rows, so the kernels keep
+// vector instructions few: bf16 conversions in hardware, a chunk map without
+// divisions, and window units that give every wave work.
 // Per batch (16-head kernel):
 //   QK  wave w scores 32-row tile w: D[row][head] via 16x16x32 bf16 MFMAs, A = rows
 //       (lane: row l%16, dims 128g+8s..+7 at k-step s, g = l/16; FP4 rows become
 //       bf16 through the hardware convert with the e8m0 scale folded in, exact),
 //       B = q (lane: head l%16, same dims; q stays in registers).
 //   max the batch maximum of every head goes through LDS, so all waves hold the
-//       same running maximum; accumulators are rescaled once per batch.
+//       same running maximum, which is lazy (below).
 //   P   the scoring wave turns its 32 scores per head into the P operand of the PV
 //       MFMA -- a bf16 head plus a bf16 residual -- and parks it in LDS.  The lane's
 //       scores are already the K-slots of that operand (rows 4g..4g+3 and
@@ -44,30 +52,50 @@
 namespace csa2 {
 namespace {
 
-constexpr int kWaves = 8;
+constexpr int kWaves = 8;             // the wide kernel
 constexpr int kThreads = kWaves * 64;
 constexpr int kRowB = 272;           // FP4 row in LDS: 256 code bytes then 16 scale bytes
 constexpr int kWinB = 1040;          // window row in LDS: 1024 bytes + 16 pad
-constexpr int kFp4Batch = 256;       // FP4 rows per batch (8 tiles)
-constexpr int kWinBatch = 64;        // window rows per batch (2 tiles)
-constexpr int kMaxTiles = kFp4Batch / 32;
-constexpr int kBufBytes = kFp4Batch * kRowB;              // 69632 >= kWinBatch * kWinB
-constexpr int kPBytes = 32;                               // per lane and tile: P head + residual
-constexpr int kStage = (kFp4Batch * 17 + kThreads - 1) / kThreads;   // 16-byte chunks per thread
-constexpr int kOffBuf = 0;
-constexpr int kPSlots = kMaxTiles + kWinBatch / 32;        // FP4 tiles, then a window batch's tiles
-constexpr int kOffP = 2 * kBufBytes;                      // [10 slots][64 lanes][32 B]
-constexpr int kOffRowId = kOffP + kPSlots * 64 * kPBytes;   // [2][256] int32
-constexpr int kOffMax = kOffRowId + 2 * kFp4Batch * 4;    // [8 waves][16] float
-constexpr int kOffL = kOffMax + kWaves * 16 * 4;          // [8 waves][16] float
-constexpr int kLdsBytes = kOffL + kWaves * 16 * 4;
-static_assert(kWinBatch * kWinB <= kBufBytes, "window batch fits a buffer");
-static_assert(kMaxTiles == kWaves, "one FP4 tile per wave");
-static_assert(2 * kFp4Batch == kThreads, "one prefetched row id per thread (two FP4 batches)");
-static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
-static_assert(16 * kWinB <= kPSlots * 64 * kPBytes, "q of 16 heads fits the P slots");
+constexpr int kPBytes = 32;          // per lane and tile: P head + residual
+
+// Geometry of the 16-head kernel with NW waves: FP4 batches of 32*NW rows (one
+// 32-row tile per wave), window batches of 8*NW rows, and 512/NW output dims per
+// wave.  With 8 waves one workgroup fills a CU; with 4 waves a workgroup takes
+// under half of the LDS, so two share a CU and each hides the other's loads.
+template <int NW>
+struct Geo16 {
+  static constexpr int NT = NW * 64;
+  static constexpr int FB = 32 * NW;                                  // FP4 rows per batch
+  static constexpr int WB = 8 * NW;                                   // window rows per batch
+  static constexpr int MT = NW;                                       // FP4 tiles per batch
+  static constexpr int DW = CSA2_D_LATENT / NW;                       // output dims per wave
+  static constexpr int NH = DW / 64;                                  // 64-dim accumulator groups
+  static constexpr int BUF = FB * kRowB > WB * kWinB ? FB * kRowB : WB * kWinB;
+  static constexpr int STAGE = (FB * 17 + NT - 1) / NT;              // 16-byte chunks per thread
+  static constexpr int PSLOTS = MT + WB / 32;                         // FP4 tiles, then a window batch's
+  static constexpr int OFF_P = 2 * BUF;                               // [PSLOTS][64 lanes][32 B]
+  static constexpr int OFF_RID = OFF_P + PSLOTS * 64 * kPBytes;      // [2][FB] int32
+  static constexpr int OFF_MAX = OFF_RID + 2 * FB * 4;               // [NW][16] float
+  static constexpr int OFF_L = OFF_MAX + NW * 16 * 4;                // [NW][16] float
+  static constexpr int LDS = OFF_L + NW * 16 * 4;
+  // q of the 16 heads is staged at the window pitch in the P slots if they hold it,
+  // else in buffer 1 (free until batch 1 is stored)
+  static constexpr bool Q_IN_P = 16 * kWinB <= PSLOTS * 64 * kPBytes;
+  static constexpr int OFF_Q = Q_IN_P ? OFF_P : BUF;
+  static constexpr int QCH = 16 * CSA2_D_LATENT * 2 / 16 / NT;      // 16-byte q pieces per thread
+  static_assert(WB * kWinB <= BUF && 16 * kWinB <= BUF, "window batch and q fit a buffer");
+  static_assert(WB % 32 == 0 && (WB * 64) % NT == 0, "whole window tiles, whole chunks per thread");
+  static_assert(NH >= 1 && NH * 64 * NW == CSA2_D_LATENT, "the waves split the dims in 64-dim groups");
+  static_assert(2 * FB == NT, "one prefetched row id per thread (two FP4 batches)");
+  static_assert(LDS <= 160 * 1024, "LDS budget");
+  static_assert(NW == 8 || 2 * LDS <= 160 * 1024, "two 4-wave workgroups per CU");
+};
 
 constexpr float kLog2e = 1.4426950408889634f;
+// The running maximum is lazy: it moves only when a batch's maximum passes it by more
+// than 2^8 (weights up to 256 are exact in the bf16 head + residual split and in
+// fp32 sums), so the accumulators are rarely rescaled.
+constexpr float kLazy = 8.0f;
 constexpr float kLn2 = 0.6931471805599453f;
 
 struct DecArgs {
@@ -108,16 +136,26 @@ __device__ __forceinline__ void make_p(const float (&z)[8], float m, float& l_pa
   uint32_t h[4], r[4];
 #pragma unroll
   for (int j = 0; j < 8; j += 2) {
-    const float p0 = exp2f(z[j] - mb), p1 = exp2f(z[j + 1] - mb);
+    const float p0 = __builtin_amdgcn_exp2f(z[j] - mb), p1 = __builtin_amdgcn_exp2f(z[j + 1] - mb);
     l_part += p0 + p1;
-    const uint32_t h0 = f32_to_bf16_rne(p0), h1 = f32_to_bf16_rne(p1);
-    const uint32_t r0 = f32_to_bf16_rne(p0 - bf16_to_f32(h0));
-    const uint32_t r1 = f32_to_bf16_rne(p1 - bf16_to_f32(h1));
-    h[j >> 1] = h0 | (h1 << 16);
-    r[j >> 1] = r0 | (r1 << 16);
+    split_pair(p0, p1, h[j >> 1], r[j >> 1]);
   }
   phi = u32x4{h[0], h[1], h[2], h[3]};
   plo = u32x4{r[0], r[1], r[2], r[3]};
+}
+
+// The same for the 4 scores of one 16-row half of a tile: half of the P operand.
+__device__ __forceinline__ void make_p4(const float (&z)[4], float m, float& l_part, u32x2& phi, u32x2& plo) {
+  const float mb = (m == -INFINITY) ? 0.f : m;
+  uint32_t h[2], r[2];
+#pragma unroll
+  for (int j = 0; j < 4; j += 2) {
+    const float p0 = __builtin_amdgcn_exp2f(z[j] - mb), p1 = __builtin_amdgcn_exp2f(z[j + 1] - mb);
+    l_part += p0 + p1;
+    split_pair(p0, p1, h[j >> 1], r[j >> 1]);
+  }
+  phi = u32x2{h[0], h[1]};
+  plo = u32x2{r[0], r[1]};
 }
 
 // Scores of the FP4 tile at row `base` of the batch in LDS.
@@ -191,6 +229,30 @@ __device__ __forceinline__ void win_qk(const uint8_t* wrows, int W, int t, int w
   }
 }
 
+// Scores of the 16 window rows from row `base` of the batch in LDS (window slots
+// w0 + row): lane (n, g) gets head n against rows base + 4g .. +3.
+__device__ __forceinline__ void win_qk16(const uint8_t* wrows, int W, int t, int w0, int base,
+                                         const u32x4 (&qf)[16], float scale_log2, float (&z)[4]) {
+  const int lane = threadIdx.x & 63;
+  const int n = lane & 15, g = lane >> 4;
+  const uint8_t* rp = wrows + (base + n) * kWinB + 256 * g;
+  f32x4 sa[4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    u32x4 rv[8];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) rv[s] = lds_ld<u32x4>(rp + 16 * (8 * half + s));
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+      sa[s & 3] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, rv[s]),
+                                                          __builtin_bit_cast(bf16x8, qf[8 * half + s]), sa[s & 3], 0,
+                                                          0, 0);
+  }
+  const f32x4 s = (sa[0] + sa[1]) + (sa[2] + sa[3]);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) z[j] = win_valid(W, t, w0 + base + 4 * g + j) ? s[j] * scale_log2 : -INFINITY;
+}
+
 // PV for this wave's 64 dims from 8 rows given as pairs d01[j] = dims (4n, 4n+1),
 // d23[j] = dims (4n+2, 4n+3) of row slot j: n-tile t holds dim 4n + t.
 __device__ __forceinline__ void pv4(f32x4 (&acc)[4], const uint32_t (&d01)[8], const uint32_t (&d23)[8], bf16x8 ph,
@@ -210,12 +272,15 @@ __device__ __forceinline__ void pv4(f32x4 (&acc)[4], const uint32_t (&d01)[8], c
   for (int t = 0; t < 4; ++t) acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, bf[t], acc[t], 0, 0, 0);
 }
 
-__global__ __launch_bounds__(kThreads) void sparse_decode_kernel(DecArgs a) {
+template <int NW>
+__global__ __launch_bounds__(NW * 64, 8 / NW) void sparse_decode_kernel(DecArgs a) {
+  using G = Geo16<NW>;
+  constexpr int NT = G::NT, FB = G::FB, WB = G::WB, STAGE = G::STAGE, BUF = G::BUF, NH = G::NH;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-  uint8_t* plds = lds + kOffP;
-  int32_t* rowid_all = reinterpret_cast<int32_t*>(lds + kOffRowId);
-  float* m_part = reinterpret_cast<float*>(lds + kOffMax);
-  float* l_w = reinterpret_cast<float*>(lds + kOffL);
+  uint8_t* plds = lds + G::OFF_P;
+  int32_t* rowid_all = reinterpret_cast<int32_t*>(lds + G::OFF_RID);
+  float* m_part = reinterpret_cast<float*>(lds + G::OFF_MAX);
+  float* l_w = reinterpret_cast<float*>(lds + G::OFF_L);
 
   // XCD-aware mapping: consecutive workgroup ids go to different XCDs; XCD x takes
   // the contiguous query range [x * q_per_xcd, (x+1) * q_per_xcd), all head groups.
@@ -244,8 +309,8 @@ __global__ __launch_bounds__(kThreads) void sparse_decode_kernel(DecArgs a) {
   const int32_t* tk = a.topk_idx + qi * a.topk;
   const int32_t* bt = a.block_table + (int64_t)b * a.max_pages;
 
-  const int n_wb = (wr1 - wr0 + kWinBatch - 1) / kWinBatch;
-  const int n_fb = (fr1 - fr0 + kFp4Batch - 1) / kFp4Batch;
+  const int n_wb = (wr1 - wr0 + WB - 1) / WB;
+  const int n_fb = (fr1 - fr0 + FB - 1) / FB;
   const int nb = n_wb + n_fb;
 
   // row id of entry e (-1: invalid id, absent page)
@@ -255,10 +320,10 @@ __global__ __launch_bounds__(kThreads) void sparse_decode_kernel(DecArgs a) {
   auto page_ok = [&](int e) { return e >= 0 && e < n_vis && (e >> 6) < a.max_pages; };
   // FP4 batch f >= 2: ids resolved when the batch is issued
   auto resolve_rows = [&](int f) {
-    const int r0 = fr0 + f * kFp4Batch;
-    const int nrows = min(fr1 - r0, kFp4Batch);
-    int32_t* rowid = rowid_all + (f & 1) * kFp4Batch;
-    for (int i = tid; i < kFp4Batch; i += kThreads) {
+    const int r0 = fr0 + f * FB;
+    const int nrows = min(fr1 - r0, FB);
+    int32_t* rowid = rowid_all + (f & 1) * FB;
+    for (int i = tid; i < FB; i += NT) {
       const int e = i < nrows ? tk[r0 + i] : -1;
       rowid[i] = page_ok(e) ? row_of(e, bt[e >> 6]) : -1;
     }
@@ -268,15 +333,15 @@ __global__ __launch_bounds__(kThreads) void sparse_decode_kernel(DecArgs a) {
   // window: piece c%64 of row c/64 -- zeros where no row is.  Every chunk is loaded
   // (one with no row reads window row 0 of the sequence or cache row 0, and is
   // dropped), so no branch splits the loads: they issue back to back.
-  auto load_batch = [&](int k, u32x4 (&st)[kStage]) {
+  auto load_batch = [&](int k, u32x4 (&st)[STAGE]) {
     const u32x4 zero = {0u, 0u, 0u, 0u};
     if (k < n_wb) {
-      const int w0 = wr0 + k * kWinBatch;
+      const int w0 = wr0 + k * WB;
       int slot0 = (t - (a.W - 1) + w0) % a.W;   // ring slot of the batch's first position
       if (slot0 < 0) slot0 += a.W;
 #pragma unroll
-      for (int u = 0; u < kWinBatch * 64 / kThreads; ++u) {
-        const int c = tid + kThreads * u;
+      for (int u = 0; u < WB * 64 / NT; ++u) {
+        const int c = tid + NT * u;
         const int r = c >> 6, piece = c & 63;
         const bool ok = w0 + r < wr1 && win_valid(a.W, t, w0 + r);
         int row = a.prefill ? ci + w0 + r : (slot0 + r >= a.W ? slot0 + r - a.W : slot0 + r);
@@ -285,22 +350,22 @@ __global__ __launch_bounds__(kThreads) void sparse_decode_kernel(DecArgs a) {
         st[u] = ok ? v : zero;
       }
 #pragma unroll
-      for (int u = kWinBatch * 64 / kThreads; u < kStage; ++u) st[u] = zero;
+      for (int u = WB * 64 / NT; u < STAGE; ++u) st[u] = zero;
     } else {
       const int f = k - n_wb;
-      const int nrows = min(fr1 - fr0 - f * kFp4Batch, kFp4Batch);
-      const int32_t* rowid = rowid_all + (f & 1) * kFp4Batch;
-      int rid[kStage];
+      const int nrows = min(fr1 - fr0 - f * FB, FB);
+      const int32_t* rowid = rowid_all + (f & 1) * FB;
+      int rid[STAGE];
 #pragma unroll
-      for (int u = 0; u < kStage; ++u) {
-        const int c = tid + kThreads * u;
-        rid[u] = rowid[min(c / 17, kFp4Batch - 1)];
+      for (int u = 0; u < STAGE; ++u) {
+        const int c = tid + NT * u;
+        rid[u] = rowid[min(c / 17, FB - 1)];
       }
 #pragma unroll
-      for (int u = 0; u < kStage; ++u) {
-        const int c = tid + kThreads * u;
+      for (int u = 0; u < STAGE; ++u) {
+        const int c = tid + NT * u;
         const int r = c / 17, piece = c - r * 17;
-        const bool ok = c < kFp4Batch * 17 && r < nrows && rid[u] >= 0;
+        const bool ok = c < FB * 17 && r < nrows && rid[u] >= 0;
         const int64_t rw = ok ? rid[u] : 0;
         const uint8_t* src = piece < 16 ? a.lat_codes + rw * CSA2_LAT_CODE_BYTES + 16 * piece
                                         : a.lat_scales + rw * CSA2_LAT_SCALE_BYTES;
@@ -309,19 +374,19 @@ __global__ __launch_bounds__(kThreads) void sparse_decode_kernel(DecArgs a) {
       }
     }
   };
-  auto store_batch = [&](int k, const u32x4 (&st)[kStage]) {
-    uint8_t* buf = lds + kOffBuf + (k & 1) * kBufBytes;
+  auto store_batch = [&](int k, const u32x4 (&st)[STAGE]) {
+    uint8_t* buf = lds + (k & 1) * BUF;
     if (k < n_wb) {
 #pragma unroll
-      for (int u = 0; u < kWinBatch * 64 / kThreads; ++u) {
-        const int c = tid + kThreads * u;
+      for (int u = 0; u < WB * 64 / NT; ++u) {
+        const int c = tid + NT * u;
         *reinterpret_cast<u32x4*>(buf + (c >> 6) * kWinB + (c & 63) * 16) = st[u];
       }
     } else {
 #pragma unroll
-      for (int u = 0; u < kStage; ++u) {
-        const int c = tid + kThreads * u;
-        if (c < kFp4Batch * 17) *reinterpret_cast<u32x4*>(buf + c * 16) = st[u];
+      for (int u = 0; u < STAGE; ++u) {
+        const int c = tid + NT * u;
+        if (c < FB * 17) *reinterpret_cast<u32x4*>(buf + c * 16) = st[u];
       }
     }
   };
@@ -329,18 +394,20 @@ __global__ __launch_bounds__(kThreads) void sparse_decode_kernel(DecArgs a) {
   // ---- start: the entry ids of the first two FP4 batches (thread tid: batch tid/256,
   // row tid%256) go out first, then batch 0 (window rows need no lookups) and q.  The
   // ids' page lookups are issued as soon as the ids land, while the rest is in flight.
-  u32x4 st[kStage];
-  const int pf_i = tid & (kFp4Batch - 1), pf_f = tid >> 8;
-  const int pf_r = fr0 + pf_f * kFp4Batch + pf_i;
+  u32x4 st[STAGE];
+  const int pf_i = tid % FB, pf_f = tid / FB;
+  const int pf_r = fr0 + pf_f * FB + pf_i;
   const int pf_e = (pf_f < n_fb && pf_r < fr1) ? tk[pf_r] : -1;
   // q of the 16 heads is read from memory once per workgroup -- thread tid: head
-  // tid/32, dims 16(tid%32) .. +15 -- and handed to the waves through the P slots,
-  // which are free until the first P (rows at the window pitch, as win_qk reads them).
-  u32x4 qs[2];
+  // tid/TPH, QCH 16-byte pieces from dim 8*QCH*(tid%TPH) -- and handed to the waves
+  // through LDS at the window pitch, as win_qk reads rows: in the P slots, free until
+  // the first P, or in buffer 1, free until batch 1 is stored.
+  constexpr int TPH = NT / 16;   // threads per head
+  u32x4 qs[G::QCH];
   {
-    const uint16_t* qp = a.q + (qi * a.H + hg * 16 + (tid >> 5)) * CSA2_D_LATENT + 16 * (tid & 31);
-    qs[0] = *reinterpret_cast<const u32x4*>(qp);
-    qs[1] = *reinterpret_cast<const u32x4*>(qp + 8);
+    const uint16_t* qp = a.q + (qi * a.H + hg * 16 + tid / TPH) * CSA2_D_LATENT + 8 * G::QCH * (tid % TPH);
+#pragma unroll
+    for (int u = 0; u < G::QCH; ++u) qs[u] = *reinterpret_cast<const u32x4*>(qp + 8 * u);
   }
   // W >= 1 (checked by the launcher), so the run starts with a window batch, which
   // needs no lookups; the ids' page lookups are issued behind it.
@@ -353,47 +420,54 @@ __global__ __launch_bounds__(kThreads) void sparse_decode_kernel(DecArgs a) {
   // batch is stored after PV.
   __builtin_amdgcn_s_waitcnt(0);
   {
-    uint8_t* qd = plds + (tid >> 5) * kWinB + 32 * (tid & 31);
-    *reinterpret_cast<u32x4*>(qd) = qs[0];
-    *reinterpret_cast<u32x4*>(qd + 16) = qs[1];
+    uint8_t* qd = lds + G::OFF_Q + (tid / TPH) * kWinB + 16 * G::QCH * (tid % TPH);
+#pragma unroll
+    for (int u = 0; u < G::QCH; ++u) *reinterpret_cast<u32x4*>(qd + 16 * u) = qs[u];
   }
   u32x4 qf[16];   // q operand of head hg*16+n: dims 128g + 8s .. +7 for k-step s
   auto read_q = [&]() {   // after a barrier that follows the stores above
-    const uint8_t* qp = plds + n * kWinB + 256 * g;
+    const uint8_t* qp = lds + G::OFF_Q + n * kWinB + 256 * g;
 #pragma unroll
     for (int s = 0; s < 16; ++s) qf[s] = lds_ld<u32x4>(qp + 16 * s);
   };
 
-  f32x4 acc[4];
+  f32x4 acc[NH][4];   // group hh: dims DW*wid + 64*hh .. +63
 #pragma unroll
-  for (int i = 0; i < 4; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int hh = 0; hh < NH; ++hh) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[hh][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
   float m_run = -INFINITY, l_part = 0.f;
 
   // PV of one 32-row tile of a batch in LDS (window rows: bf16; else FP4), this wave's
-  // 64 dims, with the P operand from P slot ps.
+  // DW dims, with the P operand from P slot ps.
   auto pv_tile = [&](const uint8_t* buf, bool win, int tile, int ps) {
     const uint8_t* pp = plds + (ps * 64 + lane) * kPBytes;
     const bf16x8 ph = __builtin_bit_cast(bf16x8, lds_ld<u32x4>(pp));
     const bf16x8 pl = __builtin_bit_cast(bf16x8, lds_ld<u32x4>(pp + 16));
-    uint32_t d01[8], d23[8];
-    if (win) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const u32x2 v = lds_ld<u32x2>(buf + (tile * 32 + slot_row(g, j)) * kWinB + 128 * wid + 8 * n);
-        d01[j] = v.x;
-        d23[j] = v.y;
-      }
-    } else {
+    for (int hh = 0; hh < NH; ++hh) {
+      const int d0 = G::DW * wid + 64 * hh;   // first dim of the group
+      uint32_t d01[8], d23[8];
+      if (win) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const uint8_t* rp = buf + (tile * 32 + slot_row(g, j)) * kRowB;
-        const uint32_t c2 = lds_ld<uint16_t>(rp + 32 * wid + 2 * n);
-        const float sc = e8m0_scale(rp[256 + 2 * wid + (n >> 3)]);
-        d01[j] = fp4x2_to_bf16x2<0>(c2, sc);
-        d23[j] = fp4x2_to_bf16x2<1>(c2, sc);
+        for (int j = 0; j < 8; ++j) {
+          const u32x2 v = lds_ld<u32x2>(buf + (tile * 32 + slot_row(g, j)) * kWinB + 2 * d0 + 8 * n);
+          d01[j] = v.x;
+          d23[j] = v.y;
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const uint8_t* rp = buf + (tile * 32 + slot_row(g, j)) * kRowB;
+          const uint32_t c2 = lds_ld<uint16_t>(rp + d0 / 2 + 2 * n);
+          const float sc = e8m0_scale(rp[256 + d0 / 32 + (n >> 3)]);
+          d01[j] = fp4x2_to_bf16x2<0>(c2, sc);
+          d23[j] = fp4x2_to_bf16x2<1>(c2, sc);
+        }
       }
+      pv4(acc[hh], d01, d23, ph, pl);
     }
-    pv4(acc, d01, d23, ph, pl);
   };
   auto put_p = [&](const float (&z)[8], float m, int ps) {
     u32x4 ph, pl;
@@ -407,10 +481,10 @@ __global__ __launch_bounds__(kThreads) void sparse_decode_kernel(DecArgs a) {
     // One window batch (buffer 0, stored in the prologue) and one FP4 batch (buffer 1)
     // in a single pass: the window tiles are scored while the FP4 rows load, then one
     // softmax and one PV cover all tiles.
-    uint8_t* bufw = lds + kOffBuf;
-    uint8_t* buff = lds + kOffBuf + kBufBytes;
-    const int ntl_w = (min(wr1 - wr0, kWinBatch) + 31) >> 5;
-    const int nrows_f = min(fr1 - fr0, kFp4Batch);
+    uint8_t* bufw = lds;
+    uint8_t* buff = lds + BUF;
+    const int ntl_w = (min(wr1 - wr0, WB) + 31) >> 5;
+    const int nrows_f = min(fr1 - fr0, FB);
     const int ntl_f = (nrows_f + 31) >> 5;
     rowid_all[tid] = row_of(pf_e, pf_page);
     __syncthreads();   // window rows, q and the FP4 row ids stored by every thread
@@ -420,6 +494,7 @@ __global__ __launch_bounds__(kThreads) void sparse_decode_kernel(DecArgs a) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) zw[j] = zf[j] = -INFINITY;
     if (wid < ntl_w) win_qk(bufw, a.W, t, wr0, wid * 32, qf, a.scale_log2, zw);
+    if constexpr (!G::Q_IN_P) __syncthreads();   // q, staged in buffer 1, read by every wave
     store_batch(1, st);
     __syncthreads();   // FP4 rows stored by every thread
     if (wid < ntl_f) fp4_qk(buff, rowid_all, nrows_f, wid * 32, qf, a.scale_log2, zf);
@@ -432,13 +507,13 @@ __global__ __launch_bounds__(kThreads) void sparse_decode_kernel(DecArgs a) {
     __syncthreads();
     float mb = m_part[n];
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w) mb = fmaxf(mb, m_part[w * 16 + n]);
+    for (int w = 1; w < NW; ++w) mb = fmaxf(mb, m_part[w * 16 + n]);
     if (wid < ntl_f) put_p(zf, mb, wid);
-    if (wid < ntl_w) put_p(zw, mb, kMaxTiles + wid);
+    if (wid < ntl_w) put_p(zw, mb, G::MT + wid);
     m_run = mb;
     __syncthreads();
 #pragma unroll 1
-    for (int tile = 0; tile < ntl_w; ++tile) pv_tile(bufw, true, tile, kMaxTiles + tile);
+    for (int tile = 0; tile < ntl_w; ++tile) pv_tile(bufw, true, tile, G::MT + tile);
 #pragma unroll 1
     for (int tile = 0; tile < ntl_f; ++tile) pv_tile(buff, false, tile, tile);
   } else {
@@ -447,11 +522,11 @@ __global__ __launch_bounds__(kThreads) void sparse_decode_kernel(DecArgs a) {
 #pragma unroll 1
   for (int k = 0; k < nb; ++k) {
     const bool is_win = k < n_wb;
-    uint8_t* buf = lds + kOffBuf + (k & 1) * kBufBytes;
+    uint8_t* buf = lds + (k & 1) * BUF;
     const int f = k - n_wb;
-    const int w0 = wr0 + k * kWinBatch;
-    const int nrows = is_win ? min(wr1 - w0, kWinBatch) : min(fr1 - fr0 - f * kFp4Batch, kFp4Batch);
-    const int32_t* rowid = rowid_all + (f & 1) * kFp4Batch;
+    const int w0 = wr0 + k * WB;
+    const int nrows = is_win ? min(wr1 - w0, WB) : min(fr1 - fr0 - f * FB, FB);
+    const int32_t* rowid = rowid_all + (f & 1) * FB;
     const int ntl = (nrows + 31) >> 5;
 
     __syncthreads();   // batch k stored by every thread; batch k-1 fully consumed
@@ -492,9 +567,9 @@ __global__ __launch_bounds__(kThreads) void sparse_decode_kernel(DecArgs a) {
     // ---- batch max of head n (identical in every wave), P for the scored tile ----
     float mb = m_part[n];
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w) mb = fmaxf(mb, m_part[w * 16 + n]);
-    const float m_new = fmaxf(m_run, mb);
-    const float fac = (m_run == -INFINITY || m_new == m_run) ? 1.f : exp2f(m_run - m_new);
+    for (int w = 1; w < NW; ++w) mb = fmaxf(mb, m_part[w * 16 + n]);
+    const float m_new = mb > m_run + kLazy ? mb : m_run;   // lazy: moves only past 2^8 headroom
+    const float fac = (m_run == -INFINITY || m_new == m_run) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
     l_part *= fac;
     if (wid < ntl) put_p(z, m_new, wid);
     // rescale: acc[t][i] belongs to head 4g+i, whose factor lives in lane 4g+i
@@ -508,9 +583,12 @@ __global__ __launch_bounds__(kThreads) void sparse_decode_kernel(DecArgs a) {
       }
       if (__any(any)) {
 #pragma unroll
-        for (int tt = 0; tt < 4; ++tt) {
+        for (int hh = 0; hh < NH; ++hh) {
 #pragma unroll
-          for (int ii = 0; ii < 4; ++ii) acc[tt][ii] *= fo[ii];
+          for (int tt = 0; tt < 4; ++tt) {
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) acc[hh][tt][ii] *= fo[ii];
+          }
         }
       }
     }
@@ -535,72 +613,89 @@ __global__ __launch_bounds__(kThreads) void sparse_decode_kernel(DecArgs a) {
   for (int ii = 0; ii < 4; ++ii) {
     float s = 0.f;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) s += l_w[w * 16 + 4 * g + ii];
+    for (int w = 0; w < NW; ++w) s += l_w[w * 16 + 4 * g + ii];
     lh[ii] = s;
   }
 #pragma unroll
   for (int ii = 0; ii < 4; ++ii) {
     const float inv = lh[ii] > 0.f ? 1.f / lh[ii] : 0.f;
-    const uint32_t v0 = f32_to_bf16_rne(acc[0][ii] * inv), v1 = f32_to_bf16_rne(acc[1][ii] * inv);
-    const uint32_t v2 = f32_to_bf16_rne(acc[2][ii] * inv), v3 = f32_to_bf16_rne(acc[3][ii] * inv);
-    *reinterpret_cast<u32x2*>(a.out + (qi * a.H + hg * 16 + 4 * g + ii) * CSA2_D_LATENT + 64 * wid + 4 * n) =
-        u32x2{v0 | (v1 << 16), v2 | (v3 << 16)};
+#pragma unroll
+    for (int hh = 0; hh < NH; ++hh) {
+      const uint32_t v0 = f32_to_bf16_rne(acc[hh][0][ii] * inv), v1 = f32_to_bf16_rne(acc[hh][1][ii] * inv);
+      const uint32_t v2 = f32_to_bf16_rne(acc[hh][2][ii] * inv), v3 = f32_to_bf16_rne(acc[hh][3][ii] * inv);
+      *reinterpret_cast<u32x2*>(a.out + (qi * a.H + hg * 16 + 4 * g + ii) * CSA2_D_LATENT + G::DW * wid + 64 * hh +
+                                4 * n) = u32x2{v0 | (v1 << 16), v2 | (v3 << 16)};
+    }
   }
   if (a.lse && wid == 0 && g == 0) {
     float s = 0.f;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) s += l_w[w * 16 + n];
+    for (int w = 0; w < NW; ++w) s += l_w[w * 16 + n];
     a.lse[qi * a.H + hg * 16 + n] = s > 0.f ? (m_run + log2f(s)) * kLn2 : -INFINITY;
   }
 }
 
 
 // ---------------------------------------------------------------------------------
-// All 64 heads of a query in one workgroup (H a multiple of 64).  The 16-head
-// kernel above converts every FP4 element once per head group; here the PV operand
-// of a row is converted once and feeds the MFMAs of all four head groups, and every
-// row is read from memory once per query instead of four times.
-//   batches  window batches of 32 rows and FP4 batches of 128 rows (one 34 KB
-//            buffer each), double-buffered, staged through registers as above.
-//   QK       unit (tile t, head group h) = the scores of 16 heads x 32 rows; wave w
-//            takes head group w%4 (its q fragments stay in registers) and tiles
-//            w/4 and w/4 + 2 of the batch.
-//   max, P   per head group through LDS, as above; P of every unit is parked in LDS.
-//   PV       wave w accumulates O[64 heads][dims 64w..64w+63] (64 registers): per
+// 16G heads of a query in one workgroup (G = 2 or 4).  The 16-head kernel above
+// converts every FP4 element once per head group; here the PV operand of a row is
+// converted once and feeds the MFMAs of all G head groups, and every row is read
+// from memory once per workgroup instead of once per head group.
+//   batches  window batches of 128/G rows and FP4 batches of 128 rows, double-
+//            buffered, staged through registers as above.  The FP4 chunk map:
+//            thread tid loads code piece tid%16 of rows tid/16 + 32u and, for
+//            tid < 128, the scales of row tid.
+//   QK       FP4 unit (tile t, head group h) = the scores of 16 heads x 32 rows;
+//            wave w takes head group w%G (its q fragments stay in registers) and
+//            tile w/G (G = 2), or tiles w/4 and w/4 + 2 (G = 4).  Window unit
+//            (tile, head group, 16-row half): one per wave.
+//   max, P   per head group through LDS, as above; P of every unit is parked in LDS
+//            (a window half fills half of its tile's P operand).
+//   PV       wave w accumulates O[16G heads][dims 64w..64w+63] (16G registers): per
 //            tile it converts its 8 rows x 4 dims once and runs the 2 x 4 MFMAs of
-//            each of the four head groups on them.
+//            each head group on them.
 // ---------------------------------------------------------------------------------
-constexpr int kG4 = 4;                                    // head groups per workgroup
-constexpr int64_t kH64MinQueries = 512;                   // launches with fewer queries use 16 heads
+constexpr int64_t kH64MinQueries = 512;                   // launches with fewer queries use 32 heads
 constexpr int kFb64 = 128;                                // FP4 rows per batch (4 tiles)
-constexpr int kWb64 = 32;                                 // window rows per batch (1 tile)
 constexpr int kTiles64 = kFb64 / 32;
-constexpr int kBuf64 = kFb64 * kRowB;                     // 34816 >= kWb64 * kWinB
-constexpr int kStage64 = (kFb64 * 17 + kThreads - 1) / kThreads;
 constexpr int kPf64 = 4;                                  // FP4 batches whose ids are prefetched
-constexpr int kOff64P = 2 * kBuf64;                       // [4 tiles][4 groups][64 lanes][32 B]
-constexpr int kOff64RowId = kOff64P + kTiles64 * kG4 * 64 * kPBytes;   // [4][128] int32
-constexpr int kOff64Max = kOff64RowId + kPf64 * kFb64 * 4;           // [8 waves][16] float
-constexpr int kOff64L = kOff64Max + kWaves * 16 * 4;                  // [8 waves][16] float
-constexpr int kLds64 = kOff64L + kWaves * 16 * 4;
-static_assert(kWb64 * kWinB <= kBuf64, "window batch fits a buffer");
 static_assert(kPf64 * kFb64 == kThreads, "one prefetched row id per thread");
-static_assert(kTiles64 * kG4 == 2 * kWaves, "two QK units per wave");
-static_assert(kLds64 <= 160 * 1024, "LDS budget");
 
-__global__ __launch_bounds__(kThreads) void sparse_decode64_kernel(DecArgs a) {
+// Geometry of the kernel with G head groups.  A window batch holds 8/G tiles so that
+// its units (tile, head group, 16-row half) give every wave one.
+template <int G>
+struct GeoW {
+  static constexpr int WB = 128 / G;                                    // window rows per batch
+  static constexpr int BUF = kFb64 * kRowB > WB * kWinB ? kFb64 * kRowB : WB * kWinB;
+  static constexpr int STAGE = WB * 64 / kThreads > 5 ? WB * 64 / kThreads : 5;   // 16-byte chunks per thread
+  static constexpr int OFF_P = 2 * BUF;                                 // [4 tiles][G groups][64 lanes][32 B]
+  static constexpr int OFF_RID = OFF_P + kTiles64 * G * 64 * kPBytes;  // [4][128] int32
+  static constexpr int OFF_MAX = OFF_RID + kPf64 * kFb64 * 4;          // [8 waves][16] float
+  static constexpr int OFF_L = OFF_MAX + kWaves * 16 * 4;              // [8 waves][16] float
+  static constexpr int LDS = OFF_L + kWaves * 16 * 4;
+  static_assert(WB / 32 * G * 2 == kWaves, "one window unit per wave");
+  static_assert(kTiles64 * G * 2 >= kWaves && kTiles64 * G % kWaves == 0, "whole FP4 units per wave");
+  static_assert(LDS <= 160 * 1024, "LDS budget");
+};
+
+template <int G>
+__global__ __launch_bounds__(kThreads) void sparse_decode_wide_kernel(DecArgs a) {
+  static_assert(G == 2 || G == 4, "32 or 64 heads per workgroup");
+  constexpr int WPG = kWaves / G;                // waves per head group
+  using GW = GeoW<G>;
+  constexpr int WB = GW::WB, STAGE = GW::STAGE;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-  uint8_t* plds = lds + kOff64P;
-  int32_t* rowid_all = reinterpret_cast<int32_t*>(lds + kOff64RowId);
-  float* m_part = reinterpret_cast<float*>(lds + kOff64Max);
-  float* l_w = reinterpret_cast<float*>(lds + kOff64L);
+  uint8_t* plds = lds + GW::OFF_P;
+  int32_t* rowid_all = reinterpret_cast<int32_t*>(lds + GW::OFF_RID);
+  float* m_part = reinterpret_cast<float*>(lds + GW::OFF_MAX);
+  float* l_w = reinterpret_cast<float*>(lds + GW::OFF_L);
 
   // XCD-aware mapping: XCD x takes the contiguous query range [x * q_per_xcd, ...).
   const int xcd = blockIdx.x & 7;
   const int li = blockIdx.x >> 3;
-  const int nhq = a.H / 64;                     // workgroups per query
+  const int nhq = a.H / (16 * G);               // workgroups per query
   const int ql = li / nhq;
-  const int hq = li - ql * nhq;                 // heads 64hq .. 64hq+63
+  const int hq = li - ql * nhq;                 // heads 16G*hq .. +16G-1
   const int64_t qi = (int64_t)xcd * a.q_per_xcd + ql;
   if (ql >= a.q_per_xcd || qi >= (int64_t)a.B * a.C) return;
   const int b = (int)(qi / a.C);
@@ -609,7 +704,7 @@ __global__ __launch_bounds__(kThreads) void sparse_decode64_kernel(DecArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15, g = lane >> 4;
-  const int my_hg = wid & 3;                    // head group of this wave's QK units
+  const int my_hg = wid % G;                    // head group of this wave's QK units
 
   int64_t Lq = a.len[b];
   if (Lq < 0) Lq = 0;
@@ -620,7 +715,7 @@ __global__ __launch_bounds__(kThreads) void sparse_decode64_kernel(DecArgs a) {
   const int32_t* tk = a.topk_idx + qi * a.topk;
   const int32_t* bt = a.block_table + (int64_t)b * a.max_pages;
 
-  const int n_wb = (a.W + kWb64 - 1) / kWb64;
+  const int n_wb = (a.W + WB - 1) / WB;
   const int n_fb = a.topk > 0 ? (a.topk + kFb64 - 1) / kFb64 : 0;
   const int nb = n_wb + n_fb;
 
@@ -637,15 +732,21 @@ __global__ __launch_bounds__(kThreads) void sparse_decode64_kernel(DecArgs a) {
       rowid[i] = page_ok(e) ? row_of(e, bt[e >> 6]) : -1;
     }
   };
-  // Every chunk is loaded, as in the 16-head kernel: no branch splits the loads.
-  auto load_batch = [&](int k, u32x4 (&st)[kStage64]) {
+  // Batch k in registers.  Window: thread tid holds chunks c = tid + 512u (piece c%64
+  // of row c/64).  FP4: code piece tid%16 of rows tid/16 + 32u (u < 4), and for
+  // tid < 128 the scales of row tid.  Every chunk is loaded (one with no row reads
+  // window row 0 of the sequence or cache row 0, and is dropped as zeros), so no
+  // branch splits the loads: they issue back to back.
+  static_assert(kFb64 == 128 && STAGE >= 5 && (WB * 64) % kThreads == 0, "chunk map of a batch");
+  const int cp = tid & 15, cr = tid >> 4;   // code piece and first row of this thread
+  auto load_batch = [&](int k, u32x4 (&st)[STAGE]) {
     const u32x4 zero = {0u, 0u, 0u, 0u};
     if (k < n_wb) {
-      const int w0 = k * kWb64;
+      const int w0 = k * WB;
       int slot0 = (t - (a.W - 1) + w0) % a.W;
       if (slot0 < 0) slot0 += a.W;
 #pragma unroll
-      for (int u = 0; u < kWb64 * 64 / kThreads; ++u) {
+      for (int u = 0; u < WB * 64 / kThreads; ++u) {
         const int c = tid + kThreads * u;
         const int r = c >> 6, piece = c & 63;
         const bool ok = win_valid(a.W, t, w0 + r);
@@ -655,55 +756,52 @@ __global__ __launch_bounds__(kThreads) void sparse_decode64_kernel(DecArgs a) {
         st[u] = ok ? v : zero;
       }
 #pragma unroll
-      for (int u = kWb64 * 64 / kThreads; u < kStage64; ++u) st[u] = zero;
+      for (int u = WB * 64 / kThreads; u < STAGE; ++u) st[u] = zero;
     } else {
       const int f = k - n_wb;
       const int nrows = min(a.topk - f * kFb64, kFb64);
       const int32_t* rowid = rowid_all + (f % kPf64) * kFb64;
-      int rid[kStage64];
+      int rid[STAGE];
 #pragma unroll
-      for (int u = 0; u < kStage64; ++u) {
-        const int c = tid + kThreads * u;
-        rid[u] = rowid[min(c / 17, kFb64 - 1)];
-      }
+      for (int u = 0; u < 4; ++u) rid[u] = cr + 32 * u < nrows ? rowid[cr + 32 * u] : -1;
+      rid[4] = tid < nrows ? rowid[tid & (kFb64 - 1)] : -1;
 #pragma unroll
-      for (int u = 0; u < kStage64; ++u) {
-        const int c = tid + kThreads * u;
-        const int r = c / 17, piece = c - r * 17;
-        const bool ok = c < kFb64 * 17 && r < nrows && rid[u] >= 0;
-        const int64_t rw = ok ? rid[u] : 0;
-        const uint8_t* src = piece < 16 ? a.lat_codes + rw * CSA2_LAT_CODE_BYTES + 16 * piece
-                                        : a.lat_scales + rw * CSA2_LAT_SCALE_BYTES;
-        const u32x4 v = *reinterpret_cast<const u32x4*>(src);
-        st[u] = ok ? v : zero;
+      for (int u = 0; u < 4; ++u) {
+        const uint32_t rw = rid[u] >= 0 ? (uint32_t)rid[u] : 0u;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(a.lat_codes + ((uint64_t)rw << 8) + 16 * cp);
+        st[u] = rid[u] >= 0 ? v : zero;
       }
+      const uint32_t rw = rid[4] >= 0 ? (uint32_t)rid[4] : 0u;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(a.lat_scales + ((uint64_t)rw << 4));
+      st[4] = rid[4] >= 0 ? v : zero;
+      // both paths write every slot, in order: merged stores then share their addresses
+#pragma unroll
+      for (int u = 5; u < STAGE; ++u) st[u] = zero;
     }
   };
-  auto store_batch = [&](int k, const u32x4 (&st)[kStage64]) {
-    uint8_t* buf = lds + (k & 1) * kBuf64;
+  auto store_batch = [&](int k, const u32x4 (&st)[STAGE]) {
+    uint8_t* buf = lds + (k & 1) * GW::BUF;
     if (k < n_wb) {
 #pragma unroll
-      for (int u = 0; u < kWb64 * 64 / kThreads; ++u) {
+      for (int u = 0; u < WB * 64 / kThreads; ++u) {
         const int c = tid + kThreads * u;
         *reinterpret_cast<u32x4*>(buf + (c >> 6) * kWinB + (c & 63) * 16) = st[u];
       }
     } else {
 #pragma unroll
-      for (int u = 0; u < kStage64; ++u) {
-        const int c = tid + kThreads * u;
-        if (c < kFb64 * 17) *reinterpret_cast<u32x4*>(buf + c * 16) = st[u];
-      }
+      for (int u = 0; u < 4; ++u) *reinterpret_cast<u32x4*>(buf + (cr + 32 * u) * kRowB + 16 * cp) = st[u];
+      if (tid < kFb64) *reinterpret_cast<u32x4*>(buf + tid * kRowB + 256) = st[4];
     }
   };
 
   // ---- start ----
-  u32x4 st[kStage64];
+  u32x4 st[STAGE];
   if (n_wb > 0) load_batch(0, st);
   const int pf_f = tid / kFb64, pf_r = tid;     // prefetched id: FP4 batch tid/128, row tid%128
   const int pf_e = (pf_f < n_fb && pf_r < a.topk) ? tk[pf_r] : -1;
   u32x4 qf[16];   // q operand of head 64hq + 16*my_hg + n: dims 128g + 8s .. +7
   {
-    const uint16_t* qp = a.q + (qi * a.H + 64 * hq + 16 * my_hg + n) * CSA2_D_LATENT + 128 * g;
+    const uint16_t* qp = a.q + (qi * a.H + 16 * G * hq + 16 * my_hg + n) * CSA2_D_LATENT + 128 * g;
 #pragma unroll
     for (int s = 0; s < 16; ++s) qf[s] = *reinterpret_cast<const u32x4*>(qp + 8 * s);
   }
@@ -711,21 +809,23 @@ __global__ __launch_bounds__(kThreads) void sparse_decode64_kernel(DecArgs a) {
   if (n_wb > 0) store_batch(0, st);
   __builtin_amdgcn_s_waitcnt(0);
 
-  f32x4 acc[kG4][4];
+  f32x4 acc[G][4];
 #pragma unroll
-  for (int h = 0; h < kG4; ++h)
+  for (int h = 0; h < G; ++h)
 #pragma unroll
     for (int i = 0; i < 4; ++i) acc[h][i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run[kG4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};   // head n of group h
+  float m_run[G];   // head n of group h
+#pragma unroll
+  for (int h = 0; h < G; ++h) m_run[h] = -INFINITY;
   float l_part = 0.f;                                                 // head n of my_hg
 
 #pragma unroll 1
   for (int k = 0; k < nb; ++k) {
     const bool is_win = k < n_wb;
-    uint8_t* buf = lds + (k & 1) * kBuf64;
+    uint8_t* buf = lds + (k & 1) * GW::BUF;
     const int f = k - n_wb;
-    const int w0 = k * kWb64;
-    const int nrows = is_win ? min(a.W - w0, kWb64) : min(a.topk - f * kFb64, kFb64);
+    const int w0 = k * WB;
+    const int nrows = is_win ? min(a.W - w0, WB) : min(a.topk - f * kFb64, kFb64);
     const int32_t* rowid = rowid_all + (f % kPf64) * kFb64;
     const int ntl = (nrows + 31) >> 5;
 
@@ -743,23 +843,23 @@ __global__ __launch_bounds__(kThreads) void sparse_decode64_kernel(DecArgs a) {
       load_batch(k + 1, st);
     }
 
-    // ---- QK: units (tile w/4, group w%4) and (tile w/4 + 2, group w%4) ----
-    const int t0 = wid >> 2, t1 = t0 + 2;
+    // ---- QK.  FP4: units (tile w/G, group w%G) and, with 4 groups, (tile w/4 + 2,
+    // group w%4).  Window: unit (tile wt, group w%G, rows 16wq .. +15 of the tile). ----
+    const int t0 = wid / G, t1 = t0 + 2;
+    const int wt = wid / (2 * G), wq = (wid / G) & 1;
     float z0[8], z1[8];
-    if (t0 < ntl) {
-      if (is_win)
-        win_qk(buf, a.W, t, w0, t0 * 32, qf, a.scale_log2, z0);
-      else
-        fp4_qk(buf, rowid, nrows, t0 * 32, qf, a.scale_log2, z0);
-    } else {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) z0[j] = -INFINITY;
-    }
-    if (t1 < ntl) {
-      fp4_qk(buf, rowid, nrows, t1 * 32, qf, a.scale_log2, z1);   // window batches hold one tile
-    } else {
+    for (int j = 0; j < 8; ++j) z0[j] = z1[j] = -INFINITY;
+    if (is_win) {
+      if (wt < ntl) {
+        float zh[4];
+        win_qk16(buf, a.W, t, w0, 32 * wt + 16 * wq, qf, a.scale_log2, zh);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) z1[j] = -INFINITY;
+        for (int j = 0; j < 4; ++j) z0[j] = zh[j];
+      }
+    } else {
+      if (t0 < ntl) fp4_qk(buf, rowid, nrows, t0 * 32, qf, a.scale_log2, z0);
+      if (G == 4 && t1 < ntl) fp4_qk(buf, rowid, nrows, t1 * 32, qf, a.scale_log2, z1);
     }
     float tmax = z0[0];
 #pragma unroll
@@ -770,39 +870,51 @@ __global__ __launch_bounds__(kThreads) void sparse_decode64_kernel(DecArgs a) {
     __syncthreads();
 
     // ---- per-group batch max of head n, P of this wave's units ----
-    float fac[kG4];
+    float fac[G];
 #pragma unroll
-    for (int h = 0; h < kG4; ++h) {
-      const float mb = fmaxf(m_part[h * 16 + n], m_part[(h + 4) * 16 + n]);
-      const float m_new = fmaxf(m_run[h], mb);
-      fac[h] = (m_run[h] == -INFINITY || m_new == m_run[h]) ? 1.f : exp2f(m_run[h] - m_new);
+    for (int h = 0; h < G; ++h) {
+      float mb = m_part[h * 16 + n];   // over the waves of group h: h, h + G, ...
+#pragma unroll
+      for (int i = 1; i < WPG; ++i) mb = fmaxf(mb, m_part[(h + G * i) * 16 + n]);
+      const float m_new = mb > m_run[h] + kLazy ? mb : m_run[h];   // lazy, as above
+      fac[h] = (m_run[h] == -INFINITY || m_new == m_run[h]) ? 1.f : __builtin_amdgcn_exp2f(m_run[h] - m_new);
       m_run[h] = m_new;
     }
     float my_fac = fac[0], my_m = m_run[0];
 #pragma unroll
-    for (int h = 1; h < kG4; ++h)
+    for (int h = 1; h < G; ++h)
       if (my_hg == h) {
         my_fac = fac[h];
         my_m = m_run[h];
       }
     l_part *= my_fac;
-    if (t0 < ntl) {
+    if (is_win) {
+      if (wt < ntl) {
+        // K-slots 4wq .. 4wq+3 of the tile's P operand: rows 16wq + 4g .. +3
+        const float zh[4] = {z0[0], z0[1], z0[2], z0[3]};
+        u32x2 ph, pl;
+        make_p4(zh, my_m, l_part, ph, pl);
+        uint8_t* pp = plds + ((wt * G + my_hg) * 64 + lane) * kPBytes + 8 * wq;
+        *reinterpret_cast<u32x2*>(pp) = ph;
+        *reinterpret_cast<u32x2*>(pp + 16) = pl;
+      }
+    } else if (t0 < ntl) {
       u32x4 ph, pl;
       make_p(z0, my_m, l_part, ph, pl);
-      uint8_t* pp = plds + ((t0 * kG4 + my_hg) * 64 + lane) * kPBytes;
+      uint8_t* pp = plds + ((t0 * G + my_hg) * 64 + lane) * kPBytes;
       *reinterpret_cast<u32x4*>(pp) = ph;
       *reinterpret_cast<u32x4*>(pp + 16) = pl;
     }
-    if (t1 < ntl) {
+    if (!is_win && G == 4 && t1 < ntl) {
       u32x4 ph, pl;
       make_p(z1, my_m, l_part, ph, pl);
-      uint8_t* pp = plds + ((t1 * kG4 + my_hg) * 64 + lane) * kPBytes;
+      uint8_t* pp = plds + ((t1 * G + my_hg) * 64 + lane) * kPBytes;
       *reinterpret_cast<u32x4*>(pp) = ph;
       *reinterpret_cast<u32x4*>(pp + 16) = pl;
     }
     // rescale: acc[h][t][i] belongs to head 4g+i of group h, factor in lane 4g+i
 #pragma unroll
-    for (int h = 0; h < kG4; ++h) {
+    for (int h = 0; h < G; ++h) {
       float fo[4];
       bool any = false;
 #pragma unroll
@@ -850,8 +962,8 @@ __global__ __launch_bounds__(kThreads) void sparse_decode64_kernel(DecArgs a) {
       bf[3] = __builtin_bit_cast(bf16x8, u32x4{pack_hi(d23[0], d23[1]), pack_hi(d23[2], d23[3]),
                                                pack_hi(d23[4], d23[5]), pack_hi(d23[6], d23[7])});
 #pragma unroll
-      for (int h = 0; h < kG4; ++h) {
-        const uint8_t* pp = plds + ((tile * kG4 + h) * 64 + lane) * kPBytes;
+      for (int h = 0; h < G; ++h) {
+        const uint8_t* pp = plds + ((tile * G + h) * 64 + lane) * kPBytes;
         const bf16x8 ph = __builtin_bit_cast(bf16x8, lds_ld<u32x4>(pp));
         const bf16x8 pl = __builtin_bit_cast(bf16x8, lds_ld<u32x4>(pp + 16));
 #pragma unroll
@@ -865,39 +977,47 @@ __global__ __launch_bounds__(kThreads) void sparse_decode64_kernel(DecArgs a) {
     if (k + 1 < nb) store_batch(k + 1, st);
   }
 
-  // ---- softmax denominators (group h: waves h and h+4), output ----
+  // ---- softmax denominators (group h: waves h, h + G, ...), output ----
   float l_head = l_part;
   l_head += __shfl_xor(l_head, 16, kWave);
   l_head += __shfl_xor(l_head, 32, kWave);
   if (g == 0) l_w[wid * 16 + n] = l_head;
   __syncthreads();
 #pragma unroll
-  for (int h = 0; h < kG4; ++h) {
+  for (int h = 0; h < G; ++h) {
 #pragma unroll
     for (int ii = 0; ii < 4; ++ii) {
-      const float lh = l_w[h * 16 + 4 * g + ii] + l_w[(h + 4) * 16 + 4 * g + ii];
+      float lh = l_w[h * 16 + 4 * g + ii];
+#pragma unroll
+      for (int i = 1; i < WPG; ++i) lh += l_w[(h + G * i) * 16 + 4 * g + ii];
       const float inv = lh > 0.f ? 1.f / lh : 0.f;
       const uint32_t v0 = f32_to_bf16_rne(acc[h][0][ii] * inv), v1 = f32_to_bf16_rne(acc[h][1][ii] * inv);
       const uint32_t v2 = f32_to_bf16_rne(acc[h][2][ii] * inv), v3 = f32_to_bf16_rne(acc[h][3][ii] * inv);
-      *reinterpret_cast<u32x2*>(a.out + (qi * a.H + 64 * hq + 16 * h + 4 * g + ii) * CSA2_D_LATENT + 64 * wid +
+      *reinterpret_cast<u32x2*>(a.out + (qi * a.H + 16 * G * hq + 16 * h + 4 * g + ii) * CSA2_D_LATENT + 64 * wid +
                                 4 * n) = u32x2{v0 | (v1 << 16), v2 | (v3 << 16)};
     }
   }
-  if (a.lse && wid < kG4 && g == 0) {
-    const float s = l_w[wid * 16 + n] + l_w[(wid + 4) * 16 + n];
-    a.lse[qi * a.H + 64 * hq + 16 * wid + n] = s > 0.f ? (m_run[0] * (wid == 0) + m_run[1] * (wid == 1) +
-                                                          m_run[2] * (wid == 2) + m_run[3] * (wid == 3) +
-                                                          log2f(s)) * kLn2
-                                                       : -INFINITY;
+  if (a.lse && wid < G && g == 0) {
+    float s = l_w[wid * 16 + n], m = m_run[0];
+#pragma unroll
+    for (int i = 1; i < WPG; ++i) s += l_w[(wid + G * i) * 16 + n];
+#pragma unroll
+    for (int h = 1; h < G; ++h) m = wid == h ? m_run[h] : m;
+    a.lse[qi * a.H + 16 * G * hq + 16 * wid + n] = s > 0.f ? (m + log2f(s)) * kLn2 : -INFINITY;
   }
 }
 
+// Waves per workgroup of the 16-head kernel.
+constexpr int kNw16 = 4;
+
 bool lds_limit_set() {
   static const bool ok =
-      hipFuncSetAttribute(reinterpret_cast<const void*>(sparse_decode_kernel),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes) == hipSuccess &&
-      hipFuncSetAttribute(reinterpret_cast<const void*>(sparse_decode64_kernel),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, kLds64) == hipSuccess;
+      hipFuncSetAttribute(reinterpret_cast<const void*>(sparse_decode_kernel<kNw16>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, Geo16<kNw16>::LDS) == hipSuccess &&
+      hipFuncSetAttribute(reinterpret_cast<const void*>(sparse_decode_wide_kernel<4>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, GeoW<4>::LDS) == hipSuccess &&
+      hipFuncSetAttribute(reinterpret_cast<const void*>(sparse_decode_wide_kernel<2>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, GeoW<2>::LDS) == hipSuccess;
   return ok;
 }
 
@@ -933,17 +1053,27 @@ int launch_attention_batch(const csa2_cache_t& c, int B, int C, int H, const int
   const int64_t nq = (int64_t)B * C;
   const int64_t per = (nq + 7) / 8;
   a.q_per_xcd = (int)per;
-  // 64 heads per workgroup do more arithmetic per byte but four times the work per
-  // workgroup: worth it once the queries alone give every CU a couple of workgroups.
+  // More heads per workgroup read and convert each row once for more heads, but
+  // leave fewer workgroups: 64 heads once the queries alone give every CU a couple of
+  // workgroups, else 32.
   if (H % 64 == 0 && nq >= kH64MinQueries) {
     const int64_t grid = 8 * per * (H / 64);
     if (grid > 0x7fffffff) return CSA2_EUNSUPPORTED;
-    hipLaunchKernelGGL(sparse_decode64_kernel, dim3((unsigned)grid), dim3(kThreads), kLds64, s, a);
+    constexpr int lds4 = GeoW<4>::LDS;
+    hipLaunchKernelGGL(sparse_decode_wide_kernel<4>, dim3((unsigned)grid), dim3(kThreads), lds4, s, a);
+    return hip_status();
+  }
+  if (H % 32 == 0) {
+    const int64_t grid = 8 * per * (H / 32);
+    if (grid > 0x7fffffff) return CSA2_EUNSUPPORTED;
+    constexpr int lds2 = GeoW<2>::LDS;
+    hipLaunchKernelGGL(sparse_decode_wide_kernel<2>, dim3((unsigned)grid), dim3(kThreads), lds2, s, a);
     return hip_status();
   }
   const int64_t grid = 8 * per * a.HG;
   if (grid > 0x7fffffff) return CSA2_EUNSUPPORTED;
-  hipLaunchKernelGGL(sparse_decode_kernel, dim3((unsigned)grid), dim3(kThreads), kLdsBytes, s, a);
+  constexpr int lds16 = Geo16<kNw16>::LDS;
+  hipLaunchKernelGGL(sparse_decode_kernel<kNw16>, dim3((unsigned)grid), dim3(kNw16 * 64), lds16, s, a);
   return hip_status();
 }
 

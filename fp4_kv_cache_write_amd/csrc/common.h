@@ -59,6 +59,17 @@ __device__ __forceinline__ u32x4 fp4x8_to_bf16x8(uint32_t codes, float scale) {
   return r;
 }
 
+// bf16 head and residual of two weights (hardware round-to-nearest-even), packed with
+// the first weight in the low half: head + residual carries 16 significant bits.
+__device__ __forceinline__ void split_pair(float p0, float p1, uint32_t& hi, uint32_t& lo) {
+  typedef __attribute__((ext_vector_type(2))) __bf16 bf2;
+  const bf2 h = {(__bf16)p0, (__bf16)p1};
+  hi = __builtin_bit_cast(uint32_t, h);
+  const float r0 = p0 - __uint_as_float(hi << 16), r1 = p1 - __uint_as_float(hi & 0xffff0000u);
+  const bf2 l = {(__bf16)r0, (__bf16)r1};
+  lo = __builtin_bit_cast(uint32_t, l);
+}
+
 // Order-preserving map of an fp32 score onto uint32 (larger score -> larger key).
 // -0 is folded onto +0 so that equal scores give equal keys.  Key 0 is reserved for
 // "no entry" (it would be a NaN pattern).

@@ -33,7 +33,7 @@ def _oracle_topk(case, oc, layer, topk):
 # The launcher picks the kernel instance from the number of (sequence, 16-head
 # group) pairs: under 128 pairs each pair's output dims go to four workgroups, from
 # 128 to two, from 512 on the batched kernels run (64 heads per workgroup with >= 512
-# queries).  A wave holds two FP4 tiles at a time; top-K 2048 makes it refill its
+# queries, else 32 heads when H is a multiple of 32, else 16).  A wave holds two FP4 tiles at a time; top-K 2048 makes it refill its
 # slots, and a window of 1024 gives every wave several window units.
 @pytest.mark.parametrize("ctx,H,topk,W", [
     ((2048,), 16, 512, 128),                    # config-0 shape
@@ -43,8 +43,9 @@ def _oracle_topk(case, oc, layer, topk):
     ((700, 3000), 16, 512, 1024),               # long window: several window units per wave
     (tuple(600 + 2 * ((53 * b) % 4000) for b in range(40)), 64, 512, 128),    # 160 pairs: dims split in two
     (tuple(60 + 2 * ((97 * b) % 3000) for b in range(34)), 64, 2048, 1024),  # 136 pairs, refills, long window
-    (tuple(40 + 2 * ((37 * b) % 700) for b in range(130)), 64, 96, 128),     # 520 pairs: batched 16-head kernel
-], ids=["c0", "c1len", "ragged", "topk2048", "win1024", "pairs160", "pairs136_long", "pairs520"])
+    (tuple(40 + 2 * ((37 * b) % 700) for b in range(130)), 64, 96, 128),     # 520 pairs: 32 heads per workgroup
+    (tuple(40 + 2 * ((41 * b) % 900) for b in range(174)), 48, 200, 100),    # 522 pairs, H 48: batched 16-head kernel
+], ids=["c0", "c1len", "ragged", "topk2048", "win1024", "pairs160", "pairs136_long", "pairs520", "pairs522_h48"])
 def test_sparse_decode_matches_oracle(fk, ctx, H, topk, W):
     cfg = small_decode(1, B=len(ctx), ctx=ctx, H=H, pages="random", heavy_frac=0.05, append=0,
                        topk=topk, window=W)
