@@ -867,10 +867,50 @@ __global__ __launch_bounds__(kThreads) void sparse_decode_wide_kernel(DecArgs a)
     tmax = fmaxf(tmax, __shfl_xor(tmax, 16, kWave));
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
     if (g == 0) m_part[wid * 16 + n] = tmax;
-    __syncthreads();
 
-    // ---- per-group batch max of head n, P of this wave's units ----
+    // ---- P of this wave's units against its group's running maximum, written before
+    // the barrier.  It stands unless some group's maximum moves, which the lazy
+    // maximum makes rare after the first rows: then it is written again. ----
+    float my_m = m_run[0];
+#pragma unroll
+    for (int h = 1; h < G; ++h) my_m = my_hg == h ? m_run[h] : my_m;
+    auto write_p = [&](float mref) -> float {
+      float l_add = 0.f;
+      if (is_win) {
+        if (wt < ntl) {
+          // K-slots 4wq .. 4wq+3 of the tile's P operand: rows 16wq + 4g .. +3
+          const float zh[4] = {z0[0], z0[1], z0[2], z0[3]};
+          u32x2 ph, pl;
+          make_p4(zh, mref, l_add, ph, pl);
+          uint8_t* pp = plds + ((wt * G + my_hg) * 64 + lane) * kPBytes + 8 * wq;
+          *reinterpret_cast<u32x2*>(pp) = ph;
+          *reinterpret_cast<u32x2*>(pp + 16) = pl;
+        }
+      } else {
+        if (t0 < ntl) {
+          u32x4 ph, pl;
+          make_p(z0, mref, l_add, ph, pl);
+          uint8_t* pp = plds + ((t0 * G + my_hg) * 64 + lane) * kPBytes;
+          *reinterpret_cast<u32x4*>(pp) = ph;
+          *reinterpret_cast<u32x4*>(pp + 16) = pl;
+        }
+        if (G == 4 && t1 < ntl) {
+          u32x4 ph, pl;
+          make_p(z1, mref, l_add, ph, pl);
+          uint8_t* pp = plds + ((t1 * G + my_hg) * 64 + lane) * kPBytes;
+          *reinterpret_cast<u32x4*>(pp) = ph;
+          *reinterpret_cast<u32x4*>(pp + 16) = pl;
+        }
+      }
+      return l_add;
+    };
+    float l_add = write_p(my_m);
+    __syncthreads();   // batch maxima and P of every unit in LDS
+
+    // ---- per-group batch max of head n (the same in every wave, so the branch below
+    // is uniform over the workgroup) ----
     float fac[G];
+    bool moved = false;
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       float mb = m_part[h * 16 + n];   // over the waves of group h: h, h + G, ...
@@ -878,58 +918,39 @@ __global__ __launch_bounds__(kThreads) void sparse_decode_wide_kernel(DecArgs a)
       for (int i = 1; i < WPG; ++i) mb = fmaxf(mb, m_part[(h + G * i) * 16 + n]);
       const float m_new = mb > m_run[h] + kLazy ? mb : m_run[h];   // lazy, as above
       fac[h] = (m_run[h] == -INFINITY || m_new == m_run[h]) ? 1.f : __builtin_amdgcn_exp2f(m_run[h] - m_new);
+      moved = moved || m_new != m_run[h];
       m_run[h] = m_new;
     }
-    float my_fac = fac[0], my_m = m_run[0];
+    if (__any(moved)) {
+      float my_fac = fac[0];
+      my_m = m_run[0];
 #pragma unroll
-    for (int h = 1; h < G; ++h)
-      if (my_hg == h) {
-        my_fac = fac[h];
-        my_m = m_run[h];
+      for (int h = 1; h < G; ++h) {
+        my_fac = my_hg == h ? fac[h] : my_fac;
+        my_m = my_hg == h ? m_run[h] : my_m;
       }
-    l_part *= my_fac;
-    if (is_win) {
-      if (wt < ntl) {
-        // K-slots 4wq .. 4wq+3 of the tile's P operand: rows 16wq + 4g .. +3
-        const float zh[4] = {z0[0], z0[1], z0[2], z0[3]};
-        u32x2 ph, pl;
-        make_p4(zh, my_m, l_part, ph, pl);
-        uint8_t* pp = plds + ((wt * G + my_hg) * 64 + lane) * kPBytes + 8 * wq;
-        *reinterpret_cast<u32x2*>(pp) = ph;
-        *reinterpret_cast<u32x2*>(pp + 16) = pl;
+      l_part *= my_fac;
+      l_add = write_p(my_m);
+      // rescale: acc[h][t][i] belongs to head 4g+i of group h, factor in lane 4g+i
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        float fo[4];
+        bool any = false;
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+          fo[ii] = __shfl(fac[h], 4 * g + ii, kWave);
+          any = any || fo[ii] != 1.f;
+        }
+        if (__any(any)) {
+#pragma unroll
+          for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) acc[h][tt][ii] *= fo[ii];
+        }
       }
-    } else if (t0 < ntl) {
-      u32x4 ph, pl;
-      make_p(z0, my_m, l_part, ph, pl);
-      uint8_t* pp = plds + ((t0 * G + my_hg) * 64 + lane) * kPBytes;
-      *reinterpret_cast<u32x4*>(pp) = ph;
-      *reinterpret_cast<u32x4*>(pp + 16) = pl;
+      __syncthreads();   // P written again by every wave
     }
-    if (!is_win && G == 4 && t1 < ntl) {
-      u32x4 ph, pl;
-      make_p(z1, my_m, l_part, ph, pl);
-      uint8_t* pp = plds + ((t1 * G + my_hg) * 64 + lane) * kPBytes;
-      *reinterpret_cast<u32x4*>(pp) = ph;
-      *reinterpret_cast<u32x4*>(pp + 16) = pl;
-    }
-    // rescale: acc[h][t][i] belongs to head 4g+i of group h, factor in lane 4g+i
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      float fo[4];
-      bool any = false;
-#pragma unroll
-      for (int ii = 0; ii < 4; ++ii) {
-        fo[ii] = __shfl(fac[h], 4 * g + ii, kWave);
-        any = any || fo[ii] != 1.f;
-      }
-      if (__any(any)) {
-#pragma unroll
-        for (int tt = 0; tt < 4; ++tt)
-#pragma unroll
-          for (int ii = 0; ii < 4; ++ii) acc[h][tt][ii] *= fo[ii];
-      }
-    }
-    __syncthreads();
+    l_part += l_add;
 
     // ---- PV: convert each tile's rows once, MFMAs for all four head groups ----
 #pragma unroll 1
