@@ -760,15 +760,14 @@ __global__ __launch_bounds__(kThreadsA) void attn_kernel(AttnArgs a) {
   const float inv = L > 0.f ? 1.f / L : 0.f;
   uint16_t* op = a.out + (qi * a.H + hg * 16 + head) * CSA2_D_LATENT + 32 * (m >> 1) + 8 * qd0 + kPer * (m & 1);
   if constexpr (kPer == 4) {
-    *reinterpret_cast<u32x2*>(op) = u32x2{f32_to_bf16_rne(o[0] * inv) | (f32_to_bf16_rne(o[1] * inv) << 16),
-                                          f32_to_bf16_rne(o[2] * inv) | (f32_to_bf16_rne(o[3] * inv) << 16)};
+    *reinterpret_cast<u32x2*>(op) = u32x2{pack_bf16x2(o[0] * inv, o[1] * inv), pack_bf16x2(o[2] * inv, o[3] * inv)};
   } else {
 #pragma unroll
     for (int i = 0; i < kPer / 8; ++i) {
       u32x4 pk;
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        pk[e] = f32_to_bf16_rne(o[8 * i + 2 * e] * inv) | (f32_to_bf16_rne(o[8 * i + 2 * e + 1] * inv) << 16);
+        pk[e] = pack_bf16x2(o[8 * i + 2 * e] * inv, o[8 * i + 2 * e + 1] * inv);
       *reinterpret_cast<u32x4*>(op + 8 * i) = pk;
     }
   }

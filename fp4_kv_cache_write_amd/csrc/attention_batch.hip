@@ -618,13 +618,12 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void sparse_decode_kernel(DecArgs 
   }
 #pragma unroll
   for (int ii = 0; ii < 4; ++ii) {
-    const float inv = lh[ii] > 0.f ? 1.f / lh[ii] : 0.f;
+    const float inv = lh[ii] > 0.f ? __builtin_amdgcn_rcpf(lh[ii]) : 0.f;
 #pragma unroll
     for (int hh = 0; hh < NH; ++hh) {
-      const uint32_t v0 = f32_to_bf16_rne(acc[hh][0][ii] * inv), v1 = f32_to_bf16_rne(acc[hh][1][ii] * inv);
-      const uint32_t v2 = f32_to_bf16_rne(acc[hh][2][ii] * inv), v3 = f32_to_bf16_rne(acc[hh][3][ii] * inv);
       *reinterpret_cast<u32x2*>(a.out + (qi * a.H + hg * 16 + 4 * g + ii) * CSA2_D_LATENT + G::DW * wid + 64 * hh +
-                                4 * n) = u32x2{v0 | (v1 << 16), v2 | (v3 << 16)};
+                                4 * n) = u32x2{pack_bf16x2(acc[hh][0][ii] * inv, acc[hh][1][ii] * inv),
+                                               pack_bf16x2(acc[hh][2][ii] * inv, acc[hh][3][ii] * inv)};
     }
   }
   if (a.lse && wid == 0 && g == 0) {
@@ -1011,11 +1010,10 @@ __global__ __launch_bounds__(kThreads) void sparse_decode_wide_kernel(DecArgs a)
       float lh = l_w[h * 16 + 4 * g + ii];
 #pragma unroll
       for (int i = 1; i < WPG; ++i) lh += l_w[(h + G * i) * 16 + 4 * g + ii];
-      const float inv = lh > 0.f ? 1.f / lh : 0.f;
-      const uint32_t v0 = f32_to_bf16_rne(acc[h][0][ii] * inv), v1 = f32_to_bf16_rne(acc[h][1][ii] * inv);
-      const uint32_t v2 = f32_to_bf16_rne(acc[h][2][ii] * inv), v3 = f32_to_bf16_rne(acc[h][3][ii] * inv);
+      const float inv = lh > 0.f ? __builtin_amdgcn_rcpf(lh) : 0.f;
       *reinterpret_cast<u32x2*>(a.out + (qi * a.H + 16 * G * hq + 16 * h + 4 * g + ii) * CSA2_D_LATENT + 64 * wid +
-                                4 * n) = u32x2{v0 | (v1 << 16), v2 | (v3 << 16)};
+                                4 * n) = u32x2{pack_bf16x2(acc[h][0][ii] * inv, acc[h][1][ii] * inv),
+                                               pack_bf16x2(acc[h][2][ii] * inv, acc[h][3][ii] * inv)};
     }
   }
   if (a.lse && wid < G && g == 0) {

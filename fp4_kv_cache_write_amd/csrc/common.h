@@ -59,6 +59,14 @@ __device__ __forceinline__ u32x4 fp4x8_to_bf16x8(uint32_t codes, float scale) {
   return r;
 }
 
+// Two floats as a packed bf16 pair (first in the low half), rounded to nearest even
+// by the hardware convert (the same bits as f32_to_bf16_rne for every non-NaN input).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  typedef __attribute__((ext_vector_type(2))) __bf16 bf2;
+  const bf2 h = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, h);
+}
+
 // bf16 head and residual of two weights (hardware round-to-nearest-even), packed with
 // the first weight in the low half: head + residual carries 16 significant bits.
 __device__ __forceinline__ void split_pair(float p0, float p1, uint32_t& hi, uint32_t& lo) {
