@@ -316,9 +316,15 @@ __global__ __launch_bounds__(kThreadsA) void attn_kernel(AttnArgs a) {
     dma16(a.q + (qi * a.H + hg * 16 + head) * CSA2_D_LATENT + 8 * swz_q(lane, head),
           lds + kOffQ + head * kWinRowB);
   }
-  // B operand of k-step 4c+u: head n, dims 128c + 32g + 8u .. +7
+  // B operand of k-step 4c+u: head n, dims 128c + 32g + 8u .. +7, at chunk
+  // swz_q(16c + 4g + u, n) = 16c + (xg ^ u) of head n's row, xg = 4g ^ n: four lane
+  // bases, the 256c in the instruction's offset.
+  const int xg = (4 * g) ^ n;
+  const uint8_t* qb[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) qb[u] = qlds + n * kWinRowB + 16 * (xg ^ u);
   auto q_op = [&](int c, int u) __attribute__((always_inline)) {
-    return __builtin_bit_cast(bf16x8, lds_ld<u32x4>(qlds + n * kWinRowB + 16 * swz_q(16 * c + 4 * g + u, n)));
+    return __builtin_bit_cast(bf16x8, lds_ld<u32x4>(qb[u] + 256 * c));
   };
   // Window unit wu into the region: row r = slot 16wu + r at win_row_off(r).  A slot
   // with no token reads the row of position t (always present) and is masked in the
@@ -415,7 +421,11 @@ __global__ __launch_bounds__(kThreadsA) void attn_kernel(AttnArgs a) {
     float z[4];
     {
       f32x4 sa[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+      // row n's chunk swz_win(16c + 4g + u, n) = 16c + (xg ^ (u ^ c)): four lane bases
       const uint8_t* rp = region + win_row_off(n);
+      const uint8_t* wb[4];
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) wb[kk] = rp + 16 * (xg ^ kk);
       // chunk c: row n's dims 128c + 32g + 8u .. +7 and q's k-steps; chunk c+1's reads
       // are issued before chunk c's products (the unit often runs with its SIMD's other
       // wave idle, so nothing else hides the LDS latency)
@@ -426,7 +436,7 @@ __global__ __launch_bounds__(kThreadsA) void attn_kernel(AttnArgs a) {
         WinIn in;
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          in.v[u] = lds_ld<u32x4>(rp + 16 * swz_win(16 * c + 4 * g + u, n));
+          in.v[u] = lds_ld<u32x4>(wb[u ^ c] + 256 * c);
           in.q[u] = __builtin_bit_cast(u32x4, q_op(c, u));
         }
         return in;
