@@ -346,6 +346,30 @@ struct MergeArgs {
 
 // blockIdx.y == 0: top-K over the chunk candidates; == 1: HSI pool over block maxima.
 // KPT (keys per thread) is the smallest of 4/8/16/32 that covers both key sets.
+// A thread's run of KPT consecutive words v[i] = base[p0 + i] (p0 a multiple of KPT);
+// words at or past n read as `fill`.  The run is read with 16-byte loads when it lies
+// inside [0, n) and base is 16-byte aligned, else word by word: word loads with
+// 4 * KPT bytes between lanes touched a cache line per lane and pair of loads.
+template <int KPT, class T>
+__device__ __forceinline__ void load_run(const T* base, int p0, int n, T fill, T (&v)[KPT]) {
+  static_assert(KPT % 4 == 0 && sizeof(T) == 4, "runs of 4-byte words in 16-byte pieces");
+  if ((reinterpret_cast<uintptr_t>(base) & 15) == 0 && p0 + KPT <= n) {
+#pragma unroll
+    for (int i = 0; i < KPT; i += 4) {
+      const u32x4 x = *reinterpret_cast<const u32x4*>(base + p0 + i);
+      // value conversions: __builtin_bit_cast of a vector element miscompiles here
+      // (every element read as .x)
+      v[i] = (T)x.x;
+      v[i + 1] = (T)x.y;
+      v[i + 2] = (T)x.z;
+      v[i + 3] = (T)x.w;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) v[i] = p0 + i < n ? base[p0 + i] : fill;
+  }
+}
+
 template <int KPT>
 __global__ __launch_bounds__(kMergeThreads) void index_merge_kernel(MergeArgs a) {
   __shared__ __align__(16) uint32_t hist[kSelectHist];
@@ -363,12 +387,8 @@ __global__ __launch_bounds__(kMergeThreads) void index_merge_kernel(MergeArgs a)
     const uint32_t* ckey = a.cand_key + (int64_t)b * a.n_chunks * a.topk;
     const int32_t* cidx = a.cand_idx + (int64_t)b * a.n_chunks * a.topk;
     int32_t id[KPT];
-#pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      const bool in = p0 + i < N;
-      kr[i] = in ? ckey[p0 + i] : 0u;
-      id[i] = in ? cidx[p0 + i] : -1;
-    }
+    load_run<KPT>(ckey, p0, N, 0u, kr);
+    load_run<KPT>(cidx, p0, N, -1, id);
     const SelectResult sr = block_select<kMergeThreads, KPT>(kr, a.topk, hist, scratch);
     int32_t* out = a.topk_idx + (int64_t)b * a.topk;
     block_emit<kMergeThreads, KPT>(kr, sr, scratch, [&](int i, uint32_t pos) { out[pos] = id[i]; });
@@ -380,11 +400,7 @@ __global__ __launch_bounds__(kMergeThreads) void index_merge_kernel(MergeArgs a)
     const int cb = a.cand_block;
     const int nb = (n_vis + cb - 1) / cb;
     const uint32_t* bm = a.block_max + (int64_t)b * a.max_blocks;
-#pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      const int v = p0 + i;
-      kr[i] = v < nb - 1 ? bm[v] : 0u;
-    }
+    load_run<KPT>(bm, p0, nb - 1, 0u, kr);
     int32_t* out = a.pool + (int64_t)b * a.pool_blocks;
     uint32_t n_old = 0;
     if (nb > 1 && a.pool_blocks > 1) {                                // uniform over the block
@@ -438,12 +454,8 @@ __global__ __launch_bounds__(kMergeThreads) void index_group_kernel(GroupArgs a)
   const int32_t* cidx = a.cand_idx + cbase * a.topk;
   uint32_t kr[KPT];
   int32_t id[KPT];
-#pragma unroll
-  for (int i = 0; i < KPT; ++i) {
-    const bool in = p0 + i < N;
-    kr[i] = in ? ckey[p0 + i] : 0u;
-    id[i] = in ? cidx[p0 + i] : -1;
-  }
+  load_run<KPT>(ckey, p0, N, 0u, kr);
+  load_run<KPT>(cidx, p0, N, -1, id);
   const SelectResult sr = block_select<kMergeThreads, KPT>(kr, a.topk, hist, scratch);
   uint32_t* gk = a.grp_key + gslot * a.topk;
   int32_t* gi = a.grp_idx + gslot * a.topk;
