@@ -21,10 +21,11 @@
 //                           workgroups share a CU.
 // Rows are processed in batches that live in one of two LDS buffers: window
 // batches of bf16 rows (pitch 1040 B), then FP4 batches (256 code bytes + 16 scale
-// bytes, pitch 272 B).  Batch k+1 is loaded into registers when batch k starts and
-// written to the free buffer after batch k's PV, so the loads overlap batch k's
-// arithmetic.  Chunks of rows that are absent are written as zeros, so stale bytes
-// never meet a zero weight (0 * NaN is not 0).  The selected entries' page lookups
+// bytes, pitch 272 B).  Batch k+1 is loaded when batch k starts -- the wide kernel
+// copies it straight into the free buffer (global_load_lds), the 16-head kernel
+// stages it in registers and stores it after batch k's PV -- so the loads overlap
+// batch k's arithmetic.  Rows that are absent arrive as zeros, so stale bytes never
+// meet a zero weight (0 * NaN is not 0).  The selected entries' page lookups
 // are loads issued at the start and consumed only when the first FP4 batch is
 // loaded, so they hide behind the window batches.  Per-wave timestamps on the
 // MI355X (the mixed batch) put the time in each batch's vector ALU work and its
@@ -640,16 +641,18 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void sparse_decode_kernel(DecArgs 
 // converts every FP4 element once per head group; here the PV operand of a row is
 // converted once and feeds the MFMAs of all G head groups, and every row is read
 // from memory once per workgroup instead of once per head group.
-//   batches  window batches of 128/G rows and FP4 batches of 128 rows, double-
-//            buffered, staged through registers as above.  The FP4 chunk map:
-//            thread tid loads code piece tid%16 of rows tid/16 + 32u and, for
-//            tid < 128, the scales of row tid.
+//   batches  window batches of 64 rows and FP4 batches of 128 rows, double-
+//            buffered, copied straight into LDS: a window row is one 1 KB copy, an
+//            FP4 batch image (17 16-byte pieces per row) 34 copies of 1 KB.  With no
+//            staging registers the 64-head instance fits 64-row window batches too
+//            (two barriers' worth of fixed cost fewer than four 32-row batches).
 //   QK       FP4 unit (tile t, head group h) = the scores of 16 heads x 32 rows;
 //            wave w takes head group w%G (its q fragments stay in registers) and
 //            tile w/G (G = 2), or tiles w/4 and w/4 + 2 (G = 4).  Window unit
-//            (tile, head group, 16-row half): one per wave.
+//            (tile w/4, head group, and with G = 2 a 16-row half): one per wave.
 //   max, P   per head group through LDS, as above; P of every unit is parked in LDS
-//            (a window half fills half of its tile's P operand).
+//            (a window half fills half of its tile's P operand), an FP4 batch's in
+//            the unused tail of its own buffer.
 //   PV       wave w accumulates O[16G heads][dims 64w..64w+63] (16G registers): per
 //            tile it converts its 8 rows x 4 dims once and runs the 2 x 4 MFMAs of
 //            each head group on them.
@@ -660,31 +663,55 @@ constexpr int kTiles64 = kFb64 / 32;
 constexpr int kPf64 = 4;                                  // FP4 batches whose ids are prefetched
 static_assert(kPf64 * kFb64 == kThreads, "one prefetched row id per thread");
 
-// Geometry of the kernel with G head groups.  A window batch holds 8/G tiles so that
-// its units (tile, head group, 16-row half) give every wave one.
+// Geometry of the kernel with G head groups.  Batches are copied from memory straight
+// into LDS (global_load_lds), so a batch in flight holds no registers.  A window batch
+// is 64 rows (two tiles); its units (tile, head group, and with G = 2 a 16-row half)
+// give every wave one.  An FP4 batch is 128 rows; its P operands sit in the unused
+// tail of its own buffer, the window batches' in an area of their own.
 template <int G>
 struct GeoW {
-  static constexpr int WB = 128 / G;                                    // window rows per batch
-  static constexpr int BUF = kFb64 * kRowB > WB * kWinB ? kFb64 * kRowB : WB * kWinB;
-  static constexpr int STAGE = WB * 64 / kThreads > 5 ? WB * 64 / kThreads : 5;   // 16-byte chunks per thread
-  static constexpr int OFF_P = 2 * BUF;                                 // [4 tiles][G groups][64 lanes][32 B]
-  static constexpr int OFF_RID = OFF_P + kTiles64 * G * 64 * kPBytes;  // [4][128] int32
+  static constexpr int WB = 64;                                        // window rows per batch
+  static constexpr int PF = kTiles64 * G * 64 * kPBytes;               // P of an FP4 batch
+  static constexpr int BUF = WB * kWinB > kFb64 * kRowB + PF ? WB * kWinB : kFb64 * kRowB + PF;
+  static constexpr int OFF_PF = kFb64 * kRowB;                          // in the FP4 batch's buffer
+  static constexpr int OFF_PW = 2 * BUF;                                // [2 tiles][G groups][64 lanes][32 B]
+  static constexpr int OFF_RID = OFF_PW + (WB / 32) * G * 64 * kPBytes; // [4][128] int32
   static constexpr int OFF_MAX = OFF_RID + kPf64 * kFb64 * 4;          // [8 waves][16] float
   static constexpr int OFF_L = OFF_MAX + kWaves * 16 * 4;              // [8 waves][16] float
   static constexpr int LDS = OFF_L + kWaves * 16 * 4;
-  static_assert(WB / 32 * G * 2 == kWaves, "one window unit per wave");
+  static_assert(WB / 32 * G * (G == 2 ? 2 : 1) == kWaves, "one window unit per wave");
+  static_assert(WB % kWaves == 0, "whole window rows per wave");
   static_assert(kTiles64 * G * 2 >= kWaves && kTiles64 * G % kWaves == 0, "whole FP4 units per wave");
   static_assert(LDS <= 160 * 1024, "LDS budget");
 };
+constexpr int kFpDma = kFb64 * 17 / 64;     // 1 KB copies of an FP4 batch image (34)
+static_assert(kFb64 * 17 % 64 == 0 && kFpDma > 4 * kWaves && kFpDma <= 5 * kWaves, "4 or 5 copies per wave");
+
+// Rows that are absent (window slots before position 0, invalid ids, unmapped pages,
+// the tail of the last batch) are copied from here, so stale LDS bytes never meet a
+// zero weight (0 * NaN is not 0).  Read only; zero from load time.
+__device__ __attribute__((aligned(16))) uint8_t g_zero_row[1024];
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+// 16 bytes per lane from global memory into LDS: lane l's bytes land at dst + 16 l.
+__device__ __forceinline__ void dma16(const void* src, uint8_t* dst) {
+  __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)dst, 16, 0, 0);
+}
+__device__ __forceinline__ void wait_all_vm() { __builtin_amdgcn_s_waitcnt(0x3f70); }   // vmcnt(0)
+// Workgroup barrier after this wave's LDS accesses have completed.  Bare: the fence of
+// __syncthreads would also wait for the LDS copies in flight.
+__device__ __forceinline__ void barrier_lds() {
+  __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
+  asm volatile("s_barrier" ::: "memory");
+}
 
 template <int G>
 __global__ __launch_bounds__(kThreads) void sparse_decode_wide_kernel(DecArgs a) {
   static_assert(G == 2 || G == 4, "32 or 64 heads per workgroup");
   constexpr int WPG = kWaves / G;                // waves per head group
   using GW = GeoW<G>;
-  constexpr int WB = GW::WB, STAGE = GW::STAGE;
+  constexpr int WB = GW::WB;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-  uint8_t* plds = lds + GW::OFF_P;
   int32_t* rowid_all = reinterpret_cast<int32_t*>(lds + GW::OFF_RID);
   float* m_part = reinterpret_cast<float*>(lds + GW::OFF_MAX);
   float* l_w = reinterpret_cast<float*>(lds + GW::OFF_L);
@@ -731,82 +758,72 @@ __global__ __launch_bounds__(kThreads) void sparse_decode_wide_kernel(DecArgs a)
       rowid[i] = page_ok(e) ? row_of(e, bt[e >> 6]) : -1;
     }
   };
-  // Batch k in registers.  Window: thread tid holds chunks c = tid + 512u (piece c%64
-  // of row c/64).  FP4: code piece tid%16 of rows tid/16 + 32u (u < 4), and for
-  // tid < 128 the scales of row tid.  Every chunk is loaded (one with no row reads
-  // window row 0 of the sequence or cache row 0, and is dropped as zeros), so no
-  // branch splits the loads: they issue back to back.
-  static_assert(kFb64 == 128 && STAGE >= 5 && (WB * 64) % kThreads == 0, "chunk map of a batch");
-  const int cp = tid & 15, cr = tid >> 4;   // code piece and first row of this thread
-  auto load_batch = [&](int k, u32x4 (&st)[STAGE]) {
-    const u32x4 zero = {0u, 0u, 0u, 0u};
-    if (k < n_wb) {
-      const int w0 = k * WB;
-      int slot0 = (t - (a.W - 1) + w0) % a.W;
-      if (slot0 < 0) slot0 += a.W;
+  // Batch j into buffer j % 2.  Window: wave w copies rows w + 8u, one 1 KB copy per
+  // row at the padded pitch.  FP4: 1 KB copy c of the batch image (chunk 64c + lane
+  // is piece p of row r, 17 pieces per row: 16 of codes, then the scales) for
+  // c = w + 8u.
+  const uint8_t* zero = g_zero_row;
+  int rp_pk[5];   // FP4 copy u of this lane: row r and piece p of chunk 64c + lane, as (r << 5) | p
 #pragma unroll
-      for (int u = 0; u < WB * 64 / kThreads; ++u) {
-        const int c = tid + kThreads * u;
-        const int r = c >> 6, piece = c & 63;
-        const bool ok = win_valid(a.W, t, w0 + r);
-        int row = a.prefill ? ci + w0 + r : (slot0 + r >= a.W ? slot0 + r - a.W : slot0 + r);
-        row = ok ? row : 0;
-        const u32x4 v = *reinterpret_cast<const u32x4*>(win_b + (int64_t)row * CSA2_D_LATENT + 8 * piece);
-        st[u] = ok ? v : zero;
+  for (int u = 0; u < 5; ++u) {
+    const int ch = 64 * (wid + kWaves * u) + lane;
+    const int r = ch / 17;
+    rp_pk[u] = (r << 5) | (ch - 17 * r);
+  }
+  auto issue_batch = [&](int j) __attribute__((always_inline)) {
+    uint8_t* buf = lds + (j & 1) * GW::BUF;
+    if (j < n_wb) {
+      const int w0 = j * WB;
+#pragma unroll
+      for (int u = 0; u < WB / kWaves; ++u) {
+        const int r = wid + kWaves * u;
+        const int sl = w0 + r;                     // window slot: position t - (W-1) + sl
+        const uint8_t* src = zero + 16 * lane;
+        if (win_valid(a.W, t, sl)) {
+          int row;
+          if (a.prefill) {
+            row = ci + sl;
+          } else {
+            row = (t - (a.W - 1) + sl) % a.W;
+            row = row < 0 ? row + a.W : row;
+          }
+          src = reinterpret_cast<const uint8_t*>(win_b + (int64_t)row * CSA2_D_LATENT) + 16 * lane;
+        }
+        dma16(src, buf + r * kWinB);
       }
-#pragma unroll
-      for (int u = WB * 64 / kThreads; u < STAGE; ++u) st[u] = zero;
     } else {
-      const int f = k - n_wb;
+      const int f = j - n_wb;
       const int nrows = min(a.topk - f * kFb64, kFb64);
       const int32_t* rowid = rowid_all + (f % kPf64) * kFb64;
-      int rid[STAGE];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) rid[u] = cr + 32 * u < nrows ? rowid[cr + 32 * u] : -1;
-      rid[4] = tid < nrows ? rowid[tid & (kFb64 - 1)] : -1;
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const uint32_t rw = rid[u] >= 0 ? (uint32_t)rid[u] : 0u;
-        const u32x4 v = *reinterpret_cast<const u32x4*>(a.lat_codes + ((uint64_t)rw << 8) + 16 * cp);
-        st[u] = rid[u] >= 0 ? v : zero;
+      for (int u = 0; u < 5; ++u) {
+        const int c = wid + kWaves * u;
+        if (c < kFpDma) {
+          const int r = rp_pk[u] >> 5, p = rp_pk[u] & 31;
+          const int rid = r < nrows ? rowid[r] : -1;
+          // one 64-bit add per copy in the loop: hoisted per-copy pointers would hold
+          // registers across the whole batch loop
+          const uint8_t* base = rid < 0 ? zero : (p < 16 ? a.lat_codes : a.lat_scales);
+          const uint64_t off = rid < 0 ? (uint64_t)(16 * p)
+                                       : (p < 16 ? ((uint64_t)rid << 8) + (uint64_t)(16 * p) : (uint64_t)rid << 4);
+          dma16(base + off, buf + 1024 * c);
+        }
       }
-      const uint32_t rw = rid[4] >= 0 ? (uint32_t)rid[4] : 0u;
-      const u32x4 v = *reinterpret_cast<const u32x4*>(a.lat_scales + ((uint64_t)rw << 4));
-      st[4] = rid[4] >= 0 ? v : zero;
-      // both paths write every slot, in order: merged stores then share their addresses
-#pragma unroll
-      for (int u = 5; u < STAGE; ++u) st[u] = zero;
-    }
-  };
-  auto store_batch = [&](int k, const u32x4 (&st)[STAGE]) {
-    uint8_t* buf = lds + (k & 1) * GW::BUF;
-    if (k < n_wb) {
-#pragma unroll
-      for (int u = 0; u < WB * 64 / kThreads; ++u) {
-        const int c = tid + kThreads * u;
-        *reinterpret_cast<u32x4*>(buf + (c >> 6) * kWinB + (c & 63) * 16) = st[u];
-      }
-    } else {
-#pragma unroll
-      for (int u = 0; u < 4; ++u) *reinterpret_cast<u32x4*>(buf + (cr + 32 * u) * kRowB + 16 * cp) = st[u];
-      if (tid < kFb64) *reinterpret_cast<u32x4*>(buf + tid * kRowB + 256) = st[4];
     }
   };
 
   // ---- start ----
-  u32x4 st[STAGE];
-  if (n_wb > 0) load_batch(0, st);
   const int pf_f = tid / kFb64, pf_r = tid;     // prefetched id: FP4 batch tid/128, row tid%128
   const int pf_e = (pf_f < n_fb && pf_r < a.topk) ? tk[pf_r] : -1;
-  u32x4 qf[16];   // q operand of head 64hq + 16*my_hg + n: dims 128g + 8s .. +7
+  u32x4 qf[16];   // q operand of head 16G*hq + 16*my_hg + n: dims 128g + 8s .. +7
   {
     const uint16_t* qp = a.q + (qi * a.H + 16 * G * hq + 16 * my_hg + n) * CSA2_D_LATENT + 128 * g;
 #pragma unroll
     for (int s = 0; s < 16; ++s) qf[s] = *reinterpret_cast<const u32x4*>(qp + 8 * s);
   }
   int pf_page = -1;
-  if (n_wb > 0) store_batch(0, st);
-  __builtin_amdgcn_s_waitcnt(0);
+  if (n_wb > 0) issue_batch(0);
+  wait_all_vm();
 
   f32x4 acc[G][4];
 #pragma unroll
@@ -828,33 +845,39 @@ __global__ __launch_bounds__(kThreads) void sparse_decode_wide_kernel(DecArgs a)
     const int32_t* rowid = rowid_all + (f % kPf64) * kFb64;
     const int ntl = (nrows + 31) >> 5;
 
-    __syncthreads();   // batch k stored by every thread; batch k-1 fully consumed
+    uint8_t* plds = is_win ? lds + GW::OFF_PW : buf + GW::OFF_PF;   // P of this batch's units
+    barrier_lds();   // batch k copied in by every wave; batch k-1 fully consumed
     if (k == 0 && page_ok(pf_e)) pf_page = bt[pf_e >> 6];
     if (k + 1 < nb) {
       const int f1 = k + 1 - n_wb;
       if (f1 == 0) {
         rowid_all[tid] = row_of(pf_e, pf_page);
-        __syncthreads();
+        barrier_lds();
       } else if (f1 >= kPf64) {
         resolve_rows(f1);
-        __syncthreads();
+        barrier_lds();
       }
-      load_batch(k + 1, st);
+      issue_batch(k + 1);   // into the other buffer, free since batch k began
     }
 
     // ---- QK.  FP4: units (tile w/G, group w%G) and, with 4 groups, (tile w/4 + 2,
-    // group w%4).  Window: unit (tile wt, group w%G, rows 16wq .. +15 of the tile). ----
+    // group w%4).  Window: unit (tile wt = w/4, group w%G), with 2 groups only rows
+    // 16wq .. +15 of the tile. ----
     const int t0 = wid / G, t1 = t0 + 2;
-    const int wt = wid / (2 * G), wq = (wid / G) & 1;
+    const int wt = wid / 4, wq = (wid / G) & 1;
     float z0[8], z1[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) z0[j] = z1[j] = -INFINITY;
     if (is_win) {
       if (wt < ntl) {
-        float zh[4];
-        win_qk16(buf, a.W, t, w0, 32 * wt + 16 * wq, qf, a.scale_log2, zh);
+        if constexpr (G == 2) {
+          float zh[4];
+          win_qk16(buf, a.W, t, w0, 32 * wt + 16 * wq, qf, a.scale_log2, zh);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) z0[j] = zh[j];
+          for (int j = 0; j < 4; ++j) z0[j] = zh[j];
+        } else {
+          win_qk(buf, a.W, t, w0, 32 * wt, qf, a.scale_log2, z0);
+        }
       }
     } else {
       if (t0 < ntl) fp4_qk(buf, rowid, nrows, t0 * 32, qf, a.scale_log2, z0);
@@ -877,13 +900,21 @@ __global__ __launch_bounds__(kThreads) void sparse_decode_wide_kernel(DecArgs a)
       float l_add = 0.f;
       if (is_win) {
         if (wt < ntl) {
-          // K-slots 4wq .. 4wq+3 of the tile's P operand: rows 16wq + 4g .. +3
-          const float zh[4] = {z0[0], z0[1], z0[2], z0[3]};
-          u32x2 ph, pl;
-          make_p4(zh, mref, l_add, ph, pl);
-          uint8_t* pp = plds + ((wt * G + my_hg) * 64 + lane) * kPBytes + 8 * wq;
-          *reinterpret_cast<u32x2*>(pp) = ph;
-          *reinterpret_cast<u32x2*>(pp + 16) = pl;
+          if constexpr (G == 2) {
+            // K-slots 4wq .. 4wq+3 of the tile's P operand: rows 16wq + 4g .. +3
+            const float zh[4] = {z0[0], z0[1], z0[2], z0[3]};
+            u32x2 ph, pl;
+            make_p4(zh, mref, l_add, ph, pl);
+            uint8_t* pp = plds + ((wt * G + my_hg) * 64 + lane) * kPBytes + 8 * wq;
+            *reinterpret_cast<u32x2*>(pp) = ph;
+            *reinterpret_cast<u32x2*>(pp + 16) = pl;
+          } else {
+            u32x4 ph, pl;
+            make_p(z0, mref, l_add, ph, pl);
+            uint8_t* pp = plds + ((wt * G + my_hg) * 64 + lane) * kPBytes;
+            *reinterpret_cast<u32x4*>(pp) = ph;
+            *reinterpret_cast<u32x4*>(pp + 16) = pl;
+          }
         }
       } else {
         if (t0 < ntl) {
@@ -904,7 +935,7 @@ __global__ __launch_bounds__(kThreads) void sparse_decode_wide_kernel(DecArgs a)
       return l_add;
     };
     float l_add = write_p(my_m);
-    __syncthreads();   // batch maxima and P of every unit in LDS
+    barrier_lds();   // batch maxima and P of every unit in LDS
 
     // ---- per-group batch max of head n (the same in every wave, so the branch below
     // is uniform over the workgroup) ----
@@ -947,7 +978,7 @@ __global__ __launch_bounds__(kThreads) void sparse_decode_wide_kernel(DecArgs a)
             for (int ii = 0; ii < 4; ++ii) acc[h][tt][ii] *= fo[ii];
         }
       }
-      __syncthreads();   // P written again by every wave
+      barrier_lds();   // P written again by every wave
     }
     l_part += l_add;
 
@@ -994,7 +1025,7 @@ __global__ __launch_bounds__(kThreads) void sparse_decode_wide_kernel(DecArgs a)
           acc[h][tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, bf[tt], acc[h][tt], 0, 0, 0);
       }
     }
-    if (k + 1 < nb) store_batch(k + 1, st);
+    wait_all_vm();   // this wave's copies of batch k+1 have landed
   }
 
   // ---- softmax denominators (group h: waves h, h + G, ...), output ----
