@@ -12,31 +12,30 @@
 
 namespace csa2 {
 
-// Quantise the lane's 8 values; the 32-value block is lanes 4q..4q+3.
+// Quantise the lane's 8 values; the 32-value block is lanes 4q..4q+3.  The block
+// maximum is reduced over the quad with two DPP quad permutations.  The codes come
+// from the gfx950 convert v_cvt_scalef32_pk_fp4_f32, which divides by the power of
+// two held in its scale operand's exponent field and rounds to the nearest e2m1 value
+// with ties to the even code, saturating at 6 (sign kept, -0 -> code 8).  Measured on
+// the MI355X against that rule: every value of a dense sweep of [0, 9) and of its
+// negatives, the ties and their neighbours, at scale exponent fields 0..254,
+// subnormal inputs included -- no difference.  So the codes are those of the plain
+// rule of csa2_write_kv; only non-finite inputs (outside that rule) differ from it.
 __device__ __forceinline__ void mx_quant8(const float (&y)[8], uint32_t& codes, uint32_t& u) {
   float a = 0.0f;
 #pragma unroll
   for (int k = 0; k < 8; ++k) a = fmaxf(a, fabsf(y[k]));
-  a = fmaxf(a, __shfl_xor(a, 1, kWave));
-  a = fmaxf(a, __shfl_xor(a, 2, kWave));
+  a = fmaxf(a, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(a), 0xb1, 0xf, 0xf, false)));  // quad_perm 1,0,3,2
+  a = fmaxf(a, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(a), 0x4e, 0xf, 0xf, false)));  // quad_perm 2,3,0,1
   // scale exponent e = floor(log2 a) - 2 clamped at -127  ->  byte u = e + 127
   const uint32_t bexp = (__float_as_uint(a) >> 23) & 0xffu;
   u = bexp > 2u ? bexp - 2u : 0u;
-  const float inv = __uint_as_float((254u - u) << 23);   // 2^-e, exact
-  const bool zero = (a == 0.0f);
-  codes = 0u;
-#pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    const float v = fabsf(y[k]) * inv;                   // in [0, 8), exact
-    // nearest e2m1 magnitude, ties to the even code: 0.25->0 0.75->2 1.25->2
-    // 1.75->4 2.5->4 3.5->6 5->6, saturating at 6 (code 7)
-    uint32_t m = (uint32_t)(v > 0.25f) + (uint32_t)(v >= 0.75f) + (uint32_t)(v > 1.25f) +
-                 (uint32_t)(v >= 1.75f) + (uint32_t)(v > 2.5f) + (uint32_t)(v >= 3.5f) +
-                 (uint32_t)(v > 5.0f);
-    const uint32_t s = __float_as_uint(y[k]) >> 31;
-    const uint32_t c = zero ? 0u : (m | (s << 3));
-    codes |= c << (4 * k);
-  }
+  const float sc = __uint_as_float(u << 23);   // exponent field u: the scale 2^e
+  uint32_t c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, y[0], y[1], sc, 0);
+  c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c, y[2], y[3], sc, 1);
+  c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c, y[4], y[5], sc, 2);
+  c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c, y[6], y[7], sc, 3);
+  codes = a == 0.0f ? 0u : c;   // an all-zero block stores +0 codes
 }
 
 __device__ __forceinline__ float lo_bf16(uint32_t d) { return __uint_as_float(d << 16); }
@@ -123,7 +122,7 @@ __device__ __forceinline__ int write_first_entry(const WriteArgs& a, int b) {
 // quantised and stored at the entry's cache row (nothing when its page is absent).
 // Lane l stores one dword of latent codes, so the wave writes the entry's 256 code
 // bytes in one coalesced store.
-__device__ __forceinline__ void write_entry_wave(const WriteArgs& a, int b, int i, int lane) {
+__device__ __forceinline__ void write_entry_wave(const WriteArgs& a, int b, int i, int lane, bool live = true) {
   // The entry's inputs do not depend on where it is stored: their loads are issued
   // first and are in flight during the page lookup (start_tok, then the block table).
   EntryWords t;
@@ -131,7 +130,7 @@ __device__ __forceinline__ void write_entry_wave(const WriteArgs& a, int b, int 
   u32x4 ka = u32x4{0u, 0u, 0u, 0u};   // lanes 0..7: channels 8l..8l+7 of the indexer key
   if (lane < 8) ka = *reinterpret_cast<const u32x4*>(a.k_idx + ((int64_t)b * a.half + i) * CSA2_D_INDEX + lane * 8);
   const int j0 = write_first_entry(a, b);
-  if (j0 < 0) return;
+  if (j0 < 0 || !live) return;
   const int j = j0 + i;
   const int page = page_of(a.block_table, a.max_pages, a.n_pages, b, j);
   if (page < 0) return;

@@ -22,11 +22,16 @@
 namespace csa2 {
 namespace {
 
-__global__ __launch_bounds__(256) void write_kv_kernel(WriteArgs a, int64_t total) {
-  const int64_t e = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (e >= total) return;
-  const int b = (int)(e / a.half);
-  write_entry_wave(a, b, (int)(e - (int64_t)b * a.half), threadIdx.x & 63);
+// The wave index is made uniform, so the entry, its sequence and the page lookup are
+// scalar: start_tok and the block table come through scalar loads, which do not wait
+// behind the entry's vector loads.  A wave past the end repeats the last entry's loads
+// and stores nothing, so no branch sits between the kernel-argument loads.
+__global__ __launch_bounds__(256) void write_kv_kernel(WriteArgs a, int total) {
+  const int e0 = (int)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const bool live = e0 < total;
+  const uint32_t e = (uint32_t)(live ? e0 : total - 1);
+  const uint32_t b = e / (uint32_t)a.half;
+  write_entry_wave(a, (int)b, (int)(e - b * (uint32_t)a.half), threadIdx.x & 63, live);
 }
 
 
@@ -254,10 +259,10 @@ int launch_write_kv(const csa2_cache_t& c, int B, const int32_t* start_tok, int 
   const int half = T_new / ratio;   // entries per sequence
   const int64_t total = (int64_t)B * half;
   if (total == 0) return CSA2_OK;
+  if (total > 0x7fffffff) return CSA2_EUNSUPPORTED;
   const int64_t grid = (total + 3) / 4;
-  if (grid > 0x7fffffff) return CSA2_EUNSUPPORTED;
   hipLaunchKernelGGL(write_kv_kernel, dim3((unsigned)grid), dim3(256), 0, s,
-                     write_args(c, start_tok, half, x, w, k_idx, ratio), total);
+                     write_args(c, start_tok, half, x, w, k_idx, ratio), (int)total);
   return hip_status();
 }
 

@@ -128,7 +128,9 @@ size_t csa2_workspace_size(int fn, int B, int H, int64_t max_ctx, int topk, int 
  *   x, w: [B][T_new][512] bf16 (device); k_idx: [B][T_new/2][64] bf16 (device);
  *   start_tok: [B] int32 (device), even.  T_new must be even (> 0); an unpaired last
  *   token is the caller's to resubmit with the next one.  The table must already
- *   hold pages for every written entry. */
+ *   hold pages for every written entry.  The rule above covers finite y; the codes of
+ *   a block holding an Inf or NaN are unspecified.  More than 2^31 - 1 entries in one
+ *   call return CSA2_EUNSUPPORTED. */
 int csa2_write_kv(const csa2_cache_t *cache, int B, const int32_t *start_tok, int T_new,
                   const uint16_t *x, const uint16_t *w, const uint16_t *k_idx, int ratio,
                   void *stream);
