@@ -10,9 +10,10 @@
 //
 // One wavefront per entry.  Lane l owns channels 8l..8l+7: four 16-byte loads
 // (x and w of both tokens), one fused multiply-add per channel, an MX block of 32
-// channels spans 4 adjacent lanes (max via two lane swaps), and the lane stores one
-// dword of codes, so a wave writes the entry's 256 code bytes in one coalesced
-// store.  The kernel is HBM-bound: 4 KB read and 306 B written per entry.
+// channels spans 4 adjacent lanes (max via two DPP quad permutations), four hardware
+// converts make the lane's 8 codes, and the lane stores one dword of codes, so a wave
+// writes the entry's 256 code bytes in one coalesced store.  The kernel is HBM-bound:
+// 4 KB read and 306 B written per entry.
 #include <algorithm>
 
 #include "common.h"
