@@ -112,3 +112,46 @@ def test_batched_append_with_per_sequence_starts(fk):
     torch.cuda.synchronize()
     diff = cache_bytes_equal(gc, oc)
     assert all(v == 0 for v in diff.values()), diff
+
+
+def test_write_quantiser_ties_and_neighbours(fk):
+    """Every e2m1 decision point (ties and grid points), each exact and one step above and
+    below, both signs, at seven scale exponents: the stored codes and scales must be the
+    oracle's bit for bit.  Entry values are y = x0 + x1 (weights 1): x0 = +-v 2^k and x1 =
+    +-2^(k-20) when the value is offset, so y sits 2^-20 of the scale from the point."""
+    points = [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0, 7.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0]
+    combos = [(s * v, o) for v in points for o in (0, 1, -1) for s in (1.0, -1.0)]   # 90
+    ks = [-100, -40, -7, 0, 3, 30, 90]
+    n_ent = 64
+    x = np.zeros((2 * n_ent, 512))
+    w = np.ones((2 * n_ent, 512))
+    kk = np.zeros((n_ent, 64))
+    for i in range(n_ent):
+        k = ks[i % len(ks)]
+        for blk in range(16):
+            c0 = 32 * blk
+            x[2 * i, c0] = 7.0 * 2.0 ** k            # block maximum: scale exponent k
+            for j in range(31):
+                v, o = combos[(i * 7 + blk * 31 + j) % len(combos)]
+                x[2 * i, c0 + 1 + j] = v * 2.0 ** k
+                x[2 * i + 1, c0 + 1 + j] = o * np.copysign(1.0, v) * 2.0 ** (k - 20)
+        for blk in range(2):
+            c0 = 32 * blk
+            kk[i, c0] = -7.0 * 2.0 ** k
+            for j in range(31):
+                v, o = combos[(i * 5 + blk * 31 + j) % len(combos)]
+                step = 2.0 ** (np.floor(np.log2(abs(v))) - 7)               # one bf16 step at |v|
+                kk[i, c0 + 1 + j] = (v + o * np.copysign(step, v)) * 2.0 ** k
+    xb, wb, kb = _bf16_from_f64(x), _bf16_from_f64(w), _bf16_from_f64(kk)
+    assert np.array_equal(xb.float().numpy().astype(np.float64), x)    # every input is exact in bf16
+    assert np.array_equal(kb.float().numpy().astype(np.float64), kk)
+    bt = torch.tensor([[1, 0]], dtype=torch.int32)
+    oc = OracleCache(2, bt.numpy())
+    start = 2 * 32                           # entries 32..95: both pages
+    oc.write(0, start, bits(xb), bits(wb), bits(kb))
+    gc = fk.PagedCache.allocate(2, bt)
+    fk.write_kv(gc, torch.tensor([start], dtype=torch.int32, device="cuda"), xb.cuda()[None].contiguous(),
+                wb.cuda()[None].contiguous(), kb.cuda()[None].contiguous())
+    torch.cuda.synchronize()
+    diff = cache_bytes_equal(gc, oc)
+    assert all(v == 0 for v in diff.values()), diff
